@@ -1,0 +1,158 @@
+"""Seeded synthetic inputs for the gated delta-rule mixer.
+
+This module only draws random numbers and applies the caller-side input
+activations that sit *outside* the mixer core: L2 normalisation of q and k
+(the feature map is the identity inside the mixer, per the "How it works"
+section of the linear-attention wiki page, which notes that many modern
+variants use an identity feature map), beta = sigmoid(noise) and
+log(alpha) = -softplus(noise + shift) (the gates live in (0,1), per the Gated
+DeltaNet section of the linear-attention blog post).  It holds none of the
+recurrence's arithmetic, so both the fp64 oracle and the HIP path can consume
+what it returns without sharing any of the method's code.
+
+Draw order for every workload (one ``torch.Generator`` seeded once):
+q, k, v, beta-noise, alpha-noise, then the initial state.
+
+All tensors are returned on the CPU.  q, k, v are cast to the workload's
+dtype (bf16 or fp32); beta, log_alpha and states are always fp32.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+ALPHA_NONE, ALPHA_SCALAR, ALPHA_CHANNEL = 0, 1, 2
+MODE_NAMES = {ALPHA_NONE: "none", ALPHA_SCALAR: "scalar", ALPHA_CHANNEL: "channel"}
+
+# Gate shifts: log alpha = -softplus(N(0,1) + shift).
+SHIFT_SCALAR = 2.0   # Gated DeltaNet workloads (mean log alpha about -2.13)
+SHIFT_CHANNEL = 3.0  # channel-wise (Kimi-style) workload (mean about -3.05)
+
+
+@dataclasses.dataclass(frozen=True)
+class ChunkedWorkload:
+    name: str
+    B: int
+    H: int
+    L: int
+    dk: int
+    dv: int
+    C: int
+    dtype: torch.dtype
+    mode: int
+    seed: int
+    s0_std: float = 0.0  # 0 => no initial state (zero)
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.L
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    N: int
+    H: int
+    dk: int
+    dv: int
+    steps: int
+    dtype: torch.dtype
+    mode: int
+    seed: int
+    s0_std: float = 0.02
+
+
+# The five workloads the measurements are quoted on.
+DELTANET_FP32 = ChunkedWorkload("deltanet_fp32_B1_H2_L256_d64", 1, 2, 256, 64, 64, 64,
+                                torch.float32, ALPHA_NONE, 1)
+GDN_BF16 = ChunkedWorkload("gdn_bf16_B8_H8_L2048_d128", 8, 8, 2048, 128, 128, 64,
+                           torch.bfloat16, ALPHA_SCALAR, 2)
+KDA_BF16 = ChunkedWorkload("kda_bf16_B4_H16_L4096_d128", 4, 16, 4096, 128, 128, 64,
+                           torch.bfloat16, ALPHA_CHANNEL, 3)
+SWEEP_BL = ((32, 2048), (8, 8192), (2, 32768), (1, 65536))
+GDN_SWEEP = tuple(
+    ChunkedWorkload(f"gdn_bf16_sweep_B{b}_H16_L{l}_d128", b, 16, l, 128, 128, 64,
+                    torch.bfloat16, ALPHA_SCALAR, 4)
+    for b, l in SWEEP_BL)
+DECODE_BF16 = DecodeWorkload("gdn_decode_bf16_N256_H16_d128", 256, 16, 128, 128, 1024,
+                             torch.bfloat16, ALPHA_SCALAR, 5)
+
+
+def _l2norm(x: torch.Tensor) -> torch.Tensor:
+    n = x.norm(dim=-1, keepdim=True)
+    return x / torch.clamp(n, min=1e-6)
+
+
+def _gate_shift(mode: int) -> float:
+    return SHIFT_CHANNEL if mode == ALPHA_CHANNEL else SHIFT_SCALAR
+
+
+def chunked_inputs(B: int, H: int, L: int, dk: int, dv: int, dtype: torch.dtype,
+                   mode: int, seed: int, s0_std: float = 0.0,
+                   alpha_shift: float | None = None) -> dict:
+    """Inputs for one chunked-forward call, drawn in the fixed order.
+
+    Returns a dict with q, k [B,H,L,dk], v [B,H,L,dv] (``dtype``), beta
+    [B,H,L] fp32, log_alpha (None | [B,H,L] | [B,H,L,dk]) fp32 and S0
+    (None | [B,H,dv,dk] fp32).
+    """
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, H, L, dk, generator=g)
+    k = torch.randn(B, H, L, dk, generator=g)
+    v = torch.randn(B, H, L, dv, generator=g)
+    beta = torch.sigmoid(torch.randn(B, H, L, generator=g))
+    shift = _gate_shift(mode) if alpha_shift is None else alpha_shift
+    if mode == ALPHA_NONE:
+        log_alpha = None
+    elif mode == ALPHA_SCALAR:
+        log_alpha = -torch.nn.functional.softplus(torch.randn(B, H, L, generator=g) + shift)
+    elif mode == ALPHA_CHANNEL:
+        log_alpha = -torch.nn.functional.softplus(torch.randn(B, H, L, dk, generator=g) + shift)
+    else:
+        raise ValueError(f"unknown alpha mode {mode}")
+    S0 = None
+    if s0_std > 0:
+        S0 = torch.randn(B, H, dv, dk, generator=g) * s0_std
+    return dict(q=_l2norm(q).to(dtype).contiguous(), k=_l2norm(k).to(dtype).contiguous(),
+                v=v.to(dtype).contiguous(), beta=beta.contiguous(),
+                log_alpha=None if log_alpha is None else log_alpha.contiguous(),
+                S0=None if S0 is None else S0.contiguous())
+
+
+def workload_inputs(w: ChunkedWorkload) -> dict:
+    return chunked_inputs(w.B, w.H, w.L, w.dk, w.dv, w.dtype, w.mode, w.seed, w.s0_std)
+
+
+def decode_inputs(N: int, H: int, dk: int, dv: int, steps: int, dtype: torch.dtype,
+                  mode: int, seed: int, s0_std: float = 0.02,
+                  alpha_shift: float | None = None) -> dict:
+    """Inputs for ``steps`` consecutive decode steps over N sequences.
+
+    q, k [steps,N,H,dk], v [steps,N,H,dv] (``dtype``); beta [steps,N,H];
+    log_alpha None | [steps,N,H] | [steps,N,H,dk]; S0 [N,H,dv,dk] fp32.
+    """
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(steps, N, H, dk, generator=g)
+    k = torch.randn(steps, N, H, dk, generator=g)
+    v = torch.randn(steps, N, H, dv, generator=g)
+    beta = torch.sigmoid(torch.randn(steps, N, H, generator=g))
+    shift = _gate_shift(mode) if alpha_shift is None else alpha_shift
+    if mode == ALPHA_NONE:
+        log_alpha = None
+    elif mode == ALPHA_SCALAR:
+        log_alpha = -torch.nn.functional.softplus(torch.randn(steps, N, H, generator=g) + shift)
+    else:
+        log_alpha = -torch.nn.functional.softplus(
+            torch.randn(steps, N, H, dk, generator=g) + shift)
+    S0 = torch.randn(N, H, dv, dk, generator=g) * s0_std
+    return dict(q=_l2norm(q).to(dtype).contiguous(), k=_l2norm(k).to(dtype).contiguous(),
+                v=v.to(dtype).contiguous(), beta=beta.contiguous(),
+                log_alpha=None if log_alpha is None else log_alpha.contiguous(),
+                S0=S0.contiguous())
+
+
+def decode_workload_inputs(w: DecodeWorkload, steps: int | None = None) -> dict:
+    return decode_inputs(w.N, w.H, w.dk, w.dv, w.steps if steps is None else steps,
+                         w.dtype, w.mode, w.seed, w.s0_std)
+

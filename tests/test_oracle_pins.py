@@ -1,0 +1,315 @@
+"""Pins for the fp64 oracle (CPU only).
+
+The oracle is trusted only because it agrees with things other than itself:
+hand-worked examples, closed forms, invariants the pages state, and
+independent brute-force routes (``brute_force.py``).  The last test plants
+plausible mistakes in a separate loop and checks that every one of them
+fails at least one pin, i.e. the pins are sensitive to such mistakes.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import brute_force as bf
+
+NONE, SCALAR, CHANNEL = oracle.ALPHA_NONE, oracle.ALPHA_SCALAR, oracle.ALPHA_CHANNEL
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+# --------------------------------------------------------------------------
+# helpers
+def _unit(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def _rand_chain(rng, L, dk, dv, mode, s0=True, shift=1.0):
+    q = _unit(rng.standard_normal((L, dk)))
+    k = _unit(rng.standard_normal((L, dk)))
+    v = rng.standard_normal((L, dv))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal(L)))
+    if mode == NONE:
+        la = None
+    elif mode == SCALAR:
+        la = -np.log1p(np.exp(rng.standard_normal(L) + shift))
+    else:
+        la = -np.log1p(np.exp(rng.standard_normal((L, dk)) + shift))
+    S0 = 0.3 * rng.standard_normal((dv, dk)) if s0 else None
+    return q, k, v, beta, la, S0
+
+
+def oracle_runner(q, k, v, beta, la=None, S0=None, no_delta=False):
+    mode = NONE if la is None else (CHANNEL if np.ndim(la) == 2 else SCALAR)
+    return oracle.run(q, k, v, beta, la, S0, mode=mode, no_delta=no_delta, nthreads=1)
+
+
+def _err(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    return float(np.max(np.abs(a - b))) / max(1.0, float(np.max(np.abs(b))))
+
+
+# --------------------------------------------------------------------------
+# pins, each written against an arbitrary runner so the mutation test can
+# reuse them.  Each returns the worst error it saw; the bound is 1e-10.
+def pin_exact_recall(run):
+    """alpha = beta = 1, orthonormal keys: S k_i = v_i, and querying with k_i
+    returns v_i ("DeltaNet" section of the blog post: perfectly orthogonal
+    keys isolate v_j; beta = 1 fully replaces the retrieved value)."""
+    rng = np.random.default_rng(11)
+    dk, dv, n = 8, 5, 6
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    keys = Qm.T[:n]                                  # orthonormal rows
+    vals = rng.standard_normal((n, dv))
+    L = 2 * n
+    k = np.vstack([keys, _unit(rng.standard_normal((n, dk)))])
+    v = np.vstack([vals, rng.standard_normal((n, dv))])
+    q = np.vstack([_unit(rng.standard_normal((n, dk))), keys])
+    beta = np.concatenate([np.ones(n), np.zeros(n)])  # write n pairs, then only read
+    worst = 0.0
+    for la in (None, np.zeros(L)):
+        o, S = run(q, k, v, beta, la, None)
+        worst = max(worst, _err(o[n:], vals), _err(S @ keys.T, vals.T))
+    return worst
+
+
+def pin_overwrite(run):
+    """The same orthonormal keys written twice: the memory returns the most
+    recent value (beta = 1 full replacement, blog "DeltaNet" section)."""
+    rng = np.random.default_rng(12)
+    dk, dv, n = 6, 4, 4
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    keys = Qm.T[:n]
+    v1, v2 = rng.standard_normal((n, dv)), rng.standard_normal((n, dv))
+    k = np.vstack([keys, keys[::-1]])
+    v = np.vstack([v1, v2[::-1]])
+    q = _unit(rng.standard_normal((2 * n, dk)))
+    o, S = run(q, k, v, np.ones(2 * n), None, 0.5 * rng.standard_normal((dv, dk)))
+    # S0 components outside span(keys) survive; the key directions hold v2.
+    return _err(S @ keys.T, v2.T)
+
+
+def pin_beta_one_write(run):
+    """beta = 1 and a unit key: after the write S_t k_t = v_t exactly, for any
+    decay and any (non-orthogonal) history (the delta rule as one SGD step on
+    0.5 |S k - v|^2 with unit step, wiki "DeltaNet" item).  With q_t = k_t the
+    output is v_t."""
+    rng = np.random.default_rng(13)
+    worst = 0.0
+    for mode in (NONE, SCALAR, CHANNEL):
+        q, k, v, beta, la, S0 = _rand_chain(rng, 20, 7, 5, mode)
+        o, _ = run(k, k, v, np.ones(20), la, S0)
+        worst = max(worst, _err(o, v))
+    return worst
+
+
+def pin_beta_zero(run):
+    """beta = 0 keeps memory apart from the decay (blog "DeltaNet": beta = 0
+    keeps old memory): o_t = S0 (prod alpha . q_t); S_final = S0 Diag(prod)."""
+    rng = np.random.default_rng(14)
+    worst = 0.0
+    for mode in (NONE, SCALAR, CHANNEL):
+        q, k, v, _, la, S0 = _rand_chain(rng, 12, 6, 4, mode, shift=-1.0)
+        o, S = run(q, k, v, np.zeros(12), la, S0)
+        if la is None:
+            cum = np.zeros((12, 6))
+        else:
+            la2 = la if np.ndim(la) == 2 else np.repeat(la[:, None], 6, axis=1)
+            cum = np.cumsum(la2, axis=0)
+        ref = (q * np.exp(cum)) @ S0.T
+        worst = max(worst, _err(o, ref), _err(S, S0 * np.exp(cum[-1])[None, :]))
+    return worst
+
+
+def pin_first_token(run):
+    """From a zero state one token gives S_1 = beta v k^T and
+    o_1 = beta (k.q) v (blog "DeltaNet" update with S_0 = 0)."""
+    rng = np.random.default_rng(15)
+    worst = 0.0
+    for mode in (NONE, SCALAR, CHANNEL):
+        q, k, v, beta, la, _ = _rand_chain(rng, 1, 5, 3, mode)
+        o, S = run(q, k, v, beta, la, None)
+        worst = max(worst, _err(o[0], beta[0] * (k[0] @ q[0]) * v[0]),
+                    _err(S, beta[0] * np.outer(v[0], k[0])))
+    return worst
+
+
+def pin_linear_attention_sum(run):
+    """Delta term removed, alpha = beta = 1: S_L = sum_i v_i k_i^T = V^T K
+    (blog "Linear Attention as a Linear RNN")."""
+    rng = np.random.default_rng(16)
+    q, k, v, _, _, _ = _rand_chain(rng, 30, 6, 4, NONE)
+    o, S = run(q, k, v, np.ones(30), None, None, no_delta=True)
+    return max(_err(S, v.T @ k), _err(o, np.tril(q @ k.T) @ v))
+
+
+def pin_masked_parallel(run):
+    """Delta term removed: the loop equals the parallel masked form, with
+    decay and beta, for every gate mode (blog "Chunkwise Parallel Form")."""
+    rng = np.random.default_rng(17)
+    worst = 0.0
+    for mode in (NONE, SCALAR, CHANNEL):
+        q, k, v, beta, la, S0 = _rand_chain(rng, 40, 6, 5, mode, shift=0.0)
+        o, _ = run(q, k, v, beta, la, S0, no_delta=True)
+        worst = max(worst, _err(o, bf.masked_parallel_no_delta(q, k, v, beta, la, S0)))
+    return worst
+
+
+def pin_dense_transition(run):
+    """Explicit d_k x d_k transitions A_t = Diag(alpha)(I - beta k k^T) (blog,
+    end of the "Kimi Delta Attention" section), all gate modes."""
+    rng = np.random.default_rng(18)
+    worst = 0.0
+    for mode in (NONE, SCALAR, CHANNEL):
+        q, k, v, beta, la, S0 = _rand_chain(rng, 24, 6, 6, mode, shift=-0.5)
+        o, S = run(q, k, v, beta, la, S0)
+        ro, rS = bf.dense_transition(q, k, v, beta, la, S0)
+        worst = max(worst, _err(o, ro), _err(S, rS))
+    return worst
+
+
+def pin_kimi_orientation(run):
+    """The blog's Kimi recurrence in the d_k x d_v orientation gives the
+    transposed state and the same outputs (orientation reading)."""
+    rng = np.random.default_rng(19)
+    worst = 0.0
+    for mode in (NONE, SCALAR, CHANNEL):
+        q, k, v, beta, la, S0 = _rand_chain(rng, 24, 6, 6, mode, shift=-0.5)
+        o, S = run(q, k, v, beta, la, S0)
+        ro, rS = bf.kimi_orientation(q, k, v, beta, la, S0)
+        worst = max(worst, _err(o, ro), _err(S, rS))
+    return worst
+
+
+def pin_mode_reductions(run):
+    """Channel gate with equal channels == scalar gate; scalar gate with
+    log alpha = 0 == DeltaNet ("Linear Attention Architectures", Sec. 3:
+    if the vector gate collapses to a scalar the update reduces to Gated
+    DeltaNet's; blog: Gated DeltaNet adds a decay to DeltaNet)."""
+    rng = np.random.default_rng(20)
+    q, k, v, beta, la, S0 = _rand_chain(rng, 30, 6, 4, SCALAR)
+    o_s, S_s = run(q, k, v, beta, la, S0)
+    o_c, S_c = run(q, k, v, beta, np.repeat(la[:, None], 6, axis=1), S0)
+    o_n, S_n = run(q, k, v, beta, None, S0)
+    o_z, S_z = run(q, k, v, beta, np.zeros(30), S0)
+    return max(_err(o_c, o_s), _err(S_c, S_s), _err(o_z, o_n), _err(S_z, S_n))
+
+
+def pin_resume(run):
+    """The state is the whole memory: running L1 tokens, then L2 tokens from
+    the resulting state equals one run of L1 + L2 tokens (blog "Chunkwise
+    Parallel Form": the state is additive across boundaries; "Recurrent
+    Linear Attention for Inference": one O(d^2) state)."""
+    rng = np.random.default_rng(21)
+    worst = 0.0
+    for mode in (NONE, SCALAR, CHANNEL):
+        q, k, v, beta, la, S0 = _rand_chain(rng, 37, 6, 5, mode)
+        o, S = run(q, k, v, beta, la, S0)
+        cut = 16
+        la1 = None if la is None else la[:cut]
+        la2 = None if la is None else la[cut:]
+        o1, S1 = run(q[:cut], k[:cut], v[:cut], beta[:cut], la1, S0)
+        o2, S2 = run(q[cut:], k[cut:], v[cut:], beta[cut:], la2, S1)
+        worst = max(worst, _err(np.vstack([o1, o2]), o), _err(S2, S))
+    return worst
+
+
+def _golden_value(x):
+    if isinstance(x, str):
+        sign = -1.0 if x.startswith("-") else 1.0
+        return sign * math.log(float(x.lstrip("-").replace("ln", "")))
+    return float(x)
+
+
+def _golden_array(a):
+    if a is None:
+        return None
+    if isinstance(a, list):
+        return np.array([_golden_array(x) for x in a], dtype=np.float64)
+    return _golden_value(a)
+
+
+def pin_worked_examples(run):
+    """Hand-worked 2x2 examples (tests/golden/worked_examples.json)."""
+    with open(GOLDEN) as f:
+        ex = json.load(f)["examples"]
+    worst = 0.0
+    for e in ex:
+        args = [_golden_array(e[n]) for n in ("q", "k", "v", "beta", "log_alpha", "S0")]
+        o, S = run(*args)
+        worst = max(worst, _err(o, _golden_array(e["o"])), _err(S, _golden_array(e["S_final"])))
+    return worst
+
+
+PINS = [pin_exact_recall, pin_overwrite, pin_beta_one_write, pin_beta_zero, pin_first_token,
+        pin_linear_attention_sum, pin_masked_parallel, pin_dense_transition,
+        pin_kimi_orientation, pin_mode_reductions, pin_resume, pin_worked_examples]
+TOL = 1e-10
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_oracle_pin(pin):
+    assert pin(oracle_runner) <= TOL
+
+
+@pytest.mark.parametrize("mutation", bf.MUTATIONS)
+def test_planted_mistake_is_caught(mutation):
+    """Every planted mistake fails at least one pin (pins are sensitive)."""
+    def run(q, k, v, beta, la=None, S0=None, no_delta=False):
+        return bf.mutant_loop(q, k, v, beta, la, S0, mutation=mutation, no_delta=no_delta)
+
+    failed = []
+    for pin in PINS:
+        try:
+            e = pin(run)
+            if not (e <= TOL):
+                failed.append(pin.__name__)
+        except (ValueError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"mutation {mutation} passed every pin"
+
+
+def test_unmutated_loop_passes_pins():
+    def run(q, k, v, beta, la=None, S0=None, no_delta=False):
+        return bf.mutant_loop(q, k, v, beta, la, S0, mutation=None, no_delta=no_delta)
+
+    for pin in PINS:
+        assert pin(run) <= TOL, pin.__name__
+
+
+def test_state_size_constant_in_length():
+    """The memory is one d_v x d_k matrix per chain whatever L is (blog
+    "Recurrent Linear Attention for Inference": O(d^2) memory)."""
+    rng = np.random.default_rng(22)
+    for L in (1, 64, 4096):
+        q, k, v, beta, la, S0 = _rand_chain(rng, L, 8, 4, SCALAR)
+        o, S = oracle.run(q[None], k[None], v[None], beta[None], la[None], S0[None])
+        assert S.shape == (1, 4, 8) and o.shape == (1, L, 4)
+
+
+def test_batched_chains_are_independent():
+    """Leading (batch, head) axes are independent chains: running them
+    together equals running each alone (blog: each head runs its own
+    recurrent state update)."""
+    rng = np.random.default_rng(23)
+    chains = [_rand_chain(rng, 19, 5, 3, CHANNEL) for _ in range(6)]
+    stack = [np.stack([c[i] for c in chains]).reshape((2, 3) + np.shape(chains[0][i]))
+             for i in range(6)]
+    o, S = oracle.run(*stack, nthreads=3)
+    for j, c in enumerate(chains):
+        oj, Sj = oracle_runner(*c)
+        b, h = divmod(j, 3)
+        assert np.array_equal(o[b, h], oj) and np.array_equal(S[b, h], Sj)
+
+
+def test_oracle_rejects_bad_shapes():
+    rng = np.random.default_rng(24)
+    q, k, v, beta, la, S0 = _rand_chain(rng, 5, 4, 3, SCALAR)
+    with pytest.raises(ValueError):
+        oracle.run(q, k[:4], v, beta, la, S0)
+    with pytest.raises(ValueError):
+        oracle.run(q, k, v, beta, la[:3], S0, mode=SCALAR)
