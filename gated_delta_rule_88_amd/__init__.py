@@ -1,0 +1,195 @@
+"""Gated delta-rule memory for MI355X: Python binding over libgdr.so.
+
+The binding only marshals arguments: it checks devices, dtypes, shapes and
+contiguity of torch tensors, allocates outputs (and the chunked forward's
+workspace) with torch, and passes raw device pointers plus the current HIP
+stream to the C ABI declared in ``include/gdr.h``.  Every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if
+``libgdr.so`` is missing or cannot be loaded, importing a function raises.
+
+Functions carry the C names:
+
+* ``gdr_fwd_chunked(q, k, v, beta, log_alpha=None, S0=None, chunk=64, ...)``
+  -> ``(o, S_final)``: chunkwise forward over ``[B, H, L, d]`` inputs.
+* ``gdr_decode_step(q, k, v, beta, log_alpha, S, o=None)`` -> ``o``: one
+  recurrent step over ``[N, H, d]`` inputs, updating ``S`` in place.
+* ``gdr_fwd_chunked_workspace_size``, ``gdr_abi_version``,
+  ``gdr_status_string``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdr.so")
+
+GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED = 0, 1, 2
+GDR_ERR_WORKSPACE_TOO_SMALL, GDR_ERR_HIP = 3, 4
+GDR_F32, GDR_BF16 = 0, 1
+GDR_ALPHA_NONE, GDR_ALPHA_SCALAR, GDR_ALPHA_CHANNEL = 0, 1, 2
+
+EXPORTED = ("gdr_abi_version", "gdr_status_string", "gdr_fwd_chunked_workspace_size",
+            "gdr_fwd_chunked", "gdr_decode_step")
+
+_lib = None
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {gdr_status_string(status)} (status {status})")
+        self.status = status
+
+
+def load_library():
+    """Load libgdr.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m gated_delta_rule_88_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.gdr_abi_version.restype = i
+    lib.gdr_status_string.argtypes = [i]
+    lib.gdr_status_string.restype = ctypes.c_char_p
+    lib.gdr_fwd_chunked_workspace_size.argtypes = [i] * 8
+    lib.gdr_fwd_chunked_workspace_size.restype = sz
+    lib.gdr_fwd_chunked.argtypes = [i] * 7 + [vp] * 4 + [i] + [vp] * 5 + [sz, vp]
+    lib.gdr_fwd_chunked.restype = i
+    lib.gdr_decode_step.argtypes = [i] * 5 + [vp] * 4 + [i] + [vp] * 4
+    lib.gdr_decode_step.restype = i
+    _lib = lib
+    return lib
+
+
+def gdr_abi_version() -> int:
+    return int(load_library().gdr_abi_version())
+
+
+def gdr_status_string(status: int) -> str:
+    return load_library().gdr_status_string(int(status)).decode()
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return GDR_BF16
+    if t == torch.float32:
+        return GDR_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t}")
+
+
+def _mode_of(log_alpha, q) -> int:
+    if log_alpha is None:
+        return GDR_ALPHA_NONE
+    return GDR_ALPHA_CHANNEL if log_alpha.dim() == q.dim() else GDR_ALPHA_SCALAR
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype, device, shape):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def gdr_fwd_chunked_workspace_size(B, H, L, d_k, d_v, C, dtype, alpha_mode) -> int:
+    return int(load_library().gdr_fwd_chunked_workspace_size(B, H, L, d_k, d_v, C, dtype,
+                                                             alpha_mode))
+
+
+def gdr_fwd_chunked(q, k, v, beta, log_alpha=None, S0=None, chunk: int = 64, *,
+                    o=None, S_final=None, write_final: bool = True, workspace=None,
+                    stream=None):
+    """Chunkwise forward.  q, k [B,H,L,dk]; v [B,H,L,dv] (bf16 or fp32);
+    beta [B,H,L] fp32; log_alpha None | [B,H,L] | [B,H,L,dk] fp32;
+    S0 None | [B,H,dv,dk] fp32.  Returns (o, S_final or None).
+    Pass S_final=S0 to update the state in place."""
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, L, d_k]")
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(dt)
+    mode = _mode_of(log_alpha, q)
+    _check(q, "q", dt, dev, (B, H, L, dk))
+    _check(k, "k", dt, dev, (B, H, L, dk))
+    _check(v, "v", dt, dev, (B, H, L, dv))
+    _check(beta, "beta", torch.float32, dev, (B, H, L))
+    if mode == GDR_ALPHA_SCALAR:
+        _check(log_alpha, "log_alpha", torch.float32, dev, (B, H, L))
+    elif mode == GDR_ALPHA_CHANNEL:
+        _check(log_alpha, "log_alpha", torch.float32, dev, (B, H, L, dk))
+    _check(S0, "S0", torch.float32, dev, (B, H, dv, dk))
+    if o is None:
+        o = torch.empty((B, H, L, dv), dtype=dt, device=dev)
+    _check(o, "o", dt, dev, (B, H, L, dv))
+    if S_final is None and write_final:
+        S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    _check(S_final, "S_final", torch.float32, dev, (B, H, dv, dk))
+    need = gdr_fwd_chunked_workspace_size(B, H, L, dk, dv, chunk, code, mode)
+    if need == ctypes.c_size_t(-1).value:
+        raise GdrError(GDR_ERR_UNSUPPORTED, "gdr_fwd_chunked_workspace_size")
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdr_fwd_chunked(B, H, L, dk, dv, chunk, code, _ptr(q), _ptr(k), _ptr(v),
+                             _ptr(beta), mode, _ptr(log_alpha), _ptr(S0), _ptr(o),
+                             _ptr(S_final), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_fwd_chunked")
+    return o, S_final
+
+
+def gdr_decode_step(q, k, v, beta, log_alpha, S, o=None, *, stream=None):
+    """One decode step.  q, k [N,H,dk]; v [N,H,dv]; beta [N,H];
+    log_alpha None | [N,H] | [N,H,dk]; S [N,H,dv,dk] fp32 (updated in
+    place).  Returns o [N,H,dv]."""
+    lib = load_library()
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, d_k]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    mode = _mode_of(log_alpha, q)
+    _check(q, "q", dt, dev, (N, H, dk))
+    _check(k, "k", dt, dev, (N, H, dk))
+    _check(v, "v", dt, dev, (N, H, dv))
+    _check(beta, "beta", torch.float32, dev, (N, H))
+    if mode == GDR_ALPHA_SCALAR:
+        _check(log_alpha, "log_alpha", torch.float32, dev, (N, H))
+    elif mode == GDR_ALPHA_CHANNEL:
+        _check(log_alpha, "log_alpha", torch.float32, dev, (N, H, dk))
+    _check(S, "S", torch.float32, dev, (N, H, dv, dk))
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    _check(o, "o", dt, dev, (N, H, dv))
+    st = lib.gdr_decode_step(N, H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), mode,
+                             _ptr(log_alpha), _ptr(S), _ptr(o), _stream(stream))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_decode_step")
+    return o

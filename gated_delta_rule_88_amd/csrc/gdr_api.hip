@@ -1,0 +1,150 @@
+// gdr_api.hip -- the C ABI (include/gdr.h): argument validation and
+// dispatch to the kernels.  Every check runs on the host before anything is
+// enqueued, so an error status means no device memory was touched.
+#include "../../include/gdr.h"
+
+#include <stdint.h>
+
+#include "gdr_internal.h"
+
+#define GDR_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi); empty when lo == hi
+};
+Range rng(const void* p, size_t bytes) {
+    const uintptr_t b = (uintptr_t)p;
+    return Range{b, p ? b + bytes : b};
+}
+bool overlap(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+bool supported_dim(int d) { return d == 64 || d == 128; }
+bool supported_chunk(int c) { return c == 16 || c == 32 || c == 64; }
+size_t elem_size(int dtype) { return dtype == gdr::kBF16 ? 2 : 4; }
+
+// Largest workgroup count along grid x times 256 threads must fit 32 bits.
+constexpr size_t kMaxGroups = (size_t)1 << 23;
+
+int check_chunk_sizes(int B, int H, int L, int dk, int dv, int C, int dtype, int mode)
+{
+    if (B < 0 || H < 0 || L < 0) return GDR_ERR_INVALID_ARG;
+    if (mode < GDR_ALPHA_NONE || mode > GDR_ALPHA_CHANNEL) return GDR_ERR_INVALID_ARG;
+    if (dtype != GDR_F32 && dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
+    if (!supported_dim(dk) || !supported_dim(dv) || !supported_chunk(C)) return GDR_ERR_UNSUPPORTED;
+    const int Ce = gdr::effective_chunk(C, dtype, dk);
+    const size_t nc = ((size_t)L + Ce - 1) / Ce;
+    if ((size_t)B * H * nc > kMaxGroups) return GDR_ERR_UNSUPPORTED;
+    return GDR_OK;
+}
+
+size_t chunk_workspace(int B, int H, int L, int dk, int C, int dtype)
+{
+    const int Ce = gdr::effective_chunk(C, dtype, dk);
+    const size_t nc = ((size_t)L + Ce - 1) / Ce;
+    return (size_t)B * H * nc * gdr::chunk_workspace_bytes_per_chunk(Ce, dtype);
+}
+
+}  // namespace
+
+GDR_EXPORT int gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+GDR_EXPORT const char* gdr_status_string(int status)
+{
+    switch (status) {
+    case GDR_OK: return "GDR_OK: success";
+    case GDR_ERR_INVALID_ARG: return "GDR_ERR_INVALID_ARG: invalid argument";
+    case GDR_ERR_UNSUPPORTED: return "GDR_ERR_UNSUPPORTED: sizes or dtype outside the supported domain";
+    case GDR_ERR_WORKSPACE_TOO_SMALL: return "GDR_ERR_WORKSPACE_TOO_SMALL: workspace smaller than required";
+    case GDR_ERR_HIP: return "GDR_ERR_HIP: a HIP launch failed";
+    default: return "unknown gdr status";
+    }
+}
+
+GDR_EXPORT size_t gdr_fwd_chunked_workspace_size(int B, int H, int L, int d_k, int d_v, int C,
+                                                 int dtype, int alpha_mode)
+{
+    if (check_chunk_sizes(B, H, L, d_k, d_v, C, dtype, alpha_mode) != GDR_OK) return (size_t)-1;
+    return chunk_workspace(B, H, L, d_k, C, dtype);
+}
+
+GDR_EXPORT int gdr_fwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                               const void* q, const void* k, const void* v,
+                               const float* beta, int alpha_mode, const float* log_alpha,
+                               const float* S0, void* o, float* S_final,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    int st = check_chunk_sizes(B, H, L, d_k, d_v, C, dtype, alpha_mode);
+    if (st != GDR_OK) return st;
+    const size_t BH = (size_t)B * H;
+    if (BH == 0) return GDR_OK;
+    const size_t es = elem_size(dtype);
+    const size_t nt = BH * L;
+    const size_t state_bytes = BH * d_v * d_k * 4;
+    if (L > 0) {
+        if (!q || !k || !v || !beta || !o) return GDR_ERR_INVALID_ARG;
+        if ((alpha_mode == GDR_ALPHA_NONE) != (log_alpha == nullptr)) return GDR_ERR_INVALID_ARG;
+    }
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(S0, 16) || !aligned(S_final, 16) || !aligned(workspace, 16) ||
+        !aligned(beta, 4) || !aligned(log_alpha, alpha_mode == GDR_ALPHA_CHANNEL ? 16 : 4))
+        return GDR_ERR_INVALID_ARG;
+
+    const size_t la_bytes = alpha_mode == GDR_ALPHA_CHANNEL ? nt * d_k * 4
+                          : alpha_mode == GDR_ALPHA_SCALAR ? nt * 4 : 0;
+    const Range rq = rng(q, nt * d_k * es), rk = rng(k, nt * d_k * es), rv = rng(v, nt * d_v * es);
+    const Range rb = rng(beta, nt * 4), ra = rng(log_alpha, la_bytes);
+    const Range r0 = rng(S0, state_bytes), ro = rng(o, nt * d_v * es);
+    const Range rf = rng(S_final, state_bytes);
+    const size_t need = chunk_workspace(B, H, L, d_k, C, dtype);
+    const Range rw = rng(workspace, need);
+    for (Range x : {rq, rk, rv, rb, ra, r0, rf, rw})
+        if (overlap(ro, x)) return GDR_ERR_INVALID_ARG;
+    for (Range x : {rq, rk, rv, rb, ra, rw})
+        if (overlap(rf, x)) return GDR_ERR_INVALID_ARG;
+    if (overlap(rf, r0) && (const void*)S_final != (const void*)S0) return GDR_ERR_INVALID_ARG;
+    for (Range x : {rq, rk, rv, rb, ra, r0})
+        if (overlap(rw, x)) return GDR_ERR_INVALID_ARG;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GDR_ERR_WORKSPACE_TOO_SMALL;
+
+    gdr::ChunkArgs a{B, H, L, d_k, d_v, C, dtype, alpha_mode, q, k, v, beta, log_alpha, S0, o,
+                     S_final, workspace, stream};
+    return gdr::launch_fwd_chunked(a) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+GDR_EXPORT int gdr_decode_step(int N, int H, int d_k, int d_v, int dtype,
+                               const void* q, const void* k, const void* v,
+                               const float* beta, int alpha_mode, const float* log_alpha,
+                               float* S, void* o, hipStream_t stream)
+{
+    if (N < 0 || H < 0) return GDR_ERR_INVALID_ARG;
+    if (alpha_mode < GDR_ALPHA_NONE || alpha_mode > GDR_ALPHA_CHANNEL) return GDR_ERR_INVALID_ARG;
+    if (dtype != GDR_F32 && dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
+    if (!supported_dim(d_k) || !supported_dim(d_v)) return GDR_ERR_UNSUPPORTED;
+    const size_t NH = (size_t)N * H;
+    if (NH * 4 > kMaxGroups) return GDR_ERR_UNSUPPORTED;
+    if (NH == 0) return GDR_OK;
+    if (!q || !k || !v || !beta || !S || !o) return GDR_ERR_INVALID_ARG;
+    if ((alpha_mode == GDR_ALPHA_NONE) != (log_alpha == nullptr)) return GDR_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(S, 16) || !aligned(beta, 4) || !aligned(log_alpha, alpha_mode == GDR_ALPHA_CHANNEL ? 16 : 4))
+        return GDR_ERR_INVALID_ARG;
+    const size_t es = elem_size(dtype);
+    const size_t la_bytes = alpha_mode == GDR_ALPHA_CHANNEL ? NH * d_k * 4
+                          : alpha_mode == GDR_ALPHA_SCALAR ? NH * 4 : 0;
+    const Range rq = rng(q, NH * d_k * es), rk = rng(k, NH * d_k * es), rv = rng(v, NH * d_v * es);
+    const Range rb = rng(beta, NH * 4), ra = rng(log_alpha, la_bytes);
+    const Range rs = rng(S, NH * d_v * d_k * 4), ro = rng(o, NH * d_v * es);
+    for (Range x : {rq, rk, rv, rb, ra, rs})
+        if (overlap(ro, x)) return GDR_ERR_INVALID_ARG;
+    for (Range x : {rq, rk, rv, rb, ra})
+        if (overlap(rs, x)) return GDR_ERR_INVALID_ARG;
+
+    gdr::DecodeArgs a{N, H, d_k, d_v, dtype, alpha_mode, q, k, v, beta, log_alpha, S, o, stream};
+    return gdr::launch_decode_step(a) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}

@@ -1,0 +1,165 @@
+// gdr_device.h -- device helpers for the gfx950 kernels: element types,
+// 16-byte vector access, bf16 conversion and 16x16 MFMA fragments.
+//
+// Fragment convention (used by every tile product in this library):
+// products are written in "NT" form, C[m][n] = sum_k A[m][k] * B[n][k], with
+// both operands stored in LDS as [outer][k] (k contiguous).  For one 32-wide
+// k-step, lane l supplies row (l % 16) of A and row (l % 16) of B, and the 8
+// consecutive k values k0 + 8*(l/16) .. +7 of each.  Because A and B use the
+// same k mapping the sum over k does not depend on how the hardware orders
+// k inside an instruction.  The 16x16 fp32 accumulator holds
+// C[4*(l/16) + e][l % 16] in element e (e = 0..3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+// ---------------------------------------------------------------- conversion
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// Elements per 16-byte vector.
+template <typename T> struct Vec { static constexpr int n = 16 / sizeof(T); };
+
+// 16-byte loads and stores (global or LDS; the pointer must be 16-B aligned).
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+// Unpack / pack a 16-byte vector of T into floats.
+template <typename T> struct Pack;
+template <> struct Pack<float> {
+    static constexpr int n = 4;
+    __device__ static __forceinline__ void unpack(u32x4 v, float* f) {
+        f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+        f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+    }
+    __device__ static __forceinline__ u32x4 pack(const float* f) {
+        u32x4 v; v.x = __float_as_uint(f[0]); v.y = __float_as_uint(f[1]);
+        v.z = __float_as_uint(f[2]); v.w = __float_as_uint(f[3]); return v;
+    }
+};
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+    bf16 x = (bf16)a, y = (bf16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+template <> struct Pack<bf16> {
+    static constexpr int n = 8;
+    __device__ static __forceinline__ void unpack(u32x4 v, float* f) {
+        f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+        f[4] = bf_lo(v.z); f[5] = bf_hi(v.z); f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
+    }
+    __device__ static __forceinline__ u32x4 pack(const float* f) {
+        u32x4 v; v.x = pack_bf2(f[0], f[1]); v.y = pack_bf2(f[2], f[3]);
+        v.z = pack_bf2(f[4], f[5]); v.w = pack_bf2(f[6], f[7]); return v;
+    }
+};
+
+// Store 4 consecutive elements (from fp32) at p (8 B for bf16, 16 B for f32).
+__device__ __forceinline__ void st4(bf16* p, float a, float b, float c, float d) {
+    u32x2 v; v.x = pack_bf2(a, b); v.y = pack_bf2(c, d); st8(p, v);
+}
+__device__ __forceinline__ void st4(float* p, float a, float b, float c, float d) {
+    u32x4 v; v.x = __float_as_uint(a); v.y = __float_as_uint(b);
+    v.z = __float_as_uint(c); v.w = __float_as_uint(d); st16(p, v);
+}
+
+// ---------------------------------------------------------------- fragments
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { f32x4 lo, hi; };
+
+// Fragment of a matrix stored [row][k] with leading dimension ld (elements):
+// lane reads row row0 + l%16, k = k0 + 8*(l/16) .. +7.
+__device__ __forceinline__ Frag<bf16> ldfrag(const bf16* base, int ld, int row0, int k0) {
+    const int l = lane_id();
+    Frag<bf16> f;
+    f.v = *reinterpret_cast<const bf16x8*>(base + (row0 + (l & 15)) * ld + k0 + 8 * (l >> 4));
+    return f;
+}
+__device__ __forceinline__ Frag<float> ldfrag(const float* base, int ld, int row0, int k0) {
+    const int l = lane_id();
+    const float* p = base + (row0 + (l & 15)) * ld + k0 + 8 * (l >> 4);
+    Frag<float> f;
+    f.lo = *reinterpret_cast<const f32x4*>(p);
+    f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+    return f;
+}
+
+// Fragment read from p (8 consecutive elements) with element j multiplied
+// by s[j] in fp32 before the operand is formed.
+__device__ __forceinline__ void load_scaled_frag(Frag<bf16>& f, const bf16* p, const float* s) {
+    float x[8];
+    Pack<bf16>::unpack(ld16(p), x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] *= s[j];
+    f.v = __builtin_bit_cast(bf16x8, Pack<bf16>::pack(x));
+}
+__device__ __forceinline__ void load_scaled_frag(Frag<float>& f, const float* p, const float* s) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    f.lo = f32x4{a.x * s[0], a.y * s[1], a.z * s[2], a.w * s[3]};
+    f.hi = f32x4{b.x * s[4], b.y * s[5], b.z * s[6], b.w * s[7]};
+}
+
+// acc += A * B^T over one 32-wide k-step.
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.y, b.lo.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.z, b.lo.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.w, b.lo.w, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.x, b.hi.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.y, b.hi.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.z, b.hi.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, acc, 0, 0, 0);
+}
+
+// fp32 product over one 16-wide k-step (k0 + 4*(l/16) .. +3 per lane), used
+// by the triangular inverse, which stays in fp32 on every path.
+__device__ __forceinline__ void mma_k16(f32x4& acc, const float* a, int lda, int arow0,
+                                        const float* b, int ldb, int brow0, int k0) {
+    const int l = lane_id();
+    f32x4 x = *reinterpret_cast<const f32x4*>(a + (arow0 + (l & 15)) * lda + k0 + 4 * (l >> 4));
+    f32x4 y = *reinterpret_cast<const f32x4*>(b + (brow0 + (l & 15)) * ldb + k0 + 4 * (l >> 4));
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.x, y.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.y, y.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.z, y.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.w, y.w, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ float wave_incl_scan(float x) {
+    const int l = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        float y = __shfl_up(x, d, kWave);
+        if (l >= d) x += y;
+    }
+    return x;
+}
+
+}  // namespace gdr

@@ -1,0 +1,43 @@
+// gdr_internal.h -- declarations shared by the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace gdr {
+
+constexpr int kAlphaNone = 0, kAlphaScalar = 1, kAlphaChannel = 2;
+constexpr int kF32 = 0, kBF16 = 1;
+
+// Channel-wise log-decay floor (see gdr.h): keeps every exponential of an
+// 8-token partial sum of log alpha inside the fp32 range.
+constexpr float kChannelLogAlphaMin = -10.0f;
+
+struct DecodeArgs {
+    int N, H, dk, dv, dtype, mode;
+    const void *q, *k, *v;
+    const float *beta, *log_alpha;
+    float* S;
+    void* o;
+    hipStream_t stream;
+};
+
+struct ChunkArgs {
+    int B, H, L, dk, dv, C, dtype, mode;
+    const void *q, *k, *v;
+    const float *beta, *log_alpha, *S0;
+    void* o;
+    float* S_final;
+    void* workspace;
+    hipStream_t stream;
+};
+
+// Chunk length the kernels actually use for a requested C.
+int effective_chunk(int C, int dtype, int dk);
+// Bytes of per-chunk workspace (WY factor + masked scores) for one chunk.
+size_t chunk_workspace_bytes_per_chunk(int C, int dtype);
+
+hipError_t launch_decode_step(const DecodeArgs& a);
+hipError_t launch_fwd_chunked(const ChunkArgs& a);
+
+}  // namespace gdr

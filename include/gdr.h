@@ -1,0 +1,160 @@
+/*
+ * gdr.h -- C ABI of the gated delta-rule memory library (libgdr.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Per head the library runs the recurrent-memory update
+ *
+ *     S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t q_t
+ *
+ * with the state S in the d_v x d_k orientation (row i = value channel i, so
+ * a read at key k returns a value-space vector).  Equivalently
+ *     Sbar = S_{t-1} Diag(alpha_t);  u = beta_t (v_t - Sbar k_t);
+ *     S_t  = Sbar + u k_t^T;         o_t = S_t q_t.
+ * Sources, by title and section:
+ *   "Linear Attention Architectures: Mechanisms, Trade-offs, and Cross-Layer
+ *   Routing", Sec. 3 (read rule Eq. (8) after the update; prediction and
+ *   residual Eqs. (9)-(10); DeltaNet, Gated DeltaNet and Kimi Delta
+ *   Attention updates; gates Eqs. (11)-(12));
+ *   "linear attention and its gated descendants" (blog), sections
+ *   "DeltaNet", "Gated DeltaNet", "Kimi Delta Attention" and "Chunkwise
+ *   Parallel Form";
+ *   "Linear Attention & DeltaNet" (wiki), "How it works" items 3-4 (the
+ *   WY/Householder chunk form).
+ *
+ * Gate modes:
+ *   GDR_ALPHA_NONE    alpha = 1 (DeltaNet)
+ *   GDR_ALPHA_SCALAR  one alpha per head and token (Gated DeltaNet)
+ *   GDR_ALPHA_CHANNEL one alpha per head, token and key channel (Kimi-style)
+ * Gates are passed as beta itself (already in (0,1), no clamping) and as
+ * log(alpha) (<= 0); the feature map is the identity (callers pass q and k
+ * already normalised) and there is no 1/sqrt(d) scale.
+ *
+ * Conventions shared by every entry point:
+ *  - All arrays are dense, contiguous, row-major in the index order given
+ *    beside each argument, and live in device memory of the current HIP
+ *    device.  The caller owns every buffer; the library allocates nothing
+ *    and keeps no global state (thread-safe per stream).
+ *  - Work is enqueued on `stream` (0 = the null stream) and is asynchronous;
+ *    results are valid after the caller synchronises with the stream.
+ *  - `dtype` selects the type of q, k, v and o: GDR_F32 (float) or GDR_BF16
+ *    (bfloat16).  beta, log_alpha and the state are always float32.
+ *  - Pointers passed to q, k, v, o, S0, S_final, S and the workspace must be
+ *    16-byte aligned; beta 4-byte aligned; log_alpha 4-byte aligned, or
+ *    16-byte aligned in GDR_ALPHA_CHANNEL mode.
+ *  - Return value: GDR_OK or an error status.  Arguments are validated
+ *    before anything is enqueued; on an error status nothing has been
+ *    written.  GDR_ERR_HIP reports a failed launch (hipGetLastError).
+ *    Faults inside a kernel surface at the caller's next synchronisation.
+ *    NaN or Inf inputs are not checked and propagate.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDR_ABI_VERSION 1
+
+enum gdr_status {
+    GDR_OK = 0,
+    GDR_ERR_INVALID_ARG = 1,          /* NULL required pointer, negative size,
+                                         misaligned pointer, mode/pointer mismatch,
+                                         o aliasing an input */
+    GDR_ERR_UNSUPPORTED = 2,          /* d_k, d_v, C or dtype outside the domain */
+    GDR_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below the queried size */
+    GDR_ERR_HIP = 4                   /* a HIP launch failed */
+};
+
+enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 };
+
+enum gdr_alpha_mode { GDR_ALPHA_NONE = 0, GDR_ALPHA_SCALAR = 1, GDR_ALPHA_CHANNEL = 2 };
+
+/* Version of this ABI (GDR_ABI_VERSION). */
+int gdr_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *gdr_status_string(int status);
+
+/*
+ * Bytes of device workspace gdr_fwd_chunked needs for these sizes (0 when
+ * the call would do no chunk work).  Returns (size_t)-1 when the sizes are
+ * invalid or unsupported.  The workspace holds, per chunk, the chunk's
+ * triangular WY factor and its masked score block; it is scratch only and
+ * its contents are not part of the result.
+ */
+size_t gdr_fwd_chunked_workspace_size(int B, int H, int L, int d_k, int d_v, int C,
+                                      int dtype, int alpha_mode);
+
+/*
+ * Chunkwise forward (training / prefill form): runs the recurrence over L
+ * tokens for every (batch b, head h) and writes every output and,
+ * optionally, the final state.
+ * ("linear attention and its gated descendants", "Chunkwise Parallel Form":
+ * the sequence is cut into chunks of C tokens; the state is carried across
+ * chunk boundaries and each chunk's outputs are dense block products.  The
+ * product of a chunk's (I - beta k k^T) factors is kept in the compact
+ * WY/Householder form named in "Linear Attention & DeltaNet", item 3.)
+ *
+ *   B, H       batch and heads (>= 0; 0 => nothing to do)
+ *   L          tokens per sequence (>= 0).  L == 0 only copies S0 (or zeros)
+ *              to S_final.  L need not be a multiple of C.
+ *   d_k, d_v   key and value head dims, each 64 or 128
+ *   C          chunk length: 16, 32 or 64.  The result does not depend on C
+ *              beyond rounding.
+ *   dtype      GDR_F32 or GDR_BF16 (type of q, k, v, o)
+ *   q, k       [B][H][L][d_k]
+ *   v          [B][H][L][d_v]
+ *   beta       [B][H][L] float, the write strength in (0,1)
+ *   alpha_mode GDR_ALPHA_NONE:    log_alpha must be NULL
+ *              GDR_ALPHA_SCALAR:  log_alpha [B][H][L] float
+ *              GDR_ALPHA_CHANNEL: log_alpha [B][H][L][d_k] float.  In this
+ *              mode every log_alpha value must be >= -10 (alpha >= 4.5e-5
+ *              per token and channel); smaller values are treated as -10 so
+ *              that every intermediate exponential stays finite.
+ *   S0         NULL => zero initial state, else [B][H][d_v][d_k] float
+ *   o          [B][H][L][d_v] (dtype); must not overlap any input
+ *   S_final    NULL => not written, else [B][H][d_v][d_k] float; may be the
+ *              same pointer as S0 (updated in place) but must not partially
+ *              overlap it
+ *   workspace  device scratch of at least
+ *              gdr_fwd_chunked_workspace_size(...) bytes (may be NULL when
+ *              that size is 0); must not overlap any other argument
+ *   stream     HIP stream to enqueue on
+ */
+int gdr_fwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                    const void *q, const void *k, const void *v,
+                    const float *beta, int alpha_mode, const float *log_alpha,
+                    const float *S0, void *o, float *S_final,
+                    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One recurrent decode step for N sequences x H heads (the constant-memory
+ * inference form: "linear attention and its gated descendants", "Recurrent
+ * Linear Attention for Inference": O(d^2) work and memory per token).  The
+ * state is read and written once; o_t is read after the write.
+ *
+ *   N, H       sequences and heads (>= 0; 0 => nothing to do)
+ *   d_k, d_v   64 or 128
+ *   dtype      GDR_F32 or GDR_BF16 (type of q, k, v, o)
+ *   q, k       [N][H][d_k];  v [N][H][d_v]
+ *   beta       [N][H] float
+ *   alpha_mode as for gdr_fwd_chunked; log_alpha NULL | [N][H] | [N][H][d_k]
+ *              (no lower bound is needed in this entry point)
+ *   S          [N][H][d_v][d_k] float, updated in place
+ *   o          [N][H][d_v] (dtype); must not overlap any input or S
+ */
+int gdr_decode_step(int N, int H, int d_k, int d_v, int dtype,
+                    const void *q, const void *k, const void *v,
+                    const float *beta, int alpha_mode, const float *log_alpha,
+                    float *S, void *o, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

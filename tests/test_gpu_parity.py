@@ -1,0 +1,269 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every case draws seeded inputs from ``gdr_inputs``, runs the library on the
+GPU and the oracle on the same rounded values, and compares element by
+element at the stated tolerance (1e-4 for fp32 inputs, 2e-2 for bf16).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_88_amd as gdr
+import gdr_inputs as gi
+import oracle
+from gpu_common import TOL, oracle_chunked, pick, rel_err, run_chunked, to_dev
+
+pytestmark = pytest.mark.gpu
+
+MODES = [gi.ALPHA_NONE, gi.ALPHA_SCALAR, gi.ALPHA_CHANNEL]
+DTYPES = [torch.float32, torch.bfloat16]
+DIMS = [(64, 64), (128, 128), (64, 128), (128, 64)]
+
+
+def _id(mode, dt, dims, extra=""):
+    return f"{gi.MODE_NAMES[mode]}-{str(dt)[6:]}-dk{dims[0]}dv{dims[1]}{extra}"
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("mode", MODES, ids=lambda m: gi.MODE_NAMES[m])
+@pytest.mark.parametrize("dt", DTYPES, ids=lambda d: str(d)[6:])
+@pytest.mark.parametrize("dims", DIMS, ids=lambda d: f"dk{d[0]}dv{d[1]}")
+def test_decode_step_parity(mode, dt, dims):
+    dk, dv = dims
+    y = gi.decode_inputs(3, 5, dk, dv, 1, dt, mode, seed=1000 + 7 * mode + dk + dv)
+    S = y["S0"].cuda().clone()
+    d = {k: (None if v is None else v[0].cuda()) for k, v in y.items() if k != "S0"}
+    o = gdr.gdr_decode_step(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], S)
+    torch.cuda.synchronize()
+    un = lambda t: None if t is None else t[0][:, :, None]
+    ro, rS = oracle.run(un(y["q"]), un(y["k"]), un(y["v"]), un(y["beta"]), un(y["log_alpha"]),
+                        y["S0"])
+    assert rel_err(o.float().cpu().numpy(), ro[:, :, 0]) <= TOL[dt]
+    assert rel_err(S.cpu().numpy(), rS) <= TOL[dt]
+
+
+@pytest.mark.parametrize("mode", MODES, ids=lambda m: gi.MODE_NAMES[m])
+def test_decode_consecutive_steps(mode):
+    """16 decode steps in a row equal the oracle over 16 tokens."""
+    steps = 16
+    y = gi.decode_inputs(2, 3, 128, 128, steps, torch.bfloat16, mode, seed=1100 + mode)
+    S = y["S0"].cuda().clone()
+    outs = []
+    for t in range(steps):
+        d = {k: (None if v is None else v[t].cuda()) for k, v in y.items() if k != "S0"}
+        outs.append(gdr.gdr_decode_step(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], S))
+    torch.cuda.synchronize()
+    o = torch.stack(outs, dim=2).float().cpu().numpy()        # [N, H, steps, dv]
+    mv = lambda t: None if t is None else t.movedim(0, 2)
+    ro, rS = oracle.run(mv(y["q"]), mv(y["k"]), mv(y["v"]), mv(y["beta"]), mv(y["log_alpha"]),
+                        y["S0"])
+    assert rel_err(o, ro) <= 2e-2
+    assert rel_err(S.cpu().numpy(), rS) <= 2e-2
+
+
+# ------------------------------------------------------------------ chunked
+CHUNK_CASES = [(m, dt, dims, C) for m in MODES for dt in DTYPES for dims in DIMS
+               for C in (16, 32, 64)]
+
+
+@pytest.mark.parametrize("mode,dt,dims,C", CHUNK_CASES,
+                         ids=[_id(m, dt, dims, f"-C{C}") for m, dt, dims, C in CHUNK_CASES])
+def test_chunked_parity(mode, dt, dims, C):
+    """Several chunks plus a ragged tail, with an initial state."""
+    dk, dv = dims
+    x = gi.chunked_inputs(2, 2, 200, dk, dv, dt, mode, seed=2000 + 13 * mode + C + dk // 8 + dv,
+                          s0_std=0.1)
+    o, S = run_chunked(x, C)
+    ro, rS = oracle_chunked(x)
+    assert rel_err(o, ro) <= TOL[dt]
+    assert rel_err(S, rS) <= TOL[dt]
+
+
+@pytest.mark.parametrize("L", [1, 15, 16, 63, 64, 65, 129])
+@pytest.mark.parametrize("mode", MODES, ids=lambda m: gi.MODE_NAMES[m])
+def test_chunked_lengths_zero_state(L, mode):
+    """Short and boundary lengths from a zero state (S0 = NULL)."""
+    x = gi.chunked_inputs(1, 3, L, 128, 128, torch.bfloat16, mode, seed=2500 + L + mode)
+    o, S = run_chunked(x, 64)
+    ro, rS = oracle_chunked(x)
+    assert rel_err(o, ro) <= 2e-2
+    assert rel_err(S, rS) <= 2e-2
+
+
+def test_chunked_empty_sequence_copies_state():
+    x = gi.chunked_inputs(2, 3, 0, 64, 128, torch.bfloat16, gi.ALPHA_SCALAR, seed=2600,
+                          s0_std=0.5)
+    d = to_dev(x)
+    o, S = gdr.gdr_fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(S.cpu(), x["S0"]) and o.numel() == 0
+    o, S = gdr.gdr_fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], None)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S).item() == 0
+
+
+@pytest.mark.parametrize("mode", MODES, ids=lambda m: gi.MODE_NAMES[m])
+def test_chunk_size_invariance(mode):
+    """C = 1 is the recurrent form and C = L the parallel form (blog,
+    "Chunkwise Parallel Form"): the result must not depend on C."""
+    x = gi.chunked_inputs(1, 2, 192, 128, 128, torch.float32, mode, seed=2700 + mode, s0_std=0.1)
+    res = [run_chunked(x, C) for C in (16, 32, 64)]
+    for o, S in res[1:]:
+        assert rel_err(o, res[0][0]) <= 1e-4
+        assert rel_err(S, res[0][1]) <= 1e-4
+
+
+@pytest.mark.parametrize("mode", MODES, ids=lambda m: gi.MODE_NAMES[m])
+@pytest.mark.parametrize("dt", DTYPES, ids=lambda d: str(d)[6:])
+def test_chunked_equals_decode_steps(mode, dt):
+    """The chunked forward over L tokens equals L decode steps."""
+    L = 40
+    x = gi.chunked_inputs(2, 2, L, 64, 64, dt, mode, seed=2800 + mode, s0_std=0.1)
+    o, S = run_chunked(x, 16)
+    d = to_dev(x)
+    Sd = d["S0"].clone()
+    outs = []
+    for t in range(L):
+        la = None if d["log_alpha"] is None else d["log_alpha"][:, :, t].contiguous()
+        outs.append(gdr.gdr_decode_step(d["q"][:, :, t].contiguous(), d["k"][:, :, t].contiguous(),
+                                        d["v"][:, :, t].contiguous(),
+                                        d["beta"][:, :, t].contiguous(), la, Sd))
+    torch.cuda.synchronize()
+    od = torch.stack(outs, dim=2).float().cpu().numpy()
+    assert rel_err(o, od) <= TOL[dt]
+    assert rel_err(S, Sd.cpu().numpy()) <= TOL[dt]
+
+
+@pytest.mark.parametrize("mode", MODES, ids=lambda m: gi.MODE_NAMES[m])
+def test_split_call_resume(mode):
+    """fwd(L1) then fwd(L2) from its final state == fwd(L1 + L2)."""
+    x = gi.chunked_inputs(2, 2, 300, 128, 128, torch.bfloat16, mode, seed=2900 + mode, s0_std=0.1)
+    o, S = run_chunked(x, 64)
+    cut = 100  # not a chunk multiple
+    a = {k: (None if v is None or k == "S0" else v[:, :, :cut].contiguous()) for k, v in x.items()}
+    a["S0"] = x["S0"]
+    o1, S1 = run_chunked(a, 64)
+    b = {k: (None if v is None or k == "S0" else v[:, :, cut:].contiguous()) for k, v in x.items()}
+    b["S0"] = torch.from_numpy(S1)
+    o2, S2 = run_chunked(b, 64)
+    ro, rS = oracle_chunked(x)
+    assert rel_err(np.concatenate([o1, o2], axis=2), ro) <= 2e-2
+    assert rel_err(S2, rS) <= 2e-2
+    assert rel_err(np.concatenate([o1, o2], axis=2), o) <= 2e-2
+
+
+def test_state_updated_in_place():
+    x = gi.chunked_inputs(2, 4, 130, 128, 64, torch.bfloat16, gi.ALPHA_SCALAR, seed=3000,
+                          s0_std=0.1)
+    d = to_dev(x)
+    S = d["S0"]
+    o, S_out = gdr.gdr_fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], S,
+                                   S_final=S)
+    torch.cuda.synchronize()
+    assert S_out.data_ptr() == S.data_ptr()
+    ro, rS = oracle_chunked(x)
+    assert rel_err(S.cpu().numpy(), rS) <= 2e-2
+    assert rel_err(o.float().cpu().numpy(), ro) <= 2e-2
+
+
+@pytest.mark.parametrize("mode", MODES, ids=lambda m: gi.MODE_NAMES[m])
+def test_deterministic(mode):
+    """No atomics: two runs give bitwise identical results."""
+    x = gi.chunked_inputs(2, 4, 333, 128, 128, torch.bfloat16, mode, seed=3100 + mode, s0_std=0.1)
+    a = run_chunked(x, 64)
+    b = run_chunked(x, 64)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_exact_recall_on_gpu():
+    """alpha = beta = 1 with orthonormal keys: reading at k_i returns v_i
+    ("DeltaNet" section of the blog post), in fp32 on the GPU."""
+    rng = np.random.default_rng(5)
+    dk = dv = 64
+    n = 48
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    keys = Qm.T[:n]
+    vals = rng.standard_normal((n, dv))
+    L = 2 * n
+    k = np.vstack([keys, keys])
+    q = np.vstack([keys, keys])
+    v = np.vstack([vals, rng.standard_normal((n, dv))])
+    beta = np.concatenate([np.ones(n), np.zeros(n)])
+    t = lambda a: torch.tensor(np.ascontiguousarray(a[None, None]), dtype=torch.float32).contiguous()
+    x = dict(q=t(q), k=t(k), v=t(v), beta=t(beta), log_alpha=None, S0=None)
+    o, S = run_chunked(x, 32)
+    assert np.abs(o[0, 0, n:] - vals).max() <= 1e-4
+    assert np.abs(S[0, 0] @ keys.T - vals.T).max() <= 1e-4
+
+
+def test_channel_gates_at_the_floor():
+    """Channel-wise log alpha down to -10 per token: every intermediate
+    exponential stays finite and the result matches the oracle."""
+    x = gi.chunked_inputs(1, 2, 160, 128, 128, torch.bfloat16, gi.ALPHA_CHANNEL, seed=3200,
+                          s0_std=0.1)
+    la = x["log_alpha"]
+    g = torch.Generator().manual_seed(3201)
+    x["log_alpha"] = torch.where(torch.rand(la.shape, generator=g) < 0.5,
+                                 torch.full_like(la, -10.0), la * 0.01)
+    o, S = run_chunked(x, 64)
+    assert np.isfinite(o).all() and np.isfinite(S).all()
+    ro, rS = oracle_chunked(x)
+    assert rel_err(o, ro) <= 2e-2
+    assert rel_err(S, rS) <= 2e-2
+
+
+# ------------------------------------------------------------------ full sizes
+def _full_size(w, heads):
+    x = gi.workload_inputs(w)
+    o, S = run_chunked(x, w.C)
+    ro, rS = oracle_chunked(x, heads)
+    tol = TOL[w.dtype]
+    assert rel_err(pick(o, heads), ro[None]) <= tol
+    assert rel_err(pick(S, heads), rS[None]) <= tol
+    assert np.isfinite(o).all() and np.isfinite(S).all()
+
+
+def test_full_deltanet_fp32():
+    w = gi.DELTANET_FP32
+    x = gi.workload_inputs(w)
+    o, S = run_chunked(x, w.C)
+    ro, rS = oracle_chunked(x)
+    assert rel_err(o, ro) <= 1e-4 and rel_err(S, rS) <= 1e-4
+
+
+def test_full_gdn_bf16():
+    _full_size(gi.GDN_BF16, [(0, 0), (3, 5), (7, 7)])
+
+
+def test_full_kda_bf16():
+    _full_size(gi.KDA_BF16, [(0, 0), (3, 15)])
+
+
+@pytest.mark.parametrize("w", gi.GDN_SWEEP, ids=lambda w: w.name)
+def test_full_gdn_sweep(w):
+    _full_size(w, [(w.B - 1, w.H - 1)])
+
+
+def test_full_decode_sampled():
+    """The decode workload at full size (256 x 16 heads), 64 consecutive
+    steps, sampled heads against the oracle."""
+    w = gi.DECODE_BF16
+    steps = 64
+    y = gi.decode_workload_inputs(w, steps=steps)
+    S = y["S0"].cuda().clone()
+    dev = {k: (None if v is None else v.cuda()) for k, v in y.items() if k != "S0"}
+    outs = []
+    for t in range(steps):
+        la = None if dev["log_alpha"] is None else dev["log_alpha"][t]
+        outs.append(gdr.gdr_decode_step(dev["q"][t], dev["k"][t], dev["v"][t], dev["beta"][t], la, S))
+    torch.cuda.synchronize()
+    heads = [(0, 0), (100, 7), (255, 15)]
+    o = torch.stack(outs, dim=2).float().cpu().numpy()
+    mv = lambda t: None if t is None else t.movedim(0, 2)
+    sel = lambda t: None if t is None else torch.stack([t[b, h] for b, h in heads])[None]
+    ro, rS = oracle.run(sel(mv(y["q"])), sel(mv(y["k"])), sel(mv(y["v"])), sel(mv(y["beta"])),
+                        sel(mv(y["log_alpha"])), sel(y["S0"]))
+    assert rel_err(pick(o, heads), ro) <= 2e-2
+    assert rel_err(pick(S.cpu().numpy(), heads), rS) <= 2e-2
