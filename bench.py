@@ -1,0 +1,247 @@
+"""Benchmark of the gated delta-rule memory on one MI355X.
+
+Default workload (the headline): Gated DeltaNet chunked forward, bf16
+inputs, fp32 state, B=8, H=8, L=2048, d_k=d_v=128, C=64.  One step is one
+gdr_fwd_chunked call over one batch (all of its kernels).  A second leg
+times the single-token decode step on 256 sequences x 16 heads (d=128,
+fp32 state of 512 MiB), 1024 consecutive steps, and reports its HBM rate.
+
+Inputs are resident in HBM before timing starts.  The chunked leg rotates
+over several input copies so its ~140 MB working set is not served from the
+256 MB Infinity Cache.  Kernel durations come from HIP events on the stream
+the library launches on.  The CPU baseline runs the fp64 oracle on a
+bounded sample of the same workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import gdr_inputs as gi  # noqa: E402
+
+METRIC = "tokens/s chunked GDN fwd (L=2048,H=8,d=128) + % MFMA peak; decode HBM GB/s"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 matrix
+
+WORKLOADS = {w.name: w for w in (gi.DELTANET_FP32, gi.GDN_BF16, gi.KDA_BF16, *gi.GDN_SWEEP)}
+
+
+def chunked_algorithmic(w: gi.ChunkedWorkload) -> tuple[float, float]:
+    """(bytes, flops) the method itself must move and compute for one call.
+
+    Bytes per head-token: q, k, v read and o written in the input dtype,
+    beta and log alpha read (4 B each, or 4 d_k B for channel gates).  Bytes
+    per (b, h): the final state written (4 d_k d_v).  Flops per head-token
+    on the triangular count with C = chunk: 5 C d + 3 d + 6 d^2 + C^2 / 3
+    (d = d_k = d_v; 1 FMA = 2 flops)."""
+    es = 2 if w.dtype == torch.bfloat16 else 4
+    ht = w.B * w.H * w.L
+    gate = 0 if w.mode == gi.ALPHA_NONE else (4 if w.mode == gi.ALPHA_SCALAR else 4 * w.dk)
+    per_tok = es * (2 * w.dk + 2 * w.dv) + 4 + gate
+    state = 4 * w.dk * w.dv * (w.B * w.H) * (2 if w.s0_std > 0 else 1)
+    d, C = w.dk, w.C
+    flops = ht * (5 * C * d + 3 * d + 6 * d * d + C * C / 3)
+    return float(ht * per_tok + state), float(flops)
+
+
+def decode_algorithmic(w: gi.DecodeWorkload) -> float:
+    """Bytes per decode step: state read + written (fp32), q, k, v read and
+    o written (dtype), beta and log alpha read."""
+    es = 2 if w.dtype == torch.bfloat16 else 4
+    nh = w.N * w.H
+    gate = 0 if w.mode == gi.ALPHA_NONE else (4 if w.mode == gi.ALPHA_SCALAR else 4 * w.dk)
+    return float(nh * (2 * 4 * w.dk * w.dv + es * (2 * w.dk + 2 * w.dv) + 4 + gate))
+
+
+def _events(n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def bench_chunked(w, steps, warmup, copies):
+    import gated_delta_rule_88_amd as gdr
+
+    dev = torch.device("cuda:0")
+    sets = []
+    for c in range(copies):
+        x = gi.chunked_inputs(w.B, w.H, w.L, w.dk, w.dv, w.dtype, w.mode, w.seed + 1000 * c,
+                              w.s0_std)
+        sets.append({k: (None if t is None else t.to(dev)) for k, t in x.items()})
+    mode = w.mode
+    code = gdr.GDR_BF16 if w.dtype == torch.bfloat16 else gdr.GDR_F32
+    need = gdr.gdr_fwd_chunked_workspace_size(w.B, w.H, w.L, w.dk, w.dv, w.C, code, mode)
+    outs = [torch.empty((w.B, w.H, w.L, w.dv), dtype=w.dtype, device=dev) for _ in range(copies)]
+    finals = [torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
+              for _ in range(copies)]
+    wss = [torch.empty(max(need, 1), dtype=torch.uint8, device=dev) for _ in range(copies)]
+
+    def call(i):
+        d = sets[i % copies]
+        gdr.gdr_fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["S0"], w.C,
+                            o=outs[i % copies], S_final=finals[i % copies],
+                            workspace=wss[i % copies])
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    # whole-job timing: K steps bracketed by synchronisations
+    t0 = time.perf_counter()
+    e0, e1 = _events(2)
+    e0.record()
+    for i in range(steps):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = e0.elapsed_time(e1)
+    # per-call durations (HIP events around each call on the library's stream)
+    n_each = min(steps, 50)
+    ev = _events(2 * n_each)
+    for i in range(n_each):
+        ev[2 * i].record()
+        call(i)
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    per_call = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n_each))
+    return dict(total_ms=total_ms, wall_s=wall, call_ms_mean=sum(per_call) / n_each,
+                call_ms_median=per_call[n_each // 2])
+
+
+def bench_decode(w, steps):
+    import gated_delta_rule_88_amd as gdr
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    N, H, dk, dv = w.N, w.H, w.dk, w.dv
+
+    def unit(x):
+        return x / torch.clamp(x.norm(dim=-1, keepdim=True), min=1e-6)
+
+    q = unit(torch.randn(steps, N, H, dk, generator=g, device=dev)).to(w.dtype)
+    k = unit(torch.randn(steps, N, H, dk, generator=g, device=dev)).to(w.dtype)
+    v = torch.randn(steps, N, H, dv, generator=g, device=dev).to(w.dtype)
+    beta = torch.sigmoid(torch.randn(steps, N, H, generator=g, device=dev))
+    la = -torch.nn.functional.softplus(torch.randn(steps, N, H, generator=g, device=dev) + 2.0)
+    S = torch.randn(N, H, dv, dk, generator=g, device=dev) * w.s0_std
+    o = torch.empty(steps, N, H, dv, dtype=w.dtype, device=dev)
+    for t in range(8):  # warm-up on a scratch copy of the state
+        gdr.gdr_decode_step(q[t], k[t], v[t], beta[t], la[t], S.clone(), o[t])
+    torch.cuda.synchronize()
+    e0, e1 = _events(2)
+    e0.record()
+    for t in range(steps):
+        gdr.gdr_decode_step(q[t], k[t], v[t], beta[t], la[t], S, o[t])
+    e1.record()
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    ok = bool(torch.isfinite(S).all().item())
+    return dict(total_ms=total_ms, step_ms=total_ms / steps, finite=ok)
+
+
+def cpu_baseline(w, chains: int):
+    """fp64 oracle on the first `chains` (b, h) chains of the workload, on all
+    host threads; scaled to the whole workload's tokens/s."""
+    import oracle
+
+    x = gi.workload_inputs(w)
+    bh = w.B * w.H
+    chains = min(chains, bh)
+    flat = lambda t: None if t is None else t.reshape((bh,) + tuple(t.shape[2:]))[:chains]
+    args = [flat(x[k]) for k in ("q", "k", "v", "beta", "log_alpha", "S0")]
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.run(*args, mode=w.mode, nthreads=threads)
+    dt = time.perf_counter() - t0
+    full_s = dt * bh / chains
+    return dict(value=w.tokens / full_s, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{chains} of {bh} (batch, head) chains at full L={w.L}, "
+                       f"{dt:.2f} s wall on {threads} threads, scaled by {bh}/{chains}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=gi.GDN_BF16.name, choices=sorted(WORKLOADS))
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-chains", type=int, default=32)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the per-(batch, head) chains are independent, so "
+              "several GPUs would each run this same kernel on their own share; run with "
+              "--gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    w = WORKLOADS[args.workload]
+    r = bench_chunked(w, args.steps, args.warmup, args.copies)
+    nbytes, flops = chunked_algorithmic(w)
+    call_s = r["call_ms_mean"] / 1e3
+    gbs = nbytes / call_s / 1e9
+    tflops = flops / call_s / 1e12
+    mfma_peak = BF16_PEAK_TFLOPS if w.dtype == torch.bfloat16 else FP32_PEAK_TFLOPS
+    ms_step = r["total_ms"] / args.steps
+    out = {
+        "metric": METRIC,
+        "value": w.tokens / (ms_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d_k": w.dk, "d_v": w.dv,
+                   "C": w.C, "alpha": gi.MODE_NAMES[w.mode], "input_copies": args.copies},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "gdr_fwd_chunked (chunk_prep_kernel + chunk_scan_kernel)",
+                     "algorithmic_bytes_per_call": nbytes,
+                     "call_ms_mean": r["call_ms_mean"], "call_ms_median": r["call_ms_median"]},
+        "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s",
+                 "frac": tflops / mfma_peak, "algorithmic_flops_per_call": flops,
+                 "count": "triangular"},
+    }
+    if not args.no_decode:
+        dw = gi.DECODE_BF16
+        dr = bench_decode(dw, args.decode_steps)
+        db = decode_algorithmic(dw)
+        dgbs = db / (dr["step_ms"] / 1e3) / 1e9
+        out["decode"] = {
+            "workload": dw.name, "steps": args.decode_steps, "ms_per_step": dr["step_ms"],
+            "tokens_per_s": dw.N / (dr["step_ms"] / 1e3),
+            "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dgbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "decode_step_kernel", "algorithmic_bytes_per_step": db},
+            "state_finite": dr["finite"],
+        }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_chains)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -45,28 +45,6 @@ __host__ __device__ constexpr int align_up(int x, int a) { return (x + a - 1) / 
 // 32-wide k-steps that cover k in [0, 16*(tt+1)) (lower-triangular operands).
 __device__ __forceinline__ constexpr int ksteps_tri(int tt) { return (16 * (tt + 1) + 31) / 32; }
 
-// Transpose a VE x VE block held as VE 16-byte row vectors (row r = token,
-// element j = channel) into VE column vectors (column j, element r).
-__device__ __forceinline__ void transpose_block(const u32x4* in, u32x4* out, bf16*) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int d = j >> 1;
-        const int sh = (j & 1) * 16;
-        uint32_t w[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t a = (in[2 * p][d] >> sh) & 0xffffu;
-            const uint32_t b = (in[2 * p + 1][d] >> sh) & 0xffffu;
-            w[p] = a | (b << 16);
-        }
-        out[j] = u32x4{w[0], w[1], w[2], w[3]};
-    }
-}
-__device__ __forceinline__ void transpose_block(const u32x4* in, u32x4* out, float*) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = u32x4{in[0][j], in[1][j], in[2][j], in[3][j]};
-}
-
 // Multiply the VE elements of a 16-byte vector by f[0..VE).
 template <typename E>
 __device__ __forceinline__ u32x4 scale_vec(u32x4 v, const float* f) {
@@ -842,6 +820,7 @@ static hipError_t by_chunk(const ChunkArgs& a)
 
 hipError_t launch_fwd_chunked(const ChunkArgs& a)
 {
+    if (a.mode != kAlphaChannel && a.L > 0 && (size_t)a.B * a.H > 0) return launch_pipe_chunked(a);
     const size_t BH = (size_t)a.B * a.H;
     if (BH == 0) return hipSuccess;
     if (a.L == 0) {

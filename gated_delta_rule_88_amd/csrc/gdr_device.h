@@ -58,9 +58,11 @@ template <> struct Pack<float> {
 };
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Round two floats to bf16 (nearest even) and pack them: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
-    bf16 x = (bf16)a, y = (bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 template <> struct Pack<bf16> {
     static constexpr int n = 8;
@@ -150,6 +152,102 @@ __device__ __forceinline__ void mma_k16(f32x4& acc, const float* a, int lda, int
 }
 
 __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
+
+// ------------------------------------------------------ tile-pair operands
+// Second operand convention, used where MFMA results feed the next product
+// directly from registers.  A 32-wide k-step is two 16-wide k-tiles p = 0, 1;
+// element j = 4p + e of lane group g = l/16 holds k = k0 + 16p + 4g + e.  A
+// 16x16 fp32 accumulator tile holds rows 4g + e of column l%16, so two such
+// tiles (k-tiles p = 0, 1 along their row index) are already an operand for
+// a product that contracts over that row index: no LDS round trip.
+__device__ __forceinline__ Frag<bf16> ldfrag_pair(const bf16* base, int ld, int row0, int k0) {
+    const int l = lane_id();
+    const bf16* p = base + (row0 + (l & 15)) * ld + k0 + 4 * (l >> 4);
+    const u32x2 lo = ld8(p), hi = ld8(p + 16);
+    Frag<bf16> f;
+    f.v = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+    return f;
+}
+__device__ __forceinline__ Frag<float> ldfrag_pair(const float* base, int ld, int row0, int k0) {
+    const int l = lane_id();
+    const float* p = base + (row0 + (l & 15)) * ld + k0 + 4 * (l >> 4);
+    Frag<float> f;
+    f.lo = *reinterpret_cast<const f32x4*>(p);
+    f.hi = *reinterpret_cast<const f32x4*>(p + 16);
+    return f;
+}
+__device__ __forceinline__ void frag_of_tiles(Frag<bf16>& f, f32x4 t0, f32x4 t1) {
+    f.v = __builtin_bit_cast(bf16x8, u32x4{pack_bf2(t0[0], t0[1]), pack_bf2(t0[2], t0[3]),
+                                           pack_bf2(t1[0], t1[1]), pack_bf2(t1[2], t1[3])});
+}
+__device__ __forceinline__ void frag_of_tiles(Frag<float>& f, f32x4 t0, f32x4 t1) {
+    f.lo = t0;
+    f.hi = t1;
+}
+
+// 16-wide k-step: element e of lane group g holds k = k0 + 4g + e.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <typename T> struct Frag16;
+template <> struct Frag16<bf16> { s16x4 v; };
+template <> struct Frag16<float> { f32x4 v; };
+__device__ __forceinline__ Frag16<bf16> ldfrag16(const bf16* base, int ld, int row0, int k0) {
+    const int l = lane_id();
+    Frag16<bf16> f;
+    f.v = __builtin_bit_cast(s16x4, ld8(base + (row0 + (l & 15)) * ld + k0 + 4 * (l >> 4)));
+    return f;
+}
+__device__ __forceinline__ Frag16<float> ldfrag16(const float* base, int ld, int row0, int k0) {
+    const int l = lane_id();
+    Frag16<float> f;
+    f.v = *reinterpret_cast<const f32x4*>(base + (row0 + (l & 15)) * ld + k0 + 4 * (l >> 4));
+    return f;
+}
+__device__ __forceinline__ void frag16_of_tile(Frag16<bf16>& f, f32x4 t) {
+    f.v = __builtin_bit_cast(s16x4, u32x2{pack_bf2(t[0], t[1]), pack_bf2(t[2], t[3])});
+}
+__device__ __forceinline__ void frag16_of_tile(Frag16<float>& f, f32x4 t) { f.v = t; }
+__device__ __forceinline__ void mma16(f32x4& acc, const Frag16<bf16>& a, const Frag16<bf16>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x4& acc, const Frag16<float>& a, const Frag16<float>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v.x, b.v.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v.y, b.v.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v.z, b.v.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v.w, b.v.w, acc, 0, 0, 0);
+}
+
+// Transpose a VE x VE block held as VE 16-byte row vectors (row r = token,
+// element j = channel) into VE column vectors (column j, element r).
+__device__ __forceinline__ void transpose_block(const u32x4* in, u32x4* out, bf16*) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int d = j >> 1;
+        const int sh = (j & 1) * 16;
+        uint32_t w[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t a = (in[2 * p][d] >> sh) & 0xffffu;
+            const uint32_t b = (in[2 * p + 1][d] >> sh) & 0xffffu;
+            w[p] = a | (b << 16);
+        }
+        out[j] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+__device__ __forceinline__ void transpose_block(const u32x4* in, u32x4* out, float*) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = u32x4{in[0][j], in[1][j], in[2][j], in[3][j]};
+}
+
+// Four consecutive elements as fp32 (one 8-byte or 16-byte read).
+__device__ __forceinline__ f32x4 load4f(const bf16* p) {
+    const u32x2 v = ld8(p);
+    return f32x4{bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y)};
+}
+__device__ __forceinline__ f32x4 load4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// Make this wave's earlier LDS accesses complete before its later ones (and
+// keep the compiler from moving memory operations across this point).
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ __forceinline__ float wave_incl_scan(float x) {

@@ -39,5 +39,9 @@ size_t chunk_workspace_bytes_per_chunk(int C, int dtype);
 
 hipError_t launch_decode_step(const DecodeArgs& a);
 hipError_t launch_fwd_chunked(const ChunkArgs& a);
+// Fused pipelined forward (alpha modes none and scalar); no workspace.
+hipError_t launch_pipe_chunked(const ChunkArgs& a);
+// Token chunk the pipelined kernel uses for a requested C.
+int pipe_chunk(int C, int dtype, int dk);
 
 }  // namespace gdr
