@@ -36,6 +36,38 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 matrix
 
+# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, scaled by
+# the same counters read for a 1 GiB device copy (FETCH_SIZE x 2, WRITE_SIZE x 1
+# on this chip), with a digest of the kernel sources they were taken on: a
+# figure whose sources have changed since is reported as null.
+MEASURED_TRAFFIC = {
+    ("gdn_bf16_B8_H8_L2048_d128", "chunk_pipe_kernel"):
+        dict(sources=("gdr_scan.hip", "gdr_device.h", "gdr_internal.h"),
+             digest="95295b85d27bcc2f", read=101.93e6, written=37.75e6),
+    ("gdn_decode_bf16_N256_H16_d128", "decode_step_kernel"):
+        dict(sources=("gdr_decode.hip", "gdr_device.h", "gdr_internal.h"),
+             digest="69415f1db6ca2722", read=279.52e6, written=269.61e6),
+}
+
+
+def source_digest(files) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "gated_delta_rule_88_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch measured with counters, or None if not measured on
+    the current kernel sources."""
+    m = MEASURED_TRAFFIC.get((workload, kernel))
+    if m is None or source_digest(m["sources"]) != m["digest"]:
+        return None
+    return m["read"] + m["written"]
+
+
 WORKLOADS = {w.name: w for w in (gi.DELTANET_FP32, gi.GDN_BF16, gi.KDA_BF16, *gi.GDN_SWEEP)}
 
 
@@ -64,6 +96,29 @@ def decode_algorithmic(w: gi.DecodeWorkload) -> float:
     nh = w.N * w.H
     gate = 0 if w.mode == gi.ALPHA_NONE else (4 if w.mode == gi.ALPHA_SCALAR else 4 * w.dk)
     return float(nh * (2 * 4 * w.dk * w.dv + es * (2 * w.dk + 2 * w.dv) + 4 + gate))
+
+
+def chunked_kernel_name(w) -> str:
+    """The kernels one gdr_fwd_chunked call launches for this workload."""
+    if w.mode == gi.ALPHA_CHANNEL:
+        return "chunk_prep_kernel + chunk_scan_kernel"
+    return "chunk_pipe_kernel"
+
+
+def copy_probe(mib: int, reps: int = 5):
+    """Plain device copies of a known size, for scaling the HBM byte counters
+    (FETCH_SIZE, WRITE_SIZE) a profiler reads for the kernels above."""
+    dev = torch.device("cuda:0")
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "reps": reps,
+                      "kernels": ["copy_", "neg"]}))
 
 
 def _events(n):
@@ -181,6 +236,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-chains", type=int, default=32)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run plain copies of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -193,6 +250,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
     w = WORKLOADS[args.workload]
     r = bench_chunked(w, args.steps, args.warmup, args.copies)
     nbytes, flops = chunked_algorithmic(w)
@@ -217,8 +277,9 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d_k": w.dk, "d_v": w.dv,
                    "C": w.C, "alpha": gi.MODE_NAMES[w.mode], "input_copies": args.copies},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "gdr_fwd_chunked (chunk_prep_kernel + chunk_scan_kernel)",
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(w.name, chunked_kernel_name(w)),
+                     "kernel": chunked_kernel_name(w),
                      "algorithmic_bytes_per_call": nbytes,
                      "call_ms_mean": r["call_ms_mean"], "call_ms_median": r["call_ms_median"]},
         "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s",
@@ -234,7 +295,8 @@ def main():
             "workload": dw.name, "steps": args.decode_steps, "ms_per_step": dr["step_ms"],
             "tokens_per_s": dw.N / (dr["step_ms"] / 1e3),
             "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": dgbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": dgbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic(dw.name, "decode_step_kernel"),
                          "kernel": "decode_step_kernel", "algorithmic_bytes_per_step": db},
             "state_finite": dr["finite"],
         }
