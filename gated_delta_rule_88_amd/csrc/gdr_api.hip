@@ -37,18 +37,14 @@ int check_chunk_sizes(int B, int H, int L, int dk, int dv, int C, int dtype, int
     if (mode < GDR_ALPHA_NONE || mode > GDR_ALPHA_CHANNEL) return GDR_ERR_INVALID_ARG;
     if (dtype != GDR_F32 && dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
     if (!supported_dim(dk) || !supported_dim(dv) || !supported_chunk(C)) return GDR_ERR_UNSUPPORTED;
-    const int Ce = gdr::effective_chunk(C, dtype, dk);
-    const size_t nc = ((size_t)L + Ce - 1) / Ce;
+    const size_t nc = ((size_t)L + 15) / 16;   // chunks at the shortest token step
     if ((size_t)B * H * nc > kMaxGroups) return GDR_ERR_UNSUPPORTED;
     return GDR_OK;
 }
 
 size_t chunk_workspace(int B, int H, int L, int dk, int C, int dtype, int mode)
 {
-    if (mode != GDR_ALPHA_CHANNEL) return 0;  // fused kernel, no workspace
-    const int Ce = gdr::effective_chunk(C, dtype, dk);
-    const size_t nc = ((size_t)L + Ce - 1) / Ce;
-    return (size_t)B * H * nc * gdr::chunk_workspace_bytes_per_chunk(Ce, dtype);
+    return gdr::chunk_workspace_bytes(B, H, L, dk, C, dtype, mode);
 }
 
 }  // namespace

@@ -32,16 +32,10 @@ struct ChunkArgs {
     hipStream_t stream;
 };
 
-// Chunk length the kernels actually use for a requested C.
-int effective_chunk(int C, int dtype, int dk);
-// Bytes of per-chunk workspace (WY factor + masked scores) for one chunk.
-size_t chunk_workspace_bytes_per_chunk(int C, int dtype);
+// Bytes of device workspace the chunked forward needs.
+size_t chunk_workspace_bytes(int B, int H, int L, int dk, int C, int dtype, int mode);
 
 hipError_t launch_decode_step(const DecodeArgs& a);
 hipError_t launch_fwd_chunked(const ChunkArgs& a);
-// Fused pipelined forward (alpha modes none and scalar); no workspace.
-hipError_t launch_pipe_chunked(const ChunkArgs& a);
-// Token chunk the pipelined kernel uses for a requested C.
-int pipe_chunk(int C, int dtype, int dk);
 
 }  // namespace gdr

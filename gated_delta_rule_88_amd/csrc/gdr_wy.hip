@@ -1,0 +1,445 @@
+// gdr_wy.hip -- per-chunk prepass of the chunked forward: everything about a
+// chunk that does not depend on the state entering it.
+//
+// For a chunk of CK tokens of one (b, h) (notation of gdr_scan.hip):
+//   g_r = sum_{s<=r} log alpha_s           in-chunk cumulative log-decay
+//   A   = strictly-lower( diag(beta) (K K^T . Gamma) ),  Gamma_ri = exp(g_r - g_i)
+//   T~  = (I + A)^{-1} diag(beta)          the WY factor of the chunk's
+//                                          (I - beta k k^T) products
+// ("Linear Attention & DeltaNet", "How it works", item 3: the chunk's
+// Householder-like factors kept in compact WY form; "linear attention and its
+// gated descendants", "Gated DeltaNet": the decay multiplies the state before
+// the delta update, which is where Gamma comes from.)
+//
+// Chunks are independent, so the whole grid runs at once: this is the part
+// of the method that is parallel over the sequence.  Two kernels:
+//   chunk_wy_kernel          alpha = 1 or scalar alpha; one wave per chunk.
+//                            Writes T~, and for scalar alpha the masked decay
+//                            matrix Gamma and gamma_r, exp(g_C - g_r), gamma_C.
+//   chunk_wy_channel_kernel  per-channel alpha; one workgroup per chunk.  The
+//                            decay sits inside the channel sums,
+//                            A_ri = beta_r sum_c k_rc k_ic exp(G_rc - G_ic), so
+//                            it also forms the decayed operands the scan needs
+//                            (K . exp(G), Q . exp(G), K . exp(G_C - G)), the
+//                            masked score block P and exp(G_C).
+// The inverse is taken in fp32 on every path: 16 x 16 diagonal blocks by
+// forward substitution (one lane per column), the block below the diagonal
+// as T_10 = -T_11 (A_10 T_00) with fp32 MFMA.
+#include "gdr_device.h"
+#include "gdr_chunk.h"
+
+namespace gdr {
+
+namespace {
+
+// K fragment (ldfrag convention) straight from global memory; rows at or
+// past `valid` read as zero.
+template <typename E>
+__device__ __forceinline__ Frag<E> gfrag(const E* base, int ld, int row0, int k0, int valid) {
+    const int l = lane_id(), r = row0 + (l & 15);
+    const E* p = base + (size_t)r * ld + k0 + 8 * (l >> 4);
+    Frag<E> f;
+    if constexpr (sizeof(E) == 2) {
+        f.v = bf16x8{};
+        if (r < valid) f.v = *reinterpret_cast<const bf16x8*>(p);
+    } else {
+        f.lo = zero4();
+        f.hi = zero4();
+        if (r < valid) {
+            f.lo = *reinterpret_cast<const f32x4*>(p);
+            f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+        }
+    }
+    return f;
+}
+
+// (I + A)^{-1} for a strictly lower-triangular CK x CK block A (CK = 16 or
+// 32) held in LDS (row stride LF), by one wave.  Writes T row-major to Tf
+// and transposed to Tt (both stride LF).  Af, Tf, Tt belong to this wave.
+template <int CK, int LF>
+__device__ __forceinline__ void unit_lower_inverse(const float* Af, float* Tf, float* Tt) {
+    constexpr int NB = CK / 16;
+    const int l = lane_id(), g4 = l >> 4, c16 = l & 15;
+    {
+        // lane (b, j) solves column j of diagonal block b; row r + 1 of A is
+        // fetched while row r is being solved
+        const int b = min(g4, NB - 1), j = c16;
+        const float* ab = Af + 16 * b * LF + 16 * b;
+        float t[16];
+        f32x4 cur[4], nxt[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cur[q] = *reinterpret_cast<const f32x4*>(ab + 4 * q);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            if (r + 1 < 16) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) nxt[q] = *reinterpret_cast<const f32x4*>(ab + (r + 1) * LF + 4 * q);
+            }
+            float acc[4] = {(r == j) ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < r; ++i) acc[i & 3] -= cur[i >> 2][i & 3] * t[i];
+            t[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            if (r + 1 < 16) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
+            }
+        }
+        if (g4 < NB) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Tf[(16 * b + r) * LF + 16 * b + j] = t[r];
+#pragma unroll
+            for (int r = 0; r < 16; r += 4)
+                *reinterpret_cast<f32x4*>(Tt + (16 * b + j) * LF + 16 * b + r) =
+                    f32x4{t[r], t[r + 1], t[r + 2], t[r + 3]};
+        }
+    }
+    wave_lds_fence();
+    if constexpr (NB == 2) {
+        // Y = A_10 T_00 (lane: Y[4g + e][c]), then Z = T_11 Y, T_10 = -Z
+        f32x4 y = zero4();
+        mma_k16(y, Af, LF, 16, Tt, LF, 0, 0);
+        const f32x4 t11 = *reinterpret_cast<const f32x4*>(Tf + (16 + c16) * LF + 16 + 4 * g4);
+        f32x4 z = zero4();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z = __builtin_amdgcn_mfma_f32_16x16x4f32(t11[e], y[e], z, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Tf[(16 + 4 * g4 + e) * LF + c16] = -z[e];
+        wave_lds_fence();
+    }
+}
+
+// Per-wave LDS scratch of chunk_wy_kernel.
+template <typename E, int CK>
+struct WyScratch {
+    static constexpr int VE = Vec<E>::n, ES = (int)sizeof(E);
+    static constexpr int LF = CK + 4;    // fp32 row stride
+    static constexpr int LM = CK + VE;   // row stride of the Gamma staging block
+    static constexpr int off_A = 0;
+    static constexpr int off_Tf = off_A + CK * LF * 4;
+    static constexpr int off_Tt = off_Tf + CK * LF * 4;
+    static constexpr int off_M = off_Tt + CK * LF * 4;
+    static constexpr int off_g = off_M + CK * LM * ES;
+    static constexpr int off_b = off_g + CK * 4;
+    static constexpr int bytes = (off_b + CK * 4 + 15) / 16 * 16;
+};
+
+}  // namespace
+
+// ======================================================================
+// alpha = 1 and scalar alpha: one wave per chunk, four chunks per workgroup.
+// ======================================================================
+template <typename E, int DK, int CK, int MODE>
+__global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
+{
+    using SC = WyScratch<E, CK>;
+    constexpr int VE = SC::VE, LF = SC::LF, LM = SC::LM;
+    constexpr int NB = CK / 16, NKS = DK / 32;
+    constexpr bool GATED = (MODE == kAlphaScalar);
+    constexpr WsLayout WL = ws_layout((int)sizeof(E), DK, CK, MODE);
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int cid = blockIdx.x * 4 + w;
+    if (cid >= p.total) return;   // wave-uniform; this kernel has no block barrier
+    const int l = lane_id(), g4 = l >> 4, c16 = l & 15;
+    const int bh = cid / p.NC, n = cid % p.NC;
+    const int t0 = n * CK, valid = min(CK, p.L - t0);
+
+    unsigned char* sw = smem + w * SC::bytes;
+    float* Af = reinterpret_cast<float*>(sw + SC::off_A);
+    float* Tf = reinterpret_cast<float*>(sw + SC::off_Tf);
+    float* Tt = reinterpret_cast<float*>(sw + SC::off_Tt);
+    E* Ms = reinterpret_cast<E*>(sw + SC::off_M);
+    float* gs = reinterpret_cast<float*>(sw + SC::off_g);
+    float* bs = reinterpret_cast<float*>(sw + SC::off_b);
+
+    // K tiles of the chunk as MFMA operands, straight from global memory
+    const E* kc = reinterpret_cast<const E*>(p.k) + ((size_t)bh * p.L + t0) * DK;
+    Frag<E> kf[NB][NKS];
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) kf[tb][ks] = gfrag<E>(kc, DK, 16 * tb, 32 * ks, valid);
+
+    // beta (zero past the end of the sequence) and the cumulative log-decay
+    float bt = 0.f, la = 0.f;
+    if (l < valid) {
+        bt = p.beta[(size_t)bh * p.L + t0 + l];
+        if (GATED) la = p.log_alpha[(size_t)bh * p.L + t0 + l];
+    }
+    const float g = wave_incl_scan(la);
+    const float glast = __shfl(g, CK - 1, kWave);
+    if (l < CK) { gs[l] = g; bs[l] = bt; }
+    wave_lds_fence();
+
+    // Gram tiles -> A; the same exponentials give Gamma for the scan
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+#pragma unroll
+        for (int ib = 0; ib <= rb; ++ib) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) mma(acc, kf[rb][ks], kf[ib][ks]);
+            const int i = 16 * ib + c16, r0 = 16 * rb + 4 * g4;
+            const float gi = gs[i];
+            const f32x4 gr = *reinterpret_cast<const f32x4*>(gs + r0);
+            const f32x4 br = *reinterpret_cast<const f32x4*>(bs + r0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float d = GATED ? __expf(fminf(gr[e] - gi, 0.f)) : 1.f;
+                Af[(r0 + e) * LF + i] = (r0 + e > i) ? br[e] * d * acc[e] : 0.f;
+                if (GATED) Ms[(r0 + e) * LM + i] = from_f32<E>((r0 + e >= i) ? d : 0.f);
+            }
+        }
+    }
+    wave_lds_fence();
+    unit_lower_inverse<CK, LF>(Af, Tf, Tt);
+
+    // T~ = T diag(beta) (and Gamma) to the workspace, zero above the diagonal
+    unsigned char* rec = p.ws + (size_t)cid * WL.bytes;
+    E* Tg = reinterpret_cast<E*>(rec + WL.T);
+    E* Mg = reinterpret_cast<E*>(rec + WL.M);
+    constexpr int RV = CK / VE, TV = CK * RV;
+#pragma unroll
+    for (int x0 = 0; x0 < TV; x0 += kWave) {
+        const int x = x0 + l;
+        if (x < TV) {
+            const int r = x / RV, c0 = (x % RV) * VE;
+            float tv[VE];
+#pragma unroll
+            for (int q = 0; q < VE; q += 4) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(Tf + r * LF + c0 + q);
+                const f32x4 b = *reinterpret_cast<const f32x4*>(bs + c0 + q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tv[q + e] = (c0 + q + e <= r) ? a[e] * b[e] : 0.f;
+            }
+            st16(Tg + r * CK + c0, Pack<E>::pack(tv));
+            if (GATED) {
+                float mv[VE];
+                Pack<E>::unpack(ld16(Ms + r * LM + c0), mv);
+#pragma unroll
+                for (int j = 0; j < VE; ++j) mv[j] = (c0 + j <= r) ? mv[j] : 0.f;
+                st16(Mg + r * CK + c0, Pack<E>::pack(mv));
+            }
+        }
+    }
+    if (GATED && l < CK) {
+        float* F = reinterpret_cast<float*>(rec + WL.F);
+        F[l] = __expf(g);
+        F[CK + l] = __expf(glast - g);
+        F[2 * CK + l] = (l == 0) ? __expf(glast) : 0.f;
+        F[3 * CK + l] = 0.f;
+    }
+}
+
+// ======================================================================
+// Per-channel alpha: one workgroup (4 waves) per chunk.
+// ======================================================================
+template <typename E, int DK, int CK>
+struct WyChannelLayout {
+    static constexpr int VE = Vec<E>::n, ES = (int)sizeof(E);
+    static constexpr int DKP = DK + VE;   // row stride of the K, Q copies
+    static constexpr int GP = DK + 4;     // fp32 [CK][DK] cumulative decay
+    static constexpr int LF = CK + 4;
+    static constexpr int LP = CK + VE;
+    static constexpr int off_K = 0;
+    static constexpr int off_Q = off_K + CK * DKP * ES;
+    static constexpr int off_G = off_Q + CK * DKP * ES;
+    static constexpr int off_A = off_G + CK * GP * 4;
+    static constexpr int off_Tf = off_A + CK * LF * 4;
+    static constexpr int off_Tt = off_Tf + CK * LF * 4;
+    static constexpr int off_P = off_Tt + CK * LF * 4;
+    static constexpr int off_b = off_P + CK * LP * ES;
+    static constexpr int bytes = off_b + CK * 4;
+};
+
+template <typename E, int DK, int CK>
+__global__ __launch_bounds__(256) void chunk_wy_channel_kernel(WyParams p)
+{
+    using LY = WyChannelLayout<E, DK, CK>;
+    constexpr int VE = LY::VE, DKP = LY::DKP, GP = LY::GP, LF = LY::LF, LP = LY::LP;
+    constexpr int NB = CK / 16, NKS = DK / 32;
+    constexpr WsLayout WL = ws_layout((int)sizeof(E), DK, CK, kAlphaChannel);
+    extern __shared__ __align__(16) unsigned char smem[];
+    E* Ks = reinterpret_cast<E*>(smem + LY::off_K);
+    E* Qs = reinterpret_cast<E*>(smem + LY::off_Q);
+    float* Gs = reinterpret_cast<float*>(smem + LY::off_G);
+    float* Af = reinterpret_cast<float*>(smem + LY::off_A);
+    float* Tf = reinterpret_cast<float*>(smem + LY::off_Tf);
+    float* Tt = reinterpret_cast<float*>(smem + LY::off_Tt);
+    E* Ps = reinterpret_cast<E*>(smem + LY::off_P);
+    float* bs = reinterpret_cast<float*>(smem + LY::off_b);
+
+    const int tid = threadIdx.x, l = lane_id(), g4 = l >> 4, c16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int cid = blockIdx.x;
+    const int bh = cid / p.NC, n = cid % p.NC;
+    const int t0 = n * CK, valid = min(CK, p.L - t0);
+    const E* kc = reinterpret_cast<const E*>(p.k) + ((size_t)bh * p.L + t0) * DK;
+    const E* qc = reinterpret_cast<const E*>(p.q) + ((size_t)bh * p.L + t0) * DK;
+    const float* lac = p.log_alpha + ((size_t)bh * p.L + t0) * DK;
+    unsigned char* rec = p.ws + (size_t)cid * WL.bytes;
+
+    // ---- stage K, Q and log alpha (floored; zero past the end), beta
+    constexpr int RV = DK / VE;
+    for (int i = tid; i < CK * RV; i += 256) {
+        const int r = i / RV, c = (i % RV) * VE;
+        u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
+        if (r < valid) { kv = ld16(kc + (size_t)r * DK + c); qv = ld16(qc + (size_t)r * DK + c); }
+        st16(Ks + r * DKP + c, kv);
+        st16(Qs + r * DKP + c, qv);
+    }
+    constexpr int RF = DK / 4;
+    for (int i = tid; i < CK * RF; i += 256) {
+        const int r = i / RF, c = (i % RF) * 4;
+        f32x4 x = zero4();
+        if (r < valid) {
+            x = *reinterpret_cast<const f32x4*>(lac + (size_t)r * DK + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = fmaxf(x[e], kChannelLogAlphaMin);
+        }
+        *reinterpret_cast<f32x4*>(Gs + r * GP + c) = x;
+    }
+    if (tid < CK) bs[tid] = (tid < valid) ? p.beta[(size_t)bh * p.L + t0 + tid] : 0.f;
+    __syncthreads();
+    // cumulative sum down each key channel
+    for (int c = tid; c < DK; c += 256) {
+        float acc = 0.f;
+#pragma unroll
+        for (int r = 0; r < CK; ++r) { acc += Gs[r * GP + c]; Gs[r * GP + c] = acc; }
+    }
+    __syncthreads();
+
+    // ---- decayed operands for the scan and exp(G_C)
+    {
+        const float* GL = Gs + (CK - 1) * GP;
+        E* KGg = reinterpret_cast<E*>(rec + WL.KG);
+        E* QGg = reinterpret_cast<E*>(rec + WL.QG);
+        E* KDg = reinterpret_cast<E*>(rec + WL.KD);
+        for (int i = tid; i < CK * RV; i += 256) {
+            const int r = i / RV, c0 = (i % RV) * VE;
+            float kx[VE], qx[VE], a[VE], b[VE], d[VE];
+            Pack<E>::unpack(ld16(Ks + r * DKP + c0), kx);
+            Pack<E>::unpack(ld16(Qs + r * DKP + c0), qx);
+#pragma unroll
+            for (int j = 0; j < VE; ++j) {
+                const float gg = Gs[r * GP + c0 + j];
+                const float eg = __expf(gg), ed = __expf(GL[c0 + j] - gg);
+                a[j] = kx[j] * eg;
+                b[j] = qx[j] * eg;
+                d[j] = kx[j] * ed;
+            }
+            st16(KGg + r * DK + c0, Pack<E>::pack(a));
+            st16(QGg + r * DK + c0, Pack<E>::pack(b));
+            st16(KDg + r * DK + c0, Pack<E>::pack(d));
+        }
+        float* F = reinterpret_cast<float*>(rec + WL.F);
+        for (int c = tid; c < DK; c += 256) F[c] = __expf(GL[c]);
+    }
+
+    // ---- Gram and score tiles.  The decay exp(G_rc - G_ic) sits inside the
+    // channel sum; each operand row is scaled relative to a reference row m:
+    // the left row r by exp(G_r - G_m), the right row i by exp(G_m - G_i).
+    // Below the diagonal m = 16 rb - 1 (both factors <= 1); on a diagonal
+    // block m = 16 rb + 7, so no factor exceeds exp(8 * 10) in fp32.
+    constexpr int NTILE = NB * (NB + 1) / 2;
+    if (w < NTILE) {
+        const int rb = (w == 0) ? 0 : 1, ib = (w == 2) ? 1 : 0;
+        const int m = (rb == ib) ? 16 * rb + 7 : 16 * rb - 1;
+        const int rl = 16 * rb + c16, rr = 16 * ib + c16;
+        f32x4 accA = zero4(), accP = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int c0 = 32 * ks + 8 * g4;
+            float fl[8], fr[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float gm = Gs[m * GP + c0 + j];
+                fl[j] = __expf(Gs[rl * GP + c0 + j] - gm);
+                fr[j] = __expf(gm - Gs[rr * GP + c0 + j]);
+            }
+            Frag<E> kl, ql, kr;
+            load_scaled_frag(kl, Ks + rl * DKP + c0, fl);
+            load_scaled_frag(ql, Qs + rl * DKP + c0, fl);
+            load_scaled_frag(kr, Ks + rr * DKP + c0, fr);
+            mma(accA, kl, kr);   // A tile: lane holds [16rb + 4g + e][16ib + c]
+            mma(accP, kr, ql);   // P^T tile: lane holds P[16rb + c][16ib + 4g + e]
+        }
+        {
+            const int i = 16 * ib + c16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * g4 + e;
+                Af[r * LF + i] = (r > i) ? bs[r] * accA[e] : 0.f;
+            }
+        }
+        {
+            const int r = 16 * rb + c16, i0 = 16 * ib + 4 * g4;
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (r >= i0 + e) ? accP[e] : 0.f;
+            st4(Ps + r * LP + i0, x[0], x[1], x[2], x[3]);
+        }
+    }
+    __syncthreads();
+    if (w == 0) unit_lower_inverse<CK, LF>(Af, Tf, Tt);
+    __syncthreads();
+
+    // ---- T~ = T diag(beta) and P to the workspace, zero above the diagonal
+    E* Tg = reinterpret_cast<E*>(rec + WL.T);
+    E* Pg = reinterpret_cast<E*>(rec + WL.M);
+    constexpr int CV = CK / VE;
+    for (int idx = tid; idx < CK * CV; idx += 256) {
+        const int r = idx / CV, c0 = (idx % CV) * VE;
+        float x[VE], y[VE];
+        Pack<E>::unpack(ld16(Ps + r * LP + c0), y);
+#pragma unroll
+        for (int j = 0; j < VE; ++j) {
+            const int c = c0 + j;
+            x[j] = (c <= r) ? Tf[r * LF + c] * bs[c] : 0.f;
+            y[j] = (c <= r) ? y[j] : 0.f;
+        }
+        st16(Tg + r * CK + c0, Pack<E>::pack(x));
+        st16(Pg + r * CK + c0, Pack<E>::pack(y));
+    }
+}
+
+// ------------------------------------------------------------------ host side
+template <typename K>
+static hipError_t launch_with_lds(K* kern, int grid, int lds, hipStream_t stream, const WyParams& wp)
+{
+    hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, wp);
+    return hipGetLastError();
+}
+
+template <typename E, int DK, int CK>
+static hipError_t launch_wy_t(const ChunkArgs& a)
+{
+    const int NC = (a.L + CK - 1) / CK;
+    WyParams wp{a.q, a.k, a.beta, a.log_alpha, static_cast<unsigned char*>(a.workspace), a.L, NC,
+                a.B * a.H * NC};
+    if (a.mode == kAlphaChannel) {
+        using LY = WyChannelLayout<E, DK, CK>;
+        static_assert(LY::bytes <= 160 * 1024, "LDS budget");
+        return launch_with_lds(chunk_wy_channel_kernel<E, DK, CK>, wp.total, LY::bytes, a.stream, wp);
+    }
+    constexpr int bytes = 4 * WyScratch<E, CK>::bytes;
+    static_assert(bytes <= 160 * 1024, "LDS budget");
+    const int grid = (wp.total + 3) / 4;
+    if (a.mode == kAlphaScalar)
+        return launch_with_lds(chunk_wy_kernel<E, DK, CK, kAlphaScalar>, grid, bytes, a.stream, wp);
+    return launch_with_lds(chunk_wy_kernel<E, DK, CK, kAlphaNone>, grid, bytes, a.stream, wp);
+}
+
+hipError_t launch_wy(const ChunkArgs& a, int CK)
+{
+    if (a.dtype == kBF16) {
+        if (a.dk == 128) return CK == 16 ? launch_wy_t<bf16, 128, 16>(a) : launch_wy_t<bf16, 128, 32>(a);
+        return CK == 16 ? launch_wy_t<bf16, 64, 16>(a) : launch_wy_t<bf16, 64, 32>(a);
+    }
+    return a.dk == 128 ? launch_wy_t<float, 128, 16>(a) : launch_wy_t<float, 64, 16>(a);
+}
+
+}  // namespace gdr

@@ -59,16 +59,19 @@ def test_version_and_status_strings(lib):
 
 def test_workspace_size_query():
     ws = gdr.gdr_fwd_chunked_workspace_size
-    # DeltaNet and Gated DeltaNet run fused: no workspace
-    assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 1) == 0
-    assert ws(1, 2, 256, 64, 64, 64, gdr.GDR_F32, 0) == 0
-    # channel-wise decay: 2 * C * C elements per chunk (WY factor, scores)
-    assert ws(4, 16, 4096, 128, 128, 64, gdr.GDR_BF16, 2) == 64 * 64 * 2 * 64 * 64 * 2
-    assert ws(1, 1, 200, 64, 64, 64, gdr.GDR_BF16, 2) == 4 * 2 * 64 * 64 * 2  # ragged tail
+    # Per chunk of CK tokens (CK = 32 for bf16, 16 for fp32 or when C = 16):
+    # T~ (CK*CK elements); scalar gates add the decay matrix (CK*CK) and
+    # 4*CK floats of decay factors; channel gates add the score block (CK*CK),
+    # d_k floats and three CK x d_k decayed operands.
+    assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 1) == 64 * 64 * (2048 + 2048 + 512)
+    assert ws(1, 2, 256, 64, 64, 64, gdr.GDR_F32, 0) == 2 * 16 * (16 * 16 * 4)
+    assert ws(4, 16, 4096, 128, 128, 64, gdr.GDR_BF16, 2) == \
+        64 * 128 * (2048 + 2048 + 512 + 3 * 32 * 128 * 2)
+    assert ws(1, 1, 200, 64, 64, 64, gdr.GDR_BF16, 2) == 7 * (2048 + 2048 + 256 + 3 * 32 * 64 * 2)
+    assert ws(1, 1, 64, 128, 128, 64, gdr.GDR_F32, 2) == 4 * (1024 + 1024 + 512 + 3 * 16 * 128 * 4)
+    assert ws(1, 1, 100, 128, 128, 16, gdr.GDR_BF16, 1) == 7 * (512 + 512 + 256)
     assert ws(1, 1, 0, 64, 64, 64, gdr.GDR_BF16, 2) == 0
     assert ws(0, 4, 100, 64, 64, 64, gdr.GDR_BF16, 2) == 0
-    # fp32 with d_k = 128 runs 32-token chunks
-    assert ws(1, 1, 64, 128, 128, 64, gdr.GDR_F32, 2) == 2 * 2 * 32 * 32 * 4
     for bad in [(1, 1, 64, 96, 128, 64, 1, 1), (1, 1, 64, 128, 128, 48, 1, 1),
                 (1, 1, 64, 128, 128, 64, 7, 1), (1, 1, 64, 128, 128, 64, 1, 3),
                 (-1, 1, 64, 128, 128, 64, 1, 1), (1, 1, -5, 128, 128, 64, 1, 1)]:
@@ -112,10 +115,11 @@ def dec(lib, N=2, H=2, dk=64, dv=64, dtype=1, q=Q, k=K, v=V, beta=BETA, mode=1, 
     (dict(mode=2, la=LA + 4), gdr.GDR_ERR_INVALID_ARG),  # channel gates need 16 B
     (dict(o=Q + 64), gdr.GDR_ERR_INVALID_ARG),        # o overlaps q
     (dict(sf=S0 + 64), gdr.GDR_ERR_INVALID_ARG),      # partial overlap of S_final and S0
-    # the workspace is only used with channel-wise decay
-    (dict(mode=2, ws=K), gdr.GDR_ERR_INVALID_ARG),            # workspace overlaps k
+    (dict(ws=K), gdr.GDR_ERR_INVALID_ARG),                    # workspace overlaps k
+    (dict(ws_bytes=16), gdr.GDR_ERR_WORKSPACE_TOO_SMALL),
+    (dict(ws=None, ws_bytes=0), gdr.GDR_ERR_WORKSPACE_TOO_SMALL),
     (dict(mode=2, ws_bytes=16), gdr.GDR_ERR_WORKSPACE_TOO_SMALL),
-    (dict(mode=2, ws=None, ws_bytes=0), gdr.GDR_ERR_WORKSPACE_TOO_SMALL),
+    (dict(mode=0, la=None, ws=None, ws_bytes=0), gdr.GDR_ERR_WORKSPACE_TOO_SMALL),
 ])
 def test_fwd_chunked_rejects_before_launch(lib, kw, status):
     assert status != gdr.GDR_OK  # every case must stop before a launch
