@@ -99,10 +99,11 @@ def decode_algorithmic(w: gi.DecodeWorkload) -> float:
 
 
 def chunked_kernel_name(w) -> str:
-    """The kernels one gdr_fwd_chunked call launches for this workload."""
+    """The kernels one gdr_fwd_chunked call launches for this workload (the
+    roofline unit is the whole call: both launches)."""
     if w.mode == gi.ALPHA_CHANNEL:
-        return "chunk_prep_kernel + chunk_scan_kernel"
-    return "chunk_pipe_kernel"
+        return "chunk_wy_channel_kernel + chunk_scan_kernel"
+    return "chunk_wy_kernel + chunk_scan_kernel"
 
 
 def copy_probe(mib: int, reps: int = 5):

@@ -22,9 +22,24 @@ __host__ __device__ constexpr int chunk_step(int C, int dtype)
     return (C == 16 || dtype == kF32) ? 16 : 32;
 }
 
+// Column order of the [CK][CK] workspace blocks (T~, Gamma, P).  For CK = 32
+// memory column 8g + 4p + e holds token 16p + 4g + e: the eight tokens that
+// lane group g of a 16x16x32 MFMA contracts over (two 16-token tiles p, four
+// consecutive tokens e each) are then one 16-byte read.  For CK = 16 the
+// order is the natural one.
+__host__ __device__ constexpr int tok_of_col(int CK, int mc)
+{
+    return CK == 32 ? 16 * ((mc >> 2) & 1) + 4 * (mc >> 3) + (mc & 3) : mc;
+}
+__host__ __device__ constexpr int col_of_tok(int CK, int t)
+{
+    return CK == 32 ? 8 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3) : t;
+}
+
 // Per-chunk workspace record (byte offsets), CK tokens, element type of size
 // ES.  Regions are 16-byte aligned and each is a dense row-major block.
 //   T   [CK][CK] E     T~ = (I + A)^{-1} diag(beta), zero above the diagonal
+//                      (rows in token order, columns in tok_of_col order)
 //   M   [CK][CK] E     scalar alpha: Gamma_ri = exp(g_r - g_i) on and below the
 //                      diagonal, zero above;  channel alpha: the masked decayed
 //                      score block P;  alpha = 1: absent

@@ -32,10 +32,21 @@
 //               per lane, then waits until chunk n + 1 has landed.
 // Every product is v_mfma_f32_16x16x32_bf16 (fp32: 16x16x4f32) in NT form;
 // result tiles feed the next product straight from registers (tile-pair
-// operands, gdr_device.h), K^T and V are read with transposing LDS loads.
-// K, Q, V, T~ and Gamma/P sit in LDS row-major with their 16-byte chunks
-// XOR-swizzled by row: the copier applies the permutation by choosing each
-// lane's source address, every reader undoes it.
+// operands, gdr_device.h).
+//
+// Layout choices that keep the per-step instruction count low:
+//  - d_k order inside the state.  Element e of state tile a = 2ks + p held by
+//    lane group g is key channel 32ks + 8g + 4p + e, so the eight key
+//    channels a lane group contracts over are contiguous in K and Q: every
+//    K or Q operand is one 16-byte LDS read.  K^T comes from transposing LDS
+//    reads whose per-lane addresses follow the same order.
+//  - LDS is region-major ([K: 4 slots][Q: 4 slots][V]...) and the step loop
+//    is unrolled over the four slots, so slot and tile offsets are
+//    instruction immediates; per-lane addresses are computed once.
+//  - K and Q rows are XOR-swizzled by (r & 15) ^ ((r & 2) << 2) on 16-byte
+//    chunks, which keeps both the 16-byte fragment reads and the
+//    transposing reads at the LDS's conflict-free rate; the copier applies
+//    the permutation by its choice of source addresses.
 #include "gdr_device.h"
 #include "gdr_chunk.h"
 
@@ -48,7 +59,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
 // Row-major LDS tile of W elements per row whose 16-byte chunks are permuted
-// within each row by XOR with swz(row).
+// within each row by XOR with swz(row); swz depends only on row % 16.
 template <typename E, int W>
 struct Swz {
     static constexpr int ES = (int)sizeof(E);
@@ -56,11 +67,10 @@ struct Swz {
     static constexpr int NCH = RB / 16;    // 16-byte chunks per row
     static_assert(NCH == 2 || NCH == 4 || NCH == 8 || NCH == 16 || NCH == 32, "row width");
     __device__ static __forceinline__ int swz(int r) {
-        if (NCH == 2) return (r >> 2) & 1;
-        if (NCH == 4) return (r >> 2) & 3;
+        if (NCH == 2) return (r >> 1) & 1;
+        if (NCH == 4) return (r >> 1) & 3;
         if (NCH == 8) return (r >> 1) & 7;
-        if (NCH == 16) return ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3);
-        return r & 15;
+        return (r & 15) ^ ((r & 2) << 2);
     }
     // byte offset of element (r, c); an access of up to 16 bytes starting at
     // c must not cross a 16-byte boundary
@@ -70,104 +80,61 @@ struct Swz {
     }
 };
 
-__device__ __forceinline__ u32x4 lds16(const unsigned char* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ u32x2 lds8(const unsigned char* p) { return *reinterpret_cast<const u32x2*>(p); }
+template <int N> __device__ __forceinline__ u32x4 lds16(const unsigned char* base, int off) {
+    return *reinterpret_cast<const u32x4*>(base + off + N);
+}
+template <int N> __device__ __forceinline__ u32x2 lds8(const unsigned char* base, int off) {
+    return *reinterpret_cast<const u32x2*>(base + off + N);
+}
 
-// Tile-pair fragment: lane reads row r0 + l%16, k = k0 + 16p + 4(l/16) + e.
-template <typename E, int W>
-__device__ __forceinline__ Frag<E> ldfrag_pair_swz(const unsigned char* base, int r0, int k0) {
-    using S = Swz<E, W>;
-    const int l = lane_id(), r = r0 + (l & 15), k = k0 + 4 * (l >> 4);
+// MFMA operand of 8 consecutive elements at base + off + N; fp32 takes two
+// 16-byte reads, the second at base + off_hi + N (the swizzle may have moved
+// it away from the first).
+template <typename E, int N>
+__device__ __forceinline__ Frag<E> ld_frag(const unsigned char* base, int off, int off_hi) {
     Frag<E> f;
     if constexpr (sizeof(E) == 2) {
-        const u32x2 lo = lds8(base + S::off(r, k)), hi = lds8(base + S::off(r, k + 16));
-        f.v = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        f.v = __builtin_bit_cast(bf16x8, lds16<N>(base, off));
     } else {
-        f.lo = __builtin_bit_cast(f32x4, lds16(base + S::off(r, k)));
-        f.hi = __builtin_bit_cast(f32x4, lds16(base + S::off(r, k + 16)));
+        f.lo = __builtin_bit_cast(f32x4, lds16<N>(base, off));
+        f.hi = __builtin_bit_cast(f32x4, lds16<N>(base, off_hi));
     }
     return f;
 }
-// 16-wide k-step fragment: lane reads row r0 + l%16, k = k0 + 4(l/16) + e.
-template <typename E, int W>
-__device__ __forceinline__ Frag16<E> ldfrag16_swz(const unsigned char* base, int r0, int k0) {
-    using S = Swz<E, W>;
-    const int l = lane_id(), r = r0 + (l & 15), k = k0 + 4 * (l >> 4);
+// 16-wide k-step operand of 4 consecutive elements.
+template <typename E, int N>
+__device__ __forceinline__ Frag16<E> ld_frag16(const unsigned char* base, int off) {
     Frag16<E> f;
-    if constexpr (sizeof(E) == 2) {
-        f.v = __builtin_bit_cast(s16x4, lds8(base + S::off(r, k)));
-    } else {
-        f.v = __builtin_bit_cast(f32x4, lds16(base + S::off(r, k)));
-    }
+    if constexpr (sizeof(E) == 2) f.v = __builtin_bit_cast(s16x4, lds8<N>(base, off));
+    else f.v = __builtin_bit_cast(f32x4, lds16<N>(base, off));
     return f;
 }
-// Four consecutive elements of row r from column c (c % 4 == 0), as fp32.
-template <typename E, int W>
-__device__ __forceinline__ f32x4 ld4_swz(const unsigned char* base, int r, int c) {
-    using S = Swz<E, W>;
+// Four consecutive elements as fp32.
+template <typename E, int N>
+__device__ __forceinline__ f32x4 ld_4f(const unsigned char* base, int off) {
     if constexpr (sizeof(E) == 2) {
-        const u32x2 w = lds8(base + S::off(r, c));
+        const u32x2 w = lds8<N>(base, off);
         return f32x4{bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y)};
     } else {
-        return __builtin_bit_cast(f32x4, lds16(base + S::off(r, c)));
+        return __builtin_bit_cast(f32x4, lds16<N>(base, off));
     }
 }
-// Transposed read: lane (g, c) = (l/16, l%16) receives M[r0 + 4g + q][c0 + c]
-// for q = 0..3.  bf16 uses the transposing LDS load (lane 16h + i supplies
-// the address of M[r0 + 4h + i/4][c0 + 4(i%4) .. +3]); fp32 reads the four
-// elements one by one.
-template <typename E, int W>
-__device__ __forceinline__ f32x4 ld_tr(const unsigned char* base, int r0, int c0, s16x4* raw = nullptr) {
-    using S = Swz<E, W>;
-    const int l = lane_id(), g = l >> 4, i = l & 15;
-    if constexpr (sizeof(E) == 2) {
-        const unsigned char* a = base + S::off(r0 + 4 * g + (i >> 2), c0 + 4 * (i & 3));
-        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(a));
-        if (raw) *raw = v;
-        const u32x2 w = __builtin_bit_cast(u32x2, v);
-        return f32x4{bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y)};
-    } else {
-        f32x4 r;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            r[q] = *reinterpret_cast<const float*>(base + S::off(r0 + 4 * g + q, c0 + i));
-        return r;
-    }
+// Transposing read of a 4 x 4 bf16 block per lane group: the lane's address
+// (from tr_off) names 4 consecutive elements; lane (g, c) receives element
+// c % 4 of the vectors addressed by lanes (g, 4q + c / 4), q = 0..3.
+template <int N>
+__device__ __forceinline__ s16x4 ld_tr16(const unsigned char* base, int off) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + off + N));
 }
-
-// Direct global->LDS copies, 16 bytes per lane: the instruction's lane l
-// writes LDS bytes [dst + 16 l, +16).
-template <int NBYTES>
-struct CopyCount { static constexpr int n = (NBYTES + 1023) / 1024; };
-
-// [CK][W] row-major tile, global row stride gstride bytes, into a swizzled
-// LDS region; rows at or past `valid` repeat row valid - 1.
-template <typename E, int W, int CK>
-__device__ __forceinline__ void copy_tile(unsigned char* dst, const unsigned char* src, size_t gstride, int valid) {
-    using S = Swz<E, W>;
-    constexpr int TB = CK * S::RB;
-    const int l = lane_id();
-#pragma unroll
-    for (int j = 0; j < CopyCount<TB>::n; ++j) {
-        const int b = 1024 * j + 16 * l;
-        if (TB % 1024 == 0 || b < TB) {
-            const int row = b / S::RB, pch = (b % S::RB) / 16;
-            const int lch = pch ^ S::swz(row);
-            const unsigned char* g = src + (size_t)min(row, valid - 1) * gstride + lch * 16;
-            __builtin_amdgcn_global_load_lds((const glb_void_t*)g, (lds_void_t*)(dst + 1024 * j), 16, 0, 0);
-        }
-    }
+__device__ __forceinline__ f32x4 unpack4(s16x4 v) {
+    const u32x2 w = __builtin_bit_cast(u32x2, v);
+    return f32x4{bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y)};
 }
-template <int NBYTES>
-__device__ __forceinline__ void copy_flat(unsigned char* dst, const unsigned char* src) {
-    const int l = lane_id();
-#pragma unroll
-    for (int j = 0; j < CopyCount<NBYTES>::n; ++j) {
-        const int b = 1024 * j + 16 * l;
-        if (NBYTES % 1024 == 0 || b < NBYTES)
-            __builtin_amdgcn_global_load_lds((const glb_void_t*)(src + b), (lds_void_t*)(dst + 1024 * j), 16, 0, 0);
-    }
+template <int N> __device__ __forceinline__ float ldf(const unsigned char* base, int off) {
+    return *reinterpret_cast<const float*>(base + off + N);
+}
+template <int N> __device__ __forceinline__ f32x4 ldf4(const unsigned char* base, int off) {
+    return *reinterpret_cast<const f32x4*>(base + off + N);
 }
 
 // Barrier for the pipeline: this wave's LDS accesses are complete, then all
@@ -178,46 +145,76 @@ __device__ __forceinline__ void step_barrier() {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Compile-time loop: f(integral_constant<int, I>) for I = B .. N - 1.
+template <int I, int N>
+struct StaticFor {
+    template <class F>
+    __device__ static __forceinline__ void run(F& f) {
+        f(std::integral_constant<int, I>{});
+        StaticFor<I + 1, N>::run(f);
+    }
+};
+template <int N>
+struct StaticFor<N, N> {
+    template <class F>
+    __device__ static __forceinline__ void run(F&) {}
+};
+
+template <int NBYTES>
+struct CopyCount { static constexpr int n = (NBYTES + 1023) / 1024; };
 }  // namespace
 
 template <typename E, int DK, int CK, int MODE>
 struct ScanLayout {
     static constexpr int ES = (int)sizeof(E);
     static constexpr int BV = 32;             // value channels per workgroup
-    static constexpr int NSLOT = 4;
     static constexpr bool CH = (MODE == kAlphaChannel);
+    // Ring of chunk slots.  At step s the copier fills chunk s + AHEAD while
+    // the state owners work on chunk s and the output waves on chunk s - 1.
+    static constexpr int AHEAD = 2;
+    static constexpr int NSLOT = AHEAD + 2;
+    static_assert(NSLOT % 2 == 0, "exchange parity follows the slot index");
     static constexpr int FB = MODE == kAlphaScalar ? 4 * CK * 4 : (CH ? DK * 4 : 0);
-    // one chunk slot
-    static constexpr int s_KX = 0;                                   // K or K.exp(G) [CK][DK]
-    static constexpr int s_KU = s_KX + CK * DK * ES;                 // K.exp(G_C-G) (channel)
-    static constexpr int s_Q = s_KU + (CH ? CK * DK * ES : 0);       // Q or Q.exp(G) [CK][DK]
-    static constexpr int s_V = s_Q + CK * DK * ES;                   // V block [CK][BV]
-    static constexpr int s_T = s_V + CK * BV * ES;                   // T~ [CK][CK]
-    static constexpr int s_M = s_T + CK * CK * ES;                   // Gamma or P [CK][CK]
-    static constexpr int s_F = s_M + (MODE != kAlphaNone ? CK * CK * ES : 0);
-    static constexpr int slot = align16(s_F + FB);
-    // exchange buffers (two steps deep): S operands and U operands of each
-    // state owner, one fragment per lane
+    static constexpr int szK = CK * DK * ES, szV = CK * BV * ES, szT = CK * CK * ES, szF = align16(FB);
+    // regions, each NSLOT slots
+    static constexpr int rK = 0;                                   // K or K.exp(G)
+    static constexpr int rKU = rK + NSLOT * szK;                   // K.exp(G_C - G) (channel)
+    static constexpr int rQ = rKU + (CH ? NSLOT * szK : 0);        // Q or Q.exp(G)
+    static constexpr int rV = rQ + NSLOT * szK;                    // V block
+    static constexpr int rT = rV + NSLOT * szV;                    // T~
+    static constexpr int rM = rT + NSLOT * szT;                    // Gamma or P
+    static constexpr int rF = rM + (MODE != kAlphaNone ? NSLOT * szT : 0);
+    // exchange buffers (two chunks deep): S and U operands of each state owner
     static constexpr int NKS = DK / 32;
     static constexpr int FS = (int)sizeof(Frag<E>);
-    static constexpr int off_xS = NSLOT * slot;
-    static constexpr int off_xU = off_xS + 2 * 2 * NKS * kWave * FS;
-    static constexpr int bytes = off_xU + 2 * 2 * kWave * FS;
+    static constexpr int XSB = 2 * NKS * kWave * FS, XUB = 2 * kWave * FS;   // one chunk's worth
+    static constexpr int rxS = rF + NSLOT * szF;                   // [parity][owner][ks][lane]
+    static constexpr int rxU = rxS + 2 * XSB;                      // [parity][owner][lane]
+    static constexpr int bytes = rxU + 2 * XUB;
+    static constexpr int NWAVES = 5;
     // copy instructions per chunk
-    static constexpr int NOPS = (CH ? 3 : 2) * CopyCount<CK * DK * ES>::n + CopyCount<CK * BV * ES>::n +
-                                CopyCount<CK * CK * ES>::n * (MODE != kAlphaNone ? 2 : 1) +
-                                (FB ? CopyCount<(FB ? FB : 1)>::n : 0);
+    static constexpr int NCK = CopyCount<szK>::n, NCV = CopyCount<szV>::n, NCT = CopyCount<szT>::n;
+    static constexpr int NCF = FB ? CopyCount<(FB ? FB : 1)>::n : 0;
+    static constexpr int NOPS = (CH ? 3 : 2) * NCK + NCV + NCT * (MODE != kAlphaNone ? 2 : 1) + NCF;
     static_assert(NOPS < 64, "vmcnt range");
 };
 
 template <typename E, int DK, int CK, int MODE>
-__global__ __launch_bounds__(320) void chunk_scan_kernel(ScanParams p)
+__global__ __launch_bounds__(64 * 5) void chunk_scan_kernel(ScanParams p)
 {
     using LY = ScanLayout<E, DK, CK, MODE>;
-    constexpr int ES = LY::ES, BV = LY::BV;
+    using SK = Swz<E, DK>;
+    using SV = Swz<E, LY::BV>;
+    using ST = Swz<E, CK>;
+    constexpr int ES = LY::ES, BV = LY::BV, NSLOT = LY::NSLOT, AHEAD = LY::AHEAD;
     constexpr int NB = CK / 16, NKT = DK / 16, NKS = DK / 32;
     constexpr bool GATED = (MODE == kAlphaScalar), CH = LY::CH;
+    constexpr int szK = LY::szK, szV = LY::szV, szT = LY::szT, szF = LY::szF, FS = LY::FS;
+    constexpr int RBK = SK::RB, RBV = SV::RB, RBT = ST::RB;
     constexpr WsLayout WL = ws_layout(ES, DK, CK, MODE);
+    static_assert(sizeof(E) == 2 || CK == 16, "fp32 operands run 16-token steps");
     extern __shared__ __align__(16) unsigned char smem[];
 
     // wave index as a scalar: the role branches below are wave-uniform
@@ -229,74 +226,151 @@ __global__ __launch_bounds__(320) void chunk_scan_kernel(ScanParams p)
     if (p.total % 8 == 0) lid = (blockIdx.x % 8) * (p.total / 8) + blockIdx.x / 8;
     const int bh = lid / p.NVB, vb = lid % p.NVB;
     const int v0 = vb * BV;
+    const int NC = p.NC;
 
-    struct Slot {
-        unsigned char *KX, *KU, *Q, *V, *T, *M;
-        float* F;
-    };
-    auto slot = [&](int m) {
-        unsigned char* b = smem + (m % LY::NSLOT) * LY::slot;
-        Slot s;
-        s.KX = b + LY::s_KX;
-        s.KU = CH ? b + LY::s_KU : b + LY::s_KX;
-        s.Q = b + LY::s_Q;
-        s.V = b + LY::s_V;
-        s.T = b + LY::s_T;
-        s.M = b + LY::s_M;
-        s.F = reinterpret_cast<float*>(b + LY::s_F);
-        return s;
-    };
-    Frag<E>* xS = reinterpret_cast<Frag<E>*>(smem + LY::off_xS);   // [buf][owner][ks][lane]
-    Frag<E>* xU = reinterpret_cast<Frag<E>*>(smem + LY::off_xU);   // [buf][owner][lane]
+    // per-lane LDS offsets shared by the readers
+    // K / Q operand: row c16 (+16 tt), key channels 32 ks + 8 g4 .. +7
+    int oKQ[NKS], oKQh[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        oKQ[ks] = SK::off(c16, 32 * ks + 8 * g4);
+        oKQh[ks] = sizeof(E) == 4 ? SK::off(c16, 32 * ks + 8 * g4 + 4) : 0;
+    }
+    // T~ (and channel P) operand: row c16 (+16 tt), memory columns 8 g4 ..
+    // (CK = 16: 4 g4 ..)
+    const int oT = ST::off(c16, (CK == 32 ? 8 : 4) * g4);
 
     if (w < 2) {
         // ===================================================== state owners
         const int vw = v0 + 16 * w;
-        f32x4 sT[NKT];   // S^T[16a + 4g + e][v = vw + c16]
+        // transposing reads of K' (per dk tile a): address lane (g, i) names
+        // token 4g + i/4 (+16 p), key channels 32ks + 4pa + 8(i%4) .. +3
+        int oKt[NKT];
+#pragma unroll
+        for (int a = 0; a < NKT; ++a)
+            oKt[a] = SK::off(4 * g4 + (c16 >> 2), 32 * (a >> 1) + 4 * (a & 1) + 8 * (c16 & 3));
+        // V block, transposed: token 4g + i/4 (+16 tt), channels 16w + 4(i%4)
+        const int oVt = SV::off(4 * g4 + (c16 >> 2), 16 * w + 4 * (c16 & 3));
+        const int oXS = LY::rxS + (w * NKS * kWave + l) * FS;   // + parity XSB + ks 64 FS
+        const int oXU = LY::rxU + (w * kWave + l) * FS;         // + parity XUB
+
+        f32x4 sT[NKT];   // S^T[key 32ks + 8g + 4p + e][v = vw + c16], a = 2ks + p
 #pragma unroll
         for (int a = 0; a < NKT; ++a) {
             sT[a] = zero4();
             if (p.S0)
-                sT[a] = *reinterpret_cast<const f32x4*>(p.S0 + ((size_t)bh * p.DV + vw + c16) * DK + 16 * a + 4 * g4);
+                sT[a] = *reinterpret_cast<const f32x4*>(p.S0 + ((size_t)bh * p.DV + vw + c16) * DK +
+                                                       32 * (a >> 1) + 8 * g4 + 4 * (a & 1));
         }
-        auto own = [&](int m) {
-            const Slot s = slot(m);
+
+        // operands of one chunk, read from its slot
+        struct In {
+            Frag<E> kx[NB][NKS];      // K rows (X = K S^T)
+            Frag<E> kt[NKT];          // K'^T, tokens 0-31 (state update)
+            Frag16<E> kt16[NKT];      //   tokens 0-15 (16-token steps)
+            Frag<E> tf[NB];           // T~ rows
+            Frag16<E> tf16;
+            s16x4 vraw[NB];           // V^T (bf16)
+            f32x4 vv[NB];             // V^T (fp32)
+            f32x4 gm[NB], dc[NB];     // gamma, exp(g_C - g) per token
+            f32x4 dS[NKT];            // decay of the state rows
+        };
+        auto load_in = [&](auto jc, In& in) {
+            constexpr int J = decltype(jc)::value;
+            constexpr int cK = LY::rK + J * szK, cKU = (CH ? LY::rKU : LY::rK) + J * szK;
+            constexpr int cV = LY::rV + J * szV, cT = LY::rT + J * szT, cF = LY::rF + J * szF;
+#pragma unroll
+            for (int tt = 0; tt < NB; ++tt)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) in.kx[tt][ks] = ld_frag<E, 0>(smem + cK + 16 * tt * RBK, oKQ[ks], oKQh[ks]);
+#pragma unroll
+            for (int tt = 0; tt < NB; ++tt) {
+                if constexpr (sizeof(E) == 2) {
+                    in.vraw[tt] = ld_tr16<0>(smem + cV + 16 * tt * RBV, oVt);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        in.vv[tt][q] = ldf<0>(smem + cV, SV::off(16 * tt + 4 * g4 + q, 16 * w + c16));
+                }
+                in.gm[tt] = GATED ? ldf4<0>(smem + cF + 64 * tt, 16 * g4) : f32x4{1.f, 1.f, 1.f, 1.f};
+                in.dc[tt] = GATED ? ldf4<0>(smem + cF + 4 * CK + 64 * tt, 16 * g4) : f32x4{1.f, 1.f, 1.f, 1.f};
+            }
+            if constexpr (NB == 2) {
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) in.tf[tt] = ld_frag<E, 0>(smem + cT + 16 * tt * RBT, oT, oT);
+            } else {
+                in.tf16 = ld_frag16<E, 0>(smem + cT, oT);
+            }
+            if constexpr (GATED) {
+                const float gC = ldf<8 * CK>(smem + cF, 0);
+#pragma unroll
+                for (int a = 0; a < NKT; ++a) in.dS[a] = f32x4{gC, gC, gC, gC};
+            } else if constexpr (CH) {
+#pragma unroll
+                for (int a = 0; a < NKT; ++a)
+                    in.dS[a] = ldf4<0>(smem + cF + 4 * (32 * (a >> 1) + 4 * (a & 1)), 32 * g4);
+            }
+#pragma unroll
+            for (int a = 0; a < NKT; ++a) {
+                if constexpr (sizeof(E) == 2) {
+                    const s16x4 k0 = ld_tr16<0>(smem + cKU, oKt[a]);
+                    if constexpr (NB == 2) {
+                        const s16x4 k1 = ld_tr16<16 * RBK>(smem + cKU, oKt[a]);
+                        const u32x2 a0 = __builtin_bit_cast(u32x2, k0), a1 = __builtin_bit_cast(u32x2, k1);
+                        in.kt[a].v = __builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y});
+                    } else {
+                        in.kt16[a].v = k0;
+                    }
+                } else {
+                    // fp32: lane (g, r) reads tokens 4g + q (+16) of key channel
+                    // 32ks + 4pa + 8(r/4) + r%4 one by one
+                    const int kc = 32 * (a >> 1) + 4 * (a & 1) + 8 * (c16 >> 2) + (c16 & 3);
+                    f32x4 lo, hi;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        lo[q] = ldf<0>(smem + cKU, SK::off(4 * g4 + q, kc));
+                        if constexpr (NB == 2) hi[q] = ldf<0>(smem + cKU, SK::off(16 + 4 * g4 + q, kc));
+                    }
+                    if constexpr (NB == 2) { in.kt[a].lo = lo; in.kt[a].hi = hi; }
+                    else in.kt16[a].v = lo;
+                }
+            }
+        };
+        // chunk m, from slot J
+        auto own = [&](auto jc, int m) {
+            constexpr int J = decltype(jc)::value;
+            In in;
+            load_in(jc, in);
+            sched_fence();
+            constexpr int pS = (J & 1) * LY::XSB, pU = (J & 1) * LY::XUB;   // m & 1 == J & 1
+            // ---- S as an operand, published for the output wave
             Frag<E> sop[NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 frag_of_tiles(sop[ks], sT[2 * ks], sT[2 * ks + 1]);
-                xS[(((m & 1) * 2 + w) * NKS + ks) * kWave + l] = sop[ks];
+                *reinterpret_cast<Frag<E>*>(smem + oXS + pS + ks * kWave * FS) = sop[ks];
             }
-            // X = K S^T and R = V - diag(gamma) X: token 16tt + 4g + e, channel c16
+            // ---- X = K S^T, R = V - diag(gamma) X (token 16tt + 4g + e, channel c16)
             f32x4 r[NB];
 #pragma unroll
             for (int tt = 0; tt < NB; ++tt) {
                 f32x4 x = zero4();
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) mma(x, ldfrag_pair_swz<E, DK>(s.KX, 16 * tt, 32 * ks), sop[ks]);
-                const f32x4 vv = ld_tr<E, BV>(s.V, 16 * tt, 16 * w);
-                const f32x4 gm = GATED ? *reinterpret_cast<const f32x4*>(s.F + 16 * tt + 4 * g4)
-                                       : f32x4{1.f, 1.f, 1.f, 1.f};
+                for (int ks = 0; ks < NKS; ++ks) mma(x, in.kx[tt][ks], sop[ks]);
+                const f32x4 vv = sizeof(E) == 2 ? unpack4(in.vraw[tt]) : in.vv[tt];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) r[tt][e] = vv[e] - gm[e] * x[e];
+                for (int e = 0; e < 4; ++e) r[tt][e] = vv[e] - in.gm[tt][e] * x[e];
             }
-            // decay of the state over the chunk
-            if (GATED) {
-                const float gC = s.F[2 * CK];
+            // ---- decay of the state over the chunk
+            if constexpr (GATED || CH) {
 #pragma unroll
                 for (int a = 0; a < NKT; ++a)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) sT[a][e] *= gC;
-            } else if (CH) {
-#pragma unroll
-                for (int a = 0; a < NKT; ++a) {
-                    const f32x4 ec = *reinterpret_cast<const f32x4*>(s.F + 16 * a + 4 * g4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sT[a][e] *= ec[e];
-                }
+                    for (int e = 0; e < 4; ++e) sT[a][e] *= in.dS[a][e];
             }
-            // U = T~ R (published for the output wave), then
-            // S^T += K'^T (dec . U), K' = K (channel: K . exp(G_C - G), dec = 1)
+            // ---- U = T~ R (published), then S^T += K'^T (dec . U)
+            Frag<E> uop;
+            Frag16<E> uop16;
             if constexpr (NB == 2) {
                 Frag<E> rop;
                 frag_of_tiles(rop, r[0], r[1]);
@@ -304,135 +378,154 @@ __global__ __launch_bounds__(320) void chunk_scan_kernel(ScanParams p)
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
                     u[tt] = zero4();
-                    mma(u[tt], ldfrag_pair_swz<E, CK>(s.T, 16 * tt, 0), rop);
+                    mma(u[tt], in.tf[tt], rop);
                 }
-                Frag<E> uop;
                 frag_of_tiles(uop, u[0], u[1]);
-                xU[((m & 1) * 2 + w) * kWave + l] = uop;
-                if (GATED) {
+                *reinterpret_cast<Frag<E>*>(smem + oXU + pU) = uop;
+                if constexpr (GATED) {
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-                        const f32x4 dc = *reinterpret_cast<const f32x4*>(s.F + CK + 16 * tt + 4 * g4);
+                    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) u[tt][e] *= dc[e];
-                    }
+                        for (int e = 0; e < 4; ++e) u[tt][e] *= in.dc[tt][e];
                     frag_of_tiles(uop, u[0], u[1]);
-                }
-#pragma unroll
-                for (int a = 0; a < NKT; ++a) {
-                    Frag<E> kt;
-                    if constexpr (sizeof(E) == 2) {
-                        s16x4 k0, k1;
-                        ld_tr<E, DK>(s.KU, 0, 16 * a, &k0);
-                        ld_tr<E, DK>(s.KU, 16, 16 * a, &k1);
-                        const u32x2 a0 = __builtin_bit_cast(u32x2, k0), a1 = __builtin_bit_cast(u32x2, k1);
-                        kt.v = __builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y});
-                    } else {
-                        kt.lo = ld_tr<E, DK>(s.KU, 0, 16 * a);
-                        kt.hi = ld_tr<E, DK>(s.KU, 16, 16 * a);
-                    }
-                    mma(sT[a], kt, uop);
                 }
             } else {
                 Frag16<E> rop;
                 frag16_of_tile(rop, r[0]);
                 f32x4 u = zero4();
-                mma16(u, ldfrag16_swz<E, CK>(s.T, 0, 0), rop);
-                Frag16<E> uop;
-                frag16_of_tile(uop, u);
-                *reinterpret_cast<Frag16<E>*>(xU + ((m & 1) * 2 + w) * kWave + l) = uop;
-                if (GATED) {
-                    const f32x4 dc = *reinterpret_cast<const f32x4*>(s.F + CK + 4 * g4);
+                mma16(u, in.tf16, rop);
+                frag16_of_tile(uop16, u);
+                *reinterpret_cast<Frag16<E>*>(smem + oXU + pU) = uop16;
+                if constexpr (GATED) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) u[e] *= dc[e];
-                    frag16_of_tile(uop, u);
+                    for (int e = 0; e < 4; ++e) u[e] *= in.dc[0][e];
+                    frag16_of_tile(uop16, u);
                 }
+            }
 #pragma unroll
-                for (int a = 0; a < NKT; ++a) {
-                    Frag16<E> kt;
-                    if constexpr (sizeof(E) == 2) {
-                        ld_tr<E, DK>(s.KU, 0, 16 * a, &kt.v);
-                    } else {
-                        kt.v = ld_tr<E, DK>(s.KU, 0, 16 * a);
-                    }
-                    mma16(sT[a], kt, uop);
-                }
+            for (int a = 0; a < NKT; ++a) {
+                if constexpr (NB == 2) mma(sT[a], in.kt[a], uop);
+                else mma16(sT[a], in.kt16[a], uop16);
             }
         };
         step_barrier();
-        for (int s = 0; s <= p.NC; ++s) {
-            if (s < p.NC) own(s);
-            step_barrier();
+        for (int s0 = 0; s0 <= NC; s0 += NSLOT) {
+            auto step = [&](auto jc) {
+                constexpr int J = decltype(jc)::value;
+                const int s = s0 + J;
+                if (s <= NC) {
+                    if (s < NC) own(jc, s);
+                    step_barrier();
+                }
+            };
+            StaticFor<0, NSLOT>::run(step);
         }
         if (p.S_final) {
 #pragma unroll
             for (int a = 0; a < NKT; ++a)
-                *reinterpret_cast<f32x4*>(p.S_final + ((size_t)bh * p.DV + vw + c16) * DK + 16 * a + 4 * g4) = sT[a];
+                *reinterpret_cast<f32x4*>(p.S_final + ((size_t)bh * p.DV + vw + c16) * DK + 32 * (a >> 1) +
+                                          8 * g4 + 4 * (a & 1)) = sT[a];
         }
     } else if (w < 4) {
         // ===================================================== output waves
         const int c = w - 2, vw = v0 + 16 * c;
         E* og = reinterpret_cast<E*>(p.o) + (size_t)bh * p.L * p.DV;
-        auto out = [&](int m) {
-            const Slot s = slot(m);
+        const int oXS = LY::rxS + (c * NKS * kWave + l) * FS;
+        const int oXU = LY::rxU + (c * kWave + l) * FS;
+        // Gamma tile (rb, ib): row c16 (+16 rb), tokens 16ib + 4g .. +3
+        int oG[NB];
+#pragma unroll
+        for (int ib = 0; ib < NB; ++ib) oG[ib] = ST::off(c16, col_of_tok(CK, 16 * ib + 4 * g4));
+
+        auto out = [&](auto jc, int m) {
+            constexpr int J = decltype(jc)::value;
+            constexpr int cK = LY::rK + J * szK, cQ = LY::rQ + J * szK;
+            constexpr int cM = LY::rM + J * szT, cF = LY::rF + J * szF;
+            constexpr int pS = (J & 1) * LY::XSB, pU = (J & 1) * LY::XUB;   // m & 1 == J & 1
             const int t0 = m * CK, valid = min(CK, p.L - t0);
+            // ---- reads
             Frag<E> sop[NKS];
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) sop[ks] = xS[(((m & 1) * 2 + c) * NKS + ks) * kWave + l];
-            Frag<E> qf[NB][NKS];
+            for (int ks = 0; ks < NKS; ++ks) sop[ks] = *reinterpret_cast<const Frag<E>*>(smem + oXS + pS + ks * kWave * FS);
+            Frag<E> qf[NB][NKS], kf[NB][NKS];
 #pragma unroll
             for (int tt = 0; tt < NB; ++tt)
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) qf[tt][ks] = ldfrag_pair_swz<E, DK>(s.Q, 16 * tt, 32 * ks);
-            // inter-chunk part: O^T = S Q^T, lane holds O[16tt + c16][vw + 4g + e]
+                for (int ks = 0; ks < NKS; ++ks) {
+                    qf[tt][ks] = ld_frag<E, 0>(smem + cQ + 16 * tt * RBK, oKQ[ks], oKQh[ks]);
+                    if constexpr (!CH) kf[tt][ks] = ld_frag<E, 0>(smem + cK + 16 * tt * RBK, oKQ[ks], oKQh[ks]);
+                }
+            f32x4 gmask[NB][NB];
+            Frag<E> pf[NB];
+            Frag16<E> pf16;
+            if constexpr (CH) {
+                if constexpr (NB == 2) {
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) pf[tt] = ld_frag<E, 0>(smem + cM + 16 * tt * RBT, oT, oT);
+                } else {
+                    pf16 = ld_frag16<E, 0>(smem + cM, oT);
+                }
+            } else if constexpr (GATED) {
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+                    for (int ib = 0; ib <= rb; ++ib) gmask[rb][ib] = ld_4f<E, 0>(smem + cM + 16 * rb * RBT, oG[ib]);
+            }
+            float gq[NB];
+#pragma unroll
+            for (int tt = 0; tt < NB; ++tt) gq[tt] = GATED ? ldf<0>(smem + cF + 64 * tt, 4 * c16) : 1.f;
+            Frag<E> uop;
+            Frag16<E> uop16;
+            if constexpr (NB == 2) uop = *reinterpret_cast<const Frag<E>*>(smem + oXU + pU);
+            else uop16 = *reinterpret_cast<const Frag16<E>*>(smem + oXU + pU);
+            sched_fence();
+            // ---- inter-chunk part: O^T = S Q^T, lane holds O[16tt + c16][vw + 4g + e]
             f32x4 oi[NB];
 #pragma unroll
             for (int tt = 0; tt < NB; ++tt) {
                 oi[tt] = zero4();
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) mma(oi[tt], sop[ks], qf[tt][ks]);
-                if (GATED) {
-                    const float gq = s.F[16 * tt + c16];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) oi[tt][e] *= gq;
-                }
             }
-            // masked score tile (rb, ib): lane holds P[16rb + c16][16ib + 4g + e]
+            // ---- masked score tile (rb, ib): lane holds P[16rb + c16][16ib + 4g + e]
             auto score = [&](int rb, int ib) {
                 f32x4 acc = zero4();
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    mma(acc, ldfrag_pair_swz<E, DK>(s.KX, 16 * ib, 32 * ks), qf[rb][ks]);
-                const int r = 16 * rb + c16, i0 = 16 * ib + 4 * g4;
-                if (GATED) {
-                    const f32x4 gm = ld4_swz<E, CK>(s.M, r, i0);
+                for (int ks = 0; ks < NKS; ++ks) mma(acc, kf[ib][ks], qf[rb][ks]);
+                if constexpr (GATED) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] *= gm[e];
+                    for (int e = 0; e < 4; ++e) acc[e] *= gmask[rb][ib][e];
                 } else {
+                    const int r = 16 * rb + c16, i0 = 16 * ib + 4 * g4;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc[e] = (r >= i0 + e) ? acc[e] : 0.f;
                 }
                 return acc;
             };
-            // intra-chunk part: O^T += U^T P^T
-            if constexpr (NB == 2) {
-                Frag<E> pf[2];
-                if constexpr (CH) {
-                    pf[0] = ldfrag_pair_swz<E, CK>(s.M, 0, 0);
-                    pf[1] = ldfrag_pair_swz<E, CK>(s.M, 16, 0);
-                } else {
+            if constexpr (!CH) {
+                if constexpr (NB == 2) {
                     frag_of_tiles(pf[0], score(0, 0), zero4());
                     frag_of_tiles(pf[1], score(1, 0), score(1, 1));
+                } else {
+                    frag16_of_tile(pf16, score(0, 0));
                 }
-                const Frag<E> uop = xU[((m & 1) * 2 + c) * kWave + l];
+            }
+#pragma unroll
+            for (int tt = 0; tt < NB; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) oi[tt][e] *= gq[tt];
+            // ---- intra-chunk part: O^T += U^T P^T
+            if constexpr (NB == 2) {
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) mma(oi[tt], uop, pf[tt]);
             } else {
-                Frag16<E> pf;
-                if constexpr (CH) pf = ldfrag16_swz<E, CK>(s.M, 0, 0);
-                else frag16_of_tile(pf, score(0, 0));
-                const Frag16<E> uop = *reinterpret_cast<const Frag16<E>*>(xU + ((m & 1) * 2 + c) * kWave + l);
-                mma16(oi[0], uop, pf);
+                // own accumulator: fed straight into a 16x16x16 product as its
+                // accumulator input, the 16x16x32 result above was read before
+                // all its rows were written (gfx950, this compiler)
+                f32x4 oin = zero4();
+                mma16(oin, uop16, pf16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) oi[0][e] += oin[e];
             }
 #pragma unroll
             for (int tt = 0; tt < NB; ++tt) {
@@ -442,49 +535,125 @@ __global__ __launch_bounds__(320) void chunk_scan_kernel(ScanParams p)
             }
         };
         step_barrier();
-        for (int s = 0; s <= p.NC; ++s) {
-            if (s >= 1) out(s - 1);
-            step_barrier();
+        for (int s0 = 0; s0 <= NC; s0 += NSLOT) {
+            // step s works on chunk s - 1, in slot (s - 1) % NSLOT
+            auto step = [&](auto jc) {
+                constexpr int J = decltype(jc)::value;
+                const int s = s0 + J;
+                if (s <= NC) {
+                    if (s >= 1) out(std::integral_constant<int, (J + NSLOT - 1) % NSLOT>{}, s - 1);
+                    step_barrier();
+                }
+            };
+            StaticFor<0, NSLOT>::run(step);
         }
     } else {
         // ===================================================== copier
+        // Per-lane source offsets of one chunk's tiles, as for a full chunk:
+        // instruction j, lane l fills LDS bytes 1024 j + 16 l of the region,
+        // i.e. row b / RB, physical chunk (b % RB) / 16, which holds logical
+        // chunk physical ^ swz(row).
+        auto tile_off = [&](auto sw, int j, int gstride, int valid) {
+            using S = decltype(sw);
+            const int b = 1024 * j + 16 * l;
+            const int row = b / S::RB, pch = (b % S::RB) / 16;
+            return (uint32_t)(min(row, valid - 1) * gstride + ((pch ^ S::swz(row)) << 4));
+        };
+        uint32_t offK[LY::NCK], offV[LY::NCV], offT[LY::NCT];
+#pragma unroll
+        for (int j = 0; j < LY::NCK; ++j) offK[j] = tile_off(SK{}, j, DK * ES, CK);
+#pragma unroll
+        for (int j = 0; j < LY::NCV; ++j) offV[j] = tile_off(SV{}, j, p.DV * ES, CK);
+#pragma unroll
+        for (int j = 0; j < LY::NCT; ++j) offT[j] = tile_off(ST{}, j, CK * ES, CK);
+
         const unsigned char* kb = static_cast<const unsigned char*>(p.k);
         const unsigned char* qb = static_cast<const unsigned char*>(p.q);
-        const unsigned char* vbase = static_cast<const unsigned char*>(p.v);
-        auto issue = [&](int m) {
-            const Slot s = slot(m);
-            const int t0 = m * CK, valid = min(CK, p.L - t0);
-            const unsigned char* rec = p.ws + ((size_t)bh * p.NC + m) * WL.bytes;
-            const size_t row0 = (size_t)bh * p.L + t0;
-            if constexpr (CH) {
-                copy_tile<E, DK, CK>(s.KX, rec + WL.KG, DK * ES, CK);
-                copy_tile<E, DK, CK>(s.KU, rec + WL.KD, DK * ES, CK);
-                copy_tile<E, DK, CK>(s.Q, rec + WL.QG, DK * ES, CK);
-            } else {
-                copy_tile<E, DK, CK>(s.KX, kb + row0 * DK * ES, DK * ES, valid);
-                copy_tile<E, DK, CK>(s.Q, qb + row0 * DK * ES, DK * ES, valid);
+        const unsigned char* vbs = static_cast<const unsigned char*>(p.v);
+        // LDS destinations as 32-bit LDS addresses (no generic-pointer round trip)
+        const uint32_t sbase = (uint32_t)(uintptr_t)(lds_void_t*)smem;
+        // one region's copies: NI instructions of 1 KiB (the last may be partial)
+        auto copy = [&](int dst, const unsigned char* src, const uint32_t* off, auto ni, int total) {
+            constexpr int NI = decltype(ni)::value;
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                if (total % 1024 == 0 || 1024 * j + 16 * l < total)
+                    __builtin_amdgcn_global_load_lds((const glb_void_t*)(src + off[j]),
+                                                     (lds_void_t*)(uintptr_t)(sbase + (uint32_t)(dst + 1024 * j)), 16, 0, 0);
             }
-            copy_tile<E, BV, CK>(s.V, vbase + (row0 * p.DV + v0) * ES, (size_t)p.DV * ES, valid);
-            copy_tile<E, CK, CK>(s.T, rec + WL.T, CK * ES, CK);
-            if constexpr (MODE != kAlphaNone) copy_tile<E, CK, CK>(s.M, rec + WL.M, CK * ES, CK);
-            if constexpr (LY::FB > 0) copy_flat<LY::FB>(reinterpret_cast<unsigned char*>(s.F), rec + WL.F);
         };
-        issue(0);
-        if (p.NC > 1) {
-            issue(1);
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS) : "memory");   // chunk 0 landed
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
-        step_barrier();
-        for (int s = 0; s <= p.NC; ++s) {
-            if (s + 2 < p.NC) {
-                issue(s + 2);
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS) : "memory");   // chunk s + 1 landed
-            } else {
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        auto issue = [&](auto jc, int m) {
+            constexpr int J = decltype(jc)::value;
+            const int t0 = m * CK, valid = min(CK, p.L - t0);
+            const unsigned char* rec = p.ws + ((size_t)bh * NC + m) * WL.bytes;
+            const size_t row0 = (size_t)bh * p.L + t0;
+            using NK = std::integral_constant<int, LY::NCK>;
+            using NV = std::integral_constant<int, LY::NCV>;
+            using NT = std::integral_constant<int, LY::NCT>;
+            if constexpr (CH) {
+                copy(LY::rK + J * szK, rec + WL.KG, offK, NK{}, szK);
+                copy(LY::rKU + J * szK, rec + WL.KD, offK, NK{}, szK);
+                copy(LY::rQ + J * szK, rec + WL.QG, offK, NK{}, szK);
             }
-            step_barrier();
+            if (valid == CK) {
+                if constexpr (!CH) {
+                    copy(LY::rK + J * szK, kb + row0 * DK * ES, offK, NK{}, szK);
+                    copy(LY::rQ + J * szK, qb + row0 * DK * ES, offK, NK{}, szK);
+                }
+                copy(LY::rV + J * szV, vbs + (row0 * p.DV + v0) * ES, offV, NV{}, szV);
+            } else {
+                // last, partial chunk: rows past the end repeat the last row
+                uint32_t rK[LY::NCK], rV[LY::NCV];
+#pragma unroll
+                for (int j = 0; j < LY::NCK; ++j) rK[j] = tile_off(SK{}, j, DK * ES, valid);
+#pragma unroll
+                for (int j = 0; j < LY::NCV; ++j) rV[j] = tile_off(SV{}, j, p.DV * ES, valid);
+                if constexpr (!CH) {
+                    copy(LY::rK + J * szK, kb + row0 * DK * ES, rK, NK{}, szK);
+                    copy(LY::rQ + J * szK, qb + row0 * DK * ES, rK, NK{}, szK);
+                }
+                copy(LY::rV + J * szV, vbs + (row0 * p.DV + v0) * ES, rV, NV{}, szV);
+            }
+            copy(LY::rT + J * szT, rec + WL.T, offT, NT{}, szT);
+            if constexpr (MODE != kAlphaNone) copy(LY::rM + J * szT, rec + WL.M, offT, NT{}, szT);
+            if constexpr (LY::FB > 0) {
+#pragma unroll
+                for (int j = 0; j < LY::NCF; ++j) {
+                    if (LY::FB % 1024 == 0 || 1024 * j + 16 * l < LY::FB)
+                        __builtin_amdgcn_global_load_lds((const glb_void_t*)(rec + WL.F + 1024 * j + 16 * l),
+                                                         (lds_void_t*)(uintptr_t)(sbase + (uint32_t)(LY::rF + J * szF + 1024 * j)),
+                                                         16, 0, 0);
+                }
+            }
+        };
+        // wait until every chunk issued before the last one has landed
+        auto wait_prev = [&](bool more) {
+            if (more) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS) : "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        };
+        {
+            auto pro = [&](auto kc) {
+                constexpr int K = decltype(kc)::value;
+                if (K < NC) issue(kc, K);
+            };
+            StaticFor<0, AHEAD>::run(pro);
+        }
+        wait_prev(AHEAD - 1 < NC);   // chunks 0 .. AHEAD - 2 have landed
+        step_barrier();
+        // step s fills chunk s + AHEAD into slot (s + AHEAD) % NSLOT, then waits
+        // for chunk s + AHEAD - 1
+        for (int s0 = 0; s0 <= NC; s0 += NSLOT) {
+            auto step = [&](auto jc) {
+                constexpr int J = decltype(jc)::value;
+                const int s = s0 + J;
+                if (s <= NC) {
+                    const bool more = s + AHEAD < NC;
+                    if (more) issue(std::integral_constant<int, (J + AHEAD) % NSLOT>{}, s + AHEAD);
+                    wait_prev(more);
+                    step_barrier();
+                }
+            };
+            StaticFor<0, NSLOT>::run(step);
         }
     }
 }
@@ -503,7 +672,7 @@ static hipError_t launch_scan_t(const ChunkArgs& a)
     auto* kern = chunk_scan_kernel<E, DK, CK, MODE>;
     hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LY::bytes);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, dim3(BH * NVB), dim3(320), LY::bytes, a.stream, sp);
+    hipLaunchKernelGGL(kern, dim3(BH * NVB), dim3(64 * LY::NWAVES), LY::bytes, a.stream, sp);
     return hipGetLastError();
 }
 

@@ -195,7 +195,8 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
     wave_lds_fence();
     unit_lower_inverse<CK, LF>(Af, Tf, Tt);
 
-    // T~ = T diag(beta) (and Gamma) to the workspace, zero above the diagonal
+    // T~ = T diag(beta) (and Gamma) to the workspace, zero above the diagonal;
+    // 16-byte row vectors of memory columns c0.., four consecutive tokens at a time
     unsigned char* rec = p.ws + (size_t)cid * WL.bytes;
     E* Tg = reinterpret_cast<E*>(rec + WL.T);
     E* Mg = reinterpret_cast<E*>(rec + WL.M);
@@ -205,22 +206,22 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
         const int x = x0 + l;
         if (x < TV) {
             const int r = x / RV, c0 = (x % RV) * VE;
-            float tv[VE];
+            float tv[VE], mv[VE];
 #pragma unroll
             for (int q = 0; q < VE; q += 4) {
-                const f32x4 a = *reinterpret_cast<const f32x4*>(Tf + r * LF + c0 + q);
-                const f32x4 b = *reinterpret_cast<const f32x4*>(bs + c0 + q);
+                const int t = tok_of_col(CK, c0 + q);
+                const f32x4 a = *reinterpret_cast<const f32x4*>(Tf + r * LF + t);
+                const f32x4 b = *reinterpret_cast<const f32x4*>(bs + t);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) tv[q + e] = (c0 + q + e <= r) ? a[e] * b[e] : 0.f;
+                for (int e = 0; e < 4; ++e) tv[q + e] = (t + e <= r) ? a[e] * b[e] : 0.f;
+                if (GATED) {
+                    const f32x4 m = load4f(Ms + r * LM + t);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) mv[q + e] = (t + e <= r) ? m[e] : 0.f;
+                }
             }
             st16(Tg + r * CK + c0, Pack<E>::pack(tv));
-            if (GATED) {
-                float mv[VE];
-                Pack<E>::unpack(ld16(Ms + r * LM + c0), mv);
-#pragma unroll
-                for (int j = 0; j < VE; ++j) mv[j] = (c0 + j <= r) ? mv[j] : 0.f;
-                st16(Mg + r * CK + c0, Pack<E>::pack(mv));
-            }
+            if (GATED) st16(Mg + r * CK + c0, Pack<E>::pack(mv));
         }
     }
     if (GATED && l < CK) {
@@ -386,18 +387,22 @@ __global__ __launch_bounds__(256) void chunk_wy_channel_kernel(WyParams p)
     __syncthreads();
 
     // ---- T~ = T diag(beta) and P to the workspace, zero above the diagonal
+    // (columns in tok_of_col order)
     E* Tg = reinterpret_cast<E*>(rec + WL.T);
     E* Pg = reinterpret_cast<E*>(rec + WL.M);
     constexpr int CV = CK / VE;
     for (int idx = tid; idx < CK * CV; idx += 256) {
         const int r = idx / CV, c0 = (idx % CV) * VE;
         float x[VE], y[VE];
-        Pack<E>::unpack(ld16(Ps + r * LP + c0), y);
 #pragma unroll
-        for (int j = 0; j < VE; ++j) {
-            const int c = c0 + j;
-            x[j] = (c <= r) ? Tf[r * LF + c] * bs[c] : 0.f;
-            y[j] = (c <= r) ? y[j] : 0.f;
+        for (int q = 0; q < VE; q += 4) {
+            const int t = tok_of_col(CK, c0 + q);
+            const f32x4 pv = load4f(Ps + r * LP + t);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[q + e] = (t + e <= r) ? Tf[r * LF + t + e] * bs[t + e] : 0.f;
+                y[q + e] = (t + e <= r) ? pv[e] : 0.f;
+            }
         }
         st16(Tg + r * CK + c0, Pack<E>::pack(x));
         st16(Pg + r * CK + c0, Pack<E>::pack(y));

@@ -50,6 +50,15 @@ def test_no_internal_symbols_leak():
     assert not [n for n in ours if "gdr" in n and not n.startswith("gdr_")]
 
 
+def test_every_kernel_is_defined():
+    # a kernel whose host-side stub was dropped leaves an undefined symbol that
+    # only shows up when the library is loaded on a GPU machine
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", gdr.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert not [ln for ln in out.splitlines() if "gdr" in ln], out
+
+
 def test_version_and_status_strings(lib):
     assert gdr.gdr_abi_version() == 1
     for st in range(5):
