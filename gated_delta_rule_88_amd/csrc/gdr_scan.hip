@@ -310,6 +310,11 @@ __global__ __launch_bounds__(64 * 5) void chunk_scan_kernel(ScanParams p)
                 for (int a = 0; a < NKT; ++a)
                     in.dS[a] = ldf4<0>(smem + cF + 4 * (32 * (a >> 1) + 4 * (a & 1)), 32 * g4);
             }
+        };
+        // K'^T for the state update: read once the X products are issued
+        auto load_kt = [&](auto jc, In& in) {
+            constexpr int J = decltype(jc)::value;
+            constexpr int cKU = (CH ? LY::rKU : LY::rK) + J * szK;
 #pragma unroll
             for (int a = 0; a < NKT; ++a) {
                 if constexpr (sizeof(E) == 2) {
@@ -341,7 +346,6 @@ __global__ __launch_bounds__(64 * 5) void chunk_scan_kernel(ScanParams p)
             constexpr int J = decltype(jc)::value;
             In in;
             load_in(jc, in);
-            sched_fence();
             constexpr int pS = (J & 1) * LY::XSB, pU = (J & 1) * LY::XUB;   // m & 1 == J & 1
             // ---- S as an operand, published for the output wave
             Frag<E> sop[NKS];
@@ -350,16 +354,24 @@ __global__ __launch_bounds__(64 * 5) void chunk_scan_kernel(ScanParams p)
                 frag_of_tiles(sop[ks], sT[2 * ks], sT[2 * ks + 1]);
                 *reinterpret_cast<Frag<E>*>(smem + oXS + pS + ks * kWave * FS) = sop[ks];
             }
-            // ---- X = K S^T, R = V - diag(gamma) X (token 16tt + 4g + e, channel c16)
+            // ---- X = K S^T
+            f32x4 x[NB];
+#pragma unroll
+            for (int tt = 0; tt < NB; ++tt) {
+                x[tt] = zero4();
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) mma(x[tt], in.kx[tt][ks], sop[ks]);
+            }
+            sched_fence();
+            load_kt(jc, in);
+            sched_fence();
+            // ---- R = V - diag(gamma) X (token 16tt + 4g + e, channel c16)
             f32x4 r[NB];
 #pragma unroll
             for (int tt = 0; tt < NB; ++tt) {
-                f32x4 x = zero4();
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) mma(x, in.kx[tt][ks], sop[ks]);
                 const f32x4 vv = sizeof(E) == 2 ? unpack4(in.vraw[tt]) : in.vv[tt];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) r[tt][e] = vv[e] - in.gm[tt][e] * x[e];
+                for (int e = 0; e < 4; ++e) r[tt][e] = vv[e] - in.gm[tt][e] * x[tt][e];
             }
             // ---- decay of the state over the chunk
             if constexpr (GATED || CH) {

@@ -55,9 +55,9 @@ __device__ __forceinline__ Frag<E> gfrag(const E* base, int ld, int row0, int k0
 
 // (I + A)^{-1} for a strictly lower-triangular CK x CK block A (CK = 16 or
 // 32) held in LDS (row stride LF), by one wave.  Writes T row-major to Tf
-// and transposed to Tt (both stride LF).  Af, Tf, Tt belong to this wave.
+// (stride LF).  Af and Tf belong to this wave.
 template <int CK, int LF>
-__device__ __forceinline__ void unit_lower_inverse(const float* Af, float* Tf, float* Tt) {
+__device__ __forceinline__ void unit_lower_inverse(const float* Af, float* Tf) {
     constexpr int NB = CK / 16;
     const int l = lane_id(), g4 = l >> 4, c16 = l & 15;
     {
@@ -87,17 +87,18 @@ __device__ __forceinline__ void unit_lower_inverse(const float* Af, float* Tf, f
         if (g4 < NB) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) Tf[(16 * b + r) * LF + 16 * b + j] = t[r];
-#pragma unroll
-            for (int r = 0; r < 16; r += 4)
-                *reinterpret_cast<f32x4*>(Tt + (16 * b + j) * LF + 16 * b + r) =
-                    f32x4{t[r], t[r + 1], t[r + 2], t[r + 3]};
         }
     }
     wave_lds_fence();
     if constexpr (NB == 2) {
-        // Y = A_10 T_00 (lane: Y[4g + e][c]), then Z = T_11 Y, T_10 = -Z
+        // Y = A_10 T_00 (lane: Y[4g + e][c]), then Z = T_11 Y, T_10 = -Z;
+        // step e contracts over k = 4g + e: lane (g, c) supplies A_10[c][k]
+        // and T_00[k][c]
+        const f32x4 a10 = *reinterpret_cast<const f32x4*>(Af + (16 + c16) * LF + 4 * g4);
         f32x4 y = zero4();
-        mma_k16(y, Af, LF, 16, Tt, LF, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(a10[e], Tf[(4 * g4 + e) * LF + c16], y, 0, 0, 0);
         const f32x4 t11 = *reinterpret_cast<const f32x4*>(Tf + (16 + c16) * LF + 16 + 4 * g4);
         f32x4 z = zero4();
 #pragma unroll
@@ -111,14 +112,11 @@ __device__ __forceinline__ void unit_lower_inverse(const float* Af, float* Tf, f
 // Per-wave LDS scratch of chunk_wy_kernel.
 template <typename E, int CK>
 struct WyScratch {
-    static constexpr int VE = Vec<E>::n, ES = (int)sizeof(E);
+    static constexpr int VE = Vec<E>::n;
     static constexpr int LF = CK + 4;    // fp32 row stride
-    static constexpr int LM = CK + VE;   // row stride of the Gamma staging block
     static constexpr int off_A = 0;
     static constexpr int off_Tf = off_A + CK * LF * 4;
-    static constexpr int off_Tt = off_Tf + CK * LF * 4;
-    static constexpr int off_M = off_Tt + CK * LF * 4;
-    static constexpr int off_g = off_M + CK * LM * ES;
+    static constexpr int off_g = off_Tf + CK * LF * 4;
     static constexpr int off_b = off_g + CK * 4;
     static constexpr int bytes = (off_b + CK * 4 + 15) / 16 * 16;
 };
@@ -132,7 +130,7 @@ template <typename E, int DK, int CK, int MODE>
 __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
 {
     using SC = WyScratch<E, CK>;
-    constexpr int VE = SC::VE, LF = SC::LF, LM = SC::LM;
+    constexpr int VE = SC::VE, LF = SC::LF;
     constexpr int NB = CK / 16, NKS = DK / 32;
     constexpr bool GATED = (MODE == kAlphaScalar);
     constexpr WsLayout WL = ws_layout((int)sizeof(E), DK, CK, MODE);
@@ -148,8 +146,6 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
     unsigned char* sw = smem + w * SC::bytes;
     float* Af = reinterpret_cast<float*>(sw + SC::off_A);
     float* Tf = reinterpret_cast<float*>(sw + SC::off_Tf);
-    float* Tt = reinterpret_cast<float*>(sw + SC::off_Tt);
-    E* Ms = reinterpret_cast<E*>(sw + SC::off_M);
     float* gs = reinterpret_cast<float*>(sw + SC::off_g);
     float* bs = reinterpret_cast<float*>(sw + SC::off_b);
 
@@ -172,7 +168,7 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
     if (l < CK) { gs[l] = g; bs[l] = bt; }
     wave_lds_fence();
 
-    // Gram tiles -> A; the same exponentials give Gamma for the scan
+    // Gram tiles -> A
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
 #pragma unroll
@@ -188,12 +184,11 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
             for (int e = 0; e < 4; ++e) {
                 const float d = GATED ? __expf(fminf(gr[e] - gi, 0.f)) : 1.f;
                 Af[(r0 + e) * LF + i] = (r0 + e > i) ? br[e] * d * acc[e] : 0.f;
-                if (GATED) Ms[(r0 + e) * LM + i] = from_f32<E>((r0 + e >= i) ? d : 0.f);
             }
         }
     }
     wave_lds_fence();
-    unit_lower_inverse<CK, LF>(Af, Tf, Tt);
+    unit_lower_inverse<CK, LF>(Af, Tf);
 
     // T~ = T diag(beta) (and Gamma) to the workspace, zero above the diagonal;
     // 16-byte row vectors of memory columns c0.., four consecutive tokens at a time
@@ -215,9 +210,10 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) tv[q + e] = (t + e <= r) ? a[e] * b[e] : 0.f;
                 if (GATED) {
-                    const f32x4 m = load4f(Ms + r * LM + t);
+                    const float gr = gs[r];
+                    const f32x4 gt = *reinterpret_cast<const f32x4*>(gs + t);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) mv[q + e] = (t + e <= r) ? m[e] : 0.f;
+                    for (int e = 0; e < 4; ++e) mv[q + e] = (t + e <= r) ? __expf(fminf(gr - gt[e], 0.f)) : 0.f;
                 }
             }
             st16(Tg + r * CK + c0, Pack<E>::pack(tv));
@@ -248,8 +244,7 @@ struct WyChannelLayout {
     static constexpr int off_G = off_Q + CK * DKP * ES;
     static constexpr int off_A = off_G + CK * GP * 4;
     static constexpr int off_Tf = off_A + CK * LF * 4;
-    static constexpr int off_Tt = off_Tf + CK * LF * 4;
-    static constexpr int off_P = off_Tt + CK * LF * 4;
+    static constexpr int off_P = off_Tf + CK * LF * 4;
     static constexpr int off_b = off_P + CK * LP * ES;
     static constexpr int bytes = off_b + CK * 4;
 };
@@ -267,7 +262,6 @@ __global__ __launch_bounds__(256) void chunk_wy_channel_kernel(WyParams p)
     float* Gs = reinterpret_cast<float*>(smem + LY::off_G);
     float* Af = reinterpret_cast<float*>(smem + LY::off_A);
     float* Tf = reinterpret_cast<float*>(smem + LY::off_Tf);
-    float* Tt = reinterpret_cast<float*>(smem + LY::off_Tt);
     E* Ps = reinterpret_cast<E*>(smem + LY::off_P);
     float* bs = reinterpret_cast<float*>(smem + LY::off_b);
 
@@ -303,11 +297,16 @@ __global__ __launch_bounds__(256) void chunk_wy_channel_kernel(WyParams p)
     }
     if (tid < CK) bs[tid] = (tid < valid) ? p.beta[(size_t)bh * p.L + t0 + tid] : 0.f;
     __syncthreads();
-    // cumulative sum down each key channel
+    // cumulative sum down each key channel (the column is read whole first,
+    // so the reads are in flight together)
     for (int c = tid; c < DK; c += 256) {
-        float acc = 0.f;
+        float col[CK];
 #pragma unroll
-        for (int r = 0; r < CK; ++r) { acc += Gs[r * GP + c]; Gs[r * GP + c] = acc; }
+        for (int r = 0; r < CK; ++r) col[r] = Gs[r * GP + c];
+#pragma unroll
+        for (int r = 1; r < CK; ++r) col[r] += col[r - 1];
+#pragma unroll
+        for (int r = 0; r < CK; ++r) Gs[r * GP + c] = col[r];
     }
     __syncthreads();
 
@@ -383,7 +382,7 @@ __global__ __launch_bounds__(256) void chunk_wy_channel_kernel(WyParams p)
         }
     }
     __syncthreads();
-    if (w == 0) unit_lower_inverse<CK, LF>(Af, Tf, Tt);
+    if (w == 0) unit_lower_inverse<CK, LF>(Af, Tf);
     __syncthreads();
 
     // ---- T~ = T diag(beta) and P to the workspace, zero above the diagonal
