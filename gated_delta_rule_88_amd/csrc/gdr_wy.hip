@@ -28,6 +28,8 @@
 #include "gdr_device.h"
 #include "gdr_chunk.h"
 
+#include <algorithm>
+
 namespace gdr {
 
 namespace {
@@ -267,35 +269,64 @@ __global__ __launch_bounds__(256) void chunk_wy_channel_kernel(WyParams p)
 
     const int tid = threadIdx.x, l = lane_id(), g4 = l >> 4, c16 = l & 15;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int cid = blockIdx.x;
-    const int bh = cid / p.NC, n = cid % p.NC;
-    const int t0 = n * CK, valid = min(CK, p.L - t0);
-    const E* kc = reinterpret_cast<const E*>(p.k) + ((size_t)bh * p.L + t0) * DK;
-    const E* qc = reinterpret_cast<const E*>(p.q) + ((size_t)bh * p.L + t0) * DK;
-    const float* lac = p.log_alpha + ((size_t)bh * p.L + t0) * DK;
+
+    // Each workgroup walks chunks blockIdx.x, + gridDim.x, ...; the next
+    // chunk's K, Q, log alpha and beta are fetched into registers while the
+    // current one is worked on, so loads and compute overlap.
+    constexpr int RV = DK / VE, RF = DK / 4;
+    constexpr int NKV = (CK * RV + 255) / 256, NGV = (CK * RF + 255) / 256;
+    u32x4 kr[NKV], qr[NKV];
+    f32x4 gr[NGV];
+    float br = 0.f;
+    auto fetch = [&](int cid) {
+        const int bh = cid / p.NC, n = cid % p.NC;
+        const int t0 = n * CK, valid = min(CK, p.L - t0);
+        const E* kc = reinterpret_cast<const E*>(p.k) + ((size_t)bh * p.L + t0) * DK;
+        const E* qc = reinterpret_cast<const E*>(p.q) + ((size_t)bh * p.L + t0) * DK;
+        const float* lac = p.log_alpha + ((size_t)bh * p.L + t0) * DK;
+#pragma unroll
+        for (int j = 0; j < NKV; ++j) {
+            const int i = tid + 256 * j, r = i / RV, c = (i % RV) * VE;
+            kr[j] = u32x4{0u, 0u, 0u, 0u};
+            qr[j] = u32x4{0u, 0u, 0u, 0u};
+            if (i < CK * RV && r < valid) {
+                kr[j] = ld16(kc + (size_t)r * DK + c);
+                qr[j] = ld16(qc + (size_t)r * DK + c);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NGV; ++j) {
+            const int i = tid + 256 * j, r = i / RF, c = (i % RF) * 4;
+            gr[j] = zero4();
+            if (i < CK * RF && r < valid) gr[j] = *reinterpret_cast<const f32x4*>(lac + (size_t)r * DK + c);
+        }
+        br = (tid < valid) ? p.beta[(size_t)bh * p.L + t0 + tid] : 0.f;
+    };
+    if ((int)blockIdx.x < p.total) fetch(blockIdx.x);
+    for (int cid = blockIdx.x; cid < p.total; cid += gridDim.x) {
     unsigned char* rec = p.ws + (size_t)cid * WL.bytes;
 
     // ---- stage K, Q and log alpha (floored; zero past the end), beta
-    constexpr int RV = DK / VE;
-    for (int i = tid; i < CK * RV; i += 256) {
-        const int r = i / RV, c = (i % RV) * VE;
-        u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
-        if (r < valid) { kv = ld16(kc + (size_t)r * DK + c); qv = ld16(qc + (size_t)r * DK + c); }
-        st16(Ks + r * DKP + c, kv);
-        st16(Qs + r * DKP + c, qv);
+#pragma unroll
+    for (int j = 0; j < NKV; ++j) {
+        const int i = tid + 256 * j, r = i / RV, c = (i % RV) * VE;
+        if (i < CK * RV) {
+            st16(Ks + r * DKP + c, kr[j]);
+            st16(Qs + r * DKP + c, qr[j]);
+        }
     }
-    constexpr int RF = DK / 4;
-    for (int i = tid; i < CK * RF; i += 256) {
-        const int r = i / RF, c = (i % RF) * 4;
-        f32x4 x = zero4();
-        if (r < valid) {
-            x = *reinterpret_cast<const f32x4*>(lac + (size_t)r * DK + c);
+#pragma unroll
+    for (int j = 0; j < NGV; ++j) {
+        const int i = tid + 256 * j, r = i / RF, c = (i % RF) * 4;
+        if (i < CK * RF) {
+            f32x4 x = gr[j];
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = fmaxf(x[e], kChannelLogAlphaMin);
+            *reinterpret_cast<f32x4*>(Gs + r * GP + c) = x;
         }
-        *reinterpret_cast<f32x4*>(Gs + r * GP + c) = x;
     }
-    if (tid < CK) bs[tid] = (tid < valid) ? p.beta[(size_t)bh * p.L + t0 + tid] : 0.f;
+    if (tid < CK) bs[tid] = br;
+    if (cid + (int)gridDim.x < p.total) fetch(cid + gridDim.x);
     __syncthreads();
     // cumulative sum down each key channel (the column is read whole first,
     // so the reads are in flight together)
@@ -406,9 +437,23 @@ __global__ __launch_bounds__(256) void chunk_wy_channel_kernel(WyParams p)
         st16(Tg + r * CK + c0, Pack<E>::pack(x));
         st16(Pg + r * CK + c0, Pack<E>::pack(y));
     }
+    __syncthreads();   // the LDS is restaged for the next chunk
+    }
 }
 
 // ------------------------------------------------------------------ host side
+static int compute_units()
+{
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+    }
+    return n;
+}
+
 template <typename K>
 static hipError_t launch_with_lds(K* kern, int grid, int lds, hipStream_t stream, const WyParams& wp)
 {
@@ -427,7 +472,10 @@ static hipError_t launch_wy_t(const ChunkArgs& a)
     if (a.mode == kAlphaChannel) {
         using LY = WyChannelLayout<E, DK, CK>;
         static_assert(LY::bytes <= 160 * 1024, "LDS budget");
-        return launch_with_lds(chunk_wy_channel_kernel<E, DK, CK>, wp.total, LY::bytes, a.stream, wp);
+        // persistent: as many workgroups as fit the CUs at once
+        const int per_cu = (160 * 1024) / LY::bytes;
+        const int grid = std::min(wp.total, per_cu * compute_units());
+        return launch_with_lds(chunk_wy_channel_kernel<E, DK, CK>, grid, LY::bytes, a.stream, wp);
     }
     constexpr int bytes = 4 * WyScratch<E, CK>::bytes;
     static_assert(bytes <= 160 * 1024, "LDS budget");
