@@ -19,7 +19,7 @@
 //
 // Rows of S (value channels) evolve independently given K, beta and alpha,
 // which is what lets the value dimension be split across workgroups and
-// waves.  Five waves, one barrier per chunk step, four rotating LDS slots:
+// waves.  Six waves, one barrier per chunk step, four rotating LDS slots:
 //   waves 0, 1  (state owners)  each holds the state of 16 value channels
 //               (d_k x 16 fp32) in registers; for chunk n it publishes S as
 //               an MFMA operand, forms X, R, U (published too) and the next
@@ -27,9 +27,10 @@
 //   waves 2, 3  (output waves)  for chunk n - 1, from the published S and U:
 //               the inter-chunk output diag(gamma) Q S^T, the masked score
 //               block P (MFMA), P U, and the store of o.
-//   wave 4      (copier)        direct global->LDS copies of chunk n + 2 (K,
-//               Q, the V block, T~, Gamma or P, the decay factors), 16 bytes
-//               per lane, then waits until chunk n + 1 has landed.
+//   waves 4, 5  (copiers)       direct global->LDS copies of chunk n + 2 (K,
+//               Q, the V block, T~, Gamma or P, the decay factors; the two
+//               split the regions), 16 bytes per lane, then wait until chunk
+//               n + 1 has landed.
 // Every product is v_mfma_f32_16x16x32_bf16 (fp32: 16x16x4f32) in NT form;
 // result tiles feed the next product straight from registers (tile-pair
 // operands, gdr_device.h).
@@ -193,16 +194,19 @@ struct ScanLayout {
     static constexpr int rxS = rF + NSLOT * szF;                   // [parity][owner][ks][lane]
     static constexpr int rxU = rxS + 2 * XSB;                      // [parity][owner][lane]
     static constexpr int bytes = rxU + 2 * XUB;
-    static constexpr int NWAVES = 5;
-    // copy instructions per chunk
+    static constexpr int NWAVES = 6;
+    // copy instructions per chunk.  Copier 0 takes K (and K.exp(G_C - G)) and
+    // the decay factors, plus V and T~ unless alpha is per channel; copier 1
+    // the rest, which keeps the two within a few KiB of each other.
     static constexpr int NCK = CopyCount<szK>::n, NCV = CopyCount<szV>::n, NCT = CopyCount<szT>::n;
     static constexpr int NCF = FB ? CopyCount<(FB ? FB : 1)>::n : 0;
-    static constexpr int NOPS = (CH ? 3 : 2) * NCK + NCV + NCT * (MODE != kAlphaNone ? 2 : 1) + NCF;
-    static_assert(NOPS < 64, "vmcnt range");
+    static constexpr int NOPS0 = (CH ? 2 : 1) * NCK + NCF + (CH ? 0 : NCV + NCT);
+    static constexpr int NOPS1 = NCK + (MODE != kAlphaNone ? NCT : 0) + (CH ? NCV + NCT : 0);
+    static_assert(NOPS0 < 64 && NOPS1 < 64, "vmcnt range");
 };
 
 template <typename E, int DK, int CK, int MODE>
-__global__ __launch_bounds__(64 * 5) void chunk_scan_kernel(ScanParams p)
+__global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
 {
     using LY = ScanLayout<E, DK, CK, MODE>;
     using SK = Swz<E, DK>;
@@ -560,7 +564,7 @@ __global__ __launch_bounds__(64 * 5) void chunk_scan_kernel(ScanParams p)
             StaticFor<0, NSLOT>::run(step);
         }
     } else {
-        // ===================================================== copier
+        // ===================================================== copiers (waves 4, 5)
         // Per-lane source offsets of one chunk's tiles, as for a full chunk:
         // instruction j, lane l fills LDS bytes 1024 j + 16 l of the region,
         // i.e. row b / RB, physical chunk (b % RB) / 16, which holds logical
@@ -579,6 +583,7 @@ __global__ __launch_bounds__(64 * 5) void chunk_scan_kernel(ScanParams p)
 #pragma unroll
         for (int j = 0; j < LY::NCT; ++j) offT[j] = tile_off(ST{}, j, CK * ES, CK);
 
+        const int cw = w - 4;   // which copier
         const unsigned char* kb = static_cast<const unsigned char*>(p.k);
         const unsigned char* qb = static_cast<const unsigned char*>(p.q);
         const unsigned char* vbs = static_cast<const unsigned char*>(p.v);
@@ -602,17 +607,22 @@ __global__ __launch_bounds__(64 * 5) void chunk_scan_kernel(ScanParams p)
             using NK = std::integral_constant<int, LY::NCK>;
             using NV = std::integral_constant<int, LY::NCV>;
             using NT = std::integral_constant<int, LY::NCT>;
+            // V and T~ go with copier 0 unless alpha is per channel
+            const bool vt = (cw == (CH ? 1 : 0));
             if constexpr (CH) {
-                copy(LY::rK + J * szK, rec + WL.KG, offK, NK{}, szK);
-                copy(LY::rKU + J * szK, rec + WL.KD, offK, NK{}, szK);
-                copy(LY::rQ + J * szK, rec + WL.QG, offK, NK{}, szK);
+                if (cw == 0) {
+                    copy(LY::rK + J * szK, rec + WL.KG, offK, NK{}, szK);
+                    copy(LY::rKU + J * szK, rec + WL.KD, offK, NK{}, szK);
+                } else {
+                    copy(LY::rQ + J * szK, rec + WL.QG, offK, NK{}, szK);
+                }
             }
             if (valid == CK) {
                 if constexpr (!CH) {
-                    copy(LY::rK + J * szK, kb + row0 * DK * ES, offK, NK{}, szK);
-                    copy(LY::rQ + J * szK, qb + row0 * DK * ES, offK, NK{}, szK);
+                    if (cw == 0) copy(LY::rK + J * szK, kb + row0 * DK * ES, offK, NK{}, szK);
+                    else copy(LY::rQ + J * szK, qb + row0 * DK * ES, offK, NK{}, szK);
                 }
-                copy(LY::rV + J * szV, vbs + (row0 * p.DV + v0) * ES, offV, NV{}, szV);
+                if (vt) copy(LY::rV + J * szV, vbs + (row0 * p.DV + v0) * ES, offV, NV{}, szV);
             } else {
                 // last, partial chunk: rows past the end repeat the last row
                 uint32_t rK[LY::NCK], rV[LY::NCV];
@@ -621,27 +631,32 @@ __global__ __launch_bounds__(64 * 5) void chunk_scan_kernel(ScanParams p)
 #pragma unroll
                 for (int j = 0; j < LY::NCV; ++j) rV[j] = tile_off(SV{}, j, p.DV * ES, valid);
                 if constexpr (!CH) {
-                    copy(LY::rK + J * szK, kb + row0 * DK * ES, rK, NK{}, szK);
-                    copy(LY::rQ + J * szK, qb + row0 * DK * ES, rK, NK{}, szK);
+                    if (cw == 0) copy(LY::rK + J * szK, kb + row0 * DK * ES, rK, NK{}, szK);
+                    else copy(LY::rQ + J * szK, qb + row0 * DK * ES, rK, NK{}, szK);
                 }
-                copy(LY::rV + J * szV, vbs + (row0 * p.DV + v0) * ES, rV, NV{}, szV);
+                if (vt) copy(LY::rV + J * szV, vbs + (row0 * p.DV + v0) * ES, rV, NV{}, szV);
             }
-            copy(LY::rT + J * szT, rec + WL.T, offT, NT{}, szT);
-            if constexpr (MODE != kAlphaNone) copy(LY::rM + J * szT, rec + WL.M, offT, NT{}, szT);
+            if (vt) copy(LY::rT + J * szT, rec + WL.T, offT, NT{}, szT);
+            if constexpr (MODE != kAlphaNone) {
+                if (cw == 1) copy(LY::rM + J * szT, rec + WL.M, offT, NT{}, szT);
+            }
             if constexpr (LY::FB > 0) {
+                if (cw == 0) {
 #pragma unroll
-                for (int j = 0; j < LY::NCF; ++j) {
-                    if (LY::FB % 1024 == 0 || 1024 * j + 16 * l < LY::FB)
-                        __builtin_amdgcn_global_load_lds((const glb_void_t*)(rec + WL.F + 1024 * j + 16 * l),
-                                                         (lds_void_t*)(uintptr_t)(sbase + (uint32_t)(LY::rF + J * szF + 1024 * j)),
-                                                         16, 0, 0);
+                    for (int j = 0; j < LY::NCF; ++j) {
+                        if (LY::FB % 1024 == 0 || 1024 * j + 16 * l < LY::FB)
+                            __builtin_amdgcn_global_load_lds((const glb_void_t*)(rec + WL.F + 1024 * j + 16 * l),
+                                                             (lds_void_t*)(uintptr_t)(sbase + (uint32_t)(LY::rF + J * szF + 1024 * j)),
+                                                             16, 0, 0);
+                    }
                 }
             }
         };
         // wait until every chunk issued before the last one has landed
         auto wait_prev = [&](bool more) {
-            if (more) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS) : "memory");
-            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (!more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            else if (cw == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS0) : "memory");
+            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS1) : "memory");
         };
         {
             auto pro = [&](auto kc) {
