@@ -83,9 +83,13 @@ const char *gdr_status_string(int status);
 /*
  * Bytes of device workspace gdr_fwd_chunked needs for these sizes (0 when
  * the call would do no chunk work).  Returns (size_t)-1 when the sizes are
- * invalid or unsupported.  The workspace holds, per chunk, the chunk's
- * triangular WY factor and its masked score block; it is scratch only and
- * its contents are not part of the result.
+ * invalid or unsupported.  The workspace holds one record per chunk of 32
+ * tokens (16 for GDR_F32 or C == 16): the chunk's triangular WY factor
+ * (I + A)^-1 diag(beta); with scalar alpha also its decay matrix and decay
+ * factors; with channel alpha also its masked decayed score block, the
+ * chunk's total per-channel decay and three decayed copies of its keys and
+ * queries.  It is scratch only: written and read within the call, its
+ * contents are not part of the result.
  */
 size_t gdr_fwd_chunked_workspace_size(int B, int H, int L, int d_k, int d_v, int C,
                                       int dtype, int alpha_mode);
