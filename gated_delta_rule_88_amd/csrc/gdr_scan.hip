@@ -222,7 +222,12 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
     extern __shared__ __align__(16) unsigned char smem[];
 
     // wave index as a scalar: the role branches below are wave-uniform
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    // Role index w: 0, 1 state owners, 2, 3 output waves, 4, 5 copiers.  The
+    // hardware places wave i of a workgroup on SIMD i % 4, so waves 2, 3 run
+    // the owners (a SIMD each) and the copiers share SIMDs 0, 1 with the
+    // output waves.
+    const int hw = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int w = hw < 2 ? hw + 2 : (hw < 4 ? hw - 2 : hw);
     const int l = lane_id(), g4 = l >> 4, c16 = l & 15;
     int lid = blockIdx.x;
     // consecutive block ids land on different XCDs: give the value blocks of
