@@ -147,6 +147,14 @@ __device__ __forceinline__ void step_barrier() {
     asm volatile("" ::: "memory");
 }
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+// A per-lane LDS offset that already includes a region's base: hidden from
+// constant folding so the slot and tile offsets that are added to it stay
+// within the 16-bit immediate of the LDS instructions (the regions past
+// 64 KiB would otherwise cost an address add per access).
+__device__ __forceinline__ int lane_base(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
 
 // Compile-time loop: f(integral_constant<int, I>) for I = B .. N - 1.
 template <int I, int N>
@@ -259,9 +267,12 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
         for (int a = 0; a < NKT; ++a)
             oKt[a] = SK::off(4 * g4 + (c16 >> 2), 32 * (a >> 1) + 4 * (a & 1) + 8 * (c16 & 3));
         // V block, transposed: token 4g + i/4 (+16 tt), channels 16w + 4(i%4)
-        const int oVt = SV::off(4 * g4 + (c16 >> 2), 16 * w + 4 * (c16 & 3));
-        const int oXS = LY::rxS + (w * NKS * kWave + l) * FS;   // + parity XSB + ks 64 FS
-        const int oXU = LY::rxU + (w * kWave + l) * FS;         // + parity XUB
+        const int oVt = lane_base(LY::rV + SV::off(4 * g4 + (c16 >> 2), 16 * w + 4 * (c16 & 3)));
+        const int oXS = lane_base(LY::rxS + (w * NKS * kWave + l) * FS);   // + parity XSB + ks 64 FS
+        const int oXU = lane_base(LY::rxU + (w * kWave + l) * FS);         // + parity XUB
+        const int oTo = lane_base(LY::rT + oT);
+        const int oFg = lane_base(LY::rF + 16 * g4);
+        const int oF0 = lane_base(LY::rF);
 
         f32x4 sT[NKT];   // S^T[key 32ks + 8g + 4p + e][v = vw + c16], a = 2ks + p
 #pragma unroll
@@ -287,7 +298,8 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
         auto load_in = [&](auto jc, In& in) {
             constexpr int J = decltype(jc)::value;
             constexpr int cK = LY::rK + J * szK, cKU = (CH ? LY::rKU : LY::rK) + J * szK;
-            constexpr int cV = LY::rV + J * szV, cT = LY::rT + J * szT, cF = LY::rF + J * szF;
+            // slot offsets relative to the lane bases above
+            constexpr int cV = J * szV, cT = J * szT, cF = J * szF;
 #pragma unroll
             for (int tt = 0; tt < NB; ++tt)
 #pragma unroll
@@ -299,25 +311,25 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
                 } else {
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        in.vv[tt][q] = ldf<0>(smem + cV, SV::off(16 * tt + 4 * g4 + q, 16 * w + c16));
+                        in.vv[tt][q] = ldf<0>(smem + LY::rV + cV, SV::off(16 * tt + 4 * g4 + q, 16 * w + c16));
                 }
-                in.gm[tt] = GATED ? ldf4<0>(smem + cF + 64 * tt, 16 * g4) : f32x4{1.f, 1.f, 1.f, 1.f};
-                in.dc[tt] = GATED ? ldf4<0>(smem + cF + 4 * CK + 64 * tt, 16 * g4) : f32x4{1.f, 1.f, 1.f, 1.f};
+                in.gm[tt] = GATED ? ldf4<0>(smem + cF + 64 * tt, oFg) : f32x4{1.f, 1.f, 1.f, 1.f};
+                in.dc[tt] = GATED ? ldf4<0>(smem + cF + 4 * CK + 64 * tt, oFg) : f32x4{1.f, 1.f, 1.f, 1.f};
             }
             if constexpr (NB == 2) {
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) in.tf[tt] = ld_frag<E, 0>(smem + cT + 16 * tt * RBT, oT, oT);
+                for (int tt = 0; tt < 2; ++tt) in.tf[tt] = ld_frag<E, 0>(smem + cT + 16 * tt * RBT, oTo, oTo);
             } else {
-                in.tf16 = ld_frag16<E, 0>(smem + cT, oT);
+                in.tf16 = ld_frag16<E, 0>(smem + cT, oTo);
             }
             if constexpr (GATED) {
-                const float gC = ldf<8 * CK>(smem + cF, 0);
+                const float gC = ldf<8 * CK>(smem + cF, oF0);
 #pragma unroll
                 for (int a = 0; a < NKT; ++a) in.dS[a] = f32x4{gC, gC, gC, gC};
             } else if constexpr (CH) {
 #pragma unroll
                 for (int a = 0; a < NKT; ++a)
-                    in.dS[a] = ldf4<0>(smem + cF + 4 * (32 * (a >> 1) + 4 * (a & 1)), 32 * g4);
+                    in.dS[a] = ldf4<0>(smem + cF + 4 * (32 * (a >> 1) + 4 * (a & 1)), oF0 + 32 * g4);
             }
         };
         // K'^T for the state update: read once the X products are issued
@@ -451,17 +463,26 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
         // ===================================================== output waves
         const int c = w - 2, vw = v0 + 16 * c;
         E* og = reinterpret_cast<E*>(p.o) + (size_t)bh * p.L * p.DV;
-        const int oXS = LY::rxS + (c * NKS * kWave + l) * FS;
-        const int oXU = LY::rxU + (c * kWave + l) * FS;
+        const int oXS = lane_base(LY::rxS + (c * NKS * kWave + l) * FS);
+        const int oXU = lane_base(LY::rxU + (c * kWave + l) * FS);
         // Gamma tile (rb, ib): row c16 (+16 rb), tokens 16ib + 4g .. +3
         int oG[NB];
 #pragma unroll
-        for (int ib = 0; ib < NB; ++ib) oG[ib] = ST::off(c16, col_of_tok(CK, 16 * ib + 4 * g4));
+        for (int ib = 0; ib < NB; ++ib) oG[ib] = lane_base(LY::rM + ST::off(c16, col_of_tok(CK, 16 * ib + 4 * g4)));
+        const int oMo = lane_base(LY::rM + oT);
+        const int oFq = lane_base(LY::rF + 4 * c16);
+        int oQ[NKS], oQh[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            oQ[ks] = lane_base(LY::rQ + oKQ[ks]);
+            oQh[ks] = sizeof(E) == 4 ? lane_base(LY::rQ + oKQh[ks]) : 0;
+        }
 
         auto out = [&](auto jc, int m) {
             constexpr int J = decltype(jc)::value;
-            constexpr int cK = LY::rK + J * szK, cQ = LY::rQ + J * szK;
-            constexpr int cM = LY::rM + J * szT, cF = LY::rF + J * szF;
+            // slot offsets relative to the lane bases above (K: region at 0)
+            constexpr int cK = LY::rK + J * szK, cQ = J * szK;
+            constexpr int cM = J * szT, cF = J * szF;
             constexpr int pS = (J & 1) * LY::XSB, pU = (J & 1) * LY::XUB;   // m & 1 == J & 1
             const int t0 = m * CK, valid = min(CK, p.L - t0);
             // ---- reads
@@ -473,7 +494,7 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
             for (int tt = 0; tt < NB; ++tt)
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
-                    qf[tt][ks] = ld_frag<E, 0>(smem + cQ + 16 * tt * RBK, oKQ[ks], oKQh[ks]);
+                    qf[tt][ks] = ld_frag<E, 0>(smem + cQ + 16 * tt * RBK, oQ[ks], oQh[ks]);
                     if constexpr (!CH) kf[tt][ks] = ld_frag<E, 0>(smem + cK + 16 * tt * RBK, oKQ[ks], oKQh[ks]);
                 }
             f32x4 gmask[NB][NB];
@@ -482,9 +503,9 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
             if constexpr (CH) {
                 if constexpr (NB == 2) {
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) pf[tt] = ld_frag<E, 0>(smem + cM + 16 * tt * RBT, oT, oT);
+                    for (int tt = 0; tt < 2; ++tt) pf[tt] = ld_frag<E, 0>(smem + cM + 16 * tt * RBT, oMo, oMo);
                 } else {
-                    pf16 = ld_frag16<E, 0>(smem + cM, oT);
+                    pf16 = ld_frag16<E, 0>(smem + cM, oMo);
                 }
             } else if constexpr (GATED) {
 #pragma unroll
@@ -494,7 +515,7 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
             }
             float gq[NB];
 #pragma unroll
-            for (int tt = 0; tt < NB; ++tt) gq[tt] = GATED ? ldf<0>(smem + cF + 64 * tt, 4 * c16) : 1.f;
+            for (int tt = 0; tt < NB; ++tt) gq[tt] = GATED ? ldf<0>(smem + cF + 64 * tt, oFq) : 1.f;
             Frag<E> uop;
             Frag16<E> uop16;
             if constexpr (NB == 2) uop = *reinterpret_cast<const Frag<E>*>(smem + oXU + pU);
