@@ -42,9 +42,9 @@ int check_chunk_sizes(int B, int H, int L, int dk, int dv, int C, int dtype, int
     return GDR_OK;
 }
 
-size_t chunk_workspace(int B, int H, int L, int dk, int C, int dtype, int mode)
+size_t chunk_workspace(int B, int H, int L, int dk, int dv, int C, int dtype, int mode)
 {
-    return gdr::chunk_workspace_bytes(B, H, L, dk, C, dtype, mode);
+    return gdr::chunk_workspace_bytes(B, H, L, dk, dv, C, dtype, mode);
 }
 
 }  // namespace
@@ -67,7 +67,7 @@ GDR_EXPORT size_t gdr_fwd_chunked_workspace_size(int B, int H, int L, int d_k, i
                                                  int dtype, int alpha_mode)
 {
     if (check_chunk_sizes(B, H, L, d_k, d_v, C, dtype, alpha_mode) != GDR_OK) return (size_t)-1;
-    return chunk_workspace(B, H, L, d_k, C, dtype, alpha_mode);
+    return chunk_workspace(B, H, L, d_k, d_v, C, dtype, alpha_mode);
 }
 
 GDR_EXPORT int gdr_fwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
@@ -98,7 +98,7 @@ GDR_EXPORT int gdr_fwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int
     const Range rb = rng(beta, nt * 4), ra = rng(log_alpha, la_bytes);
     const Range r0 = rng(S0, state_bytes), ro = rng(o, nt * d_v * es);
     const Range rf = rng(S_final, state_bytes);
-    const size_t need = chunk_workspace(B, H, L, d_k, C, dtype, alpha_mode);
+    const size_t need = chunk_workspace(B, H, L, d_k, d_v, C, dtype, alpha_mode);
     const Range rw = rng(workspace, need);
     for (Range x : {rq, rk, rv, rb, ra, r0, rf, rw})
         if (overlap(ro, x)) return GDR_ERR_INVALID_ARG;

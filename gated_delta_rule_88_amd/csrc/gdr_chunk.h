@@ -75,10 +75,63 @@ struct ScanParams {
     const unsigned char* ws;
     void* o;
     float* S_final;
-    int L, NC, DV, NVB, total;   // total = B * H * NVB workgroups
+    int L, NC, DV, NVB, total;   // total = B * H * (NVB + (SEG - 1) * (NVB + NMB)) workgroups
+    // Segment-parallel scan (SEG > 1): segment g covers chunks
+    // [g NCS, min((g + 1) NCS, NC)); NMB blocks of 32 key rows per later segment.
+    int SEG, NCS, NMB;
+    void* qt;       // [B*H][L][d_k] (input dtype): (transition from the segment start) q_t
+    float* Sseg;    // [B*H][SEG][d_v][d_k]: segment end state from S0 (g = 0) or zero (g > 0)
+    float* Pseg;    // [B*H][SEG][d_k][d_k]: segment transition (g > 0)
 };
 
+// Segment-parallel scan.  A head's chunk scan is one sequential chain; when
+// the batch has too few (b, h) chains to give every CU a workgroup, the chain
+// is cut into SEG segments that run at the same time.  Segment 0 runs from
+// the true initial state; segment g > 0 runs from a zero state, plus d_k key
+// rows started from the identity, whose end values are the segment's
+// transition P_g (S_end = S_entry P_g + Z_g, Z_g = its end state from zero)
+// and whose outputs are (P up to t) q_t.  Afterwards the entry states follow
+// in order, E_1 = Z_0, E_{g+1} = E_g P_g + Z_g, and every output of
+// segment g gains E_g (P up to t) q_t.  Only for bf16 operands: the entry
+// states enter these last products as bf16 operands.
+constexpr int kSegWorkgroups = 256;   // scan workgroups the device runs at once (one per CU)
+constexpr int kSegMinChunks = 16;     // shortest segment worth splitting off
+constexpr int kMaxSeg = 16;
+
+struct SegPlan {
+    int SEG, NCS;                     // segments, chunks per segment (the last may be shorter)
+    size_t off_Z, off_P, off_E, off_qt, bytes;   // extra workspace after the chunk records
+};
+
+inline SegPlan seg_plan(int B, int H, int L, int dk, int dv, int CK, int dtype, size_t base)
+{
+    SegPlan sp{1, 0, 0, 0, 0, 0, 0};
+    const int NC = (L + CK - 1) / CK;
+    sp.NCS = NC;
+    const size_t BH = (size_t)B * H;
+    const int NVB = dv / 32, NMB = dk / 32;
+    if (dtype != kBF16 || BH == 0) return sp;
+    int seg = 1;
+    for (int g = 2; g <= kMaxSeg; ++g) {
+        if (BH * (size_t)(NVB + (g - 1) * (NVB + NMB)) > (size_t)kSegWorkgroups) break;
+        if (NC < g * kSegMinChunks) break;
+        seg = g;
+    }
+    if (seg == 1) return sp;
+    sp.NCS = (NC + seg - 1) / seg;
+    sp.SEG = (NC + sp.NCS - 1) / sp.NCS;
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    size_t o = al(base);
+    sp.off_Z = o; o = al(o + BH * sp.SEG * dv * dk * 4);
+    sp.off_P = o; o = al(o + BH * sp.SEG * dk * dk * 4);
+    sp.off_E = o; o = al(o + BH * sp.SEG * dv * dk * 2);
+    sp.off_qt = o; o = al(o + BH * (size_t)L * dk * 2);
+    sp.bytes = o;
+    return sp;
+}
+
 hipError_t launch_wy(const ChunkArgs& a, int CK);
-hipError_t launch_scan(const ChunkArgs& a, int CK);
+hipError_t launch_scan(const ChunkArgs& a, int CK, const SegPlan& sp);
+hipError_t launch_seg_combine(const ChunkArgs& a, int CK, const SegPlan& sp);
 
 }  // namespace gdr

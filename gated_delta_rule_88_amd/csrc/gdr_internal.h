@@ -33,7 +33,7 @@ struct ChunkArgs {
 };
 
 // Bytes of device workspace the chunked forward needs.
-size_t chunk_workspace_bytes(int B, int H, int L, int dk, int C, int dtype, int mode);
+size_t chunk_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int dtype, int mode);
 
 hipError_t launch_decode_step(const DecodeArgs& a);
 hipError_t launch_fwd_chunked(const ChunkArgs& a);

@@ -241,9 +241,38 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
     // consecutive block ids land on different XCDs: give the value blocks of
     // one head neighbouring logical ids on one XCD so they share its L2
     if (p.total % 8 == 0) lid = (blockIdx.x % 8) * (p.total / 8) + blockIdx.x / 8;
-    const int bh = lid / p.NVB, vb = lid % p.NVB;
-    const int v0 = vb * BV;
-    const int NC = p.NC;
+    // This workgroup's job.  Segment 0 (the whole sequence unless the scan is
+    // split into p.SEG segments) runs value blocks from the true initial
+    // state.  Every later segment runs its value blocks from a zero state and,
+    // as further rows of the same recurrence, d_k key rows started from the
+    // identity: those rows give the segment's transition matrix and
+    // (transition so far) q_t, from which the segment's true result follows
+    // once its entry state is known.
+    int bh, vb, sg = 0;
+    bool keyrows = false;
+    {
+        const int per_seg = p.NVB + p.NMB;
+        const int units = p.NVB + (p.SEG - 1) * per_seg;
+        bh = lid / units;
+        int u = lid % units;
+        if (u < p.NVB) {
+            vb = u;
+        } else {
+            u -= p.NVB;
+            sg = 1 + u / per_seg;
+            const int r = u % per_seg;
+            keyrows = r >= p.NVB;
+            vb = keyrows ? r - p.NVB : r;
+        }
+    }
+    const int v0 = vb * BV;                            // first value channel (key row for key rows)
+    const int c0 = sg * p.NCS;                         // first chunk
+    const int NC = min(p.NCS, p.NC - c0);              // chunks this workgroup walks
+    if (keyrows) {
+        // key rows carry no values: the V slots stay zero
+        for (int i = threadIdx.x; i < NSLOT * szV / 16; i += 64 * LY::NWAVES)
+            *reinterpret_cast<u32x4*>(smem + LY::rV + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+    }
 
     // per-lane LDS offsets shared by the readers
     // K / Q operand: row c16 (+16 tt), key channels 32 ks + 8 g4 .. +7
@@ -278,7 +307,11 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
 #pragma unroll
         for (int a = 0; a < NKT; ++a) {
             sT[a] = zero4();
-            if (p.S0)
+            if (keyrows) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sT[a][e] = (32 * (a >> 1) + 8 * g4 + 4 * (a & 1) + e == vw + c16) ? 1.f : 0.f;
+            } else if (sg == 0 && p.S0)
                 sT[a] = *reinterpret_cast<const f32x4*>(p.S0 + ((size_t)bh * p.DV + vw + c16) * DK +
                                                        32 * (a >> 1) + 8 * g4 + 4 * (a & 1));
         }
@@ -453,16 +486,30 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
             };
             StaticFor<0, NSLOT>::run(step);
         }
-        if (p.S_final) {
+        // final state: S_final, or this segment's end state; key rows store
+        // the segment's transition transposed (row k' of P^T, column vw + c16)
+        if (keyrows) {
+            float* pt = p.Pseg + ((size_t)bh * p.SEG + sg) * DK * DK + vw + c16;
 #pragma unroll
             for (int a = 0; a < NKT; ++a)
-                *reinterpret_cast<f32x4*>(p.S_final + ((size_t)bh * p.DV + vw + c16) * DK + 32 * (a >> 1) +
-                                          8 * g4 + 4 * (a & 1)) = sT[a];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pt[(size_t)(32 * (a >> 1) + 8 * g4 + 4 * (a & 1) + e) * DK] = sT[a][e];
+        } else {
+            float* sf = p.S_final ? p.S_final + ((size_t)bh * p.DV + vw + c16) * DK : nullptr;
+            if (p.SEG > 1) sf = p.Sseg + (((size_t)bh * p.SEG + sg) * p.DV + vw + c16) * DK;
+            if (sf) {
+#pragma unroll
+                for (int a = 0; a < NKT; ++a)
+                    *reinterpret_cast<f32x4*>(sf + 32 * (a >> 1) + 8 * g4 + 4 * (a & 1)) = sT[a];
+            }
         }
     } else if (w < 4) {
         // ===================================================== output waves
         const int c = w - 2, vw = v0 + 16 * c;
-        E* og = reinterpret_cast<E*>(p.o) + (size_t)bh * p.L * p.DV;
+        // key rows write (transition so far) q_t, d_k per token, to p.qt
+        E* og = keyrows ? reinterpret_cast<E*>(p.qt) + (size_t)bh * p.L * DK
+                        : reinterpret_cast<E*>(p.o) + (size_t)bh * p.L * p.DV;
+        const int ostride = keyrows ? DK : p.DV;
         const int oXS = lane_base(LY::rxS + (c * NKS * kWave + l) * FS);
         const int oXU = lane_base(LY::rxU + (c * kWave + l) * FS);
         // Gamma tile (rb, ib): row c16 (+16 rb), tokens 16ib + 4g .. +3
@@ -484,7 +531,7 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
             constexpr int cK = LY::rK + J * szK, cQ = J * szK;
             constexpr int cM = J * szT, cF = J * szF;
             constexpr int pS = (J & 1) * LY::XSB, pU = (J & 1) * LY::XUB;   // m & 1 == J & 1
-            const int t0 = m * CK, valid = min(CK, p.L - t0);
+            const int t0 = (c0 + m) * CK, valid = min(CK, p.L - t0);
             // ---- reads
             Frag<E> sop[NKS];
 #pragma unroll
@@ -573,7 +620,7 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
             for (int tt = 0; tt < NB; ++tt) {
                 const int tok = 16 * tt + c16;
                 if (tok < valid)
-                    st4(og + (size_t)(t0 + tok) * p.DV + vw + 4 * g4, oi[tt][0], oi[tt][1], oi[tt][2], oi[tt][3]);
+                    st4(og + (size_t)(t0 + tok) * ostride + vw + 4 * g4, oi[tt][0], oi[tt][1], oi[tt][2], oi[tt][3]);
             }
         };
         step_barrier();
@@ -627,13 +674,14 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
         };
         auto issue = [&](auto jc, int m) {
             constexpr int J = decltype(jc)::value;
-            const int t0 = m * CK, valid = min(CK, p.L - t0);
-            const unsigned char* rec = p.ws + ((size_t)bh * NC + m) * WL.bytes;
+            const int t0 = (c0 + m) * CK, valid = min(CK, p.L - t0);
+            const unsigned char* rec = p.ws + ((size_t)bh * p.NC + c0 + m) * WL.bytes;
             const size_t row0 = (size_t)bh * p.L + t0;
             using NK = std::integral_constant<int, LY::NCK>;
             using NV = std::integral_constant<int, LY::NCV>;
             using NT = std::integral_constant<int, LY::NCT>;
-            // V and T~ go with copier 0 unless alpha is per channel
+            // V and T~ go with copier 0 unless alpha is per channel; key rows
+            // have no V to copy
             const bool vt = (cw == (CH ? 1 : 0));
             if constexpr (CH) {
                 if (cw == 0) {
@@ -648,7 +696,7 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
                     if (cw == 0) copy(LY::rK + J * szK, kb + row0 * DK * ES, offK, NK{}, szK);
                     else copy(LY::rQ + J * szK, qb + row0 * DK * ES, offK, NK{}, szK);
                 }
-                if (vt) copy(LY::rV + J * szV, vbs + (row0 * p.DV + v0) * ES, offV, NV{}, szV);
+                if (vt && !keyrows) copy(LY::rV + J * szV, vbs + (row0 * p.DV + v0) * ES, offV, NV{}, szV);
             } else {
                 // last, partial chunk: rows past the end repeat the last row
                 uint32_t rK[LY::NCK], rV[LY::NCV];
@@ -660,7 +708,7 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
                     if (cw == 0) copy(LY::rK + J * szK, kb + row0 * DK * ES, rK, NK{}, szK);
                     else copy(LY::rQ + J * szK, qb + row0 * DK * ES, rK, NK{}, szK);
                 }
-                if (vt) copy(LY::rV + J * szV, vbs + (row0 * p.DV + v0) * ES, rV, NV{}, szV);
+                if (vt && !keyrows) copy(LY::rV + J * szV, vbs + (row0 * p.DV + v0) * ES, rV, NV{}, szV);
             }
             if (vt) copy(LY::rT + J * szT, rec + WL.T, offT, NT{}, szT);
             if constexpr (MODE != kAlphaNone) {
@@ -679,10 +727,14 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
             }
         };
         // wait until every chunk issued before the last one has landed
+        // (the count is that of the last chunk's copies, without V for key rows)
+        constexpr int NOPS0K = LY::NOPS0 - (CH ? 0 : LY::NCV), NOPS1K = LY::NOPS1 - (CH ? LY::NCV : 0);
         auto wait_prev = [&](bool more) {
             if (!more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            else if (cw == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS0) : "memory");
-            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS1) : "memory");
+            else if (cw == 0 && !keyrows) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS0) : "memory");
+            else if (cw == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NOPS0K) : "memory");
+            else if (!keyrows) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS1) : "memory");
+            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NOPS1K) : "memory");
         };
         {
             auto pro = [&](auto kc) {
@@ -713,37 +765,44 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
 
 // ------------------------------------------------------------------ host side
 template <typename E, int DK, int CK, int MODE>
-static hipError_t launch_scan_t(const ChunkArgs& a)
+static hipError_t launch_scan_t(const ChunkArgs& a, const SegPlan& seg)
 {
     using LY = ScanLayout<E, DK, CK, MODE>;
     static_assert(LY::bytes <= 160 * 1024, "LDS budget");
     const int BH = a.B * a.H;
     const int NC = (a.L + CK - 1) / CK;
-    const int NVB = a.dv / LY::BV;
-    ScanParams sp{a.q, a.k, a.v, a.S0, static_cast<const unsigned char*>(a.workspace), a.o, a.S_final,
-                  a.L, NC, a.dv, NVB, BH * NVB};
+    const int NVB = a.dv / LY::BV, NMB = DK / 32;
+    const int total = BH * (NVB + (seg.SEG - 1) * (NVB + NMB));
+    unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+    ScanParams sp{a.q, a.k, a.v, a.S0, ws, a.o, a.S_final, a.L, NC, a.dv, NVB, total,
+                  seg.SEG, seg.NCS, NMB, nullptr, nullptr, nullptr};
+    if (seg.SEG > 1) {
+        sp.qt = ws + seg.off_qt;
+        sp.Sseg = reinterpret_cast<float*>(ws + seg.off_Z);
+        sp.Pseg = reinterpret_cast<float*>(ws + seg.off_P);
+    }
     auto* kern = chunk_scan_kernel<E, DK, CK, MODE>;
     hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LY::bytes);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, dim3(BH * NVB), dim3(64 * LY::NWAVES), LY::bytes, a.stream, sp);
+    hipLaunchKernelGGL(kern, dim3(total), dim3(64 * LY::NWAVES), LY::bytes, a.stream, sp);
     return hipGetLastError();
 }
 
 template <typename E, int DK, int CK>
-static hipError_t launch_scan_m(const ChunkArgs& a)
+static hipError_t launch_scan_m(const ChunkArgs& a, const SegPlan& sp)
 {
-    if (a.mode == kAlphaChannel) return launch_scan_t<E, DK, CK, kAlphaChannel>(a);
-    if (a.mode == kAlphaScalar) return launch_scan_t<E, DK, CK, kAlphaScalar>(a);
-    return launch_scan_t<E, DK, CK, kAlphaNone>(a);
+    if (a.mode == kAlphaChannel) return launch_scan_t<E, DK, CK, kAlphaChannel>(a, sp);
+    if (a.mode == kAlphaScalar) return launch_scan_t<E, DK, CK, kAlphaScalar>(a, sp);
+    return launch_scan_t<E, DK, CK, kAlphaNone>(a, sp);
 }
 
-hipError_t launch_scan(const ChunkArgs& a, int CK)
+hipError_t launch_scan(const ChunkArgs& a, int CK, const SegPlan& sp)
 {
     if (a.dtype == kBF16) {
-        if (a.dk == 128) return CK == 16 ? launch_scan_m<bf16, 128, 16>(a) : launch_scan_m<bf16, 128, 32>(a);
-        return CK == 16 ? launch_scan_m<bf16, 64, 16>(a) : launch_scan_m<bf16, 64, 32>(a);
+        if (a.dk == 128) return CK == 16 ? launch_scan_m<bf16, 128, 16>(a, sp) : launch_scan_m<bf16, 128, 32>(a, sp);
+        return CK == 16 ? launch_scan_m<bf16, 64, 16>(a, sp) : launch_scan_m<bf16, 64, 32>(a, sp);
     }
-    return a.dk == 128 ? launch_scan_m<float, 128, 16>(a) : launch_scan_m<float, 64, 16>(a);
+    return a.dk == 128 ? launch_scan_m<float, 128, 16>(a, sp) : launch_scan_m<float, 64, 16>(a, sp);
 }
 
 }  // namespace gdr

@@ -79,6 +79,15 @@ def test_workspace_size_query():
     assert ws(1, 1, 200, 64, 64, 64, gdr.GDR_BF16, 2) == 7 * (2048 + 2048 + 256 + 3 * 32 * 64 * 2)
     assert ws(1, 1, 64, 128, 128, 64, gdr.GDR_F32, 2) == 4 * (1024 + 1024 + 512 + 3 * 16 * 128 * 4)
     assert ws(1, 1, 100, 128, 128, 16, gdr.GDR_BF16, 1) == 7 * (512 + 512 + 256)
+    # few (b, h) chains and many chunks (bf16): the segment-parallel scan adds,
+    # per segment, an end state (fp32 d_v x d_k), a transition (fp32 d_k x d_k)
+    # and an entry state (bf16 d_v x d_k), plus d_k bf16 values per token
+    # (here 2 segments of 16 chunks)
+    rec = 2 * 32 * (2048 + 2048 + 512)
+    assert ws(1, 2, 1024, 128, 128, 64, gdr.GDR_BF16, 1) == \
+        rec + 2 * 2 * (128 * 128 * 4 * 2 + 128 * 128 * 2) + 2 * 1024 * 128 * 2
+    # fp32 operands never segment
+    assert ws(1, 2, 1024, 128, 128, 64, gdr.GDR_F32, 1) == 2 * 64 * (1024 + 1024 + 256)
     assert ws(1, 1, 0, 64, 64, 64, gdr.GDR_BF16, 2) == 0
     assert ws(0, 4, 100, 64, 64, 64, gdr.GDR_BF16, 2) == 0
     for bad in [(1, 1, 64, 96, 128, 64, 1, 1), (1, 1, 64, 128, 128, 48, 1, 1),

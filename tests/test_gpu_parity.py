@@ -81,6 +81,42 @@ def test_chunked_parity(mode, dt, dims, C):
     assert rel_err(S, rS) <= TOL[dt]
 
 
+# (mode, B, H, L, d_k, d_v, segments the library plans for these sizes)
+SEG_CASES = [(gi.ALPHA_SCALAR, 1, 2, 1100, 128, 128, 2), (gi.ALPHA_NONE, 1, 1, 2048, 128, 128, 4),
+             (gi.ALPHA_CHANNEL, 1, 2, 1100, 128, 128, 2), (gi.ALPHA_SCALAR, 1, 1, 1600, 64, 64, 3),
+             (gi.ALPHA_SCALAR, 1, 1, 1600, 64, 128, 3), (gi.ALPHA_CHANNEL, 1, 1, 1600, 128, 64, 3)]
+
+
+def _record_bytes(mode, dk, ck=32, es=2):
+    """Per-chunk workspace record (see the layout in gdr_chunk.h)."""
+    t = ck * ck * es
+    if mode == gi.ALPHA_NONE:
+        return t
+    if mode == gi.ALPHA_SCALAR:
+        return 2 * t + 16 * ck
+    return 2 * t + 4 * dk + 3 * ck * dk * es
+
+
+@pytest.mark.parametrize("mode,B,H,L,dk,dv,seg", SEG_CASES,
+                         ids=[f"{gi.MODE_NAMES[c[0]]}-B{c[1]}H{c[2]}L{c[3]}-dk{c[4]}dv{c[5]}-seg{c[6]}"
+                              for c in SEG_CASES])
+def test_segmented_scan_parity(mode, B, H, L, dk, dv, seg):
+    """Few (b, h) chains and many chunks: the scan runs as `seg` segments at
+    once, combined through their transitions.  Ragged last chunk and last
+    segment, with an initial state and the final state checked."""
+    nc = (L + 31) // 32
+    rec = B * H * nc * _record_bytes(mode, dk)
+    ws = gdr.gdr_fwd_chunked_workspace_size(B, H, L, dk, dv, 64, gdr.GDR_BF16, mode)
+    extra = B * H * seg * (dv * dk * 4 + dk * dk * 4 + dv * dk * 2) + B * H * L * dk * 2
+    assert rec + extra <= ws <= rec + extra + 4 * 256   # the segment-parallel plan is in use
+    x = gi.chunked_inputs(B, H, L, dk, dv, torch.bfloat16, mode, seed=3300 + L + dk + mode,
+                          s0_std=0.1)
+    o, S = run_chunked(x, 64)
+    ro, rS = oracle_chunked(x)
+    assert rel_err(o, ro) <= 2e-2
+    assert rel_err(S, rS) <= 2e-2
+
+
 @pytest.mark.parametrize("L", [1, 15, 16, 63, 64, 65, 129])
 @pytest.mark.parametrize("mode", MODES, ids=lambda m: gi.MODE_NAMES[m])
 def test_chunked_lengths_zero_state(L, mode):
