@@ -106,13 +106,18 @@ __global__ __launch_bounds__(64) void seg_entry_kernel(SegArgs p)
     }
 }
 
-// One workgroup per (head, segment g >= 1, 128 tokens): E_g (bf16) in LDS,
-// each wave adds E_g (P up to t) q_t to 32 tokens of o.
+// One workgroup per (head, segment g >= 1, kTokWG tokens): E_g (bf16) in LDS,
+// each wave walks 16-token tiles and adds E_g (P up to t) q_t to o.  A tile's
+// reads of o and q are all issued before its products, so one round trip to
+// memory covers the whole tile.
+constexpr int kTokWG = 512;
+
 template <int DK>
 __global__ __launch_bounds__(256) void seg_correct_kernel(SegArgs p, int tiles_per_seg)
 {
     constexpr int NKS = DK / 32;
     constexpr int RS = DK + 8;                 // padded LDS row (elements)
+    constexpr int MAXVT = 8;                   // d_v / 16 <= 8
     extern __shared__ __align__(16) unsigned char smem[];
     bf16* es = reinterpret_cast<bf16*>(smem);
     const int l = lane_id(), g4 = l >> 4, c16 = l & 15, w = wave_id();
@@ -121,6 +126,7 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(SegArgs p, int tiles_p
     const int rem = blockIdx.x % per_head;
     const int g = 1 + rem / tiles_per_seg, tile = rem % tiles_per_seg;
     const int t_seg = g * p.TS, t_end = min(t_seg + p.TS, p.L);
+    const int nvt = p.DV / 16;
 
     const bf16* eb = p.Eb + (((size_t)bh * p.SEG + g) * p.DV) * DK;
     for (int i = threadIdx.x; i < p.DV * DK / 8; i += 256) {
@@ -131,30 +137,35 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(SegArgs p, int tiles_p
 
     const bf16* qt = p.qt + (size_t)bh * p.L * DK;
     bf16* o = p.o + (size_t)bh * p.L * p.DV;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        const int t0 = t_seg + 128 * tile + 32 * w + 16 * tt;
-        if (t0 >= t_end) break;   // wave-uniform
+    const int tw0 = t_seg + kTokWG * tile;
+    const int tw1 = min(tw0 + kTokWG, t_end);
+    for (int t0 = tw0 + 16 * w; t0 < tw1; t0 += 64) {   // wave-uniform
         const int t = t0 + c16;
-        const int tc = min(t, t_end - 1);
+        const bool live = t < tw1;
+        const int tc = min(t, tw1 - 1);
         Frag<bf16> qf[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
             qf[ks].v = *reinterpret_cast<const bf16x8*>(qt + (size_t)tc * DK + 32 * ks + 8 * g4);
-        for (int vt = 0; vt < p.DV / 16; ++vt) {
-            // lane (g4, c16): correction to o[t][16 vt + 4 g4 + i]
-            f32x4 acc = zero4();
+        // lane (g4, c16): o[t][16 vt + 4 g4 + i]
+        bf16* orow = o + (size_t)tc * p.DV + 4 * g4;
+        u32x2 cur[MAXVT];
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                Frag<bf16> a;
-                a.v = *reinterpret_cast<const bf16x8*>(es + (16 * vt + c16) * RS + 32 * ks + 8 * g4);
-                mma(acc, a, qf[ks]);
-            }
-            if (t < t_end) {
-                bf16* dst = o + (size_t)t * p.DV + 16 * vt + 4 * g4;
-                const u32x2 cur = ld8(dst);
-                st4(dst, bf_lo(cur.x) + acc[0], bf_hi(cur.x) + acc[1], bf_lo(cur.y) + acc[2],
-                    bf_hi(cur.y) + acc[3]);
+        for (int vt = 0; vt < MAXVT; ++vt)
+            if (vt < nvt) cur[vt] = ld8(orow + 16 * vt);
+#pragma unroll
+        for (int vt = 0; vt < MAXVT; ++vt) {
+            if (vt < nvt) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    Frag<bf16> a;
+                    a.v = *reinterpret_cast<const bf16x8*>(es + (16 * vt + c16) * RS + 32 * ks + 8 * g4);
+                    mma(acc, a, qf[ks]);
+                }
+                if (live)
+                    st4(orow + 16 * vt, bf_lo(cur[vt].x) + acc[0], bf_hi(cur[vt].x) + acc[1],
+                        bf_lo(cur[vt].y) + acc[2], bf_hi(cur[vt].y) + acc[3]);
             }
         }
     }
@@ -171,7 +182,7 @@ static hipError_t launch_combine_t(const ChunkArgs& a, int CK, const SegPlan& sp
     hipLaunchKernelGGL(seg_entry_kernel<DK>, dim3(BH * (a.dv / 16)), dim3(64), 0, a.stream, s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int tiles = (s.TS + 127) / 128;
+    const int tiles = (s.TS + kTokWG - 1) / kTokWG;
     const int lds = a.dv * (DK + 8) * 2;
     hipLaunchKernelGGL(seg_correct_kernel<DK>, dim3(BH * (sp.SEG - 1) * tiles), dim3(256), lds, a.stream, s,
                        tiles);
