@@ -88,8 +88,12 @@ const char *gdr_status_string(int status);
  * (I + A)^-1 diag(beta); with scalar alpha also its decay matrix and decay
  * factors; with channel alpha also its masked decayed score block, the
  * chunk's total per-channel decay and three decayed copies of its keys and
- * queries.  It is scratch only: written and read within the call, its
- * contents are not part of the result.
+ * queries.  When there are too few (batch, head) chains to occupy the GPU
+ * and many chunks (bf16 only), the scan runs several segments of each chain
+ * at once and the workspace also holds, per segment, its end state, its
+ * transition and its entry state, plus d_k values per token.  It is scratch
+ * only: written and read within the call, its contents are not part of the
+ * result.
  */
 size_t gdr_fwd_chunked_workspace_size(int B, int H, int L, int d_k, int d_v, int C,
                                       int dtype, int alpha_mode);
