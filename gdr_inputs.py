@@ -13,6 +13,12 @@ what it returns without sharing any of the method's code.
 Draw order for every workload (one ``torch.Generator`` seeded once):
 q, k, v, beta-noise, alpha-noise, then the initial state.
 
+``raw_inputs`` draws inputs for the library's optional input-side prologue
+instead: q and k un-normalised (each token scaled by a log-normal factor, so
+norms spread over two orders of magnitude) and the gates as the raw
+pre-activations b and a (beta = sigmoid(b), alpha = sigmoid(a) on the
+library's side); it applies no activation at all.
+
 All tensors are returned on the CPU.  q, k, v are cast to the workload's
 dtype (bf16 or fp32); beta, log_alpha and states are always fp32.
 """
@@ -156,3 +162,47 @@ def decode_workload_inputs(w: DecodeWorkload, steps: int | None = None) -> dict:
     return decode_inputs(w.N, w.H, w.dk, w.dv, w.steps if steps is None else steps,
                          w.dtype, w.mode, w.seed, w.s0_std)
 
+
+def raw_inputs(lead: tuple, L: int | None, dk: int, dv: int, dtype: torch.dtype, mode: int,
+               seed: int, s0_std: float = 0.0, alpha_shift: float | None = None,
+               raw_qk: bool = True, raw_gates: bool = True) -> dict:
+    """Inputs for the input-side prologue: q, k [*lead, (L,) dk], v
+    [*lead, (L,) dv] in ``dtype``; beta, log_alpha (None | [*lead, (L)] |
+    [*lead, (L,) dk]) fp32; S0 (None | [*lead, dv, dk]).  L = None drops the
+    token axis (decode).
+
+    raw_qk: q and k un-normalised, each token scaled by a log-normal factor;
+    else L2-normalised as in ``chunked_inputs``.
+    raw_gates: beta = b and log_alpha = a are the pre-activations, with
+    a = -(N(0,1) + shift) so that sigmoid(a) has the decay distribution of the
+    activated workloads; else beta = sigmoid(b), log alpha = -softplus(-a) as
+    in ``chunked_inputs`` (a call that asks only for the normalisation must
+    get gates in their domain)."""
+    g = torch.Generator().manual_seed(seed)
+    tok = tuple(lead) + (() if L is None else (L,))
+    scale = lambda: torch.exp(torch.randn(tok + (1,), generator=g))   # log-normal per token
+    q = torch.randn(tok + (dk,), generator=g) * scale()
+    k = torch.randn(tok + (dk,), generator=g) * scale()
+    v = torch.randn(tok + (dv,), generator=g)
+    b = torch.randn(tok, generator=g)
+    shift = _gate_shift(mode) if alpha_shift is None else alpha_shift
+    if mode == ALPHA_NONE:
+        a = None
+    elif mode == ALPHA_SCALAR:
+        a = -(torch.randn(tok, generator=g) + shift)
+    elif mode == ALPHA_CHANNEL:
+        a = -(torch.randn(tok + (dk,), generator=g) + shift)
+    else:
+        raise ValueError(f"unknown alpha mode {mode}")
+    S0 = None
+    if s0_std > 0:
+        S0 = torch.randn(tuple(lead) + (dv, dk), generator=g) * s0_std
+    if not raw_qk:
+        q, k = _l2norm(q), _l2norm(k)
+    if not raw_gates:
+        b = torch.sigmoid(b)
+        a = None if a is None else -torch.nn.functional.softplus(-a)
+    return dict(q=q.to(dtype).contiguous(), k=k.to(dtype).contiguous(),
+                v=v.to(dtype).contiguous(), beta=b.contiguous(),
+                log_alpha=None if a is None else a.contiguous(),
+                S0=None if S0 is None else S0.contiguous())

@@ -5,10 +5,12 @@ the CPU-baseline leg of ``bench.py`` may import this package.  The product
 path (``gated_delta_rule_88_amd``) never imports, links or executes it, and
 this package imports nothing from the product path.
 
-The arithmetic lives in ``gdr_oracle.c`` (plain C, double precision, one
+The recurrence lives in ``gdr_oracle.c`` (plain C, double precision, one
 token at a time); see that file's header for the recurrence and the passages
-it follows.  This wrapper only converts arrays to contiguous float64 and
-calls it.
+it follows.  This wrapper converts arrays to contiguous float64 and calls
+it.  The only arithmetic written here is the optional input-side prologue
+(``prologue``): unit-norm queries and keys and the sigmoid gates, applied
+elementwise in float64 before the recurrence runs.
 """
 from __future__ import annotations
 
@@ -23,6 +25,8 @@ _SRC = os.path.join(_HERE, "gdr_oracle.c")
 LIB_PATH = os.path.join(_HERE, "libgdr_oracle.so")
 
 ALPHA_NONE, ALPHA_SCALAR, ALPHA_CHANNEL = 0, 1, 2
+PRO_L2NORM_QK, PRO_GATES = 1, 2
+NORM_EPS = 1e-6
 
 _lib = None
 
@@ -67,21 +71,73 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
+def l2_normalise(x):
+    """x / max(||x||_2, 1e-6) along the last axis, in float64.
+
+    Keys (and queries) of unit length are what make a read by a stored key
+    return its value exactly when the keys are orthogonal ("linear attention
+    and its gated descendants", section "DeltaNet"); the floor keeps an
+    all-zero vector at zero instead of dividing by zero.
+    """
+    x = _f64(x)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, NORM_EPS)
+
+
+def sigmoid(x):
+    """1 / (1 + exp(-x)) in float64, evaluated as exp(-|x|) ratios so that
+    neither tail overflows (the write-strength and decay gates of the
+    minimal pseudocode in "Linear Attention & DeltaNet" are sigmoids)."""
+    x = _f64(x)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def log_sigmoid(x):
+    """log(sigmoid(x)) = min(x, 0) - log(1 + exp(-|x|)) in float64: the log
+    of a sigmoid decay gate, finite for every finite x."""
+    x = _f64(x)
+    return np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))
+
+
+def prologue(q, k, beta, log_alpha, flags: int):
+    """The input-side steps a caller may ask the library to apply.
+
+    flags & PRO_L2NORM_QK: q and k are divided by their L2 norms.
+    flags & PRO_GATES: beta and log_alpha hold raw pre-activations b, a; the
+    gates are beta = sigmoid(b) and alpha = sigmoid(a), so log alpha =
+    log_sigmoid(a).  Returns float64 (q, k, beta, log_alpha); absent
+    log_alpha stays None.
+    """
+    q, k, beta, la = _f64(q), _f64(k), _f64(beta), _f64(log_alpha)
+    if flags & ~(PRO_L2NORM_QK | PRO_GATES):
+        raise ValueError(f"unknown prologue bits {flags}")
+    if flags & PRO_L2NORM_QK:
+        q, k = l2_normalise(q), l2_normalise(k)
+    if flags & PRO_GATES:
+        beta = sigmoid(beta)
+        la = None if la is None else log_sigmoid(la)
+    return q, k, beta, la
+
+
 def max_threads() -> int:
     return int(_load().gdr_oracle_max_threads())
 
 
 def run(q, k, v, beta, log_alpha=None, S0=None, mode: int | None = None,
-        no_delta: bool = False, nthreads: int = 0):
+        no_delta: bool = False, nthreads: int = 0, pro: int = 0):
     """Token-by-token fp64 recurrence.
 
     q, k: [..., L, dk]; v: [..., L, dv]; beta: [..., L];
     log_alpha: None | [..., L] | [..., L, dk]; S0: None | [..., dv, dk].
     The leading dimensions (batch, head, ...) are independent chains.
+    ``pro`` applies ``prologue`` to q, k, beta and log_alpha first.
     Returns (o [..., L, dv], S_final [..., dv, dk]) as float64 arrays.
     """
     q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
     la, s0 = _f64(log_alpha), _f64(S0)
+    if pro:
+        q, k, beta, la = prologue(q, k, beta, la, pro)
     lead = q.shape[:-2]
     L, dk = q.shape[-2:]
     dv = v.shape[-1]

@@ -313,3 +313,113 @@ def test_oracle_rejects_bad_shapes():
         oracle.run(q, k[:4], v, beta, la, S0)
     with pytest.raises(ValueError):
         oracle.run(q, k, v, beta, la[:3], S0, mode=SCALAR)
+
+
+# --------------------------------------------------------------------------
+# the input-side prologue (unit-norm q, k; sigmoid gates)
+def test_prologue_gates_closed_forms():
+    """sigmoid and log-sigmoid at points with exact values, and in both far
+    tails, where a naive exp(-x) would overflow."""
+    ln3 = math.log(3.0)
+    s = oracle.sigmoid(np.array([0.0, ln3, -ln3, 800.0, -800.0]))
+    assert np.allclose(s[:3], [0.5, 0.75, 0.25], rtol=1e-15, atol=0)
+    assert s[3] == 1.0 and 0.0 <= s[4] < 1e-300
+    ls = oracle.log_sigmoid(np.array([0.0, ln3, -ln3, 800.0, -800.0]))
+    assert np.allclose(ls[:3], [-math.log(2.0), math.log(0.75), math.log(0.25)], rtol=1e-15, atol=0)
+    assert ls[3] == 0.0 and ls[4] == -800.0
+
+
+def test_prologue_gates_against_scipy():
+    """The gates agree with scipy's expit / log_expit (independent routines)
+    over the range a gate pre-activation takes, and obey
+    sigmoid(x) + sigmoid(-x) = 1 and exp(log_sigmoid(x)) = sigmoid(x)."""
+    from scipy import special
+    x = np.linspace(-60.0, 60.0, 4801)
+    assert np.max(np.abs(oracle.sigmoid(x) - special.expit(x)) / special.expit(x)) < 1e-14
+    assert np.max(np.abs(oracle.log_sigmoid(x) - special.log_expit(x))
+                  / np.maximum(np.abs(special.log_expit(x)), 1e-300)) < 1e-13
+    assert np.max(np.abs(oracle.sigmoid(x) + oracle.sigmoid(-x) - 1.0)) < 1e-15
+    assert np.max(np.abs(np.exp(oracle.log_sigmoid(x)) - oracle.sigmoid(x))) < 1e-15
+
+
+def test_prologue_norm_closed_forms():
+    x = np.array([[3.0, 4.0, 0.0], [0.0, 0.0, 0.0], [1e-9, 0.0, 0.0], [0.0, -2.0, 0.0]])
+    y = oracle.l2_normalise(x)
+    assert np.array_equal(y[0], [0.6, 0.8, 0.0])
+    assert np.array_equal(y[1], [0.0, 0.0, 0.0])           # zero stays zero
+    assert np.allclose(y[2], [1e-3, 0.0, 0.0], rtol=1e-15)  # below the 1e-6 floor
+    assert np.array_equal(y[3], [0.0, -1.0, 0.0])
+    rng = np.random.default_rng(31)
+    z = rng.standard_normal((50, 128)) * rng.lognormal(0.0, 2.0, (50, 1))
+    assert np.max(np.abs(np.linalg.norm(oracle.l2_normalise(z), axis=-1) - 1.0)) < 1e-14
+    assert np.max(np.abs(oracle.l2_normalise(7.5 * z) - oracle.l2_normalise(z))) < 1e-15
+
+
+def test_prologue_feeds_the_recurrence():
+    """run(raw, pro=3) equals the recurrence on inputs activated by
+    independent routines (numpy's norm, scipy's expit / log_expit), for every
+    gate mode; each flag alone touches only its own inputs."""
+    from scipy import special
+    rng = np.random.default_rng(32)
+    for mode in (NONE, SCALAR, CHANNEL):
+        L, dk, dv = 23, 8, 5
+        q = rng.standard_normal((L, dk)) * rng.lognormal(0.0, 1.0, (L, 1))
+        k = rng.standard_normal((L, dk)) * rng.lognormal(0.0, 1.0, (L, 1))
+        v = rng.standard_normal((L, dv))
+        b = rng.standard_normal(L)
+        a = None if mode == NONE else rng.standard_normal((L,) if mode == SCALAR else (L, dk)) + 2.0
+        S0 = 0.3 * rng.standard_normal((dv, dk))
+        qn = q / np.linalg.norm(q, axis=-1, keepdims=True)
+        kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+        la = None if a is None else special.log_expit(a)
+        ro, rS = oracle_runner(qn, kn, v, special.expit(b), la, S0)
+        o, S = oracle.run(q, k, v, b, a, S0, mode=mode, pro=3, nthreads=1)
+        assert _err(o, ro) < 1e-12 and _err(S, rS) < 1e-12
+        o1, _ = oracle.run(q, k, v, special.expit(b), la, S0, mode=mode, pro=1, nthreads=1)
+        assert _err(o1, ro) < 1e-12
+        o2, _ = oracle.run(qn, kn, v, b, a, S0, mode=mode, pro=2, nthreads=1)
+        assert _err(o2, ro) < 1e-12
+
+
+def test_prologue_gate_signs():
+    """alpha = sigmoid(a): a -> +inf keeps the memory (DeltaNet), a -> -inf
+    empties it before every write, so with S0 = 0 each output is the lone
+    write read back, o_t = beta_t v_t (k_t . q_t).  Swapping the sign of
+    either gate fails one of the two."""
+    rng = np.random.default_rng(33)
+    L, dk, dv = 17, 6, 4
+    q, k = _unit(rng.standard_normal((L, dk))), _unit(rng.standard_normal((L, dk)))
+    v, b = rng.standard_normal((L, dv)), rng.standard_normal(L)
+    beta = 1.0 / (1.0 + np.exp(-b))
+    keep, _ = oracle.run(q, k, v, b, np.full(L, 60.0), None, mode=SCALAR, pro=2, nthreads=1)
+    delta, _ = oracle_runner(q, k, v, beta)
+    assert _err(keep, delta) < 1e-12
+    gone, _ = oracle.run(q, k, v, b, np.full(L, -700.0), None, mode=SCALAR, pro=2, nthreads=1)
+    lone = beta[:, None] * v * np.sum(k * q, axis=-1)[:, None]
+    assert _err(gone, lone) < 1e-12
+
+
+def test_prologue_norm_exact_recall():
+    """With PRO_L2NORM_QK, orthogonal keys of any length and beta = 1 store
+    each value exactly, and a query along a stored key (any length) reads
+    that value back ("linear attention and its gated descendants",
+    "DeltaNet": recall is exact for normalised, orthogonal keys).  Tokens
+    0-3 write key t; tokens 4-7 (beta = 0, nothing written) read keys
+    1, 3, 0, 2 back."""
+    k = np.vstack([np.diag([5.0, 0.1, 2.0, 30.0]), np.full((4, 4), 9.0)])
+    v = np.vstack([np.arange(12.0).reshape(4, 3) - 4.0, np.full((4, 3), 100.0)])
+    perm = [1, 3, 0, 2]
+    q = np.vstack([np.ones((4, 4)), np.diag([7.0, 0.02, 1.0, 3.0])[perm]])
+    beta = np.array([1.0] * 4 + [0.0] * 4)
+    o, S = oracle.run(q, k, v, beta, None, None, mode=NONE, pro=1, nthreads=1)
+    assert _err(S, v[:4].T) < 1e-14
+    assert _err(o[4:], v[perm]) < 1e-14
+    # without the prologue the same raw keys store scaled, mixed values
+    o_raw, _ = oracle.run(q, k, v, beta, None, None, mode=NONE, nthreads=1)
+    assert _err(o_raw[4:], v[perm]) > 1e-3
+
+
+def test_prologue_rejects_unknown_bits():
+    x = np.zeros((2, 4))
+    with pytest.raises(ValueError):
+        oracle.prologue(x, x, np.zeros(2), None, 4)
