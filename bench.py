@@ -129,14 +129,20 @@ def _events(n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
-def bench_chunked(w, steps, warmup, copies):
+def bench_chunked(w, steps, warmup, copies, prologue=0):
+    """prologue != 0: raw inputs, and the library applies those input-side
+    steps itself (gdr_fwd_chunked_ex)."""
     import gated_delta_rule_88_amd as gdr
 
     dev = torch.device("cuda:0")
     sets = []
     for c in range(copies):
-        x = gi.chunked_inputs(w.B, w.H, w.L, w.dk, w.dv, w.dtype, w.mode, w.seed + 1000 * c,
-                              w.s0_std)
+        if prologue:
+            x = gi.raw_inputs((w.B, w.H), w.L, w.dk, w.dv, w.dtype, w.mode, w.seed + 1000 * c,
+                              w.s0_std, raw_qk=bool(prologue & 1), raw_gates=bool(prologue & 2))
+        else:
+            x = gi.chunked_inputs(w.B, w.H, w.L, w.dk, w.dv, w.dtype, w.mode,
+                                  w.seed + 1000 * c, w.s0_std)
         sets.append({k: (None if t is None else t.to(dev)) for k, t in x.items()})
     mode = w.mode
     code = gdr.GDR_BF16 if w.dtype == torch.bfloat16 else gdr.GDR_F32
@@ -150,7 +156,7 @@ def bench_chunked(w, steps, warmup, copies):
         d = sets[i % copies]
         gdr.gdr_fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["S0"], w.C,
                             o=outs[i % copies], S_final=finals[i % copies],
-                            workspace=wss[i % copies])
+                            workspace=wss[i % copies], prologue=prologue)
 
     for i in range(warmup):
         call(i)
@@ -178,30 +184,36 @@ def bench_chunked(w, steps, warmup, copies):
                 call_ms_median=per_call[n_each // 2])
 
 
-def bench_decode(w, steps):
+def bench_decode(w, steps, prologue=0):
     import gated_delta_rule_88_amd as gdr
 
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev).manual_seed(w.seed)
     N, H, dk, dv = w.N, w.H, w.dk, w.dv
 
-    def unit(x):
+    def unit(x):   # the caller-side normalisation, unless the library does it
+        if prologue & 1:
+            return x
         return x / torch.clamp(x.norm(dim=-1, keepdim=True), min=1e-6)
 
     q = unit(torch.randn(steps, N, H, dk, generator=g, device=dev)).to(w.dtype)
     k = unit(torch.randn(steps, N, H, dk, generator=g, device=dev)).to(w.dtype)
     v = torch.randn(steps, N, H, dv, generator=g, device=dev).to(w.dtype)
-    beta = torch.sigmoid(torch.randn(steps, N, H, generator=g, device=dev))
-    la = -torch.nn.functional.softplus(torch.randn(steps, N, H, generator=g, device=dev) + 2.0)
+    b = torch.randn(steps, N, H, generator=g, device=dev)
+    a = -(torch.randn(steps, N, H, generator=g, device=dev) + 2.0)
+    if prologue & 2:   # raw pre-activations: the library applies the gates
+        beta, la = b, a
+    else:
+        beta, la = torch.sigmoid(b), -torch.nn.functional.softplus(-a)
     S = torch.randn(N, H, dv, dk, generator=g, device=dev) * w.s0_std
     o = torch.empty(steps, N, H, dv, dtype=w.dtype, device=dev)
     for t in range(8):  # warm-up on a scratch copy of the state
-        gdr.gdr_decode_step(q[t], k[t], v[t], beta[t], la[t], S.clone(), o[t])
+        gdr.gdr_decode_step(q[t], k[t], v[t], beta[t], la[t], S.clone(), o[t], prologue=prologue)
     torch.cuda.synchronize()
     e0, e1 = _events(2)
     e0.record()
     for t in range(steps):
-        gdr.gdr_decode_step(q[t], k[t], v[t], beta[t], la[t], S, o[t])
+        gdr.gdr_decode_step(q[t], k[t], v[t], beta[t], la[t], S, o[t], prologue=prologue)
     e1.record()
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
@@ -247,6 +259,9 @@ def main():
     ap.add_argument("--cpu-chains", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--prologue", type=int, default=0, choices=(0, 1, 2, 3),
+                    help="time the fused input-side prologue on raw inputs: 1 = L2-normalise "
+                         "q, k; 2 = sigmoid gates; 3 = both")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run plain copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -265,7 +280,7 @@ def main():
         copy_probe(args.copy_probe_mib)
         return
     w = WORKLOADS[args.workload]
-    r = bench_chunked(w, args.steps, args.warmup, args.copies)
+    r = bench_chunked(w, args.steps, args.warmup, args.copies, args.prologue)
     nbytes, flops = chunked_algorithmic(w)
     call_s = r["call_ms_mean"] / 1e3
     gbs = nbytes / call_s / 1e9
@@ -286,10 +301,12 @@ def main():
         "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d_k": w.dk, "d_v": w.dv,
-                   "C": w.C, "alpha": gi.MODE_NAMES[w.mode], "input_copies": args.copies},
+                   "C": w.C, "alpha": gi.MODE_NAMES[w.mode], "input_copies": args.copies,
+                   "prologue": args.prologue},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(w.name, chunked_kernel_name(w)),
+                     "traffic": (None if args.prologue else
+                                 measured_traffic(w.name, chunked_kernel_name(w))),
                      "kernel": chunked_kernel_name(w),
                      "algorithmic_bytes_per_call": nbytes,
                      "call_ms_mean": r["call_ms_mean"], "call_ms_median": r["call_ms_median"]},
@@ -299,7 +316,7 @@ def main():
     }
     if not args.no_decode:
         dw = gi.DECODE_BF16
-        dr = bench_decode(dw, args.decode_steps)
+        dr = bench_decode(dw, args.decode_steps, args.prologue)
         db = decode_algorithmic(dw)
         dgbs = db / (dr["step_ms"] / 1e3) / 1e9
         out["decode"] = {
@@ -307,7 +324,8 @@ def main():
             "tokens_per_s": dw.N / (dr["step_ms"] / 1e3),
             "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": dgbs / HBM_PEAK_GBS,
-                         "traffic": measured_traffic(dw.name, "decode_step_kernel"),
+                         "traffic": (None if args.prologue else
+                                     measured_traffic(dw.name, "decode_step_kernel")),
                          "kernel": "decode_step_kernel", "algorithmic_bytes_per_step": db},
             "state_finite": dr["finite"],
         }

@@ -30,9 +30,10 @@ GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED = 0, 1, 2
 GDR_ERR_WORKSPACE_TOO_SMALL, GDR_ERR_HIP = 3, 4
 GDR_F32, GDR_BF16 = 0, 1
 GDR_ALPHA_NONE, GDR_ALPHA_SCALAR, GDR_ALPHA_CHANNEL = 0, 1, 2
+GDR_PRO_L2NORM_QK, GDR_PRO_GATES = 1, 2
 
 EXPORTED = ("gdr_abi_version", "gdr_status_string", "gdr_fwd_chunked_workspace_size",
-            "gdr_fwd_chunked", "gdr_decode_step")
+            "gdr_fwd_chunked", "gdr_fwd_chunked_ex", "gdr_decode_step", "gdr_decode_step_ex")
 
 _lib = None
 
@@ -60,8 +61,12 @@ def load_library():
     lib.gdr_fwd_chunked_workspace_size.restype = sz
     lib.gdr_fwd_chunked.argtypes = [i] * 7 + [vp] * 4 + [i] + [vp] * 5 + [sz, vp]
     lib.gdr_fwd_chunked.restype = i
+    lib.gdr_fwd_chunked_ex.argtypes = lib.gdr_fwd_chunked.argtypes + [ctypes.c_uint]
+    lib.gdr_fwd_chunked_ex.restype = i
     lib.gdr_decode_step.argtypes = [i] * 5 + [vp] * 4 + [i] + [vp] * 4
     lib.gdr_decode_step.restype = i
+    lib.gdr_decode_step_ex.argtypes = lib.gdr_decode_step.argtypes + [ctypes.c_uint]
+    lib.gdr_decode_step_ex.restype = i
     _lib = lib
     return lib
 
@@ -121,11 +126,13 @@ def gdr_fwd_chunked_workspace_size(B, H, L, d_k, d_v, C, dtype, alpha_mode) -> i
 
 def gdr_fwd_chunked(q, k, v, beta, log_alpha=None, S0=None, chunk: int = 64, *,
                     o=None, S_final=None, write_final: bool = True, workspace=None,
-                    stream=None):
+                    stream=None, prologue: int = 0):
     """Chunkwise forward.  q, k [B,H,L,dk]; v [B,H,L,dv] (bf16 or fp32);
     beta [B,H,L] fp32; log_alpha None | [B,H,L] | [B,H,L,dk] fp32;
     S0 None | [B,H,dv,dk] fp32.  Returns (o, S_final or None).
-    Pass S_final=S0 to update the state in place."""
+    Pass S_final=S0 to update the state in place.  ``prologue`` (a set of
+    GDR_PRO_* bits) asks the library to L2-normalise q and k and/or to take
+    beta and log_alpha as raw gate pre-activations (gdr_fwd_chunked_ex)."""
     lib = load_library()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, L, d_k]")
@@ -156,18 +163,22 @@ def gdr_fwd_chunked(q, k, v, beta, log_alpha=None, S0=None, chunk: int = 64, *,
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.gdr_fwd_chunked(B, H, L, dk, dv, chunk, code, _ptr(q), _ptr(k), _ptr(v),
-                             _ptr(beta), mode, _ptr(log_alpha), _ptr(S0), _ptr(o),
-                             _ptr(S_final), _ptr(workspace), ws_bytes, _stream(stream))
+    args = (B, H, L, dk, dv, chunk, code, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), mode,
+            _ptr(log_alpha), _ptr(S0), _ptr(o), _ptr(S_final), _ptr(workspace), ws_bytes,
+            _stream(stream))
+    if prologue:
+        st, name = lib.gdr_fwd_chunked_ex(*args, int(prologue)), "gdr_fwd_chunked_ex"
+    else:
+        st, name = lib.gdr_fwd_chunked(*args), "gdr_fwd_chunked"
     if st != GDR_OK:
-        raise GdrError(st, "gdr_fwd_chunked")
+        raise GdrError(st, name)
     return o, S_final
 
 
-def gdr_decode_step(q, k, v, beta, log_alpha, S, o=None, *, stream=None):
+def gdr_decode_step(q, k, v, beta, log_alpha, S, o=None, *, stream=None, prologue: int = 0):
     """One decode step.  q, k [N,H,dk]; v [N,H,dv]; beta [N,H];
     log_alpha None | [N,H] | [N,H,dk]; S [N,H,dv,dk] fp32 (updated in
-    place).  Returns o [N,H,dv]."""
+    place).  Returns o [N,H,dv].  ``prologue`` as for gdr_fwd_chunked."""
     lib = load_library()
     if q.dim() != 3:
         raise ValueError("q must be [N, H, d_k]")
@@ -188,8 +199,12 @@ def gdr_decode_step(q, k, v, beta, log_alpha, S, o=None, *, stream=None):
     if o is None:
         o = torch.empty((N, H, dv), dtype=dt, device=dev)
     _check(o, "o", dt, dev, (N, H, dv))
-    st = lib.gdr_decode_step(N, H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), mode,
-                             _ptr(log_alpha), _ptr(S), _ptr(o), _stream(stream))
+    args = (N, H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), mode, _ptr(log_alpha),
+            _ptr(S), _ptr(o), _stream(stream))
+    if prologue:
+        st, name = lib.gdr_decode_step_ex(*args, int(prologue)), "gdr_decode_step_ex"
+    else:
+        st, name = lib.gdr_decode_step(*args), "gdr_decode_step"
     if st != GDR_OK:
-        raise GdrError(st, "gdr_decode_step")
+        raise GdrError(st, name)
     return o

@@ -70,12 +70,14 @@ GDR_EXPORT size_t gdr_fwd_chunked_workspace_size(int B, int H, int L, int d_k, i
     return chunk_workspace(B, H, L, d_k, d_v, C, dtype, alpha_mode);
 }
 
-GDR_EXPORT int gdr_fwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
-                               const void* q, const void* k, const void* v,
-                               const float* beta, int alpha_mode, const float* log_alpha,
-                               const float* S0, void* o, float* S_final,
-                               void* workspace, size_t workspace_bytes, hipStream_t stream)
+GDR_EXPORT int gdr_fwd_chunked_ex(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                                  const void* q, const void* k, const void* v,
+                                  const float* beta, int alpha_mode, const float* log_alpha,
+                                  const float* S0, void* o, float* S_final,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                  unsigned prologue)
 {
+    if (prologue & ~(unsigned)(GDR_PRO_L2NORM_QK | GDR_PRO_GATES)) return GDR_ERR_INVALID_ARG;
     int st = check_chunk_sizes(B, H, L, d_k, d_v, C, dtype, alpha_mode);
     if (st != GDR_OK) return st;
     const size_t BH = (size_t)B * H;
@@ -110,15 +112,26 @@ GDR_EXPORT int gdr_fwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GDR_ERR_WORKSPACE_TOO_SMALL;
 
     gdr::ChunkArgs a{B, H, L, d_k, d_v, C, dtype, alpha_mode, q, k, v, beta, log_alpha, S0, o,
-                     S_final, workspace, stream};
+                     S_final, workspace, stream, prologue};
     return gdr::launch_fwd_chunked(a) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
-GDR_EXPORT int gdr_decode_step(int N, int H, int d_k, int d_v, int dtype,
+GDR_EXPORT int gdr_fwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
                                const void* q, const void* k, const void* v,
                                const float* beta, int alpha_mode, const float* log_alpha,
-                               float* S, void* o, hipStream_t stream)
+                               const float* S0, void* o, float* S_final,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
+    return gdr_fwd_chunked_ex(B, H, L, d_k, d_v, C, dtype, q, k, v, beta, alpha_mode, log_alpha, S0, o,
+                              S_final, workspace, workspace_bytes, stream, 0u);
+}
+
+GDR_EXPORT int gdr_decode_step_ex(int N, int H, int d_k, int d_v, int dtype,
+                                  const void* q, const void* k, const void* v,
+                                  const float* beta, int alpha_mode, const float* log_alpha,
+                                  float* S, void* o, hipStream_t stream, unsigned prologue)
+{
+    if (prologue & ~(unsigned)(GDR_PRO_L2NORM_QK | GDR_PRO_GATES)) return GDR_ERR_INVALID_ARG;
     if (N < 0 || H < 0) return GDR_ERR_INVALID_ARG;
     if (alpha_mode < GDR_ALPHA_NONE || alpha_mode > GDR_ALPHA_CHANNEL) return GDR_ERR_INVALID_ARG;
     if (dtype != GDR_F32 && dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
@@ -142,6 +155,14 @@ GDR_EXPORT int gdr_decode_step(int N, int H, int d_k, int d_v, int dtype,
     for (Range x : {rq, rk, rv, rb, ra})
         if (overlap(rs, x)) return GDR_ERR_INVALID_ARG;
 
-    gdr::DecodeArgs a{N, H, d_k, d_v, dtype, alpha_mode, q, k, v, beta, log_alpha, S, o, stream};
+    gdr::DecodeArgs a{N, H, d_k, d_v, dtype, alpha_mode, q, k, v, beta, log_alpha, S, o, stream, prologue};
     return gdr::launch_decode_step(a) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+GDR_EXPORT int gdr_decode_step(int N, int H, int d_k, int d_v, int dtype,
+                               const void* q, const void* k, const void* v,
+                               const float* beta, int alpha_mode, const float* log_alpha,
+                               float* S, void* o, hipStream_t stream)
+{
+    return gdr_decode_step_ex(N, H, d_k, d_v, dtype, q, k, v, beta, alpha_mode, log_alpha, S, o, stream, 0u);
 }

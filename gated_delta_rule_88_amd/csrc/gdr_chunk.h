@@ -40,33 +40,37 @@ __host__ __device__ constexpr int col_of_tok(int CK, int t)
 // ES.  Regions are 16-byte aligned and each is a dense row-major block.
 //   T   [CK][CK] E     T~ = (I + A)^{-1} diag(beta), zero above the diagonal
 //                      (rows in token order, columns in tok_of_col order)
-//   M   [CK][CK] E     scalar alpha: Gamma_ri = exp(g_r - g_i) on and below the
-//                      diagonal, zero above;  channel alpha: the masked decayed
-//                      score block P;  alpha = 1: absent
-//   F   fp32           scalar alpha: gamma_r = exp(g_r) [CK], exp(g_C - g_r) [CK],
-//                      gamma_C, zero padding (4 CK floats);
-//                      channel alpha: exp(G_C) per key channel [DK];  alpha = 1: absent
+//   M   [CK][CK] E     scalar alpha: Gamma_ri = exp(g_r - g_i) / (||q_r|| ||k_i||)
+//                      on and below the diagonal (norms 1 unless the prologue
+//                      normalises q and k), zero above;  channel alpha: the
+//                      masked decayed score block P
+//   F   fp32           scalar alpha: gamma_r / ||k_r|| [CK], exp(g_C - g_r) / ||k_r||
+//                      [CK], gamma_C and zeros [CK], gamma_r / ||q_r|| [CK];
+//                      channel alpha: exp(G_C) per key channel [DK]
 //   KG, QG, KD [CK][DK] E   channel alpha only: K . exp(G), Q . exp(G),
 //                      K . exp(G_C - G)
+// alpha = 1 uses the scalar layout with log alpha = 0.
 struct WsLayout {
     int T, M, F, KG, QG, KD, bytes;
 };
 
 __host__ __device__ constexpr WsLayout ws_layout(int ES, int DK, int CK, int MODE)
 {
+    const bool channel = (MODE == kAlphaChannel);   // else scalar alpha or alpha = 1
     const int t = 0;
     const int m = t + CK * CK * ES;
-    const int f = m + (MODE != kAlphaNone ? CK * CK * ES : 0);
-    const int kg = f + (MODE == kAlphaScalar ? 4 * CK * 4 : (MODE == kAlphaChannel ? DK * 4 : 0));
-    const int ch = (MODE == kAlphaChannel) ? CK * DK * ES : 0;
+    const int f = m + CK * CK * ES;
+    const int kg = f + (channel ? DK * 4 : 4 * CK * 4);
+    const int ch = channel ? CK * DK * ES : 0;
     return WsLayout{t, m, f, kg, kg + ch, kg + 2 * ch, kg + 3 * ch};
 }
 
 struct WyParams {
     const void *q, *k;
-    const float *beta, *log_alpha;
+    const float *beta, *log_alpha;   // log_alpha NULL: alpha = 1
     unsigned char* ws;
     int L, NC, total;   // total = B * H * NC chunks
+    unsigned pro;       // input-side prologue (kProNorm, kProGates)
 };
 
 struct ScanParams {

@@ -16,7 +16,10 @@
 // (16 B per lane), reduced across those lanes, updated and written back.
 // The step moves 2 * 4 * d_k * d_v bytes of state per head and does 6 d^2
 // flops, so it is bound by HBM bandwidth; the launch shape keeps several
-// 16-byte loads per lane in flight.
+// 16-byte loads per lane in flight.  The optional input-side prologue
+// (gdr_decode_step_ex) costs nothing measurable on top: each row group
+// already holds all of q and k, so their norms are one more lane reduction,
+// and the gates are two activations per head (per key channel).
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
@@ -31,7 +34,7 @@ template <typename T, int DK, int MODE>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     int DV, const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ beta, const float* __restrict__ log_alpha,
-    float* __restrict__ S, T* __restrict__ o)
+    float* __restrict__ S, T* __restrict__ o, unsigned pro)
 {
     constexpr int LPR = DK / 4;              // lanes per row
     constexpr int RPW = kWave / LPR;         // rows per wave per pass
@@ -51,11 +54,30 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         const T* qp = q + (size_t)head * DK + 4 * c;
 #pragma unroll
         for (int j = 0; j < 4; ++j) { kk[j] = to_f32(kp[j]); qq[j] = to_f32(qp[j]); }
+        if (pro & kProNorm) {
+            // the row group's lanes together hold all d_k channels
+            float nk = kk[0] * kk[0] + kk[1] * kk[1] + kk[2] * kk[2] + kk[3] * kk[3];
+            float nq = qq[0] * qq[0] + qq[1] * qq[1] + qq[2] * qq[2] + qq[3] * qq[3];
+#pragma unroll
+            for (int m = LPR / 2; m >= 1; m >>= 1) {
+                nk += __shfl_xor(nk, m, kWave);
+                nq += __shfl_xor(nq, m, kWave);
+            }
+            const float sk = 1.f / fmaxf(sqrtf(nk), kNormEps), sq = 1.f / fmaxf(sqrtf(nq), kNormEps);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { kk[j] *= sk; qq[j] *= sq; }
+        }
+        const bool gates = (pro & kProGates) != 0;
         if (MODE == kAlphaChannel) {
-            const float4 la = *reinterpret_cast<const float4*>(log_alpha + (size_t)head * DK + 4 * c);
+            float4 la = *reinterpret_cast<const float4*>(log_alpha + (size_t)head * DK + 4 * c);
+            if (gates) {
+                la.x = log_sigmoid_f(la.x); la.y = log_sigmoid_f(la.y);
+                la.z = log_sigmoid_f(la.z); la.w = log_sigmoid_f(la.w);
+            }
             a[0] = __expf(la.x); a[1] = __expf(la.y); a[2] = __expf(la.z); a[3] = __expf(la.w);
         } else if (MODE == kAlphaScalar) {
-            const float s = __expf(log_alpha[head]);
+            const float la = log_alpha[head];
+            const float s = __expf(gates ? log_sigmoid_f(la) : la);
             a[0] = a[1] = a[2] = a[3] = s;
         } else {
             a[0] = a[1] = a[2] = a[3] = 1.0f;
@@ -66,7 +88,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     float kq = kk[0] * qq[0] + kk[1] * qq[1] + kk[2] * qq[2] + kk[3] * qq[3];
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) kq += __shfl_xor(kq, m, kWave);
-    const float b = beta[head];
+    const float b = (pro & kProGates) ? sigmoid_f(beta[head]) : beta[head];
 
     float4 s[U];
     int row[U];
@@ -99,24 +121,24 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 template <typename T, int DK, int MODE>
 static hipError_t launch_decode(int NH, int DV, const void* q, const void* k, const void* v,
                                 const float* beta, const float* log_alpha, float* S, void* o,
-                                hipStream_t stream)
+                                hipStream_t stream, unsigned pro)
 {
     constexpr int RB = decode_rows_per_block<DK>();
     const int blocks = NH * (DV / RB);
     hipLaunchKernelGGL((decode_step_kernel<T, DK, MODE>), dim3(blocks), dim3(256), 0, stream,
-                       DV, (const T*)q, (const T*)k, (const T*)v, beta, log_alpha, S, (T*)o);
+                       DV, (const T*)q, (const T*)k, (const T*)v, beta, log_alpha, S, (T*)o, pro);
     return hipGetLastError();
 }
 
 template <typename T, int DK>
 static hipError_t dispatch_mode(int mode, int NH, int DV, const void* q, const void* k,
                                 const void* v, const float* beta, const float* la, float* S,
-                                void* o, hipStream_t st)
+                                void* o, hipStream_t st, unsigned pro)
 {
     switch (mode) {
-    case kAlphaNone: return launch_decode<T, DK, kAlphaNone>(NH, DV, q, k, v, beta, la, S, o, st);
-    case kAlphaScalar: return launch_decode<T, DK, kAlphaScalar>(NH, DV, q, k, v, beta, la, S, o, st);
-    default: return launch_decode<T, DK, kAlphaChannel>(NH, DV, q, k, v, beta, la, S, o, st);
+    case kAlphaNone: return launch_decode<T, DK, kAlphaNone>(NH, DV, q, k, v, beta, la, S, o, st, pro);
+    case kAlphaScalar: return launch_decode<T, DK, kAlphaScalar>(NH, DV, q, k, v, beta, la, S, o, st, pro);
+    default: return launch_decode<T, DK, kAlphaChannel>(NH, DV, q, k, v, beta, la, S, o, st, pro);
     }
 }
 
@@ -124,11 +146,11 @@ hipError_t launch_decode_step(const DecodeArgs& a)
 {
     const int NH = a.N * a.H;
     if (a.dtype == kBF16) {
-        if (a.dk == 128) return dispatch_mode<bf16, 128>(a.mode, NH, a.dv, a.q, a.k, a.v, a.beta, a.log_alpha, a.S, a.o, a.stream);
-        return dispatch_mode<bf16, 64>(a.mode, NH, a.dv, a.q, a.k, a.v, a.beta, a.log_alpha, a.S, a.o, a.stream);
+        if (a.dk == 128) return dispatch_mode<bf16, 128>(a.mode, NH, a.dv, a.q, a.k, a.v, a.beta, a.log_alpha, a.S, a.o, a.stream, a.pro);
+        return dispatch_mode<bf16, 64>(a.mode, NH, a.dv, a.q, a.k, a.v, a.beta, a.log_alpha, a.S, a.o, a.stream, a.pro);
     }
-    if (a.dk == 128) return dispatch_mode<float, 128>(a.mode, NH, a.dv, a.q, a.k, a.v, a.beta, a.log_alpha, a.S, a.o, a.stream);
-    return dispatch_mode<float, 64>(a.mode, NH, a.dv, a.q, a.k, a.v, a.beta, a.log_alpha, a.S, a.o, a.stream);
+    if (a.dk == 128) return dispatch_mode<float, 128>(a.mode, NH, a.dv, a.q, a.k, a.v, a.beta, a.log_alpha, a.S, a.o, a.stream, a.pro);
+    return dispatch_mode<float, 64>(a.mode, NH, a.dv, a.q, a.k, a.v, a.beta, a.log_alpha, a.S, a.o, a.stream, a.pro);
 }
 
 }  // namespace gdr

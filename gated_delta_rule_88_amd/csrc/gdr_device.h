@@ -249,6 +249,15 @@ __device__ __forceinline__ f32x4 load4f(const float* p) { return *reinterpret_ca
 // keep the compiler from moving memory operations across this point).
 __device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Gate activations of the input-side prologue: beta = sigmoid(b) and
+// log alpha = log sigmoid(a) = min(a, 0) - log(1 + exp(-|a|)), a form that
+// never overflows.  Both use the hardware exp / log: where 1 + exp(-|a|)
+// rounds to 1 the dropped tail is below 6e-8 absolute, and the per-channel
+// gates run on every key channel of every token, where a full-precision
+// log1p would cost more than the rest of the prepass.
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float log_sigmoid_f(float x) { return fminf(x, 0.f) - __logf(1.f + __expf(-fabsf(x))); }
+
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ __forceinline__ float wave_incl_scan(float x) {
     const int l = lane_id();

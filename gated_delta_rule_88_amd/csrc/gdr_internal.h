@@ -13,6 +13,11 @@ constexpr int kF32 = 0, kBF16 = 1;
 // 8-token partial sum of log alpha inside the fp32 range.
 constexpr float kChannelLogAlphaMin = -10.0f;
 
+// Input-side steps the library applies itself on request (gdr.h:
+// GDR_PRO_L2NORM_QK, GDR_PRO_GATES).
+constexpr unsigned kProNorm = 1u, kProGates = 2u;
+constexpr float kNormEps = 1e-6f;   // x / max(||x||_2, eps)
+
 struct DecodeArgs {
     int N, H, dk, dv, dtype, mode;
     const void *q, *k, *v;
@@ -20,6 +25,7 @@ struct DecodeArgs {
     float* S;
     void* o;
     hipStream_t stream;
+    unsigned pro;
 };
 
 struct ChunkArgs {
@@ -30,6 +36,7 @@ struct ChunkArgs {
     float* S_final;
     void* workspace;
     hipStream_t stream;
+    unsigned pro;
 };
 
 // Bytes of device workspace the chunked forward needs.

@@ -16,6 +16,10 @@
 // by Q . exp(G), exp(g_C - g) K by K . exp(G_C - G), gamma_C S by
 // S Diag(exp(G_C)) ("Kimi Delta Attention": the decay acts on the key
 // dimension), and the score block P comes precomputed.
+// When the library normalises q and k itself (gdr_fwd_chunked_ex), K and Q
+// reach this kernel raw: the prepass has folded 1 / ||k_t|| into gamma and
+// exp(g_C - g) (and into K . exp(G) etc. per channel) and 1 / ||q_t|| into a
+// second copy of gamma and into Gamma, so the scan's arithmetic is unchanged.
 //
 // Rows of S (value channels) evolve independently given K, beta and alpha,
 // which is what lets the value dimension be split across workgroups and
@@ -175,8 +179,11 @@ template <int NBYTES>
 struct CopyCount { static constexpr int n = (NBYTES + 1023) / 1024; };
 }  // namespace
 
+// MODE is kAlphaScalar or kAlphaChannel: alpha = 1 runs as scalar alpha with
+// log alpha = 0 (the prepass writes gamma = 1 and Gamma = the causal mask).
 template <typename E, int DK, int CK, int MODE>
 struct ScanLayout {
+    static_assert(MODE == kAlphaScalar || MODE == kAlphaChannel, "gate mode of the scan");
     static constexpr int ES = (int)sizeof(E);
     static constexpr int BV = 32;             // value channels per workgroup
     static constexpr bool CH = (MODE == kAlphaChannel);
@@ -185,7 +192,7 @@ struct ScanLayout {
     static constexpr int AHEAD = 2;
     static constexpr int NSLOT = AHEAD + 2;
     static_assert(NSLOT % 2 == 0, "exchange parity follows the slot index");
-    static constexpr int FB = MODE == kAlphaScalar ? 4 * CK * 4 : (CH ? DK * 4 : 0);
+    static constexpr int FB = CH ? DK * 4 : 4 * CK * 4;
     static constexpr int szK = CK * DK * ES, szV = CK * BV * ES, szT = CK * CK * ES, szF = align16(FB);
     // regions, each NSLOT slots
     static constexpr int rK = 0;                                   // K or K.exp(G)
@@ -194,7 +201,7 @@ struct ScanLayout {
     static constexpr int rV = rQ + NSLOT * szK;                    // V block
     static constexpr int rT = rV + NSLOT * szV;                    // T~
     static constexpr int rM = rT + NSLOT * szT;                    // Gamma or P
-    static constexpr int rF = rM + (MODE != kAlphaNone ? NSLOT * szT : 0);
+    static constexpr int rF = rM + NSLOT * szT;
     // exchange buffers (two chunks deep): S and U operands of each state owner
     static constexpr int NKS = DK / 32;
     static constexpr int FS = (int)sizeof(Frag<E>);
@@ -207,9 +214,9 @@ struct ScanLayout {
     // the decay factors, plus V and T~ unless alpha is per channel; copier 1
     // the rest, which keeps the two within a few KiB of each other.
     static constexpr int NCK = CopyCount<szK>::n, NCV = CopyCount<szV>::n, NCT = CopyCount<szT>::n;
-    static constexpr int NCF = FB ? CopyCount<(FB ? FB : 1)>::n : 0;
+    static constexpr int NCF = CopyCount<FB>::n;
     static constexpr int NOPS0 = (CH ? 2 : 1) * NCK + NCF + (CH ? 0 : NCV + NCT);
-    static constexpr int NOPS1 = NCK + (MODE != kAlphaNone ? NCT : 0) + (CH ? NCV + NCT : 0);
+    static constexpr int NOPS1 = NCK + NCT + (CH ? NCV + NCT : 0);
     static_assert(NOPS0 < 64 && NOPS1 < 64, "vmcnt range");
 };
 
@@ -517,7 +524,7 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
 #pragma unroll
         for (int ib = 0; ib < NB; ++ib) oG[ib] = lane_base(LY::rM + ST::off(c16, col_of_tok(CK, 16 * ib + 4 * g4)));
         const int oMo = lane_base(LY::rM + oT);
-        const int oFq = lane_base(LY::rF + 4 * c16);
+        const int oFq = lane_base(LY::rF + 12 * CK + 4 * c16);   // gamma / ||q||
         int oQ[NKS], oQh[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -711,18 +718,14 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
                 if (vt && !keyrows) copy(LY::rV + J * szV, vbs + (row0 * p.DV + v0) * ES, rV, NV{}, szV);
             }
             if (vt) copy(LY::rT + J * szT, rec + WL.T, offT, NT{}, szT);
-            if constexpr (MODE != kAlphaNone) {
-                if (cw == 1) copy(LY::rM + J * szT, rec + WL.M, offT, NT{}, szT);
-            }
-            if constexpr (LY::FB > 0) {
-                if (cw == 0) {
+            if (cw == 1) copy(LY::rM + J * szT, rec + WL.M, offT, NT{}, szT);
+            if (cw == 0) {
 #pragma unroll
-                    for (int j = 0; j < LY::NCF; ++j) {
-                        if (LY::FB % 1024 == 0 || 1024 * j + 16 * l < LY::FB)
-                            __builtin_amdgcn_global_load_lds((const glb_void_t*)(rec + WL.F + 1024 * j + 16 * l),
-                                                             (lds_void_t*)(uintptr_t)(sbase + (uint32_t)(LY::rF + J * szF + 1024 * j)),
-                                                             16, 0, 0);
-                    }
+                for (int j = 0; j < LY::NCF; ++j) {
+                    if (LY::FB % 1024 == 0 || 1024 * j + 16 * l < LY::FB)
+                        __builtin_amdgcn_global_load_lds((const glb_void_t*)(rec + WL.F + 1024 * j + 16 * l),
+                                                         (lds_void_t*)(uintptr_t)(sbase + (uint32_t)(LY::rF + J * szF + 1024 * j)),
+                                                         16, 0, 0);
                 }
             }
         };
@@ -792,8 +795,8 @@ template <typename E, int DK, int CK>
 static hipError_t launch_scan_m(const ChunkArgs& a, const SegPlan& sp)
 {
     if (a.mode == kAlphaChannel) return launch_scan_t<E, DK, CK, kAlphaChannel>(a, sp);
-    if (a.mode == kAlphaScalar) return launch_scan_t<E, DK, CK, kAlphaScalar>(a, sp);
-    return launch_scan_t<E, DK, CK, kAlphaNone>(a, sp);
+    // scalar alpha, and alpha = 1 as log alpha = 0 (the prepass wrote gamma = 1)
+    return launch_scan_t<E, DK, CK, kAlphaScalar>(a, sp);
 }
 
 hipError_t launch_scan(const ChunkArgs& a, int CK, const SegPlan& sp)

@@ -25,6 +25,14 @@
 // The inverse is taken in fp32 on every path: 16 x 16 diagonal blocks by
 // forward substitution (one lane per column), the block below the diagonal
 // as T_10 = -T_11 (A_10 T_00) with fp32 MFMA.
+//
+// The optional input-side prologue (gdr_fwd_chunked_ex) lives here too: the
+// gate activations beta = sigmoid(b), log alpha = log sigmoid(a) are applied
+// where beta and log alpha are first read, and the unit-norm q and k are
+// never written out: the key tiles are rescaled in registers for the Gram
+// products, and 1 / ||k||, 1 / ||q|| are folded into the per-token factors
+// and score masks the scan reads.  Each kernel has a PRO = false
+// instantiation that compiles all of it out.
 #include "gdr_device.h"
 #include "gdr_chunk.h"
 
@@ -120,22 +128,65 @@ struct WyScratch {
     static constexpr int off_Tf = off_A + CK * LF * 4;
     static constexpr int off_g = off_Tf + CK * LF * 4;
     static constexpr int off_b = off_g + CK * 4;
-    static constexpr int bytes = (off_b + CK * 4 + 15) / 16 * 16;
+    static constexpr int off_nk = off_b + CK * 4;    // 1 / ||k||, 1 / ||q|| per token
+    static constexpr int off_nq = off_nk + CK * 4;
+    static constexpr int bytes = (off_nq + CK * 4 + 15) / 16 * 16;
 };
+
+// 1 / max(||row||, eps) for the row 16 tb + (lane % 16) of the fragments
+// f[tb][*] (every lane of the row's four lane groups gets the value).
+template <typename E, int NB, int NKS>
+__device__ __forceinline__ void row_inv_norms(const Frag<E> (&f)[NB][NKS], float (&inv)[NB]) {
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) {
+        float ss = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            float x[8];
+            if constexpr (sizeof(E) == 2) {
+                Pack<bf16>::unpack(__builtin_bit_cast(u32x4, f[tb][ks].v), x);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { x[i] = f[tb][ks].lo[i]; x[4 + i] = f[tb][ks].hi[i]; }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
+        }
+        ss += __shfl_xor(ss, 16, kWave);
+        ss += __shfl_xor(ss, 32, kWave);
+        inv[tb] = 1.f / fmaxf(sqrtf(ss), kNormEps);
+    }
+}
+
+template <typename E>
+__device__ __forceinline__ void scale_frag(Frag<E>& f, float s) {
+    if constexpr (sizeof(E) == 2) {
+        float x[8];
+        Pack<bf16>::unpack(__builtin_bit_cast(u32x4, f.v), x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] *= s;
+        f.v = __builtin_bit_cast(bf16x8, Pack<bf16>::pack(x));
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { f.lo[i] *= s; f.hi[i] *= s; }
+    }
+}
 
 }  // namespace
 
 // ======================================================================
-// alpha = 1 and scalar alpha: one wave per chunk, four chunks per workgroup.
+// alpha = 1 and scalar alpha (alpha = 1 runs as log alpha = 0): one wave per
+// chunk, four chunks per workgroup.  PRO = false compiles the input-side
+// prologue out (it costs registers, hence occupancy, even when unused).
 // ======================================================================
-template <typename E, int DK, int CK, int MODE>
+template <typename E, int DK, int CK, bool PRO>
 __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
 {
+    const unsigned pro = PRO ? p.pro : 0u;
     using SC = WyScratch<E, CK>;
     constexpr int VE = SC::VE, LF = SC::LF;
     constexpr int NB = CK / 16, NKS = DK / 32;
-    constexpr bool GATED = (MODE == kAlphaScalar);
-    constexpr WsLayout WL = ws_layout((int)sizeof(E), DK, CK, MODE);
+    constexpr WsLayout WL = ws_layout((int)sizeof(E), DK, CK, kAlphaScalar);
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -150,24 +201,61 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
     float* Tf = reinterpret_cast<float*>(sw + SC::off_Tf);
     float* gs = reinterpret_cast<float*>(sw + SC::off_g);
     float* bs = reinterpret_cast<float*>(sw + SC::off_b);
+    float* nks = reinterpret_cast<float*>(sw + SC::off_nk);
+    float* nqs = reinterpret_cast<float*>(sw + SC::off_nq);
+
+    // input-side prologue, queries first: only their norms are needed here
+    // (the scan applies 1 / ||q|| through the decay factors and Gamma), so
+    // their tiles are dropped before the key tiles are loaded
+    float nk = 1.f, nq = 1.f;   // for token l
+    if (pro & kProNorm) {
+        const E* qc = reinterpret_cast<const E*>(p.q) + ((size_t)bh * p.L + t0) * DK;
+        Frag<E> qf[NB][NKS];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) qf[tb][ks] = gfrag<E>(qc, DK, 16 * tb, 32 * ks, valid);
+        float iq[NB];
+        row_inv_norms<E, NB, NKS>(qf, iq);
+        nq = iq[min(g4, NB - 1)];
+    }
 
     // K tiles of the chunk as MFMA operands, straight from global memory
+    // (scaled to unit rows by the prologue)
     const E* kc = reinterpret_cast<const E*>(p.k) + ((size_t)bh * p.L + t0) * DK;
     Frag<E> kf[NB][NKS];
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) kf[tb][ks] = gfrag<E>(kc, DK, 16 * tb, 32 * ks, valid);
+    if (pro & kProNorm) {
+        float ik[NB];
+        row_inv_norms<E, NB, NKS>(kf, ik);
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) scale_frag(kf[tb][ks], ik[tb]);
+        nk = ik[min(g4, NB - 1)];
+    }
 
     // beta (zero past the end of the sequence) and the cumulative log-decay
+    // (log alpha = 0 for alpha = 1)
     float bt = 0.f, la = 0.f;
     if (l < valid) {
         bt = p.beta[(size_t)bh * p.L + t0 + l];
-        if (GATED) la = p.log_alpha[(size_t)bh * p.L + t0 + l];
+        if (p.log_alpha) la = p.log_alpha[(size_t)bh * p.L + t0 + l];
+        if (pro & kProGates) {
+            bt = sigmoid_f(bt);
+            if (p.log_alpha) la = log_sigmoid_f(la);
+        }
     }
     const float g = wave_incl_scan(la);
     const float glast = __shfl(g, CK - 1, kWave);
-    if (l < CK) { gs[l] = g; bs[l] = bt; }
+    if (l < CK) {
+        gs[l] = g;
+        bs[l] = bt;
+        if (PRO) { nks[l] = nk; nqs[l] = nq; }
+    }
     wave_lds_fence();
 
     // Gram tiles -> A
@@ -184,7 +272,7 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
             const f32x4 br = *reinterpret_cast<const f32x4*>(bs + r0);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float d = GATED ? __expf(fminf(gr[e] - gi, 0.f)) : 1.f;
+                const float d = __expf(fminf(gr[e] - gi, 0.f));
                 Af[(r0 + e) * LF + i] = (r0 + e > i) ? br[e] * d * acc[e] : 0.f;
             }
         }
@@ -211,23 +299,26 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
                 const f32x4 b = *reinterpret_cast<const f32x4*>(bs + t);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) tv[q + e] = (t + e <= r) ? a[e] * b[e] : 0.f;
-                if (GATED) {
-                    const float gr = gs[r];
-                    const f32x4 gt = *reinterpret_cast<const f32x4*>(gs + t);
+                // Gamma, with the token norms of the scores q_r . k_t folded in
+                const float gr = gs[r], qn = PRO ? nqs[r] : 1.f;
+                const f32x4 gt = *reinterpret_cast<const f32x4*>(gs + t);
+                const f32x4 kn = PRO ? *reinterpret_cast<const f32x4*>(nks + t) : f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) mv[q + e] = (t + e <= r) ? __expf(fminf(gr - gt[e], 0.f)) : 0.f;
-                }
+                for (int e = 0; e < 4; ++e)
+                    mv[q + e] = (t + e <= r) ? __expf(fminf(gr - gt[e], 0.f)) * qn * kn[e] : 0.f;
             }
             st16(Tg + r * CK + c0, Pack<E>::pack(tv));
-            if (GATED) st16(Mg + r * CK + c0, Pack<E>::pack(mv));
+            st16(Mg + r * CK + c0, Pack<E>::pack(mv));
         }
     }
-    if (GATED && l < CK) {
+    if (l < CK) {
+        // gamma_r and exp(g_C - g_r) scaled by 1 / ||k_r|| (they multiply the
+        // key-side products), gamma_C, and gamma_r / ||q_r|| for the outputs
         float* F = reinterpret_cast<float*>(rec + WL.F);
-        F[l] = __expf(g);
-        F[CK + l] = __expf(glast - g);
+        F[l] = __expf(g) * nk;
+        F[CK + l] = __expf(glast - g) * nk;
         F[2 * CK + l] = (l == 0) ? __expf(glast) : 0.f;
-        F[3 * CK + l] = 0.f;
+        F[3 * CK + l] = __expf(g) * nq;
     }
 }
 
@@ -248,12 +339,18 @@ struct WyChannelLayout {
     static constexpr int off_Tf = off_A + CK * LF * 4;
     static constexpr int off_P = off_Tf + CK * LF * 4;
     static constexpr int off_b = off_P + CK * LP * ES;
-    static constexpr int bytes = off_b + CK * 4;
+    static constexpr int off_nk = off_b + CK * 4;    // 1 / ||k||, 1 / ||q|| per token
+    static constexpr int off_nq = off_nk + CK * 4;
+    static constexpr int bytes = off_nq + CK * 4;
 };
 
-template <typename E, int DK, int CK>
-__global__ __launch_bounds__(256) void chunk_wy_channel_kernel(WyParams p)
+// Three workgroups fit a CU's LDS at d_k = 128, C = 32; the second bound
+// holds the register budget to three waves per SIMD to match, which the
+// prologue's extra code would otherwise exceed.
+template <typename E, int DK, int CK, bool PRO>
+__global__ __launch_bounds__(256, 3) void chunk_wy_channel_kernel(WyParams p)
 {
+    const unsigned pro = PRO ? p.pro : 0u;
     using LY = WyChannelLayout<E, DK, CK>;
     constexpr int VE = LY::VE, DKP = LY::DKP, GP = LY::GP, LF = LY::LF, LP = LY::LP;
     constexpr int NB = CK / 16, NKS = DK / 32;
@@ -266,6 +363,9 @@ __global__ __launch_bounds__(256) void chunk_wy_channel_kernel(WyParams p)
     float* Tf = reinterpret_cast<float*>(smem + LY::off_Tf);
     E* Ps = reinterpret_cast<E*>(smem + LY::off_P);
     float* bs = reinterpret_cast<float*>(smem + LY::off_b);
+    float* nks = reinterpret_cast<float*>(smem + LY::off_nk);
+    float* nqs = reinterpret_cast<float*>(smem + LY::off_nq);
+    const bool gates = (pro & kProGates) != 0;
 
     const int tid = threadIdx.x, l = lane_id(), g4 = l >> 4, c16 = l & 15;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -306,7 +406,9 @@ __global__ __launch_bounds__(256) void chunk_wy_channel_kernel(WyParams p)
     for (int cid = blockIdx.x; cid < p.total; cid += gridDim.x) {
     unsigned char* rec = p.ws + (size_t)cid * WL.bytes;
 
-    // ---- stage K, Q and log alpha (floored; zero past the end), beta
+    // ---- stage K, Q and log alpha (floored; zero past the end), beta; the
+    // prologue's gate activations apply to the chunk's valid tokens
+    const int valid = min(CK, p.L - (cid % p.NC) * CK);
 #pragma unroll
     for (int j = 0; j < NKV; ++j) {
         const int i = tid + 256 * j, r = i / RV, c = (i % RV) * VE;
@@ -314,18 +416,45 @@ __global__ __launch_bounds__(256) void chunk_wy_channel_kernel(WyParams p)
             st16(Ks + r * DKP + c, kr[j]);
             st16(Qs + r * DKP + c, qr[j]);
         }
+        if (PRO) {
+            // the prologue's 1 / max(||row||, eps) for K and Q row r: the row
+            // is spread over RV consecutive lanes, a whole aligned lane group
+            // (1 when the norms are not asked for)
+            float sk = 1.f, sq = 1.f;
+            if (pro & kProNorm) {
+                float x[VE], y[VE];
+                Pack<E>::unpack(kr[j], x);
+                Pack<E>::unpack(qr[j], y);
+                sk = 0.f;
+                sq = 0.f;
+#pragma unroll
+                for (int e = 0; e < VE; ++e) { sk += x[e] * x[e]; sq += y[e] * y[e]; }
+#pragma unroll
+                for (int m = RV / 2; m >= 1; m >>= 1) {
+                    sk += __shfl_xor(sk, m, kWave);
+                    sq += __shfl_xor(sq, m, kWave);
+                }
+                sk = 1.f / fmaxf(sqrtf(sk), kNormEps);
+                sq = 1.f / fmaxf(sqrtf(sq), kNormEps);
+            }
+            if (i < CK * RV && c == 0) { nks[r] = sk; nqs[r] = sq; }
+        }
     }
 #pragma unroll
     for (int j = 0; j < NGV; ++j) {
         const int i = tid + 256 * j, r = i / RF, c = (i % RF) * 4;
         if (i < CK * RF) {
             f32x4 x = gr[j];
+            if (gates && r < valid) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = log_sigmoid_f(x[e]);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = fmaxf(x[e], kChannelLogAlphaMin);
             *reinterpret_cast<f32x4*>(Gs + r * GP + c) = x;
         }
     }
-    if (tid < CK) bs[tid] = br;
+    if (tid < CK) bs[tid] = (gates && tid < valid) ? sigmoid_f(br) : br;
     if (cid + (int)gridDim.x < p.total) fetch(cid + gridDim.x);
     __syncthreads();
     // cumulative sum down each key channel (the column is read whole first,
@@ -356,9 +485,9 @@ __global__ __launch_bounds__(256) void chunk_wy_channel_kernel(WyParams p)
             for (int j = 0; j < VE; ++j) {
                 const float gg = Gs[r * GP + c0 + j];
                 const float eg = __expf(gg), ed = __expf(GL[c0 + j] - gg);
-                a[j] = kx[j] * eg;
-                b[j] = qx[j] * eg;
-                d[j] = kx[j] * ed;
+                a[j] = kx[j] * eg * (PRO ? nks[r] : 1.f);
+                b[j] = qx[j] * eg * (PRO ? nqs[r] : 1.f);
+                d[j] = kx[j] * ed * (PRO ? nks[r] : 1.f);
             }
             st16(KGg + r * DK + c0, Pack<E>::pack(a));
             st16(QGg + r * DK + c0, Pack<E>::pack(b));
@@ -382,16 +511,19 @@ __global__ __launch_bounds__(256) void chunk_wy_channel_kernel(WyParams p)
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const int c0 = 32 * ks + 8 * g4;
-            float fl[8], fr[8];
+            float fk[8], fq[8], fr[8];
+            const float nkl = PRO ? nks[rl] : 1.f, nql = PRO ? nqs[rl] : 1.f, nkr = PRO ? nks[rr] : 1.f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float gm = Gs[m * GP + c0 + j];
-                fl[j] = __expf(Gs[rl * GP + c0 + j] - gm);
-                fr[j] = __expf(gm - Gs[rr * GP + c0 + j]);
+                const float fl = __expf(Gs[rl * GP + c0 + j] - gm);
+                fk[j] = fl * nkl;
+                fq[j] = fl * nql;
+                fr[j] = __expf(gm - Gs[rr * GP + c0 + j]) * nkr;
             }
             Frag<E> kl, ql, kr;
-            load_scaled_frag(kl, Ks + rl * DKP + c0, fl);
-            load_scaled_frag(ql, Qs + rl * DKP + c0, fl);
+            load_scaled_frag(kl, Ks + rl * DKP + c0, fk);
+            load_scaled_frag(ql, Qs + rl * DKP + c0, fq);
             load_scaled_frag(kr, Ks + rr * DKP + c0, fr);
             mma(accA, kl, kr);   // A tile: lane holds [16rb + 4g + e][16ib + c]
             mma(accP, kr, ql);   // P^T tile: lane holds P[16rb + c][16ib + 4g + e]
@@ -468,21 +600,22 @@ static hipError_t launch_wy_t(const ChunkArgs& a)
 {
     const int NC = (a.L + CK - 1) / CK;
     WyParams wp{a.q, a.k, a.beta, a.log_alpha, static_cast<unsigned char*>(a.workspace), a.L, NC,
-                a.B * a.H * NC};
+                a.B * a.H * NC, a.pro};
     if (a.mode == kAlphaChannel) {
         using LY = WyChannelLayout<E, DK, CK>;
         static_assert(LY::bytes <= 160 * 1024, "LDS budget");
         // persistent: as many workgroups as fit the CUs at once
         const int per_cu = (160 * 1024) / LY::bytes;
         const int grid = std::min(wp.total, per_cu * compute_units());
-        return launch_with_lds(chunk_wy_channel_kernel<E, DK, CK>, grid, LY::bytes, a.stream, wp);
+        return a.pro ? launch_with_lds(chunk_wy_channel_kernel<E, DK, CK, true>, grid, LY::bytes, a.stream, wp)
+                     : launch_with_lds(chunk_wy_channel_kernel<E, DK, CK, false>, grid, LY::bytes, a.stream, wp);
     }
     constexpr int bytes = 4 * WyScratch<E, CK>::bytes;
     static_assert(bytes <= 160 * 1024, "LDS budget");
     const int grid = (wp.total + 3) / 4;
-    if (a.mode == kAlphaScalar)
-        return launch_with_lds(chunk_wy_kernel<E, DK, CK, kAlphaScalar>, grid, bytes, a.stream, wp);
-    return launch_with_lds(chunk_wy_kernel<E, DK, CK, kAlphaNone>, grid, bytes, a.stream, wp);
+    // alpha = 1 runs the scalar path with log alpha = 0 (log_alpha is NULL)
+    return a.pro ? launch_with_lds(chunk_wy_kernel<E, DK, CK, true>, grid, bytes, a.stream, wp)
+                 : launch_with_lds(chunk_wy_kernel<E, DK, CK, false>, grid, bytes, a.stream, wp);
 }
 
 hipError_t launch_wy(const ChunkArgs& a, int CK)

@@ -74,6 +74,24 @@ enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 };
 
 enum gdr_alpha_mode { GDR_ALPHA_NONE = 0, GDR_ALPHA_SCALAR = 1, GDR_ALPHA_CHANNEL = 2 };
 
+/*
+ * Input-side steps the *_ex entry points apply themselves (a bit set; 0 =
+ * none, which makes them identical to the plain entry points):
+ *   GDR_PRO_L2NORM_QK  q and k are raw; every token's q and k is divided by
+ *                      max(||.||_2, 1e-6) before use (recall by a key is
+ *                      exact for normalised, orthogonal keys: "linear
+ *                      attention and its gated descendants", "DeltaNet").
+ *   GDR_PRO_GATES      beta and log_alpha hold raw pre-activations b and a:
+ *                      the library uses beta = sigmoid(b) and
+ *                      alpha = sigmoid(a), i.e. log alpha = -softplus(-a)
+ *                      (the sigmoid gates of "Linear Attention & DeltaNet",
+ *                      "Minimal pseudocode"; channel a gives one sigmoid per
+ *                      key channel).  With channel alpha the floor of
+ *                      gdr_fwd_chunked applies after the activation.
+ * Other bits are rejected with GDR_ERR_INVALID_ARG.
+ */
+enum gdr_prologue { GDR_PRO_L2NORM_QK = 1, GDR_PRO_GATES = 2 };
+
 /* Version of this ABI (GDR_ABI_VERSION). */
 int gdr_abi_version(void);
 
@@ -85,10 +103,10 @@ const char *gdr_status_string(int status);
  * the call would do no chunk work).  Returns (size_t)-1 when the sizes are
  * invalid or unsupported.  The workspace holds one record per chunk of 32
  * tokens (16 for GDR_F32 or C == 16): the chunk's triangular WY factor
- * (I + A)^-1 diag(beta); with scalar alpha also its decay matrix and decay
- * factors; with channel alpha also its masked decayed score block, the
- * chunk's total per-channel decay and three decayed copies of its keys and
- * queries.  When there are too few (batch, head) chains to occupy the GPU
+ * (I + A)^-1 diag(beta); with scalar alpha, and with alpha = 1 (run as
+ * log alpha = 0), also its decay matrix and decay factors; with channel
+ * alpha also its masked decayed score block, the chunk's total per-channel
+ * decay and three decayed copies of its keys and queries.  When there are too few (batch, head) chains to occupy the GPU
  * and many chunks (bf16 only), the scan runs several segments of each chain
  * at once and the workspace also holds, per segment, its end state, its
  * transition and its entry state, plus d_k values per token.  It is scratch
@@ -140,6 +158,15 @@ int gdr_fwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
                     const float *S0, void *o, float *S_final,
                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* gdr_fwd_chunked with the input-side steps of `prologue` (gdr_prologue);
+ * same arguments, layouts, workspace size and errors otherwise. */
+int gdr_fwd_chunked_ex(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                       const void *q, const void *k, const void *v,
+                       const float *beta, int alpha_mode, const float *log_alpha,
+                       const float *S0, void *o, float *S_final,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream,
+                       unsigned prologue);
+
 /*
  * One recurrent decode step for N sequences x H heads (the constant-memory
  * inference form: "linear attention and its gated descendants", "Recurrent
@@ -160,6 +187,12 @@ int gdr_decode_step(int N, int H, int d_k, int d_v, int dtype,
                     const void *q, const void *k, const void *v,
                     const float *beta, int alpha_mode, const float *log_alpha,
                     float *S, void *o, hipStream_t stream);
+
+/* gdr_decode_step with the input-side steps of `prologue` (gdr_prologue). */
+int gdr_decode_step_ex(int N, int H, int d_k, int d_v, int dtype,
+                       const void *q, const void *k, const void *v,
+                       const float *beta, int alpha_mode, const float *log_alpha,
+                       float *S, void *o, hipStream_t stream, unsigned prologue);
 
 #ifdef __cplusplus
 }

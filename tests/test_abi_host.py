@@ -69,11 +69,13 @@ def test_version_and_status_strings(lib):
 def test_workspace_size_query():
     ws = gdr.gdr_fwd_chunked_workspace_size
     # Per chunk of CK tokens (CK = 32 for bf16, 16 for fp32 or when C = 16):
-    # T~ (CK*CK elements); scalar gates add the decay matrix (CK*CK) and
-    # 4*CK floats of decay factors; channel gates add the score block (CK*CK),
-    # d_k floats and three CK x d_k decayed operands.
+    # T~ (CK*CK elements); scalar gates, and alpha = 1 which runs as scalar
+    # gates with log alpha = 0, add the decay matrix (CK*CK) and 4*CK floats
+    # of decay factors; channel gates add the score block (CK*CK), d_k floats
+    # and three CK x d_k decayed operands.
     assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 1) == 64 * 64 * (2048 + 2048 + 512)
-    assert ws(1, 2, 256, 64, 64, 64, gdr.GDR_F32, 0) == 2 * 16 * (16 * 16 * 4)
+    assert ws(1, 2, 256, 64, 64, 64, gdr.GDR_F32, 0) == 2 * 16 * (1024 + 1024 + 256)
+    assert ws(1, 2, 256, 64, 64, 64, gdr.GDR_F32, 0) == ws(1, 2, 256, 64, 64, 64, gdr.GDR_F32, 1)
     assert ws(4, 16, 4096, 128, 128, 64, gdr.GDR_BF16, 2) == \
         64 * 128 * (2048 + 2048 + 512 + 3 * 32 * 128 * 2)
     assert ws(1, 1, 200, 64, 64, 64, gdr.GDR_BF16, 2) == 7 * (2048 + 2048 + 256 + 3 * 32 * 64 * 2)
@@ -106,6 +108,17 @@ def fwd(lib, B=1, H=1, L=64, dk=64, dv=64, C=64, dtype=1, q=Q, k=K, v=V, beta=BE
     p = lambda x: None if x is None else ctypes.c_void_p(x)
     return lib.gdr_fwd_chunked(B, H, L, dk, dv, C, dtype, p(q), p(k), p(v), p(beta), mode, p(la),
                                p(s0), p(o), p(sf), p(ws), ws_bytes, None)
+
+
+def fwd_ex(lib, pro, **kw):
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    a = dict(B=1, H=1, L=64, dk=64, dv=64, C=64, dtype=1, q=Q, k=K, v=V, beta=BETA, mode=1, la=LA,
+             s0=S0, o=O, sf=SF, ws=WS, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.gdr_fwd_chunked_ex(a["B"], a["H"], a["L"], a["dk"], a["dv"], a["C"], a["dtype"],
+                                  p(a["q"]), p(a["k"]), p(a["v"]), p(a["beta"]), a["mode"],
+                                  p(a["la"]), p(a["s0"]), p(a["o"]), p(a["sf"]), p(a["ws"]),
+                                  a["ws_bytes"], None, pro)
 
 
 def dec(lib, N=2, H=2, dk=64, dv=64, dtype=1, q=Q, k=K, v=V, beta=BETA, mode=1, la=LA, S=S0,
@@ -168,6 +181,21 @@ def test_decode_rejects_before_launch(lib, kw, status):
 
 def test_decode_empty_is_a_noop(lib):
     assert dec(lib, N=0) == gdr.GDR_OK
+
+
+def test_prologue_entry_points_validate_like_the_plain_ones(lib):
+    p = lambda x: ctypes.c_void_p(x)
+    for pro in (4, 8, 1 << 31, 7):   # unknown bits
+        assert fwd_ex(lib, pro, B=0) == gdr.GDR_ERR_INVALID_ARG
+        assert lib.gdr_decode_step_ex(0, 2, 64, 64, 1, p(Q), p(K), p(V), p(BETA), 1, p(LA), p(S0),
+                                      p(O), None, pro) == gdr.GDR_ERR_INVALID_ARG
+    for pro in (0, 1, 2, 3):
+        assert fwd_ex(lib, pro, B=0) == gdr.GDR_OK
+        assert fwd_ex(lib, pro, dk=96) == gdr.GDR_ERR_UNSUPPORTED
+        assert fwd_ex(lib, pro, q=Q + 8) == gdr.GDR_ERR_INVALID_ARG
+        assert fwd_ex(lib, pro, ws_bytes=16) == gdr.GDR_ERR_WORKSPACE_TOO_SMALL
+        assert lib.gdr_decode_step_ex(2, 2, 64, 64, 1, p(Q), p(K), p(V), p(BETA), 1, None, p(S0),
+                                      p(O), None, pro) == gdr.GDR_ERR_INVALID_ARG
 
 
 def test_binding_refuses_cpu_tensors():

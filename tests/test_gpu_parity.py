@@ -90,9 +90,7 @@ SEG_CASES = [(gi.ALPHA_SCALAR, 1, 2, 1100, 128, 128, 2), (gi.ALPHA_NONE, 1, 1, 2
 def _record_bytes(mode, dk, ck=32, es=2):
     """Per-chunk workspace record (see the layout in gdr_chunk.h)."""
     t = ck * ck * es
-    if mode == gi.ALPHA_NONE:
-        return t
-    if mode == gi.ALPHA_SCALAR:
+    if mode in (gi.ALPHA_NONE, gi.ALPHA_SCALAR):   # alpha = 1 runs as log alpha = 0
         return 2 * t + 16 * ck
     return 2 * t + 4 * dk + 3 * ck * dk * es
 
