@@ -18,6 +18,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import itertools
 import json
 import os
 import sys
@@ -184,6 +185,42 @@ def bench_chunked(w, steps, warmup, copies, prologue=0):
                 call_ms_median=per_call[n_each // 2])
 
 
+def bench_varlen(w, steps, warmup, copies):
+    """The packed variable-length forward over one fixed length mix."""
+    import gated_delta_rule_88_amd as gdr
+
+    dev = torch.device("cuda:0")
+    lens = gi.varlen_lengths(w.N, w.T, w.seed)
+    cu = torch.tensor([0] + list(itertools.accumulate(lens)), dtype=torch.int32, device=dev)
+    sets = []
+    for c in range(copies):
+        x = gi.chunked_inputs(1, w.H, w.T, w.dk, w.dv, w.dtype, w.mode, w.seed + 1000 * c)
+        sets.append({k: (None if t is None else t[0].to(dev)) for k, t in x.items()})
+    code = gdr.GDR_BF16 if w.dtype == torch.bfloat16 else gdr.GDR_F32
+    need = gdr.gdr_fwd_varlen_workspace_size(w.N, w.H, w.T, w.dk, w.dv, w.C, code, w.mode)
+    outs = [torch.empty((w.H, w.T, w.dv), dtype=w.dtype, device=dev) for _ in range(copies)]
+    finals = [torch.empty((w.N, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
+              for _ in range(copies)]
+    wss = [torch.empty(max(need, 1), dtype=torch.uint8, device=dev) for _ in range(copies)]
+
+    def call(i):
+        d = sets[i % copies]
+        gdr.gdr_fwd_varlen(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], None, cu, w.C,
+                           o=outs[i % copies], S_final=finals[i % copies],
+                           workspace=wss[i % copies])
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    e0, e1 = _events(2)
+    e0.record()
+    for i in range(steps):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return dict(total_ms=e0.elapsed_time(e1), lengths=lens)
+
+
 def bench_decode(w, steps, prologue=0):
     import gated_delta_rule_88_amd as gdr
 
@@ -259,6 +296,9 @@ def main():
     ap.add_argument("--cpu-chains", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--varlen", action="store_true",
+                    help="time the packed variable-length forward on its length-mix workload "
+                         "instead (one JSON line of its own)")
     ap.add_argument("--prologue", type=int, default=0, choices=(0, 1, 2, 3),
                     help="time the fused input-side prologue on raw inputs: 1 = L2-normalise "
                          "q, k; 2 = sigmoid gates; 3 = both")
@@ -278,6 +318,25 @@ def main():
 
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.varlen:
+        vw = gi.VARLEN_GDN_BF16
+        r = bench_varlen(vw, args.steps, args.warmup, args.copies)
+        ms = r["total_ms"] / args.steps
+        vb = vw.H * vw.T * (2 * (2 * vw.dk + 2 * vw.dv) + 8) + vw.N * vw.H * 4 * vw.dk * vw.dv
+        print(json.dumps({
+            "metric": "tokens/s packed variable-length GDN fwd", "value": vw.tokens / (ms / 1e3),
+            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": vw.name, "N": vw.N, "H": vw.H, "T": vw.T, "d_k": vw.dk,
+                       "d_v": vw.dv, "C": vw.C, "lengths": r["lengths"],
+                       "input_copies": args.copies},
+            "roofline": {"bound": "hbm", "achieved": vb / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": vb / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": None, "kernel": "chunk_wy_kernel + chunk_scan_kernel",
+                         "algorithmic_bytes_per_call": vb},
+        }))
         return
     w = WORKLOADS[args.workload]
     r = bench_chunked(w, args.steps, args.warmup, args.copies, args.prologue)

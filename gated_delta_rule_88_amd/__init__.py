@@ -33,7 +33,8 @@ GDR_ALPHA_NONE, GDR_ALPHA_SCALAR, GDR_ALPHA_CHANNEL = 0, 1, 2
 GDR_PRO_L2NORM_QK, GDR_PRO_GATES = 1, 2
 
 EXPORTED = ("gdr_abi_version", "gdr_status_string", "gdr_fwd_chunked_workspace_size",
-            "gdr_fwd_chunked", "gdr_fwd_chunked_ex", "gdr_decode_step", "gdr_decode_step_ex")
+            "gdr_fwd_chunked", "gdr_fwd_chunked_ex", "gdr_fwd_varlen_workspace_size",
+            "gdr_fwd_varlen", "gdr_decode_step", "gdr_decode_step_ex")
 
 _lib = None
 
@@ -63,6 +64,11 @@ def load_library():
     lib.gdr_fwd_chunked.restype = i
     lib.gdr_fwd_chunked_ex.argtypes = lib.gdr_fwd_chunked.argtypes + [ctypes.c_uint]
     lib.gdr_fwd_chunked_ex.restype = i
+    lib.gdr_fwd_varlen_workspace_size.argtypes = [i] * 8
+    lib.gdr_fwd_varlen_workspace_size.restype = sz
+    lib.gdr_fwd_varlen.argtypes = [i] * 3 + [vp] + [i] * 4 + [vp] * 4 + [i] + [vp] * 5 + [sz, vp,
+                                                                                        ctypes.c_uint]
+    lib.gdr_fwd_varlen.restype = i
     lib.gdr_decode_step.argtypes = [i] * 5 + [vp] * 4 + [i] + [vp] * 4
     lib.gdr_decode_step.restype = i
     lib.gdr_decode_step_ex.argtypes = lib.gdr_decode_step.argtypes + [ctypes.c_uint]
@@ -172,6 +178,64 @@ def gdr_fwd_chunked(q, k, v, beta, log_alpha=None, S0=None, chunk: int = 64, *,
         st, name = lib.gdr_fwd_chunked(*args), "gdr_fwd_chunked"
     if st != GDR_OK:
         raise GdrError(st, name)
+    return o, S_final
+
+
+def gdr_fwd_varlen_workspace_size(N, H, T, d_k, d_v, C, dtype, alpha_mode) -> int:
+    return int(load_library().gdr_fwd_varlen_workspace_size(N, H, T, d_k, d_v, C, dtype,
+                                                            alpha_mode))
+
+
+def gdr_fwd_varlen(q, k, v, beta, log_alpha, S0, cu_seqlens, chunk: int = 64, *, o=None,
+                   S_final=None, write_final: bool = True, workspace=None, stream=None,
+                   prologue: int = 0):
+    """Chunkwise forward over a packed batch of N sequences.  q, k [H,T,dk];
+    v [H,T,dv] (bf16 or fp32); beta [H,T] fp32; log_alpha None | [H,T] |
+    [H,T,dk] fp32; cu_seqlens int32 GPU tensor [N+1] (cumulative offsets);
+    S0 None | [N,H,dv,dk] fp32.  Returns (o [H,T,dv], S_final [N,H,dv,dk] or
+    None)."""
+    lib = load_library()
+    if q.dim() != 3:
+        raise ValueError("q must be [H, T, d_k]")
+    H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    if log_alpha is None:
+        mode = GDR_ALPHA_NONE
+    else:
+        mode = GDR_ALPHA_CHANNEL if log_alpha.dim() == 3 else GDR_ALPHA_SCALAR
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be [N + 1]")
+    N = cu_seqlens.numel() - 1
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev, (N + 1,))
+    _check(q, "q", dt, dev, (H, T, dk))
+    _check(k, "k", dt, dev, (H, T, dk))
+    _check(v, "v", dt, dev, (H, T, dv))
+    _check(beta, "beta", torch.float32, dev, (H, T))
+    if mode == GDR_ALPHA_SCALAR:
+        _check(log_alpha, "log_alpha", torch.float32, dev, (H, T))
+    elif mode == GDR_ALPHA_CHANNEL:
+        _check(log_alpha, "log_alpha", torch.float32, dev, (H, T, dk))
+    _check(S0, "S0", torch.float32, dev, (N, H, dv, dk))
+    if o is None:
+        o = torch.empty((H, T, dv), dtype=dt, device=dev)
+    _check(o, "o", dt, dev, (H, T, dv))
+    if S_final is None and write_final:
+        S_final = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+    _check(S_final, "S_final", torch.float32, dev, (N, H, dv, dk))
+    need = gdr_fwd_varlen_workspace_size(N, H, T, dk, dv, chunk, code, mode)
+    if need == ctypes.c_size_t(-1).value:
+        raise GdrError(GDR_ERR_UNSUPPORTED, "gdr_fwd_varlen_workspace_size")
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdr_fwd_varlen(N, H, T, _ptr(cu_seqlens), dk, dv, chunk, code, _ptr(q), _ptr(k),
+                            _ptr(v), _ptr(beta), mode, _ptr(log_alpha), _ptr(S0), _ptr(o),
+                            _ptr(S_final), _ptr(workspace), ws_bytes, _stream(stream),
+                            int(prologue))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_fwd_varlen")
     return o, S_final
 
 

@@ -47,6 +47,18 @@ size_t chunk_workspace(int B, int H, int L, int dk, int dv, int C, int dtype, in
     return gdr::chunk_workspace_bytes(B, H, L, dk, dv, C, dtype, mode);
 }
 
+int check_varlen_sizes(int N, int H, int T, int dk, int dv, int C, int dtype, int mode)
+{
+    if (N < 0 || H < 0 || T < 0) return GDR_ERR_INVALID_ARG;
+    if (mode < GDR_ALPHA_NONE || mode > GDR_ALPHA_CHANNEL) return GDR_ERR_INVALID_ARG;
+    if (dtype != GDR_F32 && dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
+    if (!supported_dim(dk) || !supported_dim(dv) || !supported_chunk(C)) return GDR_ERR_UNSUPPORTED;
+    // record slots per head at the shortest token step: (T + 15 N) / 16
+    const size_t slots = ((size_t)T + 15 * (size_t)N) / 16;
+    if ((size_t)H * slots > kMaxGroups || (size_t)N * H * 4 > kMaxGroups) return GDR_ERR_UNSUPPORTED;
+    return GDR_OK;
+}
+
 }  // namespace
 
 GDR_EXPORT int gdr_abi_version(void) { return GDR_ABI_VERSION; }
@@ -165,4 +177,58 @@ GDR_EXPORT int gdr_decode_step(int N, int H, int d_k, int d_v, int dtype,
                                float* S, void* o, hipStream_t stream)
 {
     return gdr_decode_step_ex(N, H, d_k, d_v, dtype, q, k, v, beta, alpha_mode, log_alpha, S, o, stream, 0u);
+}
+
+GDR_EXPORT size_t gdr_fwd_varlen_workspace_size(int N, int H, int T, int d_k, int d_v, int C,
+                                                int dtype, int alpha_mode)
+{
+    if (check_varlen_sizes(N, H, T, d_k, d_v, C, dtype, alpha_mode) != GDR_OK) return (size_t)-1;
+    return gdr::varlen_workspace_bytes(N, H, T, d_k, d_v, C, dtype, alpha_mode);
+}
+
+GDR_EXPORT int gdr_fwd_varlen(int N, int H, int T, const int* cu_seqlens, int d_k, int d_v, int C,
+                              int dtype, const void* q, const void* k, const void* v,
+                              const float* beta, int alpha_mode, const float* log_alpha,
+                              const float* S0, void* o, float* S_final,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream,
+                              unsigned prologue)
+{
+    if (prologue & ~(unsigned)(GDR_PRO_L2NORM_QK | GDR_PRO_GATES)) return GDR_ERR_INVALID_ARG;
+    int st = check_varlen_sizes(N, H, T, d_k, d_v, C, dtype, alpha_mode);
+    if (st != GDR_OK) return st;
+    const size_t NH = (size_t)N * H;
+    if (NH == 0) return GDR_OK;
+    if (!cu_seqlens || !aligned(cu_seqlens, 4)) return GDR_ERR_INVALID_ARG;
+    const size_t es = elem_size(dtype);
+    const size_t nt = (size_t)H * T;
+    const size_t state_bytes = NH * d_v * d_k * 4;
+    if (T > 0) {
+        if (!q || !k || !v || !beta || !o) return GDR_ERR_INVALID_ARG;
+        if ((alpha_mode == GDR_ALPHA_NONE) != (log_alpha == nullptr)) return GDR_ERR_INVALID_ARG;
+    }
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(S0, 16) || !aligned(S_final, 16) || !aligned(workspace, 16) ||
+        !aligned(beta, 4) || !aligned(log_alpha, alpha_mode == GDR_ALPHA_CHANNEL ? 16 : 4))
+        return GDR_ERR_INVALID_ARG;
+
+    const size_t la_bytes = alpha_mode == GDR_ALPHA_CHANNEL ? nt * d_k * 4
+                          : alpha_mode == GDR_ALPHA_SCALAR ? nt * 4 : 0;
+    const Range rq = rng(q, nt * d_k * es), rk = rng(k, nt * d_k * es), rv = rng(v, nt * d_v * es);
+    const Range rb = rng(beta, nt * 4), ra = rng(log_alpha, la_bytes);
+    const Range r0 = rng(S0, state_bytes), ro = rng(o, nt * d_v * es);
+    const Range rf = rng(S_final, state_bytes), rc = rng(cu_seqlens, ((size_t)N + 1) * 4);
+    const size_t need = gdr::varlen_workspace_bytes(N, H, T, d_k, d_v, C, dtype, alpha_mode);
+    const Range rw = rng(workspace, need);
+    for (Range x : {rq, rk, rv, rb, ra, r0, rf, rw, rc})
+        if (overlap(ro, x)) return GDR_ERR_INVALID_ARG;
+    for (Range x : {rq, rk, rv, rb, ra, rw, rc})
+        if (overlap(rf, x)) return GDR_ERR_INVALID_ARG;
+    if (overlap(rf, r0) && (const void*)S_final != (const void*)S0) return GDR_ERR_INVALID_ARG;
+    for (Range x : {rq, rk, rv, rb, ra, r0, rc})
+        if (overlap(rw, x)) return GDR_ERR_INVALID_ARG;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GDR_ERR_WORKSPACE_TOO_SMALL;
+
+    gdr::ChunkArgs a{1, H, T, d_k, d_v, C, dtype, alpha_mode, q, k, v, beta, log_alpha, S0, o,
+                     S_final, workspace, stream, prologue, cu_seqlens, N, gdr::Varlen{}};
+    return gdr::launch_fwd_varlen(a) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }

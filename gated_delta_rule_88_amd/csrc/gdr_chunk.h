@@ -65,12 +65,40 @@ __host__ __device__ constexpr WsLayout ws_layout(int ES, int DK, int CK, int MOD
     return WsLayout{t, m, f, kg, kg + ch, kg + 2 * ch, kg + 3 * ch};
 }
 
+// The chunk in record slot cid: its first token on the token axis
+// (head-row * L + position) and its number of tokens (0 for a slot no
+// sequence fills).
+struct ChunkSlot {
+    size_t tok;
+    int valid;
+};
+
+__device__ __forceinline__ ChunkSlot chunk_slot(const Varlen& vl, int L, int NC, int CK, int cid)
+{
+    if (!vl.start) {
+        const int bh = cid / NC, n = cid % NC;
+        return ChunkSlot{(size_t)bh * L + (size_t)n * CK, min(CK, L - n * CK)};
+    }
+    const int h = cid / vl.NCmax, j = cid % vl.NCmax;
+    if (j >= vl.choff[vl.NS]) return ChunkSlot{0, 0};
+    // the sequence s with choff[s] <= j < choff[s + 1]
+    int lo = 0, hi = vl.NS;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (vl.choff[mid] <= j) lo = mid;
+        else hi = mid;
+    }
+    const int c = j - vl.choff[lo];
+    return ChunkSlot{(size_t)h * L + vl.start[lo] + (size_t)c * CK, min(CK, vl.len[lo] - c * CK)};
+}
+
 struct WyParams {
     const void *q, *k;
     const float *beta, *log_alpha;   // log_alpha NULL: alpha = 1
     unsigned char* ws;
-    int L, NC, total;   // total = B * H * NC chunks
+    int L, NC, total;   // total = B * H * NC chunks (varlen: H * NCmax)
     unsigned pro;       // input-side prologue (kProNorm, kProGates)
+    Varlen vl;
 };
 
 struct ScanParams {
@@ -86,6 +114,10 @@ struct ScanParams {
     void* qt;       // [B*H][L][d_k] (input dtype): (transition from the segment start) q_t
     float* Sseg;    // [B*H][SEG][d_v][d_k]: segment end state from S0 (g = 0) or zero (g > 0)
     float* Pseg;    // [B*H][SEG][d_k][d_k]: segment transition (g > 0)
+    // Packed variable-length batch (vl.start != NULL; one segment): chain
+    // n * H + h is sequence n of head h, total = NS * H * NVB workgroups.
+    int H;
+    Varlen vl;
 };
 
 // Segment-parallel scan.  A head's chunk scan is one sequential chain; when

@@ -28,6 +28,16 @@ struct DecodeArgs {
     unsigned pro;
 };
 
+// Packed variable-length batch: NS sequences along one head row of L tokens
+// (L = T, the packed length).  Per sequence, computed on the device from the
+// caller's cumulative offsets (clamped into [0, T]): its first token, its
+// length and its first chunk; choff[NS] is the number of chunks per head,
+// at most NCmax = T / CK + NS.  Chunk records are [H][NCmax].
+struct Varlen {
+    const int *start, *len, *choff;   // start == NULL: fixed-length batch
+    int NS, NCmax;
+};
+
 struct ChunkArgs {
     int B, H, L, dk, dv, C, dtype, mode;
     const void *q, *k, *v;
@@ -37,12 +47,19 @@ struct ChunkArgs {
     void* workspace;
     hipStream_t stream;
     unsigned pro;
+    // packed variable-length batch (B = 1, L = T): cumulative offsets
+    // [NS + 1] in device memory, or NULL; vl is filled in by the driver
+    const int* cu_seqlens;
+    int NS;
+    Varlen vl;
 };
 
 // Bytes of device workspace the chunked forward needs.
 size_t chunk_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int dtype, int mode);
+size_t varlen_workspace_bytes(int NS, int H, int T, int dk, int dv, int C, int dtype, int mode);
 
 hipError_t launch_decode_step(const DecodeArgs& a);
 hipError_t launch_fwd_chunked(const ChunkArgs& a);
+hipError_t launch_fwd_varlen(ChunkArgs a);
 
 }  // namespace gdr

@@ -257,7 +257,11 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
     // once its entry state is known.
     int bh, vb, sg = 0;
     bool keyrows = false;
-    {
+    if (p.vl.start) {
+        // packed variable-length batch: chain bh = n * H + h, one segment
+        bh = lid / p.NVB;
+        vb = lid % p.NVB;
+    } else {
         const int per_seg = p.NVB + p.NMB;
         const int units = p.NVB + (p.SEG - 1) * per_seg;
         bh = lid / units;
@@ -274,7 +278,28 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
     }
     const int v0 = vb * BV;                            // first value channel (key row for key rows)
     const int c0 = sg * p.NCS;                         // first chunk
-    const int NC = min(p.NCS, p.NC - c0);              // chunks this workgroup walks
+    // the chain's tokens: head row start on the token axis, length, first record
+    size_t tok0 = (size_t)bh * p.L, rec0 = (size_t)bh * p.NC;
+    int len = p.L;
+    int NC = min(p.NCS, p.NC - c0);                    // chunks this workgroup walks
+    if (p.vl.start) {
+        const int n = bh / p.H, h = bh % p.H;
+        const int cb = p.vl.choff[n];
+        tok0 = (size_t)h * p.L + p.vl.start[n];
+        len = p.vl.len[n];
+        rec0 = (size_t)h * p.vl.NCmax + cb;
+        NC = min((len + CK - 1) / CK, max(0, p.vl.NCmax - cb));
+        if (NC == 0) {
+            // an empty sequence: its final state is its initial state
+            if (w < 2 && p.S_final) {
+                const size_t r = ((size_t)bh * p.DV + v0 + 16 * w + c16) * DK;
+                for (int c = 4 * g4; c < DK; c += 16)
+                    *reinterpret_cast<f32x4*>(p.S_final + r + c) =
+                        p.S0 ? *reinterpret_cast<const f32x4*>(p.S0 + r + c) : zero4();
+            }
+            return;   // workgroup-uniform, before any barrier
+        }
+    }
     if (keyrows) {
         // key rows carry no values: the V slots stay zero
         for (int i = threadIdx.x; i < NSLOT * szV / 16; i += 64 * LY::NWAVES)
@@ -514,9 +539,8 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
         // ===================================================== output waves
         const int c = w - 2, vw = v0 + 16 * c;
         // key rows write (transition so far) q_t, d_k per token, to p.qt
-        E* og = keyrows ? reinterpret_cast<E*>(p.qt) + (size_t)bh * p.L * DK
-                        : reinterpret_cast<E*>(p.o) + (size_t)bh * p.L * p.DV;
         const int ostride = keyrows ? DK : p.DV;
+        E* og = (keyrows ? reinterpret_cast<E*>(p.qt) : reinterpret_cast<E*>(p.o)) + tok0 * ostride;
         const int oXS = lane_base(LY::rxS + (c * NKS * kWave + l) * FS);
         const int oXU = lane_base(LY::rxU + (c * kWave + l) * FS);
         // Gamma tile (rb, ib): row c16 (+16 rb), tokens 16ib + 4g .. +3
@@ -538,7 +562,7 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
             constexpr int cK = LY::rK + J * szK, cQ = J * szK;
             constexpr int cM = J * szT, cF = J * szF;
             constexpr int pS = (J & 1) * LY::XSB, pU = (J & 1) * LY::XUB;   // m & 1 == J & 1
-            const int t0 = (c0 + m) * CK, valid = min(CK, p.L - t0);
+            const int t0 = (c0 + m) * CK, valid = min(CK, len - t0);
             // ---- reads
             Frag<E> sop[NKS];
 #pragma unroll
@@ -681,9 +705,9 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
         };
         auto issue = [&](auto jc, int m) {
             constexpr int J = decltype(jc)::value;
-            const int t0 = (c0 + m) * CK, valid = min(CK, p.L - t0);
-            const unsigned char* rec = p.ws + ((size_t)bh * p.NC + c0 + m) * WL.bytes;
-            const size_t row0 = (size_t)bh * p.L + t0;
+            const int t0 = (c0 + m) * CK, valid = min(CK, len - t0);
+            const unsigned char* rec = p.ws + (rec0 + c0 + m) * WL.bytes;
+            const size_t row0 = tok0 + t0;
             using NK = std::integral_constant<int, LY::NCK>;
             using NV = std::integral_constant<int, LY::NCV>;
             using NT = std::integral_constant<int, LY::NCT>;
@@ -775,10 +799,10 @@ static hipError_t launch_scan_t(const ChunkArgs& a, const SegPlan& seg)
     const int BH = a.B * a.H;
     const int NC = (a.L + CK - 1) / CK;
     const int NVB = a.dv / LY::BV, NMB = DK / 32;
-    const int total = BH * (NVB + (seg.SEG - 1) * (NVB + NMB));
+    const int total = a.vl.start ? a.vl.NS * a.H * NVB : BH * (NVB + (seg.SEG - 1) * (NVB + NMB));
     unsigned char* ws = static_cast<unsigned char*>(a.workspace);
     ScanParams sp{a.q, a.k, a.v, a.S0, ws, a.o, a.S_final, a.L, NC, a.dv, NVB, total,
-                  seg.SEG, seg.NCS, NMB, nullptr, nullptr, nullptr};
+                  seg.SEG, seg.NCS, NMB, nullptr, nullptr, nullptr, a.H, a.vl};
     if (seg.SEG > 1) {
         sp.qt = ws + seg.off_qt;
         sp.Sseg = reinterpret_cast<float*>(ws + seg.off_Z);

@@ -193,8 +193,9 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
     const int cid = blockIdx.x * 4 + w;
     if (cid >= p.total) return;   // wave-uniform; this kernel has no block barrier
     const int l = lane_id(), g4 = l >> 4, c16 = l & 15;
-    const int bh = cid / p.NC, n = cid % p.NC;
-    const int t0 = n * CK, valid = min(CK, p.L - t0);
+    const ChunkSlot cs = chunk_slot(p.vl, p.L, p.NC, CK, cid);
+    const size_t tok = cs.tok;   // first token on the token axis
+    const int valid = cs.valid;
 
     unsigned char* sw = smem + w * SC::bytes;
     float* Af = reinterpret_cast<float*>(sw + SC::off_A);
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
     // their tiles are dropped before the key tiles are loaded
     float nk = 1.f, nq = 1.f;   // for token l
     if (pro & kProNorm) {
-        const E* qc = reinterpret_cast<const E*>(p.q) + ((size_t)bh * p.L + t0) * DK;
+        const E* qc = reinterpret_cast<const E*>(p.q) + tok * DK;
         Frag<E> qf[NB][NKS];
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb)
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
 
     // K tiles of the chunk as MFMA operands, straight from global memory
     // (scaled to unit rows by the prologue)
-    const E* kc = reinterpret_cast<const E*>(p.k) + ((size_t)bh * p.L + t0) * DK;
+    const E* kc = reinterpret_cast<const E*>(p.k) + tok * DK;
     Frag<E> kf[NB][NKS];
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb)
@@ -242,8 +243,8 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
     // (log alpha = 0 for alpha = 1)
     float bt = 0.f, la = 0.f;
     if (l < valid) {
-        bt = p.beta[(size_t)bh * p.L + t0 + l];
-        if (p.log_alpha) la = p.log_alpha[(size_t)bh * p.L + t0 + l];
+        bt = p.beta[tok + l];
+        if (p.log_alpha) la = p.log_alpha[tok + l];
         if (pro & kProGates) {
             bt = sigmoid_f(bt);
             if (p.log_alpha) la = log_sigmoid_f(la);
@@ -379,11 +380,11 @@ __global__ __launch_bounds__(256, 3) void chunk_wy_channel_kernel(WyParams p)
     f32x4 gr[NGV];
     float br = 0.f;
     auto fetch = [&](int cid) {
-        const int bh = cid / p.NC, n = cid % p.NC;
-        const int t0 = n * CK, valid = min(CK, p.L - t0);
-        const E* kc = reinterpret_cast<const E*>(p.k) + ((size_t)bh * p.L + t0) * DK;
-        const E* qc = reinterpret_cast<const E*>(p.q) + ((size_t)bh * p.L + t0) * DK;
-        const float* lac = p.log_alpha + ((size_t)bh * p.L + t0) * DK;
+        const ChunkSlot cs = chunk_slot(p.vl, p.L, p.NC, CK, cid);
+        const int valid = cs.valid;
+        const E* kc = reinterpret_cast<const E*>(p.k) + cs.tok * DK;
+        const E* qc = reinterpret_cast<const E*>(p.q) + cs.tok * DK;
+        const float* lac = p.log_alpha + cs.tok * DK;
 #pragma unroll
         for (int j = 0; j < NKV; ++j) {
             const int i = tid + 256 * j, r = i / RV, c = (i % RV) * VE;
@@ -400,7 +401,7 @@ __global__ __launch_bounds__(256, 3) void chunk_wy_channel_kernel(WyParams p)
             gr[j] = zero4();
             if (i < CK * RF && r < valid) gr[j] = *reinterpret_cast<const f32x4*>(lac + (size_t)r * DK + c);
         }
-        br = (tid < valid) ? p.beta[(size_t)bh * p.L + t0 + tid] : 0.f;
+        br = (tid < valid) ? p.beta[cs.tok + tid] : 0.f;
     };
     if ((int)blockIdx.x < p.total) fetch(blockIdx.x);
     for (int cid = blockIdx.x; cid < p.total; cid += gridDim.x) {
@@ -408,7 +409,7 @@ __global__ __launch_bounds__(256, 3) void chunk_wy_channel_kernel(WyParams p)
 
     // ---- stage K, Q and log alpha (floored; zero past the end), beta; the
     // prologue's gate activations apply to the chunk's valid tokens
-    const int valid = min(CK, p.L - (cid % p.NC) * CK);
+    const int valid = chunk_slot(p.vl, p.L, p.NC, CK, cid).valid;
 #pragma unroll
     for (int j = 0; j < NKV; ++j) {
         const int i = tid + 256 * j, r = i / RV, c = (i % RV) * VE;
@@ -599,8 +600,9 @@ template <typename E, int DK, int CK>
 static hipError_t launch_wy_t(const ChunkArgs& a)
 {
     const int NC = (a.L + CK - 1) / CK;
+    const int total = a.vl.start ? a.H * a.vl.NCmax : a.B * a.H * NC;   // record slots
     WyParams wp{a.q, a.k, a.beta, a.log_alpha, static_cast<unsigned char*>(a.workspace), a.L, NC,
-                a.B * a.H * NC, a.pro};
+                total, a.pro, a.vl};
     if (a.mode == kAlphaChannel) {
         using LY = WyChannelLayout<E, DK, CK>;
         static_assert(LY::bytes <= 160 * 1024, "LDS budget");

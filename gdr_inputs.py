@@ -85,6 +85,40 @@ DECODE_BF16 = DecodeWorkload("gdn_decode_bf16_N256_H16_d128", 256, 16, 128, 128,
                              torch.bfloat16, ALPHA_SCALAR, 5)
 
 
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    name: str
+    N: int          # sequences packed per call
+    H: int
+    T: int          # packed tokens per head
+    dk: int
+    dv: int
+    C: int
+    dtype: torch.dtype
+    mode: int
+    seed: int
+
+    @property
+    def tokens(self) -> int:
+        return self.T
+
+
+# The headline's 16 384 tokens per head (8 x 2048) as a packed prefill batch of
+# 16 prompts of mixed length.
+VARLEN_GDN_BF16 = VarlenWorkload("gdn_bf16_varlen_N16_H8_T16384_d128", 16, 8, 16384, 128, 128, 64,
+                                 torch.bfloat16, ALPHA_SCALAR, 6)
+
+
+def varlen_lengths(N: int, T: int, seed: int) -> list[int]:
+    """N sequence lengths summing to T: log-uniform draws over [64, 4096]
+    scaled to the total (each at least 1)."""
+    g = torch.Generator().manual_seed(seed)
+    raw = torch.exp(torch.empty(N).uniform_(4.1589, 8.3178, generator=g))   # ln 64 .. ln 4096
+    lens = [max(1, int(x)) for x in (raw / raw.sum() * T)]
+    lens[int(torch.argmax(raw))] += T - sum(lens)
+    return lens
+
+
 def _l2norm(x: torch.Tensor) -> torch.Tensor:
     n = x.norm(dim=-1, keepdim=True)
     return x / torch.clamp(n, min=1e-6)

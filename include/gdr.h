@@ -168,6 +168,55 @@ int gdr_fwd_chunked_ex(int B, int H, int L, int d_k, int d_v, int C, int dtype,
                        unsigned prologue);
 
 /*
+ * Bytes of device workspace gdr_fwd_varlen needs (0 when N * H == 0), or
+ * (size_t)-1 for invalid or unsupported sizes.  It is sized for any split
+ * of the T tokens into N sequences: chunk records for at most
+ * (T + N (C' - 1)) / C' chunks per head (C' = 32, or 16 for GDR_F32 or
+ * C == 16), plus three ints per sequence.
+ */
+size_t gdr_fwd_varlen_workspace_size(int N, int H, int T, int d_k, int d_v, int C,
+                                     int dtype, int alpha_mode);
+
+/*
+ * Chunkwise forward over a packed batch of N sequences of different lengths
+ * (prefill of several prompts in one call).  The sequences lie back to back
+ * on one token axis of T tokens per head; sequence n owns tokens
+ * [cu_seqlens[n], cu_seqlens[n + 1]) and runs the recurrence of
+ * gdr_fwd_chunked from its own initial state to its own final state.  Chunks
+ * never straddle two sequences, so each sequence's result is the one a
+ * separate call would give, up to rounding.  ("linear attention and its
+ * gated descendants", "Chunkwise Parallel Form", applied per sequence; the
+ * chunk form itself is that of gdr_fwd_chunked.)
+ *
+ *   N, H       sequences and heads (>= 0; N * H == 0 => nothing to do)
+ *   T          packed tokens per head (>= 0)
+ *   cu_seqlens [N + 1] int32 in DEVICE memory, read by the kernels (no host
+ *              synchronisation): cumulative offsets, cu_seqlens[0] = 0,
+ *              non-decreasing, cu_seqlens[N] = T.  Offsets outside [0, T]
+ *              are clamped and a decreasing one gives an empty sequence;
+ *              tokens no sequence covers are left unwritten in o.  No such
+ *              input makes the library touch memory outside the arrays.
+ *   q, k       [H][T][d_k];  v, o [H][T][d_v] (dtype)
+ *   beta       [H][T] float
+ *   log_alpha  NULL | [H][T] | [H][T][d_k] float, as for gdr_fwd_chunked
+ *   S0         NULL => zero initial states, else [N][H][d_v][d_k] float
+ *   S_final    NULL or [N][H][d_v][d_k] float (may equal S0); an empty
+ *              sequence's final state is its initial state
+ *   workspace  at least gdr_fwd_varlen_workspace_size(...) bytes
+ *   prologue   gdr_prologue bits, as for gdr_fwd_chunked_ex
+ * Other arguments, alignment, aliasing rules and errors as for
+ * gdr_fwd_chunked (cu_seqlens 4-byte aligned, and it must not overlap o,
+ * S_final or the workspace).  Always one scan chain per (sequence, head):
+ * the segment-parallel scan of gdr_fwd_chunked is not used here.
+ */
+int gdr_fwd_varlen(int N, int H, int T, const int *cu_seqlens, int d_k, int d_v, int C, int dtype,
+                   const void *q, const void *k, const void *v,
+                   const float *beta, int alpha_mode, const float *log_alpha,
+                   const float *S0, void *o, float *S_final,
+                   void *workspace, size_t workspace_bytes, hipStream_t stream,
+                   unsigned prologue);
+
+/*
  * One recurrent decode step for N sequences x H heads (the constant-memory
  * inference form: "linear attention and its gated descendants", "Recurrent
  * Linear Attention for Inference": O(d^2) work and memory per token).  The

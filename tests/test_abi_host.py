@@ -198,6 +198,57 @@ def test_prologue_entry_points_validate_like_the_plain_ones(lib):
                                       p(O), None, pro) == gdr.GDR_ERR_INVALID_ARG
 
 
+def test_varlen_workspace_size_query():
+    ws = gdr.gdr_fwd_varlen_workspace_size
+    # records for (T + N (CK - 1)) / CK chunks per head, then three int
+    # arrays (start, length: N each; first chunk: N + 1), each 256-aligned
+    ncmax = (100 + 3 * 31) // 32
+    assert ws(3, 2, 100, 64, 64, 64, gdr.GDR_BF16, 1) == 2 * ncmax * (4096 + 512) + 3 * 256
+    ncmax = (1000 + 5 * 15) // 16
+    rec = 2 * 16 * 16 * 4 + 4 * 16 * 4                     # fp32, scalar layout (alpha = 1)
+    assert ws(5, 1, 1000, 128, 128, 64, gdr.GDR_F32, 0) == (ncmax * rec + 255) // 256 * 256 + 3 * 256
+    assert ws(0, 4, 100, 64, 64, 64, gdr.GDR_BF16, 1) == 0
+    assert ws(2, 0, 100, 64, 64, 64, gdr.GDR_BF16, 1) == 0
+    for bad in [(-1, 1, 64, 128, 128, 64, 1, 1), (1, 1, -1, 128, 128, 64, 1, 1),
+                (1, 1, 64, 96, 128, 64, 1, 1), (1, 1, 64, 128, 128, 64, 1, 5)]:
+        assert ws(*bad) == SIZE_MAX, bad
+
+
+CU = A + 9 * (1 << 32)
+
+
+def varlen(lib, N=2, H=1, T=64, cu=CU, dk=64, dv=64, C=64, dtype=1, q=Q, k=K, v=V, beta=BETA,
+           mode=1, la=LA, s0=S0, o=O, sf=SF, ws=WS, ws_bytes=1 << 30, pro=0):
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gdr_fwd_varlen(N, H, T, p(cu), dk, dv, C, dtype, p(q), p(k), p(v), p(beta), mode,
+                              p(la), p(s0), p(o), p(sf), p(ws), ws_bytes, None, pro)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), gdr.GDR_ERR_INVALID_ARG),
+    (dict(cu=CU + 2), gdr.GDR_ERR_INVALID_ARG),               # misaligned offsets
+    (dict(o=CU - 64), gdr.GDR_ERR_INVALID_ARG),               # o overlaps the offsets
+    (dict(ws=CU), gdr.GDR_ERR_INVALID_ARG),                   # workspace overlaps the offsets
+    (dict(N=-1), gdr.GDR_ERR_INVALID_ARG),
+    (dict(T=-3), gdr.GDR_ERR_INVALID_ARG),
+    (dict(pro=4), gdr.GDR_ERR_INVALID_ARG),
+    (dict(dk=32), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(C=8), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(q=None), gdr.GDR_ERR_INVALID_ARG),
+    (dict(mode=0), gdr.GDR_ERR_INVALID_ARG),                  # log_alpha with mode NONE
+    (dict(sf=S0 + 64), gdr.GDR_ERR_INVALID_ARG),
+    (dict(ws_bytes=16), gdr.GDR_ERR_WORKSPACE_TOO_SMALL),
+    (dict(ws=None, ws_bytes=0), gdr.GDR_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_varlen_rejects_before_launch(lib, kw, status):
+    assert varlen(lib, **kw) == status
+
+
+def test_varlen_empty_is_a_noop(lib):
+    assert varlen(lib, N=0, cu=None) == gdr.GDR_OK
+    assert varlen(lib, H=0) == gdr.GDR_OK
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 1, 4, 64)
