@@ -5,9 +5,10 @@ the CPU-baseline leg of ``bench.py`` may import this package.  The product
 path (``gated_delta_rule_88_amd``) never imports, links or executes it, and
 this package imports nothing from the product path.
 
-The recurrence lives in ``gdr_oracle.c`` (plain C, double precision, one
-token at a time); see that file's header for the recurrence and the passages
-it follows.  This wrapper converts arrays to contiguous float64 and calls
+The recurrence and its reverse mode (gradients, for training) live in
+``gdr_oracle.c`` (plain C, double precision, one token at a time); see that
+file for the recurrence, the passages it follows and the per-token chain
+rule of the backward.  This wrapper converts arrays to contiguous float64 and calls
 it.  The only arithmetic written here is the optional input-side prologue
 (``prologue``): unit-norm queries and keys and the sigmoid gates, applied
 elementwise in float64 before the recurrence runs.
@@ -53,6 +54,8 @@ def _load():
         lib.gdr_oracle_run.argtypes = [ctypes.c_int] * 6 + [dp] * 8 + [ctypes.c_int]
         lib.gdr_oracle_run.restype = ctypes.c_int
         lib.gdr_oracle_max_threads.restype = ctypes.c_int
+        lib.gdr_oracle_backward.argtypes = [ctypes.c_int] * 5 + [dp] * 14 + [ctypes.c_int]
+        lib.gdr_oracle_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -163,3 +166,72 @@ def run(q, k, v, beta, log_alpha=None, S0=None, mode: int | None = None,
     if rc != 0:
         raise RuntimeError("oracle run failed")
     return o, S
+
+
+def backward(q, k, v, beta, log_alpha=None, S0=None, do=None, dS_final=None,
+             mode: int | None = None, nthreads: int = 0, pro: int = 0):
+    """Gradients of the token recurrence (reverse mode, fp64), for a loss
+    whose gradient with respect to the outputs is ``do`` [..., L, dv] and
+    with respect to the final state ``dS_final`` (None = 0).
+
+    Shapes as ``run``.  Returns a dict with dq, dk [..., L, dk], dv
+    [..., L, dv], dbeta [..., L], dlog_alpha (None | like log_alpha) and dS0
+    [..., dv, dk].  With ``pro`` the inputs are taken raw, the prologue is
+    applied first and the gradients are with respect to the raw inputs
+    (chained through the prologue by ``prologue_backward``).
+    """
+    if pro:
+        raw = (q, k, beta, log_alpha)
+        q, k, beta, log_alpha = prologue(q, k, beta, log_alpha, pro)
+    q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
+    la, s0, dout, dsf = _f64(log_alpha), _f64(S0), _f64(do), _f64(dS_final)
+    lead = q.shape[:-2]
+    L, dk = q.shape[-2:]
+    dv = v.shape[-1]
+    if mode is None:
+        mode = ALPHA_NONE if la is None else (ALPHA_CHANNEL if la.shape == q.shape
+                                              else ALPHA_SCALAR)
+    if mode == ALPHA_NONE:
+        la = None
+    if dout is None or dout.shape != v.shape:
+        raise ValueError("do must have the shape of v")
+    if dsf is not None and dsf.shape != lead + (dv, dk):
+        raise ValueError("dS_final must be [..., dv, dk]")
+    BH = int(np.prod(lead)) if lead else 1
+    g = dict(dq=np.zeros(q.shape), dk=np.zeros(q.shape), dv=np.zeros(v.shape),
+             dbeta=np.zeros(beta.shape), dlog_alpha=None if la is None else np.zeros(la.shape),
+             dS0=np.zeros(lead + (dv, dk)))
+    rc = _load().gdr_oracle_backward(BH, L, dk, dv, int(mode), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(beta), _ptr(la), _ptr(s0), _ptr(dout), _ptr(dsf),
+                                     _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+                                     _ptr(g["dbeta"]), _ptr(g["dlog_alpha"]), _ptr(g["dS0"]),
+                                     int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle backward failed")
+    if pro:
+        g = prologue_backward(*raw, g, pro)
+    return g
+
+
+def prologue_backward(q_raw, k_raw, beta_raw, la_raw, g: dict, flags: int) -> dict:
+    """Chain gradients with respect to the prologue's outputs back to its raw
+    inputs: for y = x / max(||x||, eps), dx = (dy - y (y . dy)) / ||x|| while
+    ||x|| > eps (dx = dy / eps below the floor); for beta = sigmoid(b),
+    db = dbeta beta (1 - beta); for log alpha = log sigmoid(a),
+    da = dlog_alpha (1 - sigmoid(a))."""
+    g = dict(g)
+    if flags & PRO_L2NORM_QK:
+        for name, x in (("dq", q_raw), ("dk", k_raw)):
+            x = _f64(x)
+            n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+            y = x / np.maximum(n, NORM_EPS)
+            dy = g[name]
+            inside = n > NORM_EPS
+            g[name] = np.where(inside, (dy - y * np.sum(y * dy, axis=-1, keepdims=True))
+                               / np.maximum(n, NORM_EPS), dy / NORM_EPS)
+    if flags & PRO_GATES:
+        b = sigmoid(beta_raw)
+        g["dbeta"] = g["dbeta"] * b * (1.0 - b)
+        if g["dlog_alpha"] is not None:
+            g["dlog_alpha"] = g["dlog_alpha"] * (1.0 - sigmoid(la_raw))
+    return g

@@ -423,3 +423,114 @@ def test_prologue_rejects_unknown_bits():
     x = np.zeros((2, 4))
     with pytest.raises(ValueError):
         oracle.prologue(x, x, np.zeros(2), None, 4)
+
+
+# --------------------------------------------------------------------------
+# gradients (reverse mode of the token recurrence)
+def _fd_grads(loss, args, h=1e-6):
+    """Central finite differences of loss(**args) for every array argument."""
+    out = {}
+    for name, x in args.items():
+        if x is None:
+            continue
+        fd = np.zeros(np.shape(x))
+        for idx in np.ndindex(fd.shape):
+            xp, xm = np.array(x, dtype=np.float64), np.array(x, dtype=np.float64)
+            xp[idx] += h
+            xm[idx] -= h
+            fd[idx] = (loss(**{**args, name: xp}) - loss(**{**args, name: xm})) / (2 * h)
+        out[name] = fd
+    return out
+
+
+GRAD_NAMES = dict(q="dq", k="dk", v="dv", beta="dbeta", la="dlog_alpha", S0="dS0")
+
+
+@pytest.mark.parametrize("mode", [NONE, SCALAR, CHANNEL])
+def test_backward_matches_finite_differences(mode):
+    """Every gradient of L = <o, do> + <S_final, dS_final> against central
+    differences of the forward oracle, over 70 tokens (the backward keeps a
+    state every 64 tokens and recomputes the rest)."""
+    rng = np.random.default_rng(40 + mode)
+    q, k, v, beta, la, S0 = _rand_chain(rng, 70, 5, 3, mode)
+    do = rng.standard_normal((70, 3))
+    dSf = rng.standard_normal((3, 5))
+
+    def loss(q, k, v, beta, la, S0):
+        o, S = oracle.run(q, k, v, beta, la, S0, mode=mode, nthreads=1)
+        return float(np.sum(o * do) + np.sum(S * dSf))
+
+    g = oracle.backward(q, k, v, beta, la, S0, do, dSf, mode=mode, nthreads=1)
+    fd = _fd_grads(loss, dict(q=q, k=k, v=v, beta=beta, la=la, S0=S0))
+    for name, ref in fd.items():
+        got = g[GRAD_NAMES[name]]
+        assert np.max(np.abs(got - ref)) / max(1.0, np.max(np.abs(ref))) < 1e-7, name
+    if mode == NONE:
+        assert g["dlog_alpha"] is None
+
+
+def test_backward_first_token_closed_form():
+    """L = 1 from S0: o = S_1 q with S_1 = a S0 + beta (v - a S0 k) k^T, so
+    dv = beta (k.q) do, dq = S_1^T do, dk = beta (v - a S0 k).do q - beta a S0^T do (k.q),
+    dbeta = (k.q) (v - a S0 k).do, dS0 = a do (q - beta (k.q) k)^T,
+    dlog a = a <do (q - beta (k.q) k)^T, S0>."""
+    rng = np.random.default_rng(41)
+    dk_, dv_ = 6, 4
+    q, k = _unit(rng.standard_normal(dk_)), _unit(rng.standard_normal(dk_))
+    v, S0, do = rng.standard_normal(dv_), rng.standard_normal((dv_, dk_)), rng.standard_normal(dv_)
+    b, la = 0.7, -0.4
+    a = math.exp(la)
+    r = v - a * S0 @ k
+    S1 = a * S0 + b * np.outer(r, k)
+    g = oracle.backward(q[None], k[None], v[None], np.array([b]), np.array([la]), S0, do[None],
+                        None, mode=SCALAR, nthreads=1)
+    kq = k @ q
+    assert np.allclose(g["dv"][0], b * kq * do, atol=1e-13)
+    assert np.allclose(g["dq"][0], S1.T @ do, atol=1e-13)
+    assert np.allclose(g["dk"][0], b * (r @ do) * q - b * a * kq * (S0.T @ do), atol=1e-13)
+    assert np.allclose(g["dbeta"][0], kq * (r @ do), atol=1e-13)
+    w = q - b * kq * k
+    assert np.allclose(g["dS0"], a * np.outer(do, w), atol=1e-13)
+    assert np.allclose(g["dlog_alpha"][0], a * np.sum(np.outer(do, w) * S0), atol=1e-13)
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3])
+def test_backward_through_the_prologue(flags):
+    """Gradients with respect to raw q, k and gate pre-activations against
+    finite differences of run(raw, pro=flags)."""
+    rng = np.random.default_rng(42 + flags)
+    L, dk_, dv_ = 9, 4, 3
+    q = rng.standard_normal((L, dk_)) * 3.0
+    k = rng.standard_normal((L, dk_)) * 0.5
+    v = rng.standard_normal((L, dv_))
+    b = rng.standard_normal(L)
+    a = -(rng.standard_normal((L, dk_)) + 2.0)
+    if not flags & 1:
+        q, k = _unit(q), _unit(k)
+    if not flags & 2:
+        b, a = 1.0 / (1.0 + np.exp(-b)), -np.log1p(np.exp(-a))
+    S0 = 0.3 * rng.standard_normal((dv_, dk_))
+    do = rng.standard_normal((L, dv_))
+
+    def loss(q, k, v, beta, la, S0):
+        o, _ = oracle.run(q, k, v, beta, la, S0, mode=CHANNEL, pro=flags, nthreads=1)
+        return float(np.sum(o * do))
+
+    g = oracle.backward(q, k, v, b, a, S0, do, None, mode=CHANNEL, pro=flags, nthreads=1)
+    fd = _fd_grads(loss, dict(q=q, k=k, v=v, beta=b, la=a, S0=S0))
+    for name, ref in fd.items():
+        got = g[GRAD_NAMES[name]]
+        assert np.max(np.abs(got - ref)) / max(1.0, np.max(np.abs(ref))) < 1e-7, name
+
+
+def test_backward_chains_are_independent():
+    rng = np.random.default_rng(43)
+    chains = [_rand_chain(rng, 11, 4, 3, SCALAR) for _ in range(4)]
+    dos = [rng.standard_normal((11, 3)) for _ in range(4)]
+    stack = lambda i: np.stack([c[i] for c in chains]).reshape((2, 2) + np.shape(chains[0][i]))
+    g = oracle.backward(*[stack(i) for i in range(6)], np.stack(dos).reshape(2, 2, 11, 3), None,
+                        nthreads=2)
+    for j, c in enumerate(chains):
+        gj = oracle.backward(*c, dos[j], None, mode=SCALAR, nthreads=1)
+        for name in ("dq", "dk", "dv", "dbeta", "dlog_alpha", "dS0"):
+            assert np.array_equal(g[name][j // 2, j % 2], gj[name]), name
