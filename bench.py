@@ -221,6 +221,40 @@ def bench_varlen(w, steps, warmup, copies):
     return dict(total_ms=e0.elapsed_time(e1), lengths=lens)
 
 
+def bench_backward(w, steps, warmup, copies):
+    """gdr_bwd_chunked on the workload's inputs with a random output gradient
+    (the forward is recomputed inside every call)."""
+    import gated_delta_rule_88_amd as gdr
+
+    dev = torch.device("cuda:0")
+    sets = []
+    for c in range(copies):
+        x = gi.chunked_inputs(w.B, w.H, w.L, w.dk, w.dv, w.dtype, w.mode, w.seed + 1000 * c,
+                              w.s0_std)
+        g = torch.Generator().manual_seed(w.seed + 1000 * c + 7)
+        x["dO"] = torch.randn(w.B, w.H, w.L, w.dv, generator=g).to(w.dtype)
+        sets.append({k: (None if t is None else t.to(dev)) for k, t in x.items()})
+    code = gdr.GDR_BF16 if w.dtype == torch.bfloat16 else gdr.GDR_F32
+    need = gdr.gdr_bwd_chunked_workspace_size(w.B, w.H, w.L, w.dk, w.dv, w.C, code, w.mode)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        d = sets[i % copies]
+        gdr.gdr_bwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["S0"], d["dO"],
+                            None, w.C, workspace=ws)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    e0, e1 = _events(2)
+    e0.record()
+    for i in range(steps):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return dict(total_ms=e0.elapsed_time(e1), ws_bytes=need)
+
+
 def bench_decode(w, steps, prologue=0):
     import gated_delta_rule_88_amd as gdr
 
@@ -296,6 +330,9 @@ def main():
     ap.add_argument("--cpu-chains", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the chunked backward (gradients) on --workload instead (one JSON "
+                         "line of its own)")
     ap.add_argument("--varlen", action="store_true",
                     help="time the packed variable-length forward on its length-mix workload "
                          "instead (one JSON line of its own)")
@@ -318,6 +355,31 @@ def main():
 
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.backward:
+        w = WORKLOADS[args.workload]
+        r = bench_backward(w, args.steps, args.warmup, min(args.copies, 2))
+        ms = r["total_ms"] / args.steps
+        es = 2 if w.dtype == torch.bfloat16 else 4
+        ht = w.B * w.H * w.L
+        gate = 0 if w.mode == gi.ALPHA_NONE else 4
+        # read q, k, v, dO, beta, log alpha; write dq, dk, dv, dbeta, dlog alpha
+        nbytes = ht * (es * (3 * w.dk + 3 * w.dv) + 8 + 2 * gate)
+        print(json.dumps({
+            "metric": "tokens/s chunked GDN backward (gradients; forward recomputed inside)",
+            "value": w.tokens / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+            "data": "synthetic",
+            "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d_k": w.dk, "d_v": w.dv,
+                       "C": w.C, "alpha": gi.MODE_NAMES[w.mode], "workspace_bytes": r["ws_bytes"]},
+            "roofline": {"bound": "hbm", "achieved": nbytes / (ms / 1e3) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "chunk_wy_kernel + chunk_scan_kernel + chunk_bwd_chain_kernel "
+                                   "+ chunk_bwd_grad_kernel",
+                         "algorithmic_bytes_per_call": nbytes},
+        }))
         return
     if args.varlen:
         vw = gi.VARLEN_GDN_BF16

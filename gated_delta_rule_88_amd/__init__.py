@@ -34,7 +34,8 @@ GDR_PRO_L2NORM_QK, GDR_PRO_GATES = 1, 2
 
 EXPORTED = ("gdr_abi_version", "gdr_status_string", "gdr_fwd_chunked_workspace_size",
             "gdr_fwd_chunked", "gdr_fwd_chunked_ex", "gdr_fwd_varlen_workspace_size",
-            "gdr_fwd_varlen", "gdr_decode_step", "gdr_decode_step_ex")
+            "gdr_fwd_varlen", "gdr_bwd_chunked_workspace_size", "gdr_bwd_chunked",
+            "gdr_decode_step", "gdr_decode_step_ex")
 
 _lib = None
 
@@ -69,6 +70,10 @@ def load_library():
     lib.gdr_fwd_varlen.argtypes = [i] * 3 + [vp] + [i] * 4 + [vp] * 4 + [i] + [vp] * 5 + [sz, vp,
                                                                                         ctypes.c_uint]
     lib.gdr_fwd_varlen.restype = i
+    lib.gdr_bwd_chunked_workspace_size.argtypes = [i] * 8
+    lib.gdr_bwd_chunked_workspace_size.restype = sz
+    lib.gdr_bwd_chunked.argtypes = [i] * 7 + [vp] * 4 + [i] + [vp] * 11 + [sz, vp]
+    lib.gdr_bwd_chunked.restype = i
     lib.gdr_decode_step.argtypes = [i] * 5 + [vp] * 4 + [i] + [vp] * 4
     lib.gdr_decode_step.restype = i
     lib.gdr_decode_step_ex.argtypes = lib.gdr_decode_step.argtypes + [ctypes.c_uint]
@@ -179,6 +184,54 @@ def gdr_fwd_chunked(q, k, v, beta, log_alpha=None, S0=None, chunk: int = 64, *,
     if st != GDR_OK:
         raise GdrError(st, name)
     return o, S_final
+
+
+def gdr_bwd_chunked_workspace_size(B, H, L, d_k, d_v, C, dtype, alpha_mode) -> int:
+    return int(load_library().gdr_bwd_chunked_workspace_size(B, H, L, d_k, d_v, C, dtype,
+                                                             alpha_mode))
+
+
+def gdr_bwd_chunked(q, k, v, beta, log_alpha, S0, dO, dS_final=None, chunk: int = 64, *,
+                    want_dS0: bool = True, workspace=None, stream=None):
+    """Gradients of gdr_fwd_chunked for output gradient dO [B,H,L,dv] (dtype
+    of q) and final-state gradient dS_final (None | [B,H,dv,dk] fp32).
+    Returns a dict of dq, dk, dv (dtype of q), dbeta, dlog_alpha (None for
+    alpha = 1) and dS0 (fp32, or None)."""
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, L, d_k]")
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    mode = _mode_of(log_alpha, q)
+    _check(q, "q", dt, dev, (B, H, L, dk))
+    _check(k, "k", dt, dev, (B, H, L, dk))
+    _check(v, "v", dt, dev, (B, H, L, dv))
+    _check(beta, "beta", torch.float32, dev, (B, H, L))
+    if mode == GDR_ALPHA_SCALAR:
+        _check(log_alpha, "log_alpha", torch.float32, dev, (B, H, L))
+    _check(S0, "S0", torch.float32, dev, (B, H, dv, dk))
+    _check(dO, "dO", dt, dev, (B, H, L, dv))
+    _check(dS_final, "dS_final", torch.float32, dev, (B, H, dv, dk))
+    g = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+             dbeta=torch.empty_like(beta),
+             dlog_alpha=None if log_alpha is None else torch.empty_like(log_alpha),
+             dS0=torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_dS0 else None)
+    need = gdr_bwd_chunked_workspace_size(B, H, L, dk, dv, chunk, code, mode)
+    if need == ctypes.c_size_t(-1).value:
+        raise GdrError(GDR_ERR_UNSUPPORTED, "gdr_bwd_chunked_workspace_size")
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdr_bwd_chunked(B, H, L, dk, dv, chunk, code, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                             mode, _ptr(log_alpha), _ptr(S0), _ptr(dO), _ptr(dS_final),
+                             _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dbeta"]),
+                             _ptr(g["dlog_alpha"]), _ptr(g["dS0"]), _ptr(workspace), ws_bytes,
+                             _stream(stream))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_bwd_chunked")
+    return g
 
 
 def gdr_fwd_varlen_workspace_size(N, H, T, d_k, d_v, C, dtype, alpha_mode) -> int:

@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdr.so")
-SOURCES = ["gdr_api.hip", "gdr_decode.hip", "gdr_fwd.hip", "gdr_wy.hip", "gdr_scan.hip", "gdr_segment.hip"]
+SOURCES = ["gdr_api.hip", "gdr_decode.hip", "gdr_fwd.hip", "gdr_wy.hip", "gdr_scan.hip", "gdr_segment.hip",
+           "gdr_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU forms are switched off for every device pass; the host

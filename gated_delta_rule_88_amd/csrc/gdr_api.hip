@@ -232,3 +232,61 @@ GDR_EXPORT int gdr_fwd_varlen(int N, int H, int T, const int* cu_seqlens, int d_
                      S_final, workspace, stream, prologue, cu_seqlens, N, gdr::Varlen{}};
     return gdr::launch_fwd_varlen(a) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
+
+GDR_EXPORT size_t gdr_bwd_chunked_workspace_size(int B, int H, int L, int d_k, int d_v, int C,
+                                                 int dtype, int alpha_mode)
+{
+    if (check_chunk_sizes(B, H, L, d_k, d_v, C, dtype, alpha_mode) != GDR_OK) return (size_t)-1;
+    if (alpha_mode == GDR_ALPHA_CHANNEL) return (size_t)-1;
+    return gdr::bwd_workspace_bytes(B, H, L, d_k, d_v, C, dtype);
+}
+
+GDR_EXPORT int gdr_bwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                               const void* q, const void* k, const void* v,
+                               const float* beta, int alpha_mode, const float* log_alpha,
+                               const float* S0, const void* dO, const float* dS_final,
+                               void* dq, void* dk, void* dv, float* dbeta, float* dlog_alpha,
+                               float* dS0, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream)
+{
+    int st = check_chunk_sizes(B, H, L, d_k, d_v, C, dtype, alpha_mode);
+    if (st != GDR_OK) return st;
+    if (alpha_mode == GDR_ALPHA_CHANNEL) return GDR_ERR_UNSUPPORTED;
+    const size_t BH = (size_t)B * H;
+    if (BH == 0) return GDR_OK;
+    const size_t es = elem_size(dtype);
+    const size_t nt = BH * L;
+    const size_t state_bytes = BH * d_v * d_k * 4;
+    if (L > 0) {
+        if (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta) return GDR_ERR_INVALID_ARG;
+        if ((alpha_mode == GDR_ALPHA_NONE) != (log_alpha == nullptr)) return GDR_ERR_INVALID_ARG;
+        if ((alpha_mode == GDR_ALPHA_NONE) != (dlog_alpha == nullptr)) return GDR_ERR_INVALID_ARG;
+    }
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dO, 16) || !aligned(dq, 16) ||
+        !aligned(dk, 16) || !aligned(dv, 16) || !aligned(S0, 16) || !aligned(dS_final, 16) ||
+        !aligned(dS0, 16) || !aligned(workspace, 16) || !aligned(beta, 4) || !aligned(log_alpha, 4) ||
+        !aligned(dbeta, 4) || !aligned(dlog_alpha, 4))
+        return GDR_ERR_INVALID_ARG;
+
+    const size_t la_bytes = alpha_mode == GDR_ALPHA_SCALAR ? nt * 4 : 0;
+    const Range rq = rng(q, nt * d_k * es), rk = rng(k, nt * d_k * es), rv = rng(v, nt * d_v * es);
+    const Range rb = rng(beta, nt * 4), ra = rng(log_alpha, la_bytes), r0 = rng(S0, state_bytes);
+    const Range rdo = rng(dO, nt * d_v * es), rdf = rng(dS_final, state_bytes);
+    const Range oq = rng(dq, nt * d_k * es), ok = rng(dk, nt * d_k * es), ov = rng(dv, nt * d_v * es);
+    const Range ob = rng(dbeta, nt * 4), oa = rng(dlog_alpha, la_bytes), o0 = rng(dS0, state_bytes);
+    const size_t need = gdr::bwd_workspace_bytes(B, H, L, d_k, d_v, C, dtype);
+    const Range rw = rng(workspace, need);
+    const Range ins[] = {rq, rk, rv, rb, ra, r0, rdo, rdf};
+    const Range outs[] = {oq, ok, ov, ob, oa, o0, rw};
+    for (int i = 0; i < 7; ++i) {
+        for (Range x : ins)
+            if (overlap(outs[i], x)) return GDR_ERR_INVALID_ARG;
+        for (int j = 0; j < i; ++j)
+            if (overlap(outs[i], outs[j])) return GDR_ERR_INVALID_ARG;
+    }
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GDR_ERR_WORKSPACE_TOO_SMALL;
+
+    gdr::BwdArgs a{B, H, L, d_k, d_v, C, dtype, alpha_mode, q, k, v, beta, log_alpha, S0, dO, dS_final,
+                   dq, dk, dv, dbeta, dlog_alpha, dS0, workspace, stream};
+    return gdr::launch_bwd_chunked(a) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}

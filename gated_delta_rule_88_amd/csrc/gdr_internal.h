@@ -52,6 +52,20 @@ struct ChunkArgs {
     const int* cu_seqlens;
     int NS;
     Varlen vl;
+    // backward's forward recompute: every chunk's entry state, or null
+    float* Sck;
+};
+
+struct BwdArgs {
+    int B, H, L, dk, dv, C, dtype, mode;
+    const void *q, *k, *v;
+    const float *beta, *log_alpha, *S0;
+    const void* dO;
+    const float* dS_final;
+    void *dq, *dk_out, *dv_out;
+    float *dbeta, *dlog_alpha, *dS0;
+    void* workspace;
+    hipStream_t stream;
 };
 
 // Bytes of device workspace the chunked forward needs.
@@ -61,5 +75,7 @@ size_t varlen_workspace_bytes(int NS, int H, int T, int dk, int dv, int C, int d
 hipError_t launch_decode_step(const DecodeArgs& a);
 hipError_t launch_fwd_chunked(const ChunkArgs& a);
 hipError_t launch_fwd_varlen(ChunkArgs a);
+size_t bwd_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int dtype);
+hipError_t launch_bwd_chunked(const BwdArgs& b);
 
 }  // namespace gdr

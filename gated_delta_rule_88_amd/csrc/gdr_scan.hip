@@ -512,7 +512,16 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
                 constexpr int J = decltype(jc)::value;
                 const int s = s0 + J;
                 if (s <= NC) {
-                    if (s < NC) own(jc, s);
+                    if (s < NC) {
+                        if (p.Sck) {
+                            // the state entering chunk s, for the backward
+                            float* ck = p.Sck + (((size_t)bh * p.NC + c0 + s) * p.DV + vw + c16) * DK;
+#pragma unroll
+                            for (int a = 0; a < NKT; ++a)
+                                *reinterpret_cast<f32x4*>(ck + 32 * (a >> 1) + 8 * g4 + 4 * (a & 1)) = sT[a];
+                        }
+                        own(jc, s);
+                    }
                     step_barrier();
                 }
             };
@@ -802,7 +811,7 @@ static hipError_t launch_scan_t(const ChunkArgs& a, const SegPlan& seg)
     const int total = a.vl.start ? a.vl.NS * a.H * NVB : BH * (NVB + (seg.SEG - 1) * (NVB + NMB));
     unsigned char* ws = static_cast<unsigned char*>(a.workspace);
     ScanParams sp{a.q, a.k, a.v, a.S0, ws, a.o, a.S_final, a.L, NC, a.dv, NVB, total,
-                  seg.SEG, seg.NCS, NMB, nullptr, nullptr, nullptr, a.H, a.vl};
+                  seg.SEG, seg.NCS, NMB, nullptr, nullptr, nullptr, a.H, a.vl, a.Sck};
     if (seg.SEG > 1) {
         sp.qt = ws + seg.off_qt;
         sp.Sseg = reinterpret_cast<float*>(ws + seg.off_Z);

@@ -168,6 +168,46 @@ int gdr_fwd_chunked_ex(int B, int H, int L, int d_k, int d_v, int C, int dtype,
                        unsigned prologue);
 
 /*
+ * Bytes of device workspace gdr_bwd_chunked needs (0 when B * H == 0 or
+ * L == 0), or (size_t)-1 for invalid or unsupported sizes (channel alpha
+ * included).  It holds the forward's chunk records, the state entering every
+ * chunk and the state gradient at every chunk's end (fp32 d_v x d_k per
+ * chunk each, chunks of 32 tokens, or 16 for GDR_F32 or C == 16) and the
+ * recomputed outputs.
+ */
+size_t gdr_bwd_chunked_workspace_size(int B, int H, int L, int d_k, int d_v, int C,
+                                      int dtype, int alpha_mode);
+
+/*
+ * Backward of gdr_fwd_chunked (training): for a loss with gradient dO with
+ * respect to the outputs o and dS_final with respect to the final state,
+ * the gradients with respect to q, k, v, beta, log alpha and S0.  The
+ * forward is recomputed inside the call from the same inputs (nothing from
+ * the forward call is kept).  The result is the derivative of the
+ * recurrence of gdr_fwd_chunked, taken chunk by chunk ("linear attention and
+ * its gated descendants", "Chunkwise Parallel Form" and "Gated DeltaNet").
+ *
+ *   B, H, L, d_k, d_v, C, dtype, q, k, v, beta, S0   as for gdr_fwd_chunked
+ *   alpha_mode GDR_ALPHA_NONE or GDR_ALPHA_SCALAR (GDR_ALPHA_CHANNEL gives
+ *              GDR_ERR_UNSUPPORTED); log_alpha as for gdr_fwd_chunked
+ *   dO         [B][H][L][d_v] (dtype)
+ *   dS_final   NULL (zero) or [B][H][d_v][d_k] float
+ *   dq, dk     [B][H][L][d_k] (dtype);  dv [B][H][L][d_v] (dtype)
+ *   dbeta      [B][H][L] float
+ *   dlog_alpha NULL for GDR_ALPHA_NONE, else [B][H][L] float
+ *   dS0        NULL (not written) or [B][H][d_v][d_k] float
+ *   workspace  at least gdr_bwd_chunked_workspace_size(...) bytes
+ * Outputs must not overlap any input, each other or the workspace.  Errors
+ * as for gdr_fwd_chunked.
+ */
+int gdr_bwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                    const void *q, const void *k, const void *v,
+                    const float *beta, int alpha_mode, const float *log_alpha,
+                    const float *S0, const void *dO, const float *dS_final,
+                    void *dq, void *dk, void *dv, float *dbeta, float *dlog_alpha,
+                    float *dS0, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Bytes of device workspace gdr_fwd_varlen needs (0 when N * H == 0), or
  * (size_t)-1 for invalid or unsupported sizes.  It is sized for any split
  * of the T tokens into N sequences: chunk records for at most

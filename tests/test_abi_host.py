@@ -249,6 +249,48 @@ def test_varlen_empty_is_a_noop(lib):
     assert varlen(lib, H=0) == gdr.GDR_OK
 
 
+def test_backward_workspace_size_query():
+    ws = gdr.gdr_bwd_chunked_workspace_size
+    # records, the state entering and the gradient leaving every chunk (fp32
+    # d_v x d_k each), the recomputed outputs; each region 256-aligned
+    nc = 2048 // 32
+    rec = 64 * nc * (2048 + 2048 + 512)
+    st = 64 * nc * 128 * 128 * 4
+    assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 1) == rec + 2 * st + 64 * 2048 * 128 * 2
+    assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 2) == SIZE_MAX      # channel gates
+    assert ws(1, 2, 0, 64, 64, 64, gdr.GDR_F32, 1) == 0
+
+
+def bwd(lib, B=1, H=1, L=64, dk=64, dv=64, C=64, dtype=1, mode=1, la=LA, ws_bytes=1 << 30, **kw):
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    ptr = dict(q=Q, k=K, v=V, beta=BETA, s0=S0, dO=A + 10 * (1 << 32), dsf=A + 11 * (1 << 32),
+               dq=A + 12 * (1 << 32), dkp=A + 13 * (1 << 32), dvp=A + 14 * (1 << 32),
+               db=A + 15 * (1 << 32), dla=A + 16 * (1 << 32), ds0=A + 17 * (1 << 32), ws=WS)
+    ptr.update(kw)
+    return lib.gdr_bwd_chunked(B, H, L, dk, dv, C, dtype, p(ptr["q"]), p(ptr["k"]), p(ptr["v"]),
+                               p(ptr["beta"]), mode, p(la), p(ptr["s0"]), p(ptr["dO"]), p(ptr["dsf"]),
+                               p(ptr["dq"]), p(ptr["dkp"]), p(ptr["dvp"]), p(ptr["db"]), p(ptr["dla"]),
+                               p(ptr["ds0"]), p(ptr["ws"]), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mode=2), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(dk=96), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(dO=None), gdr.GDR_ERR_INVALID_ARG),
+    (dict(dq=None), gdr.GDR_ERR_INVALID_ARG),
+    (dict(dla=None), gdr.GDR_ERR_INVALID_ARG),                  # scalar gates need dlog_alpha
+    (dict(mode=0, la=None), gdr.GDR_ERR_INVALID_ARG),           # alpha = 1 takes no dlog_alpha
+    (dict(dq=Q), gdr.GDR_ERR_INVALID_ARG),                      # dq overlaps q
+    (dict(dkp=A + 12 * (1 << 32) + 64), gdr.GDR_ERR_INVALID_ARG),  # dk overlaps dq
+    (dict(ds0=S0 + 16), gdr.GDR_ERR_INVALID_ARG),               # dS0 overlaps S0
+    (dict(dq=Q + 8), gdr.GDR_ERR_INVALID_ARG),                  # misaligned
+    (dict(ws_bytes=16), gdr.GDR_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_backward_rejects_before_launch(lib, kw, status):
+    assert status != gdr.GDR_OK   # every case must stop before a launch
+    assert bwd(lib, **kw) == status
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 1, 4, 64)
