@@ -55,29 +55,41 @@ __device__ __forceinline__ void pack_frag<float>(Frag<float>& f, const float* x)
     f.hi = f32x4{x[4], x[5], x[6], x[7]};
 }
 
-// acc += A B^T on one 16 x 16 tile: A(m, k) = A[m * ars + k * aks] for rows
-// m0 .. m0 + 15, B(n, k) = B[n * brs + k * bks] for rows n0 .. n0 + 15, over
-// k < K (zero-filled up to the next multiple of 32).  Operands are gathered
-// element by element, so any layout serves; lane (g, c) ends with
+// 8 consecutive elements of a row as floats (16-byte aligned reads), zero
+// when they lie at or past K.
+__device__ __forceinline__ void load8f(const bf16* p, float* x) { Pack<bf16>::unpack(ld16(p), x); }
+__device__ __forceinline__ void load8f(const float* p, float* x) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// Operand fragment of a row-major [rows][ld] array (contraction index
+// contiguous): lane reads row row0 + l % 16, k = k0 + 8 (l / 16) .. + 7.
+template <typename E, typename T>
+__device__ __forceinline__ Frag<E> cfrag(const T* base, int ld, int row0, int k0, int K) {
+    const int l = lane_id(), k = k0 + 8 * (l >> 4);
+    const T* p = base + (row0 + (l & 15)) * ld + k;
+    Frag<E> f;
+    if constexpr (sizeof(E) == 2 && sizeof(T) == 2) {
+        f.v = k < K ? *reinterpret_cast<const bf16x8*>(p) : bf16x8{};
+    } else {
+        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (k < K) load8f(p, x);
+        pack_frag<E>(f, x);
+    }
+    return f;
+}
+
+// acc += A B^T on one 16 x 16 tile, A = rows m0.. of a row-major [.][lda]
+// array, B = rows n0.. of [.][ldb], contracting over k < K (a multiple of 8,
+// zero-filled to the next multiple of 32).  Lane (g, c) ends with
 // acc[e] = (A B^T)[m0 + 4 g + e][n0 + c].
 template <typename E, typename TA, typename TB>
-__device__ __forceinline__ void tmma(f32x4& acc, const TA* A, int ars, int aks, int m0,
-                                     const TB* B, int brs, int bks, int n0, int K)
+__device__ __forceinline__ void tmma(f32x4& acc, const TA* A, int lda, int m0, const TB* B, int ldb, int n0,
+                                     int K)
 {
-    const int l = lane_id(), r = l & 15, g = l >> 4;
-    for (int k0 = 0; k0 < K; k0 += 32) {
-        float xa[8], xb[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int k = k0 + 8 * g + j;
-            xa[j] = k < K ? to_f32(A[(m0 + r) * ars + k * aks]) : 0.f;
-            xb[j] = k < K ? to_f32(B[(n0 + r) * brs + k * bks]) : 0.f;
-        }
-        Frag<E> fa, fb;
-        pack_frag<E>(fa, xa);
-        pack_frag<E>(fb, xb);
-        mma(acc, fa, fb);
-    }
+    for (int k0 = 0; k0 < K; k0 += 32) mma(acc, cfrag<E>(A, lda, m0, k0, K), cfrag<E>(B, ldb, n0, k0, K));
 }
 
 // Sum of x over the 16 lanes that share l / 16 (one tile row).
@@ -87,32 +99,81 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// Rows of a [ROWS][ld] global array into registers, 16 bytes per read, NT
+// threads (every read of the stage in flight at once); rows at or past
+// `valid` read as zero.  Then into LDS, plain [ROWS][COLS] (row stride LD)
+// and transposed [COLS][ROWS] (row stride LT).  Consecutive threads take
+// consecutive rows, so the transposed 2- or 4-byte stores of a wave land in
+// consecutive LDS words.
+template <typename E, int ROWS, int COLS, int NT>
+struct RowStage {
+    static constexpr int VE = Vec<E>::n, PER = COLS / VE, NV = (ROWS * PER + NT - 1) / NT;
+    u32x4 v[NV];
+    __device__ __forceinline__ void load(const E* src, int ld, int valid, int tid) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int x = tid + NT * j, r = x % ROWS, c = (x / ROWS) * VE;
+            v[j] = u32x4{0u, 0u, 0u, 0u};
+            if (x < ROWS * PER && r < valid) v[j] = ld16(src + (size_t)r * ld + c);
+        }
+    }
+    __device__ __forceinline__ void store(E* dst, int LD, E* dstT, int LT, int tid) const {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int x = tid + NT * j, r = x % ROWS, c = (x / ROWS) * VE;
+            if (x < ROWS * PER) {
+                st16(dst + r * LD + c, v[j]);
+                E e[VE];
+                __builtin_memcpy(e, &v[j], 16);
+#pragma unroll
+                for (int i = 0; i < VE; ++i) dstT[(c + i) * LT + r] = e[i];
+            }
+        }
+    }
+};
+
 struct BwdParams {
     const void *q, *k, *v, *dO;
     const float *beta, *log_alpha;   // log_alpha NULL: alpha = 1
     const float* dS_final;           // [B*H][d_v][d_k] or null
     const unsigned char* ws;         // forward prepass records
-    const float* Sck;                // [B*H][NC][d_v][d_k]: state entering each chunk
-    float* dSck;                     // [B*H][NC][d_v][d_k]: dS at each chunk's end
+    const void* Sck;                 // [B*H][NC][d_v][d_k] (operand type): state entering each chunk
+    void* dSck;                      // [B*H][NC][d_v][d_k] (operand type): dS at each chunk's end
     void *dq, *dk, *dv;
     float *dbeta, *dlog_alpha, *dS0;
     int L, NC, DV, total;
 };
 
+// LDS row strides: every row padded by 16 bytes, so that the 16 rows a
+// fragment read touches (and the rows a transposed store walks) fall on
+// different banks.
+template <typename E, int DK, int CK>
+struct Strides {
+    static constexpr int PE = 16 / (int)sizeof(E);
+    static constexpr int LDK = DK + PE;    // rows of d_k elements
+    static constexpr int LCK = CK + PE;    // rows of CK elements
+    static constexpr int LBV = kBV + PE;   // rows of kBV elements
+    static constexpr int LF = CK + 4;      // fp32 rows of CK
+    static constexpr int LBF = kBV + 4;    // fp32 rows of kBV
+};
+
 // ---------------------------------------------------------------- chain
 template <typename E, int DK, int CK>
-struct ChainLds {
+struct ChainLds : Strides<E, DK, CK> {
+    using S = Strides<E, DK, CK>;
     static constexpr int ES = (int)sizeof(E);
-    static constexpr int off_K = 0;                          // [CK][DK] E
-    static constexpr int off_Q = off_K + CK * DK * ES;       // [CK][DK] E
-    static constexpr int off_dO = off_Q + CK * DK * ES;      // [CK][kBV] E
-    static constexpr int off_gdO = off_dO + CK * kBV * ES;   // gamma . dO
-    static constexpr int off_T = off_gdO + CK * kBV * ES;    // [CK][CK] f32, T~
-    static constexpr int off_M = off_T + CK * CK * 4;        // [CK][CK] f32, Gamma . M_incl
-    static constexpr int off_P = off_M + CK * CK * 4;        // [CK][CK] f32
-    static constexpr int off_f = off_P + CK * CK * 4;        // gamma [CK], D [CK], gamma_C
-    static constexpr int off_w = off_f + (2 * CK + 4) * 4;   // per wave: dS [16][DK], dU, -gamma dR [CK][16]
-    static constexpr int wbytes = 16 * DK * ES + 2 * CK * 16 * ES;
+    static constexpr int off_K = 0;                            // [CK][LDK] E
+    static constexpr int off_Kt = off_K + CK * S::LDK * ES;    // [DK][LCK] E
+    static constexpr int off_Q = off_Kt + DK * S::LCK * ES;    // [CK][LDK] E
+    static constexpr int off_Qt = off_Q + CK * S::LDK * ES;    // [DK][LCK] E
+    static constexpr int off_dOt = off_Qt + DK * S::LCK * ES;  // [kBV][LCK] E, dO^T
+    static constexpr int off_gdOt = off_dOt + kBV * S::LCK * ES;   // (gamma . dO)^T
+    static constexpr int off_Tt = off_gdOt + kBV * S::LCK * ES;    // [CK][LCK] E, T~^T
+    static constexpr int off_Pt = off_Tt + CK * S::LCK * ES;       // [CK][LCK] E, P^T
+    static constexpr int off_M = off_Pt + CK * S::LCK * ES;        // [CK][LF] f32, Gamma . M_incl
+    static constexpr int off_f = off_M + CK * S::LF * 4;           // gamma [CK], D [CK], gamma_C
+    static constexpr int off_w = off_f + (2 * CK + 4) * 4;         // per wave: dS [16][LDK], dU^T, -gamma dR^T [16][LCK]
+    static constexpr int wbytes = 16 * S::LDK * ES + 2 * 16 * S::LCK * ES;
     static constexpr int bytes = off_w + 2 * wbytes;
 };
 
@@ -120,22 +181,25 @@ template <typename E, int DK, int CK>
 __global__ __launch_bounds__(128) void chunk_bwd_chain_kernel(BwdParams p)
 {
     using LY = ChainLds<E, DK, CK>;
-    constexpr int NJ = DK / 16, NB = CK / 16;
+    constexpr int NJ = DK / 16, NB = CK / 16, VE = Vec<E>::n;
+    constexpr int LDK = LY::LDK, LCK = LY::LCK, LF = LY::LF;
     constexpr WsLayout WL = ws_layout((int)sizeof(E), DK, CK, kAlphaScalar);
     extern __shared__ __align__(16) unsigned char smem[];
     E* Ks = reinterpret_cast<E*>(smem + LY::off_K);
+    E* Kt = reinterpret_cast<E*>(smem + LY::off_Kt);
     E* Qs = reinterpret_cast<E*>(smem + LY::off_Q);
-    E* dOs = reinterpret_cast<E*>(smem + LY::off_dO);
-    E* gdOs = reinterpret_cast<E*>(smem + LY::off_gdO);
-    float* Ts = reinterpret_cast<float*>(smem + LY::off_T);
+    E* Qt = reinterpret_cast<E*>(smem + LY::off_Qt);
+    E* dOt = reinterpret_cast<E*>(smem + LY::off_dOt);
+    E* gdOt = reinterpret_cast<E*>(smem + LY::off_gdOt);
+    E* Tts = reinterpret_cast<E*>(smem + LY::off_Tt);
+    E* Pt = reinterpret_cast<E*>(smem + LY::off_Pt);
     float* Ms = reinterpret_cast<float*>(smem + LY::off_M);
-    float* Ps = reinterpret_cast<float*>(smem + LY::off_P);
     float* gam = reinterpret_cast<float*>(smem + LY::off_f);
     float* Dd = gam + CK;
     const int tid = threadIdx.x, w = wave_id(), l = lane_id(), g4 = l >> 4, c16 = l & 15;
-    E* dSw = reinterpret_cast<E*>(smem + LY::off_w + w * LY::wbytes);   // [16][DK]
-    E* dUw = dSw + 16 * DK;                                             // [CK][16]
-    E* dRw = dUw + CK * 16;                                             // -gamma dR, [CK][16]
+    E* dSw = reinterpret_cast<E*>(smem + LY::off_w + w * LY::wbytes);   // [16][LDK]
+    E* dUt = dSw + 16 * LDK;                                            // [16][LCK]
+    E* dRt = dUt + 16 * LCK;                                            // -gamma dR, [16][LCK]
 
     const int nvb = p.DV / kBV;
     const int bh = blockIdx.x / nvb, v0 = (blockIdx.x % nvb) * kBV;
@@ -152,82 +216,113 @@ __global__ __launch_bounds__(128) void chunk_bwd_chain_kernel(BwdParams p)
                 dS[jb][e] = p.dS_final[((size_t)bh * p.DV + i0 + 4 * g4 + e) * DK + 16 * jb + c16];
     }
 
-    for (int n = p.NC - 1; n >= 0; --n) {
-        const int t0 = n * CK, valid = min(CK, p.L - t0);
-        const size_t tok = (size_t)bh * p.L + t0;
+    // The next chunk's inputs wait in registers: its reads are issued as soon
+    // as the current chunk's are in LDS, and land while it is worked on.
+    constexpr int NRV = CK * CK / VE;            // 16-byte vectors of T~ (and of Gamma)
+    constexpr int PERO = kBV / VE;               // 16-byte vectors per token of the dO block
+    constexpr int NOV = (CK * PERO + 127) / 128;
+    RowStage<E, CK, DK, 128> ks, qs;
+    u32x4 tv, mv, ov[NOV];
+    float fv;
+    auto fetch = [&](int n) {
+        const int valid = min(CK, p.L - n * CK);
+        const size_t tok = (size_t)bh * p.L + n * CK;
         const unsigned char* rec = p.ws + ((size_t)bh * p.NC + n) * WL.bytes;
-        // ---- stage the chunk; keep dS at the chunk's end
-        const E* kg = reinterpret_cast<const E*>(p.k) + tok * DK;
-        const E* qg = reinterpret_cast<const E*>(p.q) + tok * DK;
+        ks.load(reinterpret_cast<const E*>(p.k) + tok * DK, DK, valid, tid);
+        qs.load(reinterpret_cast<const E*>(p.q) + tok * DK, DK, valid, tid);
+        tv = mv = u32x4{0u, 0u, 0u, 0u};
+        if (tid < NRV) {
+            tv = ld16(rec + WL.T + 16 * tid);
+            mv = ld16(rec + WL.M + 16 * tid);
+        }
+        fv = tid <= 2 * CK ? reinterpret_cast<const float*>(rec + WL.F)[tid] : 0.f;
         const E* dog = reinterpret_cast<const E*>(p.dO) + tok * p.DV + v0;
-        const E* Tg = reinterpret_cast<const E*>(rec + WL.T);
-        const E* Mg = reinterpret_cast<const E*>(rec + WL.M);
-        const float* Fg = reinterpret_cast<const float*>(rec + WL.F);
-        if (tid < CK) {
-            gam[tid] = Fg[tid];
-            Dd[tid] = Fg[CK + tid];
+#pragma unroll
+        for (int j = 0; j < NOV; ++j) {
+            const int x = tid + 128 * j, r = x % CK, c = (x / CK) * VE;
+            ov[j] = (x < CK * PERO && r < valid) ? ld16(dog + (size_t)r * p.DV + c) : u32x4{0u, 0u, 0u, 0u};
         }
-        if (tid == 0) gam[2 * CK] = Fg[2 * CK];
-        for (int x = tid; x < CK * DK; x += 128) {
-            const int r = x / DK;
-            Ks[x] = r < valid ? kg[x] : from_f32<E>(0.f);
-            Qs[x] = r < valid ? qg[x] : from_f32<E>(0.f);
+    };
+    fetch(p.NC - 1);
+
+    for (int n = p.NC - 1; n >= 0; --n) {
+        // ---- the chunk into LDS; keep dS at the chunk's end
+        ks.store(Ks, LDK, Kt, LCK, tid);
+        qs.store(Qs, LDK, Qt, LCK, tid);
+        if (tid < NRV) {
+            const int r = (VE * tid) / CK, mc0 = (VE * tid) % CK;
+            E te[VE];
+            float me[VE];
+            __builtin_memcpy(te, &tv, 16);
+            Pack<E>::unpack(mv, me);
+#pragma unroll
+            for (int j = 0; j < VE; ++j) {
+                const int t = tok_of_col(CK, mc0 + j);
+                Tts[t * LCK + r] = te[j];
+                Ms[r * LF + t] = me[j];
+            }
         }
-        for (int x = tid; x < CK * CK; x += 128) {
-            const int r = x / CK, mc = x % CK, t = tok_of_col(CK, mc);
-            Ts[r * CK + t] = to_f32(Tg[x]);
-            Ms[r * CK + t] = to_f32(Mg[x]);
+        if (tid <= 2 * CK) gam[tid] = fv;   // gamma, D (Dd = gam + CK), gamma_C
+#pragma unroll
+        for (int j = 0; j < NOV; ++j) {
+            const int x = tid + 128 * j, r = x % CK, c = (x / CK) * VE;
+            if (x < CK * PERO) {
+                E d[VE];
+                __builtin_memcpy(d, &ov[j], 16);
+#pragma unroll
+                for (int i = 0; i < VE; ++i) dOt[(c + i) * LCK + r] = d[i];
+            }
         }
-        float* dsk = p.dSck + (((size_t)bh * p.NC + n) * p.DV + i0) * DK;
+        E* dsk = static_cast<E*>(p.dSck) + (((size_t)bh * p.NC + n) * p.DV + i0) * DK;
 #pragma unroll
         for (int jb = 0; jb < NJ; ++jb)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * g4 + e, j = 16 * jb + c16;
-                dsk[(size_t)i * DK + j] = dS[jb][e];
-                dSw[i * DK + j] = from_f32<E>(dS[jb][e]);
+                dsk[(size_t)i * DK + j] = from_f32<E>(dS[jb][e]);
+                dSw[i * LDK + j] = from_f32<E>(dS[jb][e]);
             }
+        if (n > 0) fetch(n - 1);
         __syncthreads();
+        // (gamma . dO)^T
         for (int x = tid; x < CK * kBV; x += 128) {
-            const int r = x / kBV, i = x % kBV;
-            const float d = r < valid ? to_f32(dog[(size_t)r * p.DV + i]) : 0.f;
-            dOs[x] = from_f32<E>(d);
-            gdOs[x] = from_f32<E>(gam[r] * d);
+            const int r = x % CK, i = x / CK;
+            gdOt[i * LCK + r] = from_f32<E>(gam[r] * to_f32(dOt[i * LCK + r]));
         }
-        // ---- P = Q K^T . Gamma . M_incl (tiles on or below the diagonal)
+        // ---- P = Q K^T . Gamma . M_incl (tiles on or below the diagonal), kept as P^T
         for (int tl = w; tl < NB * NB; tl += 2) {
             const int rb = tl / NB, ib = tl % NB;
             f32x4 acc = zero4();
-            if (ib <= rb) tmma<E>(acc, Qs, DK, 1, 16 * rb, Ks, DK, 1, 16 * ib, DK);
+            if (ib <= rb) tmma<E>(acc, Qs, LDK, 16 * rb, Ks, LDK, 16 * ib, DK);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * g4 + e, s = 16 * ib + c16;
-                Ps[r * CK + s] = acc[e] * Ms[r * CK + s];
+                Pt[s * LCK + r] = from_f32<E>(acc[e] * Ms[r * LF + s]);
             }
         }
         __syncthreads();
-        // ---- dU = P^T dO + diag(D) K dS^T  (token r, value channel 16 w + c)
+        // ---- dU = P^T dO + diag(D) K dS^T  (token r, value channel 16 w + c), kept as dU^T
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb) {
             f32x4 kds = zero4(), y = zero4();
-            tmma<E>(kds, Ks, DK, 1, 16 * rb, dSw, DK, 1, 0, DK);
-            tmma<E>(y, Ps, 1, CK, 16 * rb, dOs + 16 * w, 1, kBV, 0, CK);
+            tmma<E>(kds, Ks, LDK, 16 * rb, dSw, LDK, 0, DK);
+            tmma<E>(y, Pt, LCK, 16 * rb, dOt + 16 * w * LCK, LCK, 0, CK);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * g4 + e;
-                dUw[r * 16 + c16] = from_f32<E>(y[e] + Dd[r] * kds[e]);
+                dUt[c16 * LCK + r] = from_f32<E>(y[e] + Dd[r] * kds[e]);
             }
         }
         wave_lds_fence();
-        // ---- dR = T~^T dU, kept as -gamma dR
+        // ---- dR = T~^T dU, kept as -gamma dR (transposed)
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb) {
             f32x4 dr = zero4();
-            tmma<E>(dr, Ts, 1, CK, 16 * rb, dUw, 1, 16, 0, CK);
+            tmma<E>(dr, Tts, LCK, 16 * rb, dUt, LCK, 0, CK);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * g4 + e;
-                dRw[r * 16 + c16] = from_f32<E>(-gam[r] * dr[e]);
+                dRt[c16 * LCK + r] = from_f32<E>(-gam[r] * dr[e]);
             }
         }
         wave_lds_fence();
@@ -238,8 +333,8 @@ __global__ __launch_bounds__(128) void chunk_bwd_chain_kernel(BwdParams p)
             f32x4 acc = dS[jb];
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] *= gC;
-            tmma<E>(acc, gdOs + 16 * w, 1, kBV, 0, Qs, 1, DK, 16 * jb, CK);
-            tmma<E>(acc, dRw, 1, 16, 0, Ks, 1, DK, 16 * jb, CK);
+            tmma<E>(acc, gdOt + 16 * w * LCK, LCK, 0, Qt, LCK, 16 * jb, CK);
+            tmma<E>(acc, dRt, LCK, 0, Kt, LCK, 16 * jb, CK);
             dS[jb] = acc;
         }
         __syncthreads();   // the LDS is restaged for the previous chunk
@@ -255,76 +350,84 @@ __global__ __launch_bounds__(128) void chunk_bwd_chain_kernel(BwdParams p)
 
 // ---------------------------------------------------------------- grads
 template <typename E, int DK, int CK>
-struct GradLds {
+struct GradLds : Strides<E, DK, CK> {
+    using S = Strides<E, DK, CK>;
     static constexpr int ES = (int)sizeof(E);
-    static constexpr int LF = CK + 4;                        // fp32 C x C row stride
-    static constexpr int off_K = 0;                          // [CK][DK] E
-    static constexpr int off_Q = off_K + CK * DK * ES;
-    static constexpr int off_S0 = off_Q + CK * DK * ES;      // [kBV][DK] E (one value block)
-    static constexpr int off_dS = off_S0 + kBV * DK * ES;
-    static constexpr int off_dO = off_dS + kBV * DK * ES;    // [CK][kBV] E
-    static constexpr int off_gdO = off_dO + CK * kBV * ES;
-    static constexpr int off_R = off_gdO + CK * kBV * ES;
-    static constexpr int off_U = off_R + CK * kBV * ES;
-    static constexpr int off_DU = off_U + CK * kBV * ES;
-    static constexpr int off_dU = off_DU + CK * kBV * ES;
-    static constexpr int off_dX = off_dU + CK * kBV * ES;
-    static constexpr int off_V = off_dX + CK * kBV * ES;     // [CK][kBV] f32
-    static constexpr int off_X = off_V + CK * kBV * 4;
-    static constexpr int off_KdS = off_X + CK * kBV * 4;
-    static constexpr int off_Bm = off_KdS + CK * kBV * 4;    // [CK][LF] f32 each
-    static constexpr int off_A = off_Bm + CK * LF * 4;
-    static constexpr int off_T = off_A + CK * LF * 4;
-    static constexpr int off_Tt = off_T + CK * LF * 4;       // T~ = T diag(beta)
-    static constexpr int off_P = off_Tt + CK * LF * 4;
-    static constexpr int off_dPW = off_P + CK * LF * 4;
-    static constexpr int off_Em = off_dPW + CK * LF * 4;     // dP . P, then dA . A
-    static constexpr int off_dTb = off_Em + CK * LF * 4;     // dT~ diag(beta)
-    static constexpr int off_dTt = off_dTb + CK * LF * 4;
-    static constexpr int off_Y1 = off_dTt + CK * LF * 4;
-    static constexpr int off_dA = off_Y1 + CK * LF * 4;
-    static constexpr int off_dG = off_dA + CK * LF * 4;
-    static constexpr int off_vec = off_dG + CK * LF * 4;     // g, gamma, D, beta, dg [CK]; parts
+    static constexpr int FCC = CK * S::LF * 4, ECC = CK * S::LCK * ES;
+    static constexpr int ECB = CK * S::LBV * ES, EBC = kBV * S::LCK * ES, FCB = CK * S::LBF * 4;
+    // kept for the whole chunk
+    static constexpr int off_K = 0;                            // [CK][LDK] E and [DK][LCK]
+    static constexpr int off_Kt = off_K + CK * S::LDK * ES;
+    static constexpr int off_Q = off_Kt + DK * S::LCK * ES;
+    static constexpr int off_Qt = off_Q + CK * S::LDK * ES;
+    static constexpr int off_Bm = off_Qt + DK * S::LCK * ES;   // [CK][LF] f32: K K^T . Gamma (strict)
+    static constexpr int off_A = off_Bm + FCC;                 //   A
+    static constexpr int off_T = off_A + FCC;                  //   T
+    static constexpr int off_Tft = off_T + FCC;                //   T^T
+    static constexpr int off_P = off_Tft + FCC;                //   P
+    static constexpr int off_Tt = off_P + FCC;                 // [CK][LCK] E: T~, T~^T, P^T
+    static constexpr int off_Ttt = off_Tt + ECC;
+    static constexpr int off_Pt = off_Ttt + ECC;
+    static constexpr int off_vec = off_Pt + ECC;               // g, gamma, D, beta, dg [CK]; parts
     static constexpr int NVEC = 5 * CK + 4 * (2 * CK) + 8;
-    static constexpr int bytes = off_vec + NVEC * 4;
+    // one block of value channels (reused by the last phase)
+    static constexpr int off_blk = (off_vec + NVEC * 4 + 15) / 16 * 16;
+    static constexpr int off_S0 = off_blk;                     // [kBV][LDK] E and [DK][LBV]
+    static constexpr int off_S0t = off_S0 + kBV * S::LDK * ES;
+    static constexpr int off_dS = off_S0t + DK * S::LBV * ES;
+    static constexpr int off_dSt = off_dS + kBV * S::LDK * ES;
+    static constexpr int off_dO = off_dSt + DK * S::LBV * ES;  // [CK][LBV] E
+    static constexpr int off_gdO = off_dO + ECB;
+    static constexpr int off_R = off_gdO + ECB;
+    static constexpr int off_U = off_R + ECB;
+    static constexpr int off_DU = off_U + ECB;
+    static constexpr int off_dU = off_DU + ECB;
+    static constexpr int off_dX = off_dU + ECB;
+    static constexpr int off_dOt = off_dX + ECB;               // [kBV][LCK] E
+    static constexpr int off_Rt = off_dOt + EBC;
+    static constexpr int off_dUt = off_Rt + EBC;
+    static constexpr int off_V = off_dUt + EBC;                // [CK][LBF] f32
+    static constexpr int off_X = off_V + FCB;
+    static constexpr int off_KdS = off_X + FCB;
+    static constexpr int blk_end = off_KdS + FCB;
+    // the last phase, over the block region
+    static constexpr int off_dTt = off_blk;                    // [CK][LF] f32
+    static constexpr int off_dTb = off_dTt + FCC;
+    static constexpr int off_Em = off_dTb + FCC;
+    static constexpr int off_Y1t = off_Em + FCC;
+    static constexpr int off_dA = off_Y1t + FCC;
+    static constexpr int off_dPW = off_dA + FCC;               // [CK][LCK] E
+    static constexpr int off_dPWt = off_dPW + ECC;
+    static constexpr int off_dG = off_dPWt + ECC;
+    static constexpr int off_dGt = off_dG + ECC;
+    static constexpr int last_end = off_dGt + ECC;
+    static constexpr int bytes = blk_end > last_end ? blk_end : last_end;
 };
 
 template <typename E, int DK, int CK>
 __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
 {
     using LY = GradLds<E, DK, CK>;
-    constexpr int LF = LY::LF, NB = CK / 16, NJ = DK / 16;
+    constexpr int NB = CK / 16, NJ = DK / 16, VE = Vec<E>::n;
+    constexpr int LF = LY::LF, LDK = LY::LDK, LCK = LY::LCK, LBV = LY::LBV, LBF = LY::LBF;
     constexpr int NQT = NB * NJ;                 // C x DK tiles
     constexpr int NQW = (NQT + 3) / 4;           // per wave
     constexpr int NCB = NB * (kBV / 16);         // C x kBV tiles (<= 4)
     constexpr int NCC = NB * NB;                 // C x C tiles (<= 4)
     extern __shared__ __align__(16) unsigned char smem[];
-    E* Ks = reinterpret_cast<E*>(smem + LY::off_K);
-    E* Qs = reinterpret_cast<E*>(smem + LY::off_Q);
-    E* S0s = reinterpret_cast<E*>(smem + LY::off_S0);
-    E* dSs = reinterpret_cast<E*>(smem + LY::off_dS);
-    E* dOs = reinterpret_cast<E*>(smem + LY::off_dO);
-    E* gdOs = reinterpret_cast<E*>(smem + LY::off_gdO);
-    E* Rs = reinterpret_cast<E*>(smem + LY::off_R);
-    E* Us = reinterpret_cast<E*>(smem + LY::off_U);
-    E* DUs = reinterpret_cast<E*>(smem + LY::off_DU);
-    E* dUs = reinterpret_cast<E*>(smem + LY::off_dU);
-    E* dXs = reinterpret_cast<E*>(smem + LY::off_dX);
-    float* Vs = reinterpret_cast<float*>(smem + LY::off_V);
-    float* Xs = reinterpret_cast<float*>(smem + LY::off_X);
-    float* KdSs = reinterpret_cast<float*>(smem + LY::off_KdS);
-    float* Bm = reinterpret_cast<float*>(smem + LY::off_Bm);
-    float* Af = reinterpret_cast<float*>(smem + LY::off_A);
-    float* Tf = reinterpret_cast<float*>(smem + LY::off_T);
-    float* Tt = reinterpret_cast<float*>(smem + LY::off_Tt);
-    float* Pf = reinterpret_cast<float*>(smem + LY::off_P);
-    float* dPW = reinterpret_cast<float*>(smem + LY::off_dPW);
-    float* Em = reinterpret_cast<float*>(smem + LY::off_Em);
-    float* dTb = reinterpret_cast<float*>(smem + LY::off_dTb);
-    float* dTt = reinterpret_cast<float*>(smem + LY::off_dTt);
-    float* Y1 = reinterpret_cast<float*>(smem + LY::off_Y1);
-    float* dAf = reinterpret_cast<float*>(smem + LY::off_dA);
-    float* dGf = reinterpret_cast<float*>(smem + LY::off_dG);
+#define GL_E(name, off) E* name = reinterpret_cast<E*>(smem + LY::off)
+#define GL_F(name, off) float* name = reinterpret_cast<float*>(smem + LY::off)
+    GL_E(Ks, off_K); GL_E(Kt, off_Kt); GL_E(Qs, off_Q); GL_E(Qt, off_Qt);
+    GL_F(Bm, off_Bm); GL_F(Af, off_A); GL_F(Tf, off_T); GL_F(Tft, off_Tft); GL_F(Pf, off_P);
+    GL_E(Tt, off_Tt); GL_E(Ttt, off_Ttt); GL_E(Pt, off_Pt);
+    GL_E(S0s, off_S0); GL_E(S0t, off_S0t); GL_E(dSs, off_dS); GL_E(dSt, off_dSt);
+    GL_E(dOs, off_dO); GL_E(gdOs, off_gdO); GL_E(Rs, off_R); GL_E(Us, off_U); GL_E(DUs, off_DU);
+    GL_E(dUs, off_dU); GL_E(dXs, off_dX); GL_E(dOt, off_dOt); GL_E(Rt, off_Rt); GL_E(dUt, off_dUt);
+    GL_F(Vs, off_V); GL_F(Xs, off_X); GL_F(KdSs, off_KdS);
+    GL_F(dTt, off_dTt); GL_F(dTb, off_dTb); GL_F(Em, off_Em); GL_F(Y1t, off_Y1t); GL_F(dAf, off_dA);
+    GL_E(dPW, off_dPW); GL_E(dPWt, off_dPWt); GL_E(dGf, off_dG); GL_E(dGt, off_dGt);
+#undef GL_E
+#undef GL_F
     float* gs = reinterpret_cast<float*>(smem + LY::off_vec);
     float* gam = gs + CK;
     float* Dd = gam + CK;
@@ -339,14 +442,14 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
     const int bh = cid / p.NC, n = cid % p.NC;
     const int t0 = n * CK, valid = min(CK, p.L - t0);
     const size_t tok = (size_t)bh * p.L + t0;
-    const E* kg = reinterpret_cast<const E*>(p.k) + tok * DK;
-    const E* qg = reinterpret_cast<const E*>(p.q) + tok * DK;
 
     // ---- the chunk's keys, queries and gates
-    for (int x = tid; x < CK * DK; x += 256) {
-        const int r = x / DK;
-        Ks[x] = r < valid ? kg[x] : from_f32<E>(0.f);
-        Qs[x] = r < valid ? qg[x] : from_f32<E>(0.f);
+    {
+        RowStage<E, CK, DK, 256> ks, qs;
+        ks.load(reinterpret_cast<const E*>(p.k) + tok * DK, DK, valid, tid);
+        qs.load(reinterpret_cast<const E*>(p.q) + tok * DK, DK, valid, tid);
+        ks.store(Ks, LDK, Kt, LCK, tid);
+        qs.store(Qs, LDK, Qt, LCK, tid);
     }
     for (int x = tid; x < 8 * CK; x += 256) hgp[x] = 0.f;   // hgp and frp
     if (w == 0) {
@@ -371,8 +474,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
         const int rb = w / NB, ib = w % NB;
         f32x4 kk = zero4(), qk = zero4();
         if (ib <= rb) {
-            tmma<E>(kk, Ks, DK, 1, 16 * rb, Ks, DK, 1, 16 * ib, DK);
-            tmma<E>(qk, Qs, DK, 1, 16 * rb, Ks, DK, 1, 16 * ib, DK);
+            tmma<E>(kk, Ks, LDK, 16 * rb, Ks, LDK, 16 * ib, DK);
+            tmma<E>(qk, Qs, LDK, 16 * rb, Ks, LDK, 16 * ib, DK);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -381,17 +484,20 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
             Bm[r * LF + s] = r > s ? kk[e] * G : 0.f;
             Af[r * LF + s] = r > s ? bs[r] * kk[e] * G : 0.f;
             Pf[r * LF + s] = qk[e] * G;
+            Pt[s * LCK + r] = from_f32<E>(qk[e] * G);
         }
     }
     __syncthreads();
     if (w == 0) unit_lower_inverse<CK, LF>(Af, Tf);
     __syncthreads();
-    // the inverse leaves the block above the diagonal unwritten
+    // T (the inverse leaves the block above the diagonal unwritten), T^T, T~, T~^T
     for (int x = tid; x < CK * CK; x += 256) {
-        const int r = x / CK, s = x % CK;
+        const int r = x % CK, s = x / CK;
         const float t = s <= r ? Tf[r * LF + s] : 0.f;
         Tf[r * LF + s] = t;
-        Tt[r * LF + s] = t * bs[s];
+        Tft[s * LF + r] = t;
+        Tt[r * LCK + s] = from_f32<E>(t * bs[s]);
+        Ttt[s * LCK + r] = from_f32<E>(t * bs[s]);
     }
 
     f32x4 dQa[NQW], dKa[NQW];
@@ -400,43 +506,78 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
     f32x4 dPa = zero4(), dTa = zero4();   // C x C tile w (w < NCC)
     float hS = 0.f;                       // this thread's part of <dS_end, S0>
 
-    const float* S0g = p.Sck + (size_t)cid * p.DV * DK;
-    const float* dSg = p.dSck + (size_t)cid * p.DV * DK;
+    const E* S0g = static_cast<const E*>(p.Sck) + (size_t)cid * p.DV * DK;
+    const E* dSg = static_cast<const E*>(p.dSck) + (size_t)cid * p.DV * DK;
+    const E* vg = reinterpret_cast<const E*>(p.v) + tok * p.DV;
+    const E* dog = reinterpret_cast<const E*>(p.dO) + tok * p.DV;
+    // one block of value channels: S0 and dS_end rows, V and dO columns.
+    // Thread x takes row x % kBV (token x % CK), so the transposed stores of
+    // a wave are consecutive; the next block's reads are issued before the
+    // current block is worked on.
+    constexpr int NSV = kBV * DK / VE / 256;   // 16-byte vectors per thread and state
+    constexpr int PERV = kBV / VE;
+    u32x4 sa[NSV], sb[NSV], va, da;
+    auto fetch = [&](int v0) {
+#pragma unroll
+        for (int u = 0; u < NSV; ++u) {
+            const int xs = tid + 256 * u, i = xs % kBV, j = VE * (xs / kBV);
+            sa[u] = ld16(S0g + (size_t)(v0 + i) * DK + j);
+            sb[u] = ld16(dSg + (size_t)(v0 + i) * DK + j);
+        }
+        const int r = tid % CK, c = (tid / CK) * VE;
+        const bool ok = tid < CK * PERV && r < valid;
+        va = ok ? ld16(vg + (size_t)r * p.DV + v0 + c) : u32x4{0u, 0u, 0u, 0u};
+        da = ok ? ld16(dog + (size_t)r * p.DV + v0 + c) : u32x4{0u, 0u, 0u, 0u};
+    };
+    fetch(0);
     for (int v0 = 0; v0 < p.DV; v0 += kBV) {
         __syncthreads();   // the previous block's operands are consumed
-        // ---- one block of value channels: S0, dS_end rows, V and dO columns
-        for (int x = tid; x < kBV * DK; x += 256) {
-            const float a = S0g[(size_t)v0 * DK + x], b = dSg[(size_t)v0 * DK + x];
-            S0s[x] = from_f32<E>(a);
-            dSs[x] = from_f32<E>(b);
-            hS += a * b;
+#pragma unroll
+        for (int u = 0; u < NSV; ++u) {
+            const int xs = tid + 256 * u, i = xs % kBV, j = VE * (xs / kBV);
+            E a[VE], b[VE];
+            __builtin_memcpy(a, &sa[u], 16);
+            __builtin_memcpy(b, &sb[u], 16);
+            st16(S0s + i * LDK + j, sa[u]);
+            st16(dSs + i * LDK + j, sb[u]);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                S0t[(j + e) * LBV + i] = a[e];
+                dSt[(j + e) * LBV + i] = b[e];
+                hS += to_f32(a[e]) * to_f32(b[e]);
+            }
         }
-        const E* vg = reinterpret_cast<const E*>(p.v) + tok * p.DV + v0;
-        const E* dog = reinterpret_cast<const E*>(p.dO) + tok * p.DV + v0;
-        for (int x = tid; x < CK * kBV; x += 256) {
-            const int r = x / kBV, i = x % kBV;
-            const bool ok = r < valid;
-            const float vv = ok ? to_f32(vg[(size_t)r * p.DV + i]) : 0.f;
-            const float d = ok ? to_f32(dog[(size_t)r * p.DV + i]) : 0.f;
-            Vs[x] = vv;
-            dOs[x] = from_f32<E>(d);
-            gdOs[x] = from_f32<E>(gam[r] * d);
+        if (tid < CK * PERV) {
+            const int r = tid % CK, c = (tid / CK) * VE;
+            float a[VE], d[VE];
+            Pack<E>::unpack(va, a);
+            Pack<E>::unpack(da, d);
+#pragma unroll
+            for (int j = 0; j < VE; ++j) {
+                Vs[r * LBF + c + j] = a[j];
+                dOs[r * LBV + c + j] = from_f32<E>(d[j]);
+                dOt[(c + j) * LCK + r] = from_f32<E>(d[j]);
+                gdOs[r * LBV + c + j] = from_f32<E>(gam[r] * d[j]);
+            }
         }
+        if (v0 + kBV < p.DV) fetch(v0 + kBV);
         __syncthreads();
         // ---- X = K S0^T, R = V - gamma X; K dS^T; the gamma . dO . Q S0^T term
         if (w < NCB) {
             const int rb = w / 2, cb = w % 2;
             f32x4 x = zero4(), qs = zero4(), kds = zero4();
-            tmma<E>(x, Ks, DK, 1, 16 * rb, S0s, DK, 1, 16 * cb, DK);
-            tmma<E>(qs, Qs, DK, 1, 16 * rb, S0s, DK, 1, 16 * cb, DK);
-            tmma<E>(kds, Ks, DK, 1, 16 * rb, dSs, DK, 1, 16 * cb, DK);
+            tmma<E>(x, Ks, LDK, 16 * rb, S0s, LDK, 16 * cb, DK);
+            tmma<E>(qs, Qs, LDK, 16 * rb, S0s, LDK, 16 * cb, DK);
+            tmma<E>(kds, Ks, LDK, 16 * rb, dSs, LDK, 16 * cb, DK);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
-                Xs[r * kBV + i] = x[e];
-                KdSs[r * kBV + i] = kds[e];
-                Rs[r * kBV + i] = from_f32<E>(Vs[r * kBV + i] - gam[r] * x[e]);
-                const float h = row16_sum(to_f32(gdOs[r * kBV + i]) * qs[e]);
+                const float rr = Vs[r * LBF + i] - gam[r] * x[e];
+                Xs[r * LBF + i] = x[e];
+                KdSs[r * LBF + i] = kds[e];
+                Rs[r * LBV + i] = from_f32<E>(rr);
+                Rt[i * LCK + r] = from_f32<E>(rr);
+                const float h = row16_sum(to_f32(gdOs[r * LBV + i]) * qs[e]);
                 if (c16 == 0) hgp[w * CK + r] += h;
             }
         }
@@ -445,15 +586,17 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
         if (w < NCB) {
             const int rb = w / 2, cb = w % 2;
             f32x4 u = zero4(), du = zero4();
-            tmma<E>(u, Tt, LF, 1, 16 * rb, Rs + 16 * cb, 1, kBV, 0, CK);
-            tmma<E>(du, Pf, 1, LF, 16 * rb, dOs + 16 * cb, 1, kBV, 0, CK);
+            tmma<E>(u, Tt, LCK, 16 * rb, Rt + 16 * cb * LCK, LCK, 0, CK);
+            tmma<E>(du, Pt, LCK, 16 * rb, dOt + 16 * cb * LCK, LCK, 0, CK);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
-                const float kds = KdSs[r * kBV + i];
-                Us[r * kBV + i] = from_f32<E>(u[e]);
-                DUs[r * kBV + i] = from_f32<E>(Dd[r] * u[e]);
-                dUs[r * kBV + i] = from_f32<E>(du[e] + Dd[r] * kds);
+                const float kds = KdSs[r * LBF + i];
+                const float dd = du[e] + Dd[r] * kds;
+                Us[r * LBV + i] = from_f32<E>(u[e]);
+                DUs[r * LBV + i] = from_f32<E>(Dd[r] * u[e]);
+                dUs[r * LBV + i] = from_f32<E>(dd);
+                dUt[i * LCK + r] = from_f32<E>(dd);
                 const float f = row16_sum(Dd[r] * u[e] * kds);
                 if (c16 == 0) frp[w * CK + r] += f;
             }
@@ -463,14 +606,14 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
         if (w < NCB) {
             const int rb = w / 2, cb = w % 2;
             f32x4 dr = zero4();
-            tmma<E>(dr, Tt, 1, LF, 16 * rb, dUs + 16 * cb, 1, kBV, 0, CK);
+            tmma<E>(dr, Ttt, LCK, 16 * rb, dUt + 16 * cb * LCK, LCK, 0, CK);
             E* dvg = reinterpret_cast<E*>(p.dv) + tok * p.DV + v0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
                 if (r < valid) dvg[(size_t)r * p.DV + i] = from_f32<E>(dr[e]);
-                dXs[r * kBV + i] = from_f32<E>(-gam[r] * dr[e]);
-                const float h = row16_sum(-gam[r] * dr[e] * Xs[r * kBV + i]);
+                dXs[r * LBV + i] = from_f32<E>(-gam[r] * dr[e]);
+                const float h = row16_sum(-gam[r] * dr[e] * Xs[r * LBF + i]);
                 if (c16 == 0) hgp[w * CK + r] += h;
             }
         }
@@ -481,17 +624,18 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
             const int t = w + 4 * u;
             if (t < NQT) {
                 const int rb = t / NJ, jb = t % NJ;
-                tmma<E>(dQa[u], gdOs, kBV, 1, 16 * rb, S0s, 1, DK, 16 * jb, kBV);
-                tmma<E>(dKa[u], DUs, kBV, 1, 16 * rb, dSs, 1, DK, 16 * jb, kBV);
-                tmma<E>(dKa[u], dXs, kBV, 1, 16 * rb, S0s, 1, DK, 16 * jb, kBV);
+                tmma<E>(dQa[u], gdOs, LBV, 16 * rb, S0t, LBV, 16 * jb, kBV);
+                tmma<E>(dKa[u], DUs, LBV, 16 * rb, dSt, LBV, 16 * jb, kBV);
+                tmma<E>(dKa[u], dXs, LBV, 16 * rb, S0t, LBV, 16 * jb, kBV);
             }
         }
         if (w < NCC) {
             const int rb = w / NB, sb = w % NB;
-            tmma<E>(dPa, dOs, kBV, 1, 16 * rb, Us, kBV, 1, 16 * sb, kBV);
-            tmma<E>(dTa, dUs, kBV, 1, 16 * rb, Rs, kBV, 1, 16 * sb, kBV);
+            tmma<E>(dPa, dOs, LBV, 16 * rb, Us, LBV, 16 * sb, kBV);
+            tmma<E>(dTa, dUs, LBV, 16 * rb, Rs, LBV, 16 * sb, kBV);
         }
     }
+    __syncthreads();   // the block region is reused below
 
     // ---- C x C terms
     if (w < NCC) {
@@ -500,7 +644,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * rb + 4 * g4 + e, s = 16 * sb + c16;
             const float W = r >= s ? __expf(gs[r] - gs[s]) : 0.f;
-            dPW[r * LF + s] = dPa[e] * W;
+            dPW[r * LCK + s] = from_f32<E>(dPa[e] * W);
+            dPWt[s * LCK + r] = from_f32<E>(dPa[e] * W);
             Em[r * LF + s] = dPa[e] * Pf[r * LF + s];
             dTt[r * LF + s] = dTa[e];
             dTb[r * LF + s] = dTa[e] * bs[s];
@@ -520,16 +665,16 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
         const int t = w + 4 * u;
         if (t < NQT) {
             const int rb = t / NJ, jb = t % NJ;
-            tmma<E>(dQa[u], dPW, LF, 1, 16 * rb, Ks, 1, DK, 16 * jb, CK);
-            tmma<E>(dKa[u], dPW, 1, LF, 16 * rb, Qs, 1, DK, 16 * jb, CK);
+            tmma<E>(dQa[u], dPW, LCK, 16 * rb, Kt, LCK, 16 * jb, CK);
+            tmma<E>(dKa[u], dPWt, LCK, 16 * rb, Qt, LCK, 16 * jb, CK);
         }
     }
     if (w < NCC) {
         const int rb = w / NB, sb = w % NB;
         f32x4 y = zero4();
-        tmma<float>(y, dTb, LF, 1, 16 * rb, Tf, LF, 1, 16 * sb, CK);
+        tmma<float>(y, dTb, LF, 16 * rb, Tf, LF, 16 * sb, CK);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Y1[(16 * rb + 4 * g4 + e) * LF + 16 * sb + c16] = y[e];
+        for (int e = 0; e < 4; ++e) Y1t[(16 * sb + c16) * LF + 16 * rb + 4 * g4 + e] = y[e];
     }
     // the dg terms of dP . P
     if (tid < CK) {
@@ -542,13 +687,15 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
     if (w < NCC) {
         const int rb = w / NB, sb = w % NB;
         f32x4 y = zero4();
-        tmma<float>(y, Tf, 1, LF, 16 * rb, Y1, 1, LF, 16 * sb, CK);
+        tmma<float>(y, Tft, LF, 16 * rb, Y1t, LF, 16 * sb, CK);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * rb + 4 * g4 + e, s = 16 * sb + c16;
             const float da = r > s ? -y[e] : 0.f;
+            const float dgv = r > s ? da * bs[r] * __expf(gs[r] - gs[s]) : 0.f;
             dAf[r * LF + s] = da;
-            dGf[r * LF + s] = r > s ? da * bs[r] * __expf(gs[r] - gs[s]) : 0.f;
+            dGf[r * LCK + s] = from_f32<E>(dgv);
+            dGt[s * LCK + r] = from_f32<E>(dgv);
             Em[r * LF + s] = da * Af[r * LF + s];
         }
     }
@@ -559,15 +706,15 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
         const int t = w + 4 * u;
         if (t < NQT) {
             const int rb = t / NJ, jb = t % NJ;
-            tmma<E>(dKa[u], dGf, LF, 1, 16 * rb, Ks, 1, DK, 16 * jb, CK);
-            tmma<E>(dKa[u], dGf, 1, LF, 16 * rb, Ks, 1, DK, 16 * jb, CK);
+            tmma<E>(dKa[u], dGf, LCK, 16 * rb, Kt, LCK, 16 * jb, CK);
+            tmma<E>(dKa[u], dGt, LCK, 16 * rb, Kt, LCK, 16 * jb, CK);
         }
     }
     // dbeta and dg per token, then d log alpha = suffix sums of dg
     if (w == 0) {
         float db = 0.f, dgl = 0.f, fr = 0.f;
         if (l < CK) {
-            for (int u = 0; u < CK; ++u) db += Tf[u * LF + l] * dTt[u * LF + l];
+            for (int u = 0; u < CK; ++u) db += Tft[l * LF + u] * dTt[u * LF + l];
             for (int s = 0; s < CK; ++s) db += dAf[l * LF + s] * Bm[l * LF + s];
             float fa = 0.f, hg = 0.f;
             for (int s = 0; s < CK; ++s) fa += Em[l * LF + s] - Em[s * LF + l];
@@ -644,8 +791,8 @@ static BwdWs bwd_ws(int B, int H, int L, int dk, int dv, int C, int dtype)
     const int es = dtype == kBF16 ? 2 : 4;
     BwdWs w{};
     size_t o = al(BH * NC * (size_t)ws_layout(es, dk, CK, kAlphaScalar).bytes);
-    w.off_Sck = o; o = al(o + BH * NC * dv * dk * 4);
-    w.off_dSck = o; o = al(o + BH * NC * dv * dk * 4);
+    w.off_Sck = o; o = al(o + BH * NC * dv * dk * es);
+    w.off_dSck = o; o = al(o + BH * NC * dv * dk * es);
     w.off_o = o; o = al(o + BH * (size_t)L * dv * es);
     w.bytes = o;
     return w;
@@ -681,14 +828,14 @@ hipError_t launch_bwd_chunked(const BwdArgs& b)
     unsigned char* ws = static_cast<unsigned char*>(b.workspace);
     // forward again: the prepass records and every chunk's entry state
     ChunkArgs a{b.B, b.H, b.L, b.dk, b.dv, b.C, b.dtype, b.mode, b.q, b.k, b.v, b.beta, b.log_alpha, b.S0,
-                ws + w.off_o, nullptr, ws, b.stream, 0u, nullptr, 0, Varlen{}, reinterpret_cast<float*>(ws + w.off_Sck)};
+                ws + w.off_o, nullptr, ws, b.stream, 0u, nullptr, 0, Varlen{}, ws + w.off_Sck};
     hipError_t err = launch_wy(a, CK);
     if (err != hipSuccess) return err;
     SegPlan one{1, NC, 0, 0, 0, 0, 0};
     err = launch_scan(a, CK, one);
     if (err != hipSuccess) return err;
     BwdParams bp{b.q, b.k, b.v, b.dO, b.beta, b.log_alpha, b.dS_final, ws,
-                 reinterpret_cast<const float*>(ws + w.off_Sck), reinterpret_cast<float*>(ws + w.off_dSck),
+                 ws + w.off_Sck, ws + w.off_dSck,
                  b.dq, b.dk_out, b.dv_out, b.dbeta, b.dlog_alpha, b.dS0, b.L, NC, b.dv, (int)(BH * NC)};
     if (b.dtype == kBF16) {
         if (b.dk == 128) return CK == 16 ? launch_bwd_t<bf16, 128, 16>(bp, (int)BH, b.stream)

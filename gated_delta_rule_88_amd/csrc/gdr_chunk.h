@@ -118,9 +118,9 @@ struct ScanParams {
     // n * H + h is sequence n of head h, total = NS * H * NVB workgroups.
     int H;
     Varlen vl;
-    // [B*H][NC][d_v][d_k] fp32: the state entering every chunk (kept for the
-    // backward), or null
-    float* Sck;
+    // [B*H][NC][d_v][d_k] in the operand type: the state entering every
+    // chunk (kept for the backward), or null
+    void* Sck;
 };
 
 // Segment-parallel scan.  A head's chunk scan is one sequential chain; when

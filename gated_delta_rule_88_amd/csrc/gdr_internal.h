@@ -53,7 +53,7 @@ struct ChunkArgs {
     int NS;
     Varlen vl;
     // backward's forward recompute: every chunk's entry state, or null
-    float* Sck;
+    void* Sck;
 };
 
 struct BwdArgs {

@@ -515,10 +515,10 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
                     if (s < NC) {
                         if (p.Sck) {
                             // the state entering chunk s, for the backward
-                            float* ck = p.Sck + (((size_t)bh * p.NC + c0 + s) * p.DV + vw + c16) * DK;
+                            E* ck = static_cast<E*>(p.Sck) + (((size_t)bh * p.NC + c0 + s) * p.DV + vw + c16) * DK;
 #pragma unroll
                             for (int a = 0; a < NKT; ++a)
-                                *reinterpret_cast<f32x4*>(ck + 32 * (a >> 1) + 8 * g4 + 4 * (a & 1)) = sT[a];
+                                st4(ck + 32 * (a >> 1) + 8 * g4 + 4 * (a & 1), sT[a][0], sT[a][1], sT[a][2], sT[a][3]);
                         }
                         own(jc, s);
                     }

@@ -251,11 +251,12 @@ def test_varlen_empty_is_a_noop(lib):
 
 def test_backward_workspace_size_query():
     ws = gdr.gdr_bwd_chunked_workspace_size
-    # records, the state entering and the gradient leaving every chunk (fp32
-    # d_v x d_k each), the recomputed outputs; each region 256-aligned
+    # records, the state entering and the gradient leaving every chunk (d_v x
+    # d_k each, in the operand type), the recomputed outputs; each region
+    # 256-aligned
     nc = 2048 // 32
     rec = 64 * nc * (2048 + 2048 + 512)
-    st = 64 * nc * 128 * 128 * 4
+    st = 64 * nc * 128 * 128 * 2
     assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 1) == rec + 2 * st + 64 * 2048 * 128 * 2
     assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 2) == SIZE_MAX      # channel gates
     assert ws(1, 2, 0, 64, 64, 64, gdr.GDR_F32, 1) == 0
