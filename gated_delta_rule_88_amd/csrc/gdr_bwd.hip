@@ -369,7 +369,7 @@ struct GradLds : Strides<E, DK, CK> {
     static constexpr int off_Ttt = off_Tt + ECC;
     static constexpr int off_Pt = off_Ttt + ECC;
     static constexpr int off_vec = off_Pt + ECC;               // g, gamma, D, beta, dg [CK]; parts
-    static constexpr int NVEC = 5 * CK + 4 * (2 * CK) + 8;
+    static constexpr int NVEC = 5 * CK + 12 * CK + 8;
     // one block of value channels (reused by the last phase)
     static constexpr int off_blk = (off_vec + NVEC * 4 + 15) / 16 * 16;
     static constexpr int off_S0 = off_blk;                     // [kBV][LDK] E and [DK][LBV]
@@ -405,13 +405,14 @@ struct GradLds : Strides<E, DK, CK> {
 };
 
 template <typename E, int DK, int CK>
-__global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
+__global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
 {
     using LY = GradLds<E, DK, CK>;
     constexpr int NB = CK / 16, NJ = DK / 16, VE = Vec<E>::n;
     constexpr int LF = LY::LF, LDK = LY::LDK, LCK = LY::LCK, LBV = LY::LBV, LBF = LY::LBF;
+    constexpr int NT = 512, NW = NT / kWave;     // 8 waves
     constexpr int NQT = NB * NJ;                 // C x DK tiles
-    constexpr int NQW = (NQT + 3) / 4;           // per wave
+    constexpr int NQW = (NQT + NW - 1) / NW;     // per wave
     constexpr int NCB = NB * (kBV / 16);         // C x kBV tiles (<= 4)
     constexpr int NCC = NB * NB;                 // C x C tiles (<= 4)
     extern __shared__ __align__(16) unsigned char smem[];
@@ -433,8 +434,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
     float* Dd = gam + CK;
     float* bs = Dd + CK;
     float* dg = bs + CK;
-    float* hgp = dg + CK;        // [4][CK] per-wave partial sums of the gamma terms
-    float* frp = hgp + 4 * CK;   // [4][CK] per-wave partial sums of the D terms
+    float* hgp = dg + CK;        // [8][CK] per-wave partial sums of the gamma terms
+    float* frp = hgp + 8 * CK;   // [4][CK] per-wave partial sums of the D terms
     float* red = frp + 4 * CK;   // [8]: per-wave <dS_end, S0>
 
     const int cid = blockIdx.x;
@@ -445,13 +446,13 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
 
     // ---- the chunk's keys, queries and gates
     {
-        RowStage<E, CK, DK, 256> ks, qs;
+        RowStage<E, CK, DK, NT> ks, qs;
         ks.load(reinterpret_cast<const E*>(p.k) + tok * DK, DK, valid, tid);
         qs.load(reinterpret_cast<const E*>(p.q) + tok * DK, DK, valid, tid);
         ks.store(Ks, LDK, Kt, LCK, tid);
         qs.store(Qs, LDK, Qt, LCK, tid);
     }
-    for (int x = tid; x < 8 * CK; x += 256) hgp[x] = 0.f;   // hgp and frp
+    for (int x = tid; x < 12 * CK; x += NT) hgp[x] = 0.f;   // hgp and frp
     if (w == 0) {
         float la = 0.f, bt = 0.f;
         if (l < valid) {
@@ -491,7 +492,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
     if (w == 0) unit_lower_inverse<CK, LF>(Af, Tf);
     __syncthreads();
     // T (the inverse leaves the block above the diagonal unwritten), T^T, T~, T~^T
-    for (int x = tid; x < CK * CK; x += 256) {
+    for (int x = tid; x < CK * CK; x += NT) {
         const int r = x % CK, s = x / CK;
         const float t = s <= r ? Tf[r * LF + s] : 0.f;
         Tf[r * LF + s] = t;
@@ -514,15 +515,17 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
     // Thread x takes row x % kBV (token x % CK), so the transposed stores of
     // a wave are consecutive; the next block's reads are issued before the
     // current block is worked on.
-    constexpr int NSV = kBV * DK / VE / 256;   // 16-byte vectors per thread and state
+    constexpr int NSV = (kBV * DK / VE + NT - 1) / NT;   // 16-byte vectors per thread and state
     constexpr int PERV = kBV / VE;
     u32x4 sa[NSV], sb[NSV], va, da;
     auto fetch = [&](int v0) {
 #pragma unroll
         for (int u = 0; u < NSV; ++u) {
-            const int xs = tid + 256 * u, i = xs % kBV, j = VE * (xs / kBV);
-            sa[u] = ld16(S0g + (size_t)(v0 + i) * DK + j);
-            sb[u] = ld16(dSg + (size_t)(v0 + i) * DK + j);
+            const int xs = tid + NT * u, i = xs % kBV, j = VE * (xs / kBV);
+            if (xs < kBV * DK / VE) {
+                sa[u] = ld16(S0g + (size_t)(v0 + i) * DK + j);
+                sb[u] = ld16(dSg + (size_t)(v0 + i) * DK + j);
+            }
         }
         const int r = tid % CK, c = (tid / CK) * VE;
         const bool ok = tid < CK * PERV && r < valid;
@@ -534,7 +537,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
         __syncthreads();   // the previous block's operands are consumed
 #pragma unroll
         for (int u = 0; u < NSV; ++u) {
-            const int xs = tid + 256 * u, i = xs % kBV, j = VE * (xs / kBV);
+            const int xs = tid + NT * u, i = xs % kBV, j = VE * (xs / kBV);
+            if (xs >= kBV * DK / VE) continue;
             E a[VE], b[VE];
             __builtin_memcpy(a, &sa[u], 16);
             __builtin_memcpy(b, &sb[u], 16);
@@ -562,43 +566,50 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
         }
         if (v0 + kBV < p.DV) fetch(v0 + kBV);
         __syncthreads();
-        // ---- X = K S0^T, R = V - gamma X; K dS^T; the gamma . dO . Q S0^T term
+        // ---- X = K S0^T and R = V - gamma X (waves 0-3); K dS^T (waves 4-7)
         if (w < NCB) {
             const int rb = w / 2, cb = w % 2;
-            f32x4 x = zero4(), qs = zero4(), kds = zero4();
+            f32x4 x = zero4();
             tmma<E>(x, Ks, LDK, 16 * rb, S0s, LDK, 16 * cb, DK);
-            tmma<E>(qs, Qs, LDK, 16 * rb, S0s, LDK, 16 * cb, DK);
-            tmma<E>(kds, Ks, LDK, 16 * rb, dSs, LDK, 16 * cb, DK);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
                 const float rr = Vs[r * LBF + i] - gam[r] * x[e];
                 Xs[r * LBF + i] = x[e];
-                KdSs[r * LBF + i] = kds[e];
                 Rs[r * LBV + i] = from_f32<E>(rr);
                 Rt[i * LCK + r] = from_f32<E>(rr);
-                const float h = row16_sum(to_f32(gdOs[r * LBV + i]) * qs[e]);
-                if (c16 == 0) hgp[w * CK + r] += h;
             }
+        } else if (w >= 4 && w < 4 + NCB) {
+            const int rb = (w - 4) / 2, cb = (w - 4) % 2;
+            f32x4 kds = zero4();
+            tmma<E>(kds, Ks, LDK, 16 * rb, dSs, LDK, 16 * cb, DK);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) KdSs[(16 * rb + 4 * g4 + e) * LBF + 16 * cb + c16] = kds[e];
         }
         __syncthreads();
-        // ---- U = T~ R, dU = P^T dO + D . K dS^T
+        // ---- U = T~ R (waves 0-3), dU = P^T dO + D . K dS^T (waves 4-7)
         if (w < NCB) {
             const int rb = w / 2, cb = w % 2;
-            f32x4 u = zero4(), du = zero4();
+            f32x4 u = zero4();
             tmma<E>(u, Tt, LCK, 16 * rb, Rt + 16 * cb * LCK, LCK, 0, CK);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
+                Us[r * LBV + i] = from_f32<E>(u[e]);
+                DUs[r * LBV + i] = from_f32<E>(Dd[r] * u[e]);
+                const float f = row16_sum(Dd[r] * u[e] * KdSs[r * LBF + i]);
+                if (c16 == 0) frp[w * CK + r] += f;
+            }
+        } else if (w >= 4 && w < 4 + NCB) {
+            const int rb = (w - 4) / 2, cb = (w - 4) % 2;
+            f32x4 du = zero4();
             tmma<E>(du, Pt, LCK, 16 * rb, dOt + 16 * cb * LCK, LCK, 0, CK);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
-                const float kds = KdSs[r * LBF + i];
-                const float dd = du[e] + Dd[r] * kds;
-                Us[r * LBV + i] = from_f32<E>(u[e]);
-                DUs[r * LBV + i] = from_f32<E>(Dd[r] * u[e]);
+                const float dd = du[e] + Dd[r] * KdSs[r * LBF + i];
                 dUs[r * LBV + i] = from_f32<E>(dd);
                 dUt[i * LCK + r] = from_f32<E>(dd);
-                const float f = row16_sum(Dd[r] * u[e] * kds);
-                if (c16 == 0) frp[w * CK + r] += f;
             }
         }
         __syncthreads();
@@ -621,7 +632,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
         // ---- accumulate over the block's value channels
 #pragma unroll
         for (int u = 0; u < NQW; ++u) {
-            const int t = w + 4 * u;
+            const int t = w + NW * u;
             if (t < NQT) {
                 const int rb = t / NJ, jb = t % NJ;
                 tmma<E>(dQa[u], gdOs, LBV, 16 * rb, S0t, LBV, 16 * jb, kBV);
@@ -651,6 +662,21 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
             dTb[r * LF + s] = dTa[e] * bs[s];
         }
     }
+    // the gamma . dO . (Q S0^T) term of dg: sum_j Q_rj (gamma dO S0)_rj, from
+    // the dQ accumulators before the score terms join them
+#pragma unroll
+    for (int u = 0; u < NQW; ++u) {
+        const int t = w + NW * u;
+        if (t < NQT) {
+            const int rb = t / NJ, jb = t % NJ;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * g4 + e;
+                const float h = row16_sum(to_f32(Qs[r * LDK + 16 * jb + c16]) * dQa[u][e]);
+                if (c16 == 0) hgp[w * CK + r] += h;   // this wave's own slot
+            }
+        }
+    }
     {
         // <dS_end, S0> over the whole state
         float x = hS;
@@ -662,7 +688,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
     // dQ += (dP . W) K, dK += (dP . W)^T Q; Y1 = dT~ diag(beta) T^T
 #pragma unroll
     for (int u = 0; u < NQW; ++u) {
-        const int t = w + 4 * u;
+        const int t = w + NW * u;
         if (t < NQT) {
             const int rb = t / NJ, jb = t % NJ;
             tmma<E>(dQa[u], dPW, LCK, 16 * rb, Kt, LCK, 16 * jb, CK);
@@ -703,7 +729,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
     // dK += dG K + dG^T K
 #pragma unroll
     for (int u = 0; u < NQW; ++u) {
-        const int t = w + 4 * u;
+        const int t = w + NW * u;
         if (t < NQT) {
             const int rb = t / NJ, jb = t % NJ;
             tmma<E>(dKa[u], dGf, LCK, 16 * rb, Kt, LCK, 16 * jb, CK);
@@ -718,17 +744,19 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
             for (int s = 0; s < CK; ++s) db += dAf[l * LF + s] * Bm[l * LF + s];
             float fa = 0.f, hg = 0.f;
             for (int s = 0; s < CK; ++s) fa += Em[l * LF + s] - Em[s * LF + l];
-            for (int x = 0; x < 4; ++x) {
-                fr += frp[x * CK + l];
-                hg += hgp[x * CK + l];
-            }
+            for (int x = 0; x < 4; ++x) fr += frp[x * CK + l];
+            for (int x = 0; x < 8; ++x) hg += hgp[x * CK + l];
             dgl = dg[l] + fa + hg - fr;
         }
         // g_C enters gamma_C S0 and every D_r = e^{g_C - g_r}
         float fsum = fr;
 #pragma unroll
         for (int m = kWave / 2; m >= 1; m >>= 1) fsum += __shfl_xor(fsum, m, kWave);
-        if (l == CK - 1) dgl += gam[CK - 1] * (red[0] + red[1] + red[2] + red[3]) + fsum;
+        if (l == CK - 1) {
+            float hs = 0.f;
+            for (int x = 0; x < NW; ++x) hs += red[x];
+            dgl += gam[CK - 1] * hs + fsum;
+        }
         const float incl = wave_incl_scan(dgl);
         const float total = __shfl(incl, CK - 1, kWave);
         if (l < valid) {
@@ -741,7 +769,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdParams p)
     E* dkg = reinterpret_cast<E*>(p.dk) + tok * DK;
 #pragma unroll
     for (int u = 0; u < NQW; ++u) {
-        const int t = w + 4 * u;
+        const int t = w + NW * u;
         if (t < NQT) {
             const int rb = t / NJ, jb = t % NJ;
 #pragma unroll
@@ -771,7 +799,7 @@ static hipError_t launch_bwd_t(const BwdParams& bp, int BH, hipStream_t stream)
     auto* grad = chunk_bwd_grad_kernel<E, DK, CK>;
     err = hipFuncSetAttribute((const void*)grad, hipFuncAttributeMaxDynamicSharedMemorySize, GL::bytes);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(grad, dim3(bp.total), dim3(256), GL::bytes, stream, bp);
+    hipLaunchKernelGGL(grad, dim3(bp.total), dim3(512), GL::bytes, stream, bp);
     return hipGetLastError();
 }
 
