@@ -364,7 +364,7 @@ def main():
         ht = w.B * w.H * w.L
         gate = 0 if w.mode == gi.ALPHA_NONE else 4
         # read q, k, v, dO, beta, log alpha; write dq, dk, dv, dbeta, dlog alpha
-        nbytes = ht * (es * (3 * w.dk + 3 * w.dv) + 8 + 2 * gate)
+        nbytes = ht * (es * (4 * w.dk + 3 * w.dv) + 8 + 2 * gate)
         print(json.dumps({
             "metric": "tokens/s chunked GDN backward (gradients; forward recomputed inside)",
             "value": w.tokens / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
