@@ -19,6 +19,7 @@ Functions carry the C names:
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -31,6 +32,8 @@ GDR_ERR_WORKSPACE_TOO_SMALL, GDR_ERR_HIP = 3, 4
 GDR_F32, GDR_BF16 = 0, 1
 GDR_ALPHA_NONE, GDR_ALPHA_SCALAR, GDR_ALPHA_CHANNEL = 0, 1, 2
 GDR_PRO_L2NORM_QK, GDR_PRO_GATES = 1, 2
+
+_SIZE_MAX = ctypes.c_size_t(-1).value
 
 EXPORTED = ("gdr_abi_version", "gdr_status_string", "gdr_fwd_chunked_workspace_size",
             "gdr_fwd_chunked", "gdr_fwd_chunked_ex", "gdr_fwd_varlen_workspace_size",
@@ -105,7 +108,8 @@ def _mode_of(log_alpha, q) -> int:
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: the c_void_p argtype converts it without a Python object per call
+    return None if t is None else t.data_ptr()
 
 
 def _check(t, name, dtype, device, shape):
@@ -113,13 +117,14 @@ def _check(t, name, dtype, device, shape):
         return
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
-    if t.device != device:
-        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    td = t.device
+    if td.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got {td}")
+    if td != device:
+        raise ValueError(f"{name} is on {td}, expected {device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -127,7 +132,12 @@ def _check(t, name, dtype, device, shape):
 
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return s.cuda_stream
+
+
+@functools.lru_cache(maxsize=256)
+def _chunked_ws(B, H, L, dk, dv, C, code, mode) -> int:
+    return int(load_library().gdr_fwd_chunked_workspace_size(B, H, L, dk, dv, C, code, mode))
 
 
 def gdr_fwd_chunked_workspace_size(B, H, L, d_k, d_v, C, dtype, alpha_mode) -> int:
@@ -135,15 +145,10 @@ def gdr_fwd_chunked_workspace_size(B, H, L, d_k, d_v, C, dtype, alpha_mode) -> i
                                                              alpha_mode))
 
 
-def gdr_fwd_chunked(q, k, v, beta, log_alpha=None, S0=None, chunk: int = 64, *,
-                    o=None, S_final=None, write_final: bool = True, workspace=None,
-                    stream=None, prologue: int = 0):
-    """Chunkwise forward.  q, k [B,H,L,dk]; v [B,H,L,dv] (bf16 or fp32);
-    beta [B,H,L] fp32; log_alpha None | [B,H,L] | [B,H,L,dk] fp32;
-    S0 None | [B,H,dv,dk] fp32.  Returns (o, S_final or None).
-    Pass S_final=S0 to update the state in place.  ``prologue`` (a set of
-    GDR_PRO_* bits) asks the library to L2-normalise q and k and/or to take
-    beta and log_alpha as raw gate pre-activations (gdr_fwd_chunked_ex)."""
+def _prepare_fwd_chunked(q, k, v, beta, log_alpha, S0, chunk, o, S_final, write_final, workspace,
+                         stream, prologue):
+    """Checks and allocations of a gdr_fwd_chunked call; returns the C
+    function, its arguments, its name and (o, S_final)."""
     lib = load_library()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, L, d_k]")
@@ -168,8 +173,8 @@ def gdr_fwd_chunked(q, k, v, beta, log_alpha=None, S0=None, chunk: int = 64, *,
     if S_final is None and write_final:
         S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     _check(S_final, "S_final", torch.float32, dev, (B, H, dv, dk))
-    need = gdr_fwd_chunked_workspace_size(B, H, L, dk, dv, chunk, code, mode)
-    if need == ctypes.c_size_t(-1).value:
+    need = _chunked_ws(B, H, L, dk, dv, chunk, code, mode)
+    if need == _SIZE_MAX:
         raise GdrError(GDR_ERR_UNSUPPORTED, "gdr_fwd_chunked_workspace_size")
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -178,12 +183,47 @@ def gdr_fwd_chunked(q, k, v, beta, log_alpha=None, S0=None, chunk: int = 64, *,
             _ptr(log_alpha), _ptr(S0), _ptr(o), _ptr(S_final), _ptr(workspace), ws_bytes,
             _stream(stream))
     if prologue:
-        st, name = lib.gdr_fwd_chunked_ex(*args, int(prologue)), "gdr_fwd_chunked_ex"
-    else:
-        st, name = lib.gdr_fwd_chunked(*args), "gdr_fwd_chunked"
+        return lib.gdr_fwd_chunked_ex, args + (int(prologue),), "gdr_fwd_chunked_ex", (o, S_final), workspace
+    return lib.gdr_fwd_chunked, args, "gdr_fwd_chunked", (o, S_final), workspace
+
+
+def gdr_fwd_chunked(q, k, v, beta, log_alpha=None, S0=None, chunk: int = 64, *,
+                    o=None, S_final=None, write_final: bool = True, workspace=None,
+                    stream=None, prologue: int = 0):
+    """Chunkwise forward.  q, k [B,H,L,dk]; v [B,H,L,dv] (bf16 or fp32);
+    beta [B,H,L] fp32; log_alpha None | [B,H,L] | [B,H,L,dk] fp32;
+    S0 None | [B,H,dv,dk] fp32.  Returns (o, S_final or None).
+    Pass S_final=S0 to update the state in place.  ``prologue`` (a set of
+    GDR_PRO_* bits) asks the library to L2-normalise q and k and/or to take
+    beta and log_alpha as raw gate pre-activations (gdr_fwd_chunked_ex)."""
+    fn, args, name, out, _ = _prepare_fwd_chunked(q, k, v, beta, log_alpha, S0, chunk, o, S_final,
+                                                  write_final, workspace, stream, prologue)
+    st = fn(*args)
     if st != GDR_OK:
         raise GdrError(st, name)
-    return o, S_final
+    return out
+
+
+class FwdChunkedCall:
+    """One gdr_fwd_chunked call, checked and allocated once, to be enqueued
+    any number of times on the same tensors (a training or serving loop with
+    fixed shapes): calling it repeats the C call with the stored pointers and
+    stream, without the per-call Python checks.  The tensors must stay alive
+    and in place; ``o`` and ``S_final`` hold the results after each call."""
+
+    def __init__(self, q, k, v, beta, log_alpha=None, S0=None, chunk: int = 64, *, o=None,
+                 S_final=None, write_final: bool = True, workspace=None, stream=None,
+                 prologue: int = 0):
+        self._fn, self._args, self._name, (self.o, self.S_final), self.workspace = \
+            _prepare_fwd_chunked(q, k, v, beta, log_alpha, S0, chunk, o, S_final, write_final,
+                                 workspace, stream, prologue)
+        self._keep = (q, k, v, beta, log_alpha, S0)   # the pointers stay valid
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != GDR_OK:
+            raise GdrError(st, self._name)
+        return self.o, self.S_final
 
 
 def gdr_bwd_chunked_workspace_size(B, H, L, d_k, d_v, C, dtype, alpha_mode) -> int:

@@ -301,3 +301,18 @@ def test_full_decode_sampled():
                         sel(mv(y["log_alpha"])), sel(y["S0"]))
     assert rel_err(pick(o, heads), ro) <= 2e-2
     assert rel_err(pick(S.cpu().numpy(), heads), rS) <= 2e-2
+
+
+def test_fwd_call_object_repeats_the_call():
+    """FwdChunkedCall enqueues the same C call on the same tensors: its results
+    equal the plain call's, also after the inputs change in place."""
+    x = to_dev(gi.chunked_inputs(2, 3, 150, 128, 128, torch.bfloat16, gi.ALPHA_SCALAR, seed=7100,
+                                 s0_std=0.1))
+    call = gdr.FwdChunkedCall(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"], x["S0"], 64)
+    for _ in range(2):
+        o, S = call()
+        ro, rS = gdr.gdr_fwd_chunked(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"], x["S0"], 64)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ro) and torch.equal(S, rS)
+        x["v"].mul_(0.5)
+        x["beta"].mul_(0.9)
