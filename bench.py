@@ -372,11 +372,12 @@ def main():
         ms = r["total_ms"] / args.steps
         es = 2 if w.dtype == torch.bfloat16 else 4
         ht = w.B * w.H * w.L
-        gate = 0 if w.mode == gi.ALPHA_NONE else 4
+        gate = {gi.ALPHA_NONE: 0, gi.ALPHA_SCALAR: 4, gi.ALPHA_CHANNEL: 4 * w.dk}[w.mode]
         # read q, k, v, dO, beta, log alpha; write dq, dk, dv, dbeta, dlog alpha
         nbytes = ht * (es * (4 * w.dk + 3 * w.dv) + 8 + 2 * gate)
         print(json.dumps({
-            "metric": "tokens/s chunked GDN backward (gradients; forward recomputed inside)",
+            "metric": "tokens/s chunked gated delta-rule backward (gradients; forward recomputed "
+                      "inside)",
             "value": w.tokens / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
@@ -386,8 +387,11 @@ def main():
             "roofline": {"bound": "hbm", "achieved": nbytes / (ms / 1e3) / 1e9,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
-                         "kernel": "chunk_wy_kernel + chunk_scan_kernel + chunk_bwd_chain_kernel "
-                                   "+ chunk_bwd_grad_kernel",
+                         "kernel": ("chunk_wy_channel_kernel + chunk_scan_kernel + "
+                                    "chunk_bwd_chain_kernel + chunk_bwd_grad_channel_kernel"
+                                    if w.mode == gi.ALPHA_CHANNEL else
+                                    "chunk_wy_kernel + chunk_scan_kernel + chunk_bwd_chain_kernel "
+                                    "+ chunk_bwd_grad_kernel"),
                          "algorithmic_bytes_per_call": nbytes},
         }))
         return

@@ -236,7 +236,7 @@ def gdr_bwd_chunked(q, k, v, beta, log_alpha, S0, dO, dS_final=None, chunk: int 
     """Gradients of gdr_fwd_chunked for output gradient dO [B,H,L,dv] (dtype
     of q) and final-state gradient dS_final (None | [B,H,dv,dk] fp32).
     Returns a dict of dq, dk, dv (dtype of q), dbeta, dlog_alpha (None for
-    alpha = 1) and dS0 (fp32, or None)."""
+    alpha = 1, else the shape of log_alpha) and dS0 (fp32, or None)."""
     lib = load_library()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, L, d_k]")
@@ -251,6 +251,8 @@ def gdr_bwd_chunked(q, k, v, beta, log_alpha, S0, dO, dS_final=None, chunk: int 
     _check(beta, "beta", torch.float32, dev, (B, H, L))
     if mode == GDR_ALPHA_SCALAR:
         _check(log_alpha, "log_alpha", torch.float32, dev, (B, H, L))
+    elif mode == GDR_ALPHA_CHANNEL:
+        _check(log_alpha, "log_alpha", torch.float32, dev, (B, H, L, dk))
     _check(S0, "S0", torch.float32, dev, (B, H, dv, dk))
     _check(dO, "dO", dt, dev, (B, H, L, dv))
     _check(dS_final, "dS_final", torch.float32, dev, (B, H, dv, dk))

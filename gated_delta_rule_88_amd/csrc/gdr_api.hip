@@ -237,8 +237,7 @@ GDR_EXPORT size_t gdr_bwd_chunked_workspace_size(int B, int H, int L, int d_k, i
                                                  int dtype, int alpha_mode)
 {
     if (check_chunk_sizes(B, H, L, d_k, d_v, C, dtype, alpha_mode) != GDR_OK) return (size_t)-1;
-    if (alpha_mode == GDR_ALPHA_CHANNEL) return (size_t)-1;
-    return gdr::bwd_workspace_bytes(B, H, L, d_k, d_v, C, dtype);
+    return gdr::bwd_workspace_bytes(B, H, L, d_k, d_v, C, dtype, alpha_mode);
 }
 
 GDR_EXPORT int gdr_bwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
@@ -251,7 +250,6 @@ GDR_EXPORT int gdr_bwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int
 {
     int st = check_chunk_sizes(B, H, L, d_k, d_v, C, dtype, alpha_mode);
     if (st != GDR_OK) return st;
-    if (alpha_mode == GDR_ALPHA_CHANNEL) return GDR_ERR_UNSUPPORTED;
     const size_t BH = (size_t)B * H;
     if (BH == 0) return GDR_OK;
     const size_t es = elem_size(dtype);
@@ -268,13 +266,14 @@ GDR_EXPORT int gdr_bwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int
         !aligned(dbeta, 4) || !aligned(dlog_alpha, 4))
         return GDR_ERR_INVALID_ARG;
 
-    const size_t la_bytes = alpha_mode == GDR_ALPHA_SCALAR ? nt * 4 : 0;
+    const size_t la_bytes = alpha_mode == GDR_ALPHA_SCALAR ? nt * 4
+                            : alpha_mode == GDR_ALPHA_CHANNEL ? nt * d_k * 4 : 0;
     const Range rq = rng(q, nt * d_k * es), rk = rng(k, nt * d_k * es), rv = rng(v, nt * d_v * es);
     const Range rb = rng(beta, nt * 4), ra = rng(log_alpha, la_bytes), r0 = rng(S0, state_bytes);
     const Range rdo = rng(dO, nt * d_v * es), rdf = rng(dS_final, state_bytes);
     const Range oq = rng(dq, nt * d_k * es), ok = rng(dk, nt * d_k * es), ov = rng(dv, nt * d_v * es);
     const Range ob = rng(dbeta, nt * 4), oa = rng(dlog_alpha, la_bytes), o0 = rng(dS0, state_bytes);
-    const size_t need = gdr::bwd_workspace_bytes(B, H, L, d_k, d_v, C, dtype);
+    const size_t need = gdr::bwd_workspace_bytes(B, H, L, d_k, d_v, C, dtype, alpha_mode);
     const Range rw = rng(workspace, need);
     const Range ins[] = {rq, rk, rv, rb, ra, r0, rdo, rdf};
     const Range outs[] = {oq, ok, ov, ob, oa, o0, rw};

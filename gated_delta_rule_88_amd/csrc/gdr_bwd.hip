@@ -1,5 +1,5 @@
 // gdr_bwd.hip -- chunked backward (the gradients training needs) of the
-// gated delta-rule memory, for alpha = 1 and scalar alpha.
+// gated delta-rule memory, for alpha = 1, scalar alpha and channel alpha.
 //
 // Forward over one chunk of C tokens with entry state S0 (notation of
 // gdr_scan.hip; g = in-chunk cumulative log alpha, gamma = e^g,
@@ -30,7 +30,9 @@
 //                           only sequential part) and keeps dS_end of every
 //                           chunk;
 //   chunk_bwd_grad_kernel   one workgroup per chunk: every gradient of the
-//                           chunk's tokens from S0, dS_end and its inputs.
+//                           chunk's tokens from S0, dS_end and its inputs
+//                           (chunk_bwd_grad_channel_kernel for channel alpha,
+//                           whose chunk algebra is written out above it).
 // The products run on MFMA (bf16 operands for bf16 inputs, fp32 otherwise;
 // fp32 accumulation); the triangular parts (T, dA) stay in fp32.
 #include "gdr_device.h"
@@ -92,6 +94,18 @@ __device__ __forceinline__ void tmma(f32x4& acc, const TA* A, int lda, int m0, c
     for (int k0 = 0; k0 < K; k0 += 32) mma(acc, cfrag<E>(A, lda, m0, k0, K), cfrag<E>(B, ldb, n0, k0, K));
 }
 
+// acc += A B^T on one 16 x 16 tile with a 16-wide contraction in fp32
+// (A rows m0.. of [.][lda], B rows n0.. of [.][ldb], k = 0..15): lane group
+// g supplies k = 4 g + j to the j-th of four 16x16x4 products.
+template <typename TA>
+__device__ __forceinline__ void tmma16f(f32x4& acc, const TA* A, int lda, int m0, const float* B, int ldb, int n0)
+{
+    const int l = lane_id(), k = 4 * (l >> 4);
+    const f32x4 a = load4f(A + (m0 + (l & 15)) * lda + k), b = load4f(B + (n0 + (l & 15)) * ldb + k);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], acc, 0, 0, 0);
+}
+
 // Sum of x over the 16 lanes that share l / 16 (one tile row).
 __device__ __forceinline__ float row16_sum(float x) {
 #pragma unroll
@@ -118,11 +132,21 @@ struct RowStage {
         }
     }
     __device__ __forceinline__ void store(E* dst, int LD, E* dstT, int LT, int tid) const {
+        store_plain(dst, LD, tid);
+        store_t(dstT, LT, tid);
+    }
+    __device__ __forceinline__ void store_plain(E* dst, int LD, int tid) const {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int x = tid + NT * j, r = x % ROWS, c = (x / ROWS) * VE;
+            if (x < ROWS * PER) st16(dst + r * LD + c, v[j]);
+        }
+    }
+    __device__ __forceinline__ void store_t(E* dstT, int LT, int tid) const {
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             const int x = tid + NT * j, r = x % ROWS, c = (x / ROWS) * VE;
             if (x < ROWS * PER) {
-                st16(dst + r * LD + c, v[j]);
                 E e[VE];
                 __builtin_memcpy(e, &v[j], 16);
 #pragma unroll
@@ -160,6 +184,8 @@ struct Strides {
 // ---------------------------------------------------------------- chain
 template <typename E, int DK, int CK>
 struct ChainLds : Strides<E, DK, CK> {
+    // (channel alpha: K holds K . exp(G_C - G), Kt and Qt the transposes of
+    // K . exp(G) and Q . exp(G), M is unused, f holds exp(G_C) per channel)
     using S = Strides<E, DK, CK>;
     static constexpr int ES = (int)sizeof(E);
     static constexpr int off_K = 0;                            // [CK][LDK] E
@@ -172,18 +198,19 @@ struct ChainLds : Strides<E, DK, CK> {
     static constexpr int off_Pt = off_Tt + CK * S::LCK * ES;       // [CK][LCK] E, P^T
     static constexpr int off_M = off_Pt + CK * S::LCK * ES;        // [CK][LF] f32, Gamma . M_incl
     static constexpr int off_f = off_M + CK * S::LF * 4;           // gamma [CK], D [CK], gamma_C
-    static constexpr int off_w = off_f + (2 * CK + 4) * 4;         // per wave: dS [16][LDK], dU^T, -gamma dR^T [16][LCK]
+    static constexpr int NF = (2 * CK + 4 > DK ? 2 * CK + 4 : DK);
+    static constexpr int off_w = off_f + NF * 4;                    // per wave: dS [16][LDK], dU^T, -gamma dR^T [16][LCK]
     static constexpr int wbytes = 16 * S::LDK * ES + 2 * 16 * S::LCK * ES;
     static constexpr int bytes = off_w + 2 * wbytes;
 };
 
-template <typename E, int DK, int CK>
+template <typename E, int DK, int CK, bool CH>
 __global__ __launch_bounds__(128) void chunk_bwd_chain_kernel(BwdParams p)
 {
     using LY = ChainLds<E, DK, CK>;
     constexpr int NJ = DK / 16, NB = CK / 16, VE = Vec<E>::n;
     constexpr int LDK = LY::LDK, LCK = LY::LCK, LF = LY::LF;
-    constexpr WsLayout WL = ws_layout((int)sizeof(E), DK, CK, kAlphaScalar);
+    constexpr WsLayout WL = ws_layout((int)sizeof(E), DK, CK, CH ? kAlphaChannel : kAlphaScalar);
     extern __shared__ __align__(16) unsigned char smem[];
     E* Ks = reinterpret_cast<E*>(smem + LY::off_K);
     E* Kt = reinterpret_cast<E*>(smem + LY::off_Kt);
@@ -221,21 +248,28 @@ __global__ __launch_bounds__(128) void chunk_bwd_chain_kernel(BwdParams p)
     constexpr int NRV = CK * CK / VE;            // 16-byte vectors of T~ (and of Gamma)
     constexpr int PERO = kBV / VE;               // 16-byte vectors per token of the dO block
     constexpr int NOV = (CK * PERO + 127) / 128;
-    RowStage<E, CK, DK, 128> ks, qs;
+    RowStage<E, CK, DK, 128> ks, qs, gs;   // channel: K . exp(G_C - G), Q . exp(G), K . exp(G)
     u32x4 tv, mv, ov[NOV];
     float fv;
     auto fetch = [&](int n) {
         const int valid = min(CK, p.L - n * CK);
         const size_t tok = (size_t)bh * p.L + n * CK;
         const unsigned char* rec = p.ws + ((size_t)bh * p.NC + n) * WL.bytes;
-        ks.load(reinterpret_cast<const E*>(p.k) + tok * DK, DK, valid, tid);
-        qs.load(reinterpret_cast<const E*>(p.q) + tok * DK, DK, valid, tid);
+        if constexpr (CH) {
+            // the forward's decayed operands (zero past the end of the sequence)
+            ks.load(reinterpret_cast<const E*>(rec + WL.KD), DK, CK, tid);
+            qs.load(reinterpret_cast<const E*>(rec + WL.QG), DK, CK, tid);
+            gs.load(reinterpret_cast<const E*>(rec + WL.KG), DK, CK, tid);
+        } else {
+            ks.load(reinterpret_cast<const E*>(p.k) + tok * DK, DK, valid, tid);
+            qs.load(reinterpret_cast<const E*>(p.q) + tok * DK, DK, valid, tid);
+        }
         tv = mv = u32x4{0u, 0u, 0u, 0u};
         if (tid < NRV) {
             tv = ld16(rec + WL.T + 16 * tid);
             mv = ld16(rec + WL.M + 16 * tid);
         }
-        fv = tid <= 2 * CK ? reinterpret_cast<const float*>(rec + WL.F)[tid] : 0.f;
+        fv = tid < (CH ? DK : 2 * CK + 1) ? reinterpret_cast<const float*>(rec + WL.F)[tid] : 0.f;
         const E* dog = reinterpret_cast<const E*>(p.dO) + tok * p.DV + v0;
 #pragma unroll
         for (int j = 0; j < NOV; ++j) {
@@ -247,22 +281,28 @@ __global__ __launch_bounds__(128) void chunk_bwd_chain_kernel(BwdParams p)
 
     for (int n = p.NC - 1; n >= 0; --n) {
         // ---- the chunk into LDS; keep dS at the chunk's end
-        ks.store(Ks, LDK, Kt, LCK, tid);
-        qs.store(Qs, LDK, Qt, LCK, tid);
+        if constexpr (CH) {
+            ks.store_plain(Ks, LDK, tid);
+            qs.store_t(Qt, LCK, tid);
+            gs.store_t(Kt, LCK, tid);
+        } else {
+            ks.store(Ks, LDK, Kt, LCK, tid);
+            qs.store(Qs, LDK, Qt, LCK, tid);
+        }
         if (tid < NRV) {
             const int r = (VE * tid) / CK, mc0 = (VE * tid) % CK;
-            E te[VE];
-            float me[VE];
+            E te[VE], me[VE];
             __builtin_memcpy(te, &tv, 16);
-            Pack<E>::unpack(mv, me);
+            __builtin_memcpy(me, &mv, 16);
 #pragma unroll
             for (int j = 0; j < VE; ++j) {
                 const int t = tok_of_col(CK, mc0 + j);
                 Tts[t * LCK + r] = te[j];
-                Ms[r * LF + t] = me[j];
+                if constexpr (CH) Pt[t * LCK + r] = me[j];       // the score block, transposed
+                else Ms[r * LF + t] = to_f32(me[j]);
             }
         }
-        if (tid <= 2 * CK) gam[tid] = fv;   // gamma, D (Dd = gam + CK), gamma_C
+        if (tid < (CH ? DK : 2 * CK + 1)) gam[tid] = fv;   // gamma, D, gamma_C (channel: exp(G_C))
 #pragma unroll
         for (int j = 0; j < NOV; ++j) {
             const int x = tid + 128 * j, r = x % CK, c = (x / CK) * VE;
@@ -285,11 +325,13 @@ __global__ __launch_bounds__(128) void chunk_bwd_chain_kernel(BwdParams p)
         if (n > 0) fetch(n - 1);
         __syncthreads();
         // (gamma . dO)^T
+        if constexpr (!CH)
         for (int x = tid; x < CK * kBV; x += 128) {
             const int r = x % CK, i = x / CK;
             gdOt[i * LCK + r] = from_f32<E>(gam[r] * to_f32(dOt[i * LCK + r]));
         }
         // ---- P = Q K^T . Gamma . M_incl (tiles on or below the diagonal), kept as P^T
+        if constexpr (!CH)
         for (int tl = w; tl < NB * NB; tl += 2) {
             const int rb = tl / NB, ib = tl % NB;
             f32x4 acc = zero4();
@@ -310,7 +352,7 @@ __global__ __launch_bounds__(128) void chunk_bwd_chain_kernel(BwdParams p)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * g4 + e;
-                dUt[c16 * LCK + r] = from_f32<E>(y[e] + Dd[r] * kds[e]);
+                dUt[c16 * LCK + r] = from_f32<E>(y[e] + (CH ? 1.f : Dd[r]) * kds[e]);
             }
         }
         wave_lds_fence();
@@ -322,18 +364,20 @@ __global__ __launch_bounds__(128) void chunk_bwd_chain_kernel(BwdParams p)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * g4 + e;
-                dRt[c16 * LCK + r] = from_f32<E>(-gam[r] * dr[e]);
+                dRt[c16 * LCK + r] = from_f32<E>(-(CH ? 1.f : gam[r]) * dr[e]);
             }
         }
         wave_lds_fence();
         // ---- dS <- gamma_C dS + (gamma . dO)^T Q - (gamma . dR)^T K
-        const float gC = gam[2 * CK];
+        // (channel: dS Diag(exp(G_C)) + dO^T (Q . exp(G)) - dR^T (K . exp(G)))
+        const float gC = CH ? 0.f : gam[2 * CK];
 #pragma unroll
         for (int jb = 0; jb < NJ; ++jb) {
             f32x4 acc = dS[jb];
+            const float sc = CH ? gam[16 * jb + c16] : gC;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] *= gC;
-            tmma<E>(acc, gdOt + 16 * w * LCK, LCK, 0, Qt, LCK, 16 * jb, CK);
+            for (int e = 0; e < 4; ++e) acc[e] *= sc;
+            tmma<E>(acc, (CH ? dOt : gdOt) + 16 * w * LCK, LCK, 0, Qt, LCK, 16 * jb, CK);
             tmma<E>(acc, dRt, LCK, 0, Kt, LCK, 16 * jb, CK);
             dS[jb] = acc;
         }
@@ -784,23 +828,518 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
     }
 }
 
+// ------------------------------------------------------- grads, channel alpha
+// Per-channel decay G (C x d_k, cumulative within the chunk).  With
+// Kg = K . e^G, Qg = Q . e^G, Kd = K . e^{G_C - G} (from the forward's
+// record) and the scores P_ri = sum_c q_rc k_ic e^{G_rc - G_ic}, A likewise
+// from K, the gradients of one chunk are
+//   dQ = (dO S0) . e^G + dQ_P,  dQ_P[r][c] = sum_i dPM_ri k_ic e^{G_rc - G_ic}
+//   dK = (dX S0) . e^G + (U dS_end) . e^{G_C - G} + dK_A1 + dK_P2 + dK_A2
+//        dK_A1[r][c] = sum_i dAb_ri k_ic e^{G_rc - G_ic}
+//        dK_P2[i][c] = sum_r dPM_ri q_rc e^{G_rc - G_ic},  dK_A2 likewise with dAb, k
+//   dG  = (dO S0) . Qg + (dX S0) . Kg - (U dS_end) . Kd + dQ_P . Q + (dK_A1 - dK_P2 - dK_A2) . K
+//   dG_C += sum_r (U dS_end . Kd)_r + e^{G_C} <dS_end, S0> per channel,
+// with dPM = dO U^T . M_incl and dAb = diag(beta) dA.  The four sums with the
+// decay inside run per pair of 16-token tiles through a reference row m of
+// the pair (the forward's scheme): e^{G_r - G_i} = e^{G_r - G_m} e^{G_m - G_i}
+// with both factors at most 1 off the diagonal and at most e^80 on it.
+constexpr int kBVC = 16;   // value channels per block (channel alpha)
+
 template <typename E, int DK, int CK>
-static hipError_t launch_bwd_t(const BwdParams& bp, int BH, hipStream_t stream)
+struct GradChLds : Strides<E, DK, CK> {
+    using S = Strides<E, DK, CK>;
+    static constexpr int ES = (int)sizeof(E);
+    static constexpr int LB = kBVC + S::PE;      // rows of kBVC elements
+    static constexpr int LG = DK + 4;            // fp32 rows of d_k
+    static constexpr int LBF = kBVC + 4;
+    static constexpr int FCC = CK * S::LF * 4, ECC = CK * S::LCK * ES;
+    static constexpr int ERD = CK * S::LDK * ES;
+    // kept for the whole chunk
+    static constexpr int off_K = 0;                            // raw K, Q; Kg, Kd [CK][LDK] E
+    static constexpr int off_Q = off_K + ERD;
+    static constexpr int off_Kg = off_Q + ERD;
+    static constexpr int off_Kd = off_Kg + ERD;
+    static constexpr int off_G = off_Kd + ERD;                 // [CK][LG] f32
+    static constexpr int off_Bm = off_G + CK * LG * 4;         // [CK][LF] f32
+    static constexpr int off_A = off_Bm + FCC;
+    static constexpr int off_T = off_A + FCC;
+    static constexpr int off_Tft = off_T + FCC;
+    static constexpr int off_Tt = off_Tft + FCC;               // [CK][LCK] E
+    static constexpr int off_Ttt = off_Tt + ECC;
+    static constexpr int off_Pt = off_Ttt + ECC;
+    static constexpr int off_vec = off_Pt + ECC;               // beta [CK], <dS, S0> per channel [DK], red [16]
+    static constexpr int NVEC = CK + DK + 16;
+    static constexpr int off_blk = (off_vec + NVEC * 4 + 15) / 16 * 16;
+    // one block of kBVC value channels
+    static constexpr int off_S0 = off_blk;                     // [kBVC][LDK] E and [DK][LB]
+    static constexpr int off_dS = off_S0 + kBVC * S::LDK * ES;
+    static constexpr int off_S0t = off_dS + kBVC * S::LDK * ES;
+    static constexpr int off_dSt = off_S0t + DK * LB * ES;
+    static constexpr int off_dO = off_dSt + DK * LB * ES;      // [CK][LB] E
+    static constexpr int off_R = off_dO + CK * LB * ES;
+    static constexpr int off_U = off_R + CK * LB * ES;
+    static constexpr int off_dU = off_U + CK * LB * ES;
+    static constexpr int off_dX = off_dU + CK * LB * ES;
+    static constexpr int off_dOt = off_dX + CK * LB * ES;      // [kBVC][LCK] E
+    static constexpr int off_Rt = off_dOt + kBVC * S::LCK * ES;
+    static constexpr int off_dUt = off_Rt + kBVC * S::LCK * ES;
+    static constexpr int off_V = off_dUt + kBVC * S::LCK * ES; // [CK][LBF] f32
+    static constexpr int off_KdS = off_V + CK * LBF * 4;
+    static constexpr int blk_end = off_KdS + CK * LBF * 4;
+    // last phases, over the block region
+    static constexpr int off_dTt = off_blk;                    // [CK][LF] f32 (triangular part)
+    static constexpr int off_dTb = off_dTt + FCC;
+    static constexpr int off_Y1t = off_dTb + FCC;
+    static constexpr int off_dA = off_Y1t + FCC;
+    static constexpr int off_dPM = off_dA + FCC;               // [CK][LCK] E
+    static constexpr int off_dPMt = off_dPM + ECC;
+    static constexpr int off_dAb = off_dPMt + ECC;
+    static constexpr int off_dAbt = off_dAb + ECC;
+    static constexpr int LS = 16 + 4;                          // fp32 rows of 16
+    static constexpr int off_Sk = off_dAbt + ECC;              // [DK][LS] f32 per tile pair
+    static constexpr int off_Sq = off_Sk + DK * LS * 4;
+    static constexpr int off_Sk2 = off_Sq + DK * LS * 4;
+    static constexpr int pair_end = off_Sk2 + DK * LS * 4;
+    static constexpr int off_dGm = off_blk;                    // [CK][LG] f32 (after the pairs)
+    static constexpr int off_Y3Kd = off_dGm + CK * LG * 4;
+    static constexpr int last_end = off_Y3Kd + CK * LG * 4;
+    static constexpr int m1 = blk_end > pair_end ? blk_end : pair_end;
+    static constexpr int bytes = m1 > last_end ? m1 : last_end;
+};
+
+template <typename E, int DK, int CK>
+__global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p)
+{
+    using LY = GradChLds<E, DK, CK>;
+    constexpr int NB = CK / 16, NJ = DK / 16, VE = Vec<E>::n;
+    constexpr int LF = LY::LF, LDK = LY::LDK, LCK = LY::LCK, LB = LY::LB, LG = LY::LG, LBF = LY::LBF;
+    constexpr int LS = LY::LS;
+    constexpr int NT = 512, NW = NT / kWave;
+    constexpr int NQT = NB * NJ, NQW = (NQT + NW - 1) / NW;
+    constexpr int NCC = NB * NB, NPAIR = NB * (NB + 1) / 2;
+    constexpr WsLayout WL = ws_layout((int)sizeof(E), DK, CK, kAlphaChannel);
+    extern __shared__ __align__(16) unsigned char smem[];
+#define GL_E(name, off) E* name = reinterpret_cast<E*>(smem + LY::off)
+#define GL_F(name, off) float* name = reinterpret_cast<float*>(smem + LY::off)
+    GL_E(Ks, off_K); GL_E(Qs, off_Q); GL_E(Kgs, off_Kg); GL_E(Kds, off_Kd); GL_F(Gs, off_G);
+    GL_F(Bm, off_Bm); GL_F(Af, off_A); GL_F(Tf, off_T); GL_F(Tft, off_Tft);
+    GL_E(Tt, off_Tt); GL_E(Ttt, off_Ttt); GL_E(Pt, off_Pt);
+    GL_E(S0s, off_S0); GL_E(dSs, off_dS); GL_E(S0t, off_S0t); GL_E(dSt, off_dSt);
+    GL_E(dOs, off_dO); GL_E(Rs, off_R); GL_E(Us, off_U); GL_E(dUs, off_dU); GL_E(dXs, off_dX);
+    GL_E(dOt, off_dOt); GL_E(Rt, off_Rt); GL_E(dUt, off_dUt); GL_F(Vs, off_V); GL_F(KdSs, off_KdS);
+    GL_F(dTt, off_dTt); GL_F(dTb, off_dTb); GL_F(Y1t, off_Y1t); GL_F(dAf, off_dA);
+    GL_E(dPM, off_dPM); GL_E(dPMt, off_dPMt); GL_E(dAb, off_dAb); GL_E(dAbt, off_dAbt);
+    GL_F(Sk, off_Sk); GL_F(Sq, off_Sq); GL_F(Sk2, off_Sk2); GL_F(dGm, off_dGm); GL_F(Y3Kd, off_Y3Kd);
+#undef GL_E
+#undef GL_F
+    float* bs = reinterpret_cast<float*>(smem + LY::off_vec);
+    float* hC = bs + CK;         // <dS_end, S0> per key channel
+    const int cid = blockIdx.x;
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id(), g4 = l >> 4, c16 = l & 15;
+    const int bh = cid / p.NC, n = cid % p.NC;
+    const int t0 = n * CK, valid = min(CK, p.L - t0);
+    const size_t tok = (size_t)bh * p.L + t0;
+    const unsigned char* rec = p.ws + (size_t)cid * WL.bytes;
+
+    // ---- keys, queries, the forward's decayed keys, log alpha, beta
+    {
+        RowStage<E, CK, DK, NT> ks, qs, kg, kd;
+        ks.load(reinterpret_cast<const E*>(p.k) + tok * DK, DK, valid, tid);
+        qs.load(reinterpret_cast<const E*>(p.q) + tok * DK, DK, valid, tid);
+        kg.load(reinterpret_cast<const E*>(rec + WL.KG), DK, CK, tid);
+        kd.load(reinterpret_cast<const E*>(rec + WL.KD), DK, CK, tid);
+        constexpr int NLV = (CK * DK / 4 + NT - 1) / NT;
+        f32x4 lv[NLV];
+#pragma unroll
+        for (int j = 0; j < NLV; ++j) {
+            const int x = tid + NT * j, r = (4 * x) / DK;
+            lv[j] = zero4();
+            if (x < CK * DK / 4 && r < valid)
+                lv[j] = *reinterpret_cast<const f32x4*>(p.log_alpha + (tok + r) * DK + (4 * x) % DK);
+        }
+        ks.store_plain(Ks, LDK, tid);
+        qs.store_plain(Qs, LDK, tid);
+        kg.store_plain(Kgs, LDK, tid);
+        kd.store_plain(Kds, LDK, tid);
+#pragma unroll
+        for (int j = 0; j < NLV; ++j) {
+            const int x = tid + NT * j, r = (4 * x) / DK, c = (4 * x) % DK;
+            if (x < CK * DK / 4)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Gs[r * LG + c + e] = r < valid ? fmaxf(lv[j][e], kChannelLogAlphaMin) : 0.f;
+        }
+        if (tid < CK) bs[tid] = tid < valid ? p.beta[tok + tid] : 0.f;
+        if (tid < DK) hC[tid] = 0.f;
+        // the score block P (masked, from the forward's record), transposed
+        for (int x = tid; x < CK * CK; x += NT) {
+            const int r = x / CK, t = tok_of_col(CK, x % CK);
+            Pt[t * LCK + r] = reinterpret_cast<const E*>(rec + WL.M)[x];
+        }
+    }
+    __syncthreads();
+    // cumulative sum down every key channel
+    if (tid < DK) {
+        float g = 0.f;
+        for (int r = 0; r < CK; ++r) {
+            g += Gs[r * LG + tid];
+            Gs[r * LG + tid] = g;
+        }
+    }
+    __syncthreads();
+    // ---- Bm = strictly-lower(K K^T with the decay inside), A = diag(beta) Bm,
+    // through the reference rows of each tile pair
+    if (w < NPAIR) {
+        const int rb = (w == 0) ? 0 : 1, ib = (w == 2) ? 1 : 0;
+        const int m = (rb == ib) ? 16 * rb + 7 : 16 * rb - 1;
+        const int rl = 16 * rb + c16, rr = 16 * ib + c16;
+        f32x4 acc = zero4();
+        for (int c0 = 8 * g4; c0 < DK; c0 += 32) {
+            float fl[8], fr[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float gm = Gs[m * LG + c0 + j];
+                fl[j] = __expf(Gs[rl * LG + c0 + j] - gm);
+                fr[j] = __expf(gm - Gs[rr * LG + c0 + j]);
+            }
+            Frag<E> kl, kr;
+            load_scaled_frag(kl, Ks + rl * LDK + c0, fl);
+            load_scaled_frag(kr, Ks + rr * LDK + c0, fr);
+            mma(acc, kl, kr);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rb + 4 * g4 + e, i = 16 * ib + c16;
+            Bm[r * LF + i] = r > i ? acc[e] : 0.f;
+            Af[r * LF + i] = r > i ? bs[r] * acc[e] : 0.f;
+        }
+    }
+    if constexpr (NB == 2) {
+        if (w == 3) {   // the tile above the diagonal
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g4 + e, i = 16 + c16;
+                Bm[r * LF + i] = 0.f;
+                Af[r * LF + i] = 0.f;
+            }
+        }
+    }
+    __syncthreads();
+    if (w == 0) unit_lower_inverse<CK, LF>(Af, Tf);
+    __syncthreads();
+    for (int x = tid; x < CK * CK; x += NT) {
+        const int r = x % CK, s2 = x / CK;
+        const float t = s2 <= r ? Tf[r * LF + s2] : 0.f;
+        Tf[r * LF + s2] = t;
+        Tft[s2 * LF + r] = t;
+        Tt[r * LCK + s2] = from_f32<E>(t * bs[s2]);
+        Ttt[s2 * LCK + r] = from_f32<E>(t * bs[s2]);
+    }
+
+    // C x DK accumulators: Y1 = dO S0, Y2 = dX S0, Y3 = U dS_end
+    f32x4 Y1[NQW], Y2[NQW], Y3[NQW];
+#pragma unroll
+    for (int u = 0; u < NQW; ++u) { Y1[u] = zero4(); Y2[u] = zero4(); Y3[u] = zero4(); }
+    f32x4 dPa = zero4(), dTa = zero4();   // C x C tile w (w < NCC)
+
+    const E* S0g = static_cast<const E*>(p.Sck) + (size_t)cid * p.DV * DK;
+    const E* dSg = static_cast<const E*>(p.dSck) + (size_t)cid * p.DV * DK;
+    const E* vg = reinterpret_cast<const E*>(p.v) + tok * p.DV;
+    const E* dog = reinterpret_cast<const E*>(p.dO) + tok * p.DV;
+    constexpr int NSV = (kBVC * DK / VE + NT - 1) / NT;
+    constexpr int PERV = kBVC / VE;
+    u32x4 sa[NSV], sb[NSV], va, da;
+    auto fetch = [&](int v0) {
+#pragma unroll
+        for (int u = 0; u < NSV; ++u) {
+            const int xs = tid + NT * u, i = xs % kBVC, j = VE * (xs / kBVC);
+            if (xs < kBVC * DK / VE) {
+                sa[u] = ld16(S0g + (size_t)(v0 + i) * DK + j);
+                sb[u] = ld16(dSg + (size_t)(v0 + i) * DK + j);
+            }
+        }
+        const int r = tid % CK, c = (tid / CK) * VE;
+        const bool ok = tid < CK * PERV && r < valid;
+        va = ok ? ld16(vg + (size_t)r * p.DV + v0 + c) : u32x4{0u, 0u, 0u, 0u};
+        da = ok ? ld16(dog + (size_t)r * p.DV + v0 + c) : u32x4{0u, 0u, 0u, 0u};
+    };
+    fetch(0);
+    for (int v0 = 0; v0 < p.DV; v0 += kBVC) {
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < NSV; ++u) {
+            const int xs = tid + NT * u, i = xs % kBVC, j = VE * (xs / kBVC);
+            if (xs >= kBVC * DK / VE) continue;
+            E a[VE], b[VE];
+            __builtin_memcpy(a, &sa[u], 16);
+            __builtin_memcpy(b, &sb[u], 16);
+            st16(S0s + i * LDK + j, sa[u]);
+            st16(dSs + i * LDK + j, sb[u]);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                S0t[(j + e) * LB + i] = a[e];
+                dSt[(j + e) * LB + i] = b[e];
+            }
+        }
+        if (tid < CK * PERV) {
+            const int r = tid % CK, c = (tid / CK) * VE;
+            float a[VE], d[VE];
+            Pack<E>::unpack(va, a);
+            Pack<E>::unpack(da, d);
+#pragma unroll
+            for (int j = 0; j < VE; ++j) {
+                Vs[r * LBF + c + j] = a[j];
+                dOs[r * LB + c + j] = from_f32<E>(d[j]);
+                dOt[(c + j) * LCK + r] = from_f32<E>(d[j]);
+            }
+        }
+        if (v0 + kBVC < p.DV) fetch(v0 + kBVC);
+        __syncthreads();
+        // ---- X = Kg S0^T, R = V - X (waves 0..NB-1); Kd dS^T (waves 4..); <dS, S0> per channel
+        if (w < NB) {
+            const int rb = w;
+            f32x4 x = zero4();
+            tmma<E>(x, Kgs, LDK, 16 * rb, S0s, LDK, 0, DK);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * g4 + e, i = c16;
+                const float rr = Vs[r * LBF + i] - x[e];
+                Rs[r * LB + i] = from_f32<E>(rr);
+                Rt[i * LCK + r] = from_f32<E>(rr);
+            }
+        } else if (w >= 4 && w < 4 + NB) {
+            const int rb = w - 4;
+            f32x4 kds = zero4();
+            tmma<E>(kds, Kds, LDK, 16 * rb, dSs, LDK, 0, DK);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) KdSs[(16 * rb + 4 * g4 + e) * LBF + c16] = kds[e];
+        } else if (w == 2 || w == 3) {
+            for (int c = tid - 128; c < DK; c += 128) {
+                float h = 0.f;
+#pragma unroll
+                for (int i = 0; i < kBVC; ++i) h += to_f32(S0s[i * LDK + c]) * to_f32(dSs[i * LDK + c]);
+                hC[c] += h;
+            }
+        }
+        __syncthreads();
+        // ---- U = T~ R (waves 0..), dU = P^T dO + Kd dS^T (waves 4..)
+        if (w < NB) {
+            const int rb = w;
+            f32x4 u = zero4();
+            tmma<E>(u, Tt, LCK, 16 * rb, Rt, LCK, 0, CK);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Us[(16 * rb + 4 * g4 + e) * LB + c16] = from_f32<E>(u[e]);
+        } else if (w >= 4 && w < 4 + NB) {
+            const int rb = w - 4;
+            f32x4 du = zero4();
+            tmma<E>(du, Pt, LCK, 16 * rb, dOt, LCK, 0, CK);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * g4 + e;
+                const float dd = du[e] + KdSs[r * LBF + c16];
+                dUs[r * LB + c16] = from_f32<E>(dd);
+                dUt[c16 * LCK + r] = from_f32<E>(dd);
+            }
+        }
+        __syncthreads();
+        // ---- dR = T~^T dU (= dV), dX = -dR
+        if (w < NB) {
+            const int rb = w;
+            f32x4 dr = zero4();
+            tmma<E>(dr, Ttt, LCK, 16 * rb, dUt, LCK, 0, CK);
+            E* dvg = reinterpret_cast<E*>(p.dv) + tok * p.DV + v0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * g4 + e;
+                if (r < valid) dvg[(size_t)r * p.DV + c16] = from_f32<E>(dr[e]);
+                dXs[r * LB + c16] = from_f32<E>(-dr[e]);
+            }
+        }
+        __syncthreads();
+        // ---- accumulate over the block's value channels
+#pragma unroll
+        for (int u = 0; u < NQW; ++u) {
+            const int t = w + NW * u;
+            if (t < NQT) {
+                const int rb = t / NJ, jb = t % NJ;
+                tmma<E>(Y1[u], dOs, LB, 16 * rb, S0t, LB, 16 * jb, kBVC);
+                tmma<E>(Y2[u], dXs, LB, 16 * rb, S0t, LB, 16 * jb, kBVC);
+                tmma<E>(Y3[u], Us, LB, 16 * rb, dSt, LB, 16 * jb, kBVC);
+            }
+        }
+        if (w < NCC) {
+            const int rb = w / NB, sb = w % NB;
+            tmma<E>(dPa, dOs, LB, 16 * rb, Us, LB, 16 * sb, kBVC);
+            tmma<E>(dTa, dUs, LB, 16 * rb, Rs, LB, 16 * sb, kBVC);
+        }
+    }
+    __syncthreads();   // the block region is reused below
+
+    // ---- triangular part: dPM, dT~; dA = strictly-lower(-T^T dT~ diag(beta) T^T)
+    if (w < NCC) {
+        const int rb = w / NB, sb = w % NB;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rb + 4 * g4 + e, s2 = 16 * sb + c16;
+            const float dpm = r >= s2 ? dPa[e] : 0.f;
+            dPM[r * LCK + s2] = from_f32<E>(dpm);
+            dPMt[s2 * LCK + r] = from_f32<E>(dpm);
+            dTt[r * LF + s2] = dTa[e];
+            dTb[r * LF + s2] = dTa[e] * bs[s2];
+        }
+    }
+    __syncthreads();
+    if (w < NCC) {
+        const int rb = w / NB, sb = w % NB;
+        f32x4 y = zero4();
+        tmma<float>(y, dTb, LF, 16 * rb, Tf, LF, 16 * sb, CK);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Y1t[(16 * sb + c16) * LF + 16 * rb + 4 * g4 + e] = y[e];
+    }
+    __syncthreads();
+    if (w < NCC) {
+        const int rb = w / NB, sb = w % NB;
+        f32x4 y = zero4();
+        tmma<float>(y, Tft, LF, 16 * rb, Y1t, LF, 16 * sb, CK);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rb + 4 * g4 + e, s2 = 16 * sb + c16;
+            const float da = r > s2 ? -y[e] : 0.f;
+            dAf[r * LF + s2] = da;
+            dAb[r * LCK + s2] = from_f32<E>(da * bs[r]);
+            dAbt[s2 * LCK + r] = from_f32<E>(da * bs[r]);
+        }
+    }
+    __syncthreads();
+    if (w == 0 && l < valid) {
+        float db = 0.f;
+        for (int u = 0; u < CK; ++u) db += Tf[u * LF + l] * dTt[u * LF + l];
+        for (int s2 = 0; s2 < CK; ++s2) db += dAf[l * LF + s2] * Bm[l * LF + s2];
+        p.dbeta[tok + l] = db;
+    }
+
+    // ---- the four sums with the decay inside, one tile pair at a time
+    f32x4 QP[NQW], KP[NQW], KM[NQW];   // dQ_P, dK_A1, dK_P2 + dK_A2
+#pragma unroll
+    for (int u = 0; u < NQW; ++u) { QP[u] = zero4(); KP[u] = zero4(); KM[u] = zero4(); }
+    for (int pr = 0; pr < NPAIR; ++pr) {
+        const int rb = (pr == 0) ? 0 : 1, ib = (pr == 2) ? 1 : 0;
+        const int m = (rb == ib) ? 16 * rb + 7 : 16 * rb - 1;
+        __syncthreads();   // the previous pair's operands are consumed (and dA is read)
+        // Sk[c][i] = k_ic e^{G_mc - G_ic} (i in tile ib); Sq, Sk2[c][r] = (q, k)_rc e^{G_rc - G_mc}
+        // (r in tile rb).  These products stay in fp32: the terms of dG they give
+        // cancel in pairs in the suffix sums of d log alpha, which bf16
+        // operands would leave at a few percent of the result.
+        for (int x = tid; x < 16 * DK; x += NT) {
+            const int i = x % 16, c = x / 16;
+            const float gm = Gs[m * LG + c];
+            const int ri = 16 * ib + i, rr = 16 * rb + i;
+            Sk[c * LS + i] = to_f32(Ks[ri * LDK + c]) * __expf(gm - Gs[ri * LG + c]);
+            const float fr = __expf(Gs[rr * LG + c] - gm);
+            Sq[c * LS + i] = to_f32(Qs[rr * LDK + c]) * fr;
+            Sk2[c * LS + i] = to_f32(Ks[rr * LDK + c]) * fr;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < NQW; ++u) {
+            const int t = w + NW * u;
+            if (t < NQT) {
+                const int ob = t / NJ, jb = t % NJ;
+                if (ob == rb) {
+                    // rows r of tile rb: sum over i in tile ib, then e^{G_rc - G_mc}
+                    f32x4 a = zero4(), b = zero4();
+                    tmma16f(a, dPM + 16 * ib, LCK, 16 * rb, Sk, LS, 16 * jb);
+                    tmma16f(b, dAb + 16 * ib, LCK, 16 * rb, Sk, LS, 16 * jb);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 16 * rb + 4 * g4 + e, c = 16 * jb + c16;
+                        const float f = __expf(Gs[r * LG + c] - Gs[m * LG + c]);
+                        QP[u][e] += f * a[e];
+                        KP[u][e] += f * b[e];
+                    }
+                }
+                if (ob == ib) {
+                    // rows i of tile ib: sum over r in tile rb, then e^{G_mc - G_ic}
+                    f32x4 a = zero4();
+                    tmma16f(a, dPMt + 16 * rb, LCK, 16 * ib, Sq, LS, 16 * jb);
+                    tmma16f(a, dAbt + 16 * rb, LCK, 16 * ib, Sk2, LS, 16 * jb);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 16 * ib + 4 * g4 + e, c = 16 * jb + c16;
+                        KM[u][e] += __expf(Gs[m * LG + c] - Gs[i * LG + c]) * a[e];
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();   // the pair operands give way to dG
+
+    // ---- dq, dk, and dG per token and channel
+    E* dqg = reinterpret_cast<E*>(p.dq) + tok * DK;
+    E* dkg = reinterpret_cast<E*>(p.dk) + tok * DK;
+#pragma unroll
+    for (int u = 0; u < NQW; ++u) {
+        const int t = w + NW * u;
+        if (t < NQT) {
+            const int rb = t / NJ, jb = t % NJ;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * g4 + e, c = 16 * jb + c16;
+                const float g = Gs[r * LG + c], gC = Gs[(CK - 1) * LG + c];
+                const float eG = __expf(g), eD = __expf(gC - g);
+                const float q = to_f32(Qs[r * LDK + c]), k = to_f32(Ks[r * LDK + c]);
+                const float dq = Y1[u][e] * eG + QP[u][e];
+                const float dkv = Y2[u][e] * eG + Y3[u][e] * eD + KP[u][e] + KM[u][e];
+                dGm[r * LG + c] = Y1[u][e] * q * eG + Y2[u][e] * k * eG - Y3[u][e] * k * eD + QP[u][e] * q +
+                                  (KP[u][e] - KM[u][e]) * k;
+                Y3Kd[r * LG + c] = Y3[u][e] * k * eD;
+                if (r < valid) {
+                    dqg[(size_t)r * DK + c] = from_f32<E>(dq);
+                    dkg[(size_t)r * DK + c] = from_f32<E>(dkv);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // d log alpha: suffix sums of dG down each channel, with the g_C terms
+    // entering at the chunk's last token; zero where the floor was active
+    if (tid < DK) {
+        const int c = tid;
+        const float gC = Gs[(CK - 1) * LG + c];
+        float tail = __expf(gC) * hC[c];
+        for (int r = 0; r < CK; ++r) tail += Y3Kd[r * LG + c];
+        float acc = tail;
+        for (int r = CK - 1; r >= 0; --r) {
+            acc += dGm[r * LG + c];
+            if (r < valid) {
+                const float la = p.log_alpha[(tok + r) * DK + c];
+                p.dlog_alpha[(tok + r) * DK + c] = la >= kChannelLogAlphaMin ? acc : 0.f;
+            }
+        }
+    }
+}
+
+template <typename K>
+static hipError_t launch_lds(K* kern, int grid, int threads, int lds, hipStream_t stream, const BwdParams& bp)
+{
+    hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, stream, bp);
+    return hipGetLastError();
+}
+
+template <typename E, int DK, int CK>
+static hipError_t launch_bwd_t(const BwdParams& bp, int BH, bool channel, hipStream_t stream)
 {
     using CL = ChainLds<E, DK, CK>;
     using GL = GradLds<E, DK, CK>;
-    static_assert(CL::bytes <= 160 * 1024 && GL::bytes <= 160 * 1024, "LDS budget");
-    auto* chain = chunk_bwd_chain_kernel<E, DK, CK>;
-    hipError_t err = hipFuncSetAttribute((const void*)chain, hipFuncAttributeMaxDynamicSharedMemorySize, CL::bytes);
+    using GC = GradChLds<E, DK, CK>;
+    static_assert(CL::bytes <= 160 * 1024 && GL::bytes <= 160 * 1024 && GC::bytes <= 160 * 1024, "LDS budget");
+    const int chains = BH * (bp.DV / kBV);
+    hipError_t err = channel ? launch_lds(chunk_bwd_chain_kernel<E, DK, CK, true>, chains, 128, CL::bytes, stream, bp)
+                             : launch_lds(chunk_bwd_chain_kernel<E, DK, CK, false>, chains, 128, CL::bytes, stream, bp);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(chain, dim3(BH * (bp.DV / kBV)), dim3(128), CL::bytes, stream, bp);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    auto* grad = chunk_bwd_grad_kernel<E, DK, CK>;
-    err = hipFuncSetAttribute((const void*)grad, hipFuncAttributeMaxDynamicSharedMemorySize, GL::bytes);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(grad, dim3(bp.total), dim3(512), GL::bytes, stream, bp);
-    return hipGetLastError();
+    return channel ? launch_lds(chunk_bwd_grad_channel_kernel<E, DK, CK>, bp.total, 512, GC::bytes, stream, bp)
+                   : launch_lds(chunk_bwd_grad_kernel<E, DK, CK>, bp.total, 512, GL::bytes, stream, bp);
 }
 
 }  // namespace
@@ -811,14 +1350,14 @@ struct BwdWs {
     size_t off_Sck, off_dSck, off_o, bytes;
 };
 
-static BwdWs bwd_ws(int B, int H, int L, int dk, int dv, int C, int dtype)
+static BwdWs bwd_ws(int B, int H, int L, int dk, int dv, int C, int dtype, int mode)
 {
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     const int CK = chunk_step(C, dtype);
     const size_t BH = (size_t)B * H, NC = (size_t)((L + CK - 1) / CK);
     const int es = dtype == kBF16 ? 2 : 4;
     BwdWs w{};
-    size_t o = al(BH * NC * (size_t)ws_layout(es, dk, CK, kAlphaScalar).bytes);
+    size_t o = al(BH * NC * (size_t)ws_layout(es, dk, CK, mode).bytes);
     w.off_Sck = o; o = al(o + BH * NC * dv * dk * es);
     w.off_dSck = o; o = al(o + BH * NC * dv * dk * es);
     w.off_o = o; o = al(o + BH * (size_t)L * dv * es);
@@ -826,10 +1365,10 @@ static BwdWs bwd_ws(int B, int H, int L, int dk, int dv, int C, int dtype)
     return w;
 }
 
-size_t bwd_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int dtype)
+size_t bwd_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int dtype, int mode)
 {
     if ((size_t)B * H == 0 || L == 0) return 0;
-    return bwd_ws(B, H, L, dk, dv, C, dtype).bytes;
+    return bwd_ws(B, H, L, dk, dv, C, dtype, mode).bytes;
 }
 
 __global__ void copy_grad_state_kernel(const float* __restrict__ src, float* __restrict__ dst, size_t n)
@@ -852,7 +1391,7 @@ hipError_t launch_bwd_chunked(const BwdArgs& b)
     }
     const int CK = chunk_step(b.C, b.dtype);
     const int NC = (b.L + CK - 1) / CK;
-    const BwdWs w = bwd_ws(b.B, b.H, b.L, b.dk, b.dv, b.C, b.dtype);
+    const BwdWs w = bwd_ws(b.B, b.H, b.L, b.dk, b.dv, b.C, b.dtype, b.mode);
     unsigned char* ws = static_cast<unsigned char*>(b.workspace);
     // forward again: the prepass records and every chunk's entry state
     ChunkArgs a{b.B, b.H, b.L, b.dk, b.dv, b.C, b.dtype, b.mode, b.q, b.k, b.v, b.beta, b.log_alpha, b.S0,
@@ -865,12 +1404,15 @@ hipError_t launch_bwd_chunked(const BwdArgs& b)
     BwdParams bp{b.q, b.k, b.v, b.dO, b.beta, b.log_alpha, b.dS_final, ws,
                  ws + w.off_Sck, ws + w.off_dSck,
                  b.dq, b.dk_out, b.dv_out, b.dbeta, b.dlog_alpha, b.dS0, b.L, NC, b.dv, (int)(BH * NC)};
+    const bool ch = b.mode == kAlphaChannel;
     if (b.dtype == kBF16) {
-        if (b.dk == 128) return CK == 16 ? launch_bwd_t<bf16, 128, 16>(bp, (int)BH, b.stream)
-                                         : launch_bwd_t<bf16, 128, 32>(bp, (int)BH, b.stream);
-        return CK == 16 ? launch_bwd_t<bf16, 64, 16>(bp, (int)BH, b.stream) : launch_bwd_t<bf16, 64, 32>(bp, (int)BH, b.stream);
+        if (b.dk == 128) return CK == 16 ? launch_bwd_t<bf16, 128, 16>(bp, (int)BH, ch, b.stream)
+                                         : launch_bwd_t<bf16, 128, 32>(bp, (int)BH, ch, b.stream);
+        return CK == 16 ? launch_bwd_t<bf16, 64, 16>(bp, (int)BH, ch, b.stream)
+                        : launch_bwd_t<bf16, 64, 32>(bp, (int)BH, ch, b.stream);
     }
-    return b.dk == 128 ? launch_bwd_t<float, 128, 16>(bp, (int)BH, b.stream) : launch_bwd_t<float, 64, 16>(bp, (int)BH, b.stream);
+    return b.dk == 128 ? launch_bwd_t<float, 128, 16>(bp, (int)BH, ch, b.stream)
+                       : launch_bwd_t<float, 64, 16>(bp, (int)BH, ch, b.stream);
 }
 
 }  // namespace gdr

@@ -75,7 +75,7 @@ size_t varlen_workspace_bytes(int NS, int H, int T, int dk, int dv, int C, int d
 hipError_t launch_decode_step(const DecodeArgs& a);
 hipError_t launch_fwd_chunked(const ChunkArgs& a);
 hipError_t launch_fwd_varlen(ChunkArgs a);
-size_t bwd_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int dtype);
+size_t bwd_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int dtype, int mode);
 hipError_t launch_bwd_chunked(const BwdArgs& b);
 
 }  // namespace gdr

@@ -169,8 +169,7 @@ int gdr_fwd_chunked_ex(int B, int H, int L, int d_k, int d_v, int C, int dtype,
 
 /*
  * Bytes of device workspace gdr_bwd_chunked needs (0 when B * H == 0 or
- * L == 0), or (size_t)-1 for invalid or unsupported sizes (channel alpha
- * included).  It holds the forward's chunk records, the state entering every
+ * L == 0), or (size_t)-1 for invalid or unsupported sizes.  It holds the forward's chunk records, the state entering every
  * chunk and the state gradient at every chunk's end (d_v x d_k per chunk
  * each, in the dtype of q, chunks of 32 tokens, or 16 for GDR_F32 or
  * C == 16) and the recomputed outputs.
@@ -188,13 +187,15 @@ size_t gdr_bwd_chunked_workspace_size(int B, int H, int L, int d_k, int d_v, int
  * its gated descendants", "Chunkwise Parallel Form" and "Gated DeltaNet").
  *
  *   B, H, L, d_k, d_v, C, dtype, q, k, v, beta, S0   as for gdr_fwd_chunked
- *   alpha_mode GDR_ALPHA_NONE or GDR_ALPHA_SCALAR (GDR_ALPHA_CHANNEL gives
- *              GDR_ERR_UNSUPPORTED); log_alpha as for gdr_fwd_chunked
+ *   alpha_mode, log_alpha   as for gdr_fwd_chunked (channel alpha: the
+ *              floor of log alpha at -10 that the forward applies passes no
+ *              gradient, so dlog_alpha is 0 where log alpha < -10)
  *   dO         [B][H][L][d_v] (dtype)
  *   dS_final   NULL (zero) or [B][H][d_v][d_k] float
  *   dq, dk     [B][H][L][d_k] (dtype);  dv [B][H][L][d_v] (dtype)
  *   dbeta      [B][H][L] float
- *   dlog_alpha NULL for GDR_ALPHA_NONE, else [B][H][L] float
+ *   dlog_alpha NULL for GDR_ALPHA_NONE, else the shape of log_alpha:
+ *              [B][H][L] (scalar) or [B][H][L][d_k] (channel) float
  *   dS0        NULL (not written) or [B][H][d_v][d_k] float
  *   workspace  at least gdr_bwd_chunked_workspace_size(...) bytes
  * Outputs must not overlap any input, each other or the workspace.  Errors

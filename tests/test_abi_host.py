@@ -258,7 +258,10 @@ def test_backward_workspace_size_query():
     rec = 64 * nc * (2048 + 2048 + 512)
     st = 64 * nc * 128 * 128 * 2
     assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 1) == rec + 2 * st + 64 * 2048 * 128 * 2
-    assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 2) == SIZE_MAX      # channel gates
+    # channel gates: the record adds exp(G_C) per key channel and the three
+    # decayed [32][d_k] operands
+    rec_ch = 64 * nc * (2048 + 2048 + 128 * 4 + 3 * 32 * 128 * 2)
+    assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 2) == rec_ch + 2 * st + 64 * 2048 * 128 * 2
     assert ws(1, 2, 0, 64, 64, 64, gdr.GDR_F32, 1) == 0
 
 
@@ -275,8 +278,11 @@ def bwd(lib, B=1, H=1, L=64, dk=64, dv=64, C=64, dtype=1, mode=1, la=LA, ws_byte
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(mode=2), gdr.GDR_ERR_UNSUPPORTED),
     (dict(dk=96), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(mode=3), gdr.GDR_ERR_INVALID_ARG),
+    # channel gates: log alpha and its gradient span L x d_k floats
+    (dict(mode=2, dla=LA + 1024), gdr.GDR_ERR_INVALID_ARG),
+    (dict(mode=2, dq=LA + 4 * 64 * 64 - 16), gdr.GDR_ERR_INVALID_ARG),
     (dict(dO=None), gdr.GDR_ERR_INVALID_ARG),
     (dict(dq=None), gdr.GDR_ERR_INVALID_ARG),
     (dict(dla=None), gdr.GDR_ERR_INVALID_ARG),                  # scalar gates need dlog_alpha

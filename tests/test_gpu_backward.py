@@ -14,7 +14,7 @@ from gpu_common import TOL, rel_err
 
 pytestmark = pytest.mark.gpu
 
-MODES = [gi.ALPHA_NONE, gi.ALPHA_SCALAR]
+MODES = [gi.ALPHA_NONE, gi.ALPHA_SCALAR, gi.ALPHA_CHANNEL]
 DTYPES = [torch.float32, torch.bfloat16]
 NAMES = ("dq", "dk", "dv", "dbeta", "dlog_alpha", "dS0")
 
@@ -71,9 +71,30 @@ def test_backward_lengths_and_zero_state(L):
 
 
 @pytest.mark.parametrize("C", [16, 32])
-def test_backward_chunk_sizes(C):
-    x = grads_inputs(1, 2, 150, 128, 128, torch.bfloat16, gi.ALPHA_SCALAR, seed=6200 + C)
+@pytest.mark.parametrize("mode", [gi.ALPHA_SCALAR, gi.ALPHA_CHANNEL], ids=lambda m: gi.MODE_NAMES[m])
+def test_backward_chunk_sizes(C, mode):
+    x = grads_inputs(1, 2, 150, 128, 128, torch.bfloat16, mode, seed=6200 + C + mode)
     check(run_bwd(x, C), oracle_bwd(x), 2e-2)
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=lambda d: str(d)[6:])
+def test_backward_channel_strong_decay(dt):
+    """Channel gates near and past the floor of log alpha at -10: decays of
+    e^-80 inside one 8-token span of a chunk, the reference-row scaling at its
+    widest; below the floor the gradient of log alpha is zero."""
+    x = grads_inputs(1, 2, 96, 128, 128, dt, gi.ALPHA_CHANNEL, seed=6250)
+    g = torch.Generator().manual_seed(6251)
+    la = -torch.rand(1, 2, 96, 128, generator=g) * 9.5          # in (-9.5, 0]
+    la[..., ::7, :] = -9.9                                      # near the floor
+    la[..., 5::11, 3::5] = -12.0                                # below it
+    x["log_alpha"] = la.contiguous()
+    gpu = run_bwd(x)
+    floored = x["log_alpha"] < -10.0
+    assert np.all(gpu["dlog_alpha"][floored.numpy()] == 0.0)
+    ref_x = dict(x, log_alpha=torch.clamp(x["log_alpha"], min=-10.0))
+    ref = oracle_bwd(ref_x)
+    ref["dlog_alpha"] = np.where(floored.numpy(), 0.0, ref["dlog_alpha"])
+    check(gpu, ref, TOL[dt])
 
 
 def test_backward_empty_sequence():
@@ -95,6 +116,19 @@ def test_backward_full_size_sampled():
     x = grads_inputs(8, 8, 2048, 128, 128, torch.bfloat16, gi.ALPHA_SCALAR, seed=6500)
     g = run_bwd(x)
     heads = [(0, 0), (5, 3)]
+    sel = lambda t: None if t is None else torch.stack([t[b, h] for b, h in heads])[None]
+    r = oracle.backward(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["beta"]), sel(x["log_alpha"]),
+                        sel(x["S0"]), sel(x["dO"]), sel(x["dS_final"]))
+    gs = {k: (None if v is None else np.stack([v[b, h] for b, h in heads])[None]) for k, v in g.items()}
+    check(gs, r, 2e-2)
+
+
+def test_backward_full_size_sampled_channel():
+    """The channel-gate shape (B4 H16 L4096 d128, bf16): the oracle checks
+    two (b, h) chains."""
+    x = grads_inputs(4, 16, 4096, 128, 128, torch.bfloat16, gi.ALPHA_CHANNEL, seed=6600)
+    g = run_bwd(x)
+    heads = [(0, 0), (3, 11)]
     sel = lambda t: None if t is None else torch.stack([t[b, h] for b, h in heads])[None]
     r = oracle.backward(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["beta"]), sel(x["log_alpha"]),
                         sel(x["S0"]), sel(x["dO"]), sel(x["dS_final"]))
