@@ -57,6 +57,18 @@ __device__ __forceinline__ void pack_frag<float>(Frag<float>& f, const float* x)
     f.hi = f32x4{x[4], x[5], x[6], x[7]};
 }
 
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): two bf16 operands
+// that carry about 16 bits of x.
+__device__ __forceinline__ void split_frag(const float* x, Frag<bf16>& hi, Frag<bf16>& lo) {
+    float h[8], r[8];
+    const u32x4 hv = Pack<bf16>::pack(x);
+    Pack<bf16>::unpack(hv, h);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = x[j] - h[j];
+    hi.v = __builtin_bit_cast(bf16x8, hv);
+    lo.v = __builtin_bit_cast(bf16x8, Pack<bf16>::pack(r));
+}
+
 // 8 consecutive elements of a row as floats (16-byte aligned reads), zero
 // when they lie at or past K.
 __device__ __forceinline__ void load8f(const bf16* p, float* x) { Pack<bf16>::unpack(ld16(p), x); }
@@ -66,11 +78,21 @@ __device__ __forceinline__ void load8f(const float* p, float* x) {
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
+// A value the compiler cannot see through.  A persistent kernel derives its
+// lane index from it once per chunk and passes that lane to the fragment
+// loads, so that the address arithmetic built on it is not hoisted out of
+// the chunk loop (which would hold every such address in a register
+// throughout).
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // Operand fragment of a row-major [rows][ld] array (contraction index
 // contiguous): lane reads row row0 + l % 16, k = k0 + 8 (l / 16) .. + 7.
 template <typename E, typename T>
-__device__ __forceinline__ Frag<E> cfrag(const T* base, int ld, int row0, int k0, int K) {
-    const int l = lane_id(), k = k0 + 8 * (l >> 4);
+__device__ __forceinline__ Frag<E> cfrag(const T* base, int ld, int row0, int k0, int K, int l = lane_id()) {
+    const int k = k0 + 8 * (l >> 4);
     const T* p = base + (row0 + (l & 15)) * ld + k;
     Frag<E> f;
     if constexpr (sizeof(E) == 2 && sizeof(T) == 2) {
@@ -89,21 +111,9 @@ __device__ __forceinline__ Frag<E> cfrag(const T* base, int ld, int row0, int k0
 // acc[e] = (A B^T)[m0 + 4 g + e][n0 + c].
 template <typename E, typename TA, typename TB>
 __device__ __forceinline__ void tmma(f32x4& acc, const TA* A, int lda, int m0, const TB* B, int ldb, int n0,
-                                     int K)
+                                     int K, int l = lane_id())
 {
-    for (int k0 = 0; k0 < K; k0 += 32) mma(acc, cfrag<E>(A, lda, m0, k0, K), cfrag<E>(B, ldb, n0, k0, K));
-}
-
-// acc += A B^T on one 16 x 16 tile with a 16-wide contraction in fp32
-// (A rows m0.. of [.][lda], B rows n0.. of [.][ldb], k = 0..15): lane group
-// g supplies k = 4 g + j to the j-th of four 16x16x4 products.
-template <typename TA>
-__device__ __forceinline__ void tmma16f(f32x4& acc, const TA* A, int lda, int m0, const float* B, int ldb, int n0)
-{
-    const int l = lane_id(), k = 4 * (l >> 4);
-    const f32x4 a = load4f(A + (m0 + (l & 15)) * lda + k), b = load4f(B + (n0 + (l & 15)) * ldb + k);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], acc, 0, 0, 0);
+    for (int k0 = 0; k0 < K; k0 += 32) mma(acc, cfrag<E>(A, lda, m0, k0, K, l), cfrag<E>(B, ldb, n0, k0, K, l));
 }
 
 // Sum of x over the 16 lanes that share l / 16 (one tile row).
@@ -843,7 +853,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
 // decay inside run per pair of 16-token tiles through a reference row m of
 // the pair (the forward's scheme): e^{G_r - G_i} = e^{G_r - G_m} e^{G_m - G_i}
 // with both factors at most 1 off the diagonal and at most e^80 on it.
-constexpr int kBVC = 16;   // value channels per block (channel alpha)
+constexpr int kBVC = 32;   // value channels per block (channel alpha)
 
 template <typename E, int DK, int CK>
 struct GradChLds : Strides<E, DK, CK> {
@@ -867,9 +877,10 @@ struct GradChLds : Strides<E, DK, CK> {
     static constexpr int off_Tt = off_Tft + FCC;               // [CK][LCK] E
     static constexpr int off_Ttt = off_Tt + ECC;
     static constexpr int off_Pt = off_Ttt + ECC;
-    static constexpr int off_vec = off_Pt + ECC;               // beta [CK], <dS, S0> per channel [DK], red [16]
-    static constexpr int NVEC = CK + DK + 16;
-    static constexpr int off_blk = (off_vec + NVEC * 4 + 15) / 16 * 16;
+    static constexpr int off_vec = off_Pt + ECC;               // beta [CK], <dS, S0> per channel [DK]
+    static constexpr int NVEC = CK + DK;
+    static constexpr int off_fl = off_vec + NVEC * 4;          // [CK][DK] bytes: log alpha below the floor
+    static constexpr int off_blk = (off_fl + CK * DK + 15) / 16 * 16;
     // one block of kBVC value channels
     static constexpr int off_S0 = off_blk;                     // [kBVC][LDK] E and [DK][LB]
     static constexpr int off_dS = off_S0 + kBVC * S::LDK * ES;
@@ -884,8 +895,7 @@ struct GradChLds : Strides<E, DK, CK> {
     static constexpr int off_Rt = off_dOt + kBVC * S::LCK * ES;
     static constexpr int off_dUt = off_Rt + kBVC * S::LCK * ES;
     static constexpr int off_V = off_dUt + kBVC * S::LCK * ES; // [CK][LBF] f32
-    static constexpr int off_KdS = off_V + CK * LBF * 4;
-    static constexpr int blk_end = off_KdS + CK * LBF * 4;
+    static constexpr int blk_end = off_V + CK * LBF * 4;
     // last phases, over the block region
     static constexpr int off_dTt = off_blk;                    // [CK][LF] f32 (triangular part)
     static constexpr int off_dTb = off_dTt + FCC;
@@ -895,11 +905,7 @@ struct GradChLds : Strides<E, DK, CK> {
     static constexpr int off_dPMt = off_dPM + ECC;
     static constexpr int off_dAb = off_dPMt + ECC;
     static constexpr int off_dAbt = off_dAb + ECC;
-    static constexpr int LS = 16 + 4;                          // fp32 rows of 16
-    static constexpr int off_Sk = off_dAbt + ECC;              // [DK][LS] f32 per tile pair
-    static constexpr int off_Sq = off_Sk + DK * LS * 4;
-    static constexpr int off_Sk2 = off_Sq + DK * LS * 4;
-    static constexpr int pair_end = off_Sk2 + DK * LS * 4;
+    static constexpr int pair_end = off_dAbt + ECC;
     static constexpr int off_dGm = off_blk;                    // [CK][LG] f32 (after the pairs)
     static constexpr int off_Y3Kd = off_dGm + CK * LG * 4;
     static constexpr int last_end = off_Y3Kd + CK * LG * 4;
@@ -913,11 +919,11 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
     using LY = GradChLds<E, DK, CK>;
     constexpr int NB = CK / 16, NJ = DK / 16, VE = Vec<E>::n;
     constexpr int LF = LY::LF, LDK = LY::LDK, LCK = LY::LCK, LB = LY::LB, LG = LY::LG, LBF = LY::LBF;
-    constexpr int LS = LY::LS;
     constexpr int NT = 512, NW = NT / kWave;
     constexpr int NQT = NB * NJ, NQW = (NQT + NW - 1) / NW;
-    constexpr int NCC = NB * NB, NPAIR = NB * (NB + 1) / 2;
+    constexpr int NCC = NB * NB, NPAIR = NB * (NB + 1) / 2, NKS = DK / 32;
     constexpr WsLayout WL = ws_layout((int)sizeof(E), DK, CK, kAlphaChannel);
+    static_assert(NKS % 2 == 0 && 64 * NPAIR * 4 * 4 <= LY::FCC, "Bm halves");
     extern __shared__ __align__(16) unsigned char smem[];
 #define GL_E(name, off) E* name = reinterpret_cast<E*>(smem + LY::off)
 #define GL_F(name, off) float* name = reinterpret_cast<float*>(smem + LY::off)
@@ -926,30 +932,33 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
     GL_E(Tt, off_Tt); GL_E(Ttt, off_Ttt); GL_E(Pt, off_Pt);
     GL_E(S0s, off_S0); GL_E(dSs, off_dS); GL_E(S0t, off_S0t); GL_E(dSt, off_dSt);
     GL_E(dOs, off_dO); GL_E(Rs, off_R); GL_E(Us, off_U); GL_E(dUs, off_dU); GL_E(dXs, off_dX);
-    GL_E(dOt, off_dOt); GL_E(Rt, off_Rt); GL_E(dUt, off_dUt); GL_F(Vs, off_V); GL_F(KdSs, off_KdS);
+    GL_E(dOt, off_dOt); GL_E(Rt, off_Rt); GL_E(dUt, off_dUt); GL_F(Vs, off_V);
     GL_F(dTt, off_dTt); GL_F(dTb, off_dTb); GL_F(Y1t, off_Y1t); GL_F(dAf, off_dA);
     GL_E(dPM, off_dPM); GL_E(dPMt, off_dPMt); GL_E(dAb, off_dAb); GL_E(dAbt, off_dAbt);
-    GL_F(Sk, off_Sk); GL_F(Sq, off_Sq); GL_F(Sk2, off_Sk2); GL_F(dGm, off_dGm); GL_F(Y3Kd, off_Y3Kd);
+    GL_F(dGm, off_dGm); GL_F(Y3Kd, off_Y3Kd);
 #undef GL_E
 #undef GL_F
     float* bs = reinterpret_cast<float*>(smem + LY::off_vec);
-    float* hC = bs + CK;         // <dS_end, S0> per key channel
-    const int cid = blockIdx.x;
-    const int tid = threadIdx.x, w = wave_id(), l = lane_id(), g4 = l >> 4, c16 = l & 15;
-    const int bh = cid / p.NC, n = cid % p.NC;
-    const int t0 = n * CK, valid = min(CK, p.L - t0);
-    const size_t tok = (size_t)bh * p.L + t0;
-    const unsigned char* rec = p.ws + (size_t)cid * WL.bytes;
+    float* hC = bs + CK;                     // <dS_end, S0> per key channel
+    unsigned char* fl = smem + LY::off_fl;   // 1 where log alpha is below the floor
 
-    // ---- keys, queries, the forward's decayed keys, log alpha, beta
-    {
-        RowStage<E, CK, DK, NT> ks, qs, kg, kd;
+    // Each workgroup walks chunks blockIdx.x, + gridDim.x, ...; the next
+    // chunk's keys, queries, records, gates and first value block are read
+    // into registers while the current chunk is worked on.
+    constexpr int NLV = (CK * DK / 4 + NT - 1) / NT;
+    constexpr int NPV = CK * CK / VE;
+    RowStage<E, CK, DK, NT> ks, qs, kg, kd;
+    f32x4 lv[NLV];
+    u32x4 pv;
+    float bv;
+    auto fetch_chunk = [&](int c, int tid) {
+        const int n = c % p.NC, valid = min(CK, p.L - n * CK);
+        const size_t tok = (size_t)(c / p.NC) * p.L + (size_t)n * CK;
+        const unsigned char* rec = p.ws + (size_t)c * WL.bytes;
         ks.load(reinterpret_cast<const E*>(p.k) + tok * DK, DK, valid, tid);
         qs.load(reinterpret_cast<const E*>(p.q) + tok * DK, DK, valid, tid);
         kg.load(reinterpret_cast<const E*>(rec + WL.KG), DK, CK, tid);
         kd.load(reinterpret_cast<const E*>(rec + WL.KD), DK, CK, tid);
-        constexpr int NLV = (CK * DK / 4 + NT - 1) / NT;
-        f32x4 lv[NLV];
 #pragma unroll
         for (int j = 0; j < NLV; ++j) {
             const int x = tid + NT * j, r = (4 * x) / DK;
@@ -957,60 +966,132 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
             if (x < CK * DK / 4 && r < valid)
                 lv[j] = *reinterpret_cast<const f32x4*>(p.log_alpha + (tok + r) * DK + (4 * x) % DK);
         }
-        ks.store_plain(Ks, LDK, tid);
-        qs.store_plain(Qs, LDK, tid);
-        kg.store_plain(Kgs, LDK, tid);
-        kd.store_plain(Kds, LDK, tid);
+        pv = tid < NPV ? ld16(rec + WL.M + 16 * tid) : u32x4{0u, 0u, 0u, 0u};
+        bv = tid < valid ? p.beta[tok + tid] : 0.f;
+    };
+    // Thread x stages the 16-byte vector (value row x % kBVC, key channels
+    // VE (x / kBVC) ..) of S0 and dS_end; its key channels are the same in
+    // every block, so it also sums their products for <dS_end, S0>.
+    constexpr int NSV = (kBVC * DK / VE + NT - 1) / NT;
+    constexpr int PERV = kBVC / VE, NVV = (CK * PERV + NT - 1) / NT;
+    constexpr int NCB = NB * (kBVC / 16);   // C x kBVC tiles (<= 4)
+    u32x4 sa[NSV], sb[NSV], va[NVV], da[NVV];
+    auto fetch_block = [&](int c, int v0, int tid) {
+        const int n = c % p.NC, valid = min(CK, p.L - n * CK);
+        const size_t tok = (size_t)(c / p.NC) * p.L + (size_t)n * CK;
+        const E* S0g = static_cast<const E*>(p.Sck) + (size_t)c * p.DV * DK;
+        const E* dSg = static_cast<const E*>(p.dSck) + (size_t)c * p.DV * DK;
+        const E* vg = reinterpret_cast<const E*>(p.v) + tok * p.DV;
+        const E* dog = reinterpret_cast<const E*>(p.dO) + tok * p.DV;
 #pragma unroll
-        for (int j = 0; j < NLV; ++j) {
-            const int x = tid + NT * j, r = (4 * x) / DK, c = (4 * x) % DK;
-            if (x < CK * DK / 4)
+        for (int u = 0; u < NSV; ++u) {
+            const int xs = tid + NT * u, i = xs % kBVC, j = VE * (xs / kBVC);
+            if (xs < kBVC * DK / VE) {
+                sa[u] = ld16(S0g + (size_t)(v0 + i) * DK + j);
+                sb[u] = ld16(dSg + (size_t)(v0 + i) * DK + j);
+            }
+        }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) Gs[r * LG + c + e] = r < valid ? fmaxf(lv[j][e], kChannelLogAlphaMin) : 0.f;
+        for (int u = 0; u < NVV; ++u) {
+            const int x = tid + NT * u, r = x % CK, cc = (x / CK) * VE;
+            const bool ok = x < CK * PERV && r < valid;
+            va[u] = ok ? ld16(vg + (size_t)r * p.DV + v0 + cc) : u32x4{0u, 0u, 0u, 0u};
+            da[u] = ok ? ld16(dog + (size_t)r * p.DV + v0 + cc) : u32x4{0u, 0u, 0u, 0u};
         }
-        if (tid < CK) bs[tid] = tid < valid ? p.beta[tok + tid] : 0.f;
-        if (tid < DK) hC[tid] = 0.f;
-        // the score block P (masked, from the forward's record), transposed
-        for (int x = tid; x < CK * CK; x += NT) {
-            const int r = x / CK, t = tok_of_col(CK, x % CK);
-            Pt[t * LCK + r] = reinterpret_cast<const E*>(rec + WL.M)[x];
-        }
+    };
+    if ((int)blockIdx.x < p.total) {
+        fetch_chunk(blockIdx.x, threadIdx.x);
+        fetch_block(blockIdx.x, 0, threadIdx.x);
     }
+    for (int cid = blockIdx.x; cid < p.total; cid += gridDim.x) {
+    // lane-dependent values are re-derived per chunk (see vlane)
+    const int tid = opaque(threadIdx.x), l = tid & (kWave - 1), g4 = l >> 4, c16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int nxt = cid + gridDim.x;
+    const int bh = cid / p.NC, n = cid % p.NC;
+    const int t0 = n * CK, valid = min(CK, p.L - t0);
+    const size_t tok = (size_t)bh * p.L + t0;
+
+    // ---- keys, queries, the forward's decayed keys, log alpha (floored),
+    // beta, and the score block P (masked; columns in tok_of_col order) transposed
+    ks.store_plain(Ks, LDK, tid);
+    qs.store_plain(Qs, LDK, tid);
+    kg.store_plain(Kgs, LDK, tid);
+    kd.store_plain(Kds, LDK, tid);
+#pragma unroll
+    for (int j = 0; j < NLV; ++j) {
+        const int x = tid + NT * j, r = (4 * x) / DK, c = (4 * x) % DK;
+        if (x < CK * DK / 4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool in = r < valid;
+                Gs[r * LG + c + e] = in ? fmaxf(lv[j][e], kChannelLogAlphaMin) : 0.f;
+                fl[r * DK + c + e] = (in && lv[j][e] < kChannelLogAlphaMin) ? 1 : 0;
+            }
+    }
+    if (tid < CK) bs[tid] = bv;
+    if (tid < NPV) {
+        const int r = (VE * tid) / CK, mc0 = (VE * tid) % CK;
+        E pe[VE];
+        __builtin_memcpy(pe, &pv, 16);
+#pragma unroll
+        for (int j = 0; j < VE; ++j) Pt[tok_of_col(CK, mc0 + j) * LCK + r] = pe[j];
+    }
+    if (nxt < p.total) fetch_chunk(nxt, tid);
     __syncthreads();
-    // cumulative sum down every key channel
+    // cumulative sum down every key channel (the column is read whole first)
     if (tid < DK) {
-        float g = 0.f;
-        for (int r = 0; r < CK; ++r) {
-            g += Gs[r * LG + tid];
-            Gs[r * LG + tid] = g;
-        }
+        float col[CK];
+#pragma unroll
+        for (int r = 0; r < CK; ++r) col[r] = Gs[r * LG + tid];
+#pragma unroll
+        for (int r = 1; r < CK; ++r) col[r] += col[r - 1];
+#pragma unroll
+        for (int r = 0; r < CK; ++r) Gs[r * LG + tid] = col[r];
     }
     __syncthreads();
     // ---- Bm = strictly-lower(K K^T with the decay inside), A = diag(beta) Bm,
-    // through the reference rows of each tile pair
-    if (w < NPAIR) {
-        const int rb = (w == 0) ? 0 : 1, ib = (w == 2) ? 1 : 0;
+    // through the reference rows of each tile pair; waves w and w + 4 take
+    // the two halves of the key channels (the second half via Tft)
+    if (w < NPAIR || (w >= 4 && w < 4 + NPAIR)) {
+        const int pw = w & 3, half = w >> 2;
+        const int rb = (pw == 0) ? 0 : 1, ib = (pw == 2) ? 1 : 0;
         const int m = (rb == ib) ? 16 * rb + 7 : 16 * rb - 1;
         const int rl = 16 * rb + c16, rr = 16 * ib + c16;
         f32x4 acc = zero4();
-        for (int c0 = 8 * g4; c0 < DK; c0 += 32) {
-            float fl[8], fr[8];
+        for (int ksx = half * (NKS / 2); ksx < (half + 1) * (NKS / 2); ++ksx) {
+            const int c0 = 32 * ksx + 8 * g4;
+            float fa[8], fb[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float gm = Gs[m * LG + c0 + j];
-                fl[j] = __expf(Gs[rl * LG + c0 + j] - gm);
-                fr[j] = __expf(gm - Gs[rr * LG + c0 + j]);
+                fa[j] = __expf(Gs[rl * LG + c0 + j] - gm);
+                fb[j] = __expf(gm - Gs[rr * LG + c0 + j]);
             }
             Frag<E> kl, kr;
-            load_scaled_frag(kl, Ks + rl * LDK + c0, fl);
-            load_scaled_frag(kr, Ks + rr * LDK + c0, fr);
+            load_scaled_frag(kl, Ks + rl * LDK + c0, fa);
+            load_scaled_frag(kr, Ks + rr * LDK + c0, fb);
             mma(acc, kl, kr);
         }
+        if (half) *reinterpret_cast<f32x4*>(Tft + 4 * (64 * pw + l)) = acc;
+        else {
+            // kept for after the barrier
+            Bm[(16 * rb + 4 * g4) * LF + 16 * ib + c16] = acc[0];
+            Bm[(16 * rb + 4 * g4 + 1) * LF + 16 * ib + c16] = acc[1];
+            Bm[(16 * rb + 4 * g4 + 2) * LF + 16 * ib + c16] = acc[2];
+            Bm[(16 * rb + 4 * g4 + 3) * LF + 16 * ib + c16] = acc[3];
+        }
+    }
+    __syncthreads();
+    if (w < NPAIR) {
+        const int rb = (w == 0) ? 0 : 1, ib = (w == 2) ? 1 : 0;
+        const f32x4 other = *reinterpret_cast<const f32x4*>(Tft + 4 * (64 * w + l));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * rb + 4 * g4 + e, i = 16 * ib + c16;
-            Bm[r * LF + i] = r > i ? acc[e] : 0.f;
-            Af[r * LF + i] = r > i ? bs[r] * acc[e] : 0.f;
+            const float b = Bm[r * LF + i] + other[e];
+            Bm[r * LF + i] = r > i ? b : 0.f;
+            Af[r * LF + i] = r > i ? bs[r] * b : 0.f;
         }
     }
     if constexpr (NB == 2) {
@@ -1040,31 +1121,13 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
 #pragma unroll
     for (int u = 0; u < NQW; ++u) { Y1[u] = zero4(); Y2[u] = zero4(); Y3[u] = zero4(); }
     f32x4 dPa = zero4(), dTa = zero4();   // C x C tile w (w < NCC)
-
-    const E* S0g = static_cast<const E*>(p.Sck) + (size_t)cid * p.DV * DK;
-    const E* dSg = static_cast<const E*>(p.dSck) + (size_t)cid * p.DV * DK;
-    const E* vg = reinterpret_cast<const E*>(p.v) + tok * p.DV;
-    const E* dog = reinterpret_cast<const E*>(p.dO) + tok * p.DV;
-    constexpr int NSV = (kBVC * DK / VE + NT - 1) / NT;
-    constexpr int PERV = kBVC / VE;
-    u32x4 sa[NSV], sb[NSV], va, da;
-    auto fetch = [&](int v0) {
+    float hacc[NSV][VE];
 #pragma unroll
-        for (int u = 0; u < NSV; ++u) {
-            const int xs = tid + NT * u, i = xs % kBVC, j = VE * (xs / kBVC);
-            if (xs < kBVC * DK / VE) {
-                sa[u] = ld16(S0g + (size_t)(v0 + i) * DK + j);
-                sb[u] = ld16(dSg + (size_t)(v0 + i) * DK + j);
-            }
-        }
-        const int r = tid % CK, c = (tid / CK) * VE;
-        const bool ok = tid < CK * PERV && r < valid;
-        va = ok ? ld16(vg + (size_t)r * p.DV + v0 + c) : u32x4{0u, 0u, 0u, 0u};
-        da = ok ? ld16(dog + (size_t)r * p.DV + v0 + c) : u32x4{0u, 0u, 0u, 0u};
-    };
-    fetch(0);
+    for (int u = 0; u < NSV; ++u)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) hacc[u][e] = 0.f;
     for (int v0 = 0; v0 < p.DV; v0 += kBVC) {
-        __syncthreads();
+        __syncthreads();   // the previous block's operands are consumed
 #pragma unroll
         for (int u = 0; u < NSV; ++u) {
             const int xs = tid + NT * u, i = xs % kBVC, j = VE * (xs / kBVC);
@@ -1078,80 +1141,70 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
             for (int e = 0; e < VE; ++e) {
                 S0t[(j + e) * LB + i] = a[e];
                 dSt[(j + e) * LB + i] = b[e];
+                hacc[u][e] += to_f32(a[e]) * to_f32(b[e]);
             }
         }
-        if (tid < CK * PERV) {
-            const int r = tid % CK, c = (tid / CK) * VE;
-            float a[VE], d[VE];
-            Pack<E>::unpack(va, a);
-            Pack<E>::unpack(da, d);
 #pragma unroll
-            for (int j = 0; j < VE; ++j) {
-                Vs[r * LBF + c + j] = a[j];
-                dOs[r * LB + c + j] = from_f32<E>(d[j]);
-                dOt[(c + j) * LCK + r] = from_f32<E>(d[j]);
+        for (int u = 0; u < NVV; ++u) {
+            const int x = tid + NT * u, r = x % CK, c = (x / CK) * VE;
+            if (x < CK * PERV) {
+                float a[VE];
+                E d[VE];
+                Pack<E>::unpack(va[u], a);
+                __builtin_memcpy(d, &da[u], 16);
+#pragma unroll
+                for (int j = 0; j < VE; ++j) {
+                    Vs[r * LBF + c + j] = a[j];
+                    dOs[r * LB + c + j] = d[j];
+                    dOt[(c + j) * LCK + r] = d[j];
+                }
             }
         }
-        if (v0 + kBVC < p.DV) fetch(v0 + kBVC);
+        if (v0 + kBVC < p.DV) fetch_block(cid, v0 + kBVC, tid);
+        else if (nxt < p.total) fetch_block(nxt, 0, tid);
         __syncthreads();
-        // ---- X = Kg S0^T, R = V - X (waves 0..NB-1); Kd dS^T (waves 4..); <dS, S0> per channel
-        if (w < NB) {
-            const int rb = w;
+        // ---- R = V - Kg S0^T (waves 0..NCB-1); dU = P^T dO + Kd dS^T (waves 4..)
+        if (w < NCB) {
+            const int rb = w / 2, cb = w % 2;
             f32x4 x = zero4();
-            tmma<E>(x, Kgs, LDK, 16 * rb, S0s, LDK, 0, DK);
+            tmma<E>(x, Kgs, LDK, 16 * rb, S0s, LDK, 16 * cb, DK, l);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * g4 + e, i = c16;
+                const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
                 const float rr = Vs[r * LBF + i] - x[e];
                 Rs[r * LB + i] = from_f32<E>(rr);
                 Rt[i * LCK + r] = from_f32<E>(rr);
             }
-        } else if (w >= 4 && w < 4 + NB) {
-            const int rb = w - 4;
-            f32x4 kds = zero4();
-            tmma<E>(kds, Kds, LDK, 16 * rb, dSs, LDK, 0, DK);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) KdSs[(16 * rb + 4 * g4 + e) * LBF + c16] = kds[e];
-        } else if (w == 2 || w == 3) {
-            for (int c = tid - 128; c < DK; c += 128) {
-                float h = 0.f;
-#pragma unroll
-                for (int i = 0; i < kBVC; ++i) h += to_f32(S0s[i * LDK + c]) * to_f32(dSs[i * LDK + c]);
-                hC[c] += h;
-            }
-        }
-        __syncthreads();
-        // ---- U = T~ R (waves 0..), dU = P^T dO + Kd dS^T (waves 4..)
-        if (w < NB) {
-            const int rb = w;
-            f32x4 u = zero4();
-            tmma<E>(u, Tt, LCK, 16 * rb, Rt, LCK, 0, CK);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Us[(16 * rb + 4 * g4 + e) * LB + c16] = from_f32<E>(u[e]);
-        } else if (w >= 4 && w < 4 + NB) {
-            const int rb = w - 4;
+        } else if (w >= 4 && w < 4 + NCB) {
+            const int rb = (w - 4) / 2, cb = (w - 4) % 2;
             f32x4 du = zero4();
-            tmma<E>(du, Pt, LCK, 16 * rb, dOt, LCK, 0, CK);
+            tmma<E>(du, Kds, LDK, 16 * rb, dSs, LDK, 16 * cb, DK, l);
+            tmma<E>(du, Pt, LCK, 16 * rb, dOt + 16 * cb * LCK, LCK, 0, CK, l);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * g4 + e;
-                const float dd = du[e] + KdSs[r * LBF + c16];
-                dUs[r * LB + c16] = from_f32<E>(dd);
-                dUt[c16 * LCK + r] = from_f32<E>(dd);
+                const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
+                dUs[r * LB + i] = from_f32<E>(du[e]);
+                dUt[i * LCK + r] = from_f32<E>(du[e]);
             }
         }
         __syncthreads();
-        // ---- dR = T~^T dU (= dV), dX = -dR
-        if (w < NB) {
-            const int rb = w;
+        // ---- U = T~ R (waves 0..); dR = T~^T dU (= dV), dX = -dR (waves 4..)
+        if (w < NCB) {
+            const int rb = w / 2, cb = w % 2;
+            f32x4 u = zero4();
+            tmma<E>(u, Tt, LCK, 16 * rb, Rt + 16 * cb * LCK, LCK, 0, CK, l);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Us[(16 * rb + 4 * g4 + e) * LB + 16 * cb + c16] = from_f32<E>(u[e]);
+        } else if (w >= 4 && w < 4 + NCB) {
+            const int rb = (w - 4) / 2, cb = (w - 4) % 2;
             f32x4 dr = zero4();
-            tmma<E>(dr, Ttt, LCK, 16 * rb, dUt, LCK, 0, CK);
+            tmma<E>(dr, Ttt, LCK, 16 * rb, dUt + 16 * cb * LCK, LCK, 0, CK, l);
             E* dvg = reinterpret_cast<E*>(p.dv) + tok * p.DV + v0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * g4 + e;
-                if (r < valid) dvg[(size_t)r * p.DV + c16] = from_f32<E>(dr[e]);
-                dXs[r * LB + c16] = from_f32<E>(-dr[e]);
+                const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
+                if (r < valid) dvg[(size_t)r * p.DV + i] = from_f32<E>(dr[e]);
+                dXs[r * LB + i] = from_f32<E>(-dr[e]);
             }
         }
         __syncthreads();
@@ -1161,19 +1214,34 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
             const int t = w + NW * u;
             if (t < NQT) {
                 const int rb = t / NJ, jb = t % NJ;
-                tmma<E>(Y1[u], dOs, LB, 16 * rb, S0t, LB, 16 * jb, kBVC);
-                tmma<E>(Y2[u], dXs, LB, 16 * rb, S0t, LB, 16 * jb, kBVC);
-                tmma<E>(Y3[u], Us, LB, 16 * rb, dSt, LB, 16 * jb, kBVC);
+                tmma<E>(Y1[u], dOs, LB, 16 * rb, S0t, LB, 16 * jb, kBVC, l);
+                tmma<E>(Y2[u], dXs, LB, 16 * rb, S0t, LB, 16 * jb, kBVC, l);
+                tmma<E>(Y3[u], Us, LB, 16 * rb, dSt, LB, 16 * jb, kBVC, l);
             }
         }
         if (w < NCC) {
             const int rb = w / NB, sb = w % NB;
-            tmma<E>(dPa, dOs, LB, 16 * rb, Us, LB, 16 * sb, kBVC);
-            tmma<E>(dTa, dUs, LB, 16 * rb, Rs, LB, 16 * sb, kBVC);
+            tmma<E>(dPa, dOs, LB, 16 * rb, Us, LB, 16 * sb, kBVC, l);
+            tmma<E>(dTa, dUs, LB, 16 * rb, Rs, LB, 16 * sb, kBVC, l);
         }
     }
+    // <dS_end, S0> per key channel: the kBVC threads that staged the same
+    // key channels are the 32 lanes of one half wave (all sums reduced side
+    // by side)
+#pragma unroll
+    for (int m = kBVC / 2; m >= 1; m >>= 1)
+#pragma unroll
+        for (int u = 0; u < NSV; ++u)
+#pragma unroll
+            for (int e = 0; e < VE; ++e) hacc[u][e] += __shfl_xor(hacc[u][e], m, kWave);
+#pragma unroll
+    for (int u = 0; u < NSV; ++u) {
+        const int xs = tid + NT * u, j = VE * (xs / kBVC);
+        if (xs % kBVC == 0 && xs < kBVC * DK / VE)
+#pragma unroll
+            for (int e = 0; e < VE; ++e) hC[j + e] = hacc[u][e];
+    }
     __syncthreads();   // the block region is reused below
-
     // ---- triangular part: dPM, dT~; dA = strictly-lower(-T^T dT~ diag(beta) T^T)
     if (w < NCC) {
         const int rb = w / NB, sb = w % NB;
@@ -1191,7 +1259,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
     if (w < NCC) {
         const int rb = w / NB, sb = w % NB;
         f32x4 y = zero4();
-        tmma<float>(y, dTb, LF, 16 * rb, Tf, LF, 16 * sb, CK);
+        tmma<float>(y, dTb, LF, 16 * rb, Tf, LF, 16 * sb, CK, l);
 #pragma unroll
         for (int e = 0; e < 4; ++e) Y1t[(16 * sb + c16) * LF + 16 * rb + 4 * g4 + e] = y[e];
     }
@@ -1199,7 +1267,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
     if (w < NCC) {
         const int rb = w / NB, sb = w % NB;
         f32x4 y = zero4();
-        tmma<float>(y, Tft, LF, 16 * rb, Y1t, LF, 16 * sb, CK);
+        tmma<float>(y, Tft, LF, 16 * rb, Y1t, LF, 16 * sb, CK, l);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * rb + 4 * g4 + e, s2 = 16 * sb + c16;
@@ -1217,58 +1285,68 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
         p.dbeta[tok + l] = db;
     }
 
-    // ---- the four sums with the decay inside, one tile pair at a time
+    // ---- the four sums with the decay inside the channel sum.  Output tile
+    // ob (rows 16 ob ..) takes its reference row m = 16 ob + 7:
+    // e^{G_r - G_i} = e^{G_r - G_m} e^{G_m - G_i}, neither factor above e^{80};
+    // a factor that underflows belongs to a term below e^{-17} of the scale
+    // (decays of at least e^{-10} per token).  The products keep fp32
+    // accuracy: their terms of dG cancel in pairs in the suffix sums of
+    // d log alpha, which bf16 operands would leave at a few percent of the
+    // result.  For bf16 the fp32 operand is split into two bf16 parts
+    // (hi + lo, about 16 bits) against the bf16 dPM and dAb.
     f32x4 QP[NQW], KP[NQW], KM[NQW];   // dQ_P, dK_A1, dK_P2 + dK_A2
 #pragma unroll
-    for (int u = 0; u < NQW; ++u) { QP[u] = zero4(); KP[u] = zero4(); KM[u] = zero4(); }
-    for (int pr = 0; pr < NPAIR; ++pr) {
-        const int rb = (pr == 0) ? 0 : 1, ib = (pr == 2) ? 1 : 0;
-        const int m = (rb == ib) ? 16 * rb + 7 : 16 * rb - 1;
-        __syncthreads();   // the previous pair's operands are consumed (and dA is read)
-        // Sk[c][i] = k_ic e^{G_mc - G_ic} (i in tile ib); Sq, Sk2[c][r] = (q, k)_rc e^{G_rc - G_mc}
-        // (r in tile rb).  These products stay in fp32: the terms of dG they give
-        // cancel in pairs in the suffix sums of d log alpha, which bf16
-        // operands would leave at a few percent of the result.
-        for (int x = tid; x < 16 * DK; x += NT) {
-            const int i = x % 16, c = x / 16;
-            const float gm = Gs[m * LG + c];
-            const int ri = 16 * ib + i, rr = 16 * rb + i;
-            Sk[c * LS + i] = to_f32(Ks[ri * LDK + c]) * __expf(gm - Gs[ri * LG + c]);
-            const float fr = __expf(Gs[rr * LG + c] - gm);
-            Sq[c * LS + i] = to_f32(Qs[rr * LDK + c]) * fr;
-            Sk2[c * LS + i] = to_f32(Ks[rr * LDK + c]) * fr;
+    for (int u = 0; u < NQW; ++u) {
+        QP[u] = zero4(); KP[u] = zero4(); KM[u] = zero4();
+        const int t = w + NW * u;
+        if (t >= NQT) continue;
+        const int ob = t / NJ, c = 16 * (t % NJ) + c16, m = 16 * ob + 7;
+        const float gm = Gs[m * LG + c];
+        constexpr int KL = sizeof(E) == 2 ? 8 : 4;   // tokens per lane and MFMA
+        // tokens k = KL g4 + j: i side (k < 16 (ob + 1)) and r side (16 ob <= k < CK)
+        float sk[KL], sq[KL], sk2[KL];
+#pragma unroll
+        for (int j = 0; j < KL; ++j) {
+            const int kt = KL * g4 + j;
+            const bool in = kt < CK;
+            const float g = in ? Gs[kt * LG + c] : 0.f;
+            const float kx = in ? to_f32(Ks[kt * LDK + c]) : 0.f, qx = in ? to_f32(Qs[kt * LDK + c]) : 0.f;
+            sk[j] = (kt < 16 * (ob + 1)) ? kx * __expf(gm - g) : 0.f;
+            const float f = (kt >= 16 * ob && in) ? __expf(g - gm) : 0.f;
+            sq[j] = qx * f;
+            sk2[j] = kx * f;
         }
-        __syncthreads();
+        const int arow = 16 * ob + c16;
+        f32x4 a = zero4(), b = zero4(), km = zero4();
+        if constexpr (sizeof(E) == 2) {
+            Frag<bf16> skh, skl, sqh, sql, s2h, s2l;
+            split_frag(sk, skh, skl);
+            split_frag(sq, sqh, sql);
+            split_frag(sk2, s2h, s2l);
+            const Frag<bf16> apm = cfrag<bf16>(dPM, LCK, 16 * ob, 0, CK, l), aab = cfrag<bf16>(dAb, LCK, 16 * ob, 0, CK, l);
+            const Frag<bf16> apt = cfrag<bf16>(dPMt, LCK, 16 * ob, 0, CK, l), aat = cfrag<bf16>(dAbt, LCK, 16 * ob, 0, CK, l);
+            mma(a, apm, skh); mma(a, apm, skl);
+            mma(b, aab, skh); mma(b, aab, skl);
+            mma(km, apt, sqh); mma(km, apt, sql);
+            mma(km, aat, s2h); mma(km, aat, s2l);
+        } else {
+            const f32x4 apm = load4f(dPM + arow * LCK + 4 * g4), aab = load4f(dAb + arow * LCK + 4 * g4);
+            const f32x4 apt = load4f(dPMt + arow * LCK + 4 * g4), aat = load4f(dAbt + arow * LCK + 4 * g4);
 #pragma unroll
-        for (int u = 0; u < NQW; ++u) {
-            const int t = w + NW * u;
-            if (t < NQT) {
-                const int ob = t / NJ, jb = t % NJ;
-                if (ob == rb) {
-                    // rows r of tile rb: sum over i in tile ib, then e^{G_rc - G_mc}
-                    f32x4 a = zero4(), b = zero4();
-                    tmma16f(a, dPM + 16 * ib, LCK, 16 * rb, Sk, LS, 16 * jb);
-                    tmma16f(b, dAb + 16 * ib, LCK, 16 * rb, Sk, LS, 16 * jb);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 16 * rb + 4 * g4 + e, c = 16 * jb + c16;
-                        const float f = __expf(Gs[r * LG + c] - Gs[m * LG + c]);
-                        QP[u][e] += f * a[e];
-                        KP[u][e] += f * b[e];
-                    }
-                }
-                if (ob == ib) {
-                    // rows i of tile ib: sum over r in tile rb, then e^{G_mc - G_ic}
-                    f32x4 a = zero4();
-                    tmma16f(a, dPMt + 16 * rb, LCK, 16 * ib, Sq, LS, 16 * jb);
-                    tmma16f(a, dAbt + 16 * rb, LCK, 16 * ib, Sk2, LS, 16 * jb);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 16 * ib + 4 * g4 + e, c = 16 * jb + c16;
-                        KM[u][e] += __expf(Gs[m * LG + c] - Gs[i * LG + c]) * a[e];
-                    }
-                }
+            for (int j = 0; j < 4; ++j) {
+                a = __builtin_amdgcn_mfma_f32_16x16x4f32(apm[j], sk[j], a, 0, 0, 0);
+                b = __builtin_amdgcn_mfma_f32_16x16x4f32(aab[j], sk[j], b, 0, 0, 0);
+                km = __builtin_amdgcn_mfma_f32_16x16x4f32(apt[j], sq[j], km, 0, 0, 0);
+                km = __builtin_amdgcn_mfma_f32_16x16x4f32(aat[j], sk2[j], km, 0, 0, 0);
             }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float d = Gs[(16 * ob + 4 * g4 + e) * LG + c] - gm;
+            const float f = __expf(d), fi = __expf(-d);
+            QP[u][e] = f * a[e];
+            KP[u][e] = f * b[e];
+            KM[u][e] = fi * km[e];
         }
     }
     __syncthreads();   // the pair operands give way to dG
@@ -1302,19 +1380,28 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
     __syncthreads();
     // d log alpha: suffix sums of dG down each channel, with the g_C terms
     // entering at the chunk's last token; zero where the floor was active
+    // (the column is read whole first)
     if (tid < DK) {
         const int c = tid;
-        const float gC = Gs[(CK - 1) * LG + c];
-        float tail = __expf(gC) * hC[c];
-        for (int r = 0; r < CK; ++r) tail += Y3Kd[r * LG + c];
-        float acc = tail;
-        for (int r = CK - 1; r >= 0; --r) {
-            acc += dGm[r * LG + c];
-            if (r < valid) {
-                const float la = p.log_alpha[(tok + r) * DK + c];
-                p.dlog_alpha[(tok + r) * DK + c] = la >= kChannelLogAlphaMin ? acc : 0.f;
-            }
+        float col[CK];
+        float tail = __expf(Gs[(CK - 1) * LG + c]) * hC[c];
+#pragma unroll
+        for (int r = 0; r < CK; ++r) {
+            col[r] = dGm[r * LG + c];
+            tail += Y3Kd[r * LG + c];
         }
+        float acc = tail;
+#pragma unroll
+        for (int r = CK - 1; r >= 0; --r) {
+            acc += col[r];
+            col[r] = fl[r * DK + c] ? 0.f : acc;
+        }
+        float* dla = p.dlog_alpha + tok * DK + c;
+#pragma unroll
+        for (int r = 0; r < CK; ++r)
+            if (r < valid) dla[(size_t)r * DK] = col[r];
+    }
+    __syncthreads();   // the LDS is restaged for the next chunk
     }
 }
 
@@ -1338,7 +1425,11 @@ static hipError_t launch_bwd_t(const BwdParams& bp, int BH, bool channel, hipStr
     hipError_t err = channel ? launch_lds(chunk_bwd_chain_kernel<E, DK, CK, true>, chains, 128, CL::bytes, stream, bp)
                              : launch_lds(chunk_bwd_chain_kernel<E, DK, CK, false>, chains, 128, CL::bytes, stream, bp);
     if (err != hipSuccess) return err;
-    return channel ? launch_lds(chunk_bwd_grad_channel_kernel<E, DK, CK>, bp.total, 512, GC::bytes, stream, bp)
+    // channel alpha: persistent, one workgroup per CU (the next chunk's inputs
+    // are read while the current one is worked on)
+    return channel ? launch_lds(chunk_bwd_grad_channel_kernel<E, DK, CK>,
+                                std::min(bp.total, (160 * 1024 / GC::bytes) * compute_units()), 512, GC::bytes,
+                                stream, bp)
                    : launch_lds(chunk_bwd_grad_kernel<E, DK, CK>, bp.total, 512, GL::bytes, stream, bp);
 }
 

@@ -172,5 +172,7 @@ inline SegPlan seg_plan(int B, int H, int L, int dk, int dv, int CK, int dtype, 
 hipError_t launch_wy(const ChunkArgs& a, int CK);
 hipError_t launch_scan(const ChunkArgs& a, int CK, const SegPlan& sp);
 hipError_t launch_seg_combine(const ChunkArgs& a, int CK, const SegPlan& sp);
+// Compute units of the current device (256 if the query fails).
+int compute_units();
 
 }  // namespace gdr

@@ -520,7 +520,7 @@ __global__ __launch_bounds__(256, 3) void chunk_wy_channel_kernel(WyParams p)
 }
 
 // ------------------------------------------------------------------ host side
-static int compute_units()
+int compute_units()
 {
     static int n = 0;
     if (n == 0) {
