@@ -423,7 +423,7 @@ struct GradLds : Strides<E, DK, CK> {
     static constexpr int off_Ttt = off_Tt + ECC;
     static constexpr int off_Pt = off_Ttt + ECC;
     static constexpr int off_vec = off_Pt + ECC;               // g, gamma, D, beta, dg [CK]; parts
-    static constexpr int NVEC = 5 * CK + 12 * CK + 8;
+    static constexpr int NVEC = 5 * CK + 16 * CK + 8;
     // one block of value channels (reused by the last phase)
     static constexpr int off_blk = (off_vec + NVEC * 4 + 15) / 16 * 16;
     static constexpr int off_S0 = off_blk;                     // [kBV][LDK] E and [DK][LBV]
@@ -434,16 +434,13 @@ struct GradLds : Strides<E, DK, CK> {
     static constexpr int off_gdO = off_dO + ECB;
     static constexpr int off_R = off_gdO + ECB;
     static constexpr int off_U = off_R + ECB;
-    static constexpr int off_DU = off_U + ECB;
-    static constexpr int off_dU = off_DU + ECB;
+    static constexpr int off_dU = off_U + ECB;
     static constexpr int off_dX = off_dU + ECB;
     static constexpr int off_dOt = off_dX + ECB;               // [kBV][LCK] E
     static constexpr int off_Rt = off_dOt + EBC;
     static constexpr int off_dUt = off_Rt + EBC;
     static constexpr int off_V = off_dUt + EBC;                // [CK][LBF] f32
-    static constexpr int off_X = off_V + FCB;
-    static constexpr int off_KdS = off_X + FCB;
-    static constexpr int blk_end = off_KdS + FCB;
+    static constexpr int blk_end = off_V + FCB;
     // the last phase, over the block region
     static constexpr int off_dTt = off_blk;                    // [CK][LF] f32
     static constexpr int off_dTb = off_dTt + FCC;
@@ -476,9 +473,9 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
     GL_F(Bm, off_Bm); GL_F(Af, off_A); GL_F(Tf, off_T); GL_F(Tft, off_Tft); GL_F(Pf, off_P);
     GL_E(Tt, off_Tt); GL_E(Ttt, off_Ttt); GL_E(Pt, off_Pt);
     GL_E(S0s, off_S0); GL_E(S0t, off_S0t); GL_E(dSs, off_dS); GL_E(dSt, off_dSt);
-    GL_E(dOs, off_dO); GL_E(gdOs, off_gdO); GL_E(Rs, off_R); GL_E(Us, off_U); GL_E(DUs, off_DU);
+    GL_E(dOs, off_dO); GL_E(gdOs, off_gdO); GL_E(Rs, off_R); GL_E(Us, off_U);
     GL_E(dUs, off_dU); GL_E(dXs, off_dX); GL_E(dOt, off_dOt); GL_E(Rt, off_Rt); GL_E(dUt, off_dUt);
-    GL_F(Vs, off_V); GL_F(Xs, off_X); GL_F(KdSs, off_KdS);
+    GL_F(Vs, off_V);
     GL_F(dTt, off_dTt); GL_F(dTb, off_dTb); GL_F(Em, off_Em); GL_F(Y1t, off_Y1t); GL_F(dAf, off_dA);
     GL_E(dPW, off_dPW); GL_E(dPWt, off_dPWt); GL_E(dGf, off_dG); GL_E(dGt, off_dGt);
 #undef GL_E
@@ -489,39 +486,83 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
     float* bs = Dd + CK;
     float* dg = bs + CK;
     float* hgp = dg + CK;        // [8][CK] per-wave partial sums of the gamma terms
-    float* frp = hgp + 8 * CK;   // [4][CK] per-wave partial sums of the D terms
-    float* red = frp + 4 * CK;   // [8]: per-wave <dS_end, S0>
+    float* frp = hgp + 8 * CK;   // [8][CK] per-wave partial sums of the D terms
+    float* red = frp + 8 * CK;   // [8]: per-wave <dS_end, S0>
 
-    const int cid = blockIdx.x;
-    const int tid = threadIdx.x, w = wave_id(), l = lane_id(), g4 = l >> 4, c16 = l & 15;
+    // Each workgroup walks chunks blockIdx.x, + gridDim.x, ...; the next
+    // chunk's keys, queries, gates and first value block are read into
+    // registers while the current chunk is worked on.
+    RowStage<E, CK, DK, NT> ks, qs;
+    float lav = 0.f, btv = 0.f;
+    auto fetch_chunk = [&](int c, int tid) {
+        const int n = c % p.NC, valid = min(CK, p.L - n * CK);
+        const size_t tok = (size_t)(c / p.NC) * p.L + (size_t)n * CK;
+        ks.load(reinterpret_cast<const E*>(p.k) + tok * DK, DK, valid, tid);
+        qs.load(reinterpret_cast<const E*>(p.q) + tok * DK, DK, valid, tid);
+        lav = 0.f;
+        btv = 0.f;
+        if (tid < valid) {
+            btv = p.beta[tok + tid];
+            if (p.log_alpha) lav = p.log_alpha[tok + tid];
+        }
+    };
+    // one block of value channels: S0 and dS_end rows, V and dO columns.
+    // Thread x takes row x % kBV, so the transposed stores of a wave are
+    // consecutive.
+    constexpr int NSV = (kBV * DK / VE + NT - 1) / NT;   // 16-byte vectors per thread and state
+    constexpr int PERV = kBV / VE, NVV = (CK * PERV + NT - 1) / NT;
+    u32x4 sa[NSV], sb[NSV], va[NVV], da[NVV];
+    auto fetch_block = [&](int c, int v0, int tid) {
+        const int n = c % p.NC, valid = min(CK, p.L - n * CK);
+        const size_t tok = (size_t)(c / p.NC) * p.L + (size_t)n * CK;
+        const E* S0g = static_cast<const E*>(p.Sck) + (size_t)c * p.DV * DK;
+        const E* dSg = static_cast<const E*>(p.dSck) + (size_t)c * p.DV * DK;
+        const E* vg = reinterpret_cast<const E*>(p.v) + tok * p.DV;
+        const E* dog = reinterpret_cast<const E*>(p.dO) + tok * p.DV;
+#pragma unroll
+        for (int u = 0; u < NSV; ++u) {
+            const int xs = tid + NT * u, i = xs % kBV, j = VE * (xs / kBV);
+            if (xs < kBV * DK / VE) {
+                sa[u] = ld16(S0g + (size_t)(v0 + i) * DK + j);
+                sb[u] = ld16(dSg + (size_t)(v0 + i) * DK + j);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NVV; ++u) {
+            const int x = tid + NT * u, r = x % CK, cc = (x / CK) * VE;
+            const bool ok = x < CK * PERV && r < valid;
+            va[u] = ok ? ld16(vg + (size_t)r * p.DV + v0 + cc) : u32x4{0u, 0u, 0u, 0u};
+            da[u] = ok ? ld16(dog + (size_t)r * p.DV + v0 + cc) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    if ((int)blockIdx.x < p.total) {
+        fetch_chunk(blockIdx.x, threadIdx.x);
+        fetch_block(blockIdx.x, 0, threadIdx.x);
+    }
+    for (int cid = blockIdx.x; cid < p.total; cid += gridDim.x) {
+    // lane-dependent values are re-derived per chunk (see opaque)
+    const int tid = opaque(threadIdx.x), l = tid & (kWave - 1), g4 = l >> 4, c16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int nxt = cid + gridDim.x;
     const int bh = cid / p.NC, n = cid % p.NC;
     const int t0 = n * CK, valid = min(CK, p.L - t0);
     const size_t tok = (size_t)bh * p.L + t0;
 
     // ---- the chunk's keys, queries and gates
-    {
-        RowStage<E, CK, DK, NT> ks, qs;
-        ks.load(reinterpret_cast<const E*>(p.k) + tok * DK, DK, valid, tid);
-        qs.load(reinterpret_cast<const E*>(p.q) + tok * DK, DK, valid, tid);
-        ks.store(Ks, LDK, Kt, LCK, tid);
-        qs.store(Qs, LDK, Qt, LCK, tid);
-    }
-    for (int x = tid; x < 12 * CK; x += NT) hgp[x] = 0.f;   // hgp and frp
+    ks.store(Ks, LDK, Kt, LCK, tid);
+    qs.store(Qs, LDK, Qt, LCK, tid);
+    for (int x = tid; x < 16 * CK; x += NT) hgp[x] = 0.f;   // hgp and frp
     if (w == 0) {
-        float la = 0.f, bt = 0.f;
-        if (l < valid) {
-            bt = p.beta[tok + l];
-            if (p.log_alpha) la = p.log_alpha[tok + l];
-        }
-        const float g = wave_incl_scan(la);
+        const float g = wave_incl_scan(lav);
         const float gC = __shfl(g, CK - 1, kWave);
         if (l < CK) {
             gs[l] = g;
             gam[l] = __expf(g);
             Dd[l] = __expf(gC - g);
-            bs[l] = bt;
+            bs[l] = btv;
         }
     }
+    if (nxt < p.total) fetch_chunk(nxt, tid);
     __syncthreads();
     // ---- Gram and score tiles: Bm = strictly-lower(K K^T . Gamma),
     // A = diag(beta) Bm, P = Q K^T . Gamma (diagonal included)
@@ -529,8 +570,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
         const int rb = w / NB, ib = w % NB;
         f32x4 kk = zero4(), qk = zero4();
         if (ib <= rb) {
-            tmma<E>(kk, Ks, LDK, 16 * rb, Ks, LDK, 16 * ib, DK);
-            tmma<E>(qk, Qs, LDK, 16 * rb, Ks, LDK, 16 * ib, DK);
+            tmma<E>(kk, Ks, LDK, 16 * rb, Ks, LDK, 16 * ib, DK, l);
+            tmma<E>(qk, Qs, LDK, 16 * rb, Ks, LDK, 16 * ib, DK, l);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -555,38 +596,13 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
         Ttt[s * LCK + r] = from_f32<E>(t * bs[s]);
     }
 
-    f32x4 dQa[NQW], dKa[NQW];
+    // C x DK accumulators: dQa = (gamma dO) S0, dKa = dX S0, dKd = U dS_end
+    f32x4 dQa[NQW], dKa[NQW], dKd[NQW];
 #pragma unroll
-    for (int u = 0; u < NQW; ++u) { dQa[u] = zero4(); dKa[u] = zero4(); }
+    for (int u = 0; u < NQW; ++u) { dQa[u] = zero4(); dKa[u] = zero4(); dKd[u] = zero4(); }
     f32x4 dPa = zero4(), dTa = zero4();   // C x C tile w (w < NCC)
     float hS = 0.f;                       // this thread's part of <dS_end, S0>
-
-    const E* S0g = static_cast<const E*>(p.Sck) + (size_t)cid * p.DV * DK;
-    const E* dSg = static_cast<const E*>(p.dSck) + (size_t)cid * p.DV * DK;
-    const E* vg = reinterpret_cast<const E*>(p.v) + tok * p.DV;
-    const E* dog = reinterpret_cast<const E*>(p.dO) + tok * p.DV;
-    // one block of value channels: S0 and dS_end rows, V and dO columns.
-    // Thread x takes row x % kBV (token x % CK), so the transposed stores of
-    // a wave are consecutive; the next block's reads are issued before the
-    // current block is worked on.
-    constexpr int NSV = (kBV * DK / VE + NT - 1) / NT;   // 16-byte vectors per thread and state
-    constexpr int PERV = kBV / VE;
-    u32x4 sa[NSV], sb[NSV], va, da;
-    auto fetch = [&](int v0) {
-#pragma unroll
-        for (int u = 0; u < NSV; ++u) {
-            const int xs = tid + NT * u, i = xs % kBV, j = VE * (xs / kBV);
-            if (xs < kBV * DK / VE) {
-                sa[u] = ld16(S0g + (size_t)(v0 + i) * DK + j);
-                sb[u] = ld16(dSg + (size_t)(v0 + i) * DK + j);
-            }
-        }
-        const int r = tid % CK, c = (tid / CK) * VE;
-        const bool ok = tid < CK * PERV && r < valid;
-        va = ok ? ld16(vg + (size_t)r * p.DV + v0 + c) : u32x4{0u, 0u, 0u, 0u};
-        da = ok ? ld16(dog + (size_t)r * p.DV + v0 + c) : u32x4{0u, 0u, 0u, 0u};
-    };
-    fetch(0);
+    constexpr int NCB = NB * (kBV / 16);  // C x kBV tiles (<= 4)
     for (int v0 = 0; v0 < p.DV; v0 += kBV) {
         __syncthreads();   // the previous block's operands are consumed
 #pragma unroll
@@ -605,81 +621,68 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
                 hS += to_f32(a[e]) * to_f32(b[e]);
             }
         }
-        if (tid < CK * PERV) {
-            const int r = tid % CK, c = (tid / CK) * VE;
-            float a[VE], d[VE];
-            Pack<E>::unpack(va, a);
-            Pack<E>::unpack(da, d);
 #pragma unroll
-            for (int j = 0; j < VE; ++j) {
-                Vs[r * LBF + c + j] = a[j];
-                dOs[r * LBV + c + j] = from_f32<E>(d[j]);
-                dOt[(c + j) * LCK + r] = from_f32<E>(d[j]);
-                gdOs[r * LBV + c + j] = from_f32<E>(gam[r] * d[j]);
+        for (int u = 0; u < NVV; ++u) {
+            const int x = tid + NT * u, r = x % CK, c = (x / CK) * VE;
+            if (x < CK * PERV) {
+                float a[VE], d[VE];
+                Pack<E>::unpack(va[u], a);
+                Pack<E>::unpack(da[u], d);
+#pragma unroll
+                for (int j = 0; j < VE; ++j) {
+                    Vs[r * LBF + c + j] = a[j];
+                    dOs[r * LBV + c + j] = from_f32<E>(d[j]);
+                    dOt[(c + j) * LCK + r] = from_f32<E>(d[j]);
+                    gdOs[r * LBV + c + j] = from_f32<E>(gam[r] * d[j]);
+                }
             }
         }
-        if (v0 + kBV < p.DV) fetch(v0 + kBV);
+        if (v0 + kBV < p.DV) fetch_block(cid, v0 + kBV, tid);
+        else if (nxt < p.total) fetch_block(nxt, 0, tid);
         __syncthreads();
-        // ---- X = K S0^T and R = V - gamma X (waves 0-3); K dS^T (waves 4-7)
+        // ---- R = V - gamma K S0^T (waves 0..NCB-1); dU = P^T dO + D . K dS^T (waves 4..)
         if (w < NCB) {
             const int rb = w / 2, cb = w % 2;
             f32x4 x = zero4();
-            tmma<E>(x, Ks, LDK, 16 * rb, S0s, LDK, 16 * cb, DK);
+            tmma<E>(x, Ks, LDK, 16 * rb, S0s, LDK, 16 * cb, DK, l);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
                 const float rr = Vs[r * LBF + i] - gam[r] * x[e];
-                Xs[r * LBF + i] = x[e];
                 Rs[r * LBV + i] = from_f32<E>(rr);
                 Rt[i * LCK + r] = from_f32<E>(rr);
             }
         } else if (w >= 4 && w < 4 + NCB) {
             const int rb = (w - 4) / 2, cb = (w - 4) % 2;
-            f32x4 kds = zero4();
-            tmma<E>(kds, Ks, LDK, 16 * rb, dSs, LDK, 16 * cb, DK);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) KdSs[(16 * rb + 4 * g4 + e) * LBF + 16 * cb + c16] = kds[e];
-        }
-        __syncthreads();
-        // ---- U = T~ R (waves 0-3), dU = P^T dO + D . K dS^T (waves 4-7)
-        if (w < NCB) {
-            const int rb = w / 2, cb = w % 2;
-            f32x4 u = zero4();
-            tmma<E>(u, Tt, LCK, 16 * rb, Rt + 16 * cb * LCK, LCK, 0, CK);
+            f32x4 kds = zero4(), du = zero4();
+            tmma<E>(kds, Ks, LDK, 16 * rb, dSs, LDK, 16 * cb, DK, l);
+            tmma<E>(du, Pt, LCK, 16 * rb, dOt + 16 * cb * LCK, LCK, 0, CK, l);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
-                Us[r * LBV + i] = from_f32<E>(u[e]);
-                DUs[r * LBV + i] = from_f32<E>(Dd[r] * u[e]);
-                const float f = row16_sum(Dd[r] * u[e] * KdSs[r * LBF + i]);
-                if (c16 == 0) frp[w * CK + r] += f;
-            }
-        } else if (w >= 4 && w < 4 + NCB) {
-            const int rb = (w - 4) / 2, cb = (w - 4) % 2;
-            f32x4 du = zero4();
-            tmma<E>(du, Pt, LCK, 16 * rb, dOt + 16 * cb * LCK, LCK, 0, CK);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
-                const float dd = du[e] + Dd[r] * KdSs[r * LBF + i];
+                const float dd = du[e] + Dd[r] * kds[e];
                 dUs[r * LBV + i] = from_f32<E>(dd);
                 dUt[i * LCK + r] = from_f32<E>(dd);
             }
         }
         __syncthreads();
-        // ---- dR = T~^T dU (= dV), dX = -gamma dR
+        // ---- U = T~ R (waves 0..); dR = T~^T dU (= dV), dX = -gamma dR (waves 4..)
         if (w < NCB) {
             const int rb = w / 2, cb = w % 2;
+            f32x4 u = zero4();
+            tmma<E>(u, Tt, LCK, 16 * rb, Rt + 16 * cb * LCK, LCK, 0, CK, l);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Us[(16 * rb + 4 * g4 + e) * LBV + 16 * cb + c16] = from_f32<E>(u[e]);
+        } else if (w >= 4 && w < 4 + NCB) {
+            const int rb = (w - 4) / 2, cb = (w - 4) % 2;
             f32x4 dr = zero4();
-            tmma<E>(dr, Ttt, LCK, 16 * rb, dUt + 16 * cb * LCK, LCK, 0, CK);
+            tmma<E>(dr, Ttt, LCK, 16 * rb, dUt + 16 * cb * LCK, LCK, 0, CK, l);
             E* dvg = reinterpret_cast<E*>(p.dv) + tok * p.DV + v0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
                 if (r < valid) dvg[(size_t)r * p.DV + i] = from_f32<E>(dr[e]);
                 dXs[r * LBV + i] = from_f32<E>(-gam[r] * dr[e]);
-                const float h = row16_sum(-gam[r] * dr[e] * Xs[r * LBF + i]);
-                if (c16 == 0) hgp[w * CK + r] += h;
             }
         }
         __syncthreads();
@@ -689,19 +692,56 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
             const int t = w + NW * u;
             if (t < NQT) {
                 const int rb = t / NJ, jb = t % NJ;
-                tmma<E>(dQa[u], gdOs, LBV, 16 * rb, S0t, LBV, 16 * jb, kBV);
-                tmma<E>(dKa[u], DUs, LBV, 16 * rb, dSt, LBV, 16 * jb, kBV);
-                tmma<E>(dKa[u], dXs, LBV, 16 * rb, S0t, LBV, 16 * jb, kBV);
+                tmma<E>(dQa[u], gdOs, LBV, 16 * rb, S0t, LBV, 16 * jb, kBV, l);
+                tmma<E>(dKa[u], dXs, LBV, 16 * rb, S0t, LBV, 16 * jb, kBV, l);
+                tmma<E>(dKd[u], Us, LBV, 16 * rb, dSt, LBV, 16 * jb, kBV, l);
             }
         }
         if (w < NCC) {
             const int rb = w / NB, sb = w % NB;
-            tmma<E>(dPa, dOs, LBV, 16 * rb, Us, LBV, 16 * sb, kBV);
-            tmma<E>(dTa, dUs, LBV, 16 * rb, Rs, LBV, 16 * sb, kBV);
+            tmma<E>(dPa, dOs, LBV, 16 * rb, Us, LBV, 16 * sb, kBV, l);
+            tmma<E>(dTa, dUs, LBV, 16 * rb, Rs, LBV, 16 * sb, kBV, l);
         }
     }
     __syncthreads();   // the block region is reused below
 
+    // ---- the dg terms that sum over key channels, from the accumulators
+    // before the score terms join them, per row r:
+    //   gamma dO (Q S0^T):  sum_j Q_rj (gamma dO S0)_rj
+    //   -gamma dR . X:      sum_j K_rj (dX S0)_rj
+    //   D . U . K dS^T:     sum_j K_rj D_r (U dS_end)_rj     (enters with -)
+    // and dK = dX S0 + D . U dS_end.  The 16 lanes of a tile row are summed
+    // side by side for all rows of the tile.
+#pragma unroll
+    for (int u = 0; u < NQW; ++u) {
+        const int t = w + NW * u;
+        if (t < NQT) {
+            const int rb = t / NJ, jb = t % NJ;
+            float h[4], f[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * g4 + e, j = 16 * jb + c16;
+                const float kq = to_f32(Ks[r * LDK + j]), qq = to_f32(Qs[r * LDK + j]);
+                dKd[u][e] *= Dd[r];
+                h[e] = qq * dQa[u][e] + kq * dKa[u][e];
+                f[e] = kq * dKd[u][e];
+                dKa[u][e] += dKd[u][e];
+            }
+#pragma unroll
+            for (int m = 8; m >= 1; m >>= 1)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[e] += __shfl_xor(h[e], m, kWave);
+                    f[e] += __shfl_xor(f[e], m, kWave);
+                }
+            if (c16 == 0)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hgp[w * CK + 16 * rb + 4 * g4 + e] += h[e];   // this wave's own slot
+                    frp[w * CK + 16 * rb + 4 * g4 + e] += f[e];
+                }
+        }
+    }
     // ---- C x C terms
     if (w < NCC) {
         const int rb = w / NB, sb = w % NB;
@@ -714,21 +754,6 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
             Em[r * LF + s] = dPa[e] * Pf[r * LF + s];
             dTt[r * LF + s] = dTa[e];
             dTb[r * LF + s] = dTa[e] * bs[s];
-        }
-    }
-    // the gamma . dO . (Q S0^T) term of dg: sum_j Q_rj (gamma dO S0)_rj, from
-    // the dQ accumulators before the score terms join them
-#pragma unroll
-    for (int u = 0; u < NQW; ++u) {
-        const int t = w + NW * u;
-        if (t < NQT) {
-            const int rb = t / NJ, jb = t % NJ;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * g4 + e;
-                const float h = row16_sum(to_f32(Qs[r * LDK + 16 * jb + c16]) * dQa[u][e]);
-                if (c16 == 0) hgp[w * CK + r] += h;   // this wave's own slot
-            }
         }
     }
     {
@@ -745,14 +770,14 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
         const int t = w + NW * u;
         if (t < NQT) {
             const int rb = t / NJ, jb = t % NJ;
-            tmma<E>(dQa[u], dPW, LCK, 16 * rb, Kt, LCK, 16 * jb, CK);
-            tmma<E>(dKa[u], dPWt, LCK, 16 * rb, Qt, LCK, 16 * jb, CK);
+            tmma<E>(dQa[u], dPW, LCK, 16 * rb, Kt, LCK, 16 * jb, CK, l);
+            tmma<E>(dKa[u], dPWt, LCK, 16 * rb, Qt, LCK, 16 * jb, CK, l);
         }
     }
     if (w < NCC) {
         const int rb = w / NB, sb = w % NB;
         f32x4 y = zero4();
-        tmma<float>(y, dTb, LF, 16 * rb, Tf, LF, 16 * sb, CK);
+        tmma<float>(y, dTb, LF, 16 * rb, Tf, LF, 16 * sb, CK, l);
 #pragma unroll
         for (int e = 0; e < 4; ++e) Y1t[(16 * sb + c16) * LF + 16 * rb + 4 * g4 + e] = y[e];
     }
@@ -767,7 +792,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
     if (w < NCC) {
         const int rb = w / NB, sb = w % NB;
         f32x4 y = zero4();
-        tmma<float>(y, Tft, LF, 16 * rb, Y1t, LF, 16 * sb, CK);
+        tmma<float>(y, Tft, LF, 16 * rb, Y1t, LF, 16 * sb, CK, l);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * rb + 4 * g4 + e, s = 16 * sb + c16;
@@ -786,8 +811,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
         const int t = w + NW * u;
         if (t < NQT) {
             const int rb = t / NJ, jb = t % NJ;
-            tmma<E>(dKa[u], dGf, LCK, 16 * rb, Kt, LCK, 16 * jb, CK);
-            tmma<E>(dKa[u], dGt, LCK, 16 * rb, Kt, LCK, 16 * jb, CK);
+            tmma<E>(dKa[u], dGf, LCK, 16 * rb, Kt, LCK, 16 * jb, CK, l);
+            tmma<E>(dKa[u], dGt, LCK, 16 * rb, Kt, LCK, 16 * jb, CK, l);
         }
     }
     // dbeta and dg per token, then d log alpha = suffix sums of dg
@@ -798,7 +823,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
             for (int s = 0; s < CK; ++s) db += dAf[l * LF + s] * Bm[l * LF + s];
             float fa = 0.f, hg = 0.f;
             for (int s = 0; s < CK; ++s) fa += Em[l * LF + s] - Em[s * LF + l];
-            for (int x = 0; x < 4; ++x) fr += frp[x * CK + l];
+            for (int x = 0; x < NW; ++x) fr += frp[x * CK + l];
             for (int x = 0; x < 8; ++x) hg += hgp[x * CK + l];
             dgl = dg[l] + fa + hg - fr;
         }
@@ -836,7 +861,10 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
             }
         }
     }
+    __syncthreads();   // the LDS is restaged for the next chunk
+    }
 }
+
 
 // ------------------------------------------------------- grads, channel alpha
 // Per-channel decay G (C x d_k, cumulative within the chunk).  With
@@ -1425,12 +1453,14 @@ static hipError_t launch_bwd_t(const BwdParams& bp, int BH, bool channel, hipStr
     hipError_t err = channel ? launch_lds(chunk_bwd_chain_kernel<E, DK, CK, true>, chains, 128, CL::bytes, stream, bp)
                              : launch_lds(chunk_bwd_chain_kernel<E, DK, CK, false>, chains, 128, CL::bytes, stream, bp);
     if (err != hipSuccess) return err;
-    // channel alpha: persistent, one workgroup per CU (the next chunk's inputs
+    // persistent, as many workgroups as fit the CUs (the next chunk's inputs
     // are read while the current one is worked on)
     return channel ? launch_lds(chunk_bwd_grad_channel_kernel<E, DK, CK>,
                                 std::min(bp.total, (160 * 1024 / GC::bytes) * compute_units()), 512, GC::bytes,
                                 stream, bp)
-                   : launch_lds(chunk_bwd_grad_kernel<E, DK, CK>, bp.total, 512, GL::bytes, stream, bp);
+                   : launch_lds(chunk_bwd_grad_kernel<E, DK, CK>,
+                                std::min(bp.total, (160 * 1024 / GL::bytes) * compute_units()), 512, GL::bytes,
+                                stream, bp);
 }
 
 }  // namespace
