@@ -29,8 +29,9 @@
 //                           walks the chunks backwards carrying dS (the
 //                           only sequential part) and keeps dS_end of every
 //                           chunk;
-//   chunk_bwd_grad_kernel   one workgroup per chunk: every gradient of the
-//                           chunk's tokens from S0, dS_end and its inputs
+//   chunk_bwd_grad_kernel   every gradient of a chunk's tokens from S0,
+//                           dS_end and its inputs; persistent, one workgroup
+//                           per CU walking the chunks
 //                           (chunk_bwd_grad_channel_kernel for channel alpha,
 //                           whose chunk algebra is written out above it).
 // The products run on MFMA (bf16 operands for bf16 inputs, fp32 otherwise;
@@ -878,9 +879,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
 //   dG  = (dO S0) . Qg + (dX S0) . Kg - (U dS_end) . Kd + dQ_P . Q + (dK_A1 - dK_P2 - dK_A2) . K
 //   dG_C += sum_r (U dS_end . Kd)_r + e^{G_C} <dS_end, S0> per channel,
 // with dPM = dO U^T . M_incl and dAb = diag(beta) dA.  The four sums with the
-// decay inside run per pair of 16-token tiles through a reference row m of
-// the pair (the forward's scheme): e^{G_r - G_i} = e^{G_r - G_m} e^{G_m - G_i}
-// with both factors at most 1 off the diagonal and at most e^80 on it.
+// decay inside run per output tile of 16 tokens through a reference row m of
+// the tile: e^{G_r - G_i} = e^{G_r - G_m} e^{G_m - G_i}.
 constexpr int kBVC = 32;   // value channels per block (channel alpha)
 
 template <typename E, int DK, int CK>
