@@ -193,168 +193,321 @@ struct Strides {
 };
 
 // ---------------------------------------------------------------- chain
+// Two LDS buffers of one chunk's operands: the helper waves fill one with
+// chunk n - 1 while the owner waves read chunk n from the other.  (Channel
+// alpha: K holds K . exp(G_C - G), Kt and Qt the transposes of K . exp(G)
+// and Q . exp(G), f holds exp(G_C) per key channel.)
 template <typename E, int DK, int CK>
 struct ChainLds : Strides<E, DK, CK> {
-    // (channel alpha: K holds K . exp(G_C - G), Kt and Qt the transposes of
-    // K . exp(G) and Q . exp(G), M is unused, f holds exp(G_C) per channel)
     using S = Strides<E, DK, CK>;
     static constexpr int ES = (int)sizeof(E);
-    static constexpr int off_K = 0;                            // [CK][LDK] E
-    static constexpr int off_Kt = off_K + CK * S::LDK * ES;    // [DK][LCK] E
-    static constexpr int off_Q = off_Kt + DK * S::LCK * ES;    // [CK][LDK] E
-    static constexpr int off_Qt = off_Q + CK * S::LDK * ES;    // [DK][LCK] E
-    static constexpr int off_dOt = off_Qt + DK * S::LCK * ES;  // [kBV][LCK] E, dO^T
-    static constexpr int off_gdOt = off_dOt + kBV * S::LCK * ES;   // (gamma . dO)^T
-    static constexpr int off_Tt = off_gdOt + kBV * S::LCK * ES;    // [CK][LCK] E, T~^T
-    static constexpr int off_Pt = off_Tt + CK * S::LCK * ES;       // [CK][LCK] E, P^T
-    static constexpr int off_M = off_Pt + CK * S::LCK * ES;        // [CK][LF] f32, Gamma . M_incl
-    static constexpr int off_f = off_M + CK * S::LF * 4;           // gamma [CK], D [CK], gamma_C
+    static constexpr int b_K = 0;                               // [CK][LDK] E
+    static constexpr int b_Kt = b_K + CK * S::LDK * ES;         // [DK][LCK] E
+    static constexpr int b_Qt = b_Kt + DK * S::LCK * ES;        // [DK][LCK] E
+    static constexpr int b_dOt = b_Qt + DK * S::LCK * ES;       // [kBV][LCK] E, dO^T
+    static constexpr int b_gdOt = b_dOt + kBV * S::LCK * ES;    // (gamma . dO)^T
+    static constexpr int b_Tt = b_gdOt + kBV * S::LCK * ES;     // [CK][LCK] E, T~^T
+    static constexpr int b_Pt = b_Tt + CK * S::LCK * ES;        // [CK][LCK] E, P^T
+    static constexpr int b_f = b_Pt + CK * S::LCK * ES;         // gamma [CK], D [CK], gamma_C
     static constexpr int NF = (2 * CK + 4 > DK ? 2 * CK + 4 : DK);
-    static constexpr int off_w = off_f + NF * 4;                    // per wave: dS [16][LDK], dU^T, -gamma dR^T [16][LCK]
+    static constexpr int bbytes = (b_f + NF * 4 + 15) / 16 * 16;
+    static constexpr int off_w = 2 * bbytes;                    // per owner wave: dS [16][LDK], dU^T, -gamma dR^T [16][LCK]
     static constexpr int wbytes = 16 * S::LDK * ES + 2 * 16 * S::LCK * ES;
     static constexpr int bytes = off_w + 2 * wbytes;
 };
 
+// One 16-row block (rows r0 + l % 16) of a row-major [rows][DK] global array
+// as MFMA operand fragments (lane group g: key channels 32 ks + 8 g .. + 7),
+// zero at or past `valid`.
+template <typename E, int DK>
+struct RowFrags {
+    static constexpr int NKS = DK / 32;
+    Frag<E> f[NKS];
+    // Reads row min(r0 + l % 16, rmax) unconditionally: a read under a
+    // condition, or a select on its value, makes the compiler wait for it
+    // where it is issued; rows past the end are zeroed by mask() once the
+    // data is used.
+    __device__ __forceinline__ void load(const E* base, int r0, int rmax, int l) {
+        const int r = min(r0 + (l & 15), rmax), k = 8 * (l >> 4);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const E* src = base + (size_t)r * DK + 32 * ks + k;
+            if constexpr (sizeof(E) == 2) {
+                f[ks].v = *reinterpret_cast<const bf16x8*>(src);
+            } else {
+                f[ks].lo = *reinterpret_cast<const f32x4*>(src);
+                f[ks].hi = *reinterpret_cast<const f32x4*>(src + 4);
+            }
+        }
+    }
+    __device__ __forceinline__ void mask(int r0, int valid, int l) {
+        if (r0 + (l & 15) < valid) return;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            if constexpr (sizeof(E) == 2) f[ks].v = bf16x8{};
+            else { f[ks].lo = zero4(); f[ks].hi = zero4(); }
+        }
+    }
+    // Products of these fragments stay after this point (a prefetching loop
+    // would otherwise let the compiler compute them right after the reads,
+    // waiting for them there).
+    __device__ __forceinline__ void pin() {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            if constexpr (sizeof(E) == 2) {
+                asm volatile("" : "+v"(f[ks].v));
+            } else {
+                asm volatile("" : "+v"(f[ks].lo), "+v"(f[ks].hi));
+            }
+        }
+    }
+    // rows into LDS, plain [row][LD] and/or transposed [key channel][LT]
+    __device__ __forceinline__ void store(E* dst, int LD, int r0, int l) const {
+        const int r = r0 + (l & 15), k = 8 * (l >> 4);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            E* d = dst + r * LD + 32 * ks + k;
+            if constexpr (sizeof(E) == 2) {
+                st16(d, __builtin_bit_cast(u32x4, f[ks].v));
+            } else {
+                *reinterpret_cast<f32x4*>(d) = f[ks].lo;
+                *reinterpret_cast<f32x4*>(d + 4) = f[ks].hi;
+            }
+        }
+    }
+    __device__ __forceinline__ void store_t(E* dstT, int LT, int r0, int l) const {
+        const int r = r0 + (l & 15), k = 8 * (l >> 4);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            E e[8];
+            if constexpr (sizeof(E) == 2) {
+                __builtin_memcpy(e, &f[ks].v, 16);
+            } else {
+                __builtin_memcpy(e, &f[ks].lo, 16);
+                __builtin_memcpy(e + 4, &f[ks].hi, 16);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dstT[(32 * ks + k + j) * LT + r] = e[j];
+        }
+    }
+};
+
+// What a helper wave reads for one chunk.  Helpers 0, 1 (kb = 0, 1): row
+// block kb of K (channel: of K . exp(G_C - G) and K . exp(G)) and, scalar
+// alpha, the score tiles (kb, kb) and, helper 0, (1, 0) with the Q rows they
+// need; helpers 2, 3: row block kb - 2 of Q (channel: Q . exp(G)), and
+// halves of T~, P (channel), the dO block and the decay factors.
 template <typename E, int DK, int CK, bool CH>
-__global__ __launch_bounds__(128) void chunk_bwd_chain_kernel(BwdParams p)
+struct ChainIn {
+    RowFrags<E, DK> kf;          // K rows
+    RowFrags<E, DK> kg;          // channel: K . exp(G) rows
+    RowFrags<E, DK> qa;          // Q rows (scalar helpers 0, 1: block kb; helpers 2, 3: block kb - 2)
+    RowFrags<E, DK> qb;          // scalar, helper 0: Q rows 16 ..
+    u32x4 tv, mv, ov;            // T~ vector; channel: P vector; dO vector
+    float gv, fv;                // gamma of the dO vector's token; decay factor entry
+    uint32_t gm[2][4];           // scalar: Gamma entries (raw bits) of the score tiles,
+                                 // converted only when used so that reading them does not wait
+    __device__ static __forceinline__ float gval(uint32_t x) {
+        return __uint_as_float(sizeof(E) == 2 ? x << 16 : x);
+    }
+};
+
+// dS (d_v x d_k per (b, h)) carried backwards over the chunks.  Owner waves
+// 0, 1 each hold the dS rows of 16 value channels in registers and do the
+// dependent products of a step (dU, dR, the dS update); helper waves 2 .. 5
+// read chunk n - 1 from memory, stage it into the other LDS buffer and (scalar
+// alpha) form its masked score block P = Q K^T . Gamma there, so a step costs
+// one barrier and no staging on the owners' path.
+template <typename E, int DK, int CK, bool CH>
+__global__ __launch_bounds__(384, 1) void chunk_bwd_chain_kernel(BwdParams p)
 {
     using LY = ChainLds<E, DK, CK>;
+    using IN = ChainIn<E, DK, CK, CH>;
     constexpr int NJ = DK / 16, NB = CK / 16, VE = Vec<E>::n;
-    constexpr int LDK = LY::LDK, LCK = LY::LCK, LF = LY::LF;
+    constexpr int LDK = LY::LDK, LCK = LY::LCK;
     constexpr WsLayout WL = ws_layout((int)sizeof(E), DK, CK, CH ? kAlphaChannel : kAlphaScalar);
+    constexpr int NRV = CK * CK / VE;            // 16-byte vectors of T~ (and of Gamma or P)
+    constexpr int PERO = kBV / VE;               // 16-byte vectors per token of the dO block
+    constexpr int NFV = CH ? DK : 2 * CK + 1;    // decay factor entries
+    static_assert(NRV <= 128 && CK * PERO <= 128 && NFV <= 128, "two helper waves cover a chunk");
     extern __shared__ __align__(16) unsigned char smem[];
-    E* Ks = reinterpret_cast<E*>(smem + LY::off_K);
-    E* Kt = reinterpret_cast<E*>(smem + LY::off_Kt);
-    E* Qs = reinterpret_cast<E*>(smem + LY::off_Q);
-    E* Qt = reinterpret_cast<E*>(smem + LY::off_Qt);
-    E* dOt = reinterpret_cast<E*>(smem + LY::off_dOt);
-    E* gdOt = reinterpret_cast<E*>(smem + LY::off_gdOt);
-    E* Tts = reinterpret_cast<E*>(smem + LY::off_Tt);
-    E* Pt = reinterpret_cast<E*>(smem + LY::off_Pt);
-    float* Ms = reinterpret_cast<float*>(smem + LY::off_M);
-    float* gam = reinterpret_cast<float*>(smem + LY::off_f);
-    float* Dd = gam + CK;
-    const int tid = threadIdx.x, w = wave_id(), l = lane_id(), g4 = l >> 4, c16 = l & 15;
-    E* dSw = reinterpret_cast<E*>(smem + LY::off_w + w * LY::wbytes);   // [16][LDK]
-    E* dUt = dSw + 16 * LDK;                                            // [16][LCK]
-    E* dRt = dUt + 16 * LCK;                                            // -gamma dR, [16][LCK]
-
+    const int l = lane_id(), g4 = l >> 4, c16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int hr = w - 2;                        // helper role 0 .. 3
+    const bool khelp = hr < 2;                   // helpers of K (and the scores)
+    const int kb = khelp ? hr : hr - 2;          // the row block it handles
     const int nvb = p.DV / kBV;
     const int bh = blockIdx.x / nvb, v0 = (blockIdx.x % nvb) * kBV;
-    const int i0 = v0 + 16 * w;   // this wave's first value channel
+    const int i0 = v0 + 16 * w;   // owner: first value channel
 
-    // dS rows i0 + 4 g4 + e, key channels 16 jb + c16
+#define BUF_E(name, n, off) E* name = reinterpret_cast<E*>(smem + ((n) & 1) * LY::bbytes + LY::off)
+
+    // ---- helpers: read chunk n into registers
+    auto load = [&](IN& in, int n, auto kh) __attribute__((always_inline)) {
+        constexpr bool KH = decltype(kh)::value;
+        const int valid = min(CK, p.L - n * CK);
+        const size_t tok = (size_t)bh * p.L + (size_t)n * CK;
+        const unsigned char* rec = p.ws + ((size_t)bh * p.NC + n) * WL.bytes;
+        const E* qc = CH ? reinterpret_cast<const E*>(rec + WL.QG) : reinterpret_cast<const E*>(p.q) + tok * DK;
+        const int rmax = CH ? CK - 1 : valid - 1;   // records are zero past the end
+        if (16 * kb < CK) in.qa.load(qc, 16 * kb, rmax, l);
+        if constexpr (KH) {
+            if constexpr (CH) {
+                // the forward's decayed operands (zero past the end of the sequence)
+                if (16 * kb < CK) {
+                    in.kf.load(reinterpret_cast<const E*>(rec + WL.KD), 16 * kb, CK - 1, l);
+                    in.kg.load(reinterpret_cast<const E*>(rec + WL.KG), 16 * kb, CK - 1, l);
+                }
+            } else {
+                if (16 * kb < CK) in.kf.load(reinterpret_cast<const E*>(p.k) + tok * DK, 16 * kb, rmax, l);
+                if (NB == 2 && kb == 0) in.qb.load(qc, 16, rmax, l);
+                // Gamma of the score tiles: tile 0 is (kb, kb), tile 1 (helper 0) is (1, 0)
+                const E* mg = reinterpret_cast<const E*>(rec + WL.M);
+                // (read unconditionally from an index clamped into the block: a
+                // select on a loaded value would wait for the load here; the
+                // entries a helper has no tile for are never used)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int rb = t == 0 ? kb : 1, ib = t == 0 ? kb : 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = min(16 * rb + 4 * g4 + e, CK - 1), s = min(16 * ib + c16, CK - 1);
+                        const int idx = r * CK + col_of_tok(CK, s);
+                        if constexpr (sizeof(E) == 2) in.gm[t][e] = reinterpret_cast<const unsigned short*>(mg)[idx];
+                        else in.gm[t][e] = reinterpret_cast<const uint32_t*>(mg)[idx];
+                    }
+                }
+            }
+        } else {
+            // (every read unconditional from a clamped index; the entries
+            // past the ends are dropped or zeroed in stage)
+            const int x = 64 * kb + l;
+            in.tv = ld16(rec + WL.T + 16 * min(x, NRV - 1));
+            if constexpr (CH) in.mv = ld16(rec + WL.M + 16 * min(x, NRV - 1));
+            in.fv = reinterpret_cast<const float*>(rec + WL.F)[min(x, NFV - 1)];
+            const int xo = min(x, CK * PERO - 1), r = xo % CK, c = (xo / CK) * VE;
+            in.ov = ld16(reinterpret_cast<const E*>(p.dO) + (tok + min(r, valid - 1)) * p.DV + v0 + c);
+            if constexpr (!CH) in.gv = reinterpret_cast<const float*>(rec + WL.F)[r];
+        }
+    };
+    // ---- helpers: chunk n from registers into its LDS buffer
+    auto stage = [&](IN& in, int n, auto kh) __attribute__((always_inline)) {
+        constexpr bool KH = decltype(kh)::value;
+        BUF_E(Ks, n, b_K); BUF_E(Kt, n, b_Kt); BUF_E(Qt, n, b_Qt); BUF_E(dOt, n, b_dOt);
+        BUF_E(gdOt, n, b_gdOt); BUF_E(Tts, n, b_Tt); BUF_E(Pt, n, b_Pt);
+        float* f = reinterpret_cast<float*>(smem + (n & 1) * LY::bbytes + LY::b_f);
+        const int tvalid = min(CK, p.L - n * CK);
+        const int valid = CH ? CK : tvalid;   // K and Q rows (records are zero past the end)
+        if constexpr (KH) {
+            if constexpr (!CH) {
+                in.kf.pin();
+                in.qa.pin();
+                if (NB == 2) in.qb.pin();
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(in.gm[t][e]));
+                in.kf.mask(16 * kb, valid, l);
+                in.qa.mask(16 * kb, valid, l);
+                if (NB == 2) in.qb.mask(16, valid, l);
+            }
+            if (16 * kb < CK) {
+                in.kf.store(Ks, LDK, 16 * kb, l);
+                (CH ? in.kg : in.kf).store_t(Kt, LCK, 16 * kb, l);
+            }
+            if constexpr (!CH) {
+                // P = Q K^T . Gamma . M_incl on and below the diagonal, kept as
+                // P^T: tile (kb, kb) and, helper 0, (1, 0); helper 1 zeroes
+                // the tile above the diagonal
+                if (16 * kb < CK) {
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int ks = 0; ks < DK / 32; ++ks) mma(acc, in.qa.f[ks], in.kf.f[ks]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 16 * kb + 4 * g4 + e, s = 16 * kb + c16;
+                        Pt[s * LCK + r] = from_f32<E>(acc[e] * IN::gval(in.gm[0][e]));
+                    }
+                }
+                if (NB == 2 && kb == 0) {
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int ks = 0; ks < DK / 32; ++ks) mma(acc, in.qb.f[ks], in.kf.f[ks]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 16 + 4 * g4 + e, s = c16;
+                        Pt[s * LCK + r] = from_f32<E>(acc[e] * IN::gval(in.gm[1][e]));
+                    }
+                }
+                if (NB == 2 && kb == 1)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Pt[(16 + c16) * LCK + 4 * g4 + e] = from_f32<E>(0.f);
+            }
+        } else {
+            in.qa.mask(16 * kb, valid, l);
+            if (16 * kb < CK) in.qa.store_t(Qt, LCK, 16 * kb, l);
+            const int x = 64 * kb + l;
+            if (x < NRV) {
+                const int r = (VE * x) / CK, mc0 = (VE * x) % CK;
+                E te[VE], me[VE];
+                __builtin_memcpy(te, &in.tv, 16);
+                __builtin_memcpy(me, &in.mv, 16);
+#pragma unroll
+                for (int j = 0; j < VE; ++j) {
+                    const int t = tok_of_col(CK, mc0 + j);
+                    Tts[t * LCK + r] = te[j];
+                    if constexpr (CH) Pt[t * LCK + r] = me[j];   // the score block, transposed
+                }
+            }
+            if (x < NFV) f[x] = in.fv;   // gamma, D, gamma_C (channel: exp(G_C))
+            if (x < CK * PERO) {
+                const int r = x % CK, c = (x / CK) * VE;
+                E d[VE];
+                __builtin_memcpy(d, &in.ov, 16);
+                if (r >= tvalid)
+#pragma unroll
+                    for (int i = 0; i < VE; ++i) d[i] = from_f32<E>(0.f);
+#pragma unroll
+                for (int i = 0; i < VE; ++i) {
+                    dOt[(c + i) * LCK + r] = d[i];
+                    if constexpr (!CH) gdOt[(c + i) * LCK + r] = from_f32<E>(in.gv * to_f32(d[i]));
+                }
+            }
+        }
+    };
+
+    // ---- owners: dS rows i0 + 4 g4 + e, key channels 16 jb + c16
+    E* dSw = reinterpret_cast<E*>(smem + LY::off_w + (w & 1) * LY::wbytes);   // [16][LDK]
+    E* dUt = dSw + 16 * LDK;                                                  // [16][LCK]
+    E* dRt = dUt + 16 * LCK;                                                  // -gamma dR, [16][LCK]
     f32x4 dS[NJ];
 #pragma unroll
     for (int jb = 0; jb < NJ; ++jb) {
         dS[jb] = zero4();
-        if (p.dS_final)
+        if (w < 2 && p.dS_final)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 dS[jb][e] = p.dS_final[((size_t)bh * p.DV + i0 + 4 * g4 + e) * DK + 16 * jb + c16];
     }
-
-    // The next chunk's inputs wait in registers: its reads are issued as soon
-    // as the current chunk's are in LDS, and land while it is worked on.
-    constexpr int NRV = CK * CK / VE;            // 16-byte vectors of T~ (and of Gamma)
-    constexpr int PERO = kBV / VE;               // 16-byte vectors per token of the dO block
-    constexpr int NOV = (CK * PERO + 127) / 128;
-    RowStage<E, CK, DK, 128> ks, qs, gs;   // channel: K . exp(G_C - G), Q . exp(G), K . exp(G)
-    u32x4 tv, mv, ov[NOV];
-    float fv;
-    auto fetch = [&](int n) {
-        const int valid = min(CK, p.L - n * CK);
-        const size_t tok = (size_t)bh * p.L + n * CK;
-        const unsigned char* rec = p.ws + ((size_t)bh * p.NC + n) * WL.bytes;
-        if constexpr (CH) {
-            // the forward's decayed operands (zero past the end of the sequence)
-            ks.load(reinterpret_cast<const E*>(rec + WL.KD), DK, CK, tid);
-            qs.load(reinterpret_cast<const E*>(rec + WL.QG), DK, CK, tid);
-            gs.load(reinterpret_cast<const E*>(rec + WL.KG), DK, CK, tid);
-        } else {
-            ks.load(reinterpret_cast<const E*>(p.k) + tok * DK, DK, valid, tid);
-            qs.load(reinterpret_cast<const E*>(p.q) + tok * DK, DK, valid, tid);
-        }
-        tv = mv = u32x4{0u, 0u, 0u, 0u};
-        if (tid < NRV) {
-            tv = ld16(rec + WL.T + 16 * tid);
-            mv = ld16(rec + WL.M + 16 * tid);
-        }
-        fv = tid < (CH ? DK : 2 * CK + 1) ? reinterpret_cast<const float*>(rec + WL.F)[tid] : 0.f;
-        const E* dog = reinterpret_cast<const E*>(p.dO) + tok * p.DV + v0;
-#pragma unroll
-        for (int j = 0; j < NOV; ++j) {
-            const int x = tid + 128 * j, r = x % CK, c = (x / CK) * VE;
-            ov[j] = (x < CK * PERO && r < valid) ? ld16(dog + (size_t)r * p.DV + c) : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    fetch(p.NC - 1);
-
-    for (int n = p.NC - 1; n >= 0; --n) {
-        // ---- the chunk into LDS; keep dS at the chunk's end
-        if constexpr (CH) {
-            ks.store_plain(Ks, LDK, tid);
-            qs.store_t(Qt, LCK, tid);
-            gs.store_t(Kt, LCK, tid);
-        } else {
-            ks.store(Ks, LDK, Kt, LCK, tid);
-            qs.store(Qs, LDK, Qt, LCK, tid);
-        }
-        if (tid < NRV) {
-            const int r = (VE * tid) / CK, mc0 = (VE * tid) % CK;
-            E te[VE], me[VE];
-            __builtin_memcpy(te, &tv, 16);
-            __builtin_memcpy(me, &mv, 16);
-#pragma unroll
-            for (int j = 0; j < VE; ++j) {
-                const int t = tok_of_col(CK, mc0 + j);
-                Tts[t * LCK + r] = te[j];
-                if constexpr (CH) Pt[t * LCK + r] = me[j];       // the score block, transposed
-                else Ms[r * LF + t] = to_f32(me[j]);
-            }
-        }
-        if (tid < (CH ? DK : 2 * CK + 1)) gam[tid] = fv;   // gamma, D, gamma_C (channel: exp(G_C))
-#pragma unroll
-        for (int j = 0; j < NOV; ++j) {
-            const int x = tid + 128 * j, r = x % CK, c = (x / CK) * VE;
-            if (x < CK * PERO) {
-                E d[VE];
-                __builtin_memcpy(d, &ov[j], 16);
-#pragma unroll
-                for (int i = 0; i < VE; ++i) dOt[(c + i) * LCK + r] = d[i];
-            }
-        }
-        E* dsk = static_cast<E*>(p.dSck) + (((size_t)bh * p.NC + n) * p.DV + i0) * DK;
+    auto own = [&](int n) __attribute__((always_inline)) {
+        BUF_E(Ks, n, b_K); BUF_E(Kt, n, b_Kt); BUF_E(Qt, n, b_Qt); BUF_E(dOt, n, b_dOt);
+        BUF_E(gdOt, n, b_gdOt); BUF_E(Tts, n, b_Tt); BUF_E(Pt, n, b_Pt);
+        const float* gam = reinterpret_cast<const float*>(smem + (n & 1) * LY::bbytes + LY::b_f);
+        const float* Dd = gam + CK;
+        // keep dS at the chunk's end (through the wave's LDS rows, 16 bytes per store)
 #pragma unroll
         for (int jb = 0; jb < NJ; ++jb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * g4 + e, j = 16 * jb + c16;
-                dsk[(size_t)i * DK + j] = from_f32<E>(dS[jb][e]);
-                dSw[i * LDK + j] = from_f32<E>(dS[jb][e]);
-            }
-        if (n > 0) fetch(n - 1);
-        __syncthreads();
-        // (gamma . dO)^T
-        if constexpr (!CH)
-        for (int x = tid; x < CK * kBV; x += 128) {
-            const int r = x % CK, i = x / CK;
-            gdOt[i * LCK + r] = from_f32<E>(gam[r] * to_f32(dOt[i * LCK + r]));
-        }
-        // ---- P = Q K^T . Gamma . M_incl (tiles on or below the diagonal), kept as P^T
-        if constexpr (!CH)
-        for (int tl = w; tl < NB * NB; tl += 2) {
-            const int rb = tl / NB, ib = tl % NB;
-            f32x4 acc = zero4();
-            if (ib <= rb) tmma<E>(acc, Qs, LDK, 16 * rb, Ks, LDK, 16 * ib, DK);
+            for (int e = 0; e < 4; ++e) dSw[(4 * g4 + e) * LDK + 16 * jb + c16] = from_f32<E>(dS[jb][e]);
+        wave_lds_fence();
+        E* dsk = static_cast<E*>(p.dSck) + (((size_t)bh * p.NC + n) * p.DV + i0) * DK;
+        constexpr int RVS = DK / VE;   // 16-byte vectors per dS row
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * g4 + e, s = 16 * ib + c16;
-                Pt[s * LCK + r] = from_f32<E>(acc[e] * Ms[r * LF + s]);
-            }
+        for (int j = 0; j < 16 * RVS / kWave; ++j) {
+            const int v = l + kWave * j, r = v / RVS, c = (v % RVS) * VE;
+            st16(dsk + (size_t)r * DK + c, ld16(dSw + r * LDK + c));
         }
-        __syncthreads();
-        // ---- dU = P^T dO + diag(D) K dS^T  (token r, value channel 16 w + c), kept as dU^T
+        // dU = P^T dO + diag(D) K dS^T  (token r, value channel 16 w + c), kept as dU^T
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb) {
             f32x4 kds = zero4(), y = zero4();
@@ -367,7 +520,7 @@ __global__ __launch_bounds__(128) void chunk_bwd_chain_kernel(BwdParams p)
             }
         }
         wave_lds_fence();
-        // ---- dR = T~^T dU, kept as -gamma dR (transposed)
+        // dR = T~^T dU, kept as -gamma dR (transposed)
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb) {
             f32x4 dr = zero4();
@@ -379,7 +532,7 @@ __global__ __launch_bounds__(128) void chunk_bwd_chain_kernel(BwdParams p)
             }
         }
         wave_lds_fence();
-        // ---- dS <- gamma_C dS + (gamma . dO)^T Q - (gamma . dR)^T K
+        // dS <- gamma_C dS + (gamma . dO)^T Q - (gamma . dR)^T K
         // (channel: dS Diag(exp(G_C)) + dO^T (Q . exp(G)) - dR^T (K . exp(G)))
         const float gC = CH ? 0.f : gam[2 * CK];
 #pragma unroll
@@ -392,9 +545,44 @@ __global__ __launch_bounds__(128) void chunk_bwd_chain_kernel(BwdParams p)
             tmma<E>(acc, dRt, LCK, 0, Kt, LCK, 16 * jb, CK);
             dS[jb] = acc;
         }
-        __syncthreads();   // the LDS is restaged for the previous chunk
+    };
+
+    // One loop per role, each with one barrier per step (so that every wave
+    // meets the same barriers), and one register set per helper: a chunk is
+    // staged before the next one is read into it.  Separate loops keep each
+    // role's prefetched registers apart, so the compiler never has to merge
+    // them (which would wait for the reads in flight).
+    if (w < 2) {
+        __syncthreads();   // the last chunk staged
+        for (int n = p.NC - 1; n >= 0; --n) {
+            own(n);
+            __syncthreads();   // chunk n consumed, chunk n - 1 staged
+        }
+    } else {
+        // The two kinds of helper run loops of their own, for the same reason,
+        // with one register set each: a chunk is staged before the next one
+        // is read into it.  (Two sets, reading chunk n - 2 before staging
+        // chunk n - 1, measured slower.)
+        auto helper = [&](auto kh) __attribute__((always_inline)) {
+            IN in;
+            load(in, p.NC - 1, kh);
+            stage(in, p.NC - 1, kh);
+            if (p.NC >= 2) load(in, p.NC - 2, kh);
+            __syncthreads();
+            // step n: stage chunk n - 1 (read during the previous step), read chunk n - 2
+            for (int n = p.NC - 1; n >= 0; --n) {
+                if (n >= 1) {
+                    stage(in, n - 1, kh);
+                    if (n >= 2) load(in, n - 2, kh);
+                }
+                __syncthreads();
+            }
+        };
+        if (khelp) helper(std::true_type{});
+        else helper(std::false_type{});
     }
-    if (p.dS0) {
+#undef BUF_E
+    if (w < 2 && p.dS0) {
 #pragma unroll
         for (int jb = 0; jb < NJ; ++jb)
 #pragma unroll
@@ -1450,8 +1638,8 @@ static hipError_t launch_bwd_t(const BwdParams& bp, int BH, bool channel, hipStr
     using GC = GradChLds<E, DK, CK>;
     static_assert(CL::bytes <= 160 * 1024 && GL::bytes <= 160 * 1024 && GC::bytes <= 160 * 1024, "LDS budget");
     const int chains = BH * (bp.DV / kBV);
-    hipError_t err = channel ? launch_lds(chunk_bwd_chain_kernel<E, DK, CK, true>, chains, 128, CL::bytes, stream, bp)
-                             : launch_lds(chunk_bwd_chain_kernel<E, DK, CK, false>, chains, 128, CL::bytes, stream, bp);
+    hipError_t err = channel ? launch_lds(chunk_bwd_chain_kernel<E, DK, CK, true>, chains, 384, CL::bytes, stream, bp)
+                             : launch_lds(chunk_bwd_chain_kernel<E, DK, CK, false>, chains, 384, CL::bytes, stream, bp);
     if (err != hipSuccess) return err;
     // persistent, as many workgroups as fit the CUs (the next chunk's inputs
     // are read while the current one is worked on)
