@@ -142,6 +142,23 @@ struct RowStage {
             if (x < ROWS * PER && r < valid) v[j] = ld16(src + (size_t)r * ld + c);
         }
     }
+    // Prefetch form: every read unconditional, from row min(r, valid - 1)
+    // (valid >= 1) and a clamped vector index, so that issuing it never
+    // waits; mask() zeroes the rows past valid once the data is used.
+    __device__ __forceinline__ void prefetch(const E* src, int ld, int valid, int tid) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int x = min(tid + NT * j, ROWS * PER - 1), r = min(x % ROWS, valid - 1), c = (x / ROWS) * VE;
+            v[j] = ld16(src + (size_t)r * ld + c);
+        }
+    }
+    __device__ __forceinline__ void mask(int valid, int tid) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int x = tid + NT * j;
+            if (x % ROWS >= valid) v[j] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
     __device__ __forceinline__ void store(E* dst, int LD, E* dstT, int LT, int tid) const {
         store_plain(dst, LD, tid);
         store_t(dstT, LT, tid);
@@ -683,17 +700,17 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
     // registers while the current chunk is worked on.
     RowStage<E, CK, DK, NT> ks, qs;
     float lav = 0.f, btv = 0.f;
+    // (every read unconditional, from clamped indices: a read under a
+    // condition, or a select on its value, would wait for it right here;
+    // the entries past the chunk's end are zeroed where they are used)
     auto fetch_chunk = [&](int c, int tid) {
         const int n = c % p.NC, valid = min(CK, p.L - n * CK);
         const size_t tok = (size_t)(c / p.NC) * p.L + (size_t)n * CK;
-        ks.load(reinterpret_cast<const E*>(p.k) + tok * DK, DK, valid, tid);
-        qs.load(reinterpret_cast<const E*>(p.q) + tok * DK, DK, valid, tid);
-        lav = 0.f;
-        btv = 0.f;
-        if (tid < valid) {
-            btv = p.beta[tok + tid];
-            if (p.log_alpha) lav = p.log_alpha[tok + tid];
-        }
+        ks.prefetch(reinterpret_cast<const E*>(p.k) + tok * DK, DK, valid, tid);
+        qs.prefetch(reinterpret_cast<const E*>(p.q) + tok * DK, DK, valid, tid);
+        const size_t t = tok + min(tid, valid - 1);
+        btv = p.beta[t];
+        lav = p.log_alpha ? p.log_alpha[t] : 0.f;
     };
     // one block of value channels: S0 and dS_end rows, V and dO columns.
     // Thread x takes row x % kBV, so the transposed stores of a wave are
@@ -710,18 +727,15 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
         const E* dog = reinterpret_cast<const E*>(p.dO) + tok * p.DV;
 #pragma unroll
         for (int u = 0; u < NSV; ++u) {
-            const int xs = tid + NT * u, i = xs % kBV, j = VE * (xs / kBV);
-            if (xs < kBV * DK / VE) {
-                sa[u] = ld16(S0g + (size_t)(v0 + i) * DK + j);
-                sb[u] = ld16(dSg + (size_t)(v0 + i) * DK + j);
-            }
+            const int xs = min(tid + NT * u, kBV * DK / VE - 1), i = xs % kBV, j = VE * (xs / kBV);
+            sa[u] = ld16(S0g + (size_t)(v0 + i) * DK + j);
+            sb[u] = ld16(dSg + (size_t)(v0 + i) * DK + j);
         }
 #pragma unroll
         for (int u = 0; u < NVV; ++u) {
-            const int x = tid + NT * u, r = x % CK, cc = (x / CK) * VE;
-            const bool ok = x < CK * PERV && r < valid;
-            va[u] = ok ? ld16(vg + (size_t)r * p.DV + v0 + cc) : u32x4{0u, 0u, 0u, 0u};
-            da[u] = ok ? ld16(dog + (size_t)r * p.DV + v0 + cc) : u32x4{0u, 0u, 0u, 0u};
+            const int x = min(tid + NT * u, CK * PERV - 1), r = min(x % CK, valid - 1), cc = (x / CK) * VE;
+            va[u] = ld16(vg + (size_t)r * p.DV + v0 + cc);
+            da[u] = ld16(dog + (size_t)r * p.DV + v0 + cc);
         }
     };
     if ((int)blockIdx.x < p.total) {
@@ -737,18 +751,20 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
     const int t0 = n * CK, valid = min(CK, p.L - t0);
     const size_t tok = (size_t)bh * p.L + t0;
 
-    // ---- the chunk's keys, queries and gates
+    // ---- the chunk's keys, queries and gates (zero past the end)
+    ks.mask(valid, tid);
+    qs.mask(valid, tid);
     ks.store(Ks, LDK, Kt, LCK, tid);
     qs.store(Qs, LDK, Qt, LCK, tid);
     for (int x = tid; x < 16 * CK; x += NT) hgp[x] = 0.f;   // hgp and frp
     if (w == 0) {
-        const float g = wave_incl_scan(lav);
+        const float g = wave_incl_scan(l < valid ? lav : 0.f);
         const float gC = __shfl(g, CK - 1, kWave);
         if (l < CK) {
             gs[l] = g;
             gam[l] = __expf(g);
             Dd[l] = __expf(gC - g);
-            bs[l] = btv;
+            bs[l] = l < valid ? btv : 0.f;
         }
     }
     if (nxt < p.total) fetch_chunk(nxt, tid);
@@ -815,8 +831,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
             const int x = tid + NT * u, r = x % CK, c = (x / CK) * VE;
             if (x < CK * PERV) {
                 float a[VE], d[VE];
-                Pack<E>::unpack(va[u], a);
-                Pack<E>::unpack(da[u], d);
+                Pack<E>::unpack(r < valid ? va[u] : u32x4{0u, 0u, 0u, 0u}, a);
+                Pack<E>::unpack(r < valid ? da[u] : u32x4{0u, 0u, 0u, 0u}, d);
 #pragma unroll
                 for (int j = 0; j < VE; ++j) {
                     Vs[r * LBF + c + j] = a[j];
@@ -1171,19 +1187,20 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
         const int n = c % p.NC, valid = min(CK, p.L - n * CK);
         const size_t tok = (size_t)(c / p.NC) * p.L + (size_t)n * CK;
         const unsigned char* rec = p.ws + (size_t)c * WL.bytes;
-        ks.load(reinterpret_cast<const E*>(p.k) + tok * DK, DK, valid, tid);
-        qs.load(reinterpret_cast<const E*>(p.q) + tok * DK, DK, valid, tid);
-        kg.load(reinterpret_cast<const E*>(rec + WL.KG), DK, CK, tid);
-        kd.load(reinterpret_cast<const E*>(rec + WL.KD), DK, CK, tid);
+        // (every read unconditional, from clamped indices: a read under a
+        // condition, or a select on its value, would wait for it right here;
+        // the entries past the chunk's end are zeroed where they are used)
+        ks.prefetch(reinterpret_cast<const E*>(p.k) + tok * DK, DK, valid, tid);
+        qs.prefetch(reinterpret_cast<const E*>(p.q) + tok * DK, DK, valid, tid);
+        kg.prefetch(reinterpret_cast<const E*>(rec + WL.KG), DK, CK, tid);
+        kd.prefetch(reinterpret_cast<const E*>(rec + WL.KD), DK, CK, tid);
 #pragma unroll
         for (int j = 0; j < NLV; ++j) {
-            const int x = tid + NT * j, r = (4 * x) / DK;
-            lv[j] = zero4();
-            if (x < CK * DK / 4 && r < valid)
-                lv[j] = *reinterpret_cast<const f32x4*>(p.log_alpha + (tok + r) * DK + (4 * x) % DK);
+            const int x = min(tid + NT * j, CK * DK / 4 - 1), r = min((4 * x) / DK, valid - 1);
+            lv[j] = *reinterpret_cast<const f32x4*>(p.log_alpha + (tok + r) * DK + (4 * x) % DK);
         }
-        pv = tid < NPV ? ld16(rec + WL.M + 16 * tid) : u32x4{0u, 0u, 0u, 0u};
-        bv = tid < valid ? p.beta[tok + tid] : 0.f;
+        pv = ld16(rec + WL.M + 16 * min(tid, NPV - 1));
+        bv = p.beta[tok + min(tid, valid - 1)];
     };
     // Thread x stages the 16-byte vector (value row x % kBVC, key channels
     // VE (x / kBVC) ..) of S0 and dS_end; its key channels are the same in
@@ -1201,18 +1218,15 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
         const E* dog = reinterpret_cast<const E*>(p.dO) + tok * p.DV;
 #pragma unroll
         for (int u = 0; u < NSV; ++u) {
-            const int xs = tid + NT * u, i = xs % kBVC, j = VE * (xs / kBVC);
-            if (xs < kBVC * DK / VE) {
-                sa[u] = ld16(S0g + (size_t)(v0 + i) * DK + j);
-                sb[u] = ld16(dSg + (size_t)(v0 + i) * DK + j);
-            }
+            const int xs = min(tid + NT * u, kBVC * DK / VE - 1), i = xs % kBVC, j = VE * (xs / kBVC);
+            sa[u] = ld16(S0g + (size_t)(v0 + i) * DK + j);
+            sb[u] = ld16(dSg + (size_t)(v0 + i) * DK + j);
         }
 #pragma unroll
         for (int u = 0; u < NVV; ++u) {
-            const int x = tid + NT * u, r = x % CK, cc = (x / CK) * VE;
-            const bool ok = x < CK * PERV && r < valid;
-            va[u] = ok ? ld16(vg + (size_t)r * p.DV + v0 + cc) : u32x4{0u, 0u, 0u, 0u};
-            da[u] = ok ? ld16(dog + (size_t)r * p.DV + v0 + cc) : u32x4{0u, 0u, 0u, 0u};
+            const int x = min(tid + NT * u, CK * PERV - 1), r = min(x % CK, valid - 1), cc = (x / CK) * VE;
+            va[u] = ld16(vg + (size_t)r * p.DV + v0 + cc);
+            da[u] = ld16(dog + (size_t)r * p.DV + v0 + cc);
         }
     };
     if ((int)blockIdx.x < p.total) {
@@ -1230,6 +1244,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
 
     // ---- keys, queries, the forward's decayed keys, log alpha (floored),
     // beta, and the score block P (masked; columns in tok_of_col order) transposed
+    ks.mask(valid, tid);
+    qs.mask(valid, tid);
     ks.store_plain(Ks, LDK, tid);
     qs.store_plain(Qs, LDK, tid);
     kg.store_plain(Kgs, LDK, tid);
@@ -1245,7 +1261,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
                 fl[r * DK + c + e] = (in && lv[j][e] < kChannelLogAlphaMin) ? 1 : 0;
             }
     }
-    if (tid < CK) bs[tid] = bv;
+    if (tid < CK) bs[tid] = tid < valid ? bv : 0.f;
     if (tid < NPV) {
         const int r = (VE * tid) / CK, mc0 = (VE * tid) % CK;
         E pe[VE];
@@ -1366,8 +1382,9 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
             if (x < CK * PERV) {
                 float a[VE];
                 E d[VE];
-                Pack<E>::unpack(va[u], a);
-                __builtin_memcpy(d, &da[u], 16);
+                const u32x4 dz = r < valid ? da[u] : u32x4{0u, 0u, 0u, 0u};
+                Pack<E>::unpack(r < valid ? va[u] : u32x4{0u, 0u, 0u, 0u}, a);
+                __builtin_memcpy(d, &dz, 16);
 #pragma unroll
                 for (int j = 0; j < VE; ++j) {
                     Vs[r * LBF + c + j] = a[j];
