@@ -122,7 +122,9 @@ hipError_t launch_fwd_varlen(ChunkArgs a)
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     a.vl = Varlen{start, len, choff, a.NS, w.NCmax};
-    if (w.NCmax > 0) {
+    // (no tokens: every sequence is empty and the scan only copies S0; the
+    // prepass reads a token of every slot, so it runs only when there is one)
+    if (w.NCmax > 0 && a.L > 0) {
         err = launch_wy(a, CK);
         if (err != hipSuccess) return err;
     }

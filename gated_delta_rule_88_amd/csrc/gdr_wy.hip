@@ -43,25 +43,33 @@ namespace gdr {
 
 namespace {
 
-// K fragment (ldfrag convention) straight from global memory; rows at or
-// past `valid` read as zero.
+// K fragment (ldfrag convention) straight from global memory.  The read is
+// unconditional, from row min(r, valid - 1) (row 0 when valid = 0): a read
+// under a condition makes the compiler wait for it where the branches join,
+// which would serialise a wave's reads.  gmask() zeroes the rows at or past
+// `valid` once the data is used.
 template <typename E>
 __device__ __forceinline__ Frag<E> gfrag(const E* base, int ld, int row0, int k0, int valid) {
-    const int l = lane_id(), r = row0 + (l & 15);
+    const int l = lane_id(), r = max(min(row0 + (l & 15), valid - 1), 0);
     const E* p = base + (size_t)r * ld + k0 + 8 * (l >> 4);
     Frag<E> f;
     if constexpr (sizeof(E) == 2) {
+        f.v = *reinterpret_cast<const bf16x8*>(p);
+    } else {
+        f.lo = *reinterpret_cast<const f32x4*>(p);
+        f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    return f;
+}
+template <typename E>
+__device__ __forceinline__ void gmask(Frag<E>& f, int row0, int valid) {
+    if (row0 + (lane_id() & 15) < valid) return;
+    if constexpr (sizeof(E) == 2) {
         f.v = bf16x8{};
-        if (r < valid) f.v = *reinterpret_cast<const bf16x8*>(p);
     } else {
         f.lo = zero4();
         f.hi = zero4();
-        if (r < valid) {
-            f.lo = *reinterpret_cast<const f32x4*>(p);
-            f.hi = *reinterpret_cast<const f32x4*>(p + 4);
-        }
     }
-    return f;
 }
 
 // Per-wave LDS scratch of chunk_wy_kernel.
@@ -161,6 +169,10 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
         for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) qf[tb][ks] = gfrag<E>(qc, DK, 16 * tb, 32 * ks, valid);
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) gmask(qf[tb][ks], 16 * tb, valid);
         float iq[NB];
         row_inv_norms<E, NB, NKS>(qf, iq);
         nq = iq[min(g4, NB - 1)];
@@ -174,6 +186,15 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
     for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) kf[tb][ks] = gfrag<E>(kc, DK, 16 * tb, 32 * ks, valid);
+    // beta and log alpha of token l, read with the keys (clamped index; zero
+    // past the end of the sequence below)
+    const int lt = max(min(l, valid - 1), 0);
+    float bt = p.beta[tok + lt];
+    float la = p.log_alpha ? p.log_alpha[tok + lt] : 0.f;
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) gmask(kf[tb][ks], 16 * tb, valid);
     if (pro & kProNorm) {
         float ik[NB];
         row_inv_norms<E, NB, NKS>(kf, ik);
@@ -186,14 +207,14 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
 
     // beta (zero past the end of the sequence) and the cumulative log-decay
     // (log alpha = 0 for alpha = 1)
-    float bt = 0.f, la = 0.f;
     if (l < valid) {
-        bt = p.beta[tok + l];
-        if (p.log_alpha) la = p.log_alpha[tok + l];
         if (pro & kProGates) {
             bt = sigmoid_f(bt);
             if (p.log_alpha) la = log_sigmoid_f(la);
         }
+    } else {
+        bt = 0.f;
+        la = 0.f;
     }
     const float g = wave_incl_scan(la);
     const float glast = __shfl(g, CK - 1, kWave);
@@ -330,23 +351,21 @@ __global__ __launch_bounds__(256, 3) void chunk_wy_channel_kernel(WyParams p)
         const E* kc = reinterpret_cast<const E*>(p.k) + cs.tok * DK;
         const E* qc = reinterpret_cast<const E*>(p.q) + cs.tok * DK;
         const float* lac = p.log_alpha + cs.tok * DK;
+        // every read unconditional, from clamped indices (a conditional read
+        // would make the compiler wait for it here); rows past the end are
+        // zeroed when staged
 #pragma unroll
         for (int j = 0; j < NKV; ++j) {
-            const int i = tid + 256 * j, r = i / RV, c = (i % RV) * VE;
-            kr[j] = u32x4{0u, 0u, 0u, 0u};
-            qr[j] = u32x4{0u, 0u, 0u, 0u};
-            if (i < CK * RV && r < valid) {
-                kr[j] = ld16(kc + (size_t)r * DK + c);
-                qr[j] = ld16(qc + (size_t)r * DK + c);
-            }
+            const int i = min(tid + 256 * j, CK * RV - 1), r = max(min(i / RV, valid - 1), 0), c = (i % RV) * VE;
+            kr[j] = ld16(kc + (size_t)r * DK + c);
+            qr[j] = ld16(qc + (size_t)r * DK + c);
         }
 #pragma unroll
         for (int j = 0; j < NGV; ++j) {
-            const int i = tid + 256 * j, r = i / RF, c = (i % RF) * 4;
-            gr[j] = zero4();
-            if (i < CK * RF && r < valid) gr[j] = *reinterpret_cast<const f32x4*>(lac + (size_t)r * DK + c);
+            const int i = min(tid + 256 * j, CK * RF - 1), r = max(min(i / RF, valid - 1), 0), c = (i % RF) * 4;
+            gr[j] = *reinterpret_cast<const f32x4*>(lac + (size_t)r * DK + c);
         }
-        br = (tid < valid) ? p.beta[cs.tok + tid] : 0.f;
+        br = p.beta[cs.tok + max(min(tid, valid - 1), 0)];
     };
     if ((int)blockIdx.x < p.total) fetch(blockIdx.x);
     for (int cid = blockIdx.x; cid < p.total; cid += gridDim.x) {
@@ -358,6 +377,10 @@ __global__ __launch_bounds__(256, 3) void chunk_wy_channel_kernel(WyParams p)
 #pragma unroll
     for (int j = 0; j < NKV; ++j) {
         const int i = tid + 256 * j, r = i / RV, c = (i % RV) * VE;
+        if (r >= valid) {
+            kr[j] = u32x4{0u, 0u, 0u, 0u};
+            qr[j] = u32x4{0u, 0u, 0u, 0u};
+        }
         if (i < CK * RV) {
             st16(Ks + r * DKP + c, kr[j]);
             st16(Qs + r * DKP + c, qr[j]);
@@ -390,7 +413,7 @@ __global__ __launch_bounds__(256, 3) void chunk_wy_channel_kernel(WyParams p)
     for (int j = 0; j < NGV; ++j) {
         const int i = tid + 256 * j, r = i / RF, c = (i % RF) * 4;
         if (i < CK * RF) {
-            f32x4 x = gr[j];
+            f32x4 x = r < valid ? gr[j] : zero4();
             if (gates && r < valid) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = log_sigmoid_f(x[e]);
@@ -400,7 +423,7 @@ __global__ __launch_bounds__(256, 3) void chunk_wy_channel_kernel(WyParams p)
             *reinterpret_cast<f32x4*>(Gs + r * GP + c) = x;
         }
     }
-    if (tid < CK) bs[tid] = (gates && tid < valid) ? sigmoid_f(br) : br;
+    if (tid < CK) bs[tid] = tid < valid ? (gates ? sigmoid_f(br) : br) : 0.f;
     if (cid + (int)gridDim.x < p.total) fetch(cid + gridDim.x);
     __syncthreads();
     // cumulative sum down each key channel (the column is read whole first,
