@@ -336,16 +336,21 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
         const int oF0 = lane_base(LY::rF);
 
         f32x4 sT[NKT];   // S^T[key 32ks + 8g + 4p + e][v = vw + c16], a = 2ks + p
+        // (one branch around all reads of S0, so that they are in flight together)
+        if (keyrows) {
 #pragma unroll
-        for (int a = 0; a < NKT; ++a) {
-            sT[a] = zero4();
-            if (keyrows) {
+            for (int a = 0; a < NKT; ++a)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     sT[a][e] = (32 * (a >> 1) + 8 * g4 + 4 * (a & 1) + e == vw + c16) ? 1.f : 0.f;
-            } else if (sg == 0 && p.S0)
-                sT[a] = *reinterpret_cast<const f32x4*>(p.S0 + ((size_t)bh * p.DV + vw + c16) * DK +
-                                                       32 * (a >> 1) + 8 * g4 + 4 * (a & 1));
+        } else if (sg == 0 && p.S0) {
+            const float* s0 = p.S0 + ((size_t)bh * p.DV + vw + c16) * DK + 8 * g4;
+#pragma unroll
+            for (int a = 0; a < NKT; ++a)
+                sT[a] = *reinterpret_cast<const f32x4*>(s0 + 32 * (a >> 1) + 4 * (a & 1));
+        } else {
+#pragma unroll
+            for (int a = 0; a < NKT; ++a) sT[a] = zero4();
         }
 
         // operands of one chunk, read from its slot
@@ -512,16 +517,7 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
                 constexpr int J = decltype(jc)::value;
                 const int s = s0 + J;
                 if (s <= NC) {
-                    if (s < NC) {
-                        if (p.Sck) {
-                            // the state entering chunk s, for the backward
-                            E* ck = static_cast<E*>(p.Sck) + (((size_t)bh * p.NC + c0 + s) * p.DV + vw + c16) * DK;
-#pragma unroll
-                            for (int a = 0; a < NKT; ++a)
-                                st4(ck + 32 * (a >> 1) + 8 * g4 + 4 * (a & 1), sT[a][0], sT[a][1], sT[a][2], sT[a][3]);
-                        }
-                        own(jc, s);
-                    }
+                    if (s < NC) own(jc, s);
                     step_barrier();
                 }
             };
@@ -576,6 +572,22 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
             Frag<E> sop[NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) sop[ks] = *reinterpret_cast<const Frag<E>*>(smem + oXS + pS + ks * kWave * FS);
+            if (p.Sck) {
+                // the state entering chunk m, for the backward, from its
+                // published operand (value row vw + c16, key channels
+                // 32 ks + 8 g ..: 16 contiguous bytes of the [d_v][d_k]
+                // state) -- kept off the owners' chain
+                E* ck = static_cast<E*>(p.Sck) + (((size_t)bh * p.NC + c0 + m) * p.DV + vw + c16) * DK + 8 * g4;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    if constexpr (sizeof(E) == 2) {
+                        st16(ck + 32 * ks, __builtin_bit_cast(u32x4, sop[ks].v));
+                    } else {
+                        *reinterpret_cast<f32x4*>(ck + 32 * ks) = sop[ks].lo;
+                        *reinterpret_cast<f32x4*>(ck + 32 * ks + 4) = sop[ks].hi;
+                    }
+                }
+            }
             Frag<E> qf[NB][NKS], kf[NB][NKS];
 #pragma unroll
             for (int tt = 0; tt < NB; ++tt)
