@@ -117,11 +117,38 @@ __device__ __forceinline__ void tmma(f32x4& acc, const TA* A, int lda, int m0, c
     for (int k0 = 0; k0 < K; k0 += 32) mma(acc, cfrag<E>(A, lda, m0, k0, K, l), cfrag<E>(B, ldb, n0, k0, K, l));
 }
 
-// Sum of x over the 16 lanes that share l / 16 (one tile row).
+// Sum of x over the 16 lanes that share l / 16 (one tile row), in every
+// one of them: four DPP moves (swap neighbours, swap pairs, mirror the half
+// rows, mirror the rows), no LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float row16_sum(float x) {
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+    x += dpp_mov<0xB1>(x);    // quad_perm(1, 0, 3, 2)
+    x += dpp_mov<0x4E>(x);    // quad_perm(2, 3, 0, 1)
+    x += dpp_mov<0x141>(x);   // row_half_mirror
+    x += dpp_mov<0x140>(x);   // row_mirror
     return x;
+}
+// Row (over the tile's 16 columns) and column (over its 16 rows) sums of a
+// 16 x 16 tile held as MFMA accumulators (lane (g, c): rows 4 g + e, column
+// c), written to rowp[r] (lanes c = 0) and colp[c] (lanes g = 0).
+template <bool ROWS, bool COLS>
+__device__ __forceinline__ void tile_row_col_sums(const float (&v)[4], float* rowp, float* colp, int g4, int c16) {
+    if constexpr (COLS) {
+        float cs = (v[0] + v[1]) + (v[2] + v[3]);
+        cs += __shfl_xor(cs, 16, kWave);
+        cs += __shfl_xor(cs, 32, kWave);
+        if (g4 == 0) colp[c16] = cs;
+    }
+    if constexpr (ROWS) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float rs = row16_sum(v[e]);
+            if (c16 == 0) rowp[4 * g4 + e] = rs;
+        }
+    }
 }
 
 // Rows of a [ROWS][ld] global array into registers, 16 bytes per read, NT
@@ -629,7 +656,7 @@ struct GradLds : Strides<E, DK, CK> {
     static constexpr int off_Ttt = off_Tt + ECC;
     static constexpr int off_Pt = off_Ttt + ECC;
     static constexpr int off_vec = off_Pt + ECC;               // g, gamma, D, beta, dg [CK]; parts
-    static constexpr int NVEC = 5 * CK + 16 * CK + 8;
+    static constexpr int NVEC = 5 * CK + 16 * CK + 8 + 6 * (CK / 16) * CK;
     // one block of value channels (reused by the last phase)
     static constexpr int off_blk = (off_vec + NVEC * 4 + 15) / 16 * 16;
     static constexpr int off_S0 = off_blk;                     // [kBV][LDK] E and [DK][LBV]
@@ -694,6 +721,15 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
     float* hgp = dg + CK;        // [8][CK] per-wave partial sums of the gamma terms
     float* frp = hgp + 8 * CK;   // [8][CK] per-wave partial sums of the D terms
     float* red = frp + 8 * CK;   // [8]: per-wave <dS_end, S0>
+    // per-tile row ([tile column block][row]) and column ([tile row
+    // block][column]) sums of the C x C terms: dP . P (eR, eC), dA . A (fR,
+    // fC), T . dT~ (tC, columns) and dA . Bm (aR, rows)
+    float* eR = red + 8;
+    float* eC = eR + NB * CK;
+    float* fR = eC + NB * CK;
+    float* fC = fR + NB * CK;
+    float* tC = fC + NB * CK;
+    float* aR = tC + NB * CK;
 
     // Each workgroup walks chunks blockIdx.x, + gridDim.x, ...; the next
     // chunk's keys, queries, gates and first value block are read into
@@ -933,12 +969,10 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
                 dKa[u][e] += dKd[u][e];
             }
 #pragma unroll
-            for (int m = 8; m >= 1; m >>= 1)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    h[e] += __shfl_xor(h[e], m, kWave);
-                    f[e] += __shfl_xor(f[e], m, kWave);
-                }
+            for (int e = 0; e < 4; ++e) {
+                h[e] = row16_sum(h[e]);
+                f[e] = row16_sum(f[e]);
+            }
             if (c16 == 0)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -947,25 +981,28 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
                 }
         }
     }
-    // ---- C x C terms
+    // ---- C x C terms, with the row and column sums of dP . P and T . dT~
     if (w < NCC) {
         const int rb = w / NB, sb = w % NB;
+        float ep[4], tp[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * rb + 4 * g4 + e, s = 16 * sb + c16;
             const float W = r >= s ? __expf(gs[r] - gs[s]) : 0.f;
             dPW[r * LCK + s] = from_f32<E>(dPa[e] * W);
             dPWt[s * LCK + r] = from_f32<E>(dPa[e] * W);
-            Em[r * LF + s] = dPa[e] * Pf[r * LF + s];
-            dTt[r * LF + s] = dTa[e];
+            ep[e] = dPa[e] * Pf[r * LF + s];
+            tp[e] = dTa[e] * Tf[r * LF + s];
             dTb[r * LF + s] = dTa[e] * bs[s];
         }
+        tile_row_col_sums<true, true>(ep, eR + sb * CK + 16 * rb, eC + rb * CK + 16 * sb, g4, c16);
+        tile_row_col_sums<false, true>(tp, nullptr, tC + rb * CK + 16 * sb, g4, c16);
     }
     {
         // <dS_end, S0> over the whole state
-        float x = hS;
-#pragma unroll
-        for (int m = kWave / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+        float x = row16_sum(hS);
+        x += __shfl_xor(x, 16, kWave);
+        x += __shfl_xor(x, 32, kWave);
         if (l == 0) red[w] = x;
     }
     __syncthreads();
@@ -986,28 +1023,26 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
 #pragma unroll
         for (int e = 0; e < 4; ++e) Y1t[(16 * sb + c16) * LF + 16 * rb + 4 * g4 + e] = y[e];
     }
-    // the dg terms of dP . P
-    if (tid < CK) {
-        float a = 0.f;
-        for (int s = 0; s < CK; ++s) a += Em[tid * LF + s] - Em[s * LF + tid];
-        dg[tid] = a;
-    }
     __syncthreads();
     // dA = strictly-lower(-T^T Y1); dG = dA . diag(beta) Gamma; dA . A
     if (w < NCC) {
         const int rb = w / NB, sb = w % NB;
         f32x4 y = zero4();
         tmma<float>(y, Tft, LF, 16 * rb, Y1t, LF, 16 * sb, CK, l);
+        float fp[4], ap[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * rb + 4 * g4 + e, s = 16 * sb + c16;
             const float da = r > s ? -y[e] : 0.f;
             const float dgv = r > s ? da * bs[r] * __expf(gs[r] - gs[s]) : 0.f;
-            dAf[r * LF + s] = da;
             dGf[r * LCK + s] = from_f32<E>(dgv);
             dGt[s * LCK + r] = from_f32<E>(dgv);
-            Em[r * LF + s] = da * Af[r * LF + s];
+            fp[e] = da * Af[r * LF + s];
+            ap[e] = da * Bm[r * LF + s];
         }
+        // row and column sums of dA . A; row sums of dA . Bm
+        tile_row_col_sums<true, true>(fp, fR + sb * CK + 16 * rb, fC + rb * CK + 16 * sb, g4, c16);
+        tile_row_col_sums<true, false>(ap, aR + sb * CK + 16 * rb, nullptr, g4, c16);
     }
     __syncthreads();
     // dK += dG K + dG^T K
@@ -1024,13 +1059,21 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
     if (w == 0) {
         float db = 0.f, dgl = 0.f, fr = 0.f;
         if (l < CK) {
-            for (int u = 0; u < CK; ++u) db += Tft[l * LF + u] * dTt[u * LF + l];
-            for (int s = 0; s < CK; ++s) db += dAf[l * LF + s] * Bm[l * LF + s];
-            float fa = 0.f, hg = 0.f;
-            for (int s = 0; s < CK; ++s) fa += Em[l * LF + s] - Em[s * LF + l];
-            for (int x = 0; x < NW; ++x) fr += frp[x * CK + l];
-            for (int x = 0; x < 8; ++x) hg += hgp[x * CK + l];
-            dgl = dg[l] + fa + hg - fr;
+            // dbeta_t = sum_u T_ut dT~_ut + sum_s dA_ts Bm_ts; the dg terms of
+            // dP . P and dA . A (rows minus columns), the gamma and D terms
+            float ea = 0.f, fa = 0.f, hg = 0.f;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                db += tC[b * CK + l] + aR[b * CK + l];
+                ea += eR[b * CK + l] - eC[b * CK + l];
+                fa += fR[b * CK + l] - fC[b * CK + l];
+            }
+#pragma unroll
+            for (int x = 0; x < NW; ++x) {
+                fr += frp[x * CK + l];
+                hg += hgp[x * CK + l];
+            }
+            dgl = ea + fa + hg - fr;
         }
         // g_C enters gamma_C S0 and every D_r = e^{g_C - g_r}
         float fsum = fr;
