@@ -1152,8 +1152,8 @@ struct GradChLds : Strides<E, DK, CK> {
     static constexpr int off_Tt = off_Tft + FCC;               // [CK][LCK] E
     static constexpr int off_Ttt = off_Tt + ECC;
     static constexpr int off_Pt = off_Ttt + ECC;
-    static constexpr int off_vec = off_Pt + ECC;               // beta [CK], <dS, S0> per channel [DK]
-    static constexpr int NVEC = CK + DK;
+    static constexpr int off_vec = off_Pt + ECC;               // beta [CK], <dS, S0> per channel [DK],
+    static constexpr int NVEC = CK + DK + 2 * (CK / 16) * CK;  //   tile sums for dbeta [2][NB][CK]
     static constexpr int off_fl = off_vec + NVEC * 4;          // [CK][DK] bytes: log alpha below the floor
     static constexpr int off_blk = (off_fl + CK * DK + 15) / 16 * 16;
     // one block of kBVC value channels
@@ -1215,6 +1215,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
 #undef GL_F
     float* bs = reinterpret_cast<float*>(smem + LY::off_vec);
     float* hC = bs + CK;                     // <dS_end, S0> per key channel
+    float* tC = hC + DK;                     // column sums of T . dT~ per tile row block
+    float* aR = tC + NB * CK;                // row sums of dA . Bm per tile column block
     unsigned char* fl = smem + LY::off_fl;   // 1 where log alpha is below the floor
 
     // Each workgroup walks chunks blockIdx.x, + gridDim.x, ...; the next
@@ -1504,12 +1506,14 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
     // <dS_end, S0> per key channel: the kBVC threads that staged the same
     // key channels are the 32 lanes of one half wave (all sums reduced side
     // by side)
+    static_assert(kBVC == 32, "a half wave: 16-lane rows, then across the two rows");
 #pragma unroll
-    for (int m = kBVC / 2; m >= 1; m >>= 1)
+    for (int u = 0; u < NSV; ++u)
 #pragma unroll
-        for (int u = 0; u < NSV; ++u)
-#pragma unroll
-            for (int e = 0; e < VE; ++e) hacc[u][e] += __shfl_xor(hacc[u][e], m, kWave);
+        for (int e = 0; e < VE; ++e) {
+            hacc[u][e] = row16_sum(hacc[u][e]);
+            hacc[u][e] += __shfl_xor(hacc[u][e], 16, kWave);
+        }
 #pragma unroll
     for (int u = 0; u < NSV; ++u) {
         const int xs = tid + NT * u, j = VE * (xs / kBVC);
@@ -1521,15 +1525,17 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
     // ---- triangular part: dPM, dT~; dA = strictly-lower(-T^T dT~ diag(beta) T^T)
     if (w < NCC) {
         const int rb = w / NB, sb = w % NB;
+        float tp[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * rb + 4 * g4 + e, s2 = 16 * sb + c16;
             const float dpm = r >= s2 ? dPa[e] : 0.f;
             dPM[r * LCK + s2] = from_f32<E>(dpm);
             dPMt[s2 * LCK + r] = from_f32<E>(dpm);
-            dTt[r * LF + s2] = dTa[e];
             dTb[r * LF + s2] = dTa[e] * bs[s2];
+            tp[e] = dTa[e] * Tf[r * LF + s2];
         }
+        tile_row_col_sums<false, true>(tp, nullptr, tC + rb * CK + 16 * sb, g4, c16);
     }
     __syncthreads();
     if (w < NCC) {
@@ -1544,20 +1550,23 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
         const int rb = w / NB, sb = w % NB;
         f32x4 y = zero4();
         tmma<float>(y, Tft, LF, 16 * rb, Y1t, LF, 16 * sb, CK, l);
+        float ap[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * rb + 4 * g4 + e, s2 = 16 * sb + c16;
             const float da = r > s2 ? -y[e] : 0.f;
-            dAf[r * LF + s2] = da;
             dAb[r * LCK + s2] = from_f32<E>(da * bs[r]);
             dAbt[s2 * LCK + r] = from_f32<E>(da * bs[r]);
+            ap[e] = da * Bm[r * LF + s2];
         }
+        tile_row_col_sums<true, false>(ap, aR + sb * CK + 16 * rb, nullptr, g4, c16);
     }
     __syncthreads();
+    // dbeta_t = sum_u T_ut dT~_ut + sum_s dA_ts Bm_ts
     if (w == 0 && l < valid) {
         float db = 0.f;
-        for (int u = 0; u < CK; ++u) db += Tf[u * LF + l] * dTt[u * LF + l];
-        for (int s2 = 0; s2 < CK; ++s2) db += dAf[l * LF + s2] * Bm[l * LF + s2];
+#pragma unroll
+        for (int b2 = 0; b2 < NB; ++b2) db += tC[b2 * CK + l] + aR[b2 * CK + l];
         p.dbeta[tok + l] = db;
     }
 
