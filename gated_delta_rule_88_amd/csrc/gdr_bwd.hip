@@ -1723,9 +1723,9 @@ static hipError_t launch_bwd_t(const BwdParams& bp, int BH, bool channel, hipStr
 }  // namespace
 
 // Workspace of the backward: the forward's chunk records, the state entering
-// every chunk, dS at every chunk's end, and the recomputed outputs.
+// every chunk and dS at every chunk's end.
 struct BwdWs {
-    size_t off_Sck, off_dSck, off_o, bytes;
+    size_t off_Sck, off_dSck, bytes;
 };
 
 static BwdWs bwd_ws(int B, int H, int L, int dk, int dv, int C, int dtype, int mode)
@@ -1738,7 +1738,6 @@ static BwdWs bwd_ws(int B, int H, int L, int dk, int dv, int C, int dtype, int m
     size_t o = al(BH * NC * (size_t)ws_layout(es, dk, CK, mode).bytes);
     w.off_Sck = o; o = al(o + BH * NC * dv * dk * es);
     w.off_dSck = o; o = al(o + BH * NC * dv * dk * es);
-    w.off_o = o; o = al(o + BH * (size_t)L * dv * es);
     w.bytes = o;
     return w;
 }
@@ -1773,7 +1772,7 @@ hipError_t launch_bwd_chunked(const BwdArgs& b)
     unsigned char* ws = static_cast<unsigned char*>(b.workspace);
     // forward again: the prepass records and every chunk's entry state
     ChunkArgs a{b.B, b.H, b.L, b.dk, b.dv, b.C, b.dtype, b.mode, b.q, b.k, b.v, b.beta, b.log_alpha, b.S0,
-                ws + w.off_o, nullptr, ws, b.stream, 0u, nullptr, 0, Varlen{}, ws + w.off_Sck};
+                nullptr, nullptr, ws, b.stream, 0u, nullptr, 0, Varlen{}, ws + w.off_Sck};
     hipError_t err = launch_wy(a, CK);
     if (err != hipSuccess) return err;
     SegPlan one{1, NC, 0, 0, 0, 0, 0};

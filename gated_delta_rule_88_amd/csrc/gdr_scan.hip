@@ -545,7 +545,10 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
         const int c = w - 2, vw = v0 + 16 * c;
         // key rows write (transition so far) q_t, d_k per token, to p.qt
         const int ostride = keyrows ? DK : p.DV;
-        E* og = (keyrows ? reinterpret_cast<E*>(p.qt) : reinterpret_cast<E*>(p.o)) + tok0 * ostride;
+        // (no output array: the backward's recomputation, which keeps only the
+        // states entering the chunks)
+        E* const ob = keyrows ? reinterpret_cast<E*>(p.qt) : reinterpret_cast<E*>(p.o);
+        E* og = ob ? ob + tok0 * ostride : nullptr;
         const int oXS = lane_base(LY::rxS + (c * NKS * kWave + l) * FS);
         const int oXU = lane_base(LY::rxU + (c * kWave + l) * FS);
         // Gamma tile (rb, ib): row c16 (+16 rb), tokens 16ib + 4g .. +3
@@ -588,6 +591,7 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
                     }
                 }
             }
+            if (!og) return;   // states only
             Frag<E> qf[NB][NKS], kf[NB][NKS];
 #pragma unroll
             for (int tt = 0; tt < NB; ++tt)

@@ -169,10 +169,10 @@ int gdr_fwd_chunked_ex(int B, int H, int L, int d_k, int d_v, int C, int dtype,
 
 /*
  * Bytes of device workspace gdr_bwd_chunked needs (0 when B * H == 0 or
- * L == 0), or (size_t)-1 for invalid or unsupported sizes.  It holds the forward's chunk records, the state entering every
- * chunk and the state gradient at every chunk's end (d_v x d_k per chunk
- * each, in the dtype of q, chunks of 32 tokens, or 16 for GDR_F32 or
- * C == 16) and the recomputed outputs.
+ * L == 0), or (size_t)-1 for invalid or unsupported sizes.  It holds the
+ * forward's chunk records, the state entering every chunk and the state
+ * gradient at every chunk's end (d_v x d_k per chunk each, in the dtype of
+ * q, chunks of 32 tokens, or 16 for GDR_F32 or C == 16).
  */
 size_t gdr_bwd_chunked_workspace_size(int B, int H, int L, int d_k, int d_v, int C,
                                       int dtype, int alpha_mode);
