@@ -131,6 +131,28 @@ __device__ __forceinline__ float row16_sum(float x) {
     x += dpp_mov<0x140>(x);   // row_mirror
     return x;
 }
+
+// Lanes l and l ^ 1 hold the bf16 entries c .. c + 7 of rows r and r ^ 1,
+// packed in v.  Stores them transposed, dst[(c + j) * LT + r], as 4-byte words
+// that hold both rows: the two lanes trade halves (a DPP swap of neighbouring
+// lanes), then the even lane writes columns c .. c + 3 and the odd lane
+// c + 4 .. c + 7 -- half the stores of 2-byte writes, and no two lanes write
+// into one word.  Both lanes of a pair must be active; LT is even.
+__device__ __forceinline__ void store_t_pair(bf16* dst, int LT, int r, int c, u32x4 v, int l) {
+    const bool odd = l & 1;
+    const uint32_t s0 = odd ? v.x : v.z, s1 = odd ? v.y : v.w;   // for the partner
+    const uint32_t m0 = odd ? v.z : v.x, m1 = odd ? v.w : v.y;   // kept
+    const uint32_t p0 = __builtin_amdgcn_mov_dpp((int)s0, 0xB1, 0xF, 0xF, false);   // quad_perm(1, 0, 3, 2)
+    const uint32_t p1 = __builtin_amdgcn_mov_dpp((int)s1, 0xB1, 0xF, 0xF, false);
+    const uint32_t a0 = odd ? p0 : m0, a1 = odd ? p1 : m1;   // row r & ~1
+    const uint32_t b0 = odd ? m0 : p0, b1 = odd ? m1 : p1;   // row r | 1
+    uint32_t* d = reinterpret_cast<uint32_t*>(dst + (c + (odd ? 4 : 0)) * LT + (r & ~1));
+    const int ld = LT / 2;
+    d[0] = (a0 & 0xffffu) | (b0 << 16);
+    d[ld] = (a0 >> 16) | (b0 & 0xffff0000u);
+    d[2 * ld] = (a1 & 0xffffu) | (b1 << 16);
+    d[3 * ld] = (a1 >> 16) | (b1 & 0xffff0000u);
+}
 // Row (over the tile's 16 columns) and column (over its 16 rows) sums of a
 // 16 x 16 tile held as MFMA accumulators (lane (g, c): rows 4 g + e, column
 // c), written to rowp[r] (lanes c = 0) and colp[c] (lanes g = 0).
@@ -198,6 +220,15 @@ struct RowStage {
         }
     }
     __device__ __forceinline__ void store_t(E* dstT, int LT, int tid) const {
+        if constexpr (sizeof(E) == 2 && ROWS % 2 == 0 && NT % 2 == 0) {
+            // threads tid, tid ^ 1 hold rows r, r ^ 1 of the same columns
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                const int x = tid + NT * j, r = x % ROWS, c = (x / ROWS) * VE;
+                if (x < ROWS * PER) store_t_pair(dstT, LT, r, c, v[j], tid);
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             const int x = tid + NT * j, r = x % ROWS, c = (x / ROWS) * VE;
@@ -321,6 +352,13 @@ struct RowFrags {
     }
     __device__ __forceinline__ void store_t(E* dstT, int LT, int r0, int l) const {
         const int r = r0 + (l & 15), k = 8 * (l >> 4);
+        if constexpr (sizeof(E) == 2) {
+            // lanes l, l ^ 1 hold rows r, r ^ 1 of the same key channels
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                store_t_pair(dstT, LT, r, 32 * ks + k, __builtin_bit_cast(u32x4, f[ks].v), l);
+            return;
+        }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             E e[8];
@@ -506,15 +544,28 @@ __global__ __launch_bounds__(384, 1) void chunk_bwd_chain_kernel(BwdParams p)
             if (x < NFV) f[x] = in.fv;   // gamma, D, gamma_C (channel: exp(G_C))
             if (x < CK * PERO) {
                 const int r = x % CK, c = (x / CK) * VE;
-                E d[VE];
-                __builtin_memcpy(d, &in.ov, 16);
-                if (r >= tvalid)
+                if constexpr (sizeof(E) == 2) {
+                    // lanes l, l ^ 1 hold tokens r, r ^ 1 of the same value channels
+                    const u32x4 dv = r < tvalid ? in.ov : u32x4{0u, 0u, 0u, 0u};
+                    store_t_pair(dOt, LCK, r, c, dv, l);
+                    if constexpr (!CH) {
+                        float d[VE];
+                        Pack<bf16>::unpack(dv, d);
 #pragma unroll
-                    for (int i = 0; i < VE; ++i) d[i] = from_f32<E>(0.f);
+                        for (int i = 0; i < VE; ++i) d[i] *= in.gv;
+                        store_t_pair(gdOt, LCK, r, c, Pack<bf16>::pack(d), l);
+                    }
+                } else {
+                    E d[VE];
+                    __builtin_memcpy(d, &in.ov, 16);
+                    if (r >= tvalid)
 #pragma unroll
-                for (int i = 0; i < VE; ++i) {
-                    dOt[(c + i) * LCK + r] = d[i];
-                    if constexpr (!CH) gdOt[(c + i) * LCK + r] = from_f32<E>(in.gv * to_f32(d[i]));
+                        for (int i = 0; i < VE; ++i) d[i] = from_f32<E>(0.f);
+#pragma unroll
+                    for (int i = 0; i < VE; ++i) {
+                        dOt[(c + i) * LCK + r] = d[i];
+                        if constexpr (!CH) gdOt[(c + i) * LCK + r] = from_f32<E>(in.gv * to_f32(d[i]));
+                    }
                 }
             }
         }
@@ -606,7 +657,8 @@ __global__ __launch_bounds__(384, 1) void chunk_bwd_chain_kernel(BwdParams p)
         // The two kinds of helper run loops of their own, for the same reason,
         // with one register set each: a chunk is staged before the next one
         // is read into it.  (Two sets, reading chunk n - 2 before staging
-        // chunk n - 1, measured slower.)
+        // chunk n - 1, measured slower; two sets read two steps ahead of
+        // staging, no faster.)
         auto helper = [&](auto kh) __attribute__((always_inline)) {
             IN in;
             load(in, p.NC - 1, kh);
