@@ -113,7 +113,11 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         ns.y = s[u].y * a[1] + ui * kk[1];
         ns.z = s[u].z * a[2] + ui * kk[2];
         ns.w = s[u].w * a[3] + ui * kk[3];
-        *reinterpret_cast<float4*>(S + ((size_t)head * DV + row[u]) * DK + 4 * c) = ns;
+        // the new state is not read again in this step: a non-temporal store
+        // (measured 3 % faster per step than a plain one; non-temporal reads
+        // of the state were 12 % slower)
+        __builtin_nontemporal_store(f32x4{ns.x, ns.y, ns.z, ns.w},
+                                    reinterpret_cast<f32x4*>(S + ((size_t)head * DV + row[u]) * DK + 4 * c));
         if (c == 0) o[(size_t)head * DV + row[u]] = from_f32<T>(sq + ui * kq);
     }
 }
