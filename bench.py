@@ -2,15 +2,21 @@
 
 Default workload (the headline): Gated DeltaNet chunked forward, bf16
 inputs, fp32 state, B=8, H=8, L=2048, d_k=d_v=128, C=64.  One step is one
-gdr_fwd_chunked call over one batch (all of its kernels).  A second leg
-times the single-token decode step on 256 sequences x 16 heads (d=128,
-fp32 state of 512 MiB), 1024 consecutive steps, and reports its HBM rate.
+gdr_fwd_chunked call over one batch (all of its kernels).  Further legs of
+the default run, each reported in its own sub-object: the channel-gate
+(Kimi-style) forward at B=4, H=16, L=4096 ("kda"); the fixed-token
+sequence-length sweep, 65,536 tokens x 16 heads at (B, L) = (32, 2048),
+(8, 8192), (2, 32768), (1, 65536) ("sweep": time per call vs L); and the
+single-token decode step on 256 sequences x 16 heads (d=128, fp32 state of
+512 MiB) over 1024 consecutive steps, with its HBM rate ("decode").
 
-Inputs are resident in HBM before timing starts.  The chunked leg rotates
-over several input copies so its ~140 MB working set is not served from the
-256 MB Infinity Cache.  Kernel durations come from HIP events on the stream
-the library launches on.  The CPU baseline runs the fp64 oracle on a
-bounded sample of the same workload on the host cores.
+Inputs are drawn on the GPU and resident in HBM before timing starts.  The
+chunked legs rotate over several input copies so a working set is not
+served from the 256 MB Infinity Cache.  Every rate of a chunked leg comes
+from one timing: HIP events around K back-to-back calls on the stream the
+library launches on, divided by K.  The CPU baseline runs the fp64 oracle
+on a bounded sample of the headline workload on the host cores, and on
+one thread.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line.
@@ -75,20 +81,20 @@ def measured_traffic(workload: str, kernel: str):
 WORKLOADS = {w.name: w for w in (gi.DELTANET_FP32, gi.GDN_BF16, gi.KDA_BF16, *gi.GDN_SWEEP)}
 
 
-def chunked_algorithmic(w: gi.ChunkedWorkload) -> tuple[float, float]:
+def chunked_algorithmic(w: gi.ChunkedWorkload, step: int) -> tuple[float, float]:
     """(bytes, flops) the method itself must move and compute for one call.
 
     Bytes per head-token: q, k, v read and o written in the input dtype,
     beta and log alpha read (4 B each, or 4 d_k B for channel gates).  Bytes
     per (b, h): the final state written (4 d_k d_v).  Flops per head-token
-    on the triangular count with C = chunk: 5 C d + 3 d + 6 d^2 + C^2 / 3
-    (d = d_k = d_v; 1 FMA = 2 flops)."""
+    on the triangular count with C = the token step the kernels execute:
+    5 C d + 3 d + 6 d^2 + C^2 / 3 (d = d_k = d_v; 1 FMA = 2 flops)."""
     es = 2 if w.dtype == torch.bfloat16 else 4
     ht = w.B * w.H * w.L
     gate = 0 if w.mode == gi.ALPHA_NONE else (4 if w.mode == gi.ALPHA_SCALAR else 4 * w.dk)
     per_tok = es * (2 * w.dk + 2 * w.dv) + 4 + gate
     state = 4 * w.dk * w.dv * (w.B * w.H) * (2 if w.s0_std > 0 else 1)
-    d, C = w.dk, w.C
+    d, C = w.dk, step
     flops = ht * (5 * C * d + 3 * d + 6 * d * d + C * C / 3)
     return float(ht * per_tok + state), float(flops)
 
@@ -142,8 +148,10 @@ def bench_chunked(w, steps, warmup, copies, prologue=0):
             x = gi.raw_inputs((w.B, w.H), w.L, w.dk, w.dv, w.dtype, w.mode, w.seed + 1000 * c,
                               w.s0_std, raw_qk=bool(prologue & 1), raw_gates=bool(prologue & 2))
         else:
+            # drawn on the GPU: the same recipe, without minutes of host-side
+            # drawing for the larger workloads
             x = gi.chunked_inputs(w.B, w.H, w.L, w.dk, w.dv, w.dtype, w.mode,
-                                  w.seed + 1000 * c, w.s0_std)
+                                  w.seed + 1000 * c, w.s0_std, device=dev)
         sets.append({k: (None if t is None else t.to(dev)) for k, t in x.items()})
     mode = w.mode
     code = gdr.GDR_BF16 if w.dtype == torch.bfloat16 else gdr.GDR_F32
@@ -167,7 +175,8 @@ def bench_chunked(w, steps, warmup, copies, prologue=0):
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
-    # whole-job timing: K steps bracketed by synchronisations
+    # whole-job timing: K calls back to back, HIP events on the stream the
+    # library launches on (the current stream), bracketed by synchronisations
     t0 = time.perf_counter()
     e0, e1 = _events(2)
     e0.record()
@@ -177,7 +186,8 @@ def bench_chunked(w, steps, warmup, copies, prologue=0):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = e0.elapsed_time(e1)
-    # per-call durations (HIP events around each call on the library's stream)
+    # for reference: durations of calls timed one at a time (an event pair
+    # around each call), which include the gap an event inserts
     n_each = min(steps, 50)
     ev = _events(2 * n_each)
     for i in range(n_each):
@@ -186,8 +196,9 @@ def bench_chunked(w, steps, warmup, copies, prologue=0):
         ev[2 * i + 1].record()
     torch.cuda.synchronize()
     per_call = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n_each))
-    return dict(total_ms=total_ms, wall_s=wall, call_ms_mean=sum(per_call) / n_each,
-                call_ms_median=per_call[n_each // 2])
+    del sets, outs, finals, wss, calls
+    return dict(total_ms=total_ms, wall_s=wall, call_ms=total_ms / steps,
+                isolated_ms_mean=sum(per_call) / n_each, isolated_ms_median=per_call[n_each // 2])
 
 
 def bench_varlen(w, steps, warmup, copies):
@@ -300,30 +311,95 @@ def bench_decode(w, steps, prologue=0):
     return dict(total_ms=total_ms, step_ms=total_ms / steps, finite=ok)
 
 
-def cpu_baseline(w, chains: int, min_seconds: float):
+def _host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, chains: int, min_seconds: float, single_seconds: float):
     """fp64 oracle on the first `chains` (b, h) chains of the workload, on all
-    host threads, repeated until `min_seconds` have passed; scaled to the whole
-    workload's tokens/s."""
+    the host threads OpenMP is given, repeated until `min_seconds` have
+    passed; then on one thread over two chains for `single_seconds`.  Both
+    are tokens/s of the chains run (a chain's tokens count once per head, as
+    the workload's tokens/s does)."""
     import oracle
 
     x = gi.workload_inputs(w)
     bh = w.B * w.H
     chains = min(chains, bh)
-    flat = lambda t: None if t is None else t.reshape((bh,) + tuple(t.shape[2:]))[:chains]
-    args = [flat(x[k]) for k in ("q", "k", "v", "beta", "log_alpha", "S0")]
+    flat = lambda t, n: None if t is None else t.reshape((bh,) + tuple(t.shape[2:]))[:n]
+
+    def timed(n, threads, seconds):
+        args = [flat(x[k], n) for k in ("q", "k", "v", "beta", "log_alpha", "S0")]
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.run(*args, mode=w.mode, nthreads=threads)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= seconds:
+                break
+        return w.tokens * n / bh * reps / dt, reps, dt
+
     threads = oracle.max_threads()
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.run(*args, mode=w.mode, nthreads=threads)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    tokens = w.tokens * chains / bh * reps
-    return dict(value=tokens / dt, unit="tokens/s", cores=threads, kind="oracle",
+    value, reps, dt = timed(chains, threads, min_seconds)
+    one, reps1, dt1 = timed(min(2, bh), 1, single_seconds)
+    return dict(value=value, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"{chains} of {bh} (batch, head) chains at full L={w.L}, run {reps} times: "
-                       f"{dt:.1f} s wall on {threads} threads; tokens/s of those chains")
+                       f"{dt:.1f} s wall on {threads} threads; tokens/s of those chains scaled "
+                       f"to the workload's {w.tokens} tokens per call",
+                single_thread=dict(value=one, unit="tokens/s", cores=1,
+                                   sample=f"{min(2, bh)} chains, run {reps1} times: {dt1:.1f} s on "
+                                          "one thread"),
+                nproc=os.cpu_count(), host_cpu=_host_cpu_model())
+
+
+def sweep_leg(steps: int, warmup: int):
+    """The fixed-token sequence-length sweep (65,536 tokens x 16 heads per
+    call): time per call vs L, one line per (B, L) point."""
+    import gated_delta_rule_88_amd as gdr
+
+    pts = []
+    for w in gi.GDN_SWEEP:
+        r = bench_chunked(w, steps, warmup, 2)
+        step = gdr.gdr_fwd_chunked_token_step(w.C, gdr.GDR_BF16, w.mode)
+        nbytes, flops = chunked_algorithmic(w, step)
+        call_s = r["call_ms"] / 1e3
+        pts.append({"workload": w.name, "B": w.B, "L": w.L, "us_per_call": r["call_ms"] * 1e3,
+                    "tokens_per_s": w.tokens / call_s, "hbm_frac": nbytes / call_s / 1e9 / HBM_PEAK_GBS,
+                    "mfma_frac": flops / call_s / 1e12 / BF16_PEAK_TFLOPS, "token_step": step})
+        torch.cuda.empty_cache()
+    return pts
+
+
+def chunked_summary(w, r, step, prologue=0):
+    """Throughput and roofline of one chunked workload from one timing (the
+    back-to-back per-call time of bench_chunked)."""
+    nbytes, flops = chunked_algorithmic(w, step)
+    call_s = r["call_ms"] / 1e3
+    gbs = nbytes / call_s / 1e9
+    tflops = flops / call_s / 1e12
+    mfma_peak = BF16_PEAK_TFLOPS if w.dtype == torch.bfloat16 else FP32_PEAK_TFLOPS
+    return {
+        "tokens_per_s": w.tokens / call_s,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": (None if prologue else
+                                 measured_traffic(w.name, chunked_kernel_name(w))),
+                     "kernel": chunked_kernel_name(w),
+                     "algorithmic_bytes_per_call": nbytes,
+                     "call_ms": r["call_ms"],
+                     "isolated_call_ms_mean": r["isolated_ms_mean"]},
+        "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s",
+                 "frac": tflops / mfma_peak, "algorithmic_flops_per_call": flops,
+                 "count": f"triangular, at the executed {step}-token step"},
+    }
 
 
 def main():
@@ -339,7 +415,10 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-chains", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-single-seconds", type=float, default=4.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the channel-gate and sequence-length-sweep legs of the default run")
     ap.add_argument("--backward", action="store_true",
                     help="time the chunked backward (gradients) on --workload instead (one JSON "
                          "line of its own)")
@@ -414,17 +493,17 @@ def main():
                          "algorithmic_bytes_per_call": vb},
         }))
         return
+    import gated_delta_rule_88_amd as gdr
+
     w = WORKLOADS[args.workload]
+    code = gdr.GDR_BF16 if w.dtype == torch.bfloat16 else gdr.GDR_F32
+    step = gdr.gdr_fwd_chunked_token_step(w.C, code, w.mode)
     r = bench_chunked(w, args.steps, args.warmup, args.copies, args.prologue)
-    nbytes, flops = chunked_algorithmic(w)
-    call_s = r["call_ms_mean"] / 1e3
-    gbs = nbytes / call_s / 1e9
-    tflops = flops / call_s / 1e12
-    mfma_peak = BF16_PEAK_TFLOPS if w.dtype == torch.bfloat16 else FP32_PEAK_TFLOPS
-    ms_step = r["total_ms"] / args.steps
+    summ = chunked_summary(w, r, step, args.prologue)
+    ms_step = r["call_ms"]
     out = {
         "metric": METRIC,
-        "value": w.tokens / (ms_step / 1e3),
+        "value": summ["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -436,19 +515,21 @@ def main():
         "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d_k": w.dk, "d_v": w.dv,
-                   "C": w.C, "alpha": gi.MODE_NAMES[w.mode], "input_copies": args.copies,
-                   "prologue": args.prologue},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": (None if args.prologue else
-                                 measured_traffic(w.name, chunked_kernel_name(w))),
-                     "kernel": chunked_kernel_name(w),
-                     "algorithmic_bytes_per_call": nbytes,
-                     "call_ms_mean": r["call_ms_mean"], "call_ms_median": r["call_ms_median"]},
-        "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s",
-                 "frac": tflops / mfma_peak, "algorithmic_flops_per_call": flops,
-                 "count": "triangular"},
+                   "C": w.C, "token_step": step, "alpha": gi.MODE_NAMES[w.mode],
+                   "input_copies": args.copies, "prologue": args.prologue},
+        "roofline": summ["roofline"],
+        "mfma": summ["mfma"],
     }
+    torch.cuda.empty_cache()
+    if not args.no_legs and args.workload == gi.GDN_BF16.name and not args.prologue:
+        kw = gi.KDA_BF16
+        kstep = gdr.gdr_fwd_chunked_token_step(kw.C, gdr.GDR_BF16, kw.mode)
+        kr = bench_chunked(kw, max(args.steps // 4, 20), max(args.warmup // 4, 20), 2)
+        ks = chunked_summary(kw, kr, kstep)
+        out["kda"] = {"workload": kw.name, "token_step": kstep, "ms_per_call": kr["call_ms"],
+                      **ks}
+        torch.cuda.empty_cache()
+        out["sweep"] = sweep_leg(max(args.steps // 10, 10), max(args.warmup // 10, 10))
     if not args.no_decode:
         dw = gi.DECODE_BF16
         dr = bench_decode(dw, args.decode_steps, args.prologue)
@@ -465,7 +546,8 @@ def main():
             "state_finite": dr["finite"],
         }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_chains, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_chains, args.cpu_seconds,
+                                           args.cpu_single_seconds)
     print(json.dumps(out))
 
 

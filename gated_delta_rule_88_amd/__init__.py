@@ -36,6 +36,7 @@ GDR_PRO_L2NORM_QK, GDR_PRO_GATES = 1, 2
 _SIZE_MAX = ctypes.c_size_t(-1).value
 
 EXPORTED = ("gdr_abi_version", "gdr_status_string", "gdr_fwd_chunked_workspace_size",
+            "gdr_fwd_chunked_token_step",
             "gdr_fwd_chunked", "gdr_fwd_chunked_ex", "gdr_fwd_varlen_workspace_size",
             "gdr_fwd_varlen", "gdr_bwd_chunked_workspace_size", "gdr_bwd_chunked",
             "gdr_decode_step", "gdr_decode_step_ex")
@@ -64,6 +65,8 @@ def load_library():
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_fwd_chunked_workspace_size.argtypes = [i] * 8
     lib.gdr_fwd_chunked_workspace_size.restype = sz
+    lib.gdr_fwd_chunked_token_step.argtypes = [i] * 3
+    lib.gdr_fwd_chunked_token_step.restype = i
     lib.gdr_fwd_chunked.argtypes = [i] * 7 + [vp] * 4 + [i] + [vp] * 5 + [sz, vp]
     lib.gdr_fwd_chunked.restype = i
     lib.gdr_fwd_chunked_ex.argtypes = lib.gdr_fwd_chunked.argtypes + [ctypes.c_uint]
@@ -91,6 +94,12 @@ def gdr_abi_version() -> int:
 
 def gdr_status_string(status: int) -> str:
     return load_library().gdr_status_string(int(status)).decode()
+
+
+def gdr_fwd_chunked_token_step(C: int, dtype: int, alpha_mode: int) -> int:
+    """Tokens per state step the chunked forward executes for chunk length C
+    (0 for arguments outside the domain)."""
+    return int(load_library().gdr_fwd_chunked_token_step(int(C), int(dtype), int(alpha_mode)))
 
 
 def _dtype_code(t: torch.dtype) -> int:

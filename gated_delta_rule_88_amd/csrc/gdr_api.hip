@@ -5,7 +5,7 @@
 
 #include <stdint.h>
 
-#include "gdr_internal.h"
+#include "gdr_chunk.h"
 
 #define GDR_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -75,19 +75,35 @@ GDR_EXPORT const char* gdr_status_string(int status)
     }
 }
 
+size_t gdr::fwd_chunked_workspace_checked(int B, int H, int L, int dk, int dv, int C, int dtype, int mode)
+{
+    if (check_chunk_sizes(B, H, L, dk, dv, C, dtype, mode) != GDR_OK) return (size_t)-1;
+    return chunk_workspace(B, H, L, dk, dv, C, dtype, mode);
+}
+
 GDR_EXPORT size_t gdr_fwd_chunked_workspace_size(int B, int H, int L, int d_k, int d_v, int C,
                                                  int dtype, int alpha_mode)
 {
-    if (check_chunk_sizes(B, H, L, d_k, d_v, C, dtype, alpha_mode) != GDR_OK) return (size_t)-1;
-    return chunk_workspace(B, H, L, d_k, d_v, C, dtype, alpha_mode);
+    return gdr::fwd_chunked_workspace_checked(B, H, L, d_k, d_v, C, dtype, alpha_mode);
 }
 
-GDR_EXPORT int gdr_fwd_chunked_ex(int B, int H, int L, int d_k, int d_v, int C, int dtype,
-                                  const void* q, const void* k, const void* v,
-                                  const float* beta, int alpha_mode, const float* log_alpha,
-                                  const float* S0, void* o, float* S_final,
-                                  void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                  unsigned prologue)
+GDR_EXPORT int gdr_fwd_chunked_token_step(int C, int dtype, int alpha_mode)
+{
+    if (alpha_mode < GDR_ALPHA_NONE || alpha_mode > GDR_ALPHA_CHANNEL) return 0;
+    if ((dtype != GDR_F32 && dtype != GDR_BF16) || !supported_chunk(C)) return 0;
+    return gdr::fwd_token_step(C, dtype, alpha_mode);
+}
+
+namespace gdr {
+
+// gdr_fwd_chunked_ex's checks and launches (shared with the entry point
+// that brings its own scratch, gdr_noalloc.hip).
+int fwd_chunked_checked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                        const void* q, const void* k, const void* v,
+                        const float* beta, int alpha_mode, const float* log_alpha,
+                        const float* S0, void* o, float* S_final,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream,
+                        unsigned prologue)
 {
     if (prologue & ~(unsigned)(GDR_PRO_L2NORM_QK | GDR_PRO_GATES)) return GDR_ERR_INVALID_ARG;
     int st = check_chunk_sizes(B, H, L, d_k, d_v, C, dtype, alpha_mode);
@@ -126,6 +142,19 @@ GDR_EXPORT int gdr_fwd_chunked_ex(int B, int H, int L, int d_k, int d_v, int C, 
     gdr::ChunkArgs a{B, H, L, d_k, d_v, C, dtype, alpha_mode, q, k, v, beta, log_alpha, S0, o,
                      S_final, workspace, stream, prologue};
     return gdr::launch_fwd_chunked(a) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+}  // namespace gdr
+
+GDR_EXPORT int gdr_fwd_chunked_ex(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                                  const void* q, const void* k, const void* v,
+                                  const float* beta, int alpha_mode, const float* log_alpha,
+                                  const float* S0, void* o, float* S_final,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                  unsigned prologue)
+{
+    return gdr::fwd_chunked_checked(B, H, L, d_k, d_v, C, dtype, q, k, v, beta, alpha_mode, log_alpha,
+                                    S0, o, S_final, workspace, workspace_bytes, stream, prologue);
 }
 
 GDR_EXPORT int gdr_fwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
@@ -262,8 +291,9 @@ GDR_EXPORT int gdr_bwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int
     }
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dO, 16) || !aligned(dq, 16) ||
         !aligned(dk, 16) || !aligned(dv, 16) || !aligned(S0, 16) || !aligned(dS_final, 16) ||
-        !aligned(dS0, 16) || !aligned(workspace, 16) || !aligned(beta, 4) || !aligned(log_alpha, 4) ||
-        !aligned(dbeta, 4) || !aligned(dlog_alpha, 4))
+        !aligned(dS0, 16) || !aligned(workspace, 16) || !aligned(beta, 4) ||
+        !aligned(log_alpha, alpha_mode == GDR_ALPHA_CHANNEL ? 16 : 4) || !aligned(dbeta, 4) ||
+        !aligned(dlog_alpha, 4))
         return GDR_ERR_INVALID_ARG;
 
     const size_t la_bytes = alpha_mode == GDR_ALPHA_SCALAR ? nt * 4

@@ -14,12 +14,20 @@
 
 namespace gdr {
 
-// Tokens per state step.  Results do not depend on it beyond rounding (the
-// chunk form is exact); 16 for fp32 operands, whose pipeline slots would not
-// fit LDS at 32, and where the caller asks for 16.
+// Tokens per state step of the backward (and of its forward recompute).
+// Results do not depend on it beyond rounding (the chunk form is exact); 16
+// for fp32 operands, whose pipeline slots would not fit LDS at 32, and where
+// the caller asks for 16.
 __host__ __device__ constexpr int chunk_step(int C, int dtype)
 {
     return (C == 16 || dtype == kF32) ? 16 : 32;
+}
+
+// Tokens per state step of the chunked forward.
+__host__ __device__ constexpr int fwd_token_step(int C, int dtype, int mode)
+{
+    (void)mode;
+    return chunk_step(C, dtype);
 }
 
 // Column order of the [CK][CK] workspace blocks (T~, Gamma, P).  For CK = 32
@@ -133,6 +141,9 @@ struct ScanParams {
 // in order, E_1 = Z_0, E_{g+1} = E_g P_g + Z_g, and every output of
 // segment g gains E_g (P up to t) q_t.  Only for bf16 operands: the entry
 // states enter these last products as bf16 operands.
+// The budget is the MI355X's 256 CUs (one scan workgroup each) as a constant,
+// not a device query: the plan fixes the workspace size, which the size
+// query must report without a device argument.
 constexpr int kSegWorkgroups = 256;   // scan workgroups the device runs at once (one per CU)
 constexpr int kSegMinChunks = 16;     // shortest segment worth splitting off
 constexpr int kMaxSeg = 16;

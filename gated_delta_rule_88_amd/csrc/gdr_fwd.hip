@@ -22,7 +22,7 @@ static size_t record_bytes(int B, int H, int L, int dk, int CK, int dtype, int m
 
 size_t chunk_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int dtype, int mode)
 {
-    const int CK = chunk_step(C, dtype);
+    const int CK = fwd_token_step(C, dtype, mode);
     const size_t rec = record_bytes(B, H, L, dk, CK, dtype, mode);
     const SegPlan sp = seg_plan(B, H, L, dk, dv, CK, dtype, rec);
     return sp.SEG > 1 ? sp.bytes : rec;
@@ -55,7 +55,7 @@ size_t varlen_workspace_bytes(int NS, int H, int T, int dk, int dv, int C, int d
 {
     (void)dv;
     if ((size_t)NS * H == 0) return 0;
-    return varlen_ws(NS, H, T, dk, chunk_step(C, dtype), dtype, mode).bytes;
+    return varlen_ws(NS, H, T, dk, fwd_token_step(C, dtype, mode), dtype, mode).bytes;
 }
 
 // One workgroup of NT threads: every sequence's first token and length, its
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(NT) void varlen_plan_kernel(const int* __restrict__
 hipError_t launch_fwd_varlen(ChunkArgs a)
 {
     if ((size_t)a.NS * a.H == 0) return hipSuccess;
-    const int CK = chunk_step(a.C, a.dtype);
+    const int CK = fwd_token_step(a.C, a.dtype, a.mode);
     const VarlenWs w = varlen_ws(a.NS, a.H, a.L, a.dk, CK, a.dtype, a.mode);
     unsigned char* ws = static_cast<unsigned char*>(a.workspace);
     int* start = reinterpret_cast<int*>(ws + w.off_start);
@@ -144,7 +144,7 @@ hipError_t launch_fwd_chunked(const ChunkArgs& a)
                            a.S_final, n);
         return hipGetLastError();
     }
-    const int CK = chunk_step(a.C, a.dtype);
+    const int CK = fwd_token_step(a.C, a.dtype, a.mode);
     const SegPlan sp = seg_plan(a.B, a.H, a.L, a.dk, a.dv, CK, a.dtype,
                                 record_bytes(a.B, a.H, a.L, a.dk, CK, a.dtype, a.mode));
     hipError_t err = launch_wy(a, CK);

@@ -72,6 +72,17 @@ struct BwdArgs {
 size_t chunk_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int dtype, int mode);
 size_t varlen_workspace_bytes(int NS, int H, int T, int dk, int dv, int C, int dtype, int mode);
 
+// The chunked forward's argument checks and launches (gdr_fwd_chunked_ex).
+int fwd_chunked_checked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                        const void* q, const void* k, const void* v,
+                        const float* beta, int alpha_mode, const float* log_alpha,
+                        const float* S0, void* o, float* S_final,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream,
+                        unsigned prologue);
+// Bytes of workspace the chunked forward plans for these sizes, or
+// (size_t)-1 for sizes outside the domain.
+size_t fwd_chunked_workspace_checked(int B, int H, int L, int dk, int dv, int C, int dtype, int mode);
+
 hipError_t launch_decode_step(const DecodeArgs& a);
 hipError_t launch_fwd_chunked(const ChunkArgs& a);
 hipError_t launch_fwd_varlen(ChunkArgs a);

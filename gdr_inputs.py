@@ -19,7 +19,8 @@ norms spread over two orders of magnitude) and the gates as the raw
 pre-activations b and a (beta = sigmoid(b), alpha = sigmoid(a) on the
 library's side); it applies no activation at all.
 
-All tensors are returned on the CPU.  q, k, v are cast to the workload's
+Tensors are returned on the CPU unless a generator device is asked for
+(``chunked_inputs``, ``decode_stream``).  q, k, v are cast to the workload's
 dtype (bf16 or fp32); beta, log_alpha and states are always fp32.
 """
 from __future__ import annotations
@@ -130,38 +131,42 @@ def _gate_shift(mode: int) -> float:
 
 def chunked_inputs(B: int, H: int, L: int, dk: int, dv: int, dtype: torch.dtype,
                    mode: int, seed: int, s0_std: float = 0.0,
-                   alpha_shift: float | None = None) -> dict:
+                   alpha_shift: float | None = None, device="cpu") -> dict:
     """Inputs for one chunked-forward call, drawn in the fixed order.
 
     Returns a dict with q, k [B,H,L,dk], v [B,H,L,dv] (``dtype``), beta
     [B,H,L] fp32, log_alpha (None | [B,H,L] | [B,H,L,dk]) fp32 and S0
-    (None | [B,H,dv,dk] fp32).
+    (None | [B,H,dv,dk] fp32).  ``device`` places the generator and the
+    tensors (the CPU by default; a GPU generator draws a different stream
+    from the same recipe, for timing runs too large to draw on the host).
     """
-    g = torch.Generator().manual_seed(seed)
-    q = torch.randn(B, H, L, dk, generator=g)
-    k = torch.randn(B, H, L, dk, generator=g)
-    v = torch.randn(B, H, L, dv, generator=g)
-    beta = torch.sigmoid(torch.randn(B, H, L, generator=g))
+    g = torch.Generator(device=device).manual_seed(seed)
+    rnd = lambda *shape: torch.randn(*shape, generator=g, device=device)
+    q = rnd(B, H, L, dk)
+    k = rnd(B, H, L, dk)
+    v = rnd(B, H, L, dv)
+    beta = torch.sigmoid(rnd(B, H, L))
     shift = _gate_shift(mode) if alpha_shift is None else alpha_shift
     if mode == ALPHA_NONE:
         log_alpha = None
     elif mode == ALPHA_SCALAR:
-        log_alpha = -torch.nn.functional.softplus(torch.randn(B, H, L, generator=g) + shift)
+        log_alpha = -torch.nn.functional.softplus(rnd(B, H, L) + shift)
     elif mode == ALPHA_CHANNEL:
-        log_alpha = -torch.nn.functional.softplus(torch.randn(B, H, L, dk, generator=g) + shift)
+        log_alpha = -torch.nn.functional.softplus(rnd(B, H, L, dk) + shift)
     else:
         raise ValueError(f"unknown alpha mode {mode}")
     S0 = None
     if s0_std > 0:
-        S0 = torch.randn(B, H, dv, dk, generator=g) * s0_std
+        S0 = rnd(B, H, dv, dk) * s0_std
     return dict(q=_l2norm(q).to(dtype).contiguous(), k=_l2norm(k).to(dtype).contiguous(),
                 v=v.to(dtype).contiguous(), beta=beta.contiguous(),
                 log_alpha=None if log_alpha is None else log_alpha.contiguous(),
                 S0=None if S0 is None else S0.contiguous())
 
 
-def workload_inputs(w: ChunkedWorkload) -> dict:
-    return chunked_inputs(w.B, w.H, w.L, w.dk, w.dv, w.dtype, w.mode, w.seed, w.s0_std)
+def workload_inputs(w: ChunkedWorkload, device="cpu") -> dict:
+    return chunked_inputs(w.B, w.H, w.L, w.dk, w.dv, w.dtype, w.mode, w.seed, w.s0_std,
+                          device=device)
 
 
 def decode_inputs(N: int, H: int, dk: int, dv: int, steps: int, dtype: torch.dtype,
@@ -190,6 +195,40 @@ def decode_inputs(N: int, H: int, dk: int, dv: int, steps: int, dtype: torch.dty
                 v=v.to(dtype).contiguous(), beta=beta.contiguous(),
                 log_alpha=None if log_alpha is None else log_alpha.contiguous(),
                 S0=S0.contiguous())
+
+
+def decode_stream(N: int, H: int, dk: int, dv: int, dtype: torch.dtype, mode: int, seed: int,
+                  s0_std: float = 0.02, alpha_shift: float | None = None, device="cpu"):
+    """Inputs of consecutive decode steps drawn one step at a time, for runs
+    too long to hold every step's inputs at once.
+
+    Returns (S0, steps): S0 [N,H,dv,dk] fp32, and an endless iterator of
+    per-step dicts with q, k [N,H,dk], v [N,H,dv] (``dtype``), beta [N,H]
+    and log_alpha (None | [N,H] | [N,H,dk]), all on ``device``.  One
+    generator on ``device``, seeded once; draw order: S0, then per step q, k,
+    v, beta-noise, alpha-noise.  Same distributions as ``decode_inputs``."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    rnd = lambda *shape: torch.randn(*shape, generator=g, device=device)
+    S0 = (rnd(N, H, dv, dk) * s0_std).contiguous()
+    shift = _gate_shift(mode) if alpha_shift is None else alpha_shift
+
+    def steps():
+        while True:
+            q = rnd(N, H, dk)
+            k = rnd(N, H, dk)
+            v = rnd(N, H, dv)
+            beta = torch.sigmoid(rnd(N, H))
+            if mode == ALPHA_NONE:
+                la = None
+            elif mode == ALPHA_SCALAR:
+                la = -torch.nn.functional.softplus(rnd(N, H) + shift)
+            else:
+                la = -torch.nn.functional.softplus(rnd(N, H, dk) + shift)
+            yield dict(q=_l2norm(q).to(dtype).contiguous(), k=_l2norm(k).to(dtype).contiguous(),
+                       v=v.to(dtype).contiguous(), beta=beta.contiguous(),
+                       log_alpha=None if la is None else la.contiguous())
+
+    return S0, steps()
 
 
 def decode_workload_inputs(w: DecodeWorkload, steps: int | None = None) -> dict:

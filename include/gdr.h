@@ -117,6 +117,16 @@ size_t gdr_fwd_chunked_workspace_size(int B, int H, int L, int d_k, int d_v, int
                                       int dtype, int alpha_mode);
 
 /*
+ * Tokens per state step that gdr_fwd_chunked (and gdr_fwd_varlen) execute
+ * for chunk length C, dtype and gate mode: the block size of the chunk
+ * algebra the kernels actually run ("linear attention and its gated
+ * descendants", "Chunkwise Parallel Form": C tokens per block, the state
+ * carried between blocks).  The result does not depend on it beyond
+ * rounding.  Returns 0 for arguments outside the domain.
+ */
+int gdr_fwd_chunked_token_step(int C, int dtype, int alpha_mode);
+
+/*
  * Chunkwise forward (training / prefill form): runs the recurrence over L
  * tokens for every (batch b, head h) and writes every output and,
  * optionally, the final state.
@@ -131,7 +141,8 @@ size_t gdr_fwd_chunked_workspace_size(int B, int H, int L, int d_k, int d_v, int
  *              to S_final.  L need not be a multiple of C.
  *   d_k, d_v   key and value head dims, each 64 or 128
  *   C          chunk length: 16, 32 or 64.  The result does not depend on C
- *              beyond rounding.
+ *              beyond rounding.  The kernels run the chunk algebra in steps
+ *              of gdr_fwd_chunked_token_step(C, dtype, alpha_mode) tokens.
  *   dtype      GDR_F32 or GDR_BF16 (type of q, k, v, o)
  *   q, k       [B][H][L][d_k]
  *   v          [B][H][L][d_v]
@@ -139,9 +150,14 @@ size_t gdr_fwd_chunked_workspace_size(int B, int H, int L, int d_k, int d_v, int
  *   alpha_mode GDR_ALPHA_NONE:    log_alpha must be NULL
  *              GDR_ALPHA_SCALAR:  log_alpha [B][H][L] float
  *              GDR_ALPHA_CHANNEL: log_alpha [B][H][L][d_k] float.  In this
- *              mode every log_alpha value must be >= -10 (alpha >= 4.5e-5
- *              per token and channel); smaller values are treated as -10 so
- *              that every intermediate exponential stays finite.
+ *              mode log_alpha values below -10 (alpha < 4.5e-5 per token
+ *              and channel) are treated as -10, so that every intermediate
+ *              exponential stays finite.  Each such (token, channel) then
+ *              keeps at most e^-10 (4.5e-5) of the decayed state column
+ *              that the recurrence would have emptied: the result departs
+ *              from the unbounded recurrence (and from gdr_decode_step,
+ *              which has no floor) by at most that fraction per floored
+ *              value.
  *   S0         NULL => zero initial state, else [B][H][d_v][d_k] float
  *   o          [B][H][L][d_v] (dtype); must not overlap any input
  *   S_final    NULL => not written, else [B][H][d_v][d_k] float; may be the

@@ -290,6 +290,8 @@ def bwd(lib, B=1, H=1, L=64, dk=64, dv=64, C=64, dtype=1, mode=1, la=LA, ws_byte
     (dict(dkp=A + 12 * (1 << 32) + 64), gdr.GDR_ERR_INVALID_ARG),  # dk overlaps dq
     (dict(ds0=S0 + 16), gdr.GDR_ERR_INVALID_ARG),               # dS0 overlaps S0
     (dict(dq=Q + 8), gdr.GDR_ERR_INVALID_ARG),                  # misaligned
+    # channel log alpha is read as 16-byte vectors, as in the forward
+    (dict(mode=2, la=LA + 4), gdr.GDR_ERR_INVALID_ARG),
     (dict(ws_bytes=16), gdr.GDR_ERR_WORKSPACE_TOO_SMALL),
 ])
 def test_backward_rejects_before_launch(lib, kw, status):
@@ -302,3 +304,4 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 64)
     with pytest.raises((RuntimeError, ValueError, TypeError)):
         gdr.gdr_fwd_chunked(q, q, q, torch.zeros(1, 1, 4), None, None)
+
