@@ -28,7 +28,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgdr.so")
 
 GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED = 0, 1, 2
-GDR_ERR_WORKSPACE_TOO_SMALL, GDR_ERR_HIP = 3, 4
+GDR_ERR_WORKSPACE_TOO_SMALL, GDR_ERR_HIP, GDR_ERR_SCRATCH_TOO_SMALL = 3, 4, 5
+GDR_NOALLOC_SCRATCH_BYTES = 64 << 20
 GDR_F32, GDR_BF16 = 0, 1
 GDR_ALPHA_NONE, GDR_ALPHA_SCALAR, GDR_ALPHA_CHANNEL = 0, 1, 2
 GDR_PRO_L2NORM_QK, GDR_PRO_GATES = 1, 2
@@ -37,7 +38,7 @@ _SIZE_MAX = ctypes.c_size_t(-1).value
 
 EXPORTED = ("gdr_abi_version", "gdr_status_string", "gdr_fwd_chunked_workspace_size",
             "gdr_fwd_chunked_token_step",
-            "gdr_fwd_chunked", "gdr_fwd_chunked_ex", "gdr_fwd_varlen_workspace_size",
+            "gdr_fwd_chunked", "gdr_fwd_chunked_ex", "gdr_fwd_chunked_noalloc", "gdr_fwd_varlen_workspace_size",
             "gdr_fwd_varlen", "gdr_bwd_chunked_workspace_size", "gdr_bwd_chunked",
             "gdr_decode_step", "gdr_decode_step_ex")
 
@@ -71,6 +72,8 @@ def load_library():
     lib.gdr_fwd_chunked.restype = i
     lib.gdr_fwd_chunked_ex.argtypes = lib.gdr_fwd_chunked.argtypes + [ctypes.c_uint]
     lib.gdr_fwd_chunked_ex.restype = i
+    lib.gdr_fwd_chunked_noalloc.argtypes = [i] * 7 + [vp] * 4 + [i] + [vp] * 5
+    lib.gdr_fwd_chunked_noalloc.restype = i
     lib.gdr_fwd_varlen_workspace_size.argtypes = [i] * 8
     lib.gdr_fwd_varlen_workspace_size.restype = sz
     lib.gdr_fwd_varlen.argtypes = [i] * 3 + [vp] + [i] * 4 + [vp] * 4 + [i] + [vp] * 5 + [sz, vp,
@@ -211,6 +214,45 @@ def gdr_fwd_chunked(q, k, v, beta, log_alpha=None, S0=None, chunk: int = 64, *,
     if st != GDR_OK:
         raise GdrError(st, name)
     return out
+
+
+def gdr_fwd_chunked_noalloc(q, k, v, beta, log_alpha=None, S0=None, chunk: int = 64, *,
+                            o=None, S_final=None, write_final: bool = True, stream=None):
+    """gdr_fwd_chunked without a workspace: the library's fixed per-device
+    scratch array (GDR_NOALLOC_SCRATCH_BYTES) serves instead, so the C call
+    allocates nothing.  Pass ``o`` (and ``S_final``) to keep the whole call
+    free of allocations; otherwise they are allocated here, as in
+    gdr_fwd_chunked.  Calls that overlap on one GPU race on the shared
+    array."""
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, L, d_k]")
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    mode = _mode_of(log_alpha, q)
+    _check(q, "q", dt, dev, (B, H, L, dk))
+    _check(k, "k", dt, dev, (B, H, L, dk))
+    _check(v, "v", dt, dev, (B, H, L, dv))
+    _check(beta, "beta", torch.float32, dev, (B, H, L))
+    if mode == GDR_ALPHA_SCALAR:
+        _check(log_alpha, "log_alpha", torch.float32, dev, (B, H, L))
+    elif mode == GDR_ALPHA_CHANNEL:
+        _check(log_alpha, "log_alpha", torch.float32, dev, (B, H, L, dk))
+    _check(S0, "S0", torch.float32, dev, (B, H, dv, dk))
+    if o is None:
+        o = torch.empty((B, H, L, dv), dtype=dt, device=dev)
+    _check(o, "o", dt, dev, (B, H, L, dv))
+    if S_final is None and write_final:
+        S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    _check(S_final, "S_final", torch.float32, dev, (B, H, dv, dk))
+    st = lib.gdr_fwd_chunked_noalloc(B, H, L, dk, dv, chunk, code, _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(beta), mode, _ptr(log_alpha), _ptr(S0), _ptr(o),
+                                     _ptr(S_final), _stream(stream))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_fwd_chunked_noalloc")
+    return o, S_final
 
 
 class FwdChunkedCall:

@@ -71,6 +71,9 @@ GDR_EXPORT const char* gdr_status_string(int status)
     case GDR_ERR_UNSUPPORTED: return "GDR_ERR_UNSUPPORTED: sizes or dtype outside the supported domain";
     case GDR_ERR_WORKSPACE_TOO_SMALL: return "GDR_ERR_WORKSPACE_TOO_SMALL: workspace smaller than required";
     case GDR_ERR_HIP: return "GDR_ERR_HIP: a HIP launch failed";
+    case GDR_ERR_SCRATCH_TOO_SMALL:
+        return "GDR_ERR_SCRATCH_TOO_SMALL: the call needs more scratch than the library's fixed "
+               "per-device array holds (GDR_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown gdr status";
     }
 }

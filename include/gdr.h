@@ -67,8 +67,13 @@ enum gdr_status {
                                          o aliasing an input */
     GDR_ERR_UNSUPPORTED = 2,          /* d_k, d_v, C or dtype outside the domain */
     GDR_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below the queried size */
-    GDR_ERR_HIP = 4                   /* a HIP launch failed */
+    GDR_ERR_HIP = 4,                  /* a HIP launch failed */
+    GDR_ERR_SCRATCH_TOO_SMALL = 5     /* gdr_fwd_chunked_noalloc: the call needs more
+                                         than GDR_NOALLOC_SCRATCH_BYTES of workspace */
 };
+
+/* Bytes of the fixed per-device scratch array of gdr_fwd_chunked_noalloc. */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 };
 
@@ -182,6 +187,29 @@ int gdr_fwd_chunked_ex(int B, int H, int L, int d_k, int d_v, int C, int dtype,
                        const float *S0, void *o, float *S_final,
                        void *workspace, size_t workspace_bytes, hipStream_t stream,
                        unsigned prologue);
+
+/*
+ * gdr_fwd_chunked for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, layouts and results as gdr_fwd_chunked, without the
+ * workspace: the kernels use a fixed array of GDR_NOALLOC_SCRATCH_BYTES in
+ * the library's own device memory, one per GPU, held until the process ends.
+ * The call allocates nothing (no hipMalloc, no library allocation); its
+ * first call with a device current looks up that device's array address.
+ *   Returns GDR_ERR_SCRATCH_TOO_SMALL, before anything is enqueued, when
+ *   gdr_fwd_chunked_workspace_size(...) for these sizes exceeds
+ *   GDR_NOALLOC_SCRATCH_BYTES (64 MiB: for example B * H = 64 heads of
+ *   L = 2048 tokens at d_k = 128, bf16, scalar gates need about 19 MB);
+ *   other errors as for gdr_fwd_chunked, GDR_ERR_HIP also if the array's
+ *   address cannot be found.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (on different streams or host threads) race and must be serialised by
+ * the caller.  Nothing in the array needs clearing between calls.
+ */
+int gdr_fwd_chunked_noalloc(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                            const void *q, const void *k, const void *v,
+                            const float *beta, int alpha_mode, const float *log_alpha,
+                            const float *S0, void *o, float *S_final, hipStream_t stream);
 
 /*
  * Bytes of device workspace gdr_bwd_chunked needs (0 when B * H == 0 or

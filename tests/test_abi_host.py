@@ -61,7 +61,7 @@ def test_every_kernel_is_defined():
 
 def test_version_and_status_strings(lib):
     assert gdr.gdr_abi_version() == 1
-    for st in range(5):
+    for st in range(6):
         assert gdr.gdr_status_string(st).startswith("GDR_")
     assert "unknown" in gdr.gdr_status_string(99)
 
@@ -305,3 +305,36 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises((RuntimeError, ValueError, TypeError)):
         gdr.gdr_fwd_chunked(q, q, q, torch.zeros(1, 1, 4), None, None)
 
+
+def noalloc(lib, B=1, H=1, L=64, dk=64, dv=64, C=64, dtype=1, mode=1, la=LA, **kw):
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    ptr = dict(q=Q, k=K, v=V, beta=BETA, s0=S0, o=A + 20 * (1 << 32), sf=A + 21 * (1 << 32))
+    ptr.update(kw)
+    return lib.gdr_fwd_chunked_noalloc(B, H, L, dk, dv, C, dtype, p(ptr["q"]), p(ptr["k"]),
+                                       p(ptr["v"]), p(ptr["beta"]), mode, p(la), p(ptr["s0"]),
+                                       p(ptr["o"]), p(ptr["sf"]), None)
+
+
+def test_noalloc_scratch_size_is_stated():
+    text = open(HEADER).read()
+    assert "#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert gdr.GDR_NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=96), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(mode=3), gdr.GDR_ERR_INVALID_ARG),
+    (dict(B=-1), gdr.GDR_ERR_INVALID_ARG),
+    # more workspace than the fixed array holds: refused before any HIP call
+    (dict(B=64, H=16, L=65536, dk=128, dv=128), gdr.GDR_ERR_SCRATCH_TOO_SMALL),
+    (dict(B=8, H=8, L=65536, dk=128, dv=128, mode=2), gdr.GDR_ERR_SCRATCH_TOO_SMALL),
+])
+def test_noalloc_rejects_before_launch(lib, kw, status):
+    assert noalloc(lib, **kw) == status
+
+
+def test_noalloc_limit_matches_workspace_query():
+    big = gdr.gdr_fwd_chunked_workspace_size(64, 16, 65536, 128, 128, 64, gdr.GDR_BF16, 1)
+    assert big > gdr.GDR_NOALLOC_SCRATCH_BYTES
+    head = gdr.gdr_fwd_chunked_workspace_size(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 1)
+    assert 0 < head <= gdr.GDR_NOALLOC_SCRATCH_BYTES
