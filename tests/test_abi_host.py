@@ -68,11 +68,15 @@ def test_version_and_status_strings(lib):
 
 def test_workspace_size_query():
     ws = gdr.gdr_fwd_chunked_workspace_size
-    # Per chunk of CK tokens (CK = 32 for bf16, 16 for fp32 or when C = 16):
-    # T~ (CK*CK elements); scalar gates, and alpha = 1 which runs as scalar
-    # gates with log alpha = 0, add the decay matrix (CK*CK) and 4*CK floats
-    # of decay factors; channel gates add the score block (CK*CK), d_k floats
-    # and three CK x d_k decayed operands.
+    # Per chunk of CK tokens (the executed token step: 32 for bf16, 16 for
+    # fp32 or when C = 16): T~ (CK*CK elements); scalar gates, and alpha = 1
+    # which runs as scalar gates with log alpha = 0, add the decay matrix
+    # (CK*CK) and 4*CK floats of decay factors; channel gates add the score
+    # block (CK*CK), d_k floats and three CK x d_k decayed operands.
+    step = gdr.gdr_fwd_chunked_token_step
+    assert step(64, gdr.GDR_BF16, 1) == 32 and step(32, gdr.GDR_BF16, 2) == 32
+    assert step(16, gdr.GDR_BF16, 1) == 16 and step(64, gdr.GDR_F32, 0) == 16
+    assert step(48, gdr.GDR_BF16, 1) == 0 and step(64, 7, 1) == 0 and step(64, 1, 3) == 0
     assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 1) == 64 * 64 * (2048 + 2048 + 512)
     assert ws(1, 2, 256, 64, 64, 64, gdr.GDR_F32, 0) == 2 * 16 * (1024 + 1024 + 256)
     assert ws(1, 2, 256, 64, 64, 64, gdr.GDR_F32, 0) == ws(1, 2, 256, 64, 64, 64, gdr.GDR_F32, 1)

@@ -87,7 +87,7 @@ SEG_CASES = [(gi.ALPHA_SCALAR, 1, 2, 1100, 128, 128, 2), (gi.ALPHA_NONE, 1, 1, 2
              (gi.ALPHA_SCALAR, 1, 1, 1600, 64, 128, 3), (gi.ALPHA_CHANNEL, 1, 1, 1600, 128, 64, 3)]
 
 
-def _record_bytes(mode, dk, ck=32, es=2):
+def _record_bytes(mode, dk, ck, es=2):
     """Per-chunk workspace record (see the layout in gdr_chunk.h)."""
     t = ck * ck * es
     if mode in (gi.ALPHA_NONE, gi.ALPHA_SCALAR):   # alpha = 1 runs as log alpha = 0
@@ -102,8 +102,9 @@ def test_segmented_scan_parity(mode, B, H, L, dk, dv, seg):
     """Few (b, h) chains and many chunks: the scan runs as `seg` segments at
     once, combined through their transitions.  Ragged last chunk and last
     segment, with an initial state and the final state checked."""
-    nc = (L + 31) // 32
-    rec = B * H * nc * _record_bytes(mode, dk)
+    ck = gdr.gdr_fwd_chunked_token_step(64, gdr.GDR_BF16, mode)
+    nc = (L + ck - 1) // ck
+    rec = B * H * nc * _record_bytes(mode, dk, ck)
     ws = gdr.gdr_fwd_chunked_workspace_size(B, H, L, dk, dv, 64, gdr.GDR_BF16, mode)
     extra = B * H * seg * (dv * dk * 4 + dk * dk * 4 + dv * dk * 2) + B * H * L * dk * 2
     assert rec + extra <= ws <= rec + extra + 4 * 256   # the segment-parallel plan is in use
