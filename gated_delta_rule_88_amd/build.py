@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdr.so")
 OBJ = os.path.join(ROOT, "_build")
 SOURCES = ["gdr_api.hip", "gdr_decode.hip", "gdr_fwd.hip", "gdr_wy.hip", "gdr_scan.hip", "gdr_segment.hip",
-           "gdr_bwd.hip", "gdr_noalloc.hip"]
+           "gdr_bwd.hip", "gdr_bwd_chain.hip",
+           "gdr_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU forms are switched off for every device pass; the host

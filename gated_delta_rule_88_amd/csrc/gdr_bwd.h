@@ -1,0 +1,26 @@
+// gdr_bwd.h -- what the backward's two translation units share: the kernel
+// parameters and the pipelined chain's launcher.
+#pragma once
+
+#include "gdr_internal.h"
+
+namespace gdr {
+
+struct BwdParams {
+    const void *q, *k, *v, *dO;
+    const float *beta, *log_alpha;   // log_alpha NULL: alpha = 1
+    const float* dS_final;           // [B*H][d_v][d_k] or null
+    const unsigned char* ws;         // forward prepass records
+    const void* Sck;                 // [B*H][NC][d_v][d_k] (operand type): state entering each chunk
+    void* dSck;                      // [B*H][NC][d_v][d_k] (operand type): dS at each chunk's end
+    void *dq, *dk, *dv;
+    float *dbeta, *dlog_alpha, *dS0;
+    int L, NC, DV, total;
+};
+
+// The chain (dS carried backwards over the chunks of every (b, h)) for bf16
+// operands and 32-token steps, d_k = 64 or 128, d_v a multiple of 32:
+// one workgroup per (b, h, 32 value channels) on the stream.
+hipError_t launch_bwd_chain_pipe(const BwdParams& bp, int BH, int dk, bool channel, hipStream_t stream);
+
+}  // namespace gdr

@@ -39,6 +39,7 @@
 #include "gdr_device.h"
 #include "gdr_chunk.h"
 #include "gdr_tri.h"
+#include "gdr_bwd.h"
 
 namespace gdr {
 
@@ -242,17 +243,6 @@ struct RowStage {
     }
 };
 
-struct BwdParams {
-    const void *q, *k, *v, *dO;
-    const float *beta, *log_alpha;   // log_alpha NULL: alpha = 1
-    const float* dS_final;           // [B*H][d_v][d_k] or null
-    const unsigned char* ws;         // forward prepass records
-    const void* Sck;                 // [B*H][NC][d_v][d_k] (operand type): state entering each chunk
-    void* dSck;                      // [B*H][NC][d_v][d_k] (operand type): dS at each chunk's end
-    void *dq, *dk, *dv;
-    float *dbeta, *dlog_alpha, *dS0;
-    int L, NC, DV, total;
-};
 
 // LDS row strides: every row padded by 16 bytes, so that the 16 rows a
 // fragment read touches (and the rows a transposed store walks) fall on
@@ -1759,8 +1749,11 @@ static hipError_t launch_bwd_t(const BwdParams& bp, int BH, bool channel, hipStr
     using GC = GradChLds<E, DK, CK>;
     static_assert(CL::bytes <= 160 * 1024 && GL::bytes <= 160 * 1024 && GC::bytes <= 160 * 1024, "LDS budget");
     const int chains = BH * (bp.DV / kBV);
-    hipError_t err = channel ? launch_lds(chunk_bwd_chain_kernel<E, DK, CK, true>, chains, 384, CL::bytes, stream, bp)
-                             : launch_lds(chunk_bwd_chain_kernel<E, DK, CK, false>, chains, 384, CL::bytes, stream, bp);
+    // bf16 operands on 32-token steps take the pipelined chain (gdr_bwd_chain.hip)
+    hipError_t err;
+    if constexpr (sizeof(E) == 2 && CK == 32) err = launch_bwd_chain_pipe(bp, BH, DK, channel, stream);
+    else err = channel ? launch_lds(chunk_bwd_chain_kernel<E, DK, CK, true>, chains, 384, CL::bytes, stream, bp)
+                       : launch_lds(chunk_bwd_chain_kernel<E, DK, CK, false>, chains, 384, CL::bytes, stream, bp);
     if (err != hipSuccess) return err;
     // persistent, as many workgroups as fit the CUs (the next chunk's inputs
     // are read while the current one is worked on)
