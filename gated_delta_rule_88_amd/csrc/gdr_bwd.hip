@@ -677,6 +677,218 @@ __global__ __launch_bounds__(384, 1) void chunk_bwd_chain_kernel(BwdParams p)
     }
 }
 
+// ------------------------------------------- value blocks, lean form (bf16, C = 32)
+// The value-block pass of the gradient kernels for bf16 operands and 32-token
+// chunks.  Per block of 32 value channels (scalar alpha; channel alpha uses
+// K . exp(G) for the first K, K . exp(G_C - G) for the second and no gamma, D):
+//   A: R = V - gamma . K S0^T (waves 0..3), dU = P^T dO + D . K dS^T (waves 4..7)
+//   B: U = T~ R (waves 0..3), dR = T~^T dU (waves 4..7, which also store dv)
+//   C: dO S0, dR S0, U dS, dO U^T, dU R^T accumulated (all waves); waves 0..3
+//      stage the next block into the free buffer and read the one after it
+// R, dU, U, dR are kept as [value channel][token] bf16 rows (one 8-byte store
+// per result tile); every operand is a 16-byte row read or a transposing read
+// (ds_read_b64_tr_b16) of a padded row-major tile, so no transposed copy is
+// staged.  The block inputs are double-buffered; waves 0..3 hold the block
+// after next in registers, so its reads have a whole block to land.
+template <int DK>
+struct LeanVB {
+    static constexpr int LDK = DK + 8, LB = 40;       // padded row lengths (elements)
+    static constexpr int SZS = 32 * LDK * 2, SZV = 32 * LB * 2;
+    static constexpr int oS0 = 0, odS = SZS, oV = 2 * SZS, odO = 2 * SZS + SZV;
+    static constexpr int IN = 2 * SZS + 2 * SZV;     // one buffer of block inputs
+    static constexpr int SZX = 32 * LB * 2;          // one [32 v][32 tok] intermediate
+    static constexpr int oR = 0, odU = SZX, oU = 2 * SZX, odR = 3 * SZX, XB = 4 * SZX;
+    static constexpr int NS = 32 * DK / 8;           // 16-byte vectors of one state block
+    static constexpr int NPS = NS / 256;             // of them per staging thread
+    static constexpr int NPF = 2 * NPS + 1;          // registers per staging thread
+};
+
+__device__ __forceinline__ Frag<bf16> rowf(const unsigned char* p) {
+    Frag<bf16> f;
+    f.v = __builtin_bit_cast(bf16x8, ld16(p));
+    return f;
+}
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// Operand of X^T from a padded row-major bf16 tile X (row length LD): lane
+// (g, c) holds X[row0 + 8g + j][col0 + c], j = 0..7 (two transposing reads:
+// address lane (g, i) names row row0 + 8g + i/4 (+4), columns col0 + 4(i%4) ..)
+template <int LD>
+__device__ __forceinline__ Frag<bf16> trn(const unsigned char* tile, int row0, int col0, int l) {
+    const int g = l >> 4, i = l & 15;
+    const unsigned char* a = tile + ((row0 + 8 * g + (i >> 2)) * LD + col0 + 4 * (i & 3)) * 2;
+    const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a)));
+    const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 8 * LD)));
+    Frag<bf16> f;
+    f.v = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+    return f;
+}
+// X[row0 + 4g + e][col0 + c] in result-tile order (one transposing read)
+template <int LD>
+__device__ __forceinline__ f32x4 trc(const unsigned char* tile, int row0, int col0, int l) {
+    const int g = l >> 4, i = l & 15;
+    const unsigned char* a = tile + ((row0 + 4 * g + (i >> 2)) * LD + col0 + 4 * (i & 3)) * 2;
+    const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a)));
+    return f32x4{bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y)};
+}
+__device__ __forceinline__ void st4bf(unsigned char* p, f32x4 x) {
+    st8(p, u32x2{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3])});
+}
+
+// Block inputs held in registers by a staging thread t (0..255): S0 and dS
+// vectors t + 256 i of the block, and vector t % 128 of V (t < 128) or dO.
+template <int DK>
+struct LeanPf {
+    u32x4 r[LeanVB<DK>::NPF];
+    int valid;   // token rows of the block's chunk
+    __device__ __forceinline__ void load(const BwdParams& p, int c, int v0, int t) {
+        using LV = LeanVB<DK>;
+        constexpr int CK = 32;
+        const int n = c % p.NC;
+        valid = min(CK, p.L - n * CK);
+        const size_t tok = (size_t)(c / p.NC) * p.L + (size_t)n * CK;
+        const bf16* s0 = static_cast<const bf16*>(p.Sck) + ((size_t)c * p.DV + v0) * DK;
+        const bf16* ds = static_cast<const bf16*>(p.dSck) + ((size_t)c * p.DV + v0) * DK;
+#pragma unroll
+        for (int i = 0; i < LV::NPS; ++i) {
+            r[i] = ld16(s0 + 8 * (t + 256 * i));
+            r[LV::NPS + i] = ld16(ds + 8 * (t + 256 * i));
+        }
+        const int x = t & 127, row = min(x >> 2, valid - 1);
+        const bf16* src = reinterpret_cast<const bf16*>(t < 128 ? p.v : p.dO);
+        r[2 * LV::NPS] = ld16(src + (tok + row) * p.DV + v0 + 8 * (x & 3));
+    }
+    // into buffer b (rows of V and dO past the chunk's end as zeros)
+    __device__ __forceinline__ void store(unsigned char* b, int t) const {
+        using LV = LeanVB<DK>;
+        constexpr int PR = DK / 8;   // vectors per state row
+#pragma unroll
+        for (int i = 0; i < LV::NPS; ++i) {
+            const int x = t + 256 * i, row = x / PR, ch = x % PR;
+            st16(b + LV::oS0 + (row * LV::LDK + 8 * ch) * 2, r[i]);
+            st16(b + LV::odS + (row * LV::LDK + 8 * ch) * 2, r[LV::NPS + i]);
+        }
+        const int x = t & 127, row = x >> 2;
+        st16(b + (t < 128 ? LV::oV : LV::odO) + (row * LV::LB + 8 * (x & 3)) * 2,
+             row < valid ? r[2 * LV::NPS] : u32x4{0u, 0u, 0u, 0u});
+    }
+};
+
+// One chunk's value blocks in the lean form.  On entry buffer bk & 1 holds
+// block (cid, 0) and pf the block after it, (pc, pv0); on exit bk has advanced
+// by the number of blocks and the same holds for the next chunk.  Results:
+// a1 += dO S0, a2 += dR S0, a3 += U dS (tiles t = w + 8u, rows 16 (t / NJ),
+// key channels 16 (t % NJ)), dPa += dO U^T, dTa += dU R^T (tile w < 4),
+// hs[e] += S0 . dS over this thread's key channels 8 (tid / 32) + e, and dv.
+// SC: scalar alpha (gamma, D); else channel alpha (Kx = K . exp(G),
+// Kd = K . exp(G_C - G), no per-token factors).
+template <int DK, bool SC, int NQW>
+__device__ __forceinline__ void lean_value_blocks(
+    const BwdParams& p, unsigned char* smem, int in_off, int lx_off, const bf16* Kx, const bf16* Kd,
+    const bf16* Pt, const bf16* Tt, const bf16* Ttt, const float* gam, const float* Dd, int cid, int tid,
+    int& bk, LeanPf<DK>& pf, int& pc, int& pv0, f32x4* a1, f32x4* a2, f32x4* a3, f32x4& dPa, f32x4& dTa,
+    float* hs)
+{
+    using LV = LeanVB<DK>;
+    constexpr int CK = 32, NJ = DK / 16, NKS = DK / 32, NW = 8, NQT = 2 * NJ;
+    constexpr int LDK = LV::LDK, LB = LV::LB;
+    const int l = tid & 63, g4 = l >> 4, c16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = cid % p.NC, valid = min(CK, p.L - n * CK);
+    const size_t tok = (size_t)(cid / p.NC) * p.L + (size_t)n * CK;
+    const unsigned char* kx = reinterpret_cast<const unsigned char*>(Kx);
+    const unsigned char* kd = reinterpret_cast<const unsigned char*>(Kd);
+    const unsigned char* pt = reinterpret_cast<const unsigned char*>(Pt);
+    const unsigned char* tf = reinterpret_cast<const unsigned char*>(Tt);
+    const unsigned char* tft = reinterpret_cast<const unsigned char*>(Ttt);
+    unsigned char* xb = smem + lx_off;
+    for (int v0 = 0; v0 < p.DV; v0 += 32, ++bk) {
+        const unsigned char* ib = smem + in_off + (bk & 1) * LV::IN;
+        // ---- A: R = V - gamma . K S0^T (waves 0..3), dU = P^T dO + D . K dS^T
+        // (waves 4..7); tile (tokens 16 tt .., value channels 16 cb ..)
+        {
+            const int q = w & 3, tt = q & 1, cb = q >> 1;
+            const bool rw = w < 4;
+            const unsigned char* ka = (rw ? kx : kd) + ((16 * tt + c16) * LDK + 8 * g4) * 2;
+            const unsigned char* sa = ib + (rw ? LV::oS0 : LV::odS) + ((16 * cb + c16) * LDK + 8 * g4) * 2;
+            f32x4 x = zero4();
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) mma(x, rowf(ka + 64 * ks), rowf(sa + 64 * ks));
+            f32x4 y;
+            if (rw) {
+                const f32x4 vv = trc<LB>(ib + LV::oV, 16 * tt, 16 * cb, l);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = vv[e] - (SC ? gam[16 * tt + 4 * g4 + e] : 1.f) * x[e];
+            } else {
+                y = zero4();
+                mma(y, rowf(pt + ((16 * tt + c16) * LB + 8 * g4) * 2), trn<LB>(ib + LV::odO, 0, 16 * cb, l));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] += (SC ? Dd[16 * tt + 4 * g4 + e] : 1.f) * x[e];
+            }
+            st4bf(xb + (rw ? LV::oR : LV::odU) + ((16 * cb + c16) * LB + 16 * tt + 4 * g4) * 2, y);
+        }
+        __syncthreads();
+        // ---- B: U = T~ R (waves 0..3), dR = T~^T dU (waves 4..7, = dv)
+        {
+            const int q = w & 3, tt = q & 1, cb = q >> 1;
+            const bool up = w < 4;
+            f32x4 z = zero4();
+            mma(z, rowf((up ? tf : tft) + ((16 * tt + c16) * LB + 8 * g4) * 2),
+                rowf(xb + (up ? LV::oR : LV::odU) + ((16 * cb + c16) * LB + 8 * g4) * 2));
+            st4bf(xb + (up ? LV::oU : LV::odR) + ((16 * cb + c16) * LB + 16 * tt + 4 * g4) * 2, z);
+            if (!up) {
+                bf16* dvg = reinterpret_cast<bf16*>(p.dv) + tok * p.DV + v0 + 16 * cb + c16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * tt + 4 * g4 + e;
+                    if (r < valid) dvg[(size_t)r * p.DV] = (bf16)z[e];
+                }
+            }
+        }
+        __syncthreads();
+        // ---- C: accumulate over the block's value channels
+#pragma unroll
+        for (int u = 0; u < NQW; ++u) {
+            const int t = w + NW * u;
+            if (t < NQT) {
+                const int rb = t / NJ, jb = t % NJ;
+                const Frag<bf16> ado = rowf(ib + LV::odO + ((16 * rb + c16) * LB + 8 * g4) * 2);
+                const Frag<bf16> adr = trn<LB>(xb + LV::odR, 0, 16 * rb, l);
+                const Frag<bf16> au = trn<LB>(xb + LV::oU, 0, 16 * rb, l);
+                const Frag<bf16> bs0 = trn<LDK>(ib + LV::oS0, 0, 16 * jb, l);
+                const Frag<bf16> bds = trn<LDK>(ib + LV::odS, 0, 16 * jb, l);
+                mma(a1[u], ado, bs0);
+                mma(a2[u], adr, bs0);
+                mma(a3[u], au, bds);
+            }
+        }
+        if (w < 4) {
+            const int rb = w >> 1, sb = w & 1;
+            mma(dPa, rowf(ib + LV::odO + ((16 * rb + c16) * LB + 8 * g4) * 2), trn<LB>(xb + LV::oU, 0, 16 * sb, l));
+            mma(dTa, trn<LB>(xb + LV::odU, 0, 16 * rb, l), trn<LB>(xb + LV::oR, 0, 16 * sb, l));
+        }
+        if (tid < 32 * DK / 8) {
+            const int i = tid & 31, j = 8 * (tid >> 5);
+            float a[8], b[8];
+            Pack<bf16>::unpack(ld16(ib + LV::oS0 + (i * LDK + j) * 2), a);
+            Pack<bf16>::unpack(ld16(ib + LV::odS + (i * LDK + j) * 2), b);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) hs[e] += a[e] * b[e];
+        }
+        // waves 0..3: the next block into the free buffer, then read the one after it
+        if (w < 4 && pc < p.total) {
+            pf.store(smem + in_off + ((bk + 1) & 1) * LV::IN, tid);
+            if (pv0 + 32 < p.DV) {
+                pv0 += 32;
+            } else {
+                pv0 = 0;
+                pc += gridDim.x;
+            }
+            if (pc < p.total) pf.load(p, pc, pv0, tid);
+        }
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------- grads
 template <typename E, int DK, int CK>
 struct GradLds : Strides<E, DK, CK> {
@@ -717,7 +929,13 @@ struct GradLds : Strides<E, DK, CK> {
     static constexpr int off_V = off_dUt + EBC;                // [CK][LBF] f32
     static constexpr int blk_end = off_V + FCB;
     // the last phase, over the block region
-    static constexpr int off_dTt = off_blk;                    // [CK][LF] f32
+    // bf16, C = 32: double-buffered block inputs, then the tail region (whose
+    // start also holds the block intermediates during the value loop)
+    static constexpr bool LEAN = (ES == 2 && CK == 32);
+    static constexpr int off_lean = off_blk;
+    static constexpr int off_tail = LEAN ? off_blk + 2 * LeanVB<DK>::IN : off_blk;
+    static constexpr int off_lx = off_tail;
+    static constexpr int off_dTt = off_tail;                   // [CK][LF] f32
     static constexpr int off_dTb = off_dTt + FCC;
     static constexpr int off_Em = off_dTb + FCC;
     static constexpr int off_Y1t = off_Em + FCC;
@@ -727,7 +945,9 @@ struct GradLds : Strides<E, DK, CK> {
     static constexpr int off_dG = off_dPWt + ECC;
     static constexpr int off_dGt = off_dG + ECC;
     static constexpr int last_end = off_dGt + ECC;
-    static constexpr int bytes = blk_end > last_end ? blk_end : last_end;
+    static constexpr int lx_end = off_lx + LeanVB<DK>::XB;
+    static constexpr int m0 = LEAN ? (lx_end > last_end ? lx_end : last_end) : (blk_end > last_end ? blk_end : last_end);
+    static constexpr int bytes = m0;
 };
 
 template <typename E, int DK, int CK>
@@ -816,9 +1036,23 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
             da[u] = ld16(dog + (size_t)r * p.DV + v0 + cc);
         }
     };
+    // (bf16, C = 32) the lean value blocks' staging: block 0 into buffer 0,
+    // the block after it into registers
+    LeanPf<DK> lpf;
+    int lbk = 0, lpc = blockIdx.x, lpv0 = 0;
     if ((int)blockIdx.x < p.total) {
         fetch_chunk(blockIdx.x, threadIdx.x);
-        fetch_block(blockIdx.x, 0, threadIdx.x);
+        if constexpr (LY::LEAN) {
+            if (threadIdx.x < 256) {
+                lpf.load(p, lpc, 0, threadIdx.x);
+                lpf.store(smem + LY::off_lean, threadIdx.x);
+                if (p.DV > 32) lpv0 = 32;
+                else lpc += gridDim.x;
+                if (lpc < p.total) lpf.load(p, lpc, lpv0, threadIdx.x);
+            }
+        } else {
+            fetch_block(blockIdx.x, 0, threadIdx.x);
+        }
     }
     for (int cid = blockIdx.x; cid < p.total; cid += gridDim.x) {
     // lane-dependent values are re-derived per chunk (see opaque)
@@ -845,7 +1079,6 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
             bs[l] = l < valid ? btv : 0.f;
         }
     }
-    if (nxt < p.total) fetch_chunk(nxt, tid);
     __syncthreads();
     // ---- Gram and score tiles: Bm = strictly-lower(K K^T . Gamma),
     // A = diag(beta) Bm, P = Q K^T . Gamma (diagonal included)
@@ -886,107 +1119,131 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
     f32x4 dPa = zero4(), dTa = zero4();   // C x C tile w (w < NCC)
     float hS = 0.f;                       // this thread's part of <dS_end, S0>
     constexpr int NCB = NB * (kBV / 16);  // C x kBV tiles (<= 4)
-    for (int v0 = 0; v0 < p.DV; v0 += kBV) {
-        __syncthreads();   // the previous block's operands are consumed
-#pragma unroll
-        for (int u = 0; u < NSV; ++u) {
-            const int xs = tid + NT * u, i = xs % kBV, j = VE * (xs / kBV);
-            if (xs >= kBV * DK / VE) continue;
-            E a[VE], b[VE];
-            __builtin_memcpy(a, &sa[u], 16);
-            __builtin_memcpy(b, &sb[u], 16);
-            st16(S0s + i * LDK + j, sa[u]);
-            st16(dSs + i * LDK + j, sb[u]);
-#pragma unroll
-            for (int e = 0; e < VE; ++e) {
-                S0t[(j + e) * LBV + i] = a[e];
-                dSt[(j + e) * LBV + i] = b[e];
-                hS += to_f32(a[e]) * to_f32(b[e]);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < NVV; ++u) {
-            const int x = tid + NT * u, r = x % CK, c = (x / CK) * VE;
-            if (x < CK * PERV) {
-                float a[VE], d[VE];
-                Pack<E>::unpack(r < valid ? va[u] : u32x4{0u, 0u, 0u, 0u}, a);
-                Pack<E>::unpack(r < valid ? da[u] : u32x4{0u, 0u, 0u, 0u}, d);
-#pragma unroll
-                for (int j = 0; j < VE; ++j) {
-                    Vs[r * LBF + c + j] = a[j];
-                    dOs[r * LBV + c + j] = from_f32<E>(d[j]);
-                    dOt[(c + j) * LCK + r] = from_f32<E>(d[j]);
-                    gdOs[r * LBV + c + j] = from_f32<E>(gam[r] * d[j]);
-                }
-            }
-        }
-        if (v0 + kBV < p.DV) fetch_block(cid, v0 + kBV, tid);
-        else if (nxt < p.total) fetch_block(nxt, 0, tid);
-        __syncthreads();
-        // ---- R = V - gamma K S0^T (waves 0..NCB-1); dU = P^T dO + D . K dS^T (waves 4..)
-        if (w < NCB) {
-            const int rb = w / 2, cb = w % 2;
-            f32x4 x = zero4();
-            tmma<E>(x, Ks, LDK, 16 * rb, S0s, LDK, 16 * cb, DK, l);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
-                const float rr = Vs[r * LBF + i] - gam[r] * x[e];
-                Rs[r * LBV + i] = from_f32<E>(rr);
-                Rt[i * LCK + r] = from_f32<E>(rr);
-            }
-        } else if (w >= 4 && w < 4 + NCB) {
-            const int rb = (w - 4) / 2, cb = (w - 4) % 2;
-            f32x4 kds = zero4(), du = zero4();
-            tmma<E>(kds, Ks, LDK, 16 * rb, dSs, LDK, 16 * cb, DK, l);
-            tmma<E>(du, Pt, LCK, 16 * rb, dOt + 16 * cb * LCK, LCK, 0, CK, l);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
-                const float dd = du[e] + Dd[r] * kds[e];
-                dUs[r * LBV + i] = from_f32<E>(dd);
-                dUt[i * LCK + r] = from_f32<E>(dd);
-            }
-        }
-        __syncthreads();
-        // ---- U = T~ R (waves 0..); dR = T~^T dU (= dV), dX = -gamma dR (waves 4..)
-        if (w < NCB) {
-            const int rb = w / 2, cb = w % 2;
-            f32x4 u = zero4();
-            tmma<E>(u, Tt, LCK, 16 * rb, Rt + 16 * cb * LCK, LCK, 0, CK, l);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Us[(16 * rb + 4 * g4 + e) * LBV + 16 * cb + c16] = from_f32<E>(u[e]);
-        } else if (w >= 4 && w < 4 + NCB) {
-            const int rb = (w - 4) / 2, cb = (w - 4) % 2;
-            f32x4 dr = zero4();
-            tmma<E>(dr, Ttt, LCK, 16 * rb, dUt + 16 * cb * LCK, LCK, 0, CK, l);
-            E* dvg = reinterpret_cast<E*>(p.dv) + tok * p.DV + v0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
-                if (r < valid) dvg[(size_t)r * p.DV + i] = from_f32<E>(dr[e]);
-                dXs[r * LBV + i] = from_f32<E>(-gam[r] * dr[e]);
-            }
-        }
-        __syncthreads();
-        // ---- accumulate over the block's value channels
+    if constexpr (LY::LEAN) {
+        float hs8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        lean_value_blocks<DK, true, NQW>(p, smem, LY::off_lean, LY::off_lx, Ks, Ks, Pt, Tt, Ttt, gam, Dd, cid, tid,
+                                         lbk, lpf, lpc, lpv0, dQa, dKa, dKd, dPa, dTa, hs8);
+        // (gamma dO) S0 and dX S0 = -(gamma dR) S0 from the unscaled sums
 #pragma unroll
         for (int u = 0; u < NQW; ++u) {
             const int t = w + NW * u;
             if (t < NQT) {
-                const int rb = t / NJ, jb = t % NJ;
-                tmma<E>(dQa[u], gdOs, LBV, 16 * rb, S0t, LBV, 16 * jb, kBV, l);
-                tmma<E>(dKa[u], dXs, LBV, 16 * rb, S0t, LBV, 16 * jb, kBV, l);
-                tmma<E>(dKd[u], Us, LBV, 16 * rb, dSt, LBV, 16 * jb, kBV, l);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float gr = gam[16 * (t / NJ) + 4 * g4 + e];
+                    dQa[u][e] *= gr;
+                    dKa[u][e] *= -gr;
+                }
             }
         }
-        if (w < NCC) {
-            const int rb = w / NB, sb = w % NB;
-            tmma<E>(dPa, dOs, LBV, 16 * rb, Us, LBV, 16 * sb, kBV, l);
-            tmma<E>(dTa, dUs, LBV, 16 * rb, Rs, LBV, 16 * sb, kBV, l);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hS += hs8[e];
+    } else {
+    for (int v0 = 0; v0 < p.DV; v0 += kBV) {
+            __syncthreads();   // the previous block's operands are consumed
+    #pragma unroll
+            for (int u = 0; u < NSV; ++u) {
+                const int xs = tid + NT * u, i = xs % kBV, j = VE * (xs / kBV);
+                if (xs >= kBV * DK / VE) continue;
+                E a[VE], b[VE];
+                __builtin_memcpy(a, &sa[u], 16);
+                __builtin_memcpy(b, &sb[u], 16);
+                st16(S0s + i * LDK + j, sa[u]);
+                st16(dSs + i * LDK + j, sb[u]);
+    #pragma unroll
+                for (int e = 0; e < VE; ++e) {
+                    S0t[(j + e) * LBV + i] = a[e];
+                    dSt[(j + e) * LBV + i] = b[e];
+                    hS += to_f32(a[e]) * to_f32(b[e]);
+                }
+            }
+    #pragma unroll
+            for (int u = 0; u < NVV; ++u) {
+                const int x = tid + NT * u, r = x % CK, c = (x / CK) * VE;
+                if (x < CK * PERV) {
+                    float a[VE], d[VE];
+                    Pack<E>::unpack(r < valid ? va[u] : u32x4{0u, 0u, 0u, 0u}, a);
+                    Pack<E>::unpack(r < valid ? da[u] : u32x4{0u, 0u, 0u, 0u}, d);
+    #pragma unroll
+                    for (int j = 0; j < VE; ++j) {
+                        Vs[r * LBF + c + j] = a[j];
+                        dOs[r * LBV + c + j] = from_f32<E>(d[j]);
+                        dOt[(c + j) * LCK + r] = from_f32<E>(d[j]);
+                        gdOs[r * LBV + c + j] = from_f32<E>(gam[r] * d[j]);
+                    }
+                }
+            }
+            if (v0 + kBV < p.DV) fetch_block(cid, v0 + kBV, tid);
+            else if (nxt < p.total) fetch_block(nxt, 0, tid);
+            __syncthreads();
+            // ---- R = V - gamma K S0^T (waves 0..NCB-1); dU = P^T dO + D . K dS^T (waves 4..)
+            if (w < NCB) {
+                const int rb = w / 2, cb = w % 2;
+                f32x4 x = zero4();
+                tmma<E>(x, Ks, LDK, 16 * rb, S0s, LDK, 16 * cb, DK, l);
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
+                    const float rr = Vs[r * LBF + i] - gam[r] * x[e];
+                    Rs[r * LBV + i] = from_f32<E>(rr);
+                    Rt[i * LCK + r] = from_f32<E>(rr);
+                }
+            } else if (w >= 4 && w < 4 + NCB) {
+                const int rb = (w - 4) / 2, cb = (w - 4) % 2;
+                f32x4 kds = zero4(), du = zero4();
+                tmma<E>(kds, Ks, LDK, 16 * rb, dSs, LDK, 16 * cb, DK, l);
+                tmma<E>(du, Pt, LCK, 16 * rb, dOt + 16 * cb * LCK, LCK, 0, CK, l);
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
+                    const float dd = du[e] + Dd[r] * kds[e];
+                    dUs[r * LBV + i] = from_f32<E>(dd);
+                    dUt[i * LCK + r] = from_f32<E>(dd);
+                }
+            }
+            __syncthreads();
+            // ---- U = T~ R (waves 0..); dR = T~^T dU (= dV), dX = -gamma dR (waves 4..)
+            if (w < NCB) {
+                const int rb = w / 2, cb = w % 2;
+                f32x4 u = zero4();
+                tmma<E>(u, Tt, LCK, 16 * rb, Rt + 16 * cb * LCK, LCK, 0, CK, l);
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) Us[(16 * rb + 4 * g4 + e) * LBV + 16 * cb + c16] = from_f32<E>(u[e]);
+            } else if (w >= 4 && w < 4 + NCB) {
+                const int rb = (w - 4) / 2, cb = (w - 4) % 2;
+                f32x4 dr = zero4();
+                tmma<E>(dr, Ttt, LCK, 16 * rb, dUt + 16 * cb * LCK, LCK, 0, CK, l);
+                E* dvg = reinterpret_cast<E*>(p.dv) + tok * p.DV + v0;
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
+                    if (r < valid) dvg[(size_t)r * p.DV + i] = from_f32<E>(dr[e]);
+                    dXs[r * LBV + i] = from_f32<E>(-gam[r] * dr[e]);
+                }
+            }
+            __syncthreads();
+            // ---- accumulate over the block's value channels
+    #pragma unroll
+            for (int u = 0; u < NQW; ++u) {
+                const int t = w + NW * u;
+                if (t < NQT) {
+                    const int rb = t / NJ, jb = t % NJ;
+                    tmma<E>(dQa[u], gdOs, LBV, 16 * rb, S0t, LBV, 16 * jb, kBV, l);
+                    tmma<E>(dKa[u], dXs, LBV, 16 * rb, S0t, LBV, 16 * jb, kBV, l);
+                    tmma<E>(dKd[u], Us, LBV, 16 * rb, dSt, LBV, 16 * jb, kBV, l);
+                }
+            }
+            if (w < NCC) {
+                const int rb = w / NB, sb = w % NB;
+                tmma<E>(dPa, dOs, LBV, 16 * rb, Us, LBV, 16 * sb, kBV, l);
+                tmma<E>(dTa, dUs, LBV, 16 * rb, Rs, LBV, 16 * sb, kBV, l);
+            }
         }
     }
     __syncthreads();   // the block region is reused below
+    // the next chunk's keys, queries and gates: issued here rather than at the
+    // chunk's start, so that no wait at the value loop's entry covers them
+    if (nxt < p.total) fetch_chunk(nxt, tid);
 
     // ---- the dg terms that sum over key channels, from the accumulators
     // before the score terms join them, per row r:
@@ -1214,7 +1471,13 @@ struct GradChLds : Strides<E, DK, CK> {
     static constexpr int off_V = off_dUt + kBVC * S::LCK * ES; // [CK][LBF] f32
     static constexpr int blk_end = off_V + CK * LBF * 4;
     // last phases, over the block region
-    static constexpr int off_dTt = off_blk;                    // [CK][LF] f32 (triangular part)
+    // bf16, C = 32: double-buffered block inputs, then the last phases' region
+    // (whose start also holds the block intermediates during the value loop)
+    static constexpr bool LEAN = (ES == 2 && CK == 32);
+    static constexpr int off_lean = off_blk;
+    static constexpr int off_tail = LEAN ? off_blk + 2 * LeanVB<DK>::IN : off_blk;
+    static constexpr int off_lx = off_tail;
+    static constexpr int off_dTt = off_tail;                   // [CK][LF] f32 (triangular part)
     static constexpr int off_dTb = off_dTt + FCC;
     static constexpr int off_Y1t = off_dTb + FCC;
     static constexpr int off_dA = off_Y1t + FCC;
@@ -1223,10 +1486,11 @@ struct GradChLds : Strides<E, DK, CK> {
     static constexpr int off_dAb = off_dPMt + ECC;
     static constexpr int off_dAbt = off_dAb + ECC;
     static constexpr int pair_end = off_dAbt + ECC;
-    static constexpr int off_dGm = off_blk;                    // [CK][LG] f32 (after the pairs)
+    static constexpr int off_dGm = off_tail;                   // [CK][LG] f32 (after the pairs)
     static constexpr int off_Y3Kd = off_dGm + CK * LG * 4;
     static constexpr int last_end = off_Y3Kd + CK * LG * 4;
-    static constexpr int m1 = blk_end > pair_end ? blk_end : pair_end;
+    static constexpr int lx_end = off_lx + LeanVB<DK>::XB;
+    static constexpr int m1 = LEAN ? (lx_end > pair_end ? lx_end : pair_end) : (blk_end > pair_end ? blk_end : pair_end);
     static constexpr int bytes = m1 > last_end ? m1 : last_end;
 };
 
@@ -1316,9 +1580,23 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
             da[u] = ld16(dog + (size_t)r * p.DV + v0 + cc);
         }
     };
+    // (bf16, C = 32) the lean value blocks' staging: block 0 into buffer 0,
+    // the block after it into registers
+    LeanPf<DK> lpf;
+    int lbk = 0, lpc = blockIdx.x, lpv0 = 0;
     if ((int)blockIdx.x < p.total) {
         fetch_chunk(blockIdx.x, threadIdx.x);
-        fetch_block(blockIdx.x, 0, threadIdx.x);
+        if constexpr (LY::LEAN) {
+            if (threadIdx.x < 256) {
+                lpf.load(p, lpc, 0, threadIdx.x);
+                lpf.store(smem + LY::off_lean, threadIdx.x);
+                if (p.DV > 32) lpv0 = 32;
+                else lpc += gridDim.x;
+                if (lpc < p.total) lpf.load(p, lpc, lpv0, threadIdx.x);
+            }
+        } else {
+            fetch_block(blockIdx.x, 0, threadIdx.x);
+        }
     }
     for (int cid = blockIdx.x; cid < p.total; cid += gridDim.x) {
     // lane-dependent values are re-derived per chunk (see vlane)
@@ -1356,7 +1634,6 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
 #pragma unroll
         for (int j = 0; j < VE; ++j) Pt[tok_of_col(CK, mc0 + j) * LCK + r] = pe[j];
     }
-    if (nxt < p.total) fetch_chunk(nxt, tid);
     __syncthreads();
     // cumulative sum down every key channel (the column is read whole first)
     if (tid < DK) {
@@ -1445,104 +1722,118 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
     for (int u = 0; u < NSV; ++u)
 #pragma unroll
         for (int e = 0; e < VE; ++e) hacc[u][e] = 0.f;
+    if constexpr (LY::LEAN) {
+        float hs8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        lean_value_blocks<DK, false, NQW>(p, smem, LY::off_lean, LY::off_lx, Kgs, Kds, Pt, Tt, Ttt, nullptr, nullptr,
+                                          cid, tid, lbk, lpf, lpc, lpv0, Y1, Y2, Y3, dPa, dTa, hs8);
+        // dX S0 = -dR S0
+#pragma unroll
+        for (int u = 0; u < NQW; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Y2[u][e] = -Y2[u][e];
+        static_assert(NSV == 1 || !LY::LEAN, "one staged vector per thread");
+#pragma unroll
+        for (int e = 0; e < VE; ++e) hacc[0][e] = hs8[e];
+    } else {
     for (int v0 = 0; v0 < p.DV; v0 += kBVC) {
-        __syncthreads();   // the previous block's operands are consumed
-#pragma unroll
-        for (int u = 0; u < NSV; ++u) {
-            const int xs = tid + NT * u, i = xs % kBVC, j = VE * (xs / kBVC);
-            if (xs >= kBVC * DK / VE) continue;
-            E a[VE], b[VE];
-            __builtin_memcpy(a, &sa[u], 16);
-            __builtin_memcpy(b, &sb[u], 16);
-            st16(S0s + i * LDK + j, sa[u]);
-            st16(dSs + i * LDK + j, sb[u]);
-#pragma unroll
-            for (int e = 0; e < VE; ++e) {
-                S0t[(j + e) * LB + i] = a[e];
-                dSt[(j + e) * LB + i] = b[e];
-                hacc[u][e] += to_f32(a[e]) * to_f32(b[e]);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < NVV; ++u) {
-            const int x = tid + NT * u, r = x % CK, c = (x / CK) * VE;
-            if (x < CK * PERV) {
-                float a[VE];
-                E d[VE];
-                const u32x4 dz = r < valid ? da[u] : u32x4{0u, 0u, 0u, 0u};
-                Pack<E>::unpack(r < valid ? va[u] : u32x4{0u, 0u, 0u, 0u}, a);
-                __builtin_memcpy(d, &dz, 16);
-#pragma unroll
-                for (int j = 0; j < VE; ++j) {
-                    Vs[r * LBF + c + j] = a[j];
-                    dOs[r * LB + c + j] = d[j];
-                    dOt[(c + j) * LCK + r] = d[j];
+            __syncthreads();   // the previous block's operands are consumed
+    #pragma unroll
+            for (int u = 0; u < NSV; ++u) {
+                const int xs = tid + NT * u, i = xs % kBVC, j = VE * (xs / kBVC);
+                if (xs >= kBVC * DK / VE) continue;
+                E a[VE], b[VE];
+                __builtin_memcpy(a, &sa[u], 16);
+                __builtin_memcpy(b, &sb[u], 16);
+                st16(S0s + i * LDK + j, sa[u]);
+                st16(dSs + i * LDK + j, sb[u]);
+    #pragma unroll
+                for (int e = 0; e < VE; ++e) {
+                    S0t[(j + e) * LB + i] = a[e];
+                    dSt[(j + e) * LB + i] = b[e];
+                    hacc[u][e] += to_f32(a[e]) * to_f32(b[e]);
                 }
             }
-        }
-        if (v0 + kBVC < p.DV) fetch_block(cid, v0 + kBVC, tid);
-        else if (nxt < p.total) fetch_block(nxt, 0, tid);
-        __syncthreads();
-        // ---- R = V - Kg S0^T (waves 0..NCB-1); dU = P^T dO + Kd dS^T (waves 4..)
-        if (w < NCB) {
-            const int rb = w / 2, cb = w % 2;
-            f32x4 x = zero4();
-            tmma<E>(x, Kgs, LDK, 16 * rb, S0s, LDK, 16 * cb, DK, l);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
-                const float rr = Vs[r * LBF + i] - x[e];
-                Rs[r * LB + i] = from_f32<E>(rr);
-                Rt[i * LCK + r] = from_f32<E>(rr);
+    #pragma unroll
+            for (int u = 0; u < NVV; ++u) {
+                const int x = tid + NT * u, r = x % CK, c = (x / CK) * VE;
+                if (x < CK * PERV) {
+                    float a[VE];
+                    E d[VE];
+                    const u32x4 dz = r < valid ? da[u] : u32x4{0u, 0u, 0u, 0u};
+                    Pack<E>::unpack(r < valid ? va[u] : u32x4{0u, 0u, 0u, 0u}, a);
+                    __builtin_memcpy(d, &dz, 16);
+    #pragma unroll
+                    for (int j = 0; j < VE; ++j) {
+                        Vs[r * LBF + c + j] = a[j];
+                        dOs[r * LB + c + j] = d[j];
+                        dOt[(c + j) * LCK + r] = d[j];
+                    }
+                }
             }
-        } else if (w >= 4 && w < 4 + NCB) {
-            const int rb = (w - 4) / 2, cb = (w - 4) % 2;
-            f32x4 du = zero4();
-            tmma<E>(du, Kds, LDK, 16 * rb, dSs, LDK, 16 * cb, DK, l);
-            tmma<E>(du, Pt, LCK, 16 * rb, dOt + 16 * cb * LCK, LCK, 0, CK, l);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
-                dUs[r * LB + i] = from_f32<E>(du[e]);
-                dUt[i * LCK + r] = from_f32<E>(du[e]);
+            if (v0 + kBVC < p.DV) fetch_block(cid, v0 + kBVC, tid);
+            else if (nxt < p.total) fetch_block(nxt, 0, tid);
+            __syncthreads();
+            // ---- R = V - Kg S0^T (waves 0..NCB-1); dU = P^T dO + Kd dS^T (waves 4..)
+            if (w < NCB) {
+                const int rb = w / 2, cb = w % 2;
+                f32x4 x = zero4();
+                tmma<E>(x, Kgs, LDK, 16 * rb, S0s, LDK, 16 * cb, DK, l);
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
+                    const float rr = Vs[r * LBF + i] - x[e];
+                    Rs[r * LB + i] = from_f32<E>(rr);
+                    Rt[i * LCK + r] = from_f32<E>(rr);
+                }
+            } else if (w >= 4 && w < 4 + NCB) {
+                const int rb = (w - 4) / 2, cb = (w - 4) % 2;
+                f32x4 du = zero4();
+                tmma<E>(du, Kds, LDK, 16 * rb, dSs, LDK, 16 * cb, DK, l);
+                tmma<E>(du, Pt, LCK, 16 * rb, dOt + 16 * cb * LCK, LCK, 0, CK, l);
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
+                    dUs[r * LB + i] = from_f32<E>(du[e]);
+                    dUt[i * LCK + r] = from_f32<E>(du[e]);
+                }
             }
-        }
-        __syncthreads();
-        // ---- U = T~ R (waves 0..); dR = T~^T dU (= dV), dX = -dR (waves 4..)
-        if (w < NCB) {
-            const int rb = w / 2, cb = w % 2;
-            f32x4 u = zero4();
-            tmma<E>(u, Tt, LCK, 16 * rb, Rt + 16 * cb * LCK, LCK, 0, CK, l);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Us[(16 * rb + 4 * g4 + e) * LB + 16 * cb + c16] = from_f32<E>(u[e]);
-        } else if (w >= 4 && w < 4 + NCB) {
-            const int rb = (w - 4) / 2, cb = (w - 4) % 2;
-            f32x4 dr = zero4();
-            tmma<E>(dr, Ttt, LCK, 16 * rb, dUt + 16 * cb * LCK, LCK, 0, CK, l);
-            E* dvg = reinterpret_cast<E*>(p.dv) + tok * p.DV + v0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
-                if (r < valid) dvg[(size_t)r * p.DV + i] = from_f32<E>(dr[e]);
-                dXs[r * LB + i] = from_f32<E>(-dr[e]);
+            __syncthreads();
+            // ---- U = T~ R (waves 0..); dR = T~^T dU (= dV), dX = -dR (waves 4..)
+            if (w < NCB) {
+                const int rb = w / 2, cb = w % 2;
+                f32x4 u = zero4();
+                tmma<E>(u, Tt, LCK, 16 * rb, Rt + 16 * cb * LCK, LCK, 0, CK, l);
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) Us[(16 * rb + 4 * g4 + e) * LB + 16 * cb + c16] = from_f32<E>(u[e]);
+            } else if (w >= 4 && w < 4 + NCB) {
+                const int rb = (w - 4) / 2, cb = (w - 4) % 2;
+                f32x4 dr = zero4();
+                tmma<E>(dr, Ttt, LCK, 16 * rb, dUt + 16 * cb * LCK, LCK, 0, CK, l);
+                E* dvg = reinterpret_cast<E*>(p.dv) + tok * p.DV + v0;
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rb + 4 * g4 + e, i = 16 * cb + c16;
+                    if (r < valid) dvg[(size_t)r * p.DV + i] = from_f32<E>(dr[e]);
+                    dXs[r * LB + i] = from_f32<E>(-dr[e]);
+                }
             }
-        }
-        __syncthreads();
-        // ---- accumulate over the block's value channels
-#pragma unroll
-        for (int u = 0; u < NQW; ++u) {
-            const int t = w + NW * u;
-            if (t < NQT) {
-                const int rb = t / NJ, jb = t % NJ;
-                tmma<E>(Y1[u], dOs, LB, 16 * rb, S0t, LB, 16 * jb, kBVC, l);
-                tmma<E>(Y2[u], dXs, LB, 16 * rb, S0t, LB, 16 * jb, kBVC, l);
-                tmma<E>(Y3[u], Us, LB, 16 * rb, dSt, LB, 16 * jb, kBVC, l);
+            __syncthreads();
+            // ---- accumulate over the block's value channels
+    #pragma unroll
+            for (int u = 0; u < NQW; ++u) {
+                const int t = w + NW * u;
+                if (t < NQT) {
+                    const int rb = t / NJ, jb = t % NJ;
+                    tmma<E>(Y1[u], dOs, LB, 16 * rb, S0t, LB, 16 * jb, kBVC, l);
+                    tmma<E>(Y2[u], dXs, LB, 16 * rb, S0t, LB, 16 * jb, kBVC, l);
+                    tmma<E>(Y3[u], Us, LB, 16 * rb, dSt, LB, 16 * jb, kBVC, l);
+                }
             }
-        }
-        if (w < NCC) {
-            const int rb = w / NB, sb = w % NB;
-            tmma<E>(dPa, dOs, LB, 16 * rb, Us, LB, 16 * sb, kBVC, l);
-            tmma<E>(dTa, dUs, LB, 16 * rb, Rs, LB, 16 * sb, kBVC, l);
+            if (w < NCC) {
+                const int rb = w / NB, sb = w % NB;
+                tmma<E>(dPa, dOs, LB, 16 * rb, Us, LB, 16 * sb, kBVC, l);
+                tmma<E>(dTa, dUs, LB, 16 * rb, Rs, LB, 16 * sb, kBVC, l);
+            }
         }
     }
     // <dS_end, S0> per key channel: the kBVC threads that staged the same
@@ -1564,6 +1855,9 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
             for (int e = 0; e < VE; ++e) hC[j + e] = hacc[u][e];
     }
     __syncthreads();   // the block region is reused below
+    // the next chunk's inputs: issued here rather than at the chunk's start,
+    // so that no wait at the value loop's entry covers them
+    if (nxt < p.total) fetch_chunk(nxt, tid);
     // ---- triangular part: dPM, dT~; dA = strictly-lower(-T^T dT~ diag(beta) T^T)
     if (w < NCC) {
         const int rb = w / NB, sb = w % NB;

@@ -551,6 +551,9 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
         for (int j = 0; j < LY::NCT; ++j) offT[j] = tile_off(ST{}, j, CK * ES, CK);
 
         const int cw = w - 4;   // which copier
+        // Q and the score block feed only the outputs: a call that keeps only the
+        // states entering the chunks (the backward's recomputation) skips them
+        const bool need_q = keyrows || p.o != nullptr;
         const unsigned char* kb = static_cast<const unsigned char*>(p.k);
         const unsigned char* qb = static_cast<const unsigned char*>(p.q);
         const unsigned char* vbs = static_cast<const unsigned char*>(p.v);
@@ -581,14 +584,14 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
                 if (cw == 0) {
                     copy(LY::rK + J * szK, rec + WL.KG, offK, NK{}, szK);
                     copy(LY::rKU + J * szK, rec + WL.KD, offK, NK{}, szK);
-                } else {
+                } else if (need_q) {
                     copy(LY::rQ + J * szK, rec + WL.QG, offK, NK{}, szK);
                 }
             }
             if (valid == CK) {
                 if constexpr (!CH) {
                     if (cw == 0) copy(LY::rK + J * szK, kb + row0 * DK * ES, offK, NK{}, szK);
-                    else copy(LY::rQ + J * szK, qb + row0 * DK * ES, offK, NK{}, szK);
+                    else if (need_q) copy(LY::rQ + J * szK, qb + row0 * DK * ES, offK, NK{}, szK);
                 }
                 if (vt && !keyrows) copy(LY::rV + J * szV, vbs + (row0 * p.DV + v0) * ES, offV, NV{}, szV);
             } else {
@@ -600,12 +603,12 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
                 for (int j = 0; j < LY::NCV; ++j) rV[j] = tile_off(SV{}, j, p.DV * ES, valid);
                 if constexpr (!CH) {
                     if (cw == 0) copy(LY::rK + J * szK, kb + row0 * DK * ES, rK, NK{}, szK);
-                    else copy(LY::rQ + J * szK, qb + row0 * DK * ES, rK, NK{}, szK);
+                    else if (need_q) copy(LY::rQ + J * szK, qb + row0 * DK * ES, rK, NK{}, szK);
                 }
                 if (vt && !keyrows) copy(LY::rV + J * szV, vbs + (row0 * p.DV + v0) * ES, rV, NV{}, szV);
             }
             if (vt) copy(LY::rT + J * szT, rec + WL.T, offT, NT{}, szT);
-            if (cw == 1) copy(LY::rM + J * szT, rec + WL.M, offT, NT{}, szT);
+            if (cw == 1 && need_q) copy(LY::rM + J * szT, rec + WL.M, offT, NT{}, szT);
             if (cw == 0) {
 #pragma unroll
                 for (int j = 0; j < LY::NCF; ++j) {
@@ -623,6 +626,7 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
             if (!more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             else if (cw == 0 && !keyrows) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS0) : "memory");
             else if (cw == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NOPS0K) : "memory");
+            else if (!need_q) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS1 - LY::NCK - LY::NCT) : "memory");
             else if (!keyrows) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS1) : "memory");
             else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NOPS1K) : "memory");
         };
