@@ -682,9 +682,10 @@ __global__ __launch_bounds__(384, 1) void chunk_bwd_chain_kernel(BwdParams p)
 // chunks.  Per block of 32 value channels (scalar alpha; channel alpha uses
 // K . exp(G) for the first K, K . exp(G_C - G) for the second and no gamma, D):
 //   A: R = V - gamma . K S0^T (waves 0..3), dU = P^T dO + D . K dS^T (waves 4..7)
-//   B: U = T~ R (waves 0..3), dR = T~^T dU (waves 4..7, which also store dv)
-//   C: dO S0, dR S0, U dS, dO U^T, dU R^T accumulated (all waves); waves 0..3
-//      stage the next block into the free buffer and read the one after it
+//   B: U = T~ R (waves 0..3, which then stage the next block into the free
+//      buffer and read the one after it), dR = T~^T dU (waves 4..7, which
+//      also store dv)
+//   C: dO S0, dR S0, U dS, dO U^T, dU R^T accumulated (all waves)
 // R, dU, U, dR are kept as [value channel][token] bf16 rows (one 8-byte store
 // per result tile); every operand is a 16-byte row read or a transposing read
 // (ds_read_b64_tr_b16) of a padded row-major tile, so no transposed copy is
@@ -835,6 +836,18 @@ __device__ __forceinline__ void lean_value_blocks(
             mma(z, rowf((up ? tf : tft) + ((16 * tt + c16) * LB + 8 * g4) * 2),
                 rowf(xb + (up ? LV::oR : LV::odU) + ((16 * cb + c16) * LB + 8 * g4) * 2));
             st4bf(xb + (up ? LV::oU : LV::odR) + ((16 * cb + c16) * LB + 16 * tt + 4 * g4) * 2, z);
+            // waves 0..3: the next block into the free buffer (its reads were
+            // issued a block ago), then read the one after it
+            if (up && pc < p.total) {
+                pf.store(smem + in_off + ((bk + 1) & 1) * LV::IN, tid);
+                if (pv0 + 32 < p.DV) {
+                    pv0 += 32;
+                } else {
+                    pv0 = 0;
+                    pc += gridDim.x;
+                }
+                if (pc < p.total) pf.load(p, pc, pv0, tid);
+            }
             if (!up) {
                 bf16* dvg = reinterpret_cast<bf16*>(p.dv) + tok * p.DV + v0 + 16 * cb + c16;
 #pragma unroll
@@ -873,17 +886,6 @@ __device__ __forceinline__ void lean_value_blocks(
             Pack<bf16>::unpack(ld16(ib + LV::odS + (i * LDK + j) * 2), b);
 #pragma unroll
             for (int e = 0; e < 8; ++e) hs[e] += a[e] * b[e];
-        }
-        // waves 0..3: the next block into the free buffer, then read the one after it
-        if (w < 4 && pc < p.total) {
-            pf.store(smem + in_off + ((bk + 1) & 1) * LV::IN, tid);
-            if (pv0 + 32 < p.DV) {
-                pv0 += 32;
-            } else {
-                pv0 = 0;
-                pc += gridDim.x;
-            }
-            if (pc < p.total) pf.load(p, pc, pv0, tid);
         }
         __syncthreads();
     }

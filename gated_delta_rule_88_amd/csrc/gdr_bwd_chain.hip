@@ -24,13 +24,16 @@
 //   waves 2, 3 (pre)     one chunk ahead of the owners: P^T dO for their 16
 //                        value channels (scalar alpha: P from Q K^T and the
 //                        record's Gamma; channel: the record's P), handed to
-//                        the owners through LDS; and the store of the dS the
-//                        owners published a step before (the gradient kernel
-//                        reads it);
+//                        the owners through LDS;
 //   waves 4, 5 (copiers) direct global->LDS copies of the chunk three steps
-//                        ahead.
+//                        ahead;
+//   wave 6 (storer)      the store of the dS the owners published a step
+//                        before (the gradient kernel reads it).
 // T~^T, P^T (channel), Gamma^T, Q^T, K^T and dO^T come from transposing LDS
-// reads (ds_read_b64_tr_b16), so nothing is transposed on its way in.
+// reads (ds_read_b64_tr_b16), so nothing is transposed on its way in.  The
+// compiler makes a transposing read wait for every outstanding global memory
+// operation of its wave, so the waves that use them issue no global stores:
+// the dS stores have a wave of their own.
 #include "gdr_device.h"
 #include "gdr_chunk.h"
 #include "gdr_pipe.h"
@@ -65,12 +68,12 @@ __device__ __forceinline__ Frag<bf16> tr_pair(const unsigned char* base, int off
 }
 
 template <int DK, int MODE>
-__global__ __launch_bounds__(64 * 6) void chunk_bwd_chain_pipe_kernel(BwdParams p)
+__global__ __launch_bounds__(64 * 7) void chunk_bwd_chain_pipe_kernel(BwdParams p)
 {
     using E = bf16;
     constexpr int CK = 32;
-    using LY = ScanLayout<E, DK, CK, MODE>;
     using CL = ChainPipeLayout<DK, MODE>;
+    using LY = typename CL::LY;
     using SK = Swz<E, DK>;
     using SV = Swz<E, LY::BV>;
     using ST = Swz<E, CK>;
@@ -81,11 +84,12 @@ __global__ __launch_bounds__(64 * 6) void chunk_bwd_chain_pipe_kernel(BwdParams 
     constexpr int RBK = SK::RB, RBV = SV::RB, RBT = ST::RB;
     constexpr int XSB = CL::XSB, XVB = CL::XVB;
     constexpr WsLayout WL = ws_layout(ES, DK, CK, MODE);
-    static_assert(NSLOT == 4, "three chunks in flight ahead of the owners");
+    static_assert(NSLOT == 4, "slot ring");
+    constexpr int LEADC = NSLOT - 2;   // the copier fills step u + LEADC in iteration u
     extern __shared__ __align__(16) unsigned char smem[];
 
-    // Role index w: 0, 1 owners, 2, 3 pre, 4, 5 copiers; wave i runs on SIMD
-    // i % 4, so waves 2, 3 take the owners (a SIMD each).
+    // Role index w: 0, 1 owners, 2, 3 pre, 4, 5 copiers, 6 storer; wave i runs
+    // on SIMD i % 4, so waves 2, 3 take the owners (a SIMD each).
     const int hw = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int w = hw < 2 ? hw + 2 : (hw < 4 ? hw - 2 : hw);
     const int l = lane_id(), g4 = l >> 4, c16 = l & 15;
@@ -258,7 +262,6 @@ __global__ __launch_bounds__(64 * 6) void chunk_bwd_chain_pipe_kernel(BwdParams 
     } else if (w < 4) {
         // ========================================================= pre waves
         const int c = w - 2, vw = v0 + 16 * c;
-        const int oXS = lane_base(CL::rxS + (c * NKS * kWave + l) * FS);
         const int oXV = lane_base(CL::rxV + (c * NB * kWave + l) * 16);
         const int oVt = lane_base(LY::rV + SV::off(4 * g4 + (c16 >> 2), 16 * c + 4 * (c16 & 3)));
         const int oMt = lane_base(LY::rM + oTr);
@@ -266,15 +269,6 @@ __global__ __launch_bounds__(64 * 6) void chunk_bwd_chain_pipe_kernel(BwdParams 
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) oQ[ks] = lane_base(LY::rQ + oKQ[ks]);
 
-        // the dS the owners published at step s (chunk NC - 1 - s), parity PC
-        auto store_dS = [&](auto pc, int s) {
-            constexpr int PS = decltype(pc)::value * XSB;
-            const int n = NC - 1 - s;
-            E* ck = static_cast<E*>(p.dSck) + (((size_t)bh * NC + n) * p.DV + vw + c16) * DK + 8 * g4;
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                st16(ck + 32 * ks, *reinterpret_cast<const u32x4*>(smem + oXS + PS + ks * kWave * FS));
-        };
         // P^T dO of step j (slot J) for value channels 16c .., into parity J & 1:
         // lane holds (P^T dO)[16tt + 4g + e][16c + c16]
         auto pre = [&](auto jc, int j) {
@@ -331,13 +325,40 @@ __global__ __launch_bounds__(64 * 6) void chunk_bwd_chain_pipe_kernel(BwdParams 
             }
         };
         step_barrier();
-        // iteration u: P^T dO of step u, and the store of step u - 2's dS
+        // iteration u: P^T dO of step u
         for (int u0 = 0; u0 <= NC; u0 += NSLOT) {
             auto step = [&](auto jc) {
                 constexpr int J = decltype(jc)::value;
                 const int u = u0 + J;
                 if (u <= NC) {
                     if (u < NC) pre(jc, u);
+                    step_barrier();
+                }
+            };
+            StaticFor<0, NSLOT>::run(step);
+        }
+    } else if (w == 6) {
+        // ========================================================= storer
+        // the dS the owners published at step s (chunk NC - 1 - s), parity PC:
+        // owner o's value rows v0 + 16 o + c16, key channels 32 ks + 8 g4 ..
+        auto store_dS = [&](auto pc, int s) {
+            constexpr int PS = decltype(pc)::value * XSB;
+            const int n = NC - 1 - s;
+#pragma unroll
+            for (int o = 0; o < 2; ++o) {
+                E* ck = static_cast<E*>(p.dSck) + (((size_t)bh * NC + n) * p.DV + v0 + 16 * o + c16) * DK + 8 * g4;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    st16(ck + 32 * ks, *reinterpret_cast<const u32x4*>(smem + CL::rxS + PS + ((o * NKS + ks) * kWave + l) * FS));
+            }
+        };
+        step_barrier();
+        // iteration u: the store of step u - 2's dS
+        for (int u0 = 0; u0 <= NC; u0 += NSLOT) {
+            auto step = [&](auto jc) {
+                constexpr int J = decltype(jc)::value;
+                const int u = u0 + J;
+                if (u <= NC) {
                     if (u >= 2) store_dS(std::integral_constant<int, J & 1>{}, u - 2);
                     step_barrier();
                 }
@@ -429,25 +450,35 @@ __global__ __launch_bounds__(64 * 6) void chunk_bwd_chain_pipe_kernel(BwdParams 
                 }
             }
         };
-        // wait until every chunk issued before the last one has landed
-        auto wait_prev = [&](bool more) {
-            if (!more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            else if (cw == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS0) : "memory");
-            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS1) : "memory");
+        // wait until at most k chunks' copies of this copier are in flight
+        static_assert((NSLOT - 3) * LY::NOPS0 < 64 && (NSLOT - 3) * LY::NOPS1 < 64, "vmcnt range");
+        auto wait_k = [&](int k) {
+            auto one = [&](auto kc) {
+                constexpr int K = decltype(kc)::value;
+                if (k == K) {
+                    if (cw == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K * LY::NOPS0) : "memory");
+                    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K * LY::NOPS1) : "memory");
+                }
+            };
+            StaticFor<0, NSLOT - 2>::run(one);
         };
-        issue(std::integral_constant<int, 0>{}, 0);
-        if (NC > 1) issue(std::integral_constant<int, 1>{}, 1);
-        wait_prev(NC > 1);   // step 0 has landed
+        // prologue: steps 0 .. LEADC - 1, then wait for step 0
+        auto pro = [&](auto kc) {
+            constexpr int K = decltype(kc)::value;
+            if (K < NC) issue(kc, K);
+        };
+        StaticFor<0, LEADC>::run(pro);
+        wait_k(min(LEADC - 1, NC - 1));
         step_barrier();
-        // iteration u: fill step u + 2 into slot (u + 2) % NSLOT, then wait for step u + 1
+        // iteration u: fill step u + LEADC into slot (u + LEADC) % NSLOT, then
+        // wait for step u + 1
         for (int u0 = 0; u0 <= NC; u0 += NSLOT) {
             auto step = [&](auto jc) {
                 constexpr int J = decltype(jc)::value;
                 const int u = u0 + J;
                 if (u <= NC) {
-                    const bool more = u + 2 < NC;
-                    if (more) issue(std::integral_constant<int, (J + 2) % NSLOT>{}, u + 2);
-                    wait_prev(more);
+                    if (u + LEADC < NC) issue(std::integral_constant<int, (J + LEADC) % NSLOT>{}, u + LEADC);
+                    wait_k(max(0, min(LEADC - 1, NC - 2 - u)));
                     step_barrier();
                 }
             };
@@ -464,7 +495,7 @@ hipError_t launch_t(const BwdParams& bp, int BH, hipStream_t stream)
     auto* kern = chunk_bwd_chain_pipe_kernel<DK, MODE>;
     hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, CL::bytes);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, dim3(BH * (bp.DV / 32)), dim3(64 * 6), CL::bytes, stream, bp);
+    hipLaunchKernelGGL(kern, dim3(BH * (bp.DV / 32)), dim3(64 * 7), CL::bytes, stream, bp);
     return hipGetLastError();
 }
 
