@@ -47,16 +47,20 @@ FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 matrix
 # the same counters read for a 1 GiB device copy (FETCH_SIZE x 2, WRITE_SIZE x 1
 # on this chip), with a digest of the kernel sources they were taken on: a
 # figure whose sources have changed since is reported as null.
+FWD_SOURCES = ('gdr_wy.hip', 'gdr_scan.hip', 'gdr_segment.hip', 'gdr_pipe.h', 'gdr_chunk.h', 'gdr_tri.h',
+               'gdr_fwd.hip', 'gdr_device.h', 'gdr_internal.h')
+BWD_SOURCES = FWD_SOURCES + ('gdr_bwd.hip', 'gdr_bwd_chain.hip', 'gdr_bwd.h')
 MEASURED_TRAFFIC = {
     ("gdn_bf16_B8_H8_L2048_d128", "chunk_wy_kernel + chunk_scan_kernel"):
-        dict(sources=('gdr_wy.hip', 'gdr_scan.hip', 'gdr_segment.hip', 'gdr_chunk.h', 'gdr_tri.h', 'gdr_fwd.hip', 'gdr_device.h', 'gdr_internal.h'),
-             digest="05522eb0d6529cc1", read=154.92e6, written=57.00e6),
+        dict(sources=FWD_SOURCES, digest="1d606e1d8c1aea41", read=154.66e6, written=56.78e6),
     ("kda_bf16_B4_H16_L4096_d128", "chunk_wy_channel_kernel + chunk_scan_kernel"):
-        dict(sources=('gdr_wy.hip', 'gdr_scan.hip', 'gdr_segment.hip', 'gdr_chunk.h', 'gdr_tri.h', 'gdr_fwd.hip', 'gdr_device.h', 'gdr_internal.h'),
-             digest="05522eb0d6529cc1", read=576.33e6, written=310.38e6),
+        dict(sources=FWD_SOURCES, digest="1d606e1d8c1aea41", read=576.28e6, written=310.38e6),
     ("gdn_decode_bf16_N256_H16_d128", "decode_step_kernel"):
-        dict(sources=('gdr_decode.hip', 'gdr_device.h', 'gdr_internal.h'),
-             digest="cec6ec10f5861708", read=274.33e6, written=269.49e6),
+        dict(sources=('gdr_decode.hip', 'gdr_device.h', 'gdr_internal.h'), digest="881e53d339a2b9b0", read=274.33e6, written=269.50e6),
+    ("gdn_bf16_B8_H8_L2048_d128 backward", "chunk_wy_kernel + chunk_scan_kernel + chunk_bwd_chain_pipe_kernel + chunk_bwd_grad_kernel"):
+        dict(sources=BWD_SOURCES, digest="1166615f4dcf0acf", read=637.16e6, written=394.82e6),
+    ("kda_bf16_B4_H16_L4096_d128 backward", "chunk_wy_channel_kernel + chunk_scan_kernel + chunk_bwd_chain_pipe_kernel + chunk_bwd_grad_channel_kernel"):
+        dict(sources=BWD_SOURCES, digest="1166615f4dcf0acf", read=1890.87e6, written=1118.00e6),
 }
 
 
@@ -454,6 +458,12 @@ def main():
         gate = {gi.ALPHA_NONE: 0, gi.ALPHA_SCALAR: 4, gi.ALPHA_CHANNEL: 4 * w.dk}[w.mode]
         # read q, k, v, dO, beta, log alpha; write dq, dk, dv, dbeta, dlog alpha
         nbytes = ht * (es * (4 * w.dk + 3 * w.dv) + 8 + 2 * gate)
+        pipe = w.dtype == torch.bfloat16 and w.C >= 32   # 32-token steps: the pipelined chain
+        bwd_kernel = " + ".join((
+            "chunk_wy_channel_kernel" if w.mode == gi.ALPHA_CHANNEL else "chunk_wy_kernel",
+            "chunk_scan_kernel",
+            "chunk_bwd_chain_pipe_kernel" if pipe else "chunk_bwd_chain_kernel",
+            "chunk_bwd_grad_channel_kernel" if w.mode == gi.ALPHA_CHANNEL else "chunk_bwd_grad_kernel"))
         print(json.dumps({
             "metric": "tokens/s chunked gated delta-rule backward (gradients; forward recomputed "
                       "inside)",
@@ -465,12 +475,9 @@ def main():
                        "C": w.C, "alpha": gi.MODE_NAMES[w.mode], "workspace_bytes": r["ws_bytes"]},
             "roofline": {"bound": "hbm", "achieved": nbytes / (ms / 1e3) / 1e9,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
-                         "kernel": ("chunk_wy_channel_kernel + chunk_scan_kernel + "
-                                    "chunk_bwd_chain_kernel + chunk_bwd_grad_channel_kernel"
-                                    if w.mode == gi.ALPHA_CHANNEL else
-                                    "chunk_wy_kernel + chunk_scan_kernel + chunk_bwd_chain_kernel "
-                                    "+ chunk_bwd_grad_kernel"),
+                         "frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": measured_traffic(w.name + " backward", bwd_kernel),
+                         "kernel": bwd_kernel,
                          "algorithmic_bytes_per_call": nbytes},
         }))
         return
