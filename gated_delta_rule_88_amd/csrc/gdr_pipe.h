@@ -161,10 +161,15 @@ struct ScanLayout {
     static constexpr int rxS = rF + NSLOT * szF;                   // [parity][owner][ks][lane]
     static constexpr int rxU = rxS + 2 * XSB;                      // [parity][owner][lane]
     static constexpr int bytes = rxU + 2 * XUB;
-    static constexpr int NWAVES = 6;
-    // copy instructions per chunk.  Copier 0 takes K (and K.exp(G_C - G)) and
-    // the decay factors, plus V and T~ unless alpha is per channel; copier 1
-    // the rest, which keeps the two within a few KiB of each other.
+    // copier waves of the forward scan: four for bf16 operands with channel
+    // alpha (whose 30 KiB of copies per step bound the step with two), else two
+    static constexpr int NCP = (CH && ES == 2) ? 4 : 2;
+    static constexpr int NWAVES = 4 + NCP;
+    // copy instructions per chunk.  Two copiers: copier 0 takes K (and
+    // K.exp(G_C - G)) and the decay factors, plus V and T~ unless alpha is per
+    // channel; copier 1 the rest, which keeps the two within a few KiB of each
+    // other.  Four copiers (channel alpha): K.exp(G) | K.exp(G_C - G) and the
+    // decay factors | Q.exp(G) | V, T~ and P.
     static constexpr int NCK = CopyCount<szK>::n, NCV = CopyCount<szV>::n, NCT = CopyCount<szT>::n;
     static constexpr int NCF = CopyCount<FB>::n;
     static constexpr int NOPS0 = (CH ? 2 : 1) * NCK + NCF + (CH ? 0 : NCV + NCT);

@@ -31,10 +31,10 @@
 //   waves 2, 3  (output waves)  for chunk n - 1, from the published S and U:
 //               the inter-chunk output diag(gamma) Q S^T, the masked score
 //               block P (MFMA), P U, and the store of o.
-//   waves 4, 5  (copiers)       direct global->LDS copies of chunk n + 2 (K,
-//               Q, the V block, T~, Gamma or P, the decay factors; the two
-//               split the regions), 16 bytes per lane, then wait until chunk
-//               n + 1 has landed.
+//   waves 4 ..  (copiers)       direct global->LDS copies of chunk n + 2 (K,
+//               Q, the V block, T~, Gamma or P, the decay factors; two
+//               copiers split the regions, four for bf16 channel alpha), 16
+//               bytes per lane, then wait until chunk n + 1 has landed.
 // Every product is v_mfma_f32_16x16x32_bf16 (fp32: 16x16x4f32) in NT form;
 // result tiles feed the next product straight from registers (tile-pair
 // operands, gdr_device.h).
@@ -59,7 +59,7 @@
 namespace gdr {
 
 template <typename E, int DK, int CK, int MODE>
-__global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
+__global__ __launch_bounds__(64 * 8) void chunk_scan_kernel(ScanParams p)
 {
     using LY = ScanLayout<E, DK, CK, MODE>;
     using SK = Swz<E, DK>;
@@ -75,10 +75,11 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
     extern __shared__ __align__(16) unsigned char smem[];
 
     // wave index as a scalar: the role branches below are wave-uniform
-    // Role index w: 0, 1 state owners, 2, 3 output waves, 4, 5 copiers.  The
+    // Role index w: 0, 1 state owners, 2, 3 output waves, 4 .. copiers.  The
     // hardware places wave i of a workgroup on SIMD i % 4, so waves 2, 3 run
-    // the owners (a SIMD each) and the copiers share SIMDs 0, 1 with the
-    // output waves.
+    // the owners (a SIMD each) and copiers 4, 5 share SIMDs 0, 1 with the
+    // output waves (copiers 6, 7, when there are four, share the owners'
+    // SIMDs: they issue copies and wait, little else).
     const int hw = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int w = hw < 2 ? hw + 2 : (hw < 4 ? hw - 2 : hw);
     const int l = lane_id(), g4 = l >> 4, c16 = l & 15;
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
             StaticFor<0, NSLOT>::run(step);
         }
     } else {
-        // ===================================================== copiers (waves 4, 5)
+        // ===================================================== copiers (waves 4 ..)
         // Per-lane source offsets of one chunk's tiles, as for a full chunk:
         // instruction j, lane l fills LDS bytes 1024 j + 16 l of the region,
         // i.e. row b / RB, physical chunk (b % RB) / 16, which holds logical
@@ -619,10 +620,60 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
                 }
             }
         };
+        // four copiers (channel alpha): K.exp(G) | K.exp(G_C - G) and the
+        // decay factors | Q.exp(G) | V, T~ and P
+        auto issue4 = [&](auto jc, int m) {
+            constexpr int J = decltype(jc)::value;
+            const int t0 = (c0 + m) * CK, valid = min(CK, len - t0);
+            const unsigned char* rec = p.ws + (rec0 + c0 + m) * WL.bytes;
+            const size_t row0 = tok0 + t0;
+            using NK = std::integral_constant<int, LY::NCK>;
+            using NV = std::integral_constant<int, LY::NCV>;
+            using NT = std::integral_constant<int, LY::NCT>;
+            if (cw == 0) {
+                copy(LY::rK + J * szK, rec + WL.KG, offK, NK{}, szK);
+            } else if (cw == 1) {
+                copy(LY::rKU + J * szK, rec + WL.KD, offK, NK{}, szK);
+#pragma unroll
+                for (int j = 0; j < LY::NCF; ++j) {
+                    if (LY::FB % 1024 == 0 || 1024 * j + 16 * l < LY::FB)
+                        __builtin_amdgcn_global_load_lds((const glb_void_t*)(rec + WL.F + 1024 * j + 16 * l),
+                                                         (lds_void_t*)(uintptr_t)(sbase + (uint32_t)(LY::rF + J * szF + 1024 * j)),
+                                                         16, 0, 0);
+                }
+            } else if (cw == 2) {
+                if (need_q) copy(LY::rQ + J * szK, rec + WL.QG, offK, NK{}, szK);
+            } else {
+                if (!keyrows) {
+                    if (valid == CK) {
+                        copy(LY::rV + J * szV, vbs + (row0 * p.DV + v0) * ES, offV, NV{}, szV);
+                    } else {
+                        // last, partial chunk: rows past the end repeat the last row
+                        uint32_t rV[LY::NCV];
+#pragma unroll
+                        for (int j = 0; j < LY::NCV; ++j) rV[j] = tile_off(SV{}, j, p.DV * ES, valid);
+                        copy(LY::rV + J * szV, vbs + (row0 * p.DV + v0) * ES, rV, NV{}, szV);
+                    }
+                }
+                copy(LY::rT + J * szT, rec + WL.T, offT, NT{}, szT);
+                if (need_q) copy(LY::rM + J * szT, rec + WL.M, offT, NT{}, szT);
+            }
+        };
         // wait until every chunk issued before the last one has landed
         // (the count is that of the last chunk's copies, without V for key rows)
         constexpr int NOPS0K = LY::NOPS0 - (CH ? 0 : LY::NCV), NOPS1K = LY::NOPS1 - (CH ? LY::NCV : 0);
         auto wait_prev = [&](bool more) {
+            if constexpr (LY::NCP == 4) {
+                if (!more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                else if (cw == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NCK) : "memory");
+                else if (cw == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NCK + LY::NCF) : "memory");
+                else if (cw == 2 && need_q) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NCK) : "memory");
+                else if (cw == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                else if (keyrows) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LY::NCT) : "memory");
+                else if (need_q) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NCV + 2 * LY::NCT) : "memory");
+                else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NCV + LY::NCT) : "memory");
+                return;
+            }
             if (!more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             else if (cw == 0 && !keyrows) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS0) : "memory");
             else if (cw == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NOPS0K) : "memory");
@@ -630,10 +681,14 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
             else if (!keyrows) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS1) : "memory");
             else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NOPS1K) : "memory");
         };
+        auto issue_any = [&](auto jc, int m) {
+            if constexpr (LY::NCP == 4) issue4(jc, m);
+            else issue(jc, m);
+        };
         {
             auto pro = [&](auto kc) {
                 constexpr int K = decltype(kc)::value;
-                if (K < NC) issue(kc, K);
+                if (K < NC) issue_any(kc, K);
             };
             StaticFor<0, AHEAD>::run(pro);
         }
@@ -647,7 +702,7 @@ __global__ __launch_bounds__(64 * 6) void chunk_scan_kernel(ScanParams p)
                 const int s = s0 + J;
                 if (s <= NC) {
                     const bool more = s + AHEAD < NC;
-                    if (more) issue(std::integral_constant<int, (J + AHEAD) % NSLOT>{}, s + AHEAD);
+                    if (more) issue_any(std::integral_constant<int, (J + AHEAD) % NSLOT>{}, s + AHEAD);
                     wait_prev(more);
                     step_barrier();
                 }
