@@ -94,6 +94,20 @@ template <int N> __device__ __forceinline__ f32x4 ldf4(const unsigned char* base
     return *reinterpret_cast<const f32x4*>(base + off + N);
 }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n in [LO, HI) (the count is an
+// instruction immediate: a binary dispatch over its values).
+template <int LO, int HI>
+__device__ __forceinline__ void vm_wait_range(int n) {
+    if constexpr (HI - LO == 1) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LO) : "memory");
+    } else {
+        constexpr int MID = (LO + HI) / 2;
+        if (n < MID) vm_wait_range<LO, MID>(n);
+        else vm_wait_range<MID, HI>(n);
+    }
+}
+__device__ __forceinline__ void vm_wait(int n) { vm_wait_range<0, 64>(n); }
+
 // Barrier for the pipeline: this wave's LDS accesses are complete, then all
 // waves meet.  It does not wait for outstanding global->LDS copies: the
 // copier waits for those explicitly.
@@ -133,7 +147,7 @@ struct CopyCount { static constexpr int n = (NBYTES + 1023) / 1024; };
 
 // MODE is kAlphaScalar or kAlphaChannel: alpha = 1 runs as scalar alpha with
 // log alpha = 0 (the prepass writes gamma = 1 and Gamma = the causal mask).
-template <typename E, int DK, int CK, int MODE>
+template <typename E, int DK, int CK, int MODE, int AHEAD_ = 2>
 struct ScanLayout {
     static_assert(MODE == kAlphaScalar || MODE == kAlphaChannel, "gate mode of the scan");
     static constexpr int ES = (int)sizeof(E);
@@ -141,7 +155,7 @@ struct ScanLayout {
     static constexpr bool CH = (MODE == kAlphaChannel);
     // Ring of chunk slots.  At step s the copier fills chunk s + AHEAD while
     // the state owners work on chunk s and the output waves on chunk s - 1.
-    static constexpr int AHEAD = 2;
+    static constexpr int AHEAD = AHEAD_;
     static constexpr int NSLOT = AHEAD + 2;
     static_assert(NSLOT % 2 == 0, "exchange parity follows the slot index");
     static constexpr int FB = CH ? DK * 4 : 4 * CK * 4;

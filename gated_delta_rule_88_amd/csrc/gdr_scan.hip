@@ -58,10 +58,12 @@
 
 namespace gdr {
 
-template <typename E, int DK, int CK, int MODE>
+// AH: chunks the copiers run ahead of the state owners (the slot ring holds
+// AH + 2 chunks).
+template <typename E, int DK, int CK, int MODE, int AH>
 __global__ __launch_bounds__(64 * 8) void chunk_scan_kernel(ScanParams p)
 {
-    using LY = ScanLayout<E, DK, CK, MODE>;
+    using LY = ScanLayout<E, DK, CK, MODE, AH>;
     using SK = Swz<E, DK>;
     using SV = Swz<E, LY::BV>;
     using ST = Swz<E, CK>;
@@ -578,9 +580,10 @@ __global__ __launch_bounds__(64 * 8) void chunk_scan_kernel(ScanParams p)
             using NK = std::integral_constant<int, LY::NCK>;
             using NV = std::integral_constant<int, LY::NCV>;
             using NT = std::integral_constant<int, LY::NCT>;
-            // V and T~ go with copier 0 unless alpha is per channel; key rows
+            // V and T~ go with copier 0 unless alpha is per channel or the call
+            // keeps only the states (then copier 1 has no Q to copy); key rows
             // have no V to copy
-            const bool vt = (cw == (CH ? 1 : 0));
+            const bool vt = (cw == ((CH || !need_q) ? 1 : 0));
             if constexpr (CH) {
                 if (cw == 0) {
                     copy(LY::rK + J * szK, rec + WL.KG, offK, NK{}, szK);
@@ -659,28 +662,23 @@ __global__ __launch_bounds__(64 * 8) void chunk_scan_kernel(ScanParams p)
                 if (need_q) copy(LY::rM + J * szT, rec + WL.M, offT, NT{}, szT);
             }
         };
-        // wait until every chunk issued before the last one has landed
-        // (the count is that of the last chunk's copies, without V for key rows)
-        constexpr int NOPS0K = LY::NOPS0 - (CH ? 0 : LY::NCV), NOPS1K = LY::NOPS1 - (CH ? LY::NCV : 0);
-        auto wait_prev = [&](bool more) {
-            if constexpr (LY::NCP == 4) {
-                if (!more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                else if (cw == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NCK) : "memory");
-                else if (cw == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NCK + LY::NCF) : "memory");
-                else if (cw == 2 && need_q) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NCK) : "memory");
-                else if (cw == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                else if (keyrows) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LY::NCT) : "memory");
-                else if (need_q) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NCV + 2 * LY::NCT) : "memory");
-                else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NCV + LY::NCT) : "memory");
-                return;
-            }
-            if (!more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            else if (cw == 0 && !keyrows) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS0) : "memory");
-            else if (cw == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NOPS0K) : "memory");
-            else if (!need_q) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS1 - LY::NCK - LY::NCT) : "memory");
-            else if (!keyrows) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LY::NOPS1) : "memory");
-            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NOPS1K) : "memory");
-        };
+        // this copier's copy instructions per chunk
+        int nops;
+        if constexpr (LY::NCP == 4) {
+            nops = cw == 0 ? LY::NCK
+                 : cw == 1 ? LY::NCK + LY::NCF
+                 : cw == 2 ? (need_q ? LY::NCK : 0)
+                 : (keyrows ? 0 : LY::NCV) + LY::NCT + (need_q ? LY::NCT : 0);
+        } else if (!need_q && !CH) {
+            nops = cw == 0 ? LY::NCK + LY::NCF : LY::NCV + LY::NCT;
+        } else if (cw == 0) {
+            nops = LY::NOPS0 - ((!CH && keyrows) ? LY::NCV : 0);
+        } else {
+            nops = need_q ? LY::NOPS1 - ((CH && keyrows) ? LY::NCV : 0) : LY::NOPS1 - LY::NCK - LY::NCT;
+        }
+        static_assert((AH - 1) * (LY::NOPS0 > LY::NOPS1 ? LY::NOPS0 : LY::NOPS1) < 64, "vmcnt range");
+        // wait until at most k chunks issued after the one needed next are in flight
+        auto wait_k = [&](int k) { vm_wait(k * nops); };
         auto issue_any = [&](auto jc, int m) {
             if constexpr (LY::NCP == 4) issue4(jc, m);
             else issue(jc, m);
@@ -692,18 +690,17 @@ __global__ __launch_bounds__(64 * 8) void chunk_scan_kernel(ScanParams p)
             };
             StaticFor<0, AHEAD>::run(pro);
         }
-        wait_prev(AHEAD - 1 < NC);   // chunks 0 .. AHEAD - 2 have landed
+        wait_k(min(AHEAD - 1, NC - 1));   // chunk 0 has landed
         step_barrier();
         // step s fills chunk s + AHEAD into slot (s + AHEAD) % NSLOT, then waits
-        // for chunk s + AHEAD - 1
+        // for chunk s + 1
         for (int s0 = 0; s0 <= NC; s0 += NSLOT) {
             auto step = [&](auto jc) {
                 constexpr int J = decltype(jc)::value;
                 const int s = s0 + J;
                 if (s <= NC) {
-                    const bool more = s + AHEAD < NC;
-                    if (more) issue_any(std::integral_constant<int, (J + AHEAD) % NSLOT>{}, s + AHEAD);
-                    wait_prev(more);
+                    if (s + AHEAD < NC) issue_any(std::integral_constant<int, (J + AHEAD) % NSLOT>{}, s + AHEAD);
+                    wait_k(max(0, min(AHEAD - 1, NC - 2 - s)));
                     step_barrier();
                 }
             };
@@ -713,10 +710,10 @@ __global__ __launch_bounds__(64 * 8) void chunk_scan_kernel(ScanParams p)
 }
 
 // ------------------------------------------------------------------ host side
-template <typename E, int DK, int CK, int MODE>
+template <typename E, int DK, int CK, int MODE, int AH>
 static hipError_t launch_scan_t(const ChunkArgs& a, const SegPlan& seg)
 {
-    using LY = ScanLayout<E, DK, CK, MODE>;
+    using LY = ScanLayout<E, DK, CK, MODE, AH>;
     static_assert(LY::bytes <= 160 * 1024, "LDS budget");
     const int BH = a.B * a.H;
     const int NC = (a.L + CK - 1) / CK;
@@ -730,7 +727,7 @@ static hipError_t launch_scan_t(const ChunkArgs& a, const SegPlan& seg)
         sp.Sseg = reinterpret_cast<float*>(ws + seg.off_Z);
         sp.Pseg = reinterpret_cast<float*>(ws + seg.off_P);
     }
-    auto* kern = chunk_scan_kernel<E, DK, CK, MODE>;
+    auto* kern = chunk_scan_kernel<E, DK, CK, MODE, AH>;
     hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LY::bytes);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(kern, dim3(total), dim3(64 * LY::NWAVES), LY::bytes, a.stream, sp);
@@ -740,9 +737,9 @@ static hipError_t launch_scan_t(const ChunkArgs& a, const SegPlan& seg)
 template <typename E, int DK, int CK>
 static hipError_t launch_scan_m(const ChunkArgs& a, const SegPlan& sp)
 {
-    if (a.mode == kAlphaChannel) return launch_scan_t<E, DK, CK, kAlphaChannel>(a, sp);
+    if (a.mode == kAlphaChannel) return launch_scan_t<E, DK, CK, kAlphaChannel, 2>(a, sp);
     // scalar alpha, and alpha = 1 as log alpha = 0 (the prepass wrote gamma = 1)
-    return launch_scan_t<E, DK, CK, kAlphaScalar>(a, sp);
+    return launch_scan_t<E, DK, CK, kAlphaScalar, 2>(a, sp);
 }
 
 hipError_t launch_scan(const ChunkArgs& a, int CK, const SegPlan& sp)
