@@ -340,17 +340,20 @@ __global__ __launch_bounds__(64 * 7) void chunk_bwd_chain_pipe_kernel(BwdParams 
     } else if (w == 6) {
         // ========================================================= storer
         // the dS the owners published at step s (chunk NC - 1 - s), parity PC:
-        // owner o's value rows v0 + 16 o + c16, key channels 32 ks + 8 g4 ..
+        // value rows v0 .. v0 + 31 are one contiguous run of the [d_v][d_k]
+        // block, so each store writes 1 KiB of it, gathered from the owners'
+        // fragments
         auto store_dS = [&](auto pc, int s) {
             constexpr int PS = decltype(pc)::value * XSB;
+            constexpr int NI = 32 * DK * (int)sizeof(E) / 1024;
             const int n = NC - 1 - s;
+            unsigned char* ck = static_cast<unsigned char*>(p.dSck) +
+                                (((size_t)bh * NC + n) * p.DV + v0) * DK * sizeof(E) + 16 * l;
+            u32x4 x[NI];
 #pragma unroll
-            for (int o = 0; o < 2; ++o) {
-                E* ck = static_cast<E*>(p.dSck) + (((size_t)bh * NC + n) * p.DV + v0 + 16 * o + c16) * DK + 8 * g4;
+            for (int j = 0; j < NI; ++j) x[j] = *reinterpret_cast<const u32x4*>(smem + CL::rxS + PS + xs_piece<E, DK>(64 * j + l));
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    st16(ck + 32 * ks, *reinterpret_cast<const u32x4*>(smem + CL::rxS + PS + ((o * NKS + ks) * kWave + l) * FS));
-            }
+            for (int j = 0; j < NI; ++j) st16(ck + 1024 * j, x[j]);
         };
         step_barrier();
         // iteration u: the store of step u - 2's dS

@@ -108,6 +108,20 @@ __device__ __forceinline__ void vm_wait_range(int n) {
 }
 __device__ __forceinline__ void vm_wait(int n) { vm_wait_range<0, 64>(n); }
 
+// A block of 16 (or 32) value rows of a state, published as the owners'
+// MFMA operands (fragment (ks, lane 16 g + r) of owner o holds row 16 o + r,
+// key channels 32 ks + 8 g .. +7), written out row-major [row][d_k]: the LDS
+// byte offset, from the first owner's fragments, of flat 16-byte piece f of
+// the block, so that lane l of store j takes piece 64 j + l and every store
+// covers 1 KiB of contiguous rows.
+template <typename E, int DK>
+__device__ __forceinline__ int xs_piece(int f) {
+    constexpr int ES = (int)sizeof(E), PR = DK * ES / 16;   // pieces per row
+    constexpr int NKS = DK / 32, FS = (int)sizeof(Frag<E>);
+    const int r = f / PR, kc = (f % PR) * (16 / ES);
+    return (((r >> 4) * NKS + (kc >> 5)) * kWave + 16 * ((kc & 31) >> 3) + (r & 15)) * FS + (kc & 7) * ES;
+}
+
 // Barrier for the pipeline: this wave's LDS accesses are complete, then all
 // waves meet.  It does not wait for outstanding global->LDS copies: the
 // copier waits for those explicitly.

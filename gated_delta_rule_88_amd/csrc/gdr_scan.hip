@@ -417,20 +417,20 @@ __global__ __launch_bounds__(64 * 8) void chunk_scan_kernel(ScanParams p)
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) sop[ks] = *reinterpret_cast<const Frag<E>*>(smem + oXS + pS + ks * kWave * FS);
             if (p.Sck) {
-                // the state entering chunk m, for the backward, from its
-                // published operand (value row vw + c16, key channels
-                // 32 ks + 8 g ..: 16 contiguous bytes of the [d_v][d_k]
-                // state) -- kept off the owners' chain
-                E* ck = static_cast<E*>(p.Sck) + (((size_t)bh * p.NC + c0 + m) * p.DV + vw + c16) * DK + 8 * g4;
+                // the state entering chunk m, for the backward, from the
+                // operand owner c published -- kept off the owners' chain.
+                // This wave's 16 value rows are one contiguous run of the
+                // [d_v][d_k] state: each store writes 1 KiB of it, gathered
+                // from the fragments that hold those key channels.
+                constexpr int NI = 16 * DK * ES / 1024;
+                unsigned char* ck = static_cast<unsigned char*>(p.Sck) +
+                                    (((size_t)bh * p.NC + c0 + m) * p.DV + vw) * DK * ES + 16 * l;
+                const unsigned char* xs = smem + LY::rxS + pS + c * NKS * kWave * FS;
+                u32x4 pc[NI];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    if constexpr (sizeof(E) == 2) {
-                        st16(ck + 32 * ks, __builtin_bit_cast(u32x4, sop[ks].v));
-                    } else {
-                        *reinterpret_cast<f32x4*>(ck + 32 * ks) = sop[ks].lo;
-                        *reinterpret_cast<f32x4*>(ck + 32 * ks + 4) = sop[ks].hi;
-                    }
-                }
+                for (int j = 0; j < NI; ++j) pc[j] = *reinterpret_cast<const u32x4*>(xs + xs_piece<E, DK>(64 * j + l));
+#pragma unroll
+                for (int j = 0; j < NI; ++j) st16(ck + 1024 * j, pc[j]);
             }
             if (!og) return;   // states only
             Frag<E> qf[NB][NKS], kf[NB][NKS];
