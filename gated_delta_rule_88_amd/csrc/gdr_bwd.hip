@@ -849,12 +849,12 @@ __device__ __forceinline__ void lean_value_blocks(
                 if (pc < p.total) pf.load(p, pc, pv0, tid);
             }
             if (!up) {
-                bf16* dvg = reinterpret_cast<bf16*>(p.dv) + tok * p.DV + v0 + 16 * cb + c16;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * tt + 4 * g4 + e;
-                    if (r < valid) dvg[(size_t)r * p.DV] = (bf16)z[e];
-                }
+                // token 16 tt + 4 g4 + c16 % 4, value channels 16 cb + 4 (c16 / 4) ..
+                const f32x4 zt = quad_transpose(z);
+                const int r = 16 * tt + 4 * g4 + (c16 & 3);
+                if (r < valid)
+                    st4(reinterpret_cast<bf16*>(p.dv) + (tok + r) * p.DV + v0 + 16 * cb + 4 * (c16 >> 2),
+                        zt[0], zt[1], zt[2], zt[3]);
             }
         }
         __syncthreads();
@@ -1400,13 +1400,12 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
         const int t = w + NW * u;
         if (t < NQT) {
             const int rb = t / NJ, jb = t % NJ;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * g4 + e, j = 16 * jb + c16;
-                if (r < valid) {
-                    dqg[(size_t)r * DK + j] = from_f32<E>(dQa[u][e]);
-                    dkg[(size_t)r * DK + j] = from_f32<E>(dKa[u][e]);
-                }
+            // row 16 rb + 4 g4 + c16 % 4, columns 16 jb + 4 (c16 / 4) ..
+            const f32x4 q4 = quad_transpose(dQa[u]), k4 = quad_transpose(dKa[u]);
+            const int r = 16 * rb + 4 * g4 + (c16 & 3), j = 16 * jb + 4 * (c16 >> 2);
+            if (r < valid) {
+                st4(dqg + (size_t)r * DK + j, q4[0], q4[1], q4[2], q4[3]);
+                st4(dkg + (size_t)r * DK + j, k4[0], k4[1], k4[2], k4[3]);
             }
         }
     }
@@ -1982,21 +1981,26 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
         const int t = w + NW * u;
         if (t < NQT) {
             const int rb = t / NJ, jb = t % NJ;
+            f32x4 dq4, dk4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * g4 + e, c = 16 * jb + c16;
                 const float g = Gs[r * LG + c], gC = Gs[(CK - 1) * LG + c];
                 const float eG = __expf(g), eD = __expf(gC - g);
                 const float q = to_f32(Qs[r * LDK + c]), k = to_f32(Ks[r * LDK + c]);
-                const float dq = Y1[u][e] * eG + QP[u][e];
-                const float dkv = Y2[u][e] * eG + Y3[u][e] * eD + KP[u][e] + KM[u][e];
+                dq4[e] = Y1[u][e] * eG + QP[u][e];
+                dk4[e] = Y2[u][e] * eG + Y3[u][e] * eD + KP[u][e] + KM[u][e];
                 dGm[r * LG + c] = Y1[u][e] * q * eG + Y2[u][e] * k * eG - Y3[u][e] * k * eD + QP[u][e] * q +
                                   (KP[u][e] - KM[u][e]) * k;
                 Y3Kd[r * LG + c] = Y3[u][e] * k * eD;
-                if (r < valid) {
-                    dqg[(size_t)r * DK + c] = from_f32<E>(dq);
-                    dkg[(size_t)r * DK + c] = from_f32<E>(dkv);
-                }
+            }
+            // row 16 rb + 4 g4 + c16 % 4, columns 16 jb + 4 (c16 / 4) ..
+            dq4 = quad_transpose(dq4);
+            dk4 = quad_transpose(dk4);
+            const int r = 16 * rb + 4 * g4 + (c16 & 3), c = 16 * jb + 4 * (c16 >> 2);
+            if (r < valid) {
+                st4(dqg + (size_t)r * DK + c, dq4[0], dq4[1], dq4[2], dq4[3]);
+                st4(dkg + (size_t)r * DK + c, dk4[0], dk4[1], dk4[2], dk4[3]);
             }
         }
     }

@@ -13,6 +13,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace gdr {
 
@@ -257,6 +258,29 @@ __device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmc
 // log1p would cost more than the rest of the prepass.
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
 __device__ __forceinline__ float log_sigmoid_f(float x) { return fminf(x, 0.f) - __logf(1.f + __expf(-fabsf(x))); }
+
+// 4 x 4 transpose within each quad of lanes (two butterfly stages of quad
+// permutes): quad lane b, holding rows 0 .. 3 of column b, ends up holding
+// row b, columns 0 .. 3.  A 16 x 16 MFMA result tile (lane (g, c): rows
+// 4g .. 4g + 3 of column c) then gives lane (g, c) row 4g + c % 4, columns
+// 4 (c / 4) .. + 3, four consecutive elements one store can write.  Every
+// lane of a quad must execute it.
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 v) {
+    const int b = lane_id() & 3;
+    auto mv = [](float x, auto ctrl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                     decltype(ctrl)::value, 0xf, 0xf, false));
+    };
+    using X1 = std::integral_constant<int, 0xB1>;   // quad_perm [1, 0, 3, 2]
+    using X2 = std::integral_constant<int, 0x4E>;   // quad_perm [2, 3, 0, 1]
+    f32x4 y = {mv(v[1], X1{}), mv(v[0], X1{}), mv(v[3], X1{}), mv(v[2], X1{})};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = ((e ^ b) & 1) ? y[e] : v[e];
+    y = f32x4{mv(v[2], X2{}), mv(v[3], X2{}), mv(v[0], X2{}), mv(v[1], X2{})};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = ((e ^ b) & 2) ? y[e] : v[e];
+    return v;
+}
 
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ __forceinline__ float wave_incl_scan(float x) {
