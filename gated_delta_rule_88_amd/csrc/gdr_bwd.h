@@ -16,6 +16,7 @@ struct BwdParams {
     void *dq, *dk, *dv;
     float *dbeta, *dlog_alpha, *dS0;
     int L, NC, DV, total;
+    const float* Tck;                // [B*H][NC][CK][CK] fp32: each chunk's T = (I + A)^{-1}
 };
 
 // The chain (dS carried backwards over the chunks of every (b, h)) for bf16

@@ -38,7 +38,6 @@
 // fp32 accumulation); the triangular parts (T, dA) stay in fp32.
 #include "gdr_device.h"
 #include "gdr_chunk.h"
-#include "gdr_tri.h"
 #include "gdr_bwd.h"
 
 namespace gdr {
@@ -1003,11 +1002,14 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
     // (every read unconditional, from clamped indices: a read under a
     // condition, or a select on its value, would wait for it right here;
     // the entries past the chunk's end are zeroed where they are used)
+    // and 16 bytes of the chunk's T (from the forward's prepass) per thread
+    f32x4 tv;
     auto fetch_chunk = [&](int c, int tid) {
         const int n = c % p.NC, valid = min(CK, p.L - n * CK);
         const size_t tok = (size_t)(c / p.NC) * p.L + (size_t)n * CK;
         ks.prefetch(reinterpret_cast<const E*>(p.k) + tok * DK, DK, valid, tid);
         qs.prefetch(reinterpret_cast<const E*>(p.q) + tok * DK, DK, valid, tid);
+        tv = *reinterpret_cast<const f32x4*>(p.Tck + (size_t)c * CK * CK + 4 * min(tid, CK * CK / 4 - 1));
         const size_t t = tok + min(tid, valid - 1);
         btv = p.beta[t];
         lav = p.log_alpha ? p.log_alpha[t] : 0.f;
@@ -1102,9 +1104,10 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
         }
     }
     __syncthreads();
-    if (w == 0) unit_lower_inverse<CK, LF>(Af, Tf);
+    // T, as the forward's prepass computed it (dense, zero above the diagonal)
+    if (tid < CK * CK / 4) *reinterpret_cast<f32x4*>(Tf + (4 * tid / CK) * LF + 4 * tid % CK) = tv;
     __syncthreads();
-    // T (the inverse leaves the block above the diagonal unwritten), T^T, T~, T~^T
+    // T, T^T, T~, T~^T
     for (int x = tid; x < CK * CK; x += NT) {
         const int r = x % CK, s = x / CK;
         const float t = s <= r ? Tf[r * LF + s] : 0.f;
@@ -1535,6 +1538,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
     f32x4 lv[NLV];
     u32x4 pv;
     float bv;
+    f32x4 tv;   // 16 bytes of the chunk's T (from the forward's prepass) per thread
     auto fetch_chunk = [&](int c, int tid) {
         const int n = c % p.NC, valid = min(CK, p.L - n * CK);
         const size_t tok = (size_t)(c / p.NC) * p.L + (size_t)n * CK;
@@ -1542,6 +1546,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
         // (every read unconditional, from clamped indices: a read under a
         // condition, or a select on its value, would wait for it right here;
         // the entries past the chunk's end are zeroed where they are used)
+        tv = *reinterpret_cast<const f32x4*>(p.Tck + (size_t)c * CK * CK + 4 * min(tid, CK * CK / 4 - 1));
         ks.prefetch(reinterpret_cast<const E*>(p.k) + tok * DK, DK, valid, tid);
         qs.prefetch(reinterpret_cast<const E*>(p.q) + tok * DK, DK, valid, tid);
         kg.prefetch(reinterpret_cast<const E*>(rec + WL.KG), DK, CK, tid);
@@ -1702,7 +1707,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
         }
     }
     __syncthreads();
-    if (w == 0) unit_lower_inverse<CK, LF>(Af, Tf);
+    // T, as the forward's prepass computed it (dense, zero above the diagonal)
+    if (tid < CK * CK / 4) *reinterpret_cast<f32x4*>(Tf + (4 * tid / CK) * LF + 4 * tid % CK) = tv;
     __syncthreads();
     for (int x = tid; x < CK * CK; x += NT) {
         const int r = x % CK, s2 = x / CK;
@@ -2068,9 +2074,9 @@ static hipError_t launch_bwd_t(const BwdParams& bp, int BH, bool channel, hipStr
 }  // namespace
 
 // Workspace of the backward: the forward's chunk records, the state entering
-// every chunk and dS at every chunk's end.
+// every chunk, dS at every chunk's end and every chunk's T (fp32).
 struct BwdWs {
-    size_t off_Sck, off_dSck, bytes;
+    size_t off_Sck, off_dSck, off_T, bytes;
 };
 
 static BwdWs bwd_ws(int B, int H, int L, int dk, int dv, int C, int dtype, int mode)
@@ -2083,6 +2089,7 @@ static BwdWs bwd_ws(int B, int H, int L, int dk, int dv, int C, int dtype, int m
     size_t o = al(BH * NC * (size_t)ws_layout(es, dk, CK, mode).bytes);
     w.off_Sck = o; o = al(o + BH * NC * dv * dk * es);
     w.off_dSck = o; o = al(o + BH * NC * dv * dk * es);
+    w.off_T = o; o = al(o + BH * NC * CK * CK * 4);
     w.bytes = o;
     return w;
 }
@@ -2117,7 +2124,8 @@ hipError_t launch_bwd_chunked(const BwdArgs& b)
     unsigned char* ws = static_cast<unsigned char*>(b.workspace);
     // forward again: the prepass records and every chunk's entry state
     ChunkArgs a{b.B, b.H, b.L, b.dk, b.dv, b.C, b.dtype, b.mode, b.q, b.k, b.v, b.beta, b.log_alpha, b.S0,
-                nullptr, nullptr, ws, b.stream, 0u, nullptr, 0, Varlen{}, ws + w.off_Sck};
+                nullptr, nullptr, ws, b.stream, 0u, nullptr, 0, Varlen{}, ws + w.off_Sck,
+                reinterpret_cast<float*>(ws + w.off_T)};
     hipError_t err = launch_wy(a, CK);
     if (err != hipSuccess) return err;
     SegPlan one{1, NC, 0, 0, 0, 0, 0};
@@ -2125,7 +2133,8 @@ hipError_t launch_bwd_chunked(const BwdArgs& b)
     if (err != hipSuccess) return err;
     BwdParams bp{b.q, b.k, b.v, b.dO, b.beta, b.log_alpha, b.dS_final, ws,
                  ws + w.off_Sck, ws + w.off_dSck,
-                 b.dq, b.dk_out, b.dv_out, b.dbeta, b.dlog_alpha, b.dS0, b.L, NC, b.dv, (int)(BH * NC)};
+                 b.dq, b.dk_out, b.dv_out, b.dbeta, b.dlog_alpha, b.dS0, b.L, NC, b.dv, (int)(BH * NC),
+                 reinterpret_cast<const float*>(ws + w.off_T)};
     const bool ch = b.mode == kAlphaChannel;
     if (b.dtype == kBF16) {
         if (b.dk == 128) return CK == 16 ? launch_bwd_t<bf16, 128, 16>(bp, (int)BH, ch, b.stream)

@@ -107,6 +107,7 @@ struct WyParams {
     int L, NC, total;   // total = B * H * NC chunks (varlen: H * NCmax)
     unsigned pro;       // input-side prologue (kProNorm, kProGates)
     Varlen vl;
+    float* Tout;        // null, or [total][CK][CK] fp32: T = (I + A)^{-1}, zero above the diagonal
 };
 
 struct ScanParams {

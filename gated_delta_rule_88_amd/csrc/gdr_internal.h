@@ -54,6 +54,9 @@ struct ChunkArgs {
     Varlen vl;
     // backward's forward recompute: every chunk's entry state, or null
     void* Sck;
+    // backward's forward recompute: every chunk's T = (I + A)^{-1} (fp32
+    // [CK][CK], zero above the diagonal), or null
+    float* Tout;
 };
 
 struct BwdArgs {

@@ -64,4 +64,18 @@ __device__ __forceinline__ void unit_lower_inverse(const float* Af, float* Tf) {
     }
 }
 
+// T (row stride LF in LDS, as unit_lower_inverse leaves it: the block above
+// the diagonal unwritten) to dst as a dense [CK][CK] fp32 block with zeros
+// above the diagonal, 16 bytes per thread index i = t, t + n, ...
+template <int CK, int LF>
+__device__ __forceinline__ void store_T(const float* Tf, float* dst, int t, int n) {
+    for (int i = t; i < CK * CK / 4; i += n) {
+        const int r = (4 * i) / CK, s0 = (4 * i) % CK;
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (s0 + e <= r) ? Tf[r * LF + s0 + e] : 0.f;
+        *reinterpret_cast<f32x4*>(dst + 4 * i) = v;
+    }
+}
+
 }  // namespace gdr

@@ -246,6 +246,7 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
     }
     wave_lds_fence();
     unit_lower_inverse<CK, LF>(Af, Tf);
+    if (p.Tout) store_T<CK, LF>(Tf, p.Tout + (size_t)cid * CK * CK, lane_id(), kWave);
 
     // T~ = T diag(beta) (and Gamma) to the workspace, zero above the diagonal;
     // 16-byte row vectors of memory columns c0.., four consecutive tokens at a time
@@ -516,6 +517,7 @@ __global__ __launch_bounds__(256, 3) void chunk_wy_channel_kernel(WyParams p)
     __syncthreads();
     if (w == 0) unit_lower_inverse<CK, LF>(Af, Tf);
     __syncthreads();
+    if (p.Tout) store_T<CK, LF>(Tf, p.Tout + (size_t)cid * CK * CK, tid, 256);
 
     // ---- T~ = T diag(beta) and P to the workspace, zero above the diagonal
     // (columns in tok_of_col order)
@@ -570,7 +572,7 @@ static hipError_t launch_wy_t(const ChunkArgs& a)
     const int NC = (a.L + CK - 1) / CK;
     const int total = a.vl.start ? a.H * a.vl.NCmax : a.B * a.H * NC;   // record slots
     WyParams wp{a.q, a.k, a.beta, a.log_alpha, static_cast<unsigned char*>(a.workspace), a.L, NC,
-                total, a.pro, a.vl};
+                total, a.pro, a.vl, a.Tout};
     if (a.mode == kAlphaChannel) {
         using LY = WyChannelLayout<E, DK, CK>;
         static_assert(LY::bytes <= 160 * 1024, "LDS budget");

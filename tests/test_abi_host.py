@@ -256,15 +256,17 @@ def test_varlen_empty_is_a_noop(lib):
 def test_backward_workspace_size_query():
     ws = gdr.gdr_bwd_chunked_workspace_size
     # records, the state entering and the gradient leaving every chunk (d_v x
-    # d_k each, in the operand type); each region 256-aligned
+    # d_k each, in the operand type), and every chunk's fp32 T (32 x 32);
+    # each region 256-aligned
     nc = 2048 // 32
     rec = 64 * nc * (2048 + 2048 + 512)
     st = 64 * nc * 128 * 128 * 2
-    assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 1) == rec + 2 * st
+    tt = 64 * nc * 32 * 32 * 4
+    assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 1) == rec + 2 * st + tt
     # channel gates: the record adds exp(G_C) per key channel and the three
     # decayed [32][d_k] operands
     rec_ch = 64 * nc * (2048 + 2048 + 128 * 4 + 3 * 32 * 128 * 2)
-    assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 2) == rec_ch + 2 * st
+    assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 2) == rec_ch + 2 * st + tt
     assert ws(1, 2, 0, 64, 64, 64, gdr.GDR_F32, 1) == 0
 
 
