@@ -1074,8 +1074,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
     qs.store(Qs, LDK, Qt, LCK, tid);
     for (int x = tid; x < 16 * CK; x += NT) hgp[x] = 0.f;   // hgp and frp
     if (w == 0) {
-        const float g = wave_incl_scan(l < valid ? lav : 0.f);
-        const float gC = __shfl(g, CK - 1, kWave);
+        const float g = scan32(l < valid ? lav : 0.f);
+        const float gC = lane_value(g, CK - 1);
         if (l < CK) {
             gs[l] = g;
             gam[l] = __expf(g);
@@ -1380,16 +1380,14 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
             dgl = ea + fa + hg - fr;
         }
         // g_C enters gamma_C S0 and every D_r = e^{g_C - g_r}
-        float fsum = fr;
-#pragma unroll
-        for (int m = kWave / 2; m >= 1; m >>= 1) fsum += __shfl_xor(fsum, m, kWave);
+        const float fsum = lane_value(scan32(fr), 31);   // fr is 0 past token CK - 1
         if (l == CK - 1) {
             float hs = 0.f;
             for (int x = 0; x < NW; ++x) hs += red[x];
             dgl += gam[CK - 1] * hs + fsum;
         }
-        const float incl = wave_incl_scan(dgl);
-        const float total = __shfl(incl, CK - 1, kWave);
+        const float incl = scan32(dgl);
+        const float total = lane_value(incl, CK - 1);
         if (l < valid) {
             p.dbeta[tok + l] = db;
             if (p.dlog_alpha) p.dlog_alpha[tok + l] = total - incl + dgl;

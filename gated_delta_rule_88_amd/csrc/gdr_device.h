@@ -282,15 +282,26 @@ __device__ __forceinline__ f32x4 quad_transpose(f32x4 v) {
     return v;
 }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
-__device__ __forceinline__ float wave_incl_scan(float x) {
-    const int l = lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        float y = __shfl_up(x, d, kWave);
-        if (l >= d) x += y;
-    }
+// Inclusive prefix sum over lanes 0 .. 31 of a wave (lanes 32 .. 63 get
+// sums of their own rows): four shifts within each 16-lane row, then row 0's
+// total added to row 1 -- VALU data moves (DPP), no round trip through the
+// LDS unit as lane permutes take.
+__device__ __forceinline__ float scan32(float x) {
+    auto shr = [](float v, auto ctrl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                     decltype(ctrl)::value, 0xf, 0xf, true));
+    };
+    x += shr(x, std::integral_constant<int, 0x111>{});   // row_shr:1
+    x += shr(x, std::integral_constant<int, 0x112>{});   // row_shr:2
+    x += shr(x, std::integral_constant<int, 0x114>{});   // row_shr:4
+    x += shr(x, std::integral_constant<int, 0x118>{});   // row_shr:8
+    // row_bcast:15 into rows 1 and 3 (rows 0 and 2 add 0)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false));
     return x;
+}
+// Value of a wave-uniform lane (a scalar read, no lane permute).
+__device__ __forceinline__ float lane_value(float x, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
 }  // namespace gdr

@@ -216,8 +216,8 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
         bt = 0.f;
         la = 0.f;
     }
-    const float g = wave_incl_scan(la);
-    const float glast = __shfl(g, CK - 1, kWave);
+    const float g = scan32(la);
+    const float glast = lane_value(g, CK - 1);
     if (l < CK) {
         gs[l] = g;
         bs[l] = bt;
