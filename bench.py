@@ -52,15 +52,15 @@ FWD_SOURCES = ('gdr_wy.hip', 'gdr_scan.hip', 'gdr_segment.hip', 'gdr_pipe.h', 'g
 BWD_SOURCES = FWD_SOURCES + ('gdr_bwd.hip', 'gdr_bwd_chain.hip', 'gdr_bwd.h')
 MEASURED_TRAFFIC = {
     ("gdn_bf16_B8_H8_L2048_d128", "chunk_wy_kernel + chunk_scan_kernel"):
-        dict(sources=FWD_SOURCES, digest="7f3f8b2bf3d79627", read=154.67e6, written=57.00e6),
+        dict(sources=FWD_SOURCES, digest="440948908d76cdd3", read=154.74e6, written=56.87e6),
     ("kda_bf16_B4_H16_L4096_d128", "chunk_wy_channel_kernel + chunk_scan_kernel"):
-        dict(sources=FWD_SOURCES, digest="7f3f8b2bf3d79627", read=576.34e6, written=310.38e6),
+        dict(sources=FWD_SOURCES, digest="440948908d76cdd3", read=576.34e6, written=310.38e6),
     ("gdn_decode_bf16_N256_H16_d128", "decode_step_kernel"):
-        dict(sources=('gdr_decode.hip', 'gdr_device.h', 'gdr_internal.h'), digest="ba4cbfa081d125bc", read=274.34e6, written=269.50e6),
+        dict(sources=('gdr_decode.hip', 'gdr_device.h', 'gdr_internal.h'), digest="8d2e80a35a816486", read=274.33e6, written=269.50e6),
     ("gdn_bf16_B8_H8_L2048_d128 backward", "chunk_wy_kernel + chunk_scan_kernel + chunk_bwd_chain_pipe_kernel + chunk_bwd_grad_kernel"):
-        dict(sources=BWD_SOURCES, digest="7282c01ea5ab93b5", read=636.76e6, written=394.00e6),
+        dict(sources=BWD_SOURCES, digest="9d403dec0d026c49", read=653.50e6, written=411.37e6),
     ("kda_bf16_B4_H16_L4096_d128 backward", "chunk_wy_channel_kernel + chunk_scan_kernel + chunk_bwd_chain_pipe_kernel + chunk_bwd_grad_channel_kernel"):
-        dict(sources=BWD_SOURCES, digest="7282c01ea5ab93b5", read=1890.98e6, written=1117.81e6),
+        dict(sources=BWD_SOURCES, digest="9d403dec0d026c49", read=1924.58e6, written=1151.12e6),
 }
 
 
