@@ -41,6 +41,11 @@ template <typename T> struct Vec { static constexpr int n = 16 / sizeof(T); };
 // 16-byte loads and stores (global or LDS; the pointer must be 16-B aligned).
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Non-temporal 16-byte store: for data the next kernel streams in, so that it
+// does not sit dirty in the caches while that kernel reads other data.
+__device__ __forceinline__ void st16_nt(void* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 

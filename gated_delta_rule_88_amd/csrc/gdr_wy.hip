@@ -275,8 +275,9 @@ __global__ __launch_bounds__(256) void chunk_wy_kernel(WyParams p)
                 for (int e = 0; e < 4; ++e)
                     mv[q + e] = (t + e <= r) ? __expf(fminf(gr - gt[e], 0.f)) * qn * kn[e] : 0.f;
             }
-            st16(Tg + r * CK + c0, Pack<E>::pack(tv));
-            st16(Mg + r * CK + c0, Pack<E>::pack(mv));
+            // non-temporal: the scan streams the records in later
+            st16_nt(Tg + r * CK + c0, Pack<E>::pack(tv));
+            st16_nt(Mg + r * CK + c0, Pack<E>::pack(mv));
         }
     }
     if (l < CK) {
@@ -459,9 +460,12 @@ __global__ __launch_bounds__(256, 3) void chunk_wy_channel_kernel(WyParams p)
                 b[j] = qx[j] * eg * (PRO ? nqs[r] : 1.f);
                 d[j] = kx[j] * ed * (PRO ? nks[r] : 1.f);
             }
-            st16(KGg + r * DK + c0, Pack<E>::pack(a));
-            st16(QGg + r * DK + c0, Pack<E>::pack(b));
-            st16(KDg + r * DK + c0, Pack<E>::pack(d));
+            // non-temporal: 24 KiB per chunk that the scan streams in later;
+            // left dirty in the caches their write-back slowed the scan's
+            // copies by 15 %
+            st16_nt(KGg + r * DK + c0, Pack<E>::pack(a));
+            st16_nt(QGg + r * DK + c0, Pack<E>::pack(b));
+            st16_nt(KDg + r * DK + c0, Pack<E>::pack(d));
         }
         float* F = reinterpret_cast<float*>(rec + WL.F);
         for (int c = tid; c < DK; c += 256) F[c] = __expf(GL[c]);
