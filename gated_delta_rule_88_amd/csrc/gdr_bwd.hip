@@ -700,7 +700,7 @@ struct LeanVB {
     static constexpr int oR = 0, odU = SZX, oU = 2 * SZX, odR = 3 * SZX, XB = 4 * SZX;
     static constexpr int NS = 32 * DK / 8;           // 16-byte vectors of one state block
     static constexpr int NPS = NS / 256;             // of them per staging thread
-    static constexpr int NPF = 2 * NPS + 1;          // registers per staging thread
+    static constexpr int NPF = NPS + 1;              // registers per staging thread
 };
 
 __device__ __forceinline__ Frag<bf16> rowf(const unsigned char* p) {
@@ -734,8 +734,9 @@ __device__ __forceinline__ void st4bf(unsigned char* p, f32x4 x) {
     st8(p, u32x2{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3])});
 }
 
-// Block inputs held in registers by a staging thread t (0..255): S0 and dS
-// vectors t + 256 i of the block, and vector t % 128 of V (t < 128) or dO.
+// Block inputs held in registers by a staging thread t (0..255): dS vectors
+// t + 256 i of the block, and vector t % 128 of V (t < 128) or dO.  (S0 comes
+// from the carried state.)
 template <int DK>
 struct LeanPf {
     u32x4 r[LeanVB<DK>::NPF];
@@ -743,19 +744,18 @@ struct LeanPf {
     __device__ __forceinline__ void load(const BwdParams& p, int c, int v0, int t) {
         using LV = LeanVB<DK>;
         constexpr int CK = 32;
+        // the block's chunk arithmetic on the scalar unit
+        c = __builtin_amdgcn_readfirstlane(c);
+        v0 = __builtin_amdgcn_readfirstlane(v0);
         const int n = c % p.NC;
         valid = min(CK, p.L - n * CK);
         const size_t tok = (size_t)(c / p.NC) * p.L + (size_t)n * CK;
-        const bf16* s0 = static_cast<const bf16*>(p.Sck) + ((size_t)c * p.DV + v0) * DK;
         const bf16* ds = static_cast<const bf16*>(p.dSck) + ((size_t)c * p.DV + v0) * DK;
 #pragma unroll
-        for (int i = 0; i < LV::NPS; ++i) {
-            r[i] = ld16(s0 + 8 * (t + 256 * i));
-            r[LV::NPS + i] = ld16(ds + 8 * (t + 256 * i));
-        }
+        for (int i = 0; i < LV::NPS; ++i) r[i] = ld16(ds + 8 * (t + 256 * i));
         const int x = t & 127, row = min(x >> 2, valid - 1);
         const bf16* src = reinterpret_cast<const bf16*>(t < 128 ? p.v : p.dO);
-        r[2 * LV::NPS] = ld16(src + (tok + row) * p.DV + v0 + 8 * (x & 3));
+        r[LV::NPS] = ld16(src + (tok + row) * p.DV + v0 + 8 * (x & 3));
     }
     // into buffer b (rows of V and dO past the chunk's end as zeros)
     __device__ __forceinline__ void store(unsigned char* b, int t) const {
@@ -764,32 +764,88 @@ struct LeanPf {
 #pragma unroll
         for (int i = 0; i < LV::NPS; ++i) {
             const int x = t + 256 * i, row = x / PR, ch = x % PR;
-            st16(b + LV::oS0 + (row * LV::LDK + 8 * ch) * 2, r[i]);
-            st16(b + LV::odS + (row * LV::LDK + 8 * ch) * 2, r[LV::NPS + i]);
+            st16(b + LV::odS + (row * LV::LDK + 8 * ch) * 2, r[i]);
         }
         const int x = t & 127, row = x >> 2;
         st16(b + (t < 128 ? LV::oV : LV::odO) + (row * LV::LB + 8 * (x & 3)) * 2,
-             row < valid ? r[2 * LV::NPS] : u32x4{0u, 0u, 0u, 0u});
+             row < valid ? r[LV::NPS] : u32x4{0u, 0u, 0u, 0u});
     }
 };
 
-// One chunk's value blocks in the lean form.  On entry buffer bk & 1 holds
-// block (cid, 0) and pf the block after it, (pc, pv0); on exit bk has advanced
-// by the number of blocks and the same holds for the next chunk.  Results:
-// a1 += dO S0, a2 += dR S0, a3 += U dS (tiles t = w + 8u, rows 16 (t / NJ),
-// key channels 16 (t % NJ)), dPa += dO U^T, dTa += dU R^T (tile w < 4),
-// hs[e] += S0 . dS over this thread's key channels 8 (tid / 32) + e, and dv.
-// SC: scalar alpha (gamma, D); else channel alpha (Kx = K . exp(G),
-// Kd = K . exp(G_C - G), no per-token factors).
-template <int DK, bool SC, int NQW>
+// The state a gradient workgroup carries across its chunks (fp32, d_v <= 128
+// in blocks of 32 value channels).  Block vb as S^T tiles t = w + 8 u of wave
+// w: lane (g4, c16) holds S[16 (t / NJ) + c16][16 (t % NJ) + 4 g4 + e], e =
+// 0..3 (value row within the block, key channel), so the key channel
+// 16 (t % NJ) + .. is the same for every u.  (Indexed by block only in
+// unrolled loops: every entry stays in registers.)
+template <int DK>
+struct LeanCarry {
+    static constexpr int NJ = DK / 16, NQW = (2 * NJ + 7) / 8, MAXVB = 4;
+    static_assert(2 * NJ == 8 * NQW, "every wave holds NQW tiles of a block");
+    f32x4 s[MAXVB][NQW];
+    // the state entering chunk c: S0 (null: zero) at a head's first chunk,
+    // else the kept entry c / span (c a multiple of span)
+    __device__ __forceinline__ void load(const BwdParams& p, int c, int w, int l) {
+        const int g4 = l >> 4, c16 = l & 15, nvb = p.DV / 32;
+        const bool first = c % p.NC == 0;
+        const size_t row0 = first ? (size_t)(c / p.NC) * p.DV : (size_t)(c / p.span) * p.DV;
+#pragma unroll
+        for (int vb = 0; vb < MAXVB; ++vb)
+#pragma unroll
+            for (int u = 0; u < NQW; ++u) {
+                const int t = w + 8 * u;
+                const size_t e0 = (row0 + 32 * vb + 16 * (t / NJ) + c16) * DK + 16 * (t % NJ) + 4 * g4;
+                f32x4 x = zero4();
+                if (vb < nvb) {
+                    if (!first) {
+                        const u32x2 b = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(p.Sck) + e0);
+                        x = f32x4{bf_lo(b.x), bf_hi(b.x), bf_lo(b.y), bf_hi(b.y)};
+                    } else if (p.S0) {
+                        x = *reinterpret_cast<const f32x4*>(p.S0 + e0);
+                    }
+                }
+                s[vb][u] = x;
+            }
+        // s_waitcnt vmcnt(0) as an instruction the compiler tracks: the
+        // carried registers leave here complete, so no later use of them
+        // waits for the loads in flight then
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    // block vb (a constant once unrolled; bf16) into the S0 slot of input buffer b
+    __device__ __forceinline__ void stage(int vb, unsigned char* b, int w, int l) const {
+        using LV = LeanVB<DK>;
+        const int g4 = l >> 4, c16 = l & 15;
+#pragma unroll
+        for (int u = 0; u < NQW; ++u) {
+            const int t = w + 8 * u;
+            st4bf(b + LV::oS0 + ((16 * (t / NJ) + c16) * LV::LDK + 16 * (t % NJ) + 4 * g4) * 2, s[vb][u]);
+        }
+    }
+};
+
+// One chunk's value blocks in the lean form, NVB = d_v / 32 of them (2 or 4,
+// unrolled; block vb in input buffer vb & 1).  On entry buffer 0 holds block
+// (cid, 0) and pf the block after it, (pc, pv0), of the workgroup's run of
+// chunks that ends before pend; car holds the state entering cid.  On exit car
+// holds the state entering cid + 1 (its block 0 staged into buffer 0), and the
+// same holds for the next chunk.  Results: a1 += dO S0, a2 += dR S0, a3 += U dS (tiles t = w + 8u,
+// rows 16 (t / NJ), key channels 16 (t % NJ)), dPa += dO U^T, dTa += dU R^T
+// (tile w < 4), hs[e] += S0 . dS over this thread's key channels
+// 8 (tid / 32) + e, and dv.  SC: scalar alpha (gamma, D); else channel alpha
+// (Kx = K . exp(G), Kd = K . exp(G_C - G), no per-token factors).  The state
+// moves on as S <- dec . S + U^T (D . K): dec = gamma_C, or exp(G_C) of this
+// lane's key channels 16 (w % NJ) + 4 g4 + e; kdf = the X^T operand of D . K
+// (Kd for channel alpha) for key channels 16 (w % NJ) ..
+template <int DK, bool SC, int NQW, int NVB>
 __device__ __forceinline__ void lean_value_blocks(
     const BwdParams& p, unsigned char* smem, int in_off, int lx_off, const bf16* Kx, const bf16* Kd,
     const bf16* Pt, const bf16* Tt, const bf16* Ttt, const float* gam, const float* Dd, int cid, int tid,
-    int& bk, LeanPf<DK>& pf, int& pc, int& pv0, f32x4* a1, f32x4* a2, f32x4* a3, f32x4& dPa, f32x4& dTa,
-    float* hs)
+    LeanPf<DK>& pf, int& pc, int& pv0, int pend, LeanCarry<DK>& car, const Frag<bf16>& kdf,
+    f32x4 dec, f32x4* a1, f32x4* a2, f32x4* a3, f32x4& dPa, f32x4& dTa, float* hs)
 {
     using LV = LeanVB<DK>;
     constexpr int CK = 32, NJ = DK / 16, NKS = DK / 32, NW = 8, NQT = 2 * NJ;
+    static_assert(NQT == NW * NQW, "every wave holds NQW of the C x d_k tiles");
     constexpr int LDK = LV::LDK, LB = LV::LB;
     const int l = tid & 63, g4 = l >> 4, c16 = l & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -801,8 +857,13 @@ __device__ __forceinline__ void lean_value_blocks(
     const unsigned char* tf = reinterpret_cast<const unsigned char*>(Tt);
     const unsigned char* tft = reinterpret_cast<const unsigned char*>(Ttt);
     unsigned char* xb = smem + lx_off;
-    for (int v0 = 0; v0 < p.DV; v0 += 32, ++bk) {
-        const unsigned char* ib = smem + in_off + (bk & 1) * LV::IN;
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) {
+        const int v0 = 32 * vb;
+        const unsigned char* ib = smem + in_off + (vb & 1) * LV::IN;
+        // the next block's S0 into the free buffer (after the last block:
+        // block 0 of the next chunk, whose step was taken in block 0)
+        car.stage((vb + 1) % NVB, smem + in_off + ((vb + 1) & 1) * LV::IN, w, l);
         // ---- A: R = V - gamma . K S0^T (waves 0..3), dU = P^T dO + D . K dS^T
         // (waves 4..7); tile (tokens 16 tt .., value channels 16 cb ..)
         {
@@ -837,15 +898,15 @@ __device__ __forceinline__ void lean_value_blocks(
             st4bf(xb + (up ? LV::oU : LV::odR) + ((16 * cb + c16) * LB + 16 * tt + 4 * g4) * 2, z);
             // waves 0..3: the next block into the free buffer (its reads were
             // issued a block ago), then read the one after it
-            if (up && pc < p.total) {
-                pf.store(smem + in_off + ((bk + 1) & 1) * LV::IN, tid);
+            if (up && pc < pend) {
+                pf.store(smem + in_off + ((vb + 1) & 1) * LV::IN, tid);
                 if (pv0 + 32 < p.DV) {
                     pv0 += 32;
                 } else {
                     pv0 = 0;
-                    pc += gridDim.x;
+                    ++pc;
                 }
-                if (pc < p.total) pf.load(p, pc, pv0, tid);
+                if (pc < pend) pf.load(p, pc, pv0, tid);
             }
             if (!up) {
                 // token 16 tt + 4 g4 + c16 % 4, value channels 16 cb + 4 (c16 / 4) ..
@@ -857,21 +918,29 @@ __device__ __forceinline__ void lean_value_blocks(
             }
         }
         __syncthreads();
-        // ---- C: accumulate over the block's value channels
+        // ---- C: the carried state of this block over the chunk (S^T tiles:
+        // key channels 16 (w % NJ) .., value rows 16 rt ..), then accumulate
+        // over the block's value channels
 #pragma unroll
         for (int u = 0; u < NQW; ++u) {
-            const int t = w + NW * u;
-            if (t < NQT) {
-                const int rb = t / NJ, jb = t % NJ;
-                const Frag<bf16> ado = rowf(ib + LV::odO + ((16 * rb + c16) * LB + 8 * g4) * 2);
-                const Frag<bf16> adr = trn<LB>(xb + LV::odR, 0, 16 * rb, l);
-                const Frag<bf16> au = trn<LB>(xb + LV::oU, 0, 16 * rb, l);
-                const Frag<bf16> bs0 = trn<LDK>(ib + LV::oS0, 0, 16 * jb, l);
-                const Frag<bf16> bds = trn<LDK>(ib + LV::odS, 0, 16 * jb, l);
-                mma(a1[u], ado, bs0);
-                mma(a2[u], adr, bs0);
-                mma(a3[u], au, bds);
-            }
+            const int rt = (w + NW * u) / NJ;
+            f32x4 x = car.s[vb][u];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] *= dec[e];
+            mma(x, kdf, rowf(xb + LV::oU + ((16 * rt + c16) * LB + 8 * g4) * 2));
+            car.s[vb][u] = x;
+        }
+#pragma unroll
+        for (int u = 0; u < NQW; ++u) {
+            const int t = w + NW * u, rb = t / NJ, jb = t % NJ;   // (t < NQT: every wave has NQW tiles)
+            const Frag<bf16> ado = rowf(ib + LV::odO + ((16 * rb + c16) * LB + 8 * g4) * 2);
+            const Frag<bf16> adr = trn<LB>(xb + LV::odR, 0, 16 * rb, l);
+            const Frag<bf16> au = trn<LB>(xb + LV::oU, 0, 16 * rb, l);
+            const Frag<bf16> bs0 = trn<LDK>(ib + LV::oS0, 0, 16 * jb, l);
+            const Frag<bf16> bds = trn<LDK>(ib + LV::odS, 0, 16 * jb, l);
+            mma(a1[u], ado, bs0);
+            mma(a2[u], adr, bs0);
+            mma(a3[u], au, bds);
         }
         if (w < 4) {
             const int rb = w >> 1, sb = w & 1;
@@ -951,10 +1020,13 @@ struct GradLds : Strides<E, DK, CK> {
     static constexpr int bytes = m0;
 };
 
-template <typename E, int DK, int CK>
+// NVB: value blocks of 32 channels (d_v / 32) for the lean form, whose
+// value-block loop is unrolled; 0 for the other forms
+template <typename E, int DK, int CK, int NVB>
 __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
 {
     using LY = GradLds<E, DK, CK>;
+    static_assert(LY::LEAN ? (NVB == 2 || NVB == 4) : NVB == 0, "value blocks of the lean form");
     constexpr int NB = CK / 16, NJ = DK / 16, VE = Vec<E>::n;
     constexpr int LF = LY::LF, LDK = LY::LDK, LCK = LY::LCK, LBV = LY::LBV, LBF = LY::LBF;
     constexpr int NT = 512, NW = NT / kWave;     // 8 waves
@@ -1040,32 +1112,45 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
             da[u] = ld16(dog + (size_t)r * p.DV + v0 + cc);
         }
     };
-    // (bf16, C = 32) the lean value blocks' staging: block 0 into buffer 0,
-    // the block after it into registers
+    // Chunks cid0, + cstep, ... below cend: the lean form (bf16, C = 32)
+    // takes the run of p.span chunks from blockIdx.x * p.span in order and
+    // carries the state across it; otherwise chunks blockIdx.x, + gridDim.x, ..
+    const int cid0 = LY::LEAN ? (int)blockIdx.x * p.span : (int)blockIdx.x;
+    const int cend = LY::LEAN ? min(cid0 + p.span, p.total) : p.total;
+    const int cstep = LY::LEAN ? 1 : (int)gridDim.x;
+    // (lean) the value blocks' staging: block 0 into buffer 0 (its S0 from
+    // the carried state), the block after it into registers
     LeanPf<DK> lpf;
-    int lbk = 0, lpc = blockIdx.x, lpv0 = 0;
-    if ((int)blockIdx.x < p.total) {
-        fetch_chunk(blockIdx.x, threadIdx.x);
+    LeanCarry<DK> car;
+    int lpc = cid0, lpv0 = 0;
+    if (cid0 < cend) {
+        fetch_chunk(cid0, threadIdx.x);
         if constexpr (LY::LEAN) {
             if (threadIdx.x < 256) {
                 lpf.load(p, lpc, 0, threadIdx.x);
                 lpf.store(smem + LY::off_lean, threadIdx.x);
                 if (p.DV > 32) lpv0 = 32;
-                else lpc += gridDim.x;
-                if (lpc < p.total) lpf.load(p, lpc, lpv0, threadIdx.x);
+                else ++lpc;
+                if (lpc < cend) lpf.load(p, lpc, lpv0, threadIdx.x);
             }
         } else {
-            fetch_block(blockIdx.x, 0, threadIdx.x);
+            fetch_block(cid0, 0, threadIdx.x);
         }
     }
-    for (int cid = blockIdx.x; cid < p.total; cid += gridDim.x) {
+    for (int cid = cid0; cid < cend; cid += cstep) {
     // lane-dependent values are re-derived per chunk (see opaque)
     const int tid = opaque(threadIdx.x), l = tid & (kWave - 1), g4 = l >> 4, c16 = l & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int nxt = cid + gridDim.x;
+    const int nxt = cid + cstep;
     const int bh = cid / p.NC, n = cid % p.NC;
     const int t0 = n * CK, valid = min(CK, p.L - t0);
     const size_t tok = (size_t)bh * p.L + t0;
+    // (lean) a run's first chunk and a head's first chunk take the carried
+    // state afresh (staged as block 0's S0 before the value blocks)
+    const bool fresh = LY::LEAN && (cid == cid0 || n == 0);
+    if constexpr (LY::LEAN) {
+        if (fresh) car.load(p, cid, w, l);
+    }
 
     // ---- the chunk's keys, queries and gates (zero past the end)
     ks.mask(valid, tid);
@@ -1104,6 +1189,9 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
         }
     }
     __syncthreads();
+    if constexpr (LY::LEAN) {
+        if (fresh) car.stage(0, smem + LY::off_lean, w, l);
+    }
     // T, as the forward's prepass computed it (dense, zero above the diagonal)
     if (tid < CK * CK / 4) *reinterpret_cast<f32x4*>(Tf + (4 * tid / CK) * LF + 4 * tid % CK) = tv;
     __syncthreads();
@@ -1126,8 +1214,19 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
     constexpr int NCB = NB * (kBV / 16);  // C x kBV tiles (<= 4)
     if constexpr (LY::LEAN) {
         float hs8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        lean_value_blocks<DK, true, NQW>(p, smem, LY::off_lean, LY::off_lx, Ks, Ks, Pt, Tt, Ttt, gam, Dd, cid, tid,
-                                         lbk, lpf, lpc, lpv0, dQa, dKa, dKd, dPa, dTa, hs8);
+        // the carried state's step: D . K as an X^T operand, gamma_C
+        Frag<bf16> kdf = trn<LDK>(reinterpret_cast<const unsigned char*>(Ks), 0, 16 * (w % NJ), l);
+        {
+            float kv[8];
+            Pack<bf16>::unpack(__builtin_bit_cast(u32x4, kdf.v), kv);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kv[j] *= Dd[8 * g4 + j];
+            kdf.v = __builtin_bit_cast(bf16x8, Pack<bf16>::pack(kv));
+        }
+        const float gC = gam[CK - 1];
+        lean_value_blocks<DK, true, NQW, NVB>(p, smem, LY::off_lean, LY::off_lx, Ks, Ks, Pt, Tt, Ttt, gam, Dd, cid,
+                                              tid, lpf, lpc, lpv0, cend, car, kdf, f32x4{gC, gC, gC, gC},
+                                              dQa, dKa, dKd, dPa, dTa, hs8);
         // (gamma dO) S0 and dX S0 = -(gamma dR) S0 from the unscaled sums
 #pragma unroll
         for (int u = 0; u < NQW; ++u) {
@@ -1179,7 +1278,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
                 }
             }
             if (v0 + kBV < p.DV) fetch_block(cid, v0 + kBV, tid);
-            else if (nxt < p.total) fetch_block(nxt, 0, tid);
+            else if (nxt < cend) fetch_block(nxt, 0, tid);
             __syncthreads();
             // ---- R = V - gamma K S0^T (waves 0..NCB-1); dU = P^T dO + D . K dS^T (waves 4..)
             if (w < NCB) {
@@ -1248,7 +1347,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
     __syncthreads();   // the block region is reused below
     // the next chunk's keys, queries and gates: issued here rather than at the
     // chunk's start, so that no wait at the value loop's entry covers them
-    if (nxt < p.total) fetch_chunk(nxt, tid);
+    if (nxt < cend) fetch_chunk(nxt, tid);
 
     // ---- the dg terms that sum over key channels, from the accumulators
     // before the score terms join them, per row r:
@@ -1496,10 +1595,11 @@ struct GradChLds : Strides<E, DK, CK> {
     static constexpr int bytes = m1 > last_end ? m1 : last_end;
 };
 
-template <typename E, int DK, int CK>
+template <typename E, int DK, int CK, int NVB>
 __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p)
 {
     using LY = GradChLds<E, DK, CK>;
+    static_assert(LY::LEAN ? (NVB == 2 || NVB == 4) : NVB == 0, "value blocks of the lean form");
     constexpr int NB = CK / 16, NJ = DK / 16, VE = Vec<E>::n;
     constexpr int LF = LY::LF, LDK = LY::LDK, LCK = LY::LCK, LB = LY::LB, LG = LY::LG, LBF = LY::LBF;
     constexpr int NT = 512, NW = NT / kWave;
@@ -1584,32 +1684,45 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
             da[u] = ld16(dog + (size_t)r * p.DV + v0 + cc);
         }
     };
-    // (bf16, C = 32) the lean value blocks' staging: block 0 into buffer 0,
-    // the block after it into registers
+    // Chunks cid0, + cstep, ... below cend: the lean form (bf16, C = 32)
+    // takes the run of p.span chunks from blockIdx.x * p.span in order and
+    // carries the state across it; otherwise chunks blockIdx.x, + gridDim.x, ..
+    const int cid0 = LY::LEAN ? (int)blockIdx.x * p.span : (int)blockIdx.x;
+    const int cend = LY::LEAN ? min(cid0 + p.span, p.total) : p.total;
+    const int cstep = LY::LEAN ? 1 : (int)gridDim.x;
+    // (lean) the value blocks' staging: block 0 into buffer 0 (its S0 from
+    // the carried state), the block after it into registers
     LeanPf<DK> lpf;
-    int lbk = 0, lpc = blockIdx.x, lpv0 = 0;
-    if ((int)blockIdx.x < p.total) {
-        fetch_chunk(blockIdx.x, threadIdx.x);
+    LeanCarry<DK> car;
+    int lpc = cid0, lpv0 = 0;
+    if (cid0 < cend) {
+        fetch_chunk(cid0, threadIdx.x);
         if constexpr (LY::LEAN) {
             if (threadIdx.x < 256) {
                 lpf.load(p, lpc, 0, threadIdx.x);
                 lpf.store(smem + LY::off_lean, threadIdx.x);
                 if (p.DV > 32) lpv0 = 32;
-                else lpc += gridDim.x;
-                if (lpc < p.total) lpf.load(p, lpc, lpv0, threadIdx.x);
+                else ++lpc;
+                if (lpc < cend) lpf.load(p, lpc, lpv0, threadIdx.x);
             }
         } else {
-            fetch_block(blockIdx.x, 0, threadIdx.x);
+            fetch_block(cid0, 0, threadIdx.x);
         }
     }
-    for (int cid = blockIdx.x; cid < p.total; cid += gridDim.x) {
+    for (int cid = cid0; cid < cend; cid += cstep) {
     // lane-dependent values are re-derived per chunk (see vlane)
     const int tid = opaque(threadIdx.x), l = tid & (kWave - 1), g4 = l >> 4, c16 = l & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int nxt = cid + gridDim.x;
+    const int nxt = cid + cstep;
     const int bh = cid / p.NC, n = cid % p.NC;
     const int t0 = n * CK, valid = min(CK, p.L - t0);
     const size_t tok = (size_t)bh * p.L + t0;
+    // (lean) a run's first chunk and a head's first chunk take the carried
+    // state afresh (staged as block 0's S0 before the value blocks)
+    const bool fresh = LY::LEAN && (cid == cid0 || n == 0);
+    if constexpr (LY::LEAN) {
+        if (fresh) car.load(p, cid, w, l);
+    }
 
     // ---- keys, queries, the forward's decayed keys, log alpha (floored),
     // beta, and the score block P (masked; columns in tok_of_col order) transposed
@@ -1705,6 +1818,9 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
         }
     }
     __syncthreads();
+    if constexpr (LY::LEAN) {
+        if (fresh) car.stage(0, smem + LY::off_lean, w, l);
+    }
     // T, as the forward's prepass computed it (dense, zero above the diagonal)
     if (tid < CK * CK / 4) *reinterpret_cast<f32x4*>(Tf + (4 * tid / CK) * LF + 4 * tid % CK) = tv;
     __syncthreads();
@@ -1729,8 +1845,15 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
         for (int e = 0; e < VE; ++e) hacc[u][e] = 0.f;
     if constexpr (LY::LEAN) {
         float hs8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        lean_value_blocks<DK, false, NQW>(p, smem, LY::off_lean, LY::off_lx, Kgs, Kds, Pt, Tt, Ttt, nullptr, nullptr,
-                                          cid, tid, lbk, lpf, lpc, lpv0, Y1, Y2, Y3, dPa, dTa, hs8);
+        // the carried state's step: K . exp(G_C - G) as an X^T operand, and
+        // exp(G_C) of this lane's key channels
+        const Frag<bf16> kdf = trn<LDK>(reinterpret_cast<const unsigned char*>(Kds), 0, 16 * (w % NJ), l);
+        f32x4 dec;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dec[e] = __expf(Gs[(CK - 1) * LG + 16 * (w % NJ) + 4 * g4 + e]);
+        lean_value_blocks<DK, false, NQW, NVB>(p, smem, LY::off_lean, LY::off_lx, Kgs, Kds, Pt, Tt, Ttt, nullptr,
+                                               nullptr, cid, tid, lpf, lpc, lpv0, cend, car, kdf, dec,
+                                               Y1, Y2, Y3, dPa, dTa, hs8);
         // dX S0 = -dR S0
 #pragma unroll
         for (int u = 0; u < NQW; ++u)
@@ -1776,7 +1899,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
                 }
             }
             if (v0 + kBVC < p.DV) fetch_block(cid, v0 + kBVC, tid);
-            else if (nxt < p.total) fetch_block(nxt, 0, tid);
+            else if (nxt < cend) fetch_block(nxt, 0, tid);
             __syncthreads();
             // ---- R = V - Kg S0^T (waves 0..NCB-1); dU = P^T dO + Kd dS^T (waves 4..)
             if (w < NCB) {
@@ -1862,7 +1985,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
     __syncthreads();   // the block region is reused below
     // the next chunk's inputs: issued here rather than at the chunk's start,
     // so that no wait at the value loop's entry covers them
-    if (nxt < p.total) fetch_chunk(nxt, tid);
+    if (nxt < cend) fetch_chunk(nxt, tid);
     // ---- triangular part: dPM, dT~; dA = strictly-lower(-T^T dT~ diag(beta) T^T)
     if (w < NCC) {
         const int rb = w / NB, sb = w % NB;
@@ -2052,6 +2175,9 @@ static hipError_t launch_bwd_t(const BwdParams& bp, int BH, bool channel, hipStr
     using GL = GradLds<E, DK, CK>;
     using GC = GradChLds<E, DK, CK>;
     static_assert(CL::bytes <= 160 * 1024 && GL::bytes <= 160 * 1024 && GC::bytes <= 160 * 1024, "LDS budget");
+    // the lean form walks runs of chunks, every other form strides
+    if ((sizeof(E) == 2 && CK == 32) != (bp.span > 0) || (bp.span > 0 && bp.DV != 64 && bp.DV != 128))
+        return hipErrorInvalidValue;
     const int chains = BH * (bp.DV / kBV);
     // bf16 operands on 32-token steps take the pipelined chain (gdr_bwd_chain.hip)
     hipError_t err;
@@ -2060,22 +2186,44 @@ static hipError_t launch_bwd_t(const BwdParams& bp, int BH, bool channel, hipStr
                        : launch_lds(chunk_bwd_chain_kernel<E, DK, CK, false>, chains, 384, CL::bytes, stream, bp);
     if (err != hipSuccess) return err;
     // persistent, as many workgroups as fit the CUs (the next chunk's inputs
-    // are read while the current one is worked on)
-    return channel ? launch_lds(chunk_bwd_grad_channel_kernel<E, DK, CK>,
-                                std::min(bp.total, (160 * 1024 / GC::bytes) * compute_units()), 512, GC::bytes,
-                                stream, bp)
-                   : launch_lds(chunk_bwd_grad_kernel<E, DK, CK>,
-                                std::min(bp.total, (160 * 1024 / GL::bytes) * compute_units()), 512, GL::bytes,
-                                stream, bp);
+    // are read while the current one is worked on); with a span, one
+    // workgroup per run of span chunks
+    const int grid_ch = bp.span > 0 ? (bp.total + bp.span - 1) / bp.span
+                                    : std::min(bp.total, (160 * 1024 / GC::bytes) * compute_units());
+    const int grid_sc = bp.span > 0 ? (bp.total + bp.span - 1) / bp.span
+                                    : std::min(bp.total, (160 * 1024 / GL::bytes) * compute_units());
+    if constexpr (sizeof(E) == 2 && CK == 32) {
+        if (bp.DV == 128)
+            return channel ? launch_lds(chunk_bwd_grad_channel_kernel<E, DK, CK, 4>, grid_ch, 512, GC::bytes, stream, bp)
+                           : launch_lds(chunk_bwd_grad_kernel<E, DK, CK, 4>, grid_sc, 512, GL::bytes, stream, bp);
+        return channel ? launch_lds(chunk_bwd_grad_channel_kernel<E, DK, CK, 2>, grid_ch, 512, GC::bytes, stream, bp)
+                       : launch_lds(chunk_bwd_grad_kernel<E, DK, CK, 2>, grid_sc, 512, GL::bytes, stream, bp);
+    } else {
+        return channel ? launch_lds(chunk_bwd_grad_channel_kernel<E, DK, CK, 0>, grid_ch, 512, GC::bytes, stream, bp)
+                       : launch_lds(chunk_bwd_grad_kernel<E, DK, CK, 0>, grid_sc, 512, GL::bytes, stream, bp);
+    }
 }
 
 }  // namespace
 
-// Workspace of the backward: the forward's chunk records, the state entering
-// every chunk, dS at every chunk's end and every chunk's T (fp32).
+// Workspace of the backward: the forward's chunk records, the entry states
+// the gradient kernel starts from, dS at every chunk's end and every chunk's
+// T (fp32).
 struct BwdWs {
     size_t off_Sck, off_dSck, off_T, bytes;
 };
+
+// Chunks per gradient workgroup for bf16 operands on 32-token steps: the
+// chunks of all heads in about one contiguous run per CU, each walked in
+// order with the state carried across it, so the recomputing scan keeps only
+// the state entering every run.  0 otherwise (every chunk's state is kept).
+// (A constant CU count, as for the forward's segment plan: the workspace
+// size must not depend on the device.)
+static int bwd_span(size_t total, int dtype, int CK)
+{
+    if (dtype != kBF16 || CK != 32 || total == 0) return 0;
+    return (int)((total + kSegWorkgroups - 1) / kSegWorkgroups);
+}
 
 static BwdWs bwd_ws(int B, int H, int L, int dk, int dv, int C, int dtype, int mode)
 {
@@ -2083,9 +2231,11 @@ static BwdWs bwd_ws(int B, int H, int L, int dk, int dv, int C, int dtype, int m
     const int CK = chunk_step(C, dtype);
     const size_t BH = (size_t)B * H, NC = (size_t)((L + CK - 1) / CK);
     const int es = dtype == kBF16 ? 2 : 4;
+    const int span = bwd_span(BH * NC, dtype, CK);
+    const size_t nst = span > 0 ? (BH * NC + span - 1) / span : BH * NC;   // entry states kept
     BwdWs w{};
     size_t o = al(BH * NC * (size_t)ws_layout(es, dk, CK, mode).bytes);
-    w.off_Sck = o; o = al(o + BH * NC * dv * dk * es);
+    w.off_Sck = o; o = al(o + nst * dv * dk * es);
     w.off_dSck = o; o = al(o + BH * NC * dv * dk * es);
     w.off_T = o; o = al(o + BH * NC * CK * CK * 4);
     w.bytes = o;
@@ -2121,9 +2271,10 @@ hipError_t launch_bwd_chunked(const BwdArgs& b)
     const BwdWs w = bwd_ws(b.B, b.H, b.L, b.dk, b.dv, b.C, b.dtype, b.mode);
     unsigned char* ws = static_cast<unsigned char*>(b.workspace);
     // forward again: the prepass records and every chunk's entry state
+    const int span = bwd_span(BH * NC, b.dtype, CK);
     ChunkArgs a{b.B, b.H, b.L, b.dk, b.dv, b.C, b.dtype, b.mode, b.q, b.k, b.v, b.beta, b.log_alpha, b.S0,
                 nullptr, nullptr, ws, b.stream, 0u, nullptr, 0, Varlen{}, ws + w.off_Sck,
-                reinterpret_cast<float*>(ws + w.off_T)};
+                reinterpret_cast<float*>(ws + w.off_T), span};
     hipError_t err = launch_wy(a, CK);
     if (err != hipSuccess) return err;
     SegPlan one{1, NC, 0, 0, 0, 0, 0};
@@ -2132,7 +2283,7 @@ hipError_t launch_bwd_chunked(const BwdArgs& b)
     BwdParams bp{b.q, b.k, b.v, b.dO, b.beta, b.log_alpha, b.dS_final, ws,
                  ws + w.off_Sck, ws + w.off_dSck,
                  b.dq, b.dk_out, b.dv_out, b.dbeta, b.dlog_alpha, b.dS0, b.L, NC, b.dv, (int)(BH * NC),
-                 reinterpret_cast<const float*>(ws + w.off_T)};
+                 reinterpret_cast<const float*>(ws + w.off_T), span, b.S0};
     const bool ch = b.mode == kAlphaChannel;
     if (b.dtype == kBF16) {
         if (b.dk == 128) return CK == 16 ? launch_bwd_t<bf16, 128, 16>(bp, (int)BH, ch, b.stream)

@@ -127,9 +127,11 @@ struct ScanParams {
     // n * H + h is sequence n of head h, total = NS * H * NVB workgroups.
     int H;
     Varlen vl;
-    // [B*H][NC][d_v][d_k] in the operand type: the state entering every
-    // chunk (kept for the backward), or null
+    // [ceil(B*H*NC / sck_every)][d_v][d_k] in the operand type: the state
+    // entering chunks 0, sck_every, 2 sck_every, ... counted over all heads
+    // (chunk n of head bh is bh * NC + n), kept for the backward; or null
     void* Sck;
+    int sck_every;
 };
 
 // Segment-parallel scan.  A head's chunk scan is one sequential chain; when

@@ -57,6 +57,9 @@ struct ChunkArgs {
     // backward's forward recompute: every chunk's T = (I + A)^{-1} (fp32
     // [CK][CK], zero above the diagonal), or null
     float* Tout;
+    // the entry state is kept for chunks 0, sck_every, 2 sck_every, ...
+    // counted over all heads (0: every chunk)
+    int sck_every;
 };
 
 struct BwdArgs {

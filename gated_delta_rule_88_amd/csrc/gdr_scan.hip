@@ -416,7 +416,8 @@ __global__ __launch_bounds__(64 * 8) void chunk_scan_kernel(ScanParams p)
             Frag<E> sop[NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) sop[ks] = *reinterpret_cast<const Frag<E>*>(smem + oXS + pS + ks * kWave * FS);
-            if (p.Sck) {
+            const size_t fc = rec0 + c0 + m;   // chunk index over all heads
+            if (p.Sck && fc % p.sck_every == 0) {
                 // the state entering chunk m, for the backward, from the
                 // operand owner c published -- kept off the owners' chain.
                 // This wave's 16 value rows are one contiguous run of the
@@ -424,7 +425,7 @@ __global__ __launch_bounds__(64 * 8) void chunk_scan_kernel(ScanParams p)
                 // from the fragments that hold those key channels.
                 constexpr int NI = 16 * DK * ES / 1024;
                 unsigned char* ck = static_cast<unsigned char*>(p.Sck) +
-                                    (((size_t)bh * p.NC + c0 + m) * p.DV + vw) * DK * ES + 16 * l;
+                                    ((fc / p.sck_every) * p.DV + vw) * DK * ES + 16 * l;
                 const unsigned char* xs = smem + LY::rxS + pS + c * NKS * kWave * FS;
                 u32x4 pc[NI];
 #pragma unroll
@@ -722,6 +723,7 @@ static hipError_t launch_scan_t(const ChunkArgs& a, const SegPlan& seg)
     unsigned char* ws = static_cast<unsigned char*>(a.workspace);
     ScanParams sp{a.q, a.k, a.v, a.S0, ws, a.o, a.S_final, a.L, NC, a.dv, NVB, total,
                   seg.SEG, seg.NCS, NMB, nullptr, nullptr, nullptr, a.H, a.vl, a.Sck};
+    sp.sck_every = a.sck_every > 0 ? a.sck_every : 1;
     if (seg.SEG > 1) {
         sp.qt = ws + seg.off_qt;
         sp.Sseg = reinterpret_cast<float*>(ws + seg.off_Z);

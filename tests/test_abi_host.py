@@ -255,18 +255,35 @@ def test_varlen_empty_is_a_noop(lib):
 
 def test_backward_workspace_size_query():
     ws = gdr.gdr_bwd_chunked_workspace_size
-    # records, the state entering and the gradient leaving every chunk (d_v x
-    # d_k each, in the operand type), and every chunk's fp32 T (32 x 32);
-    # each region 256-aligned
+    # records, the gradient leaving every chunk (d_v x d_k, in the operand
+    # type), every chunk's fp32 T (32 x 32), and entry states: for bf16 on
+    # 32-token steps only the state entering every run of ceil(chunks / 256)
+    # chunks (one run per gradient workgroup), else every chunk's; each
+    # region 256-aligned
     nc = 2048 // 32
     rec = 64 * nc * (2048 + 2048 + 512)
     st = 64 * nc * 128 * 128 * 2
     tt = 64 * nc * 32 * 32 * 4
-    assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 1) == rec + 2 * st + tt
+    runs = -(-64 * nc // -(-64 * nc // 256))
+    assert runs == 256
+    assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 1) == rec + runs * 128 * 128 * 2 + st + tt
     # channel gates: the record adds exp(G_C) per key channel and the three
     # decayed [32][d_k] operands
     rec_ch = 64 * nc * (2048 + 2048 + 128 * 4 + 3 * 32 * 128 * 2)
-    assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 2) == rec_ch + 2 * st + tt
+    assert ws(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 2) == rec_ch + runs * 128 * 128 * 2 + st + tt
+    # a run count that does not divide: 3 * 100 chunks of 32 in runs of 2
+    nc3 = 100
+    rec3 = 3 * nc3 * (2048 + 2048 + 512)
+    st3 = 3 * nc3 * 128 * 128 * 2
+    al = lambda x: -(-x // 256) * 256
+    assert ws(1, 3, 3200, 128, 128, 64, gdr.GDR_BF16, 1) == (al(rec3) + al(150 * 128 * 128 * 2) + al(st3)
+                                                            + al(3 * nc3 * 32 * 32 * 4))
+    # fp32 operands (16-token steps) keep every chunk's entry state
+    nc4 = 2048 // 16
+    st4 = 64 * nc4 * 128 * 128 * 4
+    ws4 = ws(8, 8, 2048, 128, 128, 64, gdr.GDR_F32, 1)
+    rec4 = 64 * nc4 * (16 * 16 * 4 * 2 + 4 * 16 * 4)
+    assert ws4 == rec4 + 2 * st4 + 64 * nc4 * 16 * 16 * 4
     assert ws(1, 2, 0, 64, 64, 64, gdr.GDR_F32, 1) == 0
 
 

@@ -77,6 +77,22 @@ def test_backward_chunk_sizes(C, mode):
     check(run_bwd(x, C), oracle_bwd(x), 2e-2)
 
 
+# (B, H, L, d_k, d_v, S0): more than 256 chunks of 32 tokens, so every
+# gradient workgroup walks a run of 2..4 chunks and carries the state across
+# it; with an odd chunk count per head the runs cross into the next head,
+# which starts from S0 (or zero), and the head before ends on a ragged chunk
+RUNS = [(1, 5, 32 * 60 + 5, 128, 128, True), (2, 4, 32 * 97 + 1, 64, 64, True),
+        (1, 9, 32 * 32 + 20, 128, 64, False), (1, 3, 32 * 100, 64, 128, True)]
+
+
+@pytest.mark.parametrize("case", RUNS, ids=lambda c: f"B{c[0]}H{c[1]}L{c[2]}dk{c[3]}dv{c[4]}s0{int(c[5])}")
+@pytest.mark.parametrize("mode", MODES, ids=lambda m: gi.MODE_NAMES[m])
+def test_backward_carried_state_runs(case, mode):
+    B, H, L, dk, dv, s0 = case
+    x = grads_inputs(B, H, L, dk, dv, torch.bfloat16, mode, seed=6270 + L + mode, s0_std=0.1 if s0 else 0.0)
+    check(run_bwd(x), oracle_bwd(x), 2e-2)
+
+
 @pytest.mark.parametrize("dt", DTYPES, ids=lambda d: str(d)[6:])
 def test_backward_channel_strong_decay(dt):
     """Channel gates near and past the floor of log alpha at -10: decays of
