@@ -730,6 +730,7 @@ __device__ __forceinline__ f32x4 trc(const unsigned char* tile, int row0, int co
     const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a)));
     return f32x4{bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y)};
 }
+__device__ __forceinline__ bf16x2 bf2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
 __device__ __forceinline__ void st4bf(unsigned char* p, f32x4 x) {
     st8(p, u32x2{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3])});
 }
@@ -752,10 +753,12 @@ struct LeanPf {
         const size_t tok = (size_t)(c / p.NC) * p.L + (size_t)n * CK;
         const bf16* ds = static_cast<const bf16*>(p.dSck) + ((size_t)c * p.DV + v0) * DK;
 #pragma unroll
-        for (int i = 0; i < LV::NPS; ++i) r[i] = ld16(ds + 8 * (t + 256 * i));
+        for (int i = 0; i < LV::NPS; ++i) r[i] = ld16(ds + (uint32_t)(8 * (t + 256 * i)));
+        // (uniform bases, 32-bit lane offsets: waves 0 and 1 read V, 2 and 3 dO)
         const int x = t & 127, row = min(x >> 2, valid - 1);
-        const bf16* src = reinterpret_cast<const bf16*>(t < 128 ? p.v : p.dO);
-        r[LV::NPS] = ld16(src + (tok + row) * p.DV + v0 + 8 * (x & 3));
+        const bool vw = __builtin_amdgcn_readfirstlane(t >> 6) < 2;
+        const bf16* src = reinterpret_cast<const bf16*>(vw ? p.v : p.dO) + tok * p.DV + v0;
+        r[LV::NPS] = ld16(src + (uint32_t)(row * p.DV + 8 * (x & 3)));
     }
     // into buffer b (rows of V and dO past the chunk's end as zeros)
     __device__ __forceinline__ void store(unsigned char* b, int t) const {
@@ -828,10 +831,11 @@ struct LeanCarry {
 // (cid, 0) and pf the block after it, (pc, pv0), of the workgroup's run of
 // chunks that ends before pend; car holds the state entering cid.  On exit car
 // holds the state entering cid + 1 (its block 0 staged into buffer 0), and the
-// same holds for the next chunk.  Results: a1 += dO S0, a2 += dR S0, a3 += U dS (tiles t = w + 8u,
-// rows 16 (t / NJ), key channels 16 (t % NJ)), dPa += dO U^T, dTa += dU R^T
-// (tile w < 4), hs[e] += S0 . dS over this thread's key channels
-// 8 (tid / 32) + e, and dv.  SC: scalar alpha (gamma, D); else channel alpha
+// same holds for the next chunk.  Results: a1 += dO S0, a2 += dR S0,
+// a3 += U dS (tiles t = w + 8u, rows 16 (t / NJ), key channels 16 (t % NJ)),
+// dPa += dO U^T, dTa += dU R^T (tile w < 4), hs[e] += S0 . dS over this
+// thread's key channels 8 (tid / 32) + e (SC: only their sum counts, kept in
+// hs[0..3] by channel pairs), and dv.  SC: scalar alpha (gamma, D); else channel alpha
 // (Kx = K . exp(G), Kd = K . exp(G_C - G), no per-token factors).  The state
 // moves on as S <- dec . S + U^T (D . K): dec = gamma_C, or exp(G_C) of this
 // lane's key channels 16 (w % NJ) + 4 g4 + e; kdf = the X^T operand of D . K
@@ -898,23 +902,25 @@ __device__ __forceinline__ void lean_value_blocks(
             st4bf(xb + (up ? LV::oU : LV::odR) + ((16 * cb + c16) * LB + 16 * tt + 4 * g4) * 2, z);
             // waves 0..3: the next block into the free buffer (its reads were
             // issued a block ago), then read the one after it
-            if (up && pc < pend) {
-                pf.store(smem + in_off + ((vb + 1) & 1) * LV::IN, tid);
+            // (the block position advances on every wave: scalar arithmetic)
+            if (pc < pend) {
+                if (up) pf.store(smem + in_off + ((vb + 1) & 1) * LV::IN, tid);
                 if (pv0 + 32 < p.DV) {
                     pv0 += 32;
                 } else {
                     pv0 = 0;
                     ++pc;
                 }
-                if (pc < pend) pf.load(p, pc, pv0, tid);
+                if (up && pc < pend) pf.load(p, pc, pv0, tid);
             }
             if (!up) {
                 // token 16 tt + 4 g4 + c16 % 4, value channels 16 cb + 4 (c16 / 4) ..
+                // (a uniform base and a 32-bit lane offset)
                 const f32x4 zt = quad_transpose(z);
                 const int r = 16 * tt + 4 * g4 + (c16 & 3);
+                bf16* dvb = reinterpret_cast<bf16*>(p.dv) + tok * p.DV + v0;
                 if (r < valid)
-                    st4(reinterpret_cast<bf16*>(p.dv) + (tok + r) * p.DV + v0 + 16 * cb + 4 * (c16 >> 2),
-                        zt[0], zt[1], zt[2], zt[3]);
+                    st4(dvb + (uint32_t)(r * p.DV + 16 * cb + 4 * (c16 >> 2)), zt[0], zt[1], zt[2], zt[3]);
             }
         }
         __syncthreads();
@@ -949,11 +955,24 @@ __device__ __forceinline__ void lean_value_blocks(
         }
         if (tid < 32 * DK / 8) {
             const int i = tid & 31, j = 8 * (tid >> 5);
-            float a[8], b[8];
-            Pack<bf16>::unpack(ld16(ib + LV::oS0 + (i * LDK + j) * 2), a);
-            Pack<bf16>::unpack(ld16(ib + LV::odS + (i * LDK + j) * 2), b);
+            const u32x4 sa = ld16(ib + LV::oS0 + (i * LDK + j) * 2), sb = ld16(ib + LV::odS + (i * LDK + j) * 2);
+            if constexpr (SC) {
+                // only the total is used: pairs of channels by bf16 dot products
+                // (each bf16 product is exact in fp32)
+                hs[0] = __builtin_amdgcn_fdot2_f32_bf16(bf2(sa.x), bf2(sb.x), hs[0], false);
+                hs[1] = __builtin_amdgcn_fdot2_f32_bf16(bf2(sa.y), bf2(sb.y), hs[1], false);
+                hs[2] = __builtin_amdgcn_fdot2_f32_bf16(bf2(sa.z), bf2(sb.z), hs[2], false);
+                hs[3] = __builtin_amdgcn_fdot2_f32_bf16(bf2(sa.w), bf2(sb.w), hs[3], false);
+            } else {
+                // per channel: S0 with its other channel masked to zero
+                const uint32_t av[4] = {sa.x, sa.y, sa.z, sa.w}, bv[4] = {sb.x, sb.y, sb.z, sb.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) hs[e] += a[e] * b[e];
+                for (int e = 0; e < 4; ++e) {
+                    hs[2 * e] = __builtin_amdgcn_fdot2_f32_bf16(bf2(av[e] & 0xffffu), bf2(bv[e]), hs[2 * e], false);
+                    hs[2 * e + 1] =
+                        __builtin_amdgcn_fdot2_f32_bf16(bf2(av[e] & 0xffff0000u), bf2(bv[e]), hs[2 * e + 1], false);
+                }
+            }
         }
         __syncthreads();
     }
@@ -1129,10 +1148,10 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
             if (threadIdx.x < 256) {
                 lpf.load(p, lpc, 0, threadIdx.x);
                 lpf.store(smem + LY::off_lean, threadIdx.x);
-                if (p.DV > 32) lpv0 = 32;
-                else ++lpc;
-                if (lpc < cend) lpf.load(p, lpc, lpv0, threadIdx.x);
             }
+            if (p.DV > 32) lpv0 = 32;
+            else ++lpc;
+            if (threadIdx.x < 256 && lpc < cend) lpf.load(p, lpc, lpv0, threadIdx.x);
         } else {
             fetch_block(cid0, 0, threadIdx.x);
         }
@@ -1701,10 +1720,10 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
             if (threadIdx.x < 256) {
                 lpf.load(p, lpc, 0, threadIdx.x);
                 lpf.store(smem + LY::off_lean, threadIdx.x);
-                if (p.DV > 32) lpv0 = 32;
-                else ++lpc;
-                if (lpc < cend) lpf.load(p, lpc, lpv0, threadIdx.x);
             }
+            if (p.DV > 32) lpv0 = 32;
+            else ++lpc;
+            if (threadIdx.x < 256 && lpc < cend) lpf.load(p, lpc, lpv0, threadIdx.x);
         } else {
             fetch_block(cid0, 0, threadIdx.x);
         }
