@@ -52,15 +52,15 @@ FWD_SOURCES = ('gdr_wy.hip', 'gdr_scan.hip', 'gdr_segment.hip', 'gdr_pipe.h', 'g
 BWD_SOURCES = FWD_SOURCES + ('gdr_bwd.hip', 'gdr_bwd_chain.hip', 'gdr_bwd.h')
 MEASURED_TRAFFIC = {
     ("gdn_bf16_B8_H8_L2048_d128", "chunk_wy_kernel + chunk_scan_kernel"):
-        dict(sources=FWD_SOURCES, digest="440948908d76cdd3", read=154.74e6, written=56.87e6),
+        dict(sources=FWD_SOURCES, digest="129b4b78d9564e83", read=154.76e6, written=56.75e6),
     ("kda_bf16_B4_H16_L4096_d128", "chunk_wy_channel_kernel + chunk_scan_kernel"):
-        dict(sources=FWD_SOURCES, digest="440948908d76cdd3", read=576.34e6, written=310.38e6),
+        dict(sources=FWD_SOURCES, digest="129b4b78d9564e83", read=576.33e6, written=310.38e6),
     ("gdn_decode_bf16_N256_H16_d128", "decode_step_kernel"):
-        dict(sources=('gdr_decode.hip', 'gdr_device.h', 'gdr_internal.h'), digest="8d2e80a35a816486", read=274.33e6, written=269.50e6),
+        dict(sources=('gdr_decode.hip', 'gdr_device.h', 'gdr_internal.h'), digest="490e95c02c707566", read=274.33e6, written=269.49e6),
     ("gdn_bf16_B8_H8_L2048_d128 backward", "chunk_wy_kernel + chunk_scan_kernel + chunk_bwd_chain_pipe_kernel + chunk_bwd_grad_kernel"):
-        dict(sources=BWD_SOURCES, digest="9d403dec0d026c49", read=653.50e6, written=411.37e6),
+        dict(sources=BWD_SOURCES, digest="143fdf0257cc43f2", read=525.61e6, written=284.16e6),
     ("kda_bf16_B4_H16_L4096_d128 backward", "chunk_wy_channel_kernel + chunk_scan_kernel + chunk_bwd_chain_pipe_kernel + chunk_bwd_grad_channel_kernel"):
-        dict(sources=BWD_SOURCES, digest="9d403dec0d026c49", read=1924.58e6, written=1151.12e6),
+        dict(sources=BWD_SOURCES, digest="143fdf0257cc43f2", read=1662.44e6, written=890.25e6),
 }
 
 
