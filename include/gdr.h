@@ -214,9 +214,12 @@ int gdr_fwd_chunked_noalloc(int B, int H, int L, int d_k, int d_v, int C, int dt
 /*
  * Bytes of device workspace gdr_bwd_chunked needs (0 when B * H == 0 or
  * L == 0), or (size_t)-1 for invalid or unsupported sizes.  It holds the
- * forward's chunk records, the state entering every chunk and the state
- * gradient at every chunk's end (d_v x d_k per chunk each, in the dtype of
- * q, chunks of 32 tokens, or 16 for GDR_F32 or C == 16).
+ * forward's chunk records, every chunk's (I + A)^-1 (fp32), the state
+ * gradient at every chunk's end and entry states (d_v x d_k each, in the
+ * dtype of q; chunks of 32 tokens, or 16 for GDR_F32 or C == 16): for bf16
+ * on 32-token chunks only the state entering every run of
+ * ceil(B * H * chunks / 256) chunks, counted over all heads, else the state
+ * entering every chunk.
  */
 size_t gdr_bwd_chunked_workspace_size(int B, int H, int L, int d_k, int d_v, int C,
                                       int dtype, int alpha_mode);
