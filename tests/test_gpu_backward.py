@@ -131,12 +131,12 @@ def test_backward_deterministic():
         assert np.array_equal(a[name], b[name]), name
 
 
-def test_backward_full_size_sampled():
-    """The headline shape (B8 H8 L2048 d128, bf16, scalar gates): the oracle
-    checks two (b, h) chains."""
+def test_backward_full_size():
+    """The headline shape (B8 H8 L2048 d128, bf16, scalar gates): every
+    (b, h) chain against the oracle."""
     x = grads_inputs(8, 8, 2048, 128, 128, torch.bfloat16, gi.ALPHA_SCALAR, seed=6500)
     g = run_bwd(x)
-    heads = [(0, 0), (5, 3)]
+    heads = [(b, h) for b in range(8) for h in range(8)]
     sel = lambda t: None if t is None else torch.stack([t[b, h] for b, h in heads])[None]
     r = oracle.backward(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["beta"]), sel(x["log_alpha"]),
                         sel(x["S0"]), sel(x["dO"]), sel(x["dS_final"]))
@@ -144,12 +144,12 @@ def test_backward_full_size_sampled():
     check(gs, r, 2e-2)
 
 
-def test_backward_full_size_sampled_channel():
-    """The channel-gate shape (B4 H16 L4096 d128, bf16): the oracle checks
-    two (b, h) chains."""
+def test_backward_full_size_channel():
+    """The channel-gate shape (B4 H16 L4096 d128, bf16): every (b, h) chain
+    against the oracle."""
     x = grads_inputs(4, 16, 4096, 128, 128, torch.bfloat16, gi.ALPHA_CHANNEL, seed=6600)
     g = run_bwd(x)
-    heads = [(0, 0), (3, 11)]
+    heads = [(b, h) for b in range(4) for h in range(16)]
     sel = lambda t: None if t is None else torch.stack([t[b, h] for b, h in heads])[None]
     r = oracle.backward(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["beta"]), sel(x["log_alpha"]),
                         sel(x["S0"]), sel(x["dO"]), sel(x["dS_final"]))

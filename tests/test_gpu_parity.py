@@ -303,17 +303,22 @@ def test_full_deltanet_fp32():
     assert rel_err(o, ro) <= 1e-4 and rel_err(S, rS) <= 1e-4
 
 
+def _all_heads(w):
+    return [(b, h) for b in range(w.B) for h in range(w.H)]
+
+
+# every (b, h) chain of the workload against the oracle
 def test_full_gdn_bf16():
-    _full_size(gi.GDN_BF16, [(0, 0), (3, 5), (7, 7)])
+    _full_size(gi.GDN_BF16, _all_heads(gi.GDN_BF16))
 
 
 def test_full_kda_bf16():
-    _full_size(gi.KDA_BF16, [(0, 0), (3, 15)])
+    _full_size(gi.KDA_BF16, _all_heads(gi.KDA_BF16))
 
 
 @pytest.mark.parametrize("w", gi.GDN_SWEEP, ids=lambda w: w.name)
 def test_full_gdn_sweep(w):
-    _full_size(w, [(w.B - 1, w.H - 1)])
+    _full_size(w, _all_heads(w))
 
 
 def test_full_decode_1024_steps():
