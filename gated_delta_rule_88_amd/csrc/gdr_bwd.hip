@@ -1051,6 +1051,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
     constexpr int NT = 512, NW = NT / kWave;     // 8 waves
     constexpr int NQT = NB * NJ;                 // C x DK tiles
     constexpr int NQW = (NQT + NW - 1) / NW;     // per wave
+    constexpr bool FULLQ = NQT == NW * NQW;      // every wave holds NQW tiles (no test needed)
     constexpr int NCB = NB * (kBV / 16);         // C x kBV tiles (<= 4)
     constexpr int NCC = NB * NB;                 // C x C tiles (<= 4)
     extern __shared__ __align__(16) unsigned char smem[];
@@ -1250,7 +1251,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
 #pragma unroll
         for (int u = 0; u < NQW; ++u) {
             const int t = w + NW * u;
-            if (t < NQT) {
+            if (FULLQ || t < NQT) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float gr = gam[16 * (t / NJ) + 4 * g4 + e];
@@ -1349,7 +1350,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
     #pragma unroll
             for (int u = 0; u < NQW; ++u) {
                 const int t = w + NW * u;
-                if (t < NQT) {
+                if (FULLQ || t < NQT) {
                     const int rb = t / NJ, jb = t % NJ;
                     tmma<E>(dQa[u], gdOs, LBV, 16 * rb, S0t, LBV, 16 * jb, kBV, l);
                     tmma<E>(dKa[u], dXs, LBV, 16 * rb, S0t, LBV, 16 * jb, kBV, l);
@@ -1378,7 +1379,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
 #pragma unroll
     for (int u = 0; u < NQW; ++u) {
         const int t = w + NW * u;
-        if (t < NQT) {
+        if (FULLQ || t < NQT) {
             const int rb = t / NJ, jb = t % NJ;
             float h[4], f[4];
 #pragma unroll
@@ -1432,7 +1433,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
 #pragma unroll
     for (int u = 0; u < NQW; ++u) {
         const int t = w + NW * u;
-        if (t < NQT) {
+        if (FULLQ || t < NQT) {
             const int rb = t / NJ, jb = t % NJ;
             tmma<E>(dQa[u], dPW, LCK, 16 * rb, Kt, LCK, 16 * jb, CK, l);
             tmma<E>(dKa[u], dPWt, LCK, 16 * rb, Qt, LCK, 16 * jb, CK, l);
@@ -1471,7 +1472,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
 #pragma unroll
     for (int u = 0; u < NQW; ++u) {
         const int t = w + NW * u;
-        if (t < NQT) {
+        if (FULLQ || t < NQT) {
             const int rb = t / NJ, jb = t % NJ;
             tmma<E>(dKa[u], dGf, LCK, 16 * rb, Kt, LCK, 16 * jb, CK, l);
             tmma<E>(dKa[u], dGt, LCK, 16 * rb, Kt, LCK, 16 * jb, CK, l);
@@ -1517,7 +1518,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
 #pragma unroll
     for (int u = 0; u < NQW; ++u) {
         const int t = w + NW * u;
-        if (t < NQT) {
+        if (FULLQ || t < NQT) {
             const int rb = t / NJ, jb = t % NJ;
             // row 16 rb + 4 g4 + c16 % 4, columns 16 jb + 4 (c16 / 4) ..
             const f32x4 q4 = quad_transpose(dQa[u]), k4 = quad_transpose(dKa[u]);
@@ -1623,6 +1624,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
     constexpr int LF = LY::LF, LDK = LY::LDK, LCK = LY::LCK, LB = LY::LB, LG = LY::LG, LBF = LY::LBF;
     constexpr int NT = 512, NW = NT / kWave;
     constexpr int NQT = NB * NJ, NQW = (NQT + NW - 1) / NW;
+    constexpr bool FULLQ = NQT == NW * NQW;      // every wave holds NQW tiles (no test needed)
     constexpr int NCC = NB * NB, NPAIR = NB * (NB + 1) / 2, NKS = DK / 32;
     constexpr WsLayout WL = ws_layout((int)sizeof(E), DK, CK, kAlphaChannel);
     static_assert(NKS % 2 == 0 && 64 * NPAIR * 4 * 4 <= LY::FCC, "Bm halves");
@@ -1969,7 +1971,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
     #pragma unroll
             for (int u = 0; u < NQW; ++u) {
                 const int t = w + NW * u;
-                if (t < NQT) {
+                if (FULLQ || t < NQT) {
                     const int rb = t / NJ, jb = t % NJ;
                     tmma<E>(Y1[u], dOs, LB, 16 * rb, S0t, LB, 16 * jb, kBVC, l);
                     tmma<E>(Y2[u], dXs, LB, 16 * rb, S0t, LB, 16 * jb, kBVC, l);
@@ -2125,7 +2127,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
 #pragma unroll
     for (int u = 0; u < NQW; ++u) {
         const int t = w + NW * u;
-        if (t < NQT) {
+        if (FULLQ || t < NQT) {
             const int rb = t / NJ, jb = t % NJ;
             f32x4 dq4, dk4;
 #pragma unroll

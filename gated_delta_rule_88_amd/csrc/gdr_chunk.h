@@ -146,7 +146,8 @@ struct ScanParams {
 // states enter these last products as bf16 operands.
 // The budget is the MI355X's 256 CUs (one scan workgroup each) as a constant,
 // not a device query: the plan fixes the workspace size, which the size
-// query must report without a device argument.
+// query must report without a device argument.  (The backward's gradient
+// walk divides its chunks into as many runs, for the same reason.)
 constexpr int kSegWorkgroups = 256;   // scan workgroups the device runs at once (one per CU)
 constexpr int kSegMinChunks = 16;     // shortest segment worth splitting off
 constexpr int kMaxSeg = 16;
