@@ -272,7 +272,43 @@ def bench_backward(w, steps, warmup, copies):
         call(i)
     e1.record()
     torch.cuda.synchronize()
-    return dict(total_ms=e0.elapsed_time(e1), ws_bytes=need)
+    total = e0.elapsed_time(e1)
+
+    # a training step both ways: the forward, then the backward recomputing
+    # it; or the keeping forward, then the backward from what it kept
+    o = torch.empty((w.B, w.H, w.L, w.dv), dtype=w.dtype, device=dev)
+    fws = torch.empty(max(gdr.gdr_fwd_chunked_workspace_size(w.B, w.H, w.L, w.dk, w.dv, w.C, code, w.mode), 1),
+                      dtype=torch.uint8, device=dev)
+
+    def step_recompute(i):
+        d = sets[i % copies]
+        gdr.gdr_fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["S0"], w.C, o=o,
+                            write_final=False, workspace=fws)
+        call(i)
+
+    def step_kept(i):
+        d = sets[i % copies]
+        gdr.gdr_fwd_chunked_keep(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["S0"], w.C, o=o,
+                                 write_final=False, workspace=ws)
+        gdr.gdr_bwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["S0"], d["dO"], None,
+                            w.C, workspace=ws, kept=True)
+
+    def timed(fn, n):
+        for i in range(max(2, warmup // 2)):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = _events(2)
+        a.record()
+        for i in range(n):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3
+
+    n = max(steps // 2, 5)
+    train = {"forward_then_backward_us": timed(step_recompute, n),
+             "keep_forward_then_kept_backward_us": timed(step_kept, n)}
+    return dict(total_ms=total, ws_bytes=need, train=train)
 
 
 def bench_decode(w, steps, prologue=0):
@@ -479,6 +515,10 @@ def main():
                          "traffic": measured_traffic(w.name + " backward", bwd_kernel),
                          "kernel": bwd_kernel,
                          "algorithmic_bytes_per_call": nbytes},
+            # µs per training step (forward + backward, same inputs): with the
+            # backward recomputing the forward (the line above), and with the
+            # forward keeping its records and states for the backward
+            "training_step": r["train"],
         }))
         return
     if args.varlen:

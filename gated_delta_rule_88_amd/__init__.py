@@ -40,6 +40,7 @@ EXPORTED = ("gdr_abi_version", "gdr_status_string", "gdr_fwd_chunked_workspace_s
             "gdr_fwd_chunked_token_step",
             "gdr_fwd_chunked", "gdr_fwd_chunked_ex", "gdr_fwd_chunked_noalloc", "gdr_fwd_varlen_workspace_size",
             "gdr_fwd_varlen", "gdr_bwd_chunked_workspace_size", "gdr_bwd_chunked",
+            "gdr_fwd_chunked_keep", "gdr_bwd_chunked_kept",
             "gdr_decode_step", "gdr_decode_step_ex")
 
 _lib = None
@@ -83,6 +84,10 @@ def load_library():
     lib.gdr_bwd_chunked_workspace_size.restype = sz
     lib.gdr_bwd_chunked.argtypes = [i] * 7 + [vp] * 4 + [i] + [vp] * 11 + [sz, vp]
     lib.gdr_bwd_chunked.restype = i
+    lib.gdr_bwd_chunked_kept.argtypes = lib.gdr_bwd_chunked.argtypes
+    lib.gdr_bwd_chunked_kept.restype = i
+    lib.gdr_fwd_chunked_keep.argtypes = lib.gdr_fwd_chunked.argtypes
+    lib.gdr_fwd_chunked_keep.restype = i
     lib.gdr_decode_step.argtypes = [i] * 5 + [vp] * 4 + [i] + [vp] * 4
     lib.gdr_decode_step.restype = i
     lib.gdr_decode_step_ex.argtypes = lib.gdr_decode_step.argtypes + [ctypes.c_uint]
@@ -282,12 +287,63 @@ def gdr_bwd_chunked_workspace_size(B, H, L, d_k, d_v, C, dtype, alpha_mode) -> i
                                                              alpha_mode))
 
 
+def _bwd_workspace(B, H, L, dk, dv, chunk, code, mode, workspace, dev):
+    need = gdr_bwd_chunked_workspace_size(B, H, L, dk, dv, chunk, code, mode)
+    if need == ctypes.c_size_t(-1).value:
+        raise GdrError(GDR_ERR_UNSUPPORTED, "gdr_bwd_chunked_workspace_size")
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    return workspace, 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
+def gdr_fwd_chunked_keep(q, k, v, beta, log_alpha=None, S0=None, chunk: int = 64, *, o=None,
+                         S_final=None, write_final: bool = True, workspace=None, stream=None):
+    """The forward of a training step: gdr_fwd_chunked's results, plus what
+    the backward would recompute, kept in a backward workspace (allocated
+    here unless given).  Returns (o, S_final or None, workspace); pass the
+    workspace to gdr_bwd_chunked(..., kept=True)."""
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, L, d_k]")
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    mode = _mode_of(log_alpha, q)
+    _check(q, "q", dt, dev, (B, H, L, dk))
+    _check(k, "k", dt, dev, (B, H, L, dk))
+    _check(v, "v", dt, dev, (B, H, L, dv))
+    _check(beta, "beta", torch.float32, dev, (B, H, L))
+    if mode == GDR_ALPHA_SCALAR:
+        _check(log_alpha, "log_alpha", torch.float32, dev, (B, H, L))
+    elif mode == GDR_ALPHA_CHANNEL:
+        _check(log_alpha, "log_alpha", torch.float32, dev, (B, H, L, dk))
+    _check(S0, "S0", torch.float32, dev, (B, H, dv, dk))
+    if o is None:
+        o = torch.empty((B, H, L, dv), dtype=dt, device=dev)
+    _check(o, "o", dt, dev, (B, H, L, dv))
+    if S_final is None and write_final:
+        S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    _check(S_final, "S_final", torch.float32, dev, (B, H, dv, dk))
+    workspace, ws_bytes = _bwd_workspace(B, H, L, dk, dv, chunk, code, mode, workspace, dev)
+    st = lib.gdr_fwd_chunked_keep(B, H, L, dk, dv, chunk, code, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                  mode, _ptr(log_alpha), _ptr(S0), _ptr(o), _ptr(S_final),
+                                  _ptr(workspace), ws_bytes, _stream(stream))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_fwd_chunked_keep")
+    return o, S_final, workspace
+
+
 def gdr_bwd_chunked(q, k, v, beta, log_alpha, S0, dO, dS_final=None, chunk: int = 64, *,
-                    want_dS0: bool = True, workspace=None, stream=None):
+                    want_dS0: bool = True, workspace=None, stream=None, kept: bool = False):
     """Gradients of gdr_fwd_chunked for output gradient dO [B,H,L,dv] (dtype
     of q) and final-state gradient dS_final (None | [B,H,dv,dk] fp32).
     Returns a dict of dq, dk, dv (dtype of q), dbeta, dlog_alpha (None for
-    alpha = 1, else the shape of log_alpha) and dS0 (fp32, or None)."""
+    alpha = 1, else the shape of log_alpha) and dS0 (fp32, or None).
+    kept=True: ``workspace`` is the one gdr_fwd_chunked_keep returned for the
+    same inputs, and the forward is not recomputed (gdr_bwd_chunked_kept)."""
+    if kept and workspace is None:
+        raise ValueError("kept=True needs the workspace gdr_fwd_chunked_keep filled")
     lib = load_library()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, L, d_k]")
@@ -311,19 +367,15 @@ def gdr_bwd_chunked(q, k, v, beta, log_alpha, S0, dO, dS_final=None, chunk: int 
              dbeta=torch.empty_like(beta),
              dlog_alpha=None if log_alpha is None else torch.empty_like(log_alpha),
              dS0=torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_dS0 else None)
-    need = gdr_bwd_chunked_workspace_size(B, H, L, dk, dv, chunk, code, mode)
-    if need == ctypes.c_size_t(-1).value:
-        raise GdrError(GDR_ERR_UNSUPPORTED, "gdr_bwd_chunked_workspace_size")
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.gdr_bwd_chunked(B, H, L, dk, dv, chunk, code, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
-                             mode, _ptr(log_alpha), _ptr(S0), _ptr(dO), _ptr(dS_final),
-                             _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dbeta"]),
-                             _ptr(g["dlog_alpha"]), _ptr(g["dS0"]), _ptr(workspace), ws_bytes,
-                             _stream(stream))
+    workspace, ws_bytes = _bwd_workspace(B, H, L, dk, dv, chunk, code, mode, workspace, dev)
+    fn, name = (lib.gdr_bwd_chunked_kept, "gdr_bwd_chunked_kept") if kept else (lib.gdr_bwd_chunked,
+                                                                                "gdr_bwd_chunked")
+    st = fn(B, H, L, dk, dv, chunk, code, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), mode, _ptr(log_alpha),
+            _ptr(S0), _ptr(dO), _ptr(dS_final), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+            _ptr(g["dbeta"]), _ptr(g["dlog_alpha"]), _ptr(g["dS0"]), _ptr(workspace), ws_bytes,
+            _stream(stream))
     if st != GDR_OK:
-        raise GdrError(st, "gdr_bwd_chunked")
+        raise GdrError(st, name)
     return g
 
 

@@ -99,20 +99,15 @@ GDR_EXPORT int gdr_fwd_chunked_token_step(int C, int dtype, int alpha_mode)
 
 namespace gdr {
 
-// gdr_fwd_chunked_ex's checks and launches (shared with the entry point
-// that brings its own scratch, gdr_noalloc.hip).
-int fwd_chunked_checked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
-                        const void* q, const void* k, const void* v,
-                        const float* beta, int alpha_mode, const float* log_alpha,
-                        const float* S0, void* o, float* S_final,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream,
-                        unsigned prologue)
+// The argument checks of a chunked forward whose workspace must hold `need`
+// bytes: GDR_OK, or the status to return.
+static int check_fwd_args(int B, int H, int L, int d_k, int d_v, int dtype,
+                          const void* q, const void* k, const void* v,
+                          const float* beta, int alpha_mode, const float* log_alpha,
+                          const float* S0, void* o, float* S_final,
+                          void* workspace, size_t workspace_bytes, size_t need)
 {
-    if (prologue & ~(unsigned)(GDR_PRO_L2NORM_QK | GDR_PRO_GATES)) return GDR_ERR_INVALID_ARG;
-    int st = check_chunk_sizes(B, H, L, d_k, d_v, C, dtype, alpha_mode);
-    if (st != GDR_OK) return st;
     const size_t BH = (size_t)B * H;
-    if (BH == 0) return GDR_OK;
     const size_t es = elem_size(dtype);
     const size_t nt = BH * L;
     const size_t state_bytes = BH * d_v * d_k * 4;
@@ -131,7 +126,6 @@ int fwd_chunked_checked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
     const Range rb = rng(beta, nt * 4), ra = rng(log_alpha, la_bytes);
     const Range r0 = rng(S0, state_bytes), ro = rng(o, nt * d_v * es);
     const Range rf = rng(S_final, state_bytes);
-    const size_t need = chunk_workspace(B, H, L, d_k, d_v, C, dtype, alpha_mode);
     const Range rw = rng(workspace, need);
     for (Range x : {rq, rk, rv, rb, ra, r0, rf, rw})
         if (overlap(ro, x)) return GDR_ERR_INVALID_ARG;
@@ -141,7 +135,25 @@ int fwd_chunked_checked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
     for (Range x : {rq, rk, rv, rb, ra, r0})
         if (overlap(rw, x)) return GDR_ERR_INVALID_ARG;
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GDR_ERR_WORKSPACE_TOO_SMALL;
+    return GDR_OK;
+}
 
+// gdr_fwd_chunked_ex's checks and launches (shared with the entry point
+// that brings its own scratch, gdr_noalloc.hip).
+int fwd_chunked_checked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                        const void* q, const void* k, const void* v,
+                        const float* beta, int alpha_mode, const float* log_alpha,
+                        const float* S0, void* o, float* S_final,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream,
+                        unsigned prologue)
+{
+    if (prologue & ~(unsigned)(GDR_PRO_L2NORM_QK | GDR_PRO_GATES)) return GDR_ERR_INVALID_ARG;
+    int st = check_chunk_sizes(B, H, L, d_k, d_v, C, dtype, alpha_mode);
+    if (st != GDR_OK) return st;
+    if ((size_t)B * H == 0) return GDR_OK;
+    st = check_fwd_args(B, H, L, d_k, d_v, dtype, q, k, v, beta, alpha_mode, log_alpha, S0, o, S_final,
+                        workspace, workspace_bytes, chunk_workspace(B, H, L, d_k, d_v, C, dtype, alpha_mode));
+    if (st != GDR_OK) return st;
     gdr::ChunkArgs a{B, H, L, d_k, d_v, C, dtype, alpha_mode, q, k, v, beta, log_alpha, S0, o,
                      S_final, workspace, stream, prologue};
     return gdr::launch_fwd_chunked(a) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
@@ -272,13 +284,14 @@ GDR_EXPORT size_t gdr_bwd_chunked_workspace_size(int B, int H, int L, int d_k, i
     return gdr::bwd_workspace_bytes(B, H, L, d_k, d_v, C, dtype, alpha_mode);
 }
 
-GDR_EXPORT int gdr_bwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
-                               const void* q, const void* k, const void* v,
-                               const float* beta, int alpha_mode, const float* log_alpha,
-                               const float* S0, const void* dO, const float* dS_final,
-                               void* dq, void* dk, void* dv, float* dbeta, float* dlog_alpha,
-                               float* dS0, void* workspace, size_t workspace_bytes,
-                               hipStream_t stream)
+// gdr_bwd_chunked's checks and launches; part: gdr::kBwdAll or gdr::kBwdKept
+static int bwd_checked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                       const void* q, const void* k, const void* v,
+                       const float* beta, int alpha_mode, const float* log_alpha,
+                       const float* S0, const void* dO, const float* dS_final,
+                       void* dq, void* dk, void* dv, float* dbeta, float* dlog_alpha,
+                       float* dS0, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream, int part)
 {
     int st = check_chunk_sizes(B, H, L, d_k, d_v, C, dtype, alpha_mode);
     if (st != GDR_OK) return st;
@@ -319,6 +332,49 @@ GDR_EXPORT int gdr_bwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GDR_ERR_WORKSPACE_TOO_SMALL;
 
     gdr::BwdArgs a{B, H, L, d_k, d_v, C, dtype, alpha_mode, q, k, v, beta, log_alpha, S0, dO, dS_final,
-                   dq, dk, dv, dbeta, dlog_alpha, dS0, workspace, stream};
+                   dq, dk, dv, dbeta, dlog_alpha, dS0, workspace, stream, part};
+    return gdr::launch_bwd_chunked(a) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+GDR_EXPORT int gdr_bwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                               const void* q, const void* k, const void* v,
+                               const float* beta, int alpha_mode, const float* log_alpha,
+                               const float* S0, const void* dO, const float* dS_final,
+                               void* dq, void* dk, void* dv, float* dbeta, float* dlog_alpha,
+                               float* dS0, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream)
+{
+    return bwd_checked(B, H, L, d_k, d_v, C, dtype, q, k, v, beta, alpha_mode, log_alpha, S0, dO, dS_final,
+                       dq, dk, dv, dbeta, dlog_alpha, dS0, workspace, workspace_bytes, stream, gdr::kBwdAll);
+}
+
+GDR_EXPORT int gdr_bwd_chunked_kept(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                                    const void* q, const void* k, const void* v,
+                                    const float* beta, int alpha_mode, const float* log_alpha,
+                                    const float* S0, const void* dO, const float* dS_final,
+                                    void* dq, void* dk, void* dv, float* dbeta, float* dlog_alpha,
+                                    float* dS0, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream)
+{
+    return bwd_checked(B, H, L, d_k, d_v, C, dtype, q, k, v, beta, alpha_mode, log_alpha, S0, dO, dS_final,
+                       dq, dk, dv, dbeta, dlog_alpha, dS0, workspace, workspace_bytes, stream, gdr::kBwdKept);
+}
+
+GDR_EXPORT int gdr_fwd_chunked_keep(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                                    const void* q, const void* k, const void* v,
+                                    const float* beta, int alpha_mode, const float* log_alpha,
+                                    const float* S0, void* o, float* S_final,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    int st = check_chunk_sizes(B, H, L, d_k, d_v, C, dtype, alpha_mode);
+    if (st != GDR_OK) return st;
+    if ((size_t)B * H == 0) return GDR_OK;
+    st = gdr::check_fwd_args(B, H, L, d_k, d_v, dtype, q, k, v, beta, alpha_mode, log_alpha, S0, o, S_final,
+                             workspace, workspace_bytes,
+                             gdr::bwd_workspace_bytes(B, H, L, d_k, d_v, C, dtype, alpha_mode));
+    if (st != GDR_OK) return st;
+    gdr::BwdArgs a{B, H, L, d_k, d_v, C, dtype, alpha_mode, q, k, v, beta, log_alpha, S0, nullptr, nullptr,
+                   nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, workspace, stream, gdr::kBwdKeep,
+                   o, S_final};
     return gdr::launch_bwd_chunked(a) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }

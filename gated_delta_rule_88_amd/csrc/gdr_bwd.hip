@@ -2279,6 +2279,12 @@ hipError_t launch_bwd_chunked(const BwdArgs& b)
 {
     const size_t BH = (size_t)b.B * b.H;
     if (BH == 0) return hipSuccess;
+    if (b.part == kBwdKeep && b.L == 0) {
+        // no tokens: the plain forward (the final state is the initial one)
+        ChunkArgs a{b.B, b.H, 0, b.dk, b.dv, b.C, b.dtype, b.mode, b.q, b.k, b.v, b.beta, b.log_alpha, b.S0,
+                    b.o, b.S_final, b.workspace, b.stream};
+        return launch_fwd_chunked(a);
+    }
     if (b.L == 0) {
         // no tokens: the gradient reaching S0 is the one given for S_final
         if (!b.dS0) return hipSuccess;
@@ -2291,16 +2297,20 @@ hipError_t launch_bwd_chunked(const BwdArgs& b)
     const int NC = (b.L + CK - 1) / CK;
     const BwdWs w = bwd_ws(b.B, b.H, b.L, b.dk, b.dv, b.C, b.dtype, b.mode);
     unsigned char* ws = static_cast<unsigned char*>(b.workspace);
-    // forward again: the prepass records and every chunk's entry state
+    // the forward (again, or for the first time with its outputs): the
+    // prepass records, every chunk's T and the entry states the gradient
+    // walk starts from
     const int span = bwd_span(BH * NC, b.dtype, CK);
-    ChunkArgs a{b.B, b.H, b.L, b.dk, b.dv, b.C, b.dtype, b.mode, b.q, b.k, b.v, b.beta, b.log_alpha, b.S0,
-                nullptr, nullptr, ws, b.stream, 0u, nullptr, 0, Varlen{}, ws + w.off_Sck,
-                reinterpret_cast<float*>(ws + w.off_T), span};
-    hipError_t err = launch_wy(a, CK);
-    if (err != hipSuccess) return err;
-    SegPlan one{1, NC, 0, 0, 0, 0, 0};
-    err = launch_scan(a, CK, one);
-    if (err != hipSuccess) return err;
+    if (b.part != kBwdKept) {
+        ChunkArgs a{b.B, b.H, b.L, b.dk, b.dv, b.C, b.dtype, b.mode, b.q, b.k, b.v, b.beta, b.log_alpha, b.S0,
+                    b.part == kBwdKeep ? b.o : nullptr, b.part == kBwdKeep ? b.S_final : nullptr, ws, b.stream, 0u,
+                    nullptr, 0, Varlen{}, ws + w.off_Sck, reinterpret_cast<float*>(ws + w.off_T), span};
+        hipError_t err = launch_wy(a, CK);
+        if (err != hipSuccess) return err;
+        SegPlan one{1, NC, 0, 0, 0, 0, 0};
+        err = launch_scan(a, CK, one);
+        if (err != hipSuccess || b.part == kBwdKeep) return err;
+    }
     BwdParams bp{b.q, b.k, b.v, b.dO, b.beta, b.log_alpha, b.dS_final, ws,
                  ws + w.off_Sck, ws + w.off_dSck,
                  b.dq, b.dk_out, b.dv_out, b.dbeta, b.dlog_alpha, b.dS0, b.L, NC, b.dv, (int)(BH * NC),

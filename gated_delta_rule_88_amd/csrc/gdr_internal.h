@@ -72,7 +72,15 @@ struct BwdArgs {
     float *dbeta, *dlog_alpha, *dS0;
     void* workspace;
     hipStream_t stream;
+    // kBwdAll: recompute the forward's records and entry states, then the
+    // gradients; kBwdKeep: the forward only, also writing o and S_final (a
+    // training step's forward that keeps them); kBwdKept: the gradients only,
+    // from a workspace a kBwdKeep call filled
+    int part;
+    void* o;
+    float* S_final;
 };
+constexpr int kBwdAll = 0, kBwdKeep = 1, kBwdKept = 2;
 
 // Bytes of device workspace the chunked forward needs.
 size_t chunk_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int dtype, int mode);

@@ -256,6 +256,41 @@ int gdr_bwd_chunked(int B, int H, int L, int d_k, int d_v, int C, int dtype,
                     float *dS0, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The forward of a training step that keeps, in a backward workspace, what
+ * gdr_bwd_chunked would otherwise recompute (the chunk records, every
+ * chunk's (I + A)^-1 and the entry states), so that gdr_bwd_chunked_kept
+ * can start from them (the same chunk algebra as gdr_fwd_chunked: "linear
+ * attention and its gated descendants", "Chunkwise Parallel Form").
+ *
+ * Arguments, alignment, aliasing rules and errors as for gdr_fwd_chunked,
+ * except:
+ *   workspace  at least gdr_bwd_chunked_workspace_size(...) bytes, for the
+ *              same sizes; it is filled here and read by the backward
+ * o and S_final are those of gdr_fwd_chunked up to rounding (always one
+ * scan chain per (b, h): the segment-parallel scan is not used here).
+ */
+int gdr_fwd_chunked_keep(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                         const void *q, const void *k, const void *v,
+                         const float *beta, int alpha_mode, const float *log_alpha,
+                         const float *S0, void *o, float *S_final,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gdr_bwd_chunked without the forward's recomputation, for the workspace a
+ * gdr_fwd_chunked_keep call filled: the same sizes, dtype, alpha_mode, C and
+ * inputs (q, k, v, beta, log_alpha, S0), the workspace unchanged since.
+ * Arguments, checks and errors as for gdr_bwd_chunked, whose results it
+ * then gives bit for bit.  A workspace that does not hold what such a call
+ * left gives meaningless gradients, but no access outside the arrays.
+ */
+int gdr_bwd_chunked_kept(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                         const void *q, const void *k, const void *v,
+                         const float *beta, int alpha_mode, const float *log_alpha,
+                         const float *S0, const void *dO, const float *dS_final,
+                         void *dq, void *dk, void *dv, float *dbeta, float *dlog_alpha,
+                         float *dS0, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Bytes of device workspace gdr_fwd_varlen needs (0 when N * H == 0), or
  * (size_t)-1 for invalid or unsupported sizes.  It is sized for any split
  * of the T tokens into N sequences: chunk records for at most

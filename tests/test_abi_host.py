@@ -108,10 +108,10 @@ Q, K, V, BETA, LA, S0, O, SF, WS = (A + i * (1 << 32) for i in range(9))
 
 
 def fwd(lib, B=1, H=1, L=64, dk=64, dv=64, C=64, dtype=1, q=Q, k=K, v=V, beta=BETA, mode=1,
-        la=LA, s0=S0, o=O, sf=SF, ws=WS, ws_bytes=1 << 30):
+        la=LA, s0=S0, o=O, sf=SF, ws=WS, ws_bytes=1 << 30, fn="gdr_fwd_chunked"):
     p = lambda x: None if x is None else ctypes.c_void_p(x)
-    return lib.gdr_fwd_chunked(B, H, L, dk, dv, C, dtype, p(q), p(k), p(v), p(beta), mode, p(la),
-                               p(s0), p(o), p(sf), p(ws), ws_bytes, None)
+    return getattr(lib, fn)(B, H, L, dk, dv, C, dtype, p(q), p(k), p(v), p(beta), mode, p(la),
+                            p(s0), p(o), p(sf), p(ws), ws_bytes, None)
 
 
 def fwd_ex(lib, pro, **kw):
@@ -156,9 +156,18 @@ def dec(lib, N=2, H=2, dk=64, dv=64, dtype=1, q=Q, k=K, v=V, beta=BETA, mode=1, 
     (dict(mode=2, ws_bytes=16), gdr.GDR_ERR_WORKSPACE_TOO_SMALL),
     (dict(mode=0, la=None, ws=None, ws_bytes=0), gdr.GDR_ERR_WORKSPACE_TOO_SMALL),
 ])
-def test_fwd_chunked_rejects_before_launch(lib, kw, status):
+@pytest.mark.parametrize("fn", ["gdr_fwd_chunked", "gdr_fwd_chunked_keep"])
+def test_fwd_chunked_rejects_before_launch(lib, kw, status, fn):
     assert status != gdr.GDR_OK  # every case must stop before a launch
-    assert fwd(lib, **kw) == status
+    assert fwd(lib, fn=fn, **kw) == status
+
+
+def test_keep_forward_needs_the_backward_workspace(lib):
+    # enough for the plain forward, not for what the backward keeps
+    fwd_need = gdr.gdr_fwd_chunked_workspace_size(1, 1, 64, 64, 64, 64, gdr.GDR_BF16, 1)
+    bwd_need = gdr.gdr_bwd_chunked_workspace_size(1, 1, 64, 64, 64, 64, gdr.GDR_BF16, 1)
+    assert 0 < fwd_need < bwd_need
+    assert fwd(lib, fn="gdr_fwd_chunked_keep", ws_bytes=bwd_need - 1) == gdr.GDR_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_fwd_chunked_empty_batch_is_a_noop(lib):
@@ -287,16 +296,17 @@ def test_backward_workspace_size_query():
     assert ws(1, 2, 0, 64, 64, 64, gdr.GDR_F32, 1) == 0
 
 
-def bwd(lib, B=1, H=1, L=64, dk=64, dv=64, C=64, dtype=1, mode=1, la=LA, ws_bytes=1 << 30, **kw):
+def bwd(lib, B=1, H=1, L=64, dk=64, dv=64, C=64, dtype=1, mode=1, la=LA, ws_bytes=1 << 30,
+        fn="gdr_bwd_chunked", **kw):
     p = lambda x: None if x is None else ctypes.c_void_p(x)
     ptr = dict(q=Q, k=K, v=V, beta=BETA, s0=S0, dO=A + 10 * (1 << 32), dsf=A + 11 * (1 << 32),
                dq=A + 12 * (1 << 32), dkp=A + 13 * (1 << 32), dvp=A + 14 * (1 << 32),
                db=A + 15 * (1 << 32), dla=A + 16 * (1 << 32), ds0=A + 17 * (1 << 32), ws=WS)
     ptr.update(kw)
-    return lib.gdr_bwd_chunked(B, H, L, dk, dv, C, dtype, p(ptr["q"]), p(ptr["k"]), p(ptr["v"]),
-                               p(ptr["beta"]), mode, p(la), p(ptr["s0"]), p(ptr["dO"]), p(ptr["dsf"]),
-                               p(ptr["dq"]), p(ptr["dkp"]), p(ptr["dvp"]), p(ptr["db"]), p(ptr["dla"]),
-                               p(ptr["ds0"]), p(ptr["ws"]), ws_bytes, None)
+    return getattr(lib, fn)(B, H, L, dk, dv, C, dtype, p(ptr["q"]), p(ptr["k"]), p(ptr["v"]),
+                            p(ptr["beta"]), mode, p(la), p(ptr["s0"]), p(ptr["dO"]), p(ptr["dsf"]),
+                            p(ptr["dq"]), p(ptr["dkp"]), p(ptr["dvp"]), p(ptr["db"]), p(ptr["dla"]),
+                            p(ptr["ds0"]), p(ptr["ws"]), ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -317,9 +327,10 @@ def bwd(lib, B=1, H=1, L=64, dk=64, dv=64, C=64, dtype=1, mode=1, la=LA, ws_byte
     (dict(mode=2, la=LA + 4), gdr.GDR_ERR_INVALID_ARG),
     (dict(ws_bytes=16), gdr.GDR_ERR_WORKSPACE_TOO_SMALL),
 ])
-def test_backward_rejects_before_launch(lib, kw, status):
+@pytest.mark.parametrize("fn", ["gdr_bwd_chunked", "gdr_bwd_chunked_kept"])
+def test_backward_rejects_before_launch(lib, kw, status, fn):
     assert status != gdr.GDR_OK   # every case must stop before a launch
-    assert bwd(lib, **kw) == status
+    assert bwd(lib, fn=fn, **kw) == status
 
 
 def test_binding_refuses_cpu_tensors():

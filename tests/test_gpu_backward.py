@@ -93,6 +93,50 @@ def test_backward_carried_state_runs(case, mode):
     check(run_bwd(x), oracle_bwd(x), 2e-2)
 
 
+# (B, H, L, d_k, d_v, dtype, C): the lean path, runs across heads, 16-token
+# steps (every chunk's state kept) and fp32
+KEEP = [(2, 2, 200, 128, 128, torch.bfloat16, 64), (1, 5, 32 * 60 + 5, 128, 128, torch.bfloat16, 64),
+        (1, 3, 97, 64, 128, torch.bfloat16, 16), (1, 2, 150, 64, 64, torch.float32, 64)]
+
+
+@pytest.mark.parametrize("case", KEEP, ids=lambda c: f"B{c[0]}H{c[1]}L{c[2]}dk{c[3]}dv{c[4]}{str(c[5])[6:]}C{c[6]}")
+@pytest.mark.parametrize("mode", MODES, ids=lambda m: gi.MODE_NAMES[m])
+def test_kept_forward_and_backward_match(case, mode):
+    """A training step through gdr_fwd_chunked_keep and gdr_bwd_chunked_kept
+    gives gdr_bwd_chunked's gradients bit for bit, and gdr_fwd_chunked's
+    outputs (up to rounding where that call splits a head's scan into
+    segments; the keeping forward never does)."""
+    B, H, L, dk, dv, dt, C = case
+    x = grads_inputs(B, H, L, dk, dv, dt, mode, seed=6700 + L + mode + dk)
+    d = {k: (None if t is None else t.cuda()) for k, t in x.items()}
+    o, sf, ws = gdr.gdr_fwd_chunked_keep(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["S0"], C)
+    o_ref, sf_ref = gdr.gdr_fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["S0"], C)
+    gk = gdr.gdr_bwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["S0"], d["dO"],
+                             d["dS_final"], C, workspace=ws, kept=True)
+    gr = gdr.gdr_bwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["S0"], d["dO"],
+                             d["dS_final"], C)
+    torch.cuda.synchronize()
+    assert rel_err(o.float().cpu().numpy(), o_ref.float().cpu().numpy()) <= TOL[dt]
+    assert rel_err(sf.cpu().numpy(), sf_ref.cpu().numpy()) <= TOL[dt]
+    for name in NAMES:
+        if gr[name] is None:
+            assert gk[name] is None
+        else:
+            assert torch.equal(gk[name], gr[name]), name
+
+
+def test_kept_empty_sequence():
+    x = grads_inputs(1, 2, 0, 64, 64, torch.bfloat16, gi.ALPHA_SCALAR, seed=6750)
+    d = {k: (None if t is None else t.cuda()) for k, t in x.items()}
+    o, sf, ws = gdr.gdr_fwd_chunked_keep(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["S0"])
+    g = gdr.gdr_bwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["S0"], d["dO"],
+                            d["dS_final"], workspace=ws if ws is not None else torch.empty(0, dtype=torch.uint8, device="cuda"),
+                            kept=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sf, d["S0"])
+    assert torch.equal(g["dS0"], d["dS_final"])
+
+
 @pytest.mark.parametrize("dt", DTYPES, ids=lambda d: str(d)[6:])
 def test_backward_channel_strong_decay(dt):
     """Channel gates near and past the floor of log alpha at -10: decays of
