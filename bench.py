@@ -52,15 +52,15 @@ FWD_SOURCES = ('gdr_wy.hip', 'gdr_scan.hip', 'gdr_segment.hip', 'gdr_pipe.h', 'g
 BWD_SOURCES = FWD_SOURCES + ('gdr_bwd.hip', 'gdr_bwd_chain.hip', 'gdr_bwd.h')
 MEASURED_TRAFFIC = {
     ("gdn_bf16_B8_H8_L2048_d128", "chunk_wy_kernel + chunk_scan_kernel"):
-        dict(sources=FWD_SOURCES, digest="129b4b78d9564e83", read=154.76e6, written=56.75e6),
+        dict(sources=FWD_SOURCES, digest="34ccea5ff7ee9608", read=154.75e6, written=56.73e6),
     ("kda_bf16_B4_H16_L4096_d128", "chunk_wy_channel_kernel + chunk_scan_kernel"):
-        dict(sources=FWD_SOURCES, digest="129b4b78d9564e83", read=576.33e6, written=310.38e6),
+        dict(sources=FWD_SOURCES, digest="34ccea5ff7ee9608", read=576.33e6, written=310.38e6),
     ("gdn_decode_bf16_N256_H16_d128", "decode_step_kernel"):
-        dict(sources=('gdr_decode.hip', 'gdr_device.h', 'gdr_internal.h'), digest="490e95c02c707566", read=274.33e6, written=269.49e6),
+        dict(sources=('gdr_decode.hip', 'gdr_device.h', 'gdr_internal.h'), digest="ceeaddb62259d5a3", read=274.33e6, written=269.50e6),
     ("gdn_bf16_B8_H8_L2048_d128 backward", "chunk_wy_kernel + chunk_scan_kernel + chunk_bwd_chain_pipe_kernel + chunk_bwd_grad_kernel"):
-        dict(sources=BWD_SOURCES, digest="143fdf0257cc43f2", read=525.61e6, written=284.16e6),
+        dict(sources=BWD_SOURCES, digest="f9064a390331ed08", read=525.62e6, written=284.17e6),
     ("kda_bf16_B4_H16_L4096_d128 backward", "chunk_wy_channel_kernel + chunk_scan_kernel + chunk_bwd_chain_pipe_kernel + chunk_bwd_grad_channel_kernel"):
-        dict(sources=BWD_SOURCES, digest="143fdf0257cc43f2", read=1662.44e6, written=890.25e6),
+        dict(sources=BWD_SOURCES, digest="f9064a390331ed08", read=1662.44e6, written=890.25e6),
 }
 
 
@@ -241,7 +241,7 @@ def bench_varlen(w, steps, warmup, copies):
     return dict(total_ms=e0.elapsed_time(e1), lengths=lens)
 
 
-def bench_backward(w, steps, warmup, copies):
+def bench_backward(w, steps, warmup, copies, train=True):
     """gdr_bwd_chunked on the workload's inputs with a random output gradient
     (the forward is recomputed inside every call)."""
     import gated_delta_rule_88_amd as gdr
@@ -273,6 +273,8 @@ def bench_backward(w, steps, warmup, copies):
     e1.record()
     torch.cuda.synchronize()
     total = e0.elapsed_time(e1)
+    if not train:
+        return dict(total_ms=total, ws_bytes=need, train=None)
 
     # a training step both ways: the forward, then the backward recomputing
     # it; or the keeping forward, then the backward from what it kept
@@ -458,7 +460,8 @@ def main():
     ap.add_argument("--cpu-single-seconds", type=float, default=4.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-legs", action="store_true",
-                    help="skip the channel-gate and sequence-length-sweep legs of the default run")
+                    help="skip the channel-gate and sequence-length-sweep legs of the default run "
+                         "(with --backward: the training-step timings)")
     ap.add_argument("--backward", action="store_true",
                     help="time the chunked backward (gradients) on --workload instead (one JSON "
                          "line of its own)")
@@ -487,7 +490,7 @@ def main():
         return
     if args.backward:
         w = WORKLOADS[args.workload]
-        r = bench_backward(w, args.steps, args.warmup, min(args.copies, 2))
+        r = bench_backward(w, args.steps, args.warmup, min(args.copies, 2), train=not args.no_legs)
         ms = r["total_ms"] / args.steps
         es = 2 if w.dtype == torch.bfloat16 else 4
         ht = w.B * w.H * w.L
