@@ -741,16 +741,30 @@ __device__ __forceinline__ void st4bf(unsigned char* p, f32x4 x) {
 template <int DK>
 struct LeanPf {
     u32x4 r[LeanVB<DK>::NPF];
-    int valid;   // token rows of the block's chunk
+    int valid;      // token rows of the block's chunk
+    int pn, pbh;    // the chunk the loads read: its index within its head, the head
+    // position at chunk c (one division), then one chunk on (none)
+    __device__ __forceinline__ void at(const BwdParams& p, int c) {
+        c = __builtin_amdgcn_readfirstlane(c);
+        pn = c % p.NC;
+        pbh = c / p.NC;
+    }
+    __device__ __forceinline__ void step(const BwdParams& p) {
+        if (++pn == p.NC) {
+            pn = 0;
+            ++pbh;
+        }
+    }
+    // chunk c, which at() and step() have positioned
     __device__ __forceinline__ void load(const BwdParams& p, int c, int v0, int t) {
         using LV = LeanVB<DK>;
         constexpr int CK = 32;
         // the block's chunk arithmetic on the scalar unit
         c = __builtin_amdgcn_readfirstlane(c);
         v0 = __builtin_amdgcn_readfirstlane(v0);
-        const int n = c % p.NC;
+        const int n = pn;
         valid = min(CK, p.L - n * CK);
-        const size_t tok = (size_t)(c / p.NC) * p.L + (size_t)n * CK;
+        const size_t tok = (size_t)pbh * p.L + (size_t)n * CK;
         const bf16* ds = static_cast<const bf16*>(p.dSck) + ((size_t)c * p.DV + v0) * DK;
 #pragma unroll
         for (int i = 0; i < LV::NPS; ++i) r[i] = ld16(ds + (uint32_t)(8 * (t + 256 * i)));
@@ -910,6 +924,7 @@ __device__ __forceinline__ void lean_value_blocks(
                 } else {
                     pv0 = 0;
                     ++pc;
+                    pf.step(p);
                 }
                 if (up && pc < pend) pf.load(p, pc, pv0, tid);
             }
@@ -1146,12 +1161,17 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(BwdParams p)
     if (cid0 < cend) {
         fetch_chunk(cid0, threadIdx.x);
         if constexpr (LY::LEAN) {
+            lpf.at(p, lpc);
             if (threadIdx.x < 256) {
                 lpf.load(p, lpc, 0, threadIdx.x);
                 lpf.store(smem + LY::off_lean, threadIdx.x);
             }
-            if (p.DV > 32) lpv0 = 32;
-            else ++lpc;
+            if (p.DV > 32) {
+                lpv0 = 32;
+            } else {
+                ++lpc;
+                lpf.step(p);
+            }
             if (threadIdx.x < 256 && lpc < cend) lpf.load(p, lpc, lpv0, threadIdx.x);
         } else {
             fetch_block(cid0, 0, threadIdx.x);
@@ -1719,12 +1739,17 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_channel_kernel(BwdParams p
     if (cid0 < cend) {
         fetch_chunk(cid0, threadIdx.x);
         if constexpr (LY::LEAN) {
+            lpf.at(p, lpc);
             if (threadIdx.x < 256) {
                 lpf.load(p, lpc, 0, threadIdx.x);
                 lpf.store(smem + LY::off_lean, threadIdx.x);
             }
-            if (p.DV > 32) lpv0 = 32;
-            else ++lpc;
+            if (p.DV > 32) {
+                lpv0 = 32;
+            } else {
+                ++lpc;
+                lpf.step(p);
+            }
             if (threadIdx.x < 256 && lpc < cend) lpf.load(p, lpc, lpv0, threadIdx.x);
         } else {
             fetch_block(cid0, 0, threadIdx.x);
