@@ -313,6 +313,22 @@ def bench_backward(w, steps, warmup, copies, train=True):
     return dict(total_ms=total, ws_bytes=need, train=train)
 
 
+def backward_bytes(w):
+    """(algorithmic bytes per backward call, the kernels it launches)."""
+    es = 2 if w.dtype == torch.bfloat16 else 4
+    ht = w.B * w.H * w.L
+    gate = {gi.ALPHA_NONE: 0, gi.ALPHA_SCALAR: 4, gi.ALPHA_CHANNEL: 4 * w.dk}[w.mode]
+    # read q, k, v, dO, beta, log alpha; write dq, dk, dv, dbeta, dlog alpha
+    nbytes = ht * (es * (4 * w.dk + 3 * w.dv) + 8 + 2 * gate)
+    pipe = w.dtype == torch.bfloat16 and w.C >= 32   # 32-token steps: the pipelined chain
+    kernel = " + ".join((
+        "chunk_wy_channel_kernel" if w.mode == gi.ALPHA_CHANNEL else "chunk_wy_kernel",
+        "chunk_scan_kernel",
+        "chunk_bwd_chain_pipe_kernel" if pipe else "chunk_bwd_chain_kernel",
+        "chunk_bwd_grad_channel_kernel" if w.mode == gi.ALPHA_CHANNEL else "chunk_bwd_grad_kernel"))
+    return nbytes, kernel
+
+
 def bench_decode(w, steps, prologue=0):
     import gated_delta_rule_88_amd as gdr
 
@@ -492,17 +508,7 @@ def main():
         w = WORKLOADS[args.workload]
         r = bench_backward(w, args.steps, args.warmup, min(args.copies, 2), train=not args.no_legs)
         ms = r["total_ms"] / args.steps
-        es = 2 if w.dtype == torch.bfloat16 else 4
-        ht = w.B * w.H * w.L
-        gate = {gi.ALPHA_NONE: 0, gi.ALPHA_SCALAR: 4, gi.ALPHA_CHANNEL: 4 * w.dk}[w.mode]
-        # read q, k, v, dO, beta, log alpha; write dq, dk, dv, dbeta, dlog alpha
-        nbytes = ht * (es * (4 * w.dk + 3 * w.dv) + 8 + 2 * gate)
-        pipe = w.dtype == torch.bfloat16 and w.C >= 32   # 32-token steps: the pipelined chain
-        bwd_kernel = " + ".join((
-            "chunk_wy_channel_kernel" if w.mode == gi.ALPHA_CHANNEL else "chunk_wy_kernel",
-            "chunk_scan_kernel",
-            "chunk_bwd_chain_pipe_kernel" if pipe else "chunk_bwd_chain_kernel",
-            "chunk_bwd_grad_channel_kernel" if w.mode == gi.ALPHA_CHANNEL else "chunk_bwd_grad_kernel"))
+        nbytes, bwd_kernel = backward_bytes(w)
         print(json.dumps({
             "metric": "tokens/s chunked gated delta-rule backward (gradients; forward recomputed "
                       "inside)",
@@ -580,6 +586,22 @@ def main():
                       **ks}
         torch.cuda.empty_cache()
         out["sweep"] = sweep_leg(max(args.steps // 10, 10), max(args.warmup // 10, 10))
+        torch.cuda.empty_cache()
+        # the backward on the headline workload (forward recomputed inside),
+        # and a training step both ways
+        bw = gi.GDN_BF16
+        nb = max(args.steps // 10, 20)
+        br = bench_backward(bw, nb, max(args.warmup // 20, 5), 2)
+        bms = br["total_ms"] / nb
+        bbytes, bkern = backward_bytes(bw)
+        out["backward"] = {
+            "workload": bw.name, "us_per_call": bms * 1e3, "tokens_per_s": bw.tokens / (bms / 1e3),
+            "roofline": {"bound": "hbm", "achieved": bbytes / (bms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": bbytes / (bms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": measured_traffic(bw.name + " backward", bkern), "kernel": bkern,
+                         "algorithmic_bytes_per_call": bbytes},
+            "training_step": br["train"],
+        }
     if not args.no_decode:
         dw = gi.DECODE_BF16
         dr = bench_decode(dw, args.decode_steps, args.prologue)
