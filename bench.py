@@ -58,9 +58,9 @@ MEASURED_TRAFFIC = {
     ("gdn_decode_bf16_N256_H16_d128", "decode_step_kernel"):
         dict(sources=('gdr_decode.hip', 'gdr_device.h', 'gdr_internal.h'), digest="ceeaddb62259d5a3", read=274.33e6, written=269.50e6),
     ("gdn_bf16_B8_H8_L2048_d128 backward", "chunk_wy_kernel + chunk_scan_kernel + chunk_bwd_chain_pipe_kernel + chunk_bwd_grad_kernel"):
-        dict(sources=BWD_SOURCES, digest="dc6efcfc4ae580b7", read=525.62e6, written=284.16e6),
+        dict(sources=BWD_SOURCES, digest="28303736caff90eb", read=525.62e6, written=284.16e6),
     ("kda_bf16_B4_H16_L4096_d128 backward", "chunk_wy_channel_kernel + chunk_scan_kernel + chunk_bwd_chain_pipe_kernel + chunk_bwd_grad_channel_kernel"):
-        dict(sources=BWD_SOURCES, digest="dc6efcfc4ae580b7", read=1662.44e6, written=890.26e6),
+        dict(sources=BWD_SOURCES, digest="28303736caff90eb", read=1662.44e6, written=890.26e6),
 }
 
 

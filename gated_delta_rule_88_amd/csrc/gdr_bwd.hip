@@ -23,17 +23,23 @@
 // and "Gated DeltaNet"; the WY factor of "Linear Attention & DeltaNet",
 // "How it works", item 3.)
 //
-// Launches: the forward prepass and scan run again (the scan keeping the
-// state entering every chunk), then
+// Launches: the forward prepass and scan run again (the prepass also keeping
+// every chunk's T, the scan the entry states the gradient walk starts from:
+// every chunk's, or for bf16 on 32-token steps the state entering each run
+// of chunks), unless a keeping forward left them; then
 //   chunk_bwd_chain_kernel  one workgroup per (b, h, 32 value channels)
-//                           walks the chunks backwards carrying dS (the
-//                           only sequential part) and keeps dS_end of every
-//                           chunk;
+//                           walks the chunks backwards carrying dS and
+//                           keeps dS_end of every chunk (the pipelined form
+//                           for bf16 on 32-token steps is in
+//                           gdr_bwd_chain.hip);
 //   chunk_bwd_grad_kernel   every gradient of a chunk's tokens from S0,
-//                           dS_end and its inputs; persistent, one workgroup
-//                           per CU walking the chunks
-//                           (chunk_bwd_grad_channel_kernel for channel alpha,
-//                           whose chunk algebra is written out above it).
+//                           dS_end and its inputs: for bf16 on 32-token
+//                           steps one workgroup per run of consecutive
+//                           chunks, carrying the state across it; otherwise
+//                           persistent, one workgroup per CU walking the
+//                           chunks (chunk_bwd_grad_channel_kernel for
+//                           channel alpha, whose chunk algebra is written
+//                           out above it).
 // The products run on MFMA (bf16 operands for bf16 inputs, fp32 otherwise;
 // fp32 accumulation); the triangular parts (T, dA) stay in fp32.
 #include "gdr_device.h"
