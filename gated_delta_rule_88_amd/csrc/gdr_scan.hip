@@ -123,6 +123,10 @@ __global__ __launch_bounds__(64 * 8) void chunk_scan_kernel(ScanParams p)
     size_t tok0 = (size_t)bh * p.L, rec0 = (size_t)bh * p.NC;
     int len = p.L;
     int NC = min(p.NCS, p.NC - c0);                    // chunks this workgroup walks
+    // a recomputation that keeps only every sck_every-th entry state and forms
+    // no outputs stops at the last chunk of the head whose entry state it keeps
+    if (p.Sck && p.sck_every > 1 && !p.o && !p.S_final && p.SEG == 1 && !p.vl.start)
+        NC = max(1, NC - (int)((rec0 + NC - 1) % p.sck_every));
     if (p.vl.start) {
         const int n = bh / p.H, h = bh % p.H;
         const int cb = p.vl.choff[n];
