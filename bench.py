@@ -466,7 +466,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed calls first (200 x 66 us brings the GPU to its steady clock; "
-                         "with 20 the first timed calls run up to 8 % slower)")
+                         "with 20 the first timed calls run up to 8 %% slower)")
     ap.add_argument("--workload", default=gi.GDN_BF16.name, choices=sorted(WORKLOADS))
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--decode-steps", type=int, default=1024)
