@@ -2338,7 +2338,7 @@ hipError_t launch_bwd_chunked(const BwdArgs& b)
                     nullptr, 0, Varlen{}, ws + w.off_Sck, reinterpret_cast<float*>(ws + w.off_T), span};
         hipError_t err = launch_wy(a, CK);
         if (err != hipSuccess) return err;
-        SegPlan one{1, NC, 0, 0, 0, 0, 0};
+        SegPlan one{1, NC, NC, 0, 0, 0, 0, 0};
         err = launch_scan(a, CK, one);
         if (err != hipSuccess || b.part == kBwdKeep) return err;
     }

@@ -117,9 +117,10 @@ struct ScanParams {
     void* o;
     float* S_final;
     int L, NC, DV, NVB, total;   // total = B * H * (NVB + (SEG - 1) * (NVB + NMB)) workgroups
-    // Segment-parallel scan (SEG > 1): segment g covers chunks
-    // [g NCS, min((g + 1) NCS, NC)); NMB blocks of 32 key rows per later segment.
-    int SEG, NCS, NMB;
+    // Segment-parallel scan (SEG > 1): segment 0 covers chunks [0, N0), segment
+    // g >= 1 chunks [N0 + (g - 1) NCS, min(N0 + g NCS, NC)); NMB blocks of 32
+    // key rows per later segment.
+    int SEG, NCS, NMB, N0;
     void* qt;       // [B*H][L][d_k] (input dtype): (transition from the segment start) q_t
     float* Sseg;    // [B*H][SEG][d_v][d_k]: segment end state from S0 (g = 0) or zero (g > 0)
     float* Pseg;    // [B*H][SEG][d_k][d_k]: segment transition (g > 0)
@@ -151,29 +152,64 @@ struct ScanParams {
 constexpr int kSegWorkgroups = 256;   // scan workgroups the device runs at once (one per CU)
 constexpr int kSegMinChunks = 16;     // shortest segment worth splitting off
 constexpr int kMaxSeg = 16;
+// Chain-chunks of later segments whose output correction (seg_correct_kernel:
+// (P up to t) q_t and o read, o written) costs about one scan step of the
+// whole batch (measured at B1 H16 L65536: 97 us for 16 x 1024 chain-chunks,
+// 0.64 us per scan step).
+constexpr int kSegCorrectPerStep = 110;
 
 struct SegPlan {
-    int SEG, NCS;                     // segments, chunks per segment (the last may be shorter)
+    int SEG, NCS, N0;                 // segments, chunks per later segment (the last may be
+                                      // shorter), chunks of segment 0
     size_t off_Z, off_P, off_E, off_qt, bytes;   // extra workspace after the chunk records
 };
 
+// The plan with the shortest estimated time, in scan steps: the longest run
+// of chunks any CU walks, plus the later segments' output correction.
+//  - When every workgroup fits the budget at once, the segments are equal.
+//  - A plan may hold more workgroups than the budget when B*H is a multiple of
+//    8: the scan then orders each XCD's workgroups with every segment-0
+//    workgroup first (gdr_scan.hip), so the ones left waiting for a free CU are
+//    later-segment workgroups, which start when the first of them finish.
+//    With segment 0 twice as long as a later segment, those finish together
+//    with segment 0: NC = a + (SEG - 1) b with a = 2 b.  This needs the
+//    waiting workgroups to be no more than the later-segment workgroups of
+//    the first round: W - 256 <= 256 - B*H*NVB.
 inline SegPlan seg_plan(int B, int H, int L, int dk, int dv, int CK, int dtype, size_t base)
 {
-    SegPlan sp{1, 0, 0, 0, 0, 0, 0};
     const int NC = (L + CK - 1) / CK;
-    sp.NCS = NC;
+    SegPlan sp{1, NC, NC, 0, 0, 0, 0, 0};
     const size_t BH = (size_t)B * H;
-    const int NVB = dv / 32, NMB = dk / 32;
-    if (dtype != kBF16 || BH == 0) return sp;
-    int seg = 1;
+    const size_t NVB = dv / 32, NMB = dk / 32;
+    const size_t W0 = BH * NVB;
+    if (dtype != kBF16 || BH == 0 || W0 > (size_t)kSegWorkgroups || NC < 2 * kSegMinChunks) return sp;
+    double best = NC;
     for (int g = 2; g <= kMaxSeg; ++g) {
-        if (BH * (size_t)(NVB + (g - 1) * (NVB + NMB)) > (size_t)kSegWorkgroups) break;
-        if (NC < g * kSegMinChunks) break;
-        seg = g;
+        const size_t W = BH * (NVB + (g - 1) * (NVB + NMB));
+        int n0, ncs, seg = g;
+        if (W <= (size_t)kSegWorkgroups) {
+            ncs = (NC + g - 1) / g;
+            seg = (NC + ncs - 1) / ncs;
+            n0 = ncs;
+        } else if (BH % 8 == 0 && W + W0 <= 2 * (size_t)kSegWorkgroups) {
+            ncs = (NC + g) / (g + 1);
+            n0 = NC - (g - 1) * ncs;
+            if (n0 < ncs) continue;
+        } else {
+            break;
+        }
+        if (seg < 2 || ncs < kSegMinChunks) break;
+        const int later = NC - n0;
+        const int span = W <= (size_t)kSegWorkgroups ? max(n0, ncs) : max(n0, 2 * ncs);
+        const double t = span + (double)BH * later / kSegCorrectPerStep;
+        if (t < best) {
+            best = t;
+            sp.SEG = seg;
+            sp.NCS = ncs;
+            sp.N0 = n0;
+        }
     }
-    if (seg == 1) return sp;
-    sp.NCS = (NC + seg - 1) / seg;
-    sp.SEG = (NC + sp.NCS - 1) / sp.NCS;
+    if (sp.SEG == 1) return sp;
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     size_t o = al(base);
     sp.off_Z = o; o = al(o + BH * sp.SEG * dv * dk * 4);

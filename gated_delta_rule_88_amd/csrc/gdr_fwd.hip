@@ -128,7 +128,8 @@ hipError_t launch_fwd_varlen(ChunkArgs a)
         err = launch_wy(a, CK);
         if (err != hipSuccess) return err;
     }
-    SegPlan one{1, (a.L + CK - 1) / CK, 0, 0, 0, 0, 0};
+    const int NC = (a.L + CK - 1) / CK;
+    SegPlan one{1, NC, NC, 0, 0, 0, 0, 0};
     return launch_scan(a, CK, one);
 }
 

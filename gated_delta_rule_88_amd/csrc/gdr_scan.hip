@@ -104,9 +104,28 @@ __global__ __launch_bounds__(64 * 8) void chunk_scan_kernel(ScanParams p)
         vb = lid % p.NVB;
     } else {
         const int per_seg = p.NVB + p.NMB;
-        const int units = p.NVB + (p.SEG - 1) * per_seg;
-        bh = lid / units;
-        int u = lid % units;
+        const int later = (p.SEG - 1) * per_seg;        // later-segment workgroups per chain
+        const int units = p.NVB + later;
+        const int nbh = p.total / units;
+        int u;
+        if (p.SEG > 1 && nbh % 8 == 0) {
+            // eight groups of chains, one per XCD (the order above); in each
+            // group every segment-0 workgroup comes first, so that when the
+            // plan holds more workgroups than the CUs run at once, the ones
+            // that wait for a free CU belong to the (shorter) later segments
+            const int cpg = nbh / 8, r = lid % (cpg * units);
+            bh = (lid / (cpg * units)) * cpg;
+            if (r < cpg * p.NVB) {
+                bh += r / p.NVB;
+                u = r % p.NVB;
+            } else {
+                bh += (r - cpg * p.NVB) / later;
+                u = p.NVB + (r - cpg * p.NVB) % later;
+            }
+        } else {
+            bh = lid / units;
+            u = lid % units;
+        }
         if (u < p.NVB) {
             vb = u;
         } else {
@@ -118,11 +137,11 @@ __global__ __launch_bounds__(64 * 8) void chunk_scan_kernel(ScanParams p)
         }
     }
     const int v0 = vb * BV;                            // first value channel (key row for key rows)
-    const int c0 = sg * p.NCS;                         // first chunk
+    const int c0 = sg == 0 ? 0 : p.N0 + (sg - 1) * p.NCS;   // first chunk
     // the chain's tokens: head row start on the token axis, length, first record
     size_t tok0 = (size_t)bh * p.L, rec0 = (size_t)bh * p.NC;
     int len = p.L;
-    int NC = min(p.NCS, p.NC - c0);                    // chunks this workgroup walks
+    int NC = min(sg == 0 ? p.N0 : p.NCS, p.NC - c0);   // chunks this workgroup walks
     // a recomputation that keeps only every sck_every-th entry state and forms
     // no outputs stops at the last chunk of the head whose entry state it keeps
     if (p.Sck && p.sck_every > 1 && !p.o && !p.S_final && p.SEG == 1 && !p.vl.start)
@@ -726,7 +745,7 @@ static hipError_t launch_scan_t(const ChunkArgs& a, const SegPlan& seg)
     const int total = a.vl.start ? a.vl.NS * a.H * NVB : BH * (NVB + (seg.SEG - 1) * (NVB + NMB));
     unsigned char* ws = static_cast<unsigned char*>(a.workspace);
     ScanParams sp{a.q, a.k, a.v, a.S0, ws, a.o, a.S_final, a.L, NC, a.dv, NVB, total,
-                  seg.SEG, seg.NCS, NMB, nullptr, nullptr, nullptr, a.H, a.vl, a.Sck};
+                  seg.SEG, seg.NCS, NMB, seg.N0, nullptr, nullptr, nullptr, a.H, a.vl, a.Sck};
     sp.sck_every = a.sck_every > 0 ? a.sck_every : 1;
     if (seg.SEG > 1) {
         sp.qt = ws + seg.off_qt;

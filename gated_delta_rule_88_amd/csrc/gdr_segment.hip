@@ -31,143 +31,179 @@ struct SegArgs {
     const bf16* qt;      // [BH][L][DK]
     bf16* o;             // [BH][L][DV]
     float* S_final;      // [BH][DV][DK] or null
-    int L, DV, SEG, TS;  // TS: tokens per segment
+    int L, DV, SEG, TS;  // TS: tokens per later segment
+    int T0;              // tokens of segment 0
 };
 
-// One wave per (head, 16 value rows).  The rows of E evolve independently:
-// row r of E_{g+1} is row r of E_g times P_g plus row r of Z_g.
+// One workgroup per (head, 16 value rows), one wave per 16 key columns of E.
+// The rows of E evolve independently: row r of E_{g+1} is row r of E_g times
+// P_g plus row r of Z_g.  A wave reads its operands for the next segment (its
+// 16 columns of P_g and its tile of Z_g) before the current product, so the
+// sequential path holds only the product and the exchange of E_g's 16 rows
+// through LDS.  That exchange alternates between two buffers with one barrier
+// per segment: the compiler may schedule a wave's reads of the rows after a
+// second barrier placed behind them (it did), so no barrier is relied on to
+// order them before the rows are rewritten; a buffer is rewritten only two
+// segments later, after the next barrier, which no wave passes before every
+// wave has used its reads.
 template <int DK>
-__global__ __launch_bounds__(64) void seg_entry_kernel(SegArgs p)
+__global__ __launch_bounds__(64 * (DK / 16)) void seg_entry_kernel(SegArgs p)
 {
-    constexpr int NJ = DK / 16, NKS = DK / 32;
-    __shared__ __align__(16) float rows[16][DK + 4];
+    constexpr int NKS = DK / 32;
+    __shared__ __align__(16) float rows[2][16][DK + 4];
     const int l = lane_id(), g4 = l >> 4, c16 = l & 15;
+    const int j = wave_id();                 // key columns 16 j ..
     const int nrb = p.DV / 16;
     const int bh = blockIdx.x / nrb, r0 = 16 * (blockIdx.x % nrb);
 
-    // e[j]: lane holds E[r0 + 4 g4 + i][16 j + c16], i = 0..3
-    f32x4 e[NJ];
-    const float* Z0 = p.Z + ((size_t)bh * p.SEG * p.DV + r0) * DK;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) e[j][i] = Z0[(size_t)(4 * g4 + i) * DK + 16 * j + c16];
-
-    for (int g = 1; g < p.SEG; ++g) {
+    // segment g's operands, as read: P_g[k][16 j + c16] = P_g^T[16 j + c16][k]
+    // for k = 32 ks + 8 g4 .. + 7, and the lane's four values of Z_g
+    f32x4 plo[NKS], phi[NKS], z;
+    auto load = [&](int g) {
         const size_t bs = (size_t)bh * p.SEG + g;
-        // keep E_g (bf16) and stage it row-major for the operand reads
-        bf16* eb = p.Eb + (bs * p.DV + r0) * DK;
+        const float* src = p.Pt + bs * DK * DK + (size_t)(16 * j + c16) * DK + 8 * g4;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
+        for (int ks = 0; ks < NKS; ++ks) {
+            plo[ks] = *reinterpret_cast<const f32x4*>(src + 32 * ks);
+            phi[ks] = *reinterpret_cast<const f32x4*>(src + 32 * ks + 4);
+        }
+        const float* zg = p.Z + (bs * p.DV + r0) * DK + 16 * j + c16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                eb[(size_t)(4 * g4 + i) * DK + 16 * j + c16] = (bf16)e[j][i];
-                rows[4 * g4 + i][16 * j + c16] = e[j][i];
-            }
+        for (int i = 0; i < 4; ++i) z[i] = zg[(size_t)(4 * g4 + i) * DK];
+    };
+
+    // e: lane holds E[r0 + 4 g4 + i][16 j + c16], i = 0..3; E_1 = Z_0
+    load(0);
+    f32x4 e = z;
+    if (p.SEG > 1) load(1);
+    for (int g = 1; g < p.SEG; ++g) {
+        // keep E_g (bf16) and pass its rows to every wave
+        bf16* eb = p.Eb + (((size_t)bh * p.SEG + g) * p.DV + r0) * DK + 16 * j + c16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            eb[(size_t)(4 * g4 + i) * DK] = (bf16)e[i];
+            rows[g & 1][4 * g4 + i][16 * j + c16] = e[i];
+        }
         __syncthreads();
         Frag<bf16> a[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             float x[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = rows[c16][32 * ks + 8 * g4 + i];
+            for (int i = 0; i < 8; ++i) x[i] = rows[g & 1][c16][32 * ks + 8 * g4 + i];
             a[ks].v = __builtin_bit_cast(bf16x8, Pack<bf16>::pack(x));
         }
-        __syncthreads();
-        // E_{g+1} = E_g P_g + Z_g; operand b[j][k] = P_g[k][j] = P_g^T[j][k]
-        const float* Pt = p.Pt + bs * DK * DK;
-        const float* Zg = p.Z + (bs * p.DV + r0) * DK;
+        // E_{g+1} = E_g P_g + Z_g
+        Frag<bf16> b[NKS];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            f32x4 acc;
+        for (int ks = 0; ks < NKS; ++ks) {
+            float x[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = Zg[(size_t)(4 * g4 + i) * DK + 16 * j + c16];
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const float* src = Pt + (size_t)(16 * j + c16) * DK + 32 * ks + 8 * g4;
-                float x[8];
-                const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
-                const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) { x[i] = lo[i]; x[4 + i] = hi[i]; }
-                Frag<bf16> b;
-                b.v = __builtin_bit_cast(bf16x8, Pack<bf16>::pack(x));
-                mma(acc, a[ks], b);
-            }
-            e[j] = acc;
+            for (int i = 0; i < 4; ++i) { x[i] = plo[ks][i]; x[4 + i] = phi[ks][i]; }
+            b[ks].v = __builtin_bit_cast(bf16x8, Pack<bf16>::pack(x));
         }
+        f32x4 acc = z;
+        if (g + 1 < p.SEG) load(g + 1);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) mma(acc, a[ks], b[ks]);
+        e = acc;
     }
     if (p.S_final) {
-        float* sf = p.S_final + ((size_t)bh * p.DV + r0) * DK;
+        float* sf = p.S_final + ((size_t)bh * p.DV + r0) * DK + 16 * j + c16;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sf[(size_t)(4 * g4 + i) * DK + 16 * j + c16] = e[j][i];
+        for (int i = 0; i < 4; ++i) sf[(size_t)(4 * g4 + i) * DK] = e[i];
     }
 }
 
-// One workgroup per (head, segment g >= 1, kTokWG tokens): E_g (bf16) in LDS,
-// each wave walks 16-token tiles and adds E_g (P up to t) q_t to o.  A tile's
-// reads of o and q are all issued before its products, so one round trip to
-// memory covers the whole tile.
-constexpr int kTokWG = 512;
+// One workgroup (four waves) per (head, segment g >= 1, kTokWG tokens), E_g
+// (bf16) in LDS.  Each wave walks 32-token tiles.  The corrections
+// E_g (P up to t) q_t of a 16-token half come out of the MFMA as
+// [value][token] fragments and pass through the wave's own LDS tile to token
+// rows, so that o is read and written as whole rows, 16 bytes a lane.  The
+// next tile's q-transitions and o rows are read before the current tile's
+// products.
+constexpr int kTokWG = 1024;
 
-template <int DK>
+template <int DK, int DV>
 __global__ __launch_bounds__(256) void seg_correct_kernel(SegArgs p, int tiles_per_seg)
 {
-    constexpr int NKS = DK / 32;
-    constexpr int RS = DK + 8;                 // padded LDS row (elements)
-    constexpr int MAXVT = 8;                   // d_v / 16 <= 8
+    constexpr int NKS = DK / 32, NVT = DV / 16;
+    constexpr int RS = DK + 8;      // E row stride (bf16 elements)
+    constexpr int CS = DV + 4;      // correction tile row stride (floats)
+    constexpr int LPR = DV / 8;     // lanes per o row, 16 bytes each
+    constexpr int RPI = 64 / LPR;   // o rows per load or store instruction
+    constexpr int NI = 32 / RPI;    // o instructions per 32-token tile
     extern __shared__ __align__(16) unsigned char smem[];
     bf16* es = reinterpret_cast<bf16*>(smem);
     const int l = lane_id(), g4 = l >> 4, c16 = l & 15, w = wave_id();
+    float* cs = reinterpret_cast<float*>(smem + DV * RS * 2) + w * 16 * CS;
     const int per_head = (p.SEG - 1) * tiles_per_seg;
     const int bh = blockIdx.x / per_head;
     const int rem = blockIdx.x % per_head;
     const int g = 1 + rem / tiles_per_seg, tile = rem % tiles_per_seg;
-    const int t_seg = g * p.TS, t_end = min(t_seg + p.TS, p.L);
-    const int nvt = p.DV / 16;
+    const int t_seg = p.T0 + (g - 1) * p.TS, t_end = min(t_seg + p.TS, p.L);
 
-    const bf16* eb = p.Eb + (((size_t)bh * p.SEG + g) * p.DV) * DK;
-    for (int i = threadIdx.x; i < p.DV * DK / 8; i += 256) {
+    const bf16* eb = p.Eb + (((size_t)bh * p.SEG + g) * DV) * DK;
+    for (int i = threadIdx.x; i < DV * DK / 8; i += 256) {
         const int r = i / (DK / 8), c = (i % (DK / 8)) * 8;
         st16(es + r * RS + c, ld16(eb + (size_t)r * DK + c));
     }
     __syncthreads();
 
     const bf16* qt = p.qt + (size_t)bh * p.L * DK;
-    bf16* o = p.o + (size_t)bh * p.L * p.DV;
+    bf16* o = p.o + (size_t)bh * p.L * DV;
     const int tw0 = t_seg + kTokWG * tile;
     const int tw1 = min(tw0 + kTokWG, t_end);
-    for (int t0 = tw0 + 16 * w; t0 < tw1; t0 += 64) {   // wave-uniform
-        const int t = t0 + c16;
-        const bool live = t < tw1;
-        const int tc = min(t, tw1 - 1);
-        Frag<bf16> qf[NKS];
+    const int orow = l / LPR, ocol = (l % LPR) * 8;   // this lane's row in an o instruction, first column
+    struct Tile {
+        Frag<bf16> q[2][NKS];   // token 16 h + c16, key channels 32 ks + 8 g4 ..
+        u32x4 o[NI];            // row RPI i + orow, columns ocol ..
+    };
+    auto load = [&](int t0, Tile& T) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            qf[ks].v = *reinterpret_cast<const bf16x8*>(qt + (size_t)tc * DK + 32 * ks + 8 * g4);
-        // lane (g4, c16): o[t][16 vt + 4 g4 + i]
-        bf16* orow = o + (size_t)tc * p.DV + 4 * g4;
-        u32x2 cur[MAXVT];
+        for (int h = 0; h < 2; ++h) {
+            const int tc = min(t0 + 16 * h + c16, tw1 - 1);
 #pragma unroll
-        for (int vt = 0; vt < MAXVT; ++vt)
-            if (vt < nvt) cur[vt] = ld8(orow + 16 * vt);
+            for (int ks = 0; ks < NKS; ++ks)
+                T.q[h][ks].v = *reinterpret_cast<const bf16x8*>(qt + (size_t)tc * DK + 32 * ks + 8 * g4);
+        }
 #pragma unroll
-        for (int vt = 0; vt < MAXVT; ++vt) {
-            if (vt < nvt) {
+        for (int i = 0; i < NI; ++i) T.o[i] = ld16(o + (size_t)min(t0 + RPI * i + orow, tw1 - 1) * DV + ocol);
+    };
+    Tile cur, nxt;
+    int t0 = tw0 + 32 * w;   // wave-uniform
+    if (t0 < tw1) load(t0, cur);
+    for (; t0 < tw1; t0 += 128) {
+        if (t0 + 128 < tw1) load(t0 + 128, nxt);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt) {
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
                     Frag<bf16> a;
                     a.v = *reinterpret_cast<const bf16x8*>(es + (16 * vt + c16) * RS + 32 * ks + 8 * g4);
-                    mma(acc, a, qf[ks]);
+                    mma(acc, a, cur.q[h][ks]);
                 }
-                if (live)
-                    st4(orow + 16 * vt, bf_lo(cur[vt].x) + acc[0], bf_hi(cur[vt].x) + acc[1],
-                        bf_lo(cur[vt].y) + acc[2], bf_hi(cur[vt].y) + acc[3]);
+                // acc[e]: value 16 vt + 4 g4 + e of token 16 h + c16
+                *reinterpret_cast<f32x4*>(cs + c16 * CS + 16 * vt + 4 * g4) = acc;
             }
+            wave_lds_fence();
+#pragma unroll
+            for (int i = h * (NI / 2); i < (h + 1) * (NI / 2); ++i) {
+                const int r = RPI * i + orow;                 // row within the tile
+                const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs + (r - 16 * h) * CS + ocol);
+                const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + (r - 16 * h) * CS + ocol + 4);
+                float x[8];
+                Pack<bf16>::unpack(cur.o[i], x);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { x[e] += c0[e]; x[4 + e] += c1[e]; }
+                if (t0 + r < tw1) st16(o + (size_t)(t0 + r) * DV + ocol, Pack<bf16>::pack(x));
+            }
+            wave_lds_fence();   // the next half rewrites the tile
         }
+        cur = nxt;
     }
 }
 
@@ -178,14 +214,19 @@ static hipError_t launch_combine_t(const ChunkArgs& a, int CK, const SegPlan& sp
     const int BH = a.B * a.H;
     SegArgs s{reinterpret_cast<const float*>(ws + sp.off_Z), reinterpret_cast<const float*>(ws + sp.off_P),
               reinterpret_cast<bf16*>(ws + sp.off_E), reinterpret_cast<const bf16*>(ws + sp.off_qt),
-              static_cast<bf16*>(a.o), a.S_final, a.L, a.dv, sp.SEG, sp.NCS * CK};
-    hipLaunchKernelGGL(seg_entry_kernel<DK>, dim3(BH * (a.dv / 16)), dim3(64), 0, a.stream, s);
+              static_cast<bf16*>(a.o), a.S_final, a.L, a.dv, sp.SEG, sp.NCS * CK, sp.N0 * CK};
+    hipLaunchKernelGGL(seg_entry_kernel<DK>, dim3(BH * (a.dv / 16)), dim3(64 * (DK / 16)), 0, a.stream, s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int tiles = (s.TS + kTokWG - 1) / kTokWG;
-    const int lds = a.dv * (DK + 8) * 2;
-    hipLaunchKernelGGL(seg_correct_kernel<DK>, dim3(BH * (sp.SEG - 1) * tiles), dim3(256), lds, a.stream, s,
-                       tiles);
+    const dim3 grid(BH * (sp.SEG - 1) * tiles);
+    // E_g, then one 16-token correction tile per wave (above the 64 KiB a
+    // launch gets without asking, at d_k = d_v = 128)
+    const int lds = a.dv * (DK + 8) * 2 + 4 * 16 * (a.dv + 4) * 4;
+    auto* kern = a.dv == 128 ? seg_correct_kernel<DK, 128> : seg_correct_kernel<DK, 64>;
+    err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, a.stream, s, tiles);
     return hipGetLastError();
 }
 

@@ -92,6 +92,18 @@ def test_workspace_size_query():
     rec = 2 * 32 * (2048 + 2048 + 512)
     assert ws(1, 2, 1024, 128, 128, 64, gdr.GDR_BF16, 1) == \
         rec + 2 * 2 * (128 * 128 * 4 * 2 + 128 * 128 * 2) + 2 * 1024 * 128 * 2
+    # a plan may hold more workgroups than the 256 that run at once when B*H is
+    # a multiple of 8: segment 0 twice as long as each later segment (the
+    # sequence-length sweep at B2 L32768 splits in 2, B1 L65536 in 4); B*H = 36
+    # or the headline shape do not split
+    def seg_ws(B, H, L, seg, dk=128, dv=128):
+        return B * H * (L // 32) * (2048 + 2048 + 512) + \
+            B * H * seg * (dv * dk * 4 + dk * dk * 4 + dv * dk * 2) + B * H * L * dk * 2
+    assert ws(2, 16, 32768, 128, 128, 64, gdr.GDR_BF16, 1) == seg_ws(2, 16, 32768, 2)
+    assert ws(1, 16, 65536, 128, 128, 64, gdr.GDR_BF16, 1) == seg_ws(1, 16, 65536, 4)
+    assert ws(1, 32, 1600, 128, 128, 64, gdr.GDR_BF16, 1) == seg_ws(1, 32, 1600, 2)
+    assert ws(1, 36, 1600, 128, 128, 64, gdr.GDR_BF16, 1) == 36 * 50 * (2048 + 2048 + 512)
+    assert ws(8, 16, 8192, 128, 128, 64, gdr.GDR_BF16, 1) == 128 * 256 * (2048 + 2048 + 512)
     # fp32 operands never segment
     assert ws(1, 2, 1024, 128, 128, 64, gdr.GDR_F32, 1) == 2 * 64 * (1024 + 1024 + 256)
     assert ws(1, 1, 0, 64, 64, 64, gdr.GDR_BF16, 2) == 0
