@@ -52,15 +52,15 @@ FWD_SOURCES = ('gdr_wy.hip', 'gdr_scan.hip', 'gdr_segment.hip', 'gdr_pipe.h', 'g
 BWD_SOURCES = FWD_SOURCES + ('gdr_bwd.hip', 'gdr_bwd_chain.hip', 'gdr_bwd.h')
 MEASURED_TRAFFIC = {
     ("gdn_bf16_B8_H8_L2048_d128", "chunk_wy_kernel + chunk_scan_kernel"):
-        dict(sources=FWD_SOURCES, digest="34ccea5ff7ee9608", read=154.75e6, written=56.73e6),
+        dict(sources=FWD_SOURCES, digest="5d1dc65055561767", read=154.78e6, written=56.67e6),
     ("kda_bf16_B4_H16_L4096_d128", "chunk_wy_channel_kernel + chunk_scan_kernel"):
-        dict(sources=FWD_SOURCES, digest="34ccea5ff7ee9608", read=576.33e6, written=310.38e6),
+        dict(sources=FWD_SOURCES, digest="5d1dc65055561767", read=576.35e6, written=310.38e6),
     ("gdn_decode_bf16_N256_H16_d128", "decode_step_kernel"):
-        dict(sources=('gdr_decode.hip', 'gdr_device.h', 'gdr_internal.h'), digest="ceeaddb62259d5a3", read=274.33e6, written=269.50e6),
+        dict(sources=('gdr_decode.hip', 'gdr_device.h', 'gdr_internal.h'), digest="ceeaddb62259d5a3", read=274.34e6, written=269.49e6),
     ("gdn_bf16_B8_H8_L2048_d128 backward", "chunk_wy_kernel + chunk_scan_kernel + chunk_bwd_chain_pipe_kernel + chunk_bwd_grad_kernel"):
-        dict(sources=BWD_SOURCES, digest="28303736caff90eb", read=525.62e6, written=284.16e6),
+        dict(sources=BWD_SOURCES, digest="7697f1992b9d85ea", read=507.47e6, written=284.17e6),
     ("kda_bf16_B4_H16_L4096_d128 backward", "chunk_wy_channel_kernel + chunk_scan_kernel + chunk_bwd_chain_pipe_kernel + chunk_bwd_grad_channel_kernel"):
-        dict(sources=BWD_SOURCES, digest="28303736caff90eb", read=1662.44e6, written=890.26e6),
+        dict(sources=BWD_SOURCES, digest="7697f1992b9d85ea", read=1608.63e6, written=890.25e6),
 }
 
 

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(64 * (DK / 16)) void seg_entry_kernel(SegArgs p)
 // rows, so that o is read and written as whole rows, 16 bytes a lane.  The
 // next tile's q-transitions and o rows are read before the current tile's
 // products.
-constexpr int kTokWG = 1024;
+constexpr int kTokWG = 512;
 
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void seg_correct_kernel(SegArgs p, int tiles_per_seg)
