@@ -121,7 +121,14 @@ __global__ __launch_bounds__(64 * (DK / 16)) void seg_entry_kernel(SegArgs p)
 // [value][token] fragments and pass through the wave's own LDS tile to token
 // rows, so that o is read and written as whole rows, 16 bytes a lane.  The
 // next tile's q-transitions and o rows are read before the current tile's
-// products.
+// products.  A tile whose (P up to t) q_t are all exactly zero adds nothing
+// (for a finite entry state),
+// and its o rows are neither read nor written: with decaying gates a later
+// segment's transition underflows to zero a few chunks in (GDN gates of
+// log alpha about -2 per token: within two chunks), after which only the
+// q-transitions are read.  Such a tile is seen once its q-transitions have
+// arrived, so the next tile's o rows are read ahead only after a nonzero tile;
+// otherwise they are read when needed.
 constexpr int kTokWG = 512;
 
 template <int DK, int DV>
@@ -159,7 +166,7 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(SegArgs p, int tiles_p
         Frag<bf16> q[2][NKS];   // token 16 h + c16, key channels 32 ks + 8 g4 ..
         u32x4 o[NI];            // row RPI i + orow, columns ocol ..
     };
-    auto load = [&](int t0, Tile& T) {
+    auto load_q = [&](int t0, Tile& T) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int tc = min(t0 + 16 * h + c16, tw1 - 1);
@@ -167,14 +174,44 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(SegArgs p, int tiles_p
             for (int ks = 0; ks < NKS; ++ks)
                 T.q[h][ks].v = *reinterpret_cast<const bf16x8*>(qt + (size_t)tc * DK + 32 * ks + 8 * g4);
         }
+    };
+    auto load_o = [&](int t0, Tile& T) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) T.o[i] = ld16(o + (size_t)min(t0 + RPI * i + orow, tw1 - 1) * DV + ocol);
     };
     Tile cur, nxt;
     int t0 = tw0 + 32 * w;   // wave-uniform
-    if (t0 < tw1) load(t0, cur);
+    bool cur_o = false;      // cur.o holds the tile's o rows
+    if (t0 < tw1) {
+        load_q(t0, cur);
+        load_o(t0, cur);
+        cur_o = true;
+    }
     for (; t0 < tw1; t0 += 128) {
-        if (t0 + 128 < tw1) load(t0 + 128, nxt);
+        // does any q-transition of this tile differ from zero (bits: -0 is zero too)
+        unsigned bits = 0u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const u32x4 x = __builtin_bit_cast(u32x4, cur.q[h][ks].v);
+                bits |= (x.x | x.y | x.z | x.w) & 0x7fff7fffu;
+            }
+        const bool live = __any(bits != 0u);   // wave-uniform
+        bool nxt_o = false;
+        if (t0 + 128 < tw1) {
+            load_q(t0 + 128, nxt);
+            if (live) {
+                load_o(t0 + 128, nxt);
+                nxt_o = true;
+            }
+        }
+        if (!live) {
+            cur = nxt;
+            cur_o = nxt_o;
+            continue;
+        }
+        if (!cur_o) load_o(t0, cur);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -204,6 +241,7 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(SegArgs p, int tiles_p
             wave_lds_fence();   // the next half rewrites the tile
         }
         cur = nxt;
+        cur_o = nxt_o;
     }
 }
 
