@@ -124,18 +124,29 @@ def chunked_kernel_name(w) -> str:
 
 def copy_probe(mib: int, reps: int = 5):
     """Plain device copies of a known size, for scaling the HBM byte counters
-    (FETCH_SIZE, WRITE_SIZE) a profiler reads for the kernels above."""
+    (FETCH_SIZE, WRITE_SIZE) a profiler reads for the kernels above.  Each
+    copy is also timed (an event pair on the current stream, after one
+    untimed copy of each kind): the read + write rate a plain streaming
+    kernel reaches on this device, the practical ceiling of a kernel that
+    reads and writes its bytes once, as the decode step does."""
     dev = torch.device("cuda:0")
     n = mib << 20
     src = torch.ones(n // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
-    for _ in range(reps):
-        dst.copy_(src)
-    for _ in range(reps):
-        torch.neg(src, out=dst)
-    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.neg(src, out=dst)
+    rate = {}
+    for name, fn in (("copy_", lambda: dst.copy_(src)), ("neg", lambda: torch.neg(src, out=dst))):
+        ev = _events(2 * reps)
+        for i in range(reps):
+            ev[2 * i].record()
+            fn()
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        ms = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps))
+        rate[name] = {"median_ms": ms[reps // 2], "GB_per_s": 2 * n / (ms[reps // 2] * 1e-3) / 1e9}
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "reps": reps,
-                      "kernels": ["copy_", "neg"]}))
+                      "kernels": ["copy_", "neg"], "rate": rate}))
 
 
 def _events(n):
