@@ -469,7 +469,10 @@ def chunked_summary(w, r, step, prologue=0):
                      "isolated_call_ms_mean": r["isolated_ms_mean"]},
         "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s",
                  "frac": tflops / mfma_peak, "algorithmic_flops_per_call": flops,
-                 "count": f"triangular, at the executed {step}-token step"},
+                 "count": f"triangular, at the executed {step}-token step",
+                 # the most this call's MFMA fraction could be: its flops done in
+                 # the time its algorithmic bytes take at peak HBM bandwidth
+                 "ceiling_at_hbm_floor": flops / (nbytes / (HBM_PEAK_GBS * 1e9)) / 1e12 / mfma_peak},
     }
 
 
