@@ -384,3 +384,36 @@ def test_noalloc_limit_matches_workspace_query():
     assert big > gdr.GDR_NOALLOC_SCRATCH_BYTES
     head = gdr.gdr_fwd_chunked_workspace_size(8, 8, 2048, 128, 128, 64, gdr.GDR_BF16, 1)
     assert 0 < head <= gdr.GDR_NOALLOC_SCRATCH_BYTES
+
+def test_segment_plan_invariants():
+    """The segment plan read back from the workspace size over a grid of
+    shapes: bf16 only; never when the unsplit scan already holds more than
+    the 256 workgroups that run at once; at most 16 segments of at least 16
+    chunks; more workgroups than run at once only when B*H is a multiple of
+    8, and then no more waiting workgroups than later-segment workgroups of
+    the first round."""
+    al = lambda x: (x + 255) // 256 * 256
+    for (B, H) in [(1, 1), (1, 2), (1, 5), (1, 8), (2, 8), (1, 16), (2, 16), (1, 24), (1, 32), (2, 24),
+                   (1, 36), (1, 48), (4, 16), (8, 8), (8, 16), (32, 16)]:
+        for L in [1000, 1600, 4096, 8192, 32768, 65536]:
+            for dk, dv in [(128, 128), (64, 64), (64, 128), (128, 64)]:
+                BH, nc = B * H, (L + 31) // 32
+                rec = BH * nc * (2 * 32 * 32 * 2 + 16 * 32)
+                got = gdr.gdr_fwd_chunked_workspace_size(B, H, L, dk, dv, 64, gdr.GDR_BF16, 1)
+                seg = 1 if got == rec else None
+                for g in range(2, 17):
+                    z = al(al(rec) + BH * g * dv * dk * 4)
+                    pt = al(z + BH * g * dk * dk * 4)
+                    e = al(pt + BH * g * dv * dk * 2)
+                    if al(e + BH * L * dk * 2) == got:
+                        seg = g
+                assert seg is not None, (B, H, L, dk, dv, got)
+                nvb, nmb = dv // 32, dk // 32
+                w0, w = BH * nvb, BH * (nvb + (seg - 1) * (nvb + nmb))
+                if seg > 1:
+                    assert w0 <= 256 and nc >= 2 * 16
+                    if w > 256:
+                        assert BH % 8 == 0 and w + w0 <= 512, (B, H, L, dk, dv, seg)
+                # fp32 never splits
+                assert gdr.gdr_fwd_chunked_workspace_size(B, H, L, dk, dv, 64, gdr.GDR_F32, 1) == \
+                    BH * ((L + 15) // 16) * (2 * 16 * 16 * 4 + 16 * 16)
